@@ -1,0 +1,242 @@
+/*
+ * synth.c — seeded, counter-based synthetic inputs for the weight-streaming
+ * Q4_K-style GEMM.  This module holds no part of the GEMM's arithmetic: it only
+ * draws random fields and writes them in the canonical super-block byte layout
+ * (the input interface of the library) and bf16 activation rows.  Both the HIP
+ * path and the fp64 oracle consume what it writes; neither shares code with it
+ * beyond reading those bytes.
+ *
+ * Workloads (the matrix shapes, value ranges and row counts) follow the stated
+ * workload set for this hot path: Q4_K-style super-blocks of 256 weights with
+ * fp16 d, dmin ~ U(0.001, 0.02), eight 32-wide sub-blocks with 6-bit scale and
+ * 6-bit min ~ U{0..63}, 4-bit quants ~ U{0..15}; activations bf16 ~ N(0, 1),
+ * optionally with a fraction of entries scaled by a fixed factor (outliers).
+ *
+ * Canonical super-block (144 bytes):
+ *   [0,2)    d     IEEE binary16, little endian
+ *   [2,4)    dmin  IEEE binary16, little endian
+ *   [4,16)   96-bit little-endian bit stream of sixteen 6-bit fields:
+ *            field f (0..7) = sc_f at stream bits [6f, 6f+6),
+ *            field 8+f      = m_f  at stream bits [48+6f, 54+6f);
+ *            stream bit b is bit (b mod 8) of byte 4 + b/8
+ *   [16,144) 128 bytes of quants: byte i = q[2i] | q[2i+1] << 4, where q[k]
+ *            (k = 32*s + t) is the quant of weight k of the super-block
+ * Super-blocks of an N x K matrix are stored row-major: block (n, j) covers
+ * weights W[n, 256j .. 256j+255] and sits at byte offset 144 * (n*K/256 + j).
+ *
+ * Random numbers: SplitMix64's output function (Steele, Lea & Flood,
+ * "Fast splittable pseudorandom number generators", OOPSLA 2014) applied to a
+ * counter, keyed by (seed, stream id, field).  Any super-block of any matrix can
+ * therefore be regenerated on its own.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#include <pthread.h>
+
+#define GOLDEN 0x9E3779B97F4A7C15ULL
+
+enum {
+    F_D = 1, F_DMIN = 2, F_SC = 3, F_M = 4, F_Q = 5, F_EDGE = 6,
+    F_XA = 7, F_XB = 8, F_OUT = 9
+};
+
+uint64_t synth_mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+static uint64_t stream_key(uint64_t seed, uint64_t sid, uint64_t field)
+{
+    uint64_t k = synth_mix64(seed + GOLDEN);
+    k = synth_mix64(k ^ (sid + GOLDEN));
+    k = synth_mix64(k ^ (field * GOLDEN));
+    return k;
+}
+
+static inline uint64_t draw(uint64_t key, uint64_t i)
+{
+    return synth_mix64(key + (i + 1) * GOLDEN);
+}
+
+/* uniform in [0, 1) with 53 random bits */
+static inline double unit53(uint64_t u) { return (double)(u >> 11) * 0x1.0p-53; }
+
+/* Round a double to the nearest IEEE binary16 (ties to even). */
+uint16_t synth_f64_to_f16(double v)
+{
+    uint64_t b;
+    memcpy(&b, &v, 8);
+    uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    if (v != v) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u); /* rounds to inf */
+    int e;
+    frexp(a, &e);              /* a = f * 2^e, f in [0.5, 1) */
+    int ex = e - 1;            /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -14) ex = -14;    /* subnormal range uses quantum 2^-24 */
+    double quantum = ldexp(1.0, ex - 10);
+    double q = a / quantum;    /* exact: division by a power of two */
+    double r = nearbyint(q);   /* default rounding mode: ties to even */
+    uint32_t mant = (uint32_t)r; /* integer in [0, 2048] */
+    uint32_t out;
+    if (ex == -14 && mant < 1024) {
+        out = mant;            /* subnormal (or rounds to smallest normal: mant==1024 handled below) */
+    } else {
+        if (mant == 2048) { mant = 1024; ex += 1; }
+        if (ex > 15) return (uint16_t)(sign | 0x7C00u);
+        out = ((uint32_t)(ex + 15) << 10) | (mant - 1024);
+    }
+    return (uint16_t)(sign | out);
+}
+
+/* Round a double to the nearest bfloat16 (ties to even), directly (no
+ * intermediate float rounding).  Subnormal and overflow handling included. */
+uint16_t synth_f64_to_bf16(double v)
+{
+    uint64_t b;
+    memcpy(&b, &v, 8);
+    uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    if (v != v) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    int ex = e - 1;
+    if (ex < -126) ex = -126;
+    double quantum = ldexp(1.0, ex - 7);
+    double r = nearbyint(a / quantum);
+    uint32_t mant = (uint32_t)r; /* in [0, 256] */
+    uint32_t out;
+    if (ex == -126 && mant < 128) {
+        out = mant;
+    } else {
+        if (mant == 256) { mant = 128; ex += 1; }
+        if (ex > 127) return (uint16_t)(sign | 0x7F80u);
+        out = ((uint32_t)(ex + 127) << 7) | (mant - 128);
+    }
+    return (uint16_t)(sign | out);
+}
+
+/* ---- weights --------------------------------------------------------------
+ * edge_mode 0: every super-block drawn from the stated distributions.
+ * edge_mode 1: super-block b is of kind (b mod 4): 0 dmin = 0, 1 all quants 0,
+ *              2 all quants 15, 3 ordinary.
+ * edge_mode 2: a seeded 3% of super-blocks (1% of each special kind) are
+ *              special, the rest ordinary.                                    */
+enum { KIND_DMIN0 = 0, KIND_Q0 = 1, KIND_Q15 = 2, KIND_NORMAL = 3 };
+
+static void put_field(uint8_t *bits12, int pos, uint32_t val6)
+{
+    for (int i = 0; i < 6; i++) {
+        int b = pos + i;
+        if ((val6 >> i) & 1u) bits12[b >> 3] |= (uint8_t)(1u << (b & 7));
+    }
+}
+
+static void make_block(uint64_t kd, uint64_t kdm, uint64_t ksc, uint64_t km,
+                       uint64_t kq, uint64_t ke, int edge_mode, uint64_t b,
+                       uint8_t *out)
+{
+    int kind = KIND_NORMAL;
+    if (edge_mode == 1) {
+        kind = (int)(b & 3u);
+    } else if (edge_mode == 2) {
+        uint64_t u = draw(ke, b);
+        if (unit53(u) < 0.03) kind = (int)((u & 0xFFu) % 3u);
+    }
+    double d = 0.001 + 0.019 * unit53(draw(kd, b));
+    double dm = 0.001 + 0.019 * unit53(draw(kdm, b));
+    uint16_t hd = synth_f64_to_f16(d);
+    uint16_t hdm = (kind == KIND_DMIN0) ? 0 : synth_f64_to_f16(dm);
+    out[0] = (uint8_t)(hd & 0xFF); out[1] = (uint8_t)(hd >> 8);
+    out[2] = (uint8_t)(hdm & 0xFF); out[3] = (uint8_t)(hdm >> 8);
+    memset(out + 4, 0, 12);
+    for (int s = 0; s < 8; s++) {
+        uint32_t sc = (uint32_t)(draw(ksc, b * 8 + (uint64_t)s) >> 58);
+        uint32_t m = (uint32_t)(draw(km, b * 8 + (uint64_t)s) >> 58);
+        put_field(out + 4, 6 * s, sc);
+        put_field(out + 4, 48 + 6 * s, m);
+    }
+    uint8_t *qs = out + 16;
+    if (kind == KIND_Q0) { memset(qs, 0x00, 128); return; }
+    if (kind == KIND_Q15) { memset(qs, 0xFF, 128); return; }
+    for (int c = 0; c < 16; c++) {           /* 16 draws x 16 nibbles = 256 */
+        uint64_t u = draw(kq, b * 16 + (uint64_t)c);
+        for (int t = 0; t < 8; t++) {
+            uint8_t lo = (uint8_t)(u >> (8 * t)) & 0xF;
+            uint8_t hi = (uint8_t)(u >> (8 * t + 4)) & 0xF;
+            qs[c * 8 + t] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+typedef struct {
+    uint64_t seed, mid;
+    int64_t KB, b0, b1;
+    int edge_mode;
+    uint8_t *out;
+} wjob;
+
+static void *wrun(void *p)
+{
+    wjob *j = (wjob *)p;
+    uint64_t kd = stream_key(j->seed, j->mid, F_D), kdm = stream_key(j->seed, j->mid, F_DMIN);
+    uint64_t ksc = stream_key(j->seed, j->mid, F_SC), km = stream_key(j->seed, j->mid, F_M);
+    uint64_t kq = stream_key(j->seed, j->mid, F_Q), ke = stream_key(j->seed, j->mid, F_EDGE);
+    for (int64_t b = j->b0; b < j->b1; b++)
+        make_block(kd, kdm, ksc, km, kq, ke, j->edge_mode, (uint64_t)b,
+                   j->out + (b - j->b0) * 144);
+    return 0;
+}
+
+/* Canonical bytes for rows [n0, n1) of matrix (seed, mid), shape N x K
+ * (K a multiple of 256).  out receives (n1-n0) * K/256 * 144 bytes.
+ * Returns 0, or -1 on bad arguments. */
+int synth_matrix_rows(uint64_t seed, uint64_t mid, int64_t N, int64_t K,
+                      int64_t n0, int64_t n1, int edge_mode, uint8_t *out,
+                      int nthreads)
+{
+    if (K <= 0 || K % 256 != 0 || n0 < 0 || n1 > N || n0 > n1 || !out) return -1;
+    if (edge_mode < 0 || edge_mode > 2) return -1;
+    int64_t KB = K / 256;
+    int64_t B0 = n0 * KB, B1 = n1 * KB, nb = B1 - B0;
+    if (nb == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 64) nthreads = 64;
+    if (nb < 4096) nthreads = 1;
+    pthread_t th[64];
+    wjob jobs[64];
+    for (int t = 0; t < nthreads; t++) {
+        int64_t a = B0 + nb * t / nthreads, c = B0 + nb * (t + 1) / nthreads;
+        jobs[t] = (wjob){seed, mid, KB, a, c, edge_mode, out + (a - B0) * 144};
+    }
+    for (int t = 1; t < nthreads; t++) pthread_create(&th[t], 0, wrun, &jobs[t]);
+    wrun(&jobs[0]);
+    for (int t = 1; t < nthreads; t++) pthread_join(th[t], 0);
+    return 0;
+}
+
+/* ---- activations ----------------------------------------------------------
+ * x[r, k] for r < R, k < K, stream (seed, sid): Box-Muller standard normal
+ * from two counter draws, multiplied by outlier_scale with probability
+ * outlier_p (decided by a third draw), then rounded once to bf16. */
+int synth_x(uint64_t seed, uint64_t sid, int64_t R, int64_t K, double outlier_p,
+            double outlier_scale, uint16_t *out)
+{
+    if (R < 0 || K < 0 || (!out && R * K > 0)) return -1;
+    uint64_t ka = stream_key(seed, sid, F_XA), kb = stream_key(seed, sid, F_XB);
+    uint64_t ko = stream_key(seed, sid, F_OUT);
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int64_t i = 0; i < R * K; i++) {
+        double u1 = ((double)(draw(ka, (uint64_t)i) >> 11) + 1.0) * 0x1.0p-53; /* (0, 1] */
+        double u2 = unit53(draw(kb, (uint64_t)i));
+        double z = sqrt(-2.0 * log(u1)) * cos(two_pi * u2);
+        if (outlier_p > 0.0 && unit53(draw(ko, (uint64_t)i)) < outlier_p) z *= outlier_scale;
+        out[i] = synth_f64_to_bf16(z);
+    }
+    return 0;
+}
