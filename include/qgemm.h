@@ -1,0 +1,164 @@
+/*
+ * qgemm.h — C ABI of the weight-streaming Q4_K-style GEMM for MI355X (gfx950).
+ *
+ * The operation (OpenJet multi-agent serving page, section on moving the
+ * weights only once): one decode step stacks the rows of every active agent
+ * (each agent's next token plus two draft tokens: four agents give twelve rows)
+ * into one batch and streams the quantised weights from memory once; every
+ * weight read is applied to all stacked rows.  For one weight matrix:
+ *
+ *     y[r, n] = sum_{k=0}^{K-1} w[n, k] * x[r, k]      0 <= r < R, 0 <= n < N
+ *     w[n, k] = d * sc_s * q_k - dmin * m_s             (Q4_K-style block)
+ *
+ * with fp32 accumulation.  A block holds 256 consecutive weights of one output
+ * n: binary16 d and dmin, eight 32-wide sub-blocks s with a 6-bit scale sc_s
+ * and a 6-bit min m_s, and 4-bit quants q_k.
+ *
+ * Canonical block bytes (144 B, the input format of qgemm_pack):
+ *   [0,2) d, [2,4) dmin (binary16, little endian);
+ *   [4,16) a 96-bit little-endian bit stream of sixteen 6-bit fields: sc_s at
+ *          bits [6s, 6s+6), m_s at bits [48+6s, 54+6s);
+ *   [16,144) quants: byte i = q_{2i} | q_{2i+1} << 4.
+ * Block (n, j) covers w[n, 256j .. 256j+255] at byte 144 * (n * K/256 + j).
+ *
+ * Conventions for every call:
+ *   - Device pointers are hipMalloc'd (or torch) memory of the current device;
+ *     the library never frees memory it did not allocate.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls that take a
+ *     stream only enqueue work and return; errors of the kernels themselves
+ *     appear at the caller's next synchronisation.
+ *   - Every call validates its arguments on the host before touching the GPU
+ *     and returns a qgemm_status; nothing aborts.  Launch failures return
+ *     QGEMM_EHIP.
+ *   - Shapes: K a positive multiple of 256; N >= 1; 0 <= R <= QGEMM_MAX_R.
+ *   - x is bf16 (bit patterns, R x K row-major), y is fp32 (R x N row-major,
+ *     overwritten).  x enters the matrix cores as binary16: values with
+ *     2^-17 <= |x| <= 65504 (and zero) are exact there; smaller magnitudes are
+ *     rounded to a multiple of 2^-24 and larger ones are outside the supported
+ *     range (they become infinities).
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QGEMM_MAX_R 64
+
+typedef enum {
+    QGEMM_OK = 0,
+    QGEMM_EINVAL = -1,    /* null pointer, bad handle or bad flag */
+    QGEMM_ESHAPE = -2,    /* K not a positive multiple of 256, N < 1, or sizes overflow */
+    QGEMM_EALIGN = -3,    /* a device pointer is not 16-byte aligned */
+    QGEMM_ERANGE_R = -4,  /* R < 0, R > max_R of the handle, or max_R out of 1..QGEMM_MAX_R */
+    QGEMM_ENOMEM = -5,    /* the library could not allocate its workspace */
+    QGEMM_EHIP = -6,      /* a HIP call or kernel launch failed */
+    QGEMM_EPATH = -7      /* requested kernel path cannot serve this R */
+} qgemm_status;
+
+/* Kernel paths (the R-dependent selection chooses between them). */
+typedef enum {
+    QGEMM_PATH_AUTO = 0,  /* the library's choice for (R, N, K) */
+    QGEMM_PATH_VALU = 1,  /* vector-ALU bandwidth path (small R only) */
+    QGEMM_PATH_MFMA = 2   /* matrix-core path (any R) */
+} qgemm_path;
+
+typedef struct qgemm_handle *qgemm_t;
+typedef struct qgemm_seq *qgemm_seq_t;
+
+/* What a run of (R, path) would launch. */
+typedef struct {
+    int path;               /* QGEMM_PATH_VALU or QGEMM_PATH_MFMA */
+    int split_k;            /* number of K splits (1 = none) */
+    int row_tiles;          /* 16-row tiles on the matrix-core path (0 on the VALU path) */
+    int subtiles_per_wave;  /* 16-output sub-tiles per wave */
+    int64_t waves;          /* waves in the main kernel launch */
+    int kernels;            /* kernels enqueued per run */
+    size_t workspace_bytes; /* bytes of the handle's workspace this run touches */
+} qgemm_info;
+
+/* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights
+ * of N rounded up to a multiple of 16 (the canonical size plus N-tail padding).
+ * Errors: QGEMM_EINVAL (bytes NULL), QGEMM_ESHAPE. */
+int qgemm_packed_size(int64_t N, int64_t K, size_t *bytes);
+
+/* Rearrange canonical blocks (device, N*K/256*144 bytes, 16-byte aligned) into
+ * the packed layout (device, qgemm_packed_size bytes, 16-byte aligned).  Both
+ * buffers belong to the caller; canon may be freed once the stream has run the
+ * work.  The packed bytes are a pure re-arrangement: no value is changed.
+ * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_EHIP. */
+int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, void *stream);
+
+/* Create a handle over packed weights.  The handle BORROWS packed_dev (it must
+ * stay valid and unchanged until qgemm_destroy) and OWNS a device workspace
+ * sized for up to max_R rows (activation operands, split-K partials).  flags
+ * must be 0.  Synchronous.
+ * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_ERANGE_R,
+ * QGEMM_ENOMEM, QGEMM_EHIP. */
+int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int max_R,
+                 uint32_t flags);
+
+/* y = x . W^T for R rows on `stream`, with the R-dependent kernel choice.
+ * x: device bf16 [R x K], y: device fp32 [R x N], both 16-byte aligned.
+ * R = 0 is a no-op.  Runs of one handle share its workspace: do not run one
+ * handle on two streams at once.
+ * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_EHIP. */
+int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
+
+/* As qgemm_run with an explicit path (QGEMM_PATH_AUTO = qgemm_run).
+ * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not
+ * serve (R > 4). */
+int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, void *stream);
+
+/* The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
+ * 16-byte aligned): w_out[n, k] is the binary32 value nearest to
+ * d*sc_s*q_k - dmin*m_s (one rounding; bit-exact), decoded from the packed
+ * layout by the same unpacking the GEMM kernels use.
+ * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_EHIP. */
+int qgemm_dequantize(qgemm_t h, float *w_out, void *stream);
+
+/* idx[r] = the smallest n with y[r, n] = max over n of y[r, n], for r < R
+ * (y: device fp32 [R x N]; idx: device int32 [R]).  NaN entries never win;
+ * a row of NaNs gives 0.  The greedy pick over the output-head logits.
+ * Errors: QGEMM_EINVAL, QGEMM_ESHAPE (N < 1), QGEMM_ERANGE_R (R < 0), QGEMM_EHIP. */
+int qgemm_argmax_rows(const float *y, int R, int64_t N, int32_t *idx, void *stream);
+
+/* Describe the launch plan for (R, path) without running it.
+ * Errors: QGEMM_EINVAL, QGEMM_ERANGE_R, QGEMM_EPATH. */
+int qgemm_query(qgemm_t h, int R, int path, qgemm_info *info);
+
+/* Free the handle and its workspace (not the packed weights).  Waits for the
+ * device to finish work that may use the workspace.  NULL is a no-op. */
+int qgemm_destroy(qgemm_t h);
+
+/* ---- full weight pass -------------------------------------------------------
+ * A sequence of handles run back to back in the given (dependency) order, as
+ * one decode step's weight pass: layer after layer of projections and then the
+ * output head, each weight byte read once.  The sequence BORROWS the handles.
+ * count >= 1.  Errors: QGEMM_EINVAL, QGEMM_ENOMEM. */
+int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count);
+
+/* Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]
+ * (arrays of `count` device pointers, shapes as for qgemm_run).  If argmax_idx
+ * is not NULL, the row argmax of the LAST GEMM's output is written to it
+ * (device int32 [R]).  The first run for a given (R, pointer set) captures the
+ * launches into a HIP graph; later identical runs replay it.
+ * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays. */
+int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
+                  int32_t *argmax_idx, void *stream);
+
+/* Free the sequence and its captured graphs (not the handles).  NULL is a no-op. */
+int qgemm_seq_destroy(qgemm_seq_t s);
+
+/* Static text for a status code. */
+const char *qgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,81 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_streaming_gemm_amd as wsg
+from weight_streaming_gemm_amd import qgemm as Q
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13
+    L = Q.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in qgemm.h but not exported"
+    assert set(names) == set(Q.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        s = wsg.status_string(code)
+        assert s and s != "unknown status"
+    assert wsg.status_string(-99) == "unknown status"
+
+
+def test_packed_size():
+    assert wsg.packed_size(256, 1024) == 147456
+    assert wsg.packed_size(151936, 5120) == 437_575_680
+    assert wsg.packed_size(17, 256) == 32 * 144          # N padded to 16
+    for N, K in ((0, 256), (16, 100), (16, 0), (-1, 256), (16, 255)):
+        with pytest.raises(Q.QGemmError) as e:
+            wsg.packed_size(N, K)
+        assert e.value.status == Q.QGEMM_ESHAPE
+    assert Q.lib().qgemm_packed_size(16, 256, None) == Q.QGEMM_EINVAL
+
+
+def test_host_validation_codes():
+    L = Q.lib()
+    vp = ctypes.c_void_p
+    assert L.qgemm_pack(None, vp(4096), 16, 256, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_pack(vp(4096), vp(4096), 16, 100, None) == Q.QGEMM_ESHAPE
+    assert L.qgemm_pack(vp(4097), vp(4096), 16, 256, None) == Q.QGEMM_EALIGN
+    h = vp()
+    assert L.qgemm_create(ctypes.byref(h), vp(4096), 16, 256, 0, 0) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_create(ctypes.byref(h), vp(4096), 16, 256, 65, 0) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_create(ctypes.byref(h), vp(4096), 16, 256, 12, 1) == Q.QGEMM_EINVAL
+    assert L.qgemm_create(ctypes.byref(h), vp(4104), 16, 256, 12, 0) == Q.QGEMM_EALIGN
+    assert L.qgemm_create(None, vp(4096), 16, 256, 12, 0) == Q.QGEMM_EINVAL
+    assert L.qgemm_run(None, vp(4096), vp(4096), 1, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_run_path(None, vp(4096), vp(4096), 1, 2, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_dequantize(None, vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_query(None, 1, 0, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_argmax_rows(vp(4096), -1, 10, vp(4096), None) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_argmax_rows(vp(4096), 2, 0, vp(4096), None) == Q.QGEMM_ESHAPE
+    assert L.qgemm_argmax_rows(None, 2, 10, vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_argmax_rows(None, 0, 10, None, None) == Q.QGEMM_OK        # R = 0: no-op
+    s = vp()
+    assert L.qgemm_seq_create(ctypes.byref(s), None, 1) == Q.QGEMM_EINVAL
+    assert L.qgemm_seq_run(None, None, None, 1, None, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_destroy(None) == Q.QGEMM_OK
+    assert L.qgemm_seq_destroy(None) == Q.QGEMM_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(Q, "_lib", None)
+    with pytest.raises(RuntimeError):
+        Q.lib()

@@ -1,0 +1,233 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: dequantised fp32 weights bit-exact; y within max_rel <= 2e-3 and
+rel_l2 <= 1e-4 (tests/parity.py); argmax exact; integer/index work bit-exact.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_util as G
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg: str):
+    print(msg, flush=True)
+
+
+# ---- builtin layouts and rounding (in-bounds probes, one wave each) ----------
+
+def test_probe_mfma_16x16x32_f16_layout():
+    import torch
+    from tests import probe
+    rng = np.random.default_rng(0)
+    A = rng.integers(-4, 5, size=(16, 32)).astype(np.float16)
+    B = rng.integers(-4, 5, size=(32, 16)).astype(np.float16)
+    a = np.zeros((64, 8), np.float16)
+    b = np.zeros((64, 8), np.float16)
+    for l in range(64):
+        for e in range(8):
+            a[l, e] = A[l % 16, 8 * (l // 16) + e]
+            b[l, e] = B[8 * (l // 16) + e, l % 16]
+    ad, bd = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    d = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    assert probe.lib().probe_mfma_16x16x32_f16(ad.data_ptr(), bd.data_ptr(), d.data_ptr()) == 0
+    torch.cuda.synchronize()
+    D = A.astype(np.float64) @ B.astype(np.float64)
+    got = d.cpu().numpy()
+    for l in range(64):
+        for v in range(4):
+            assert got[l, v] == D[4 * (l // 16) + v, l % 16]
+
+
+def test_probe_mfma_16x16x4_f32_layout():
+    import torch
+    from tests import probe
+    rng = np.random.default_rng(1)
+    A = rng.integers(-9, 10, size=(16, 4)).astype(np.float32)
+    B = rng.integers(-9, 10, size=(4, 16)).astype(np.float32)
+    a = np.array([A[l % 16, l // 16] for l in range(64)], np.float32)
+    b = np.array([B[l // 16, l % 16] for l in range(64)], np.float32)
+    d = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    ad, bd = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    assert probe.lib().probe_mfma_16x16x4_f32(ad.data_ptr(), bd.data_ptr(), d.data_ptr()) == 0
+    torch.cuda.synchronize()
+    D = A.astype(np.float64) @ B.astype(np.float64)
+    got = d.cpu().numpy()
+    for l in range(64):
+        for v in range(4):
+            assert got[l, v] == D[4 * (l // 16) + v, l % 16]
+
+
+def test_probe_pk_fma_f16_exact_operands():
+    """(1024 + q) sc - 1024 sc and (1024 + 16 q) sc/16 - 64 sc must give sc q
+    exactly for every 6-bit sc and 4-bit q (single rounding of an exact value)."""
+    import torch
+    from tests import probe
+    sc, q = np.meshgrid(np.arange(64), np.arange(16), indexing="ij")
+    sc, q = sc.ravel().astype(np.float64), q.ravel().astype(np.float64)
+    a = np.stack([1024 + q, 1024 + 16 * q], 1).astype(np.float16)
+    b = np.stack([sc, sc / 16], 1).astype(np.float16)
+    c = np.stack([-1024 * sc, -64 * sc], 1).astype(np.float16)
+    n = a.shape[0]
+    out = torch.zeros((n, 2), dtype=torch.float16, device="cuda")
+    ad, bd, cd = (torch.from_numpy(v).cuda() for v in (a, b, c))
+    assert probe.lib().probe_pk_fma_f16(ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), out.data_ptr(), n) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[:, 0], sc * q)
+    assert np.array_equal(got[:, 1], sc * q)
+
+
+# ---- dequantisation: bit-exact ----------------------------------------------
+
+@pytest.mark.parametrize("N,K,edge", [(256, 1024, 0), (40, 512, 1), (1000, 2048, 2), (19, 256, 0)])
+def test_dequant_bit_exact(orc, N, K, edge):
+    _flush(f"dequant N={N} K={K} edge={edge}")
+    canon, g = G.make(4, 11, N, K, max_R=4, edge_mode=edge)
+    w = G.dequant(g)
+    ref = orc.dequant(canon, N, K, f32=True)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32))
+    g.close()
+
+
+# ---- GEMM parity ---------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def small():
+    canon, g = G.make(0, 0, 256, 1024, max_R=64)
+    yield canon, g
+    g.close()
+
+
+@pytest.mark.parametrize("R", list(range(1, 17)) + [24, 48, 64])
+def test_gemm_small_workload_all_R(orc, small, R):
+    _flush(f"gemm small R={R}")
+    canon, g = small
+    x = synth.x_bf16(0, 1, R, 1024)
+    y = G.run(g, x)
+    assert_parity(y, orc.gemm(canon, 256, 1024, x), f"R={R}")
+
+
+@pytest.mark.parametrize("N,K,R", [(40, 8192, 12), (1000, 25600, 3), (17, 5120, 7), (5120, 1024, 12),
+                                   (33, 256, 1), (4000, 2048, 48)])
+def test_gemm_ragged_and_split(orc, N, K, R):
+    _flush(f"gemm N={N} K={K} R={R}")
+    canon, g = G.make(1, 5, N, K, max_R=R)
+    info = g.query(R)
+    x = synth.x_bf16(1, 6, R, K, outlier_p=0.01)
+    y = G.run(g, x)
+    assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} split={info['split_k']}")
+    g.close()
+
+
+def test_edge_blocks_large_R(orc):
+    N, K = 512, 2048
+    canon, g = G.make(4, 0, N, K, max_R=48, edge_mode=1)
+    for R in (24, 48):
+        x = synth.x_bf16(4, R, R, K)
+        assert_parity(G.run(g, x), orc.gemm(canon, N, K, x), f"edge R={R}")
+    g.close()
+
+
+def test_one_hot_columns_pin_gemm_dequant(orc):
+    """x = e_k gives y[:, n] = w[n, k]; with the factored algebra this is the
+    fp32 dequantised weight up to the final rounding of two exact parts."""
+    N, K = 64, 512
+    canon, g = G.make(2, 3, N, K, max_R=16)
+    ks = [0, 1, 31, 32, 100, 255, 256, 300, 511, 64, 65, 127, 128, 200, 400, 480]
+    x = np.zeros((len(ks), K), np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80
+    y = G.run(g, x)
+    w = orc.dequant(canon, N, K)
+    for i, k in enumerate(ks):
+        np.testing.assert_allclose(y[i], w[:, k], rtol=1e-6, atol=1e-7)
+
+
+def test_determinism_and_row_independence(small):
+    canon, g = small
+    R = 12
+    x = synth.x_bf16(7, 1, R, 1024)
+    y1 = G.run(g, x)
+    y2 = G.run(g, x)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    x2 = x.copy()
+    x2[5:] = synth.x_bf16(8, 1, R - 5, 1024)
+    y3 = G.run(g, x2)
+    assert np.array_equal(y3[:5].view(np.uint32), y1[:5].view(np.uint32))
+
+
+def test_row_count_zero_and_errors(small):
+    import torch
+    from weight_streaming_gemm_amd import qgemm as Q
+    canon, g = small
+    x = torch.zeros((65, 1024), dtype=torch.int16, device="cuda")
+    y = torch.zeros((65, 256), dtype=torch.float32, device="cuda")
+    L = Q.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.qgemm_run(g.h, x.data_ptr(), y.data_ptr(), 0, st) == Q.QGEMM_OK
+    assert L.qgemm_run(g.h, x.data_ptr(), y.data_ptr(), 65, st) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_run(g.h, x.data_ptr(), y.data_ptr(), -1, st) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_run(g.h, x.data_ptr() + 2, y.data_ptr(), 1, st) == Q.QGEMM_EALIGN
+    assert L.qgemm_run_path(g.h, x.data_ptr(), y.data_ptr(), 1, 9, st) == Q.QGEMM_EINVAL
+    torch.cuda.synchronize()
+    assert float(y.abs().sum()) == 0.0
+
+
+# ---- argmax -------------------------------------------------------------------
+
+def test_argmax_ties_and_nan():
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    y = np.array([[1, 3, 3, 2], [-1, -1, -5, -1], [0, 0, 0, 0], [np.nan, 2, np.nan, 2],
+                  [np.nan, np.nan, np.nan, np.nan]], np.float32)
+    yd = torch.from_numpy(y).cuda()
+    idx = torch.empty(5, dtype=torch.int32, device="cuda")
+    wsg.argmax_rows(yd, idx)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [1, 0, 0, 1, 0]
+    rng = np.random.default_rng(3)
+    big = rng.standard_normal((12, 151936)).astype(np.float32)
+    big[3, 100] = big[3, 5000] = big[3].max() + 1       # tie: lowest index wins
+    bd = torch.from_numpy(big).cuda()
+    idx = torch.empty(12, dtype=torch.int32, device="cuda")
+    wsg.argmax_rows(bd, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), np.argmax(big, axis=1))
+
+
+# ---- full weight pass machinery (graph capture, replay) --------------------------
+
+def test_seq_graph_replay_matches_eager(orc):
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    shapes = [(300, 1024), (64, 2048), (1000, 1024)]
+    mats = [G.make(9, i, N, K, max_R=12) for i, (N, K) in enumerate(shapes)]
+    R = 12
+    xs_np = [synth.x_bf16(9, 100 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    xs = [G.to_dev(x) for x in xs_np]
+    ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for N, K in shapes]
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    seq = wsg.Seq([g for _, g in mats])
+    eager = [G.run(g, x) for (_, g), x in zip(mats, xs_np)]
+    for rep in range(4):
+        for y in ys:
+            y.fill_(-7.0)
+        seq.run(xs, ys, R, argmax_idx=idx)
+        torch.cuda.synchronize()
+        _ = (torch.ones(1000, device="cuda") * rep).sum().item()   # eager work between replays
+        for i, y in enumerate(ys):
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), eager[i].view(np.uint32)), (rep, i)
+        assert np.array_equal(idx.cpu().numpy(), np.argmax(eager[-1], axis=1))
+    canon_last = mats[-1][0]
+    assert_parity(eager[-1], orc.gemm(canon_last, 1000, 1024, xs_np[-1]), "seq last")
+    seq.close()
+    for _, g in mats:
+        g.close()

@@ -1,0 +1,8 @@
+"""Weight-streaming Q4_K-style GEMM for MI355X (gfx950).
+
+The C ABI is include/qgemm.h; ``qgemm`` is its ctypes binding (same names).
+``roofline`` holds the host-side bandwidth bookkeeping.
+"""
+from . import roofline  # noqa: F401
+from .qgemm import (PATH_AUTO, PATH_MFMA, PATH_VALU, MAX_R, QGemm, QGemmError, Seq,  # noqa: F401
+                    argmax_rows, pack, packed_size, status_string)

@@ -1,0 +1,81 @@
+// operand.h — per-lane decoding of the packed header and of packed quant
+// dwords into matrix-core operands.  Host and device compile the same code so
+// the operand arithmetic can be exercised on the CPU.
+//
+// For lane group g (sub-blocks 2g, 2g+1 of a block) the B operand element e of
+// step t is sc_{2g + (e & 1)} * q_k for k = operand_k(g, t, e) (layout.h): an
+// integer <= 63 * 15 = 945, exact in binary16.
+#pragma once
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <class T, class F>
+QG_HD T bitcast(F v) { return __builtin_bit_cast(T, v); }
+
+// fused multiply-add on binary16 pairs (one rounding)
+QG_HD f16x2 fma2(f16x2 a, f16x2 b, f16x2 c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_elementwise_fma(a, b, c);
+#else
+  // products and sums of binary16 values are exact in double; one rounding
+  f16x2 r;
+  r[0] = (_Float16)((double)a[0] * (double)b[0] + (double)c[0]);
+  r[1] = (_Float16)((double)a[1] * (double)b[1] + (double)c[1]);
+  return r;
+#endif
+}
+
+// per-(output, block, lane-group) constants decoded from the packed header
+struct WConst {
+  f16x2 sc;     // (sc_{2g}, sc_{2g+1})              binary16, exact
+  f16x2 sc16;   // (sc_{2g}/16, sc_{2g+1}/16)        exact
+  f16x2 b1;     // (-1024 sc_{2g}, -1024 sc_{2g+1})  exact
+  f16x2 b16;    // (-64 sc_{2g}, -64 sc_{2g+1})      exact
+  float d;      // d
+  float bm0;    // -dmin m_{2g}                        exact in fp32 (17 bits)
+  float bm1;    // -dmin m_{2g+1}
+};
+
+QG_HD WConst header_consts(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, int g) {
+  WConst c;
+  uint32_t F = header_group(h1, h2, h3, g);
+  uint32_t scpair = (F & 63u) | (((F >> 6) & 63u) << 16);
+  // binary16 with 1024 + sc (the integer sits in the mantissa), minus 1024: exact
+  f16x2 sc = bitcast<f16x2>(scpair | 0x64006400u) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
+  c.sc = sc;
+  c.sc16 = sc * f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+  c.b1 = sc * f16x2{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  c.b16 = sc * f16x2{(_Float16)-64.0f, (_Float16)-64.0f};
+  c.d = (float)bitcast<_Float16>((uint16_t)(h0 & 0xFFFFu));
+  float dmin = (float)bitcast<_Float16>((uint16_t)(h0 >> 16));
+  c.bm0 = -dmin * (float)((F >> 12) & 63u);
+  c.bm1 = -dmin * (float)((F >> 18) & 63u);
+  return c;
+}
+
+// Eight weights of one packed dword as the B operand, each equal to sc * q.
+// Nibble positions (0,4) and (2,6) become 1024 + q in the binary16 mantissa,
+// positions (1,5) and (3,7) become 1024 + 16 q; one fused multiply-add per
+// pair removes the offset: (1024 + q) sc - 1024 sc = sc q and
+// (1024 + 16 q) (sc/16) - 64 sc = sc q, both exact.
+QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
+  const uint32_t magic = 0x64006400u;
+  uint32_t w8 = w >> 8;
+  f16x2 p0 = bitcast<f16x2>((w & 0x000F000Fu) | magic);
+  f16x2 p1 = bitcast<f16x2>((w & 0x00F000F0u) | magic);
+  f16x2 p2 = bitcast<f16x2>((w8 & 0x000F000Fu) | magic);
+  f16x2 p3 = bitcast<f16x2>((w8 & 0x00F000F0u) | magic);
+  f16x2 o0 = fma2(p0, c.sc, c.b1);
+  f16x2 o1 = fma2(p1, c.sc16, c.b16);
+  f16x2 o2 = fma2(p2, c.sc, c.b1);
+  f16x2 o3 = fma2(p3, c.sc16, c.b16);
+  return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
+}
+
+}  // namespace qg

@@ -1,0 +1,176 @@
+"""Thin ctypes binding of libqgemm.so (include/qgemm.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch provides device memory (tensor.data_ptr()) and the current
+stream; nothing else from torch is used.  If the library is missing, loading
+fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemm.so")
+
+QGEMM_OK, QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN = 0, -1, -2, -3
+QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH = -4, -5, -6, -7
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+MAX_R = 64
+
+# every symbol include/qgemm.h declares
+EXPORTS = (
+    "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
+    "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_query", "qgemm_destroy",
+    "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_destroy", "qgemm_status_string",
+)
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int), ("row_tiles", ctypes.c_int),
+                ("subtiles_per_wave", ctypes.c_int), ("waves", ctypes.c_int64),
+                ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sig = {
+            "qgemm_packed_size": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+            "qgemm_pack": [vp, vp, i64, i64, vp],
+            "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
+            "qgemm_run": [vp, vp, vp, i32, vp],
+            "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
+            "qgemm_dequantize": [vp, vp, vp],
+            "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
+            "qgemm_query": [vp, i32, i32, ctypes.POINTER(Info)],
+            "qgemm_destroy": [vp],
+            "qgemm_seq_create": [ctypes.POINTER(vp), ctypes.POINTER(vp), i32],
+            "qgemm_seq_run": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp],
+            "qgemm_seq_destroy": [vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.qgemm_status_string.argtypes = [ctypes.c_int]
+        L.qgemm_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qgemm_status_string(status).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != QGEMM_OK:
+        raise QGemmError(rc, what)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream) or 0
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else (t if isinstance(t, int) else t.data_ptr())
+
+
+def packed_size(N: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().qgemm_packed_size(N, K, ctypes.byref(out)), "qgemm_packed_size")
+    return out.value
+
+
+def pack(canon_dev, packed_dev, N: int, K: int, stream=None):
+    _check(lib().qgemm_pack(_ptr(canon_dev), _ptr(packed_dev), N, K, _stream(stream)), "qgemm_pack")
+    return packed_dev
+
+
+def argmax_rows(y, idx, R: int | None = None, stream=None):
+    R = y.shape[0] if R is None else R
+    N = y.shape[1]
+    _check(lib().qgemm_argmax_rows(_ptr(y), R, N, _ptr(idx), _stream(stream)), "qgemm_argmax_rows")
+    return idx
+
+
+class QGemm:
+    """One packed weight matrix (borrowed device buffer) and its workspace."""
+
+    def __init__(self, packed_dev, N: int, K: int, max_R: int = MAX_R, flags: int = 0):
+        self.N, self.K, self.max_R = N, K, max_R
+        self._packed = packed_dev            # keep the borrowed buffer alive
+        h = ctypes.c_void_p()
+        _check(lib().qgemm_create(ctypes.byref(h), _ptr(packed_dev), N, K, max_R, flags), "qgemm_create")
+        self.h = h
+
+    def run(self, x, y, R: int | None = None, path: int = PATH_AUTO, stream=None):
+        R = x.shape[0] if R is None else R
+        _check(lib().qgemm_run_path(self.h, _ptr(x), _ptr(y), R, path, _stream(stream)), "qgemm_run")
+        return y
+
+    def dequantize(self, w, stream=None):
+        _check(lib().qgemm_dequantize(self.h, _ptr(w), _stream(stream)), "qgemm_dequantize")
+        return w
+
+    def query(self, R: int, path: int = PATH_AUTO) -> dict:
+        info = Info()
+        _check(lib().qgemm_query(self.h, R, path, ctypes.byref(info)), "qgemm_query")
+        return {f: getattr(info, f) for f, _ in Info._fields_}
+
+    def close(self):
+        if getattr(self, "h", None) is not None and self.h.value:
+            lib().qgemm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Seq:
+    """A full weight pass: handles run back to back (graph-captured per R)."""
+
+    def __init__(self, gemms):
+        self.gemms = list(gemms)
+        arr = (ctypes.c_void_p * len(self.gemms))(*[g.h.value for g in self.gemms])
+        s = ctypes.c_void_p()
+        _check(lib().qgemm_seq_create(ctypes.byref(s), arr, len(self.gemms)), "qgemm_seq_create")
+        self.s = s
+
+    def run(self, xs, ys, R: int, argmax_idx=None, stream=None):
+        n = len(self.gemms)
+        xa = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+        ya = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+        _check(lib().qgemm_seq_run(self.s, xa, ya, R, _ptr(argmax_idx), _stream(stream)), "qgemm_seq_run")
+
+    def close(self):
+        if getattr(self, "s", None) is not None and self.s.value:
+            lib().qgemm_seq_destroy(self.s)
+            self.s = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
