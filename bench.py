@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-streaming Q4_K-style GEMM on one MI355X.
+
+A step is one full decode-step weight pass: 64 transformer layers of four
+projections (Q|K|V fused, O, gate|up fused, down; hidden 5120, 64 query heads
+and 8 key/value heads of 128, MLP 25600) and a 5120 -> 151936 output head with
+its row argmax, for R stacked activation rows (4 agents x (1 token + 2 drafts)
+= 12 by default).  Weights are streamed once per step; 17,990,737,920 packed
+bytes (144 B per 256 weights).  Inputs are seeded synthetic data of those
+shapes and distributions, resident in HBM before timing.
+
+Prints one JSON line (rank 0): effective weight GB/s and ms per pass, with a
+roofline record for the dominant kernel and the fp64 CPU oracle timed on a
+bounded sample beside it.  Extra detail goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective weight GB/s and % HBM peak at R=12; ms per full 27B weight pass"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_pass(R_max: int, seed: int):
+    """Generate, upload and pack all 257 matrices; return handles and buffers."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import workloads as W
+    import weight_streaming_gemm_amd as wsg
+
+    dev = torch.device("cuda:0")
+    mats = W.full_pass()
+    max_bytes = max(m.weights // 256 * 144 for m in mats)
+    host = torch.empty(max_bytes, dtype=torch.uint8, pin_memory=True)
+    host_np = host.numpy()
+    canon_d = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
+    gemms, packed = [], []
+    t0 = time.time()
+    for i, m in enumerate(mats):
+        off = 0
+        for mid, n_part in zip(m.mids, m.splits):
+            nb = n_part * (m.K // 256) * 144
+            synth.matrix_rows(seed, mid, n_part, m.K, out=host_np[off:off + nb])
+            off += nb
+        canon_d[:off].copy_(host[:off], non_blocking=False)
+        p = torch.empty(wsg.packed_size(m.N, m.K), dtype=torch.uint8, device=dev)
+        wsg.pack(canon_d, p, m.N, m.K)
+        torch.cuda.synchronize()
+        packed.append(p)
+        gemms.append(wsg.QGemm(p, m.N, m.K, max_R=R_max))
+        if i % 64 == 0:
+            log(f"[setup] packed {i + 1}/{len(mats)} matrices, {time.time() - t0:.1f}s")
+    del canon_d, host
+    xs_by_width = {}
+    for width, sid in W.X_STREAM.items():
+        xb = synth.x_bf16(seed, sid, R_max, width)
+        xs_by_width[width] = torch.from_numpy(xb.view(np.int16)).to(dev)
+    xs = [xs_by_width[m.K] for m in mats]
+    ys = [torch.empty((R_max, m.N), dtype=torch.float32, device=dev) for m in mats]
+    idx = torch.empty(R_max, dtype=torch.int32, device=dev)
+    log(f"[setup] {len(mats)} matrices resident, {sum(p.numel() for p in packed) / 1e9:.3f} GB packed, "
+        f"{time.time() - t0:.1f}s")
+    return mats, gemms, packed, xs, ys, idx
+
+
+def time_pass(seq, xs, ys, idx, R: int, steps: int, warmup: int):
+    import torch
+    xr = [x[:R] for x in xs]
+    yr = [y[:R] for y in ys]
+    for _ in range(warmup):
+        seq.run(xr, yr, R, argmax_idx=idx)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        seq.run(xr, yr, R, argmax_idx=idx)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_dominant_kernel(gemms, xs, ys, R: int, reps: int):
+    """Average duration of the streaming kernel (qgemm_multiply enqueues exactly
+    one kernel) over back-to-back launches across all 257 matrices, timed with
+    HIP events on the stream the kernels run on (torch's current stream)."""
+    import torch
+    st = torch.cuda.current_stream()
+    for g, x in zip(gemms, xs):
+        g.stage(x[:R], R)
+    torch.cuda.synchronize()
+    for g, y in zip(gemms, ys):
+        g.multiply(y[:R], R)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        for g, y in zip(gemms, ys):
+            g.multiply(y[:R], R)
+    e1.record(st)
+    torch.cuda.synchronize()
+    launches = reps * len(gemms)
+    return e0.elapsed_time(e1) / launches, launches
+
+
+def cpu_baseline(seed: int):
+    """The fp64 oracle as it stands, on layer 0's four GEMMs at R=12 (a bounded
+    sample of the pass: one of its 64 layers), all host cores."""
+    import synth
+    import oracle
+    from synth import workloads as W
+    o = oracle.get()
+    threads = len(os.sched_getaffinity(0))
+    R = W.R_DEFAULT
+    total_bytes, total_t = 0, 0.0
+    for m in W.layer_mats(0):
+        parts = [synth.matrix_rows(seed, mid, n, m.K) for mid, n in zip(m.mids, m.splits)]
+        import numpy as np
+        canon = np.concatenate(parts)
+        x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+        t0 = time.perf_counter()
+        o.gemm(canon, m.N, m.K, x, threads=threads)
+        total_t += time.perf_counter() - t0
+        total_bytes += m.packed_bytes
+    return {"value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of the pass (Q|K|V, O, gate|up, down; {total_bytes} packed bytes) at R={R}, "
+                      f"fp64 dequantize-then-dot, {total_t:.2f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--R", type=int, default=12)
+    ap.add_argument("--sweep", default="1,3,12", help="extra row counts timed for the flatness report")
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the weight pass is not sharded across GPUs in this build "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    from weight_streaming_gemm_amd import roofline as RF
+    from synth import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
+    R_max = max(sweep)
+    mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)
+    seq = wsg.Seq(gemms)
+    pass_bytes = W.pass_bytes()
+
+    results = {}
+    for R in sweep:
+        ms, wall = time_pass(seq, xs, ys, idx, R, args.steps if R == args.R else max(5, args.steps // 2),
+                             args.warmup)
+        results[R] = ms
+        log(f"[pass] R={R:3d}: {ms:.4f} ms/pass, {pass_bytes / ms / 1e6:.1f} GB/s "
+            f"({pass_bytes / ms / 1e6 / RF.HBM_PEAK_GBS * 100:.1f}% of 8 TB/s), "
+            f"{R * 1000 / ms:.0f} rows*tok/s")
+    ms = results[args.R]
+    gbs = pass_bytes / ms / 1e6
+
+    kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=3)
+    bytes_per_launch = pass_bytes / len(gemms)
+    achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
+    info = gemms[0].query(args.R)
+    kname = f"mfma_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}>"
+    log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
+        f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.seed)
+        log(f"[cpu] oracle {cpu['value']:.4f} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4k->f16 mfma, f32 acc",
+        "data": "synthetic",
+        "config": {
+            "workload": "full decode-step weight pass: 64 layers (hidden 5120, q 8192, kv 2x1024, "
+                        "mlp 2x25600 / 25600) + lm-head 5120->151936, Q4_K-style 4.5 bit, "
+                        "257 GEMMs + row argmax",
+            "R": args.R,
+            "packed_bytes": pass_bytes,
+            "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),
+            "rows_tok_per_s": round(args.R * 1000 / ms, 1),
+            "ms_per_pass_by_R": {str(k): round(v, 5) for k, v in results.items()},
+            "flatness_t12_over_t1": round(results[12] / results[1], 4) if 1 in results and 12 in results else None,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kname,
+            "achieved": round(achieved, 1),
+            "peak": RF.HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / RF.HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(kern_ms * 1e3, 3),
+            "bytes_per_launch": round(bytes_per_launch),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    seq.close()
+    for g in gemms:
+        g.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,9 @@
  *   - Every call validates its arguments on the host before touching the GPU
  *     and returns a qgemm_status; nothing aborts.  Launch failures return
  *     QGEMM_EHIP.
- *   - Shapes: K a positive multiple of 256; N >= 1; 0 <= R <= QGEMM_MAX_R.
+ *   - Shapes: K a positive multiple of 256; N >= 1; 0 <= R <= QGEMM_MAX_R; the
+ *     packed quant region of one matrix (N rounded up to 16, times K/2 bytes)
+ *     must stay below 2 GiB (QGEMM_ESHAPE otherwise).
  *   - x is bf16 (bit patterns, R x K row-major), y is fp32 (R x N row-major,
  *     overwritten).  x enters the matrix cores as binary16: values with
  *     2^-17 <= |x| <= 65504 (and zero) are exact there; smaller magnitudes are
@@ -70,14 +72,18 @@ typedef enum {
 typedef struct qgemm_handle *qgemm_t;
 typedef struct qgemm_seq *qgemm_seq_t;
 
-/* What a run of (R, path) would launch. */
+/* What a run of (R, path) would launch.  The streaming kernel cuts the
+ * matrix into `tiles` (groups of output rows), each needing K/256 block steps,
+ * and gives each of `workgroups` workgroups an equal contiguous share of the
+ * `steps` = tiles * K/256 (tile, block) steps. */
 typedef struct {
     int path;               /* QGEMM_PATH_VALU or QGEMM_PATH_MFMA */
-    int split_k;            /* number of K splits (1 = none) */
     int row_tiles;          /* 16-row tiles on the matrix-core path (0 on the VALU path) */
     int subtiles_per_wave;  /* 16-output sub-tiles per wave */
-    int64_t waves;          /* waves in the main kernel launch */
-    int kernels;            /* kernels enqueued per run */
+    int64_t tiles;          /* output tiles */
+    int64_t workgroups;     /* workgroups of the streaming kernel */
+    int64_t steps;          /* (tile, block) steps in total */
+    int kernels;            /* kernels enqueued by qgemm_multiply */
     size_t workspace_bytes; /* bytes of the handle's workspace this run touches */
 } qgemm_info;
 
@@ -95,7 +101,8 @@ int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, vo
 
 /* Create a handle over packed weights.  The handle BORROWS packed_dev (it must
  * stay valid and unchanged until qgemm_destroy) and OWNS a device workspace
- * sized for up to max_R rows (activation operands, split-K partials).  flags
+ * sized for up to max_R rows (activation operands, split-K partials and
+ * arrival counters).  flags
  * must be 0.  Synchronous.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_ERANGE_R,
  * QGEMM_ENOMEM, QGEMM_EHIP. */
@@ -113,6 +120,17 @@ int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
  * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not
  * serve (R > 4). */
 int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, void *stream);
+
+/* The two halves of qgemm_run, for callers that time or reuse them apart.
+ * qgemm_stage converts x (device bf16 [R x K], 16-byte aligned) into the
+ * handle's operand workspace; qgemm_multiply then streams the weights once and
+ * writes y (device fp32 [R x N], 16-byte aligned) from the operands staged last
+ * on this handle (stream order; R must equal the staged R).  qgemm_multiply
+ * enqueues exactly one kernel.
+ * Errors: as qgemm_run_path; qgemm_multiply returns QGEMM_ERANGE_R when R
+ * differs from the last staged R. */
+int qgemm_stage(qgemm_t h, const void *x_bf16, int R, void *stream);
+int qgemm_multiply(qgemm_t h, float *y, int R, int path, void *stream);
 
 /* The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
  * 16-byte aligned): w_out[n, k] is the binary32 value nearest to

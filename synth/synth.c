@@ -129,14 +129,6 @@ uint16_t synth_f64_to_bf16(double v)
  *              special, the rest ordinary.                                    */
 enum { KIND_DMIN0 = 0, KIND_Q0 = 1, KIND_Q15 = 2, KIND_NORMAL = 3 };
 
-static void put_field(uint8_t *bits12, int pos, uint32_t val6)
-{
-    for (int i = 0; i < 6; i++) {
-        int b = pos + i;
-        if ((val6 >> i) & 1u) bits12[b >> 3] |= (uint8_t)(1u << (b & 7));
-    }
-}
-
 static void make_block(uint64_t kd, uint64_t kdm, uint64_t ksc, uint64_t km,
                        uint64_t kq, uint64_t ke, int edge_mode, uint64_t b,
                        uint8_t *out)
@@ -154,23 +146,22 @@ static void make_block(uint64_t kd, uint64_t kdm, uint64_t ksc, uint64_t km,
     uint16_t hdm = (kind == KIND_DMIN0) ? 0 : synth_f64_to_f16(dm);
     out[0] = (uint8_t)(hd & 0xFF); out[1] = (uint8_t)(hd >> 8);
     out[2] = (uint8_t)(hdm & 0xFF); out[3] = (uint8_t)(hdm >> 8);
-    memset(out + 4, 0, 12);
+    /* the 96-bit field stream: sc_s at bits 6s (first 48 bits), m_s at 48 + 6s */
+    uint64_t sc_bits = 0, m_bits = 0;
     for (int s = 0; s < 8; s++) {
-        uint32_t sc = (uint32_t)(draw(ksc, b * 8 + (uint64_t)s) >> 58);
-        uint32_t m = (uint32_t)(draw(km, b * 8 + (uint64_t)s) >> 58);
-        put_field(out + 4, 6 * s, sc);
-        put_field(out + 4, 48 + 6 * s, m);
+        sc_bits |= (draw(ksc, b * 8 + (uint64_t)s) >> 58) << (6 * s);
+        m_bits |= (draw(km, b * 8 + (uint64_t)s) >> 58) << (6 * s);
     }
+    uint64_t lo64 = sc_bits | (m_bits << 48);          /* stream bits 0..63 */
+    uint32_t hi32 = (uint32_t)(m_bits >> 16);          /* stream bits 64..95 */
+    for (int i = 0; i < 8; i++) out[4 + i] = (uint8_t)(lo64 >> (8 * i));
+    for (int i = 0; i < 4; i++) out[12 + i] = (uint8_t)(hi32 >> (8 * i));
     uint8_t *qs = out + 16;
     if (kind == KIND_Q0) { memset(qs, 0x00, 128); return; }
     if (kind == KIND_Q15) { memset(qs, 0xFF, 128); return; }
     for (int c = 0; c < 16; c++) {           /* 16 draws x 16 nibbles = 256 */
         uint64_t u = draw(kq, b * 16 + (uint64_t)c);
-        for (int t = 0; t < 8; t++) {
-            uint8_t lo = (uint8_t)(u >> (8 * t)) & 0xF;
-            uint8_t hi = (uint8_t)(u >> (8 * t + 4)) & 0xF;
-            qs[c * 8 + t] = (uint8_t)(lo | (hi << 4));
-        }
+        for (int t = 0; t < 8; t++) qs[c * 8 + t] = (uint8_t)(u >> (8 * t));  /* low nibble first */
     }
 }
 

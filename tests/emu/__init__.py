@@ -15,7 +15,7 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 def build(force: bool = False) -> str:
     src = os.path.join(HERE, "qgemm_emu.cpp")
     deps = [src] + [os.path.join(HERE, "..", "..", "weight_streaming_gemm_amd", "csrc", f)
-                    for f in ("layout.h", "operand.h")]
+                    for f in ("layout.h", "operand.h", "stream_sched.h")]
     if force or not os.path.exists(LIB) or any(os.path.getmtime(d) > os.path.getmtime(LIB) for d in deps):
         tmp = LIB + ".tmp"
         subprocess.check_call([CLANG, "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
@@ -34,6 +34,9 @@ def lib():
         L.emu_gemm.restype = ctypes.c_int
         L.emu_gemm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_stream.restype = ctypes.c_int
+        L.emu_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p]
         L.emu_dequant.restype = ctypes.c_int
         L.emu_dequant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.emu_pack.restype = ctypes.c_int
@@ -48,6 +51,17 @@ def gemm(canon, N, K, x_bits, NT=2, S=1):
     R = x_bits.shape[0]
     y = np.empty((R, N), dtype=np.float32)
     lib().emu_gemm(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, S, y.ctypes.data)
+    return y
+
+
+def stream(canon, N, K, x_bits, NT=2, P=8, order_seed=0):
+    canon = np.ascontiguousarray(canon, dtype=np.uint8)
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R = x_bits.shape[0]
+    y = np.empty((R, N), dtype=np.float32)
+    rc = lib().emu_stream(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, P, order_seed, y.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"emu_stream failed ({rc})")
     return y
 
 

@@ -13,6 +13,9 @@
 
 #include "../../weight_streaming_gemm_amd/csrc/layout.h"
 #include "../../weight_streaming_gemm_amd/csrc/operand.h"
+#include "../../weight_streaming_gemm_amd/csrc/stream_sched.h"
+#include <algorithm>
+#include <random>
 
 using namespace qg;
 
@@ -107,9 +110,133 @@ void xprep(const uint16_t* x, f16x8* xq, float* xs, int R, int64_t K, int RT) {
     }
 }
 
+// one block step of one 16-output sub-tile, all 64 lanes, into acc/macc[RT][64]
+void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns, int64_t j, int64_t KB, const f16x8* xq,
+               const float* xs, int RT, f32x4* acc, f32x4* macc) {
+  WConst c[64];
+  uint32_t qd[64][8];
+  for (int lane = 0; lane < 64; ++lane) {
+    const uint8_t* qp = packed + lane * 16 + quant_chunk_off(ns, j, KB);
+    memcpy(qd[lane], qp, 16);
+    memcpy(qd[lane] + 4, qp + 1024, 16);
+    uint32_t h[4];
+    memcpy(h, packed + hdr_off + (lane & 15) * 16 + header_chunk_off(ns, j, KB), 16);
+    c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
+  }
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 dsum[64];
+    for (int l = 0; l < 64; ++l) dsum[l] = f32x4{0, 0, 0, 0};
+    for (int t = 0; t < 8; ++t) {
+      f16x8 a[64], b[64];
+      for (int lane = 0; lane < 64; ++lane) {
+        a[lane] = xq[((rt * KB + j) * 8 + t) * 64 + lane];
+        b[lane] = build_b(qd[lane][t], c[lane]);
+      }
+      mfma_16x16x32(a, b, dsum);
+    }
+    float xa0[64], xa1[64], b0[64], b1[64];
+    for (int lane = 0; lane < 64; ++lane) {
+      acc[rt * 64 + lane] += c[lane].d * dsum[lane];
+      xa0[lane] = xs[((rt * KB + j) * 64 + lane) * 2];
+      xa1[lane] = xs[((rt * KB + j) * 64 + lane) * 2 + 1];
+      b0[lane] = c[lane].bm0;
+      b1[lane] = c[lane].bm1;
+    }
+    mfma_16x16x4(xa0, b0, &macc[rt * 64]);
+    mfma_16x16x4(xa1, b1, &macc[rt * 64]);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Emulated stream-K run: P workgroups of 4 waves x NT sub-tiles, executed one
+// after another in a seeded random order (the arrival order at shared tiles).
+int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int64_t P,
+               uint64_t order_seed, float* y) {
+  const int NW = 4;
+  int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
+  int RT = (R + 15) / 16;
+  int64_t T = (NS + NW * NT - 1) / (NW * NT), I = T * KB;
+  if (P > I || P < 1) return -1;
+  std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
+  pack(canon, packed.data(), N, K);
+  int64_t hdr_off = quant_region_bytes(N, K);
+  std::vector<f16x8> xq((size_t)RT * KB * 8 * 64);
+  std::vector<float> xs((size_t)RT * KB * 64 * 2);
+  xprep(x, xq.data(), xs.data(), R, K, RT);
+  const size_t slot_floats = (size_t)NW * NT * RT * 256;
+  std::vector<float> part((size_t)2 * P * slot_floats, std::nanf(""));
+  std::vector<uint32_t> cnt((size_t)T, 0);
+  std::vector<int64_t> order((size_t)P);
+  for (int64_t p = 0; p < P; ++p) order[(size_t)p] = p;
+  std::mt19937_64 rng(order_seed);
+  std::shuffle(order.begin(), order.end(), rng);
+  for (int i = 0; i < R * N; ++i) y[i] = std::nanf("");
+  for (int64_t p : order) {
+    int64_t it0 = range_first(p, P, I), it1 = range_first(p + 1, P, I);
+    std::vector<f32x4> acc((size_t)NW * NT * RT * 64), macc(acc.size());
+    auto zero = [&]() { for (auto& v : acc) v = f32x4{0, 0, 0, 0}; for (auto& v : macc) v = f32x4{0, 0, 0, 0}; };
+    zero();
+    int64_t ja = it0 % KB;
+    for (int64_t it = it0; it < it1; ++it) {
+      int64_t t = it / KB, j = it % KB;
+      for (int w = 0; w < NW; ++w)
+        for (int u = 0; u < NT; ++u) {
+          int64_t ns = (t * NW + w) * NT + u;
+          if (ns >= NS) continue;
+          size_t base = (size_t)((w * NT + u) * RT) * 64;
+          wave_step(packed.data(), hdr_off, ns, j, KB, xq.data(), xs.data(), RT, &acc[base], &macc[base]);
+        }
+      bool last = it + 1 == it1;
+      if (j != KB - 1 && !last) continue;
+      bool full = ja == 0 && j == KB - 1;
+      auto out_index = [&](int w, int u, int rt, int lane, int i, int64_t* o) {
+        int64_t n = ((t * NW + w) * NT + u) * TILE_N + (lane & 15);
+        int r = rt * 16 + 4 * (lane >> 4) + i;
+        if (n >= N || r >= R) return false;
+        *o = (int64_t)r * N + n;
+        return true;
+      };
+      if (full) {
+        for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
+          for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
+            int64_t o;
+            size_t a = (size_t)((w * NT + u) * RT + rt) * 64 + lane;
+            if (out_index(w, u, rt, lane, i, &o)) y[o] = acc[a][i] + macc[a][i];
+          }
+      } else {
+        int64_t ps = partial_slot(p, t, KB, P, I);
+        for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
+          for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
+            size_t a = (size_t)((w * NT + u) * RT + rt) * 64 + lane;
+            part[(size_t)(ps * NW + w) * NT * RT * 256 + ((u * RT + rt) * 4 + i) * 64 + lane] = acc[a][i] + macc[a][i];
+          }
+        int64_t q_lo = tile_first_owner(t, KB, P, I), q_hi = tile_last_owner(t, KB, P, I);
+        uint32_t prev = cnt[(size_t)t]++;
+        if (prev == (uint32_t)(q_hi - q_lo)) {
+          for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
+            for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
+              float v = 0.f;
+              for (int64_t q = q_lo; q <= q_hi; ++q) {
+                int64_t qs = partial_slot(q, t, KB, P, I);
+                v += part[(size_t)(qs * NW + w) * NT * RT * 256 + ((u * RT + rt) * 4 + i) * 64 + lane];
+              }
+              int64_t o;
+              if (out_index(w, u, rt, lane, i, &o)) y[o] = v;
+            }
+          cnt[(size_t)t] = 0;
+        }
+      }
+      zero();
+      ja = 0;
+    }
+  }
+  for (int64_t t = 0; t < T; ++t)
+    if (cnt[(size_t)t] != 0) return -2;   // a counter was left armed
+  return 0;
+}
 
 int emu_packed_size(int64_t N, int64_t K, int64_t* bytes) {
   *bytes = packed_bytes(N, K);

@@ -1,0 +1,111 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times (R rows, automatic kernel choice).  The oracle recomputes sampled outputs
+one by one (regenerating only the sampled weight rows); the output head's row
+argmax is checked over all 151936 outputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from synth import workloads as W
+from tests import gpu_util as G
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def fused_canon(seed, m):
+    return np.concatenate([synth.matrix_rows(seed, mid, n, m.K) for mid, n in zip(m.mids, m.splits)])
+
+
+def sampled_rows(seed, m, ns):
+    """Canonical bytes of output rows ns of a (possibly fused) matrix."""
+    out = []
+    bounds = np.cumsum((0,) + m.splits)
+    for n in ns:
+        p = int(np.searchsorted(bounds, n, side="right") - 1)
+        local = n - bounds[p]
+        out.append(synth.matrix_rows(seed, m.mids[p], m.splits[p], m.K, n0=local, n1=local + 1))
+    return np.concatenate(out)
+
+
+def sample_ns(N, count, seed):
+    rng = np.random.default_rng(seed)
+    ns = set(rng.choice(N, size=min(N, count), replace=False).tolist())
+    ns |= {0, 1, 15, 16, N - 1, N - 16}
+    return np.array(sorted(n for n in ns if 0 <= n < N))
+
+
+@pytest.mark.parametrize("R", [1, 3, 12, 24, 48])
+@pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
+def test_layer_matrix_sampled(orc, which, R):
+    seed = W.SEED_LAYER
+    m = {mm.name: mm for mm in W.layer_mats(0)}[which]
+    print(f"layer {which} N={m.N} K={m.K} R={R}", flush=True)
+    canon = fused_canon(seed, m)
+    packed = G.upload_packed(canon, m.N, m.K)
+    import weight_streaming_gemm_amd as wsg
+    g = wsg.QGemm(packed, m.N, m.K, max_R=R)
+    x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+    y = G.run(g, x)
+    ns = sample_ns(m.N, 96, R)
+    ref = orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, x)
+    assert_parity(y[:, ns], ref, f"{which} R={R} wgs={g.query(R)['workgroups']}")
+    assert np.isfinite(y).all()
+    g.close()
+
+
+def test_output_head_argmax_and_sampled_parity(orc):
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    seed, R = W.SEED_PASS, W.R_DEFAULT
+    m = W.lm_head()
+    print(f"lm_head N={m.N} K={m.K} R={R}", flush=True)
+    canon = fused_canon(seed, m)
+    packed = G.upload_packed(canon, m.N, m.K)
+    g = wsg.QGemm(packed, m.N, m.K, max_R=R)
+    x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+    xd = G.to_dev(x)
+    y = torch.empty((R, m.N), dtype=torch.float32, device="cuda")
+    g.run(xd, y)
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    wsg.argmax_rows(y, idx)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    ref = orc.gemm(canon, m.N, m.K, x)             # all 151936 outputs, fp64
+    assert_parity(yh, ref, "lm_head")
+    ref_idx = orc.argmax_rows(ref)
+    top2 = np.sort(ref, axis=1)[:, -2:]
+    margin = top2[:, 1] - top2[:, 0]
+    err = np.abs(yh - ref).max()
+    for r in range(R):
+        print(f"row {r}: argmax {ref_idx[r]} margin {margin[r]:.3e} vs max|dy| {err:.3e}", flush=True)
+        assert margin[r] > 10 * err, f"row {r} argmax ambiguous within the error bound"
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    g.close()
+
+
+def test_shared_tile_counters_rearm_over_repeats(orc):
+    """Tiles shared by several workgroups reuse their arrival counters launch after launch."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    m = {mm.name: mm for mm in W.layer_mats(0)}["down"]
+    canon = fused_canon(5, m)
+    packed = G.upload_packed(canon, m.N, m.K)
+    g = wsg.QGemm(packed, m.N, m.K, max_R=12)
+    q = g.query(12)
+    assert q["steps"] % q["workgroups"] != 0 or (q["steps"] // q["workgroups"]) % (m.K // 256) != 0   # tiles are shared
+    x = synth.x_bf16(5, 1, 12, m.K)
+    xd = G.to_dev(x)
+    ys = [torch.empty((12, m.N), dtype=torch.float32, device="cuda") for _ in range(6)]
+    g.stage(xd, 12)
+    for y in ys:
+        g.multiply(y, 12)
+    torch.cuda.synchronize()
+    first = ys[0].cpu().numpy()
+    for y in ys[1:]:
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), first.view(np.uint32))
+    ns = sample_ns(m.N, 64, 1)
+    assert_parity(first[:, ns], orc.gemm(sampled_rows(5, m, ns), len(ns), m.K, x), "down repeats")
+    g.close()

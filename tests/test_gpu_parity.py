@@ -123,7 +123,7 @@ def test_gemm_ragged_and_split(orc, N, K, R):
     info = g.query(R)
     x = synth.x_bf16(1, 6, R, K, outlier_p=0.01)
     y = G.run(g, x)
-    assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} split={info['split_k']}")
+    assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} wgs={info['workgroups']}")
     g.close()
 
 

@@ -104,10 +104,12 @@ QG_HD void pack_header(const uint8_t* sb, uint32_t out[4]) {
 }
 
 // 24-bit group field F_g from the packed header dwords h1, h2, h3
+// Group g starts at bit 24g of the 96-bit field: in dword 1 + (24g)/32 at bit
+// (24g) mod 32.  Selects without branches (g is fixed per lane).
 QG_HD uint32_t header_group(uint32_t h1, uint32_t h2, uint32_t h3, int g) {
-  uint32_t lo = (g >= 2) ? h2 : h1;
+  uint32_t lo = (g == 3) ? h3 : ((g == 2) ? h2 : h1);
   uint32_t hi = (g >= 2) ? h3 : h2;
-  uint32_t sh = (g == 0) ? 0u : (g == 1) ? 24u : (g == 2) ? 16u : 40u;
+  uint32_t sh = (uint32_t)(24 * g) & 31u;
   uint64_t v = ((uint64_t)hi << 32) | lo;
   return (uint32_t)(v >> sh) & 0xFFFFFFu;
 }

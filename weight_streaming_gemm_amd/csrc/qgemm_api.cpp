@@ -20,11 +20,14 @@ struct qgemm_handle {
   int64_t N, K, KB, NS;
   int max_R;
   int cus;
+  int occ[5][5];  // resident workgroups per CU of the streaming kernel, by [row tiles][sub-tiles]
   // workspace (owned)
   void* xq;
   void* xs;
   float* part;
-  size_t xq_bytes, xs_bytes, part_bytes;
+  uint32_t* cnt;
+  size_t xq_bytes, xs_bytes, part_bytes, cnt_bytes;
+  int staged_R;   // rows of the operands last staged (-1: none)
 };
 
 static const uint32_t HANDLE_MAGIC = 0x51474D31u;  // "QGM1"
@@ -34,81 +37,93 @@ namespace {
 
 struct Plan {
   int path;
-  int RT, NT, S;
-  int64_t kbs;
-  int64_t waves;
+  int RT, NT;
+  int64_t T, I, P;
   int kernels;
-  size_t ws_bytes;
+  size_t part_bytes, cnt_bytes, ws_bytes;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_shape(int64_t N, int64_t K) {
   if (N < 1 || K < 256 || K % 256 != 0) return false;
-  // packed bytes and N*K must fit comfortably in 64-bit arithmetic
-  if (N > (int64_t(1) << 40) / 1 || K > (int64_t(1) << 30)) return false;
-  if ((padded_n(N) / 16) * (K / 256) > (int64_t(1) << 40)) return false;
+  if (N > (int64_t(1) << 40) || K > (int64_t(1) << 30)) return false;
+  // the kernels address each region with 32-bit offsets
+  if (quant_region_bytes(N, K) >= (int64_t(1) << 31)) return false;
+  if ((K / 256) * 8192 * 4 >= (int64_t(1) << 31)) return false;
   return true;
 }
 
 bool valid_handle(const qgemm_handle* h) { return h && h->magic == HANDLE_MAGIC; }
 
-// Matrix-core plan: row tiles of 16, NT sub-tiles per wave, and a K split that
-// brings the number of waves near two per SIMD of the device (so every CU has
-// work and the tail is short), with no split smaller than one block.
-Plan plan_mfma(int64_t NS, int64_t KB, int64_t N, int R, int cus) {
+// Matrix-core plan: 16-row tiles, NT 16-output sub-tiles per wave, 4 waves per
+// workgroup, and as many workgroups as stay resident on the device (each gets
+// an equal share of the (tile, block) steps), but never fewer than two steps
+// per workgroup.
+Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5][5]) {
   Plan p{};
   p.path = QGEMM_PATH_MFMA;
   p.RT = (R + 15) / 16;
-  p.NT = (p.RT == 1) ? 2 : 1;
-  int64_t NG = (NS + p.NT - 1) / p.NT;
-  int64_t target = (int64_t)cus * 4 * 2;
-  int64_t S = (target + NG / 2) / NG;
-  if (S < 1) S = 1;
-  if (S > KB) S = KB;
-  p.kbs = (KB + S - 1) / S;
-  p.S = (int)((KB + p.kbs - 1) / p.kbs);
-  p.waves = NG * p.S;
-  p.kernels = (p.S > 1) ? 3 : 2;
-  p.ws_bytes = (size_t)p.RT * KB * 8 * 64 * 16 + (size_t)p.RT * KB * 64 * 8 +
-               (p.S > 1 ? (size_t)p.S * R * N * 4 : 0);
+  p.NT = (p.RT <= 2) ? 2 : 1;
+  p.T = (NS + 4 * p.NT - 1) / (4 * p.NT);
+  p.I = p.T * KB;
+  int64_t resident = (int64_t)cus * std::max(1, occ[p.RT][p.NT]);
+  p.P = std::max<int64_t>(1, std::min(resident, p.I / 2));
+  p.kernels = 1;
+  p.part_bytes = (size_t)(2 * p.P) * 4 * p.NT * p.RT * 256 * 4;
+  p.cnt_bytes = (size_t)p.T * 4;
+  p.ws_bytes = (size_t)p.RT * KB * 8192 + (size_t)p.RT * KB * 512 + p.part_bytes + p.cnt_bytes;
   return p;
 }
 
 int make_plan(const qgemm_handle* h, int R, int path, Plan* out) {
   if (path == QGEMM_PATH_VALU) return QGEMM_EPATH;
   if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA) return QGEMM_EINVAL;
-  *out = plan_mfma(h->NS, h->KB, h->N, R, h->cus);
+  *out = plan_stream(h->NS, h->KB, R, h->cus, h->occ);
   return QGEMM_OK;
+}
+
+int stage_impl(qgemm_handle* h, const void* x, int R, hipStream_t st) {
+  int RT = (R + 15) / 16;
+  hipError_t e = launch_xprep(reinterpret_cast<const uint16_t*>(x), h->xq, h->xs, R, h->K, RT, st);
+  if (e != hipSuccess) return QGEMM_EHIP;
+  h->staged_R = R;
+  return QGEMM_OK;
+}
+
+int multiply_impl(qgemm_handle* h, float* y, int R, int path, hipStream_t st) {
+  Plan p;
+  int rc = make_plan(h, R, path, &p);
+  if (rc) return rc;
+  StreamArgs a{};
+  a.packed = h->packed;
+  a.hdr_off = quant_region_bytes(h->N, h->K);
+  a.quant_bytes = (uint32_t)a.hdr_off;
+  a.hdr_bytes = (uint32_t)(packed_bytes(h->N, h->K) - a.hdr_off);
+  a.xq = h->xq;
+  a.xs = h->xs;
+  a.y = y;
+  a.part = h->part;
+  a.cnt = h->cnt;
+  a.N = h->N;
+  a.NS = h->NS;
+  a.KB = (int)h->KB;
+  a.R = R;
+  a.T = p.T;
+  a.I = p.I;
+  a.P = p.P;
+  a.RT = p.RT;
+  a.NT = p.NT;
+  return launch_stream(a, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
 int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStream_t st) {
   Plan p;
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
-  hipError_t e = launch_xprep(reinterpret_cast<const uint16_t*>(x), h->xq, h->xs, R, h->K, p.RT, st);
-  if (e != hipSuccess) return QGEMM_EHIP;
-  MfmaArgs a{};
-  a.packed = h->packed;
-  a.xq = h->xq;
-  a.xs = h->xs;
-  a.out = (p.S > 1) ? h->part : y;
-  a.N = h->N;
-  a.KB = h->KB;
-  a.NS = h->NS;
-  a.R = R;
-  a.S = p.S;
-  a.RT = p.RT;
-  a.NT = p.NT;
-  a.kbs = p.kbs;
-  a.hdr_off = quant_region_bytes(h->N, h->K);
-  e = launch_mfma(a, st);
-  if (e != hipSuccess) return QGEMM_EHIP;
-  if (p.S > 1) {
-    e = launch_reduce(h->part, y, (int64_t)R * h->N, p.S, st);
-    if (e != hipSuccess) return QGEMM_EHIP;
-  }
-  return QGEMM_OK;
+  rc = stage_impl(h, x, R, st);
+  if (rc) return rc;
+  return multiply_impl(h, y, R, path, st);
 }
 
 }  // namespace
@@ -167,21 +182,30 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
     return QGEMM_EHIP;
   }
   h->cus = cus;
+  for (int rt = 0; rt < 5; ++rt)
+    for (int nt = 0; nt < 5; ++nt) h->occ[rt][nt] = (rt && nt) ? stream_occupancy(rt, nt) : 0;
   int rt_max = (max_R + 15) / 16;
-  h->xq_bytes = (size_t)rt_max * h->KB * 8 * 64 * 16;
-  h->xs_bytes = (size_t)rt_max * h->KB * 64 * 8;
-  size_t part = 0;
+  h->xq_bytes = (size_t)rt_max * h->KB * 8192;
+  h->xs_bytes = (size_t)rt_max * h->KB * 512;
+  size_t part = 0, cnt = 0;
   for (int R = 1; R <= max_R; ++R) {
-    Plan p = plan_mfma(h->NS, h->KB, N, R, cus);
-    if (p.S > 1) part = std::max(part, (size_t)p.S * R * N * 4);
+    Plan p = plan_stream(h->NS, h->KB, R, cus, h->occ);
+    part = std::max(part, p.part_bytes);
+    cnt = std::max(cnt, p.cnt_bytes);
   }
   h->part_bytes = part;
-  if (hipMalloc(&h->xq, h->xq_bytes) != hipSuccess || hipMalloc(&h->xs, h->xs_bytes) != hipSuccess ||
-      (part && hipMalloc(reinterpret_cast<void**>(&h->part), part) != hipSuccess)) {
+  h->cnt_bytes = cnt;
+  h->staged_R = -1;
+  bool ok = hipMalloc(&h->xq, h->xq_bytes) == hipSuccess && hipMalloc(&h->xs, h->xs_bytes) == hipSuccess;
+  if (ok && part) ok = hipMalloc(reinterpret_cast<void**>(&h->part), part) == hipSuccess;
+  if (ok && cnt) ok = hipMalloc(reinterpret_cast<void**>(&h->cnt), cnt) == hipSuccess &&
+                      hipMemset(h->cnt, 0, cnt) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
     (void)hipGetLastError();
     if (h->xq) (void)hipFree(h->xq);
     if (h->xs) (void)hipFree(h->xs);
     if (h->part) (void)hipFree(h->part);
+    if (h->cnt) (void)hipFree(h->cnt);
     delete h;
     return QGEMM_ENOMEM;
   }
@@ -201,6 +225,26 @@ int qgemm_run_path(qgemm_t h, const void* x_bf16, float* y, int R, int path, voi
 
 int qgemm_run(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
   return qgemm_run_path(h, x_bf16, y, R, QGEMM_PATH_AUTO, stream);
+}
+
+int qgemm_stage(qgemm_t h, const void* x_bf16, int R, void* stream) {
+  if (!valid_handle(h)) return QGEMM_EINVAL;
+  if (R < 0 || R > h->max_R) return QGEMM_ERANGE_R;
+  if (R == 0) return QGEMM_OK;
+  if (!x_bf16) return QGEMM_EINVAL;
+  if (!aligned16(x_bf16)) return QGEMM_EALIGN;
+  return stage_impl(h, x_bf16, R, reinterpret_cast<hipStream_t>(stream));
+}
+
+int qgemm_multiply(qgemm_t h, float* y, int R, int path, void* stream) {
+  if (!valid_handle(h)) return QGEMM_EINVAL;
+  if (R < 0 || R > h->max_R) return QGEMM_ERANGE_R;
+  if (path < QGEMM_PATH_AUTO || path > QGEMM_PATH_MFMA) return QGEMM_EINVAL;
+  if (R == 0) return QGEMM_OK;
+  if (R != h->staged_R) return QGEMM_ERANGE_R;
+  if (!y) return QGEMM_EINVAL;
+  if (!aligned16(y)) return QGEMM_EALIGN;
+  return multiply_impl(h, y, R, path, reinterpret_cast<hipStream_t>(stream));
 }
 
 int qgemm_dequantize(qgemm_t h, float* w_out, void* stream) {
@@ -226,10 +270,11 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
   info->path = p.path;
-  info->split_k = p.S;
   info->row_tiles = p.RT;
   info->subtiles_per_wave = p.NT;
-  info->waves = p.waves;
+  info->tiles = p.T;
+  info->workgroups = p.P;
+  info->steps = p.I;
   info->kernels = p.kernels;
   info->workspace_bytes = p.ws_bytes;
   return QGEMM_OK;
@@ -242,6 +287,7 @@ int qgemm_destroy(qgemm_t h) {
   if (h->xq) (void)hipFree(h->xq);
   if (h->xs) (void)hipFree(h->xs);
   if (h->part) (void)hipFree(h->part);
+  if (h->cnt) (void)hipFree(h->cnt);
   h->magic = 0;
   delete h;
   return QGEMM_OK;

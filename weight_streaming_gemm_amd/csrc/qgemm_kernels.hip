@@ -24,6 +24,7 @@
 
 #include "layout.h"
 #include "operand.h"
+#include "stream_sched.h"
 #include "qgemm_internal.h"
 
 namespace qg {
@@ -120,112 +121,233 @@ xprep_kernel(const uint16_t* __restrict__ x, f16x8* __restrict__ xq, f32x2* __re
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core GEMM.  A wave owns NT consecutive sub-tiles (16 outputs each)
-// over the block range of one K split, and all RT row tiles (16 rows each).
-// Per block it loads x operands once (shared by its sub-tiles) and for every
-// sub-tile one 2 KiB quant chunk and the 16-byte header of its output.
+// Matrix-core streaming GEMM (stream-K over the whole matrix).
+//
+// Work: a tile is 4 waves x NT sub-tiles x 16 outputs; tile t needs KB block
+// steps.  The T*KB (tile, block) steps are cut into P equal contiguous ranges,
+// one per workgroup, so every CU gets the same number of bytes to stream
+// whatever the shape.  A range that starts or ends inside a tile leaves a
+// partial result; the last workgroup to finish a tile sums its partials in
+// workgroup order (fixed: results are deterministic) with no waiting.
+//
+// Per block step each wave reads, for each of its NT sub-tiles, one 2 KiB
+// quant chunk and its outputs' 16-byte headers (raw buffer loads, streaming
+// hint), three steps deep in a register ring; the x operands of the step are
+// shared by the four waves through a two-slot LDS ring.  Loads past the end of
+// a range address beyond the buffer's size and return zeros without memory
+// traffic, so the tail needs no branches.
+constexpr int NWAVE = 4;
+constexpr uint32_t OOB = 0x80000000u;   // beyond every buffer (sizes < 2^31)
+
+// aux 2 = streaming (non-temporal) hint for data read once; 0 for shared data
+template <class T, int AUX>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+}
+
+template <int NT>
+struct WStage {
+  u32x4 qa[NT], qb[NT], hd[NT];
+};
+
 template <int RT, int NT>
 __global__ void __launch_bounds__(256)
-mfma_kernel(const uint8_t* __restrict__ packed, const f16x8* __restrict__ xq,
-            const f32x2* __restrict__ xs, float* __restrict__ out, int64_t N, int64_t KB,
-            int64_t NS, int R, int S, int64_t kbs, int64_t hdr_off) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t NG = (NS + NT - 1) / NT;
-  const int64_t s = gw / NG;
-  if (s >= S) return;
-  const int64_t ng = gw - s * NG;
-  const int64_t ns0 = ng * NT;
-  const int64_t j0 = s * kbs;
-  const int64_t j1 = (j0 + kbs < KB) ? j0 + kbs : KB;
-  const int g = lane >> 4, nl = lane & 15;
+stream_kernel(StreamArgs a) {
+  __shared__ u32x4 xl[2][RT][8 * 64];
+  __shared__ u32x4 xsl[2][RT][32];
+  __shared__ uint32_t s_last;
 
-  const uint8_t* qbase = packed + lane * 16;
-  const uint8_t* hbase = packed + hdr_off + nl * 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, nl = lane & 15;
+  const int64_t p = blockIdx.x;
+  const int64_t I = a.I;
+  const int64_t it0 = range_first(p, a.P, I), it1 = range_first(p + 1, a.P, I);
+  const int KB = a.KB;
 
-  f32x4 acc[NT][RT], macc[NT][RT];
-  for (int u = 0; u < NT; ++u)
-    for (int rt = 0; rt < RT; ++rt) {
-      acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      macc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)a.packed, 0, (int)a.quant_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.packed + a.hdr_off), 0, (int)a.hdr_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, (int)(RT * KB * 8192), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xsr = __builtin_amdgcn_make_buffer_rsrc((void*)a.xs, 0, (int)(RT * KB * 512), 0x00020000);
 
-  bool valid[NT];
-  for (int u = 0; u < NT; ++u) valid[u] = (ns0 + u) < NS;
+  // (tile, block) of the current step and the two steps ahead
+  int64_t t_c = it0 / KB;
+  int j_c = (int)(it0 - t_c * KB);
+  const int j_first = j_c;
 
-  u32x4 qa[NT], qb[NT], hd[NT];
-  f16x8 xa[RT][8];
-  f32x2 xsv[RT];
-
-  auto load = [&](int64_t j, u32x4* qa_, u32x4* qb_, u32x4* hd_, f16x8 (*xa_)[8], f32x2* xs_) {
+  auto load_w = [&](WStage<NT>& st, int64_t it, int64_t t, int j) {
     for (int u = 0; u < NT; ++u) {
-      int64_t ns = valid[u] ? ns0 + u : ns0;
-      const uint8_t* qp = qbase + quant_chunk_off(ns, j, KB);
-      qa_[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp));
-      qb_[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + 1024));
-      hd_[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hbase + header_chunk_off(ns, j, KB)));
+      int64_t ns = (t * NWAVE + w) * NT + u;
+      bool ok = it < it1 && ns < a.NS;
+      uint32_t qo = ok ? (uint32_t)((ns * KB + j) * CHUNK_Q) + lane * 16 : OOB;
+      uint32_t ho = ok ? (uint32_t)((ns * KB + j) * CHUNK_H) + nl * 16 : OOB;
+      st.qa[u] = bload<u32x4, 2>(qr, qo);
+      st.qb[u] = bload<u32x4, 2>(qr, qo + 1024);
+      st.hd[u] = bload<u32x4, 2>(hr, ho);
     }
+  };
+  u32x4 xv[RT][2], xsv_g[RT];
+  auto load_x = [&](int64_t it, int j) {
+    bool ok = it < it1;
     for (int rt = 0; rt < RT; ++rt) {
-      const f16x8* xp = xq + ((rt * KB + j) * 8) * 64 + lane;
-      for (int t = 0; t < 8; ++t) xa_[rt][t] = xp[t * 64];
-      xs_[rt] = xs[(rt * KB + j) * 64 + lane];
+      uint32_t base = (uint32_t)((rt * KB + j) * 8192);
+      xv[rt][0] = bload<u32x4, 0>(xr, ok ? base + tid * 16 : OOB);
+      xv[rt][1] = bload<u32x4, 0>(xr, ok ? base + 4096 + tid * 16 : OOB);
+      xsv_g[rt] = bload<u32x4, 0>(xsr, (ok && tid < 32) ? (uint32_t)((rt * KB + j) * 512) + tid * 16 : OOB);
+    }
+  };
+  auto store_x = [&](int slot) {
+    for (int rt = 0; rt < RT; ++rt) {
+      xl[slot][rt][tid] = xv[rt][0];
+      xl[slot][rt][256 + tid] = xv[rt][1];
+      if (tid < 32) xsl[slot][rt][tid] = xsv_g[rt];
     }
   };
 
-  if (j0 < j1) load(j0, qa, qb, hd, xa, xsv);
-  for (int64_t j = j0; j < j1; ++j) {
-    u32x4 nqa[NT], nqb[NT], nhd[NT];
-    f16x8 nxa[RT][8];
-    f32x2 nxs[RT];
-    const bool more = (j + 1 < j1);
-    if (more) load(j + 1, nqa, nqb, nhd, nxa, nxs);
+  f32x4 acc[NT][RT], macc[NT][RT];
+  auto zero_acc = [&]() {
+    for (int u = 0; u < NT; ++u)
+      for (int rt = 0; rt < RT; ++rt) {
+        acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        macc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  };
+  zero_acc();
+
+  auto advance = [](int64_t& t, int& j, int KB_) {
+    if (++j == KB_) { j = 0; ++t; }
+  };
+
+  // prologue: x of step it0 into slot 0; weights of it0, it0+1; x of it0+1 in flight
+  int64_t t_n1 = t_c, t_n2;
+  int j_n1 = j_c, j_n2;
+  advance(t_n1, j_n1, KB);
+  t_n2 = t_n1; j_n2 = j_n1;
+  advance(t_n2, j_n2, KB);
+  load_x(it0, j_c);
+  store_x(0);
+  WStage<NT> W0, W1, W2;
+  load_w(W0, it0, t_c, j_c);
+  load_w(W1, it0 + 1, t_n1, j_n1);
+  load_x(it0 + 1, j_n1);
+  __syncthreads();
+
+  int64_t it = it0;
+  int slot = 0;
+
+  auto finish_segment = [&](int64_t t, int ja) {
+    // segment [ja, j_c] of tile t is complete
+    const bool full = (ja == 0) && (j_c == KB - 1);
+    if (full) {
+      for (int u = 0; u < NT; ++u) {
+        int64_t n = ((t * NWAVE + w) * NT + u) * TILE_N + nl;
+        if (n >= a.N) continue;
+        for (int rt = 0; rt < RT; ++rt)
+          for (int i = 0; i < 4; ++i) {
+            int r = rt * 16 + 4 * g + i;
+            if (r < a.R) a.y[(int64_t)r * a.N + n] = acc[u][rt][i] + macc[u][rt][i];
+          }
+      }
+      return;
+    }
+    const int64_t pslot = partial_slot(p, t, KB, a.P, I);
+    float* dst = a.part + (pslot * NWAVE + w) * (NT * RT * 256);
+    for (int u = 0; u < NT; ++u)
+      for (int rt = 0; rt < RT; ++rt)
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(dst + ((u * RT + rt) * 4 + i) * 64 + lane, acc[u][rt][i] + macc[u][rt][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // workgroups that hold a piece of tile t: those containing steps tKB .. tKB+KB-1
+    const int64_t q_lo = tile_first_owner(t, KB, a.P, I);
+    const int64_t q_hi = tile_last_owner(t, KB, a.P, I);
+    if (tid == 0) {
+      uint32_t prev = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (prev == (uint32_t)(q_hi - q_lo)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    f32x4 sum[NT][RT];
+    for (int u = 0; u < NT; ++u)
+      for (int rt = 0; rt < RT; ++rt) sum[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t q = q_lo; q <= q_hi; ++q) {
+      const int64_t qslot = partial_slot(q, t, KB, a.P, I);
+      const float* src = a.part + (qslot * NWAVE + w) * (NT * RT * 256);
+      for (int u = 0; u < NT; ++u)
+        for (int rt = 0; rt < RT; ++rt)
+          for (int i = 0; i < 4; ++i)
+            sum[u][rt][i] += __hip_atomic_load(src + ((u * RT + rt) * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     for (int u = 0; u < NT; ++u) {
-      WConst c = header_consts(hd[u], g);
+      int64_t n = ((t * NWAVE + w) * NT + u) * TILE_N + nl;
+      if (n >= a.N) continue;
+      for (int rt = 0; rt < RT; ++rt)
+        for (int i = 0; i < 4; ++i) {
+          int r = rt * 16 + 4 * g + i;
+          if (r < a.R) a.y[(int64_t)r * a.N + n] = sum[u][rt][i];
+        }
+    }
+    if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  auto compute = [&](const WStage<NT>& st) {
+    f16x8 xa[RT][8];
+    f32x2 xs2[RT];
+    for (int rt = 0; rt < RT; ++rt) {
+      for (int t = 0; t < 8; ++t) xa[rt][t] = __builtin_bit_cast(f16x8, xl[slot][rt][t * 64 + lane]);
+      xs2[rt] = reinterpret_cast<const f32x2*>(&xsl[slot][rt][0])[lane];
+    }
+    for (int u = 0; u < NT; ++u) {
+      WConst c = header_consts(st.hd[u], g);
       f32x4 dsum[RT];
       for (int rt = 0; rt < RT; ++rt) dsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int t = 0; t < 8; ++t) {
-        uint32_t w = (t < 4) ? qa[u][t] : qb[u][t - 4];
-        f16x8 b = build_b(w, c);
+        uint32_t wd = (t < 4) ? st.qa[u][t] : st.qb[u][t - 4];
+        f16x8 b = build_b(wd, c);
         for (int rt = 0; rt < RT; ++rt)
           dsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt][t], b, dsum[rt], 0, 0, 0);
       }
       for (int rt = 0; rt < RT; ++rt) {
         acc[u][rt] += c.d * dsum[rt];
-        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsv[rt][0], c.bm0, macc[u][rt], 0, 0, 0);
-        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsv[rt][1], c.bm1, macc[u][rt], 0, 0, 0);
+        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs2[rt][0], c.bm0, macc[u][rt], 0, 0, 0);
+        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs2[rt][1], c.bm1, macc[u][rt], 0, 0, 0);
       }
     }
-    if (more) {
-      for (int u = 0; u < NT; ++u) { qa[u] = nqa[u]; qb[u] = nqb[u]; hd[u] = nhd[u]; }
-      for (int rt = 0; rt < RT; ++rt) {
-        for (int t = 0; t < 8; ++t) xa[rt][t] = nxa[rt][t];
-        xsv[rt] = nxs[rt];
-      }
+  };
+
+  int ja = j_first;   // first block of the current segment
+  // one step: prefetch weights two steps ahead into `ahead`, compute `cur`,
+  // stage the next step's x into the other LDS slot, then close the segment if
+  // the step ends a tile or the range
+  auto step = [&](WStage<NT>& cur, WStage<NT>& ahead) -> bool {
+    load_w(ahead, it + 2, t_n2, j_n2);
+    compute(cur);
+    store_x(slot ^ 1);
+    int64_t t_n3 = t_n2;
+    int j_n3 = j_n2;
+    advance(t_n3, j_n3, KB);
+    load_x(it + 2, j_n2);
+    __syncthreads();
+    const bool last = (it + 1 == it1);
+    if (j_c == KB - 1 || last) {
+      finish_segment(t_c, ja);
+      zero_acc();
+      ja = 0;
     }
-  }
+    ++it;
+    slot ^= 1;
+    t_c = t_n1; j_c = j_n1;
+    t_n1 = t_n2; j_n1 = j_n2;
+    t_n2 = t_n3; j_n2 = j_n3;
+    return !last;
+  };
 
-  // lane (g, nl) holds rows 16 rt + 4 g + i, output 16 ns + nl
-  float* dst = out + s * (int64_t)R * N;
-  for (int u = 0; u < NT; ++u) {
-    if (!valid[u]) continue;
-    int64_t n = (ns0 + u) * TILE_N + nl;
-    if (n >= N) continue;
-    for (int rt = 0; rt < RT; ++rt)
-      for (int i = 0; i < 4; ++i) {
-        int r = rt * 16 + 4 * g + i;
-        if (r < R) dst[(int64_t)r * N + n] = acc[u][rt][i] + macc[u][rt][i];
-      }
+  while (it < it1) {
+    if (!step(W0, W2)) break;
+    if (!step(W1, W0)) break;
+    if (!step(W2, W1)) break;
   }
-}
-
-// y[r, n] = sum over splits s = 0, 1, ..., S-1 of part[s, r, n] (fixed order)
-__global__ void __launch_bounds__(256)
-splitk_reduce_kernel(const float* __restrict__ part, float* __restrict__ y, int64_t RN, int S) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= RN) return;
-  float v = part[i];
-  for (int s = 1; s < S; ++s) v += part[(int64_t)s * RN + i];
-  y[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -316,34 +438,31 @@ hipError_t launch_xprep(const uint16_t* x, void* xq, void* xs, int R, int64_t K,
 }
 
 template <int RT, int NT>
-static hipError_t launch_mfma_t(const MfmaArgs& a, hipStream_t st) {
-  int64_t NG = (a.NS + NT - 1) / NT;
-  int64_t waves = NG * a.S;
-  hipLaunchKernelGGL((mfma_kernel<RT, NT>), dim3(blocks_for(waves, 4)), dim3(256), 0, st, a.packed,
-                     reinterpret_cast<const f16x8*>(a.xq), reinterpret_cast<const f32x2*>(a.xs), a.out,
-                     a.N, a.KB, a.NS, a.R, a.S, a.kbs, a.hdr_off);
+static hipError_t launch_stream_t(const StreamArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((stream_kernel<RT, NT>), dim3((unsigned)a.P), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_mfma(const MfmaArgs& a, hipStream_t st) {
-  switch (a.RT * 16 + a.NT) {
-    case 1 * 16 + 1: return launch_mfma_t<1, 1>(a, st);
-    case 1 * 16 + 2: return launch_mfma_t<1, 2>(a, st);
-    case 1 * 16 + 4: return launch_mfma_t<1, 4>(a, st);
-    case 2 * 16 + 1: return launch_mfma_t<2, 1>(a, st);
-    case 2 * 16 + 2: return launch_mfma_t<2, 2>(a, st);
-    case 3 * 16 + 1: return launch_mfma_t<3, 1>(a, st);
-    case 3 * 16 + 2: return launch_mfma_t<3, 2>(a, st);
-    case 4 * 16 + 1: return launch_mfma_t<4, 1>(a, st);
-    case 4 * 16 + 2: return launch_mfma_t<4, 2>(a, st);
-    default: return hipErrorInvalidValue;
+#define QG_STREAM_VARIANTS(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(3, 1) X(4, 1)
+
+hipError_t launch_stream(const StreamArgs& a, hipStream_t st) {
+#define QG_CASE(rt, nt) \
+  if (a.RT == rt && a.NT == nt) return launch_stream_t<rt, nt>(a, st);
+  QG_STREAM_VARIANTS(QG_CASE)
+#undef QG_CASE
+  return hipErrorInvalidValue;
+}
+
+int stream_occupancy(int RT, int NT) {
+  int blocks = 0;
+#define QG_CASE(rt, nt) \
+  if (RT == rt && NT == nt) { \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt>, 256, 0) != hipSuccess) return 0; \
+    return blocks; \
   }
-}
-
-hipError_t launch_reduce(const float* part, float* y, int64_t RN, int S, hipStream_t st) {
-  if (RN == 0) return hipSuccess;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks_for(RN, 256)), dim3(256), 0, st, part, y, RN, S);
-  return hipGetLastError();
+  QG_STREAM_VARIANTS(QG_CASE)
+#undef QG_CASE
+  return 0;
 }
 
 hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K, hipStream_t st) {

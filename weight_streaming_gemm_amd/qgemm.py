@@ -21,6 +21,7 @@ MAX_R = 64
 # every symbol include/qgemm.h declares
 EXPORTS = (
     "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
+    "qgemm_stage", "qgemm_multiply",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_query", "qgemm_destroy",
     "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_destroy", "qgemm_status_string",
 )
@@ -33,8 +34,8 @@ class QGemmError(RuntimeError):
 
 
 class Info(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int), ("split_k", ctypes.c_int), ("row_tiles", ctypes.c_int),
-                ("subtiles_per_wave", ctypes.c_int), ("waves", ctypes.c_int64),
+    _fields_ = [("path", ctypes.c_int), ("row_tiles", ctypes.c_int), ("subtiles_per_wave", ctypes.c_int),
+                ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("steps", ctypes.c_int64),
                 ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -56,6 +57,8 @@ def lib():
             "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
             "qgemm_run": [vp, vp, vp, i32, vp],
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
+            "qgemm_stage": [vp, vp, i32, vp],
+            "qgemm_multiply": [vp, vp, i32, i32, vp],
             "qgemm_dequantize": [vp, vp, vp],
             "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
             "qgemm_query": [vp, i32, i32, ctypes.POINTER(Info)],
@@ -125,6 +128,14 @@ class QGemm:
     def run(self, x, y, R: int | None = None, path: int = PATH_AUTO, stream=None):
         R = x.shape[0] if R is None else R
         _check(lib().qgemm_run_path(self.h, _ptr(x), _ptr(y), R, path, _stream(stream)), "qgemm_run")
+        return y
+
+    def stage(self, x, R: int | None = None, stream=None):
+        R = x.shape[0] if R is None else R
+        _check(lib().qgemm_stage(self.h, _ptr(x), R, _stream(stream)), "qgemm_stage")
+
+    def multiply(self, y, R: int, path: int = PATH_AUTO, stream=None):
+        _check(lib().qgemm_multiply(self.h, _ptr(y), R, path, _stream(stream)), "qgemm_multiply")
         return y
 
     def dequantize(self, w, stream=None):
