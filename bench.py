@@ -116,6 +116,34 @@ def time_dominant_kernel(gemms, xs, ys, R: int, reps: int):
     return e0.elapsed_time(e1) / launches, launches
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP library's sources: identifies the kernel a counter run measured."""
+    import hashlib
+    csrc = os.path.join(ROOT, "weight_streaming_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(R: int):
+    """HBM bytes per launch of the streaming kernel from the committed counter summary
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE runs, scaled by a copy kernel of known
+    size), or None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest() or rec.get("R") != R:
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(seed: int):
     """The fp64 oracle as it stands, on layer 0's four GEMMs at R=12 (a bounded
     sample of the pass: one of its 64 layers), all host cores."""
@@ -149,6 +177,12 @@ def main():
     ap.add_argument("--sweep", default="1,3,12", help="extra row counts timed for the flatness report")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="skip the graph-replayed pass: only the back-to-back streaming-kernel launches (and "
+                         "the copy calibration), for hardware-counter runs")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of MIB MiB three times: a kernel of known "
+                         "traffic for scaling the HBM byte counters of a profiler run")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -167,7 +201,22 @@ def main():
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)
     seq = wsg.Seq(gemms)
     pass_bytes = W.pass_bytes()
+    if args.copy_calibration > 0:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[calib] copied {nb} bytes three times")
+        del src, dst
 
+    if args.kernel_only:
+        kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=1)
+        log(f"[kernel] {launches} launches, {kern_ms * 1e3:.2f} us average")
+        print(json.dumps({"kernel_only": True, "R": args.R, "avg_launch_us": round(kern_ms * 1e3, 3),
+                          "bytes_per_launch": round(pass_bytes / len(gemms))}), flush=True)
+        return
     results = {}
     for R in sweep:
         ms, wall = time_pass(seq, xs, ys, idx, R, args.steps if R == args.R else max(5, args.steps // 2),
@@ -223,7 +272,7 @@ def main():
             "peak": RF.HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / RF.HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.R),
             "avg_launch_us": round(kern_ms * 1e3, 3),
             "bytes_per_launch": round(bytes_per_launch),
         },
