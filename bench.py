@@ -94,22 +94,19 @@ def time_pass(seq, xs, ys, idx, R: int, steps: int, warmup: int):
 
 
 def time_dominant_kernel(gemms, xs, ys, R: int, reps: int):
-    """Average duration of the streaming kernel (qgemm_multiply enqueues exactly
-    one kernel) over back-to-back launches across all 257 matrices, timed with
-    HIP events on the stream the kernels run on (torch's current stream)."""
+    """Average duration of the streaming kernel (qgemm_run enqueues exactly one
+    kernel) over back-to-back launches across all 257 matrices, timed with HIP
+    events on the stream the kernels run on (torch's current stream)."""
     import torch
     st = torch.cuda.current_stream()
-    for g, x in zip(gemms, xs):
-        g.stage(x[:R], R)
-    torch.cuda.synchronize()
-    for g, y in zip(gemms, ys):
-        g.multiply(y[:R], R)
+    for g, x, y in zip(gemms, xs, ys):
+        g.run(x[:R], y[:R])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(reps):
-        for g, y in zip(gemms, ys):
-            g.multiply(y[:R], R)
+        for g, x, y in zip(gemms, xs, ys):
+            g.run(x[:R], y[:R])
     e1.record(st)
     torch.cuda.synchronize()
     launches = reps * len(gemms)
@@ -177,6 +174,8 @@ def main():
     ap.add_argument("--sweep", default="1,3,12", help="extra row counts timed for the flatness report")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--persistent", action="store_true",
+                    help="run the pass as one cooperative launch instead of a graph of one launch per GEMM")
     ap.add_argument("--kernel-only", action="store_true",
                     help="skip the graph-replayed pass: only the back-to-back streaming-kernel launches (and "
                          "the copy calibration), for hardware-counter runs")
@@ -199,7 +198,7 @@ def main():
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
     R_max = max(sweep)
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)
-    seq = wsg.Seq(gemms)
+    seq = wsg.Seq(gemms, persistent=args.persistent)
     pass_bytes = W.pass_bytes()
     if args.copy_calibration > 0:
         nb = args.copy_calibration << 20
@@ -232,7 +231,7 @@ def main():
     bytes_per_launch = pass_bytes / len(gemms)
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
     info = gemms[0].query(args.R)
-    kname = f"mfma_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}>"
+    kname = f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}>"
     log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
         f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
 
@@ -259,6 +258,7 @@ def main():
                         "mlp 2x25600 / 25600) + lm-head 5120->151936, Q4_K-style 4.5 bit, "
                         "257 GEMMs + row argmax",
             "R": args.R,
+            "pass_launch": "persistent" if args.persistent else "graph",
             "packed_bytes": pass_bytes,
             "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),
             "rows_tok_per_s": round(args.R * 1000 / ms, 1),

@@ -73,9 +73,9 @@ typedef struct qgemm_handle *qgemm_t;
 typedef struct qgemm_seq *qgemm_seq_t;
 
 /* What a run of (R, path) would launch.  The streaming kernel cuts the
- * matrix into `tiles` (groups of output rows), each needing K/256 block steps,
- * and gives each of `workgroups` workgroups an equal contiguous share of the
- * `steps` = tiles * K/256 (tile, block) steps. */
+ * matrix into `tiles` (groups of outputs), each needing K/256 block steps, cuts
+ * the `steps` = tiles * K/256 (tile, block) steps into `ranges` equal
+ * contiguous ranges and deals them round-robin to `workgroups` workgroups. */
 typedef struct {
     int path;               /* QGEMM_PATH_VALU or QGEMM_PATH_MFMA */
     int row_tiles;          /* 16-row tiles on the matrix-core path (0 on the VALU path) */
@@ -83,8 +83,12 @@ typedef struct {
     int64_t tiles;          /* output tiles */
     int64_t workgroups;     /* workgroups of the streaming kernel */
     int64_t steps;          /* (tile, block) steps in total */
-    int kernels;            /* kernels enqueued by qgemm_multiply */
-    size_t workspace_bytes; /* bytes of the handle's workspace this run touches */
+    int kernels;            /* kernels enqueued by qgemm_run */
+    size_t workspace_bytes; /* bytes of the handle's workspace this run may touch */
+    int64_t ranges;         /* step ranges */
+    int waves_per_workgroup;
+    int wave_columns;       /* waves of a workgroup side by side along N; the others
+                               split each step range along K */
 } qgemm_info;
 
 /* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights
@@ -101,8 +105,8 @@ int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, vo
 
 /* Create a handle over packed weights.  The handle BORROWS packed_dev (it must
  * stay valid and unchanged until qgemm_destroy) and OWNS a device workspace
- * sized for up to max_R rows (activation operands, split-K partials and
- * arrival counters).  flags
+ * sized for up to max_R rows (partial output tiles and per-tile arrival
+ * counters).  flags
  * must be 0.  Synchronous.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_ERANGE_R,
  * QGEMM_ENOMEM, QGEMM_EHIP. */
@@ -111,8 +115,9 @@ int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int
 
 /* y = x . W^T for R rows on `stream`, with the R-dependent kernel choice.
  * x: device bf16 [R x K], y: device fp32 [R x N], both 16-byte aligned.
- * R = 0 is a no-op.  Runs of one handle share its workspace: do not run one
- * handle on two streams at once.
+ * Enqueues exactly one kernel, which reads every packed weight byte once,
+ * converts x itself and writes y.  R = 0 is a no-op.  Runs of one handle share
+ * its workspace: do not run one handle on two streams at once.
  * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_EHIP. */
 int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
 
@@ -120,17 +125,6 @@ int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
  * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not
  * serve (R > 4). */
 int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, void *stream);
-
-/* The two halves of qgemm_run, for callers that time or reuse them apart.
- * qgemm_stage converts x (device bf16 [R x K], 16-byte aligned) into the
- * handle's operand workspace; qgemm_multiply then streams the weights once and
- * writes y (device fp32 [R x N], 16-byte aligned) from the operands staged last
- * on this handle (stream order; R must equal the staged R).  qgemm_multiply
- * enqueues exactly one kernel.
- * Errors: as qgemm_run_path; qgemm_multiply returns QGEMM_ERANGE_R when R
- * differs from the last staged R. */
-int qgemm_stage(qgemm_t h, const void *x_bf16, int R, void *stream);
-int qgemm_multiply(qgemm_t h, float *y, int R, int path, void *stream);
 
 /* The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
  * 16-byte aligned): w_out[n, k] is the binary32 value nearest to
@@ -157,19 +151,39 @@ int qgemm_destroy(qgemm_t h);
  * A sequence of handles run back to back in the given (dependency) order, as
  * one decode step's weight pass: layer after layer of projections and then the
  * output head, each weight byte read once.  The sequence BORROWS the handles.
- * count >= 1.  Errors: QGEMM_EINVAL, QGEMM_ENOMEM. */
-int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count);
+ * count >= 1.  flags selects how a run is launched:
+ *   0                     one streaming-kernel launch per GEMM (exactly as
+ *                         qgemm_run), captured into a HIP graph on the first
+ *                         run for a given (R, pointer set) and replayed after;
+ *   QGEMM_SEQ_PERSISTENT  one cooperative launch for all GEMMs (below).
+ * Errors: QGEMM_EINVAL (also for unknown flags), QGEMM_ENOMEM, QGEMM_ESHAPE,
+ * QGEMM_EHIP. */
+#define QGEMM_SEQ_PERSISTENT 1u
+int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32_t flags);
 
 /* Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]
- * (arrays of `count` device pointers, shapes as for qgemm_run).  If argmax_idx
- * is not NULL, the row argmax of the LAST GEMM's output is written to it
- * (device int32 [R]).  The first run for a given (R, pointer set) captures the
- * launches into a HIP graph; later identical runs replay it.
- * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays. */
+ * (arrays of `count` device pointers, shapes as for qgemm_run); GEMM i + 1
+ * starts after GEMM i has finished, as when each projection's input depends on
+ * the previous output.  If argmax_idx is not NULL, the row argmax of the LAST
+ * GEMM's output is written to it (device int32 [R]) by one more kernel.
+ * With QGEMM_SEQ_PERSISTENT, one cooperative launch runs all GEMMs: every
+ * workgroup is resident, waits at a device-wide barrier between GEMMs and
+ * already streams the next GEMM's weights while it waits; the first run for a
+ * given (R, pointer set) uploads a descriptor table (synchronous).  Do not
+ * capture a persistent run into a graph (cooperative launch).  Runs of one
+ * sequence share workspace: one stream at a time.
+ * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays, QGEMM_ENOMEM. */
 int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
                   int32_t *argmax_idx, void *stream);
 
-/* Free the sequence and its captured graphs (not the handles).  NULL is a no-op. */
+/* Waits for the device, then stores in *timeouts how many barrier waits of the
+ * sequence's launches since the previous call gave up (a bounded wait: a
+ * workgroup that waits about a second for the others proceeds and flags it;
+ * results of such a launch are not reliable).  Resets the count.
+ * Errors: QGEMM_EINVAL, QGEMM_EHIP. */
+int qgemm_seq_errors(qgemm_seq_t s, uint32_t *timeouts);
+
+/* Free the sequence and its workspace (not the handles).  NULL is a no-op. */
 int qgemm_seq_destroy(qgemm_seq_t s);
 
 /* Static text for a status code. */

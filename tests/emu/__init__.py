@@ -31,12 +31,14 @@ def lib():
     global _lib
     if _lib is None:
         L = ctypes.CDLL(build())
-        L.emu_gemm.restype = ctypes.c_int
-        L.emu_gemm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_stream_seq.restype = ctypes.c_int
+        L.emu_stream_seq.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64]
         L.emu_stream.restype = ctypes.c_int
         L.emu_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                                 ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_uint64, ctypes.c_void_p]
         L.emu_dequant.restype = ctypes.c_int
         L.emu_dequant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.emu_pack.restype = ctypes.c_int
@@ -45,24 +47,38 @@ def lib():
     return _lib
 
 
-def gemm(canon, N, K, x_bits, NT=2, S=1):
+def stream(canon, N, K, x_bits, NT=2, NW=4, V=8, order_seed=0, nwn=1):
+    """One GEMM through the emulated streaming kernel (NW waves in an nwn x NW/nwn
+    grid, NT sub-tiles per wave, V ranges)."""
     canon = np.ascontiguousarray(canon, dtype=np.uint8)
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     R = x_bits.shape[0]
     y = np.empty((R, N), dtype=np.float32)
-    lib().emu_gemm(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, S, y.ctypes.data)
-    return y
-
-
-def stream(canon, N, K, x_bits, NT=2, P=8, order_seed=0):
-    canon = np.ascontiguousarray(canon, dtype=np.uint8)
-    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
-    R = x_bits.shape[0]
-    y = np.empty((R, N), dtype=np.float32)
-    rc = lib().emu_stream(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, P, order_seed, y.ctypes.data)
+    rc = lib().emu_stream(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, NW, nwn, V, order_seed,
+                             y.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"emu_stream failed ({rc})")
     return y
+
+
+def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None):
+    """Several GEMMs in one emulated launch; mats = [(canon, N, K)], xs = [bf16 bits (R x K)]."""
+    G = len(mats)
+    canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
+    xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
+    R = xs[0].shape[0]
+    ys = [np.empty((R, N), dtype=np.float32) for _, N, _ in mats]
+    P_ = ctypes.c_void_p * G
+    Ns = np.array([N for _, N, _ in mats], dtype=np.int64)
+    Ks = np.array([K for _, _, K in mats], dtype=np.int64)
+    Vs = np.array(Vs if Vs is not None else [8] * G, dtype=np.int64)
+    nwns = np.array(nwns if nwns is not None else [1] * G, dtype=np.int32)
+    rc = lib().emu_stream_seq(G, P_(*[c.ctypes.data for c in canons]), Ns.ctypes.data, Ks.ctypes.data,
+                              P_(*[x.ctypes.data for x in xs]), P_(*[y.ctypes.data for y in ys]), R, NT, NW,
+                              nwns.ctypes.data, Vs.ctypes.data, order_seed)
+    if rc != 0:
+        raise RuntimeError(f"emu_stream_seq failed ({rc})")
+    return ys
 
 
 def dequant(canon, N, K):

@@ -1,10 +1,12 @@
 // qgemm_emu.cpp — CPU emulation of the gfx950 kernels' data flow, lane by lane.
 //
-// Test infrastructure: it compiles the library's own layout.h / operand.h
-// (the code the kernels run) for the host and replays the pack, activation
-// staging, matrix-core GEMM (with the documented lane layouts of
-// v_mfma_f32_16x16x32_f16 and v_mfma_f32_16x16x4_f32), split-K reduction and
-// dequantisation kernels thread by thread.  It lets the CPU suite check every
+// Test infrastructure: it compiles the library's own layout.h / operand.h /
+// stream_sched.h (the code the kernels run) for the host and replays the pack,
+// the streaming kernel (activation staging into the operand layout, the
+// matrix-core steps with the documented lane layout of
+// v_mfma_f32_16x16x32_f16, the stream-K schedule with partial tiles and
+// last-arriver sums, several GEMMs sharing one workspace) and the
+// dequantisation kernel thread by thread.  It lets the CPU suite check every
 // index mapping against the fp64 oracle before any GPU run.  The matrix-core
 // lane layout assumed here is itself checked on the GPU by a probe test.
 #include <stdint.h>
@@ -15,6 +17,7 @@
 #include "../../weight_streaming_gemm_amd/csrc/operand.h"
 #include "../../weight_streaming_gemm_amd/csrc/stream_sched.h"
 #include <algorithm>
+#include <cmath>
 #include <random>
 
 using namespace qg;
@@ -44,19 +47,6 @@ void mfma_16x16x32(const f16x8* a, const f16x8* b, f32x4* c) {
   for (int l = 0; l < 64; ++l) c[l] = out[l];
 }
 
-// K = 4 fp32 variant: a[l] = A[l % 16][l / 16], b[l] = B[l / 16][l % 16]
-void mfma_16x16x4(const float* a, const float* b, f32x4* c) {
-  f32x4 out[64];
-  for (int l = 0; l < 64; ++l)
-    for (int v = 0; v < 4; ++v) {
-      int i = 4 * (l / 16) + v, j = l % 16;
-      double s = c[l][v];
-      for (int k = 0; k < 4; ++k) s += (double)a[i + 16 * k] * (double)b[j + 16 * k];
-      out[l][v] = (float)s;
-    }
-  for (int l = 0; l < 64; ++l) c[l] = out[l];
-}
-
 void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
   int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
   for (int64_t ns = 0; ns < NS; ++ns)
@@ -81,243 +71,235 @@ void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
       }
 }
 
-float bf16f(uint16_t b) {
-  uint32_t u = (uint32_t)b << 16;
-  float f;
-  memcpy(&f, &u, 4);
-  return f;
+int64_t x_slot_of_emu(int64_t j, int64_t j0, int64_t KB) { return (j - j0 + KB) % KB; }
+
+// Activation staging of one range: the kernel's convert_x, slot b <- block
+// (j0 + b) mod KB for b < nslots; slot layout [b][t][gg][r < R] of 16-byte A
+// operands (R rows stored), rows >= R read as zeros.
+void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, std::vector<f16x8>& slots) {
+  const int64_t KB = K / SB_W;
+  slots.assign((size_t)nslots * 8 * 4 * R, f16x8{});
+  for (int64_t b = 0; b < nslots; ++b)
+    for (int r = 0; r < R; ++r)
+      for (int gg = 0; gg < 4; ++gg)
+        for (int t = 0; t < 8; ++t) {
+          int64_t j = j0 + b;
+          if (j >= KB) j -= KB;
+          const uint16_t* lo = x + (int64_t)r * K + j * SB_W + 64 * gg + 4 * t;
+          const uint32_t d0 = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+          const uint32_t d1 = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+          const uint32_t d2 = (uint32_t)lo[32] | ((uint32_t)lo[33] << 16);
+          const uint32_t d3 = (uint32_t)lo[34] | ((uint32_t)lo[35] << 16);
+          slots[(size_t)((b * 8 + t) * 4 + gg) * R + r] = build_a(d0, d1, d2, d3);
+        }
 }
 
-void xprep(const uint16_t* x, f16x8* xq, float* xs, int R, int64_t K, int RT) {
-  int64_t KB = K / SB_W;
-  for (int64_t rj = 0; rj < RT * KB; ++rj)
-    for (int lane = 0; lane < 64; ++lane) {
-      int rt = (int)(rj / KB);
-      int64_t j = rj % KB;
-      int g = lane >> 4, r = rt * 16 + (lane & 15);
-      float vals[64];
-      for (int c = 0; c < 64; ++c) vals[c] = (r < R) ? bf16f(x[(int64_t)r * K + j * SB_W + 64 * g + c]) : 0.f;
-      for (int t = 0; t < 8; ++t) {
-        f16x8 o;
-        for (int e = 0; e < 8; ++e) o[e] = (_Float16)vals[32 * (e & 1) + 4 * t + (e >> 1)];
-        xq[(rj * 8 + t) * 64 + lane] = o;
-      }
-      float s0 = 0.f, s1 = 0.f;
-      for (int c = 0; c < 32; ++c) s0 += vals[c];
-      for (int c = 0; c < 32; ++c) s1 += vals[32 + c];
-      xs[(rj * 64 + lane) * 2] = s0;
-      xs[(rj * 64 + lane) * 2 + 1] = s1;
-    }
+// the A operand of lane (row tile rt, lane) at step t from slot b
+f16x8 a_operand(const std::vector<f16x8>& slots, int R, int64_t b, int rt, int t, int lane) {
+  const int r = rt * 16 + (lane & 15), gg = lane >> 4;
+  if (r >= R) return f16x8{};
+  return slots[(size_t)((b * 8 + t) * 4 + gg) * R + r];
 }
 
-// one block step of one 16-output sub-tile, all 64 lanes, into acc/macc[RT][64]
-void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns, int64_t j, int64_t KB, const f16x8* xq,
-               const float* xs, int RT, f32x4* acc, f32x4* macc) {
-  WConst c[64];
-  uint32_t qd[64][8];
-  for (int lane = 0; lane < 64; ++lane) {
-    const uint8_t* qp = packed + lane * 16 + quant_chunk_off(ns, j, KB);
-    memcpy(qd[lane], qp, 16);
-    memcpy(qd[lane] + 4, qp + 1024, 16);
-    uint32_t h[4];
-    memcpy(h, packed + hdr_off + (lane & 15) * 16 + header_chunk_off(ns, j, KB), 16);
-    c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
-  }
-  for (int rt = 0; rt < RT; ++rt) {
-    f32x4 dsum[64];
-    for (int l = 0; l < 64; ++l) dsum[l] = f32x4{0, 0, 0, 0};
-    for (int t = 0; t < 8; ++t) {
-      f16x8 a[64], b[64];
-      for (int lane = 0; lane < 64; ++lane) {
-        a[lane] = xq[((rt * KB + j) * 8 + t) * 64 + lane];
-        b[lane] = build_b(qd[lane][t], c[lane]);
-      }
-      mfma_16x16x32(a, b, dsum);
-    }
-    float xa0[64], xa1[64], b0[64], b1[64];
+// One step of a wave at sub-tiles ns0 .. ns0 + NT - 1, block j (activation
+// slot b): the kernel's compute() for its NT sub-tiles and all 64 lanes,
+// accumulating into acc[NT][RT][64].
+void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int64_t NS, int64_t j, int64_t KB,
+               const std::vector<f16x8>& slots, int R, int64_t b, int RT, f32x4* acc) {
+  for (int u = 0; u < NT; ++u) {
+    const int64_t ns = ns0 + u;
+    WConst c[64];
+    f16x8 bm[64];
+    uint32_t qd[64][8];
     for (int lane = 0; lane < 64; ++lane) {
-      acc[rt * 64 + lane] += c[lane].d * dsum[lane];
-      xa0[lane] = xs[((rt * KB + j) * 64 + lane) * 2];
-      xa1[lane] = xs[((rt * KB + j) * 64 + lane) * 2 + 1];
-      b0[lane] = c[lane].bm0;
-      b1[lane] = c[lane].bm1;
+      uint32_t h[4] = {0, 0, 0, 0};
+      if (ns < NS) {
+        const uint8_t* qp = packed + lane * 16 + quant_chunk_off(ns, j, KB);
+        memcpy(qd[lane], qp, 16);
+        memcpy(qd[lane] + 4, qp + 1024, 16);
+        memcpy(h, packed + hdr_off + (lane & 15) * 16 + header_chunk_off(ns, j, KB), 16);
+      } else {
+        memset(qd[lane], 0, sizeof(qd[lane]));   // loads past the end return zeros
+      }
+      c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
+      bm[lane] = build_m(c[lane]);
     }
-    mfma_16x16x4(xa0, b0, &macc[rt * 64]);
-    mfma_16x16x4(xa1, b1, &macc[rt * 64]);
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 ds[64], ms[64];
+      for (int l = 0; l < 64; ++l) ds[l] = ms[l] = f32x4{0, 0, 0, 0};
+      for (int tt = 0; tt < 8; ++tt) {
+        f16x8 av[64], bb[64];
+        for (int lane = 0; lane < 64; ++lane) {
+          av[lane] = a_operand(slots, R, b, rt, tt, lane);
+          bb[lane] = build_b(qd[lane][tt], c[lane]);
+        }
+        mfma_16x16x32(av, bb, ds);
+        mfma_16x16x32(av, bm, ms);
+      }
+      f32x4* ac = acc + (size_t)(u * RT + rt) * 64;
+      for (int lane = 0; lane < 64; ++lane)
+        for (int i = 0; i < 4; ++i) {
+          float v = ac[lane][i];
+          v = std::fma(c[lane].d, ds[lane][i], v);
+          v = std::fma(c[lane].nmin, ms[lane][i], v);
+          ac[lane][i] = v;
+        }
+    }
   }
 }
+
+struct EmuGemm {
+  std::vector<uint8_t> packed;
+  const uint16_t* x;
+  float* y;
+  int64_t N, K, KB, NS, T, I, V, hdr_off;
+  int nwn;
+};
 
 }  // namespace
 
 extern "C" {
 
-// Emulated stream-K run: P workgroups of 4 waves x NT sub-tiles, executed one
-// after another in a seeded random order (the arrival order at shared tiles).
-int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int64_t P,
-               uint64_t order_seed, float* y) {
-  const int NW = 4;
-  int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
-  int RT = (R + 15) / 16;
-  int64_t T = (NS + NW * NT - 1) / (NW * NT), I = T * KB;
-  if (P > I || P < 1) return -1;
-  std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
-  pack(canon, packed.data(), N, K);
-  int64_t hdr_off = quant_region_bytes(N, K);
-  std::vector<f16x8> xq((size_t)RT * KB * 8 * 64);
-  std::vector<float> xs((size_t)RT * KB * 64 * 2);
-  xprep(x, xq.data(), xs.data(), R, K, RT);
-  const size_t slot_floats = (size_t)NW * NT * RT * 256;
-  std::vector<float> part((size_t)2 * P * slot_floats, std::nanf(""));
-  std::vector<uint32_t> cnt((size_t)T, 0);
-  std::vector<int64_t> order((size_t)P);
-  for (int64_t p = 0; p < P; ++p) order[(size_t)p] = p;
+// Emulated launch of the streaming kernel over G GEMMs (shapes N[g] x K[g],
+// canonical weights canon[g], bf16 x[g], outputs y[g]): NW waves per
+// workgroup in an nwn[g] x (NW / nwn[g]) grid, tiles of nwn[g] * NT
+// sub-tiles, V[g] ranges per GEMM (one per workgroup).  GEMM by GEMM (the
+// launch's barrier); ranges in a seeded random order (the arrival order at
+// tiles shared between ranges); waves of a range one after another (the
+// pieces of a tile shared by waves meet in "LDS" and are added in sub-range
+// order after the range); one partial-slot workspace and one set of tile
+// counters shared by all GEMMs.  Returns 0, -1 on a bad plan, -2 if a tile
+// counter is left armed, -3 on an inconsistent activation slot.
+int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const int64_t* Ks,
+                   const uint16_t* const* xs, float* const* ys, int R, int NT, int NW, const int* nwns,
+                   const int64_t* Vs, uint64_t order_seed) {
+  const int RT = (R + 15) / 16;
+  std::vector<EmuGemm> gs((size_t)G);
+  int64_t Tmax = 0, Vslots = 0;
+  for (int g = 0; g < G; ++g) {
+    EmuGemm& e = gs[(size_t)g];
+    e.N = Ns[g]; e.K = Ks[g]; e.KB = e.K / SB_W; e.NS = padded_n(e.N) / TILE_N;
+    e.nwn = nwns[g];
+    if (e.nwn < 1 || NW % e.nwn) return -1;
+    e.T = (e.NS + (int64_t)e.nwn * NT - 1) / ((int64_t)e.nwn * NT);
+    e.I = e.T * e.KB;
+    e.V = Vs[g];
+    if (e.V > e.I || e.V < 1) return -1;
+    e.packed.resize((size_t)packed_bytes(e.N, e.K));
+    pack(canon[g], e.packed.data(), e.N, e.K);
+    e.hdr_off = quant_region_bytes(e.N, e.K);
+    e.x = xs[g];
+    e.y = ys[g];
+    Tmax = std::max(Tmax, e.T);
+    Vslots = std::max(Vslots, e.V * e.nwn);
+  }
+  const size_t tile_f4 = (size_t)NT * RT * 64;            // f32x4 per wave piece (one column of a tile)
+  std::vector<f32x4> part((size_t)2 * Vslots * tile_f4, f32x4{NAN, NAN, NAN, NAN});
+  std::vector<uint32_t> cnt((size_t)Tmax, 0);
+  std::vector<f16x8> xslots;
   std::mt19937_64 rng(order_seed);
-  std::shuffle(order.begin(), order.end(), rng);
-  for (int i = 0; i < R * N; ++i) y[i] = std::nanf("");
-  for (int64_t p : order) {
-    int64_t it0 = range_first(p, P, I), it1 = range_first(p + 1, P, I);
-    std::vector<f32x4> acc((size_t)NW * NT * RT * 64), macc(acc.size());
-    auto zero = [&]() { for (auto& v : acc) v = f32x4{0, 0, 0, 0}; for (auto& v : macc) v = f32x4{0, 0, 0, 0}; };
-    zero();
-    int64_t ja = it0 % KB;
-    for (int64_t it = it0; it < it1; ++it) {
-      int64_t t = it / KB, j = it % KB;
-      for (int w = 0; w < NW; ++w)
-        for (int u = 0; u < NT; ++u) {
-          int64_t ns = (t * NW + w) * NT + u;
-          if (ns >= NS) continue;
-          size_t base = (size_t)((w * NT + u) * RT) * 64;
-          wave_step(packed.data(), hdr_off, ns, j, KB, xq.data(), xs.data(), RT, &acc[base], &macc[base]);
-        }
-      bool last = it + 1 == it1;
-      if (j != KB - 1 && !last) continue;
-      bool full = ja == 0 && j == KB - 1;
-      auto out_index = [&](int w, int u, int rt, int lane, int i, int64_t* o) {
-        int64_t n = ((t * NW + w) * NT + u) * TILE_N + (lane & 15);
-        int r = rt * 16 + 4 * (lane >> 4) + i;
-        if (n >= N || r >= R) return false;
-        *o = (int64_t)r * N + n;
-        return true;
-      };
-      if (full) {
-        for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
-          for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
-            int64_t o;
-            size_t a = (size_t)((w * NT + u) * RT + rt) * 64 + lane;
-            if (out_index(w, u, rt, lane, i, &o)) y[o] = acc[a][i] + macc[a][i];
-          }
-      } else {
-        int64_t ps = partial_slot(p, t, KB, P, I);
-        for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
-          for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
-            size_t a = (size_t)((w * NT + u) * RT + rt) * 64 + lane;
-            part[(size_t)(ps * NW + w) * NT * RT * 256 + ((u * RT + rt) * 4 + i) * 64 + lane] = acc[a][i] + macc[a][i];
-          }
-        int64_t q_lo = tile_first_owner(t, KB, P, I), q_hi = tile_last_owner(t, KB, P, I);
-        uint32_t prev = cnt[(size_t)t]++;
-        if (prev == (uint32_t)(q_hi - q_lo)) {
-          for (int w = 0; w < NW; ++w) for (int u = 0; u < NT; ++u) for (int rt = 0; rt < RT; ++rt)
-            for (int lane = 0; lane < 64; ++lane) for (int i = 0; i < 4; ++i) {
-              float v = 0.f;
-              for (int64_t q = q_lo; q <= q_hi; ++q) {
-                int64_t qs = partial_slot(q, t, KB, P, I);
-                v += part[(size_t)(qs * NW + w) * NT * RT * 256 + ((u * RT + rt) * 4 + i) * 64 + lane];
-              }
-              int64_t o;
-              if (out_index(w, u, rt, lane, i, &o)) y[o] = v;
+  for (int g = 0; g < G; ++g) {
+    EmuGemm& e = gs[(size_t)g];
+    const int64_t KB = e.KB;
+    const int nwn = e.nwn, nwk = NW / e.nwn;
+    for (int64_t i = 0; i < (int64_t)R * e.N; ++i) e.y[i] = std::nanf("");
+    // column wn of tile t: sub-tiles (t nwn + wn) NT + u
+    auto write_y = [&](int64_t t, int wn, const f32x4* v) {
+      for (int u = 0; u < NT; ++u)
+        for (int rt = 0; rt < RT; ++rt)
+          for (int lane = 0; lane < 64; ++lane)
+            for (int i = 0; i < 4; ++i) {
+              const int64_t n = ((t * nwn + wn) * NT + u) * TILE_N + (lane & 15);
+              const int r = rt * 16 + 4 * (lane >> 4) + i;
+              if (n < e.N && r < R) e.y[(int64_t)r * e.N + n] = v[(size_t)(u * RT + rt) * 64 + lane][i];
             }
-          cnt[(size_t)t] = 0;
+    };
+    std::vector<int64_t> order((size_t)e.V);
+    for (int64_t v = 0; v < e.V; ++v) order[(size_t)v] = v;
+    std::shuffle(order.begin(), order.end(), rng);
+    for (int64_t v : order) {
+      const int64_t A = range_first(v, e.V, e.I), B = range_first(v + 1, e.V, e.I), L = B - A;
+      const int64_t j0 = A % KB;
+      convert_x(e.x, R, e.K, j0, x_slots(A, B, KB), xslots);
+      // pieces[wk][slot][wn][tile_f4]
+      auto piece = [&](int64_t wk, int sl, int wn) { return (size_t)((wk * 2 + sl) * nwn + wn) * tile_f4; };
+      std::vector<f32x4> pieces((size_t)NW * 2 * tile_f4, f32x4{NAN, NAN, NAN, NAN});
+      for (int w = 0; w < NW; ++w) {
+        const int wn = w % nwn, wk = w / nwn;
+        const int64_t a_w = A + range_first<int64_t>(wk, nwk, L), b_w = A + range_first<int64_t>(wk + 1, nwk, L);
+        std::vector<f32x4> acc(tile_f4, f32x4{0, 0, 0, 0});
+        int64_t ja = a_w % KB;
+        for (int64_t it = a_w; it < b_w; ++it) {
+          const int64_t t = it / KB, j = it % KB;
+          const int64_t b = (it - A) % KB;
+          if (b != x_slot_of_emu(j, j0, KB)) return -3;
+          wave_step(e.packed.data(), e.hdr_off, (t * nwn + wn) * NT, NT, e.NS, j, KB, xslots, R, b, RT, acc.data());
+          const bool sub_end = it + 1 == b_w;
+          if (j != KB - 1 && !sub_end) continue;
+          if (ja == 0 && j == KB - 1) {
+            write_y(t, wn, acc.data());
+          } else {
+            const int sl = (a_w > t * KB) ? 0 : 1;
+            std::copy(acc.begin(), acc.end(), pieces.begin() + piece(wk, sl, wn));
+          }
+          std::fill(acc.begin(), acc.end(), f32x4{0, 0, 0, 0});
+          ja = 0;
         }
       }
-      zero();
-      ja = 0;
+      // after the range: tiles shared by waves, then tiles shared with other ranges
+      const int64_t tA = A / KB, tB = (B - 1) / KB;
+      const bool cross_a = tA * KB < A, cross_b = (tB + 1) * KB > B;
+      for (int64_t t = tA; t <= tB; ++t)
+        for (int wn = 0; wn < nwn; ++wn) {
+          const int64_t s0 = std::max(A, t * KB) - A, s1 = std::min(B, (t + 1) * KB) - A;
+          const int64_t k_lo = range_owner<int64_t>(s0, nwk, L), k_hi = range_owner<int64_t>(s1 - 1, nwk, L);
+          const bool crossing = (t == tA && cross_a) || (t == tB && cross_b);
+          if (k_lo == k_hi && !crossing) continue;
+          std::vector<f32x4> sum(tile_f4, f32x4{0, 0, 0, 0});
+          for (int64_t kk = k_lo; kk <= k_hi; ++kk) {
+            const int64_t a_k = A + range_first<int64_t>(kk, nwk, L), b_k = A + range_first<int64_t>(kk + 1, nwk, L);
+            if (a_k == b_k) continue;
+            const int sl = (a_k > t * KB) ? 0 : 1;
+            for (size_t k = 0; k < tile_f4; ++k) sum[k] += pieces[piece(kk, sl, wn) + k];
+          }
+          if (!crossing) {
+            write_y(t, wn, sum.data());
+          } else {
+            const int64_t gsl = partial_slot(v, t, KB, e.V, e.I);
+            std::copy(sum.begin(), sum.end(), part.begin() + (size_t)(gsl * nwn + wn) * tile_f4);
+          }
+        }
+      auto arrive = [&](int64_t t) {
+        const int64_t q_lo = tile_first_owner(t, KB, e.V, e.I), q_hi = tile_last_owner(t, KB, e.V, e.I);
+        const uint32_t prev = cnt[(size_t)t]++;
+        if (prev != (uint32_t)(q_hi - q_lo)) return;
+        for (int wn = 0; wn < nwn; ++wn) {
+          std::vector<f32x4> sum(tile_f4, f32x4{0, 0, 0, 0});
+          for (int64_t q = q_lo; q <= q_hi; ++q) {
+            const int64_t qs = partial_slot(q, t, KB, e.V, e.I);
+            for (size_t k = 0; k < tile_f4; ++k) sum[k] += part[(size_t)(qs * nwn + wn) * tile_f4 + k];
+          }
+          write_y(t, wn, sum.data());
+        }
+        cnt[(size_t)t] = 0;
+      };
+      if (cross_a) arrive(tA);
+      if (cross_b && !(cross_a && tB == tA)) arrive(tB);
     }
+    for (int64_t t = 0; t < Tmax; ++t)
+      if (cnt[(size_t)t] != 0) return -2;   // a counter was left armed
   }
-  for (int64_t t = 0; t < T; ++t)
-    if (cnt[(size_t)t] != 0) return -2;   // a counter was left armed
   return 0;
 }
 
-int emu_packed_size(int64_t N, int64_t K, int64_t* bytes) {
-  *bytes = packed_bytes(N, K);
-  return 0;
+int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int NW, int nwn,
+               int64_t V, uint64_t order_seed, float* y) {
+  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, order_seed);
 }
 
 int emu_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
   pack(canon, packed, N, K);
   return 0;
-}
-
-// Emulated matrix-core run with NT sub-tiles per wave and S K-splits; writes y.
-int emu_gemm(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int S, float* y) {
-  int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
-  int RT = (R + 15) / 16;
-  std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
-  pack(canon, packed.data(), N, K);
-  std::vector<f16x8> xq((size_t)RT * KB * 8 * 64);
-  std::vector<float> xs((size_t)RT * KB * 64 * 2);
-  xprep(x, xq.data(), xs.data(), R, K, RT);
-  int64_t kbs = (KB + S - 1) / S;
-  S = (int)((KB + kbs - 1) / kbs);
-  std::vector<float> part((size_t)S * R * N, 0.f);
-  int64_t hdr_off = quant_region_bytes(N, K);
-  int64_t NG = (NS + NT - 1) / NT;
-  for (int64_t s = 0; s < S; ++s)
-    for (int64_t ng = 0; ng < NG; ++ng)
-      for (int u = 0; u < NT; ++u) {
-        int64_t ns = ng * NT + u;
-        if (ns >= NS) continue;
-        std::vector<f32x4> acc((size_t)RT * 64, f32x4{0, 0, 0, 0}), macc((size_t)RT * 64, f32x4{0, 0, 0, 0});
-        int64_t j1 = (s * kbs + kbs < KB) ? s * kbs + kbs : KB;
-        for (int64_t j = s * kbs; j < j1; ++j) {
-          WConst c[64];
-          uint32_t qd[64][8];
-          for (int lane = 0; lane < 64; ++lane) {
-            const uint8_t* qp = packed.data() + lane * 16 + quant_chunk_off(ns, j, KB);
-            memcpy(qd[lane], qp, 16);
-            memcpy(qd[lane] + 4, qp + 1024, 16);
-            uint32_t h[4];
-            memcpy(h, packed.data() + hdr_off + (lane & 15) * 16 + header_chunk_off(ns, j, KB), 16);
-            c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
-          }
-          for (int rt = 0; rt < RT; ++rt) {
-            std::vector<f32x4> dsum(64, f32x4{0, 0, 0, 0});
-            for (int t = 0; t < 8; ++t) {
-              f16x8 a[64], b[64];
-              for (int lane = 0; lane < 64; ++lane) {
-                a[lane] = xq[((rt * KB + j) * 8 + t) * 64 + lane];
-                b[lane] = build_b(qd[lane][t], c[lane]);
-              }
-              mfma_16x16x32(a, b, dsum.data());
-            }
-            float xa0[64], xa1[64], b0[64], b1[64];
-            for (int lane = 0; lane < 64; ++lane) {
-              acc[rt * 64 + lane] += c[lane].d * dsum[lane];
-              xa0[lane] = xs[((rt * KB + j) * 64 + lane) * 2];
-              xa1[lane] = xs[((rt * KB + j) * 64 + lane) * 2 + 1];
-              b0[lane] = c[lane].bm0;
-              b1[lane] = c[lane].bm1;
-            }
-            mfma_16x16x4(xa0, b0, &macc[rt * 64]);
-            mfma_16x16x4(xa1, b1, &macc[rt * 64]);
-          }
-        }
-        for (int lane = 0; lane < 64; ++lane) {
-          int64_t n = ns * TILE_N + (lane & 15);
-          if (n >= N) continue;
-          for (int rt = 0; rt < RT; ++rt)
-            for (int i = 0; i < 4; ++i) {
-              int r = rt * 16 + 4 * (lane >> 4) + i;
-              if (r < R) part[((size_t)s * R + r) * N + n] = acc[rt * 64 + lane][i] + macc[rt * 64 + lane][i];
-            }
-        }
-      }
-  for (int64_t i = 0; i < (int64_t)R * N; ++i) {
-    float v = part[i];
-    for (int s = 1; s < S; ++s) v += part[(size_t)s * R * N + i];
-    y[i] = v;
-  }
-  return S;
 }
 
 // Emulated dequantisation kernel (from the packed layout).
@@ -346,7 +328,7 @@ int emu_dequant(const uint8_t* canon, int64_t N, int64_t K, float* w) {
           for (int p = 0; p < 8; ++p) {
             int hb = p >> 2;
             float qq = (float)((q[t] >> (4 * p)) & 15u);
-            w[n * K + j * SB_W + slot_k(g, t, p)] = __builtin_fmaf(A[hb], qq, -B[hb]);
+            w[n * K + j * SB_W + slot_k(g, t, p)] = std::fma(A[hb], qq, -B[hb]);
           }
       }
   return 0;

@@ -68,7 +68,8 @@ def test_host_validation_codes():
     assert L.qgemm_argmax_rows(None, 2, 10, vp(4096), None) == Q.QGEMM_EINVAL
     assert L.qgemm_argmax_rows(None, 0, 10, None, None) == Q.QGEMM_OK        # R = 0: no-op
     s = vp()
-    assert L.qgemm_seq_create(ctypes.byref(s), None, 1) == Q.QGEMM_EINVAL
+    assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 0) == Q.QGEMM_EINVAL
+    assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 4) == Q.QGEMM_EINVAL
     assert L.qgemm_seq_run(None, None, None, 1, None, None) == Q.QGEMM_EINVAL
     assert L.qgemm_destroy(None) == Q.QGEMM_OK
     assert L.qgemm_seq_destroy(None) == Q.QGEMM_OK

@@ -28,17 +28,21 @@ def test_packed_size_and_padding():
     assert np.count_nonzero(p) <= np.count_nonzero(canon)
 
 
-@pytest.mark.parametrize("N,K,R,NT,S", [
-    (256, 1024, 12, 2, 1),     # the small correctness workload
-    (40, 1024, 5, 2, 3),       # ragged N, K split into uneven parts
-    (33, 512, 1, 1, 2),
-    (48, 512, 20, 1, 1),       # two row tiles
-    (16, 256, 48, 1, 1),       # three row tiles
+@pytest.mark.parametrize("N,K,R,NT,NW,V", [
+    (256, 1024, 12, 2, 8, 1),     # the small correctness workload, one range
+    (40, 1024, 5, 2, 8, 3),       # ragged N, K split into uneven parts
+    (33, 512, 1, 1, 8, 2),
+    (48, 512, 20, 1, 8, 1),       # two row tiles
+    (16, 256, 48, 1, 4, 1),       # three row tiles
+    (20, 256, 64, 1, 4, 1),       # four row tiles
+    (700, 2048, 12, 2, 8, 4),     # several tiles, ranges shorter than a tile row
+    (16, 512, 5, 1, 8, 1),        # 2 steps for 8 waves: empty sub-ranges
+    (48, 1024, 7, 1, 8, 5),       # ranges of 2-3 steps over 8 waves
 ])
-def test_gemm_data_flow_matches_oracle(orc, N, K, R, NT, S):
+def test_gemm_data_flow_matches_oracle(orc, N, K, R, NT, NW, V):
     canon = synth.matrix_rows(0, 3, N, K)
     x = synth.x_bf16(0, 5, R, K, outlier_p=0.01)
-    y = emu.gemm(canon, N, K, x, NT=NT, S=S)
+    y = emu.stream(canon, N, K, x, NT=NT, NW=NW, V=V)
     ref = orc.gemm(canon, N, K, x)
     m = assert_parity(y, ref, f"emu N={N} K={K} R={R}")
     assert m["rel_l2"] < 2e-6
@@ -48,27 +52,67 @@ def test_edge_blocks_emulated(orc):
     N, K, R = 64, 1024, 24
     canon = synth.matrix_rows(4, 0, N, K, edge_mode=1)
     x = synth.x_bf16(4, 1, R, K)
-    assert_parity(emu.gemm(canon, N, K, x), orc.gemm(canon, N, K, x), "edge blocks")
+    assert_parity(emu.stream(canon, N, K, x, NT=1, NW=8, V=3), orc.gemm(canon, N, K, x), "edge blocks")
 
 
-@pytest.mark.parametrize("N,K,R,NT,P", [
-    (256, 1024, 12, 2, 7),      # 2 tiles x 4 blocks over 7 workgroups: every tile shared
-    (256, 1024, 12, 2, 2),      # one workgroup per tile (no partials)
-    (300, 2048, 5, 1, 13),      # ragged last tile, uneven ranges
-    (40, 3072, 20, 2, 6),       # one tile, 12 blocks, 2 row tiles
-    (700, 512, 3, 2, 11),
+@pytest.mark.parametrize("N,K,R,NT,NW,V", [
+    (256, 1024, 12, 2, 4, 7),      # 2 tiles x 4 blocks over 7 ranges: every tile shared
+    (256, 1024, 12, 2, 4, 2),      # one range per tile (no partials)
+    (300, 2048, 5, 1, 8, 13),      # ragged last tile, uneven ranges
+    (40, 3072, 20, 2, 4, 6),       # one tile, 12 blocks, 2 row tiles
+    (700, 512, 3, 2, 4, 11),
+    (1000, 8192, 12, 1, 8, 50),    # ranges of a few blocks each (activation slots < K/256)
 ])
-def test_stream_schedule_matches_oracle_any_order(orc, N, K, R, NT, P):
+def test_stream_schedule_matches_oracle_any_order(orc, N, K, R, NT, NW, V):
     canon = synth.matrix_rows(2, 8, N, K)
     x = synth.x_bf16(2, 9, R, K, outlier_p=0.01)
     ref = orc.gemm(canon, N, K, x)
-    ys = [emu.stream(canon, N, K, x, NT=NT, P=P, order_seed=s) for s in range(3)]
+    ys = [emu.stream(canon, N, K, x, NT=NT, NW=NW, V=V, order_seed=s) for s in range(3)]
     for y in ys:
-        m = assert_parity(y, ref, f"stream N={N} K={K} R={R} P={P}")
+        m = assert_parity(y, ref, f"stream N={N} K={K} R={R} V={V}")
         assert m["rel_l2"] < 2e-6
     # the reduction order is fixed: any arrival order gives the same bits
     for y in ys[1:]:
         assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,R,NW,nwn,V", [
+    (256, 1024, 12, 8, 2, 3),      # 2 columns x 4 sub-ranges, tiles of 32 outputs
+    (320, 6144, 12, 8, 2, 40),     # an attention-output-like K, ranges over tile edges
+    (330, 4352, 12, 8, 4, 23),     # ragged N: the last tile has idle columns
+    (128, 4352, 5, 8, 8, 17),      # every wave its own column (no K split)
+    (50, 2048, 20, 8, 4, 3),       # two row tiles, a single ragged tile
+    (700, 1024, 48, 4, 2, 9),      # three row tiles, 4 waves
+    (64, 512, 1, 8, 8, 1),         # one step per column
+])
+def test_wave_grid_matches_oracle_any_order(orc, N, K, R, NW, nwn, V):
+    """Waves side by side along N (nwn columns) and along K (NW / nwn rows)."""
+    canon = synth.matrix_rows(3, 4, N, K)
+    x = synth.x_bf16(3, 7, R, K, outlier_p=0.01)
+    ref = orc.gemm(canon, N, K, x)
+    ys = [emu.stream(canon, N, K, x, NT=1, NW=NW, V=V, order_seed=s, nwn=nwn) for s in range(2)]
+    for y in ys:
+        m = assert_parity(y, ref, f"grid N={N} K={K} R={R} nwn={nwn} V={V}")
+        assert m["rel_l2"] < 2e-6
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+
+
+def test_sequence_shares_workspace_across_gemms(orc):
+    """Several GEMMs of different shapes in one launch reuse the partial slots and
+    tile counters; each result still matches the oracle and no counter stays armed."""
+    shapes = [(300, 1024), (64, 2048), (1000, 512), (40, 3072)]
+    R = 12
+    mats = [(synth.matrix_rows(6, i, N, K), N, K) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.x_bf16(6, 50 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    Vs = [5, 5, 5, 5]
+    nwns = [1, 2, 4, 1]            # each GEMM its own wave grid
+    ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns)
+    for (canon, N, K), x, y, V, nwn in zip(mats, xs, ys, Vs, nwns):
+        m = assert_parity(y, orc.gemm(canon, N, K, x), f"seq N={N} K={K}")
+        assert m["rel_l2"] < 2e-6
+        # the same GEMM alone in its own launch gives the same bits
+        alone = emu.stream(canon, N, K, x, NT=2, NW=4, V=V, order_seed=11, nwn=nwn)
+        assert np.array_equal(alone.view(np.uint32), y.view(np.uint32))
 
 
 def test_stream_schedule_slots_unique():

@@ -99,9 +99,8 @@ def test_shared_tile_counters_rearm_over_repeats(orc):
     x = synth.x_bf16(5, 1, 12, m.K)
     xd = G.to_dev(x)
     ys = [torch.empty((12, m.N), dtype=torch.float32, device="cuda") for _ in range(6)]
-    g.stage(xd, 12)
     for y in ys:
-        g.multiply(y, 12)
+        g.run(xd, y)
     torch.cuda.synchronize()
     first = ys[0].cpu().numpy()
     for y in ys[1:]:

@@ -203,31 +203,43 @@ def test_argmax_ties_and_nan():
     assert np.array_equal(idx.cpu().numpy(), np.argmax(big, axis=1))
 
 
-# ---- full weight pass machinery (graph capture, replay) --------------------------
+# ---- full weight pass machinery (one cooperative launch over several GEMMs) ----
 
-def test_seq_graph_replay_matches_eager(orc):
+@pytest.mark.parametrize("persistent", [False, True])
+def test_seq_matches_oracle_and_repeats_bitwise(orc, persistent):
     import torch
     import weight_streaming_gemm_amd as wsg
-    shapes = [(300, 1024), (64, 2048), (1000, 1024)]
-    mats = [G.make(9, i, N, K, max_R=12) for i, (N, K) in enumerate(shapes)]
+    shapes = [(300, 1024), (64, 2048), (1000, 1024), (40, 3072), (151, 512)]
     R = 12
+    mats = [G.make(9, i, N, K, max_R=12) for i, (N, K) in enumerate(shapes)]
     xs_np = [synth.x_bf16(9, 100 + i, R, K) for i, (N, K) in enumerate(shapes)]
     xs = [G.to_dev(x) for x in xs_np]
     ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for N, K in shapes]
     idx = torch.empty(R, dtype=torch.int32, device="cuda")
-    seq = wsg.Seq([g for _, g in mats])
-    eager = [G.run(g, x) for (_, g), x in zip(mats, xs_np)]
+    seq = wsg.Seq([g for _, g in mats], persistent=persistent)
+    first = None
     for rep in range(4):
+        _flush(f"seq persistent={persistent} rep {rep}")
         for y in ys:
             y.fill_(-7.0)
         seq.run(xs, ys, R, argmax_idx=idx)
         torch.cuda.synchronize()
-        _ = (torch.ones(1000, device="cuda") * rep).sum().item()   # eager work between replays
-        for i, y in enumerate(ys):
-            assert np.array_equal(y.cpu().numpy().view(np.uint32), eager[i].view(np.uint32)), (rep, i)
-        assert np.array_equal(idx.cpu().numpy(), np.argmax(eager[-1], axis=1))
-    canon_last = mats[-1][0]
-    assert_parity(eager[-1], orc.gemm(canon_last, 1000, 1024, xs_np[-1]), "seq last")
+        _ = (torch.ones(1000, device="cuda") * rep).sum().item()   # other work between launches
+        got = [y.cpu().numpy() for y in ys]
+        if first is None:
+            first = got
+            for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+                assert_parity(got[i], orc.gemm(canon, N, K, xs_np[i]), f"seq gemm {i}")
+        for i in range(len(shapes)):
+            assert np.array_equal(got[i].view(np.uint32), first[i].view(np.uint32)), (rep, i)
+        assert np.array_equal(idx.cpu().numpy(), np.argmax(got[-1], axis=1))
+    assert seq.errors() == 0
+    # fewer rows through the same sequence
+    seq.run([x[:3] for x in xs], [y[:3] for y in ys], 3)
+    torch.cuda.synchronize()
+    for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+        assert_parity(ys[i][:3].cpu().numpy(), orc.gemm(canon, N, K, xs_np[i][:3]), f"seq R=3 gemm {i}")
+    assert seq.errors() == 0
     seq.close()
     for _, g in mats:
         g.close()

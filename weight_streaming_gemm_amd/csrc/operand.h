@@ -4,7 +4,9 @@
 //
 // For lane group g (sub-blocks 2g, 2g+1 of a block) the B operand element e of
 // step t is sc_{2g + (e & 1)} * q_k for k = operand_k(g, t, e) (layout.h): an
-// integer <= 63 * 15 = 945, exact in binary16.
+// integer <= 63 * 15 = 945, exact in binary16.  The min term uses a second B
+// operand whose element e is m_{2g + (e & 1)} (<= 63, exact), the same for
+// every step t of the block.
 #pragma once
 #include <stdint.h>
 
@@ -37,9 +39,9 @@ struct WConst {
   f16x2 sc16;   // (sc_{2g}/16, sc_{2g+1}/16)        exact
   f16x2 b1;     // (-1024 sc_{2g}, -1024 sc_{2g+1})  exact
   f16x2 b16;    // (-64 sc_{2g}, -64 sc_{2g+1})      exact
+  f16x2 m;      // (m_{2g}, m_{2g+1})                exact
   float d;      // d
-  float bm0;    // -dmin m_{2g}                        exact in fp32 (17 bits)
-  float bm1;    // -dmin m_{2g+1}
+  float nmin;   // -dmin
 };
 
 QG_HD WConst header_consts(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, int g) {
@@ -52,10 +54,10 @@ QG_HD WConst header_consts(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, i
   c.sc16 = sc * f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
   c.b1 = sc * f16x2{(_Float16)-1024.0f, (_Float16)-1024.0f};
   c.b16 = sc * f16x2{(_Float16)-64.0f, (_Float16)-64.0f};
+  uint32_t mpair = ((F >> 12) & 63u) | (((F >> 18) & 63u) << 16);
+  c.m = bitcast<f16x2>(mpair | 0x64006400u) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
   c.d = (float)bitcast<_Float16>((uint16_t)(h0 & 0xFFFFu));
-  float dmin = (float)bitcast<_Float16>((uint16_t)(h0 >> 16));
-  c.bm0 = -dmin * (float)((F >> 12) & 63u);
-  c.bm1 = -dmin * (float)((F >> 18) & 63u);
+  c.nmin = -(float)bitcast<_Float16>((uint16_t)(h0 >> 16));
   return c;
 }
 
@@ -76,6 +78,24 @@ QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
   f16x2 o2 = fma2(p2, c.sc, c.b1);
   f16x2 o3 = fma2(p3, c.sc16, c.b16);
   return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
+}
+
+// the min-term B operand: (m_{2g}, m_{2g+1}) in every pair
+QG_HD f16x8 build_m(const WConst& c) {
+  return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1]};
+}
+
+// Eight activations of one matrix-core A operand from two runs of four bf16
+// values, lo = x[k0 .. k0+3] and hi = x[k0+32 .. k0+35] (two dwords each, low
+// half first): element 2v + h is run h's value v, converted to binary16 with
+// round-to-nearest-even (exact for |x| in [2^-17, 65504]).
+QG_HD f16x8 build_a(uint32_t lo0, uint32_t lo1, uint32_t hi0, uint32_t hi1) {
+  const float a0 = bitcast<float>(lo0 << 16), a1 = bitcast<float>(lo0 & 0xFFFF0000u);
+  const float a2 = bitcast<float>(lo1 << 16), a3 = bitcast<float>(lo1 & 0xFFFF0000u);
+  const float b0 = bitcast<float>(hi0 << 16), b1 = bitcast<float>(hi0 & 0xFFFF0000u);
+  const float b2 = bitcast<float>(hi1 << 16), b3 = bitcast<float>(hi1 & 0xFFFF0000u);
+  return f16x8{(_Float16)a0, (_Float16)b0, (_Float16)a1, (_Float16)b1,
+               (_Float16)a2, (_Float16)b2, (_Float16)a3, (_Float16)b3};
 }
 
 }  // namespace qg

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <map>
 #include <new>
@@ -20,27 +22,23 @@ struct qgemm_handle {
   int64_t N, K, KB, NS;
   int max_R;
   int cus;
-  int occ[5][5];  // resident workgroups per CU of the streaming kernel, by [row tiles][sub-tiles]
+  int occ[5];     // resident workgroups per CU of the streaming kernel, by row tiles
   // workspace (owned)
-  void* xq;
-  void* xs;
   float* part;
   uint32_t* cnt;
-  size_t xq_bytes, xs_bytes, part_bytes, cnt_bytes;
-  int staged_R;   // rows of the operands last staged (-1: none)
+  size_t part_bytes, cnt_bytes;
 };
 
-static const uint32_t HANDLE_MAGIC = 0x51474D31u;  // "QGM1"
-static const uint32_t SEQ_MAGIC = 0x51475331u;     // "QGS1"
+static const uint32_t HANDLE_MAGIC = 0x51474D32u;  // "QGM2"
+static const uint32_t SEQ_MAGIC = 0x51475332u;     // "QGS2"
 
 namespace {
 
 struct Plan {
   int path;
-  int RT, NT;
-  int64_t T, I, P;
-  int kernels;
-  size_t part_bytes, cnt_bytes, ws_bytes;
+  int RT, NT, NW, nwn;
+  int64_t T, I, V, P;
+  size_t part_bytes, cnt_bytes;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -48,82 +46,104 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_shape(int64_t N, int64_t K) {
   if (N < 1 || K < 256 || K % 256 != 0) return false;
   if (N > (int64_t(1) << 40) || K > (int64_t(1) << 30)) return false;
-  // the kernels address each region with 32-bit offsets
+  // the kernels address each region, and x, with 32-bit offsets
   if (quant_region_bytes(N, K) >= (int64_t(1) << 31)) return false;
-  if ((K / 256) * 8192 * 4 >= (int64_t(1) << 31)) return false;
+  if ((int64_t)QGEMM_MAX_R * K * 2 >= (int64_t(1) << 31)) return false;
   return true;
 }
 
 bool valid_handle(const qgemm_handle* h) { return h && h->magic == HANDLE_MAGIC; }
 
-// Matrix-core plan: 16-row tiles, NT 16-output sub-tiles per wave, 4 waves per
-// workgroup, and as many workgroups as stay resident on the device (each gets
-// an equal share of the (tile, block) steps), but never fewer than two steps
-// per workgroup.
-Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5][5]) {
+// Matrix-core plan for one GEMM: 16-row tiles, NW waves per workgroup in an
+// nwn x (NW / nwn) grid, tiles of nwn * NT 16-output sub-tiles, one workgroup
+// per CU, one range of (tile, block) steps per workgroup.  V = P ranges: as
+// many as stay resident (at most P_cap), fewer if there are fewer steps.  A
+// range's activations must fit the workgroup's LDS: nwn is the smallest wave
+// grid width for which they do (wider tiles mean fewer steps per range); if
+// none does, the widest grid runs ranges of at most cap steps in several rounds.
+Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64_t P_cap = 0) {
   Plan p{};
   p.path = QGEMM_PATH_MFMA;
   p.RT = (R + 15) / 16;
-  p.NT = (p.RT <= 2) ? 2 : 1;
-  p.T = (NS + 4 * p.NT - 1) / (4 * p.NT);
-  p.I = p.T * KB;
-  int64_t resident = (int64_t)cus * std::max(1, occ[p.RT][p.NT]);
-  p.P = std::max<int64_t>(1, std::min(resident, p.I / 2));
-  p.kernels = 1;
-  p.part_bytes = (size_t)(2 * p.P) * 4 * p.NT * p.RT * 256 * 4;
+  p.NW = waves_for(p.RT);
+  p.NT = subtiles_for(p.RT);
+  int64_t resident = (int64_t)cus * std::max(1, occ[p.RT]);
+  if (P_cap > 0) resident = std::min(resident, P_cap);
+  const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW);
+  for (int nwn = 1; nwn <= p.NW; nwn *= 2) {
+    if (p.NW % nwn) break;
+    p.nwn = nwn;
+    p.T = (NS + (int64_t)nwn * p.NT - 1) / ((int64_t)nwn * p.NT);
+    p.I = p.T * KB;
+    p.V = std::max<int64_t>(1, std::min(resident, p.I));
+    if (std::min((p.I + p.V - 1) / p.V, KB) <= cap) break;   // one round
+    if (2 * nwn > p.NW || p.NW % (2 * nwn))                  // the widest grid: rounds of
+      p.V = std::min(p.I, std::max(p.V, (p.I + cap - 1) / cap));   // at most cap steps
+  }
+  p.P = p.V;
+  p.part_bytes = (size_t)(2 * p.V) * partial_slot_bytes(p.RT, p.NT, p.nwn);
   p.cnt_bytes = (size_t)p.T * 4;
-  p.ws_bytes = (size_t)p.RT * KB * 8192 + (size_t)p.RT * KB * 512 + p.part_bytes + p.cnt_bytes;
   return p;
 }
+
+// the kernel's schedule arithmetic is 32-bit: (V + 1) * I must stay below 2^31
+bool plan_fits(const Plan& p) { return (p.V + 1) * (p.I + 1) < (int64_t(1) << 31); }
 
 int make_plan(const qgemm_handle* h, int R, int path, Plan* out) {
   if (path == QGEMM_PATH_VALU) return QGEMM_EPATH;
   if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA) return QGEMM_EINVAL;
   *out = plan_stream(h->NS, h->KB, R, h->cus, h->occ);
-  return QGEMM_OK;
+  return plan_fits(*out) ? QGEMM_OK : QGEMM_ESHAPE;
 }
 
-int stage_impl(qgemm_handle* h, const void* x, int R, hipStream_t st) {
-  int RT = (R + 15) / 16;
-  hipError_t e = launch_xprep(reinterpret_cast<const uint16_t*>(x), h->xq, h->xs, R, h->K, RT, st);
-  if (e != hipSuccess) return QGEMM_EHIP;
-  h->staged_R = R;
-  return QGEMM_OK;
-}
-
-int multiply_impl(qgemm_handle* h, float* y, int R, int path, hipStream_t st) {
-  Plan p;
-  int rc = make_plan(h, R, path, &p);
-  if (rc) return rc;
-  StreamArgs a{};
-  a.packed = h->packed;
-  a.hdr_off = quant_region_bytes(h->N, h->K);
-  a.quant_bytes = (uint32_t)a.hdr_off;
-  a.hdr_bytes = (uint32_t)(packed_bytes(h->N, h->K) - a.hdr_off);
-  a.xq = h->xq;
-  a.xs = h->xs;
-  a.y = y;
-  a.part = h->part;
-  a.cnt = h->cnt;
-  a.N = h->N;
-  a.NS = h->NS;
-  a.KB = (int)h->KB;
-  a.R = R;
-  a.T = p.T;
-  a.I = p.I;
-  a.P = p.P;
-  a.RT = p.RT;
-  a.NT = p.NT;
-  return launch_stream(a, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+GemmDesc make_desc(const qgemm_handle* h, const void* x, float* y, const Plan& p) {
+  GemmDesc d{};
+  d.packed = h->packed;
+  d.x = reinterpret_cast<const uint16_t*>(x);
+  d.y = y;
+  d.quant_bytes = (uint32_t)quant_region_bytes(h->N, h->K);
+  d.hdr_bytes = (uint32_t)(packed_bytes(h->N, h->K) - d.quant_bytes);
+  d.N = (int32_t)h->N;
+  d.NS = (int32_t)h->NS;
+  d.KB = (int32_t)h->KB;
+  d.nwn = (int32_t)p.nwn;
+  d.T = (int32_t)p.T;
+  d.I = (int32_t)p.I;
+  d.V = (int32_t)p.V;
+  return d;
 }
 
 int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStream_t st) {
   Plan p;
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
-  rc = stage_impl(h, x, R, st);
-  if (rc) return rc;
-  return multiply_impl(h, y, R, path, st);
+  StreamArgs a{};
+  a.d0 = make_desc(h, x, y, p);
+  a.descs = nullptr;
+  a.part = h->part;
+  a.cnt = h->cnt;
+  a.sync = nullptr;
+  a.err = nullptr;
+  a.G = 1;
+  a.R = R;
+  a.P = (int32_t)p.P;
+  a.RT = p.RT;
+  a.NT = p.NT;
+  a.NW = p.NW;
+  return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+}
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QGEMM_EHIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || *cus <= 0)
+    return QGEMM_EHIP;
+  return QGEMM_OK;
+}
+
+void fill_occupancy(int occ[5]) {
+  occ[0] = 0;
+  for (int rt = 1; rt < 5; ++rt) occ[rt] = stream_occupancy(rt, subtiles_for(rt), waves_for(rt));
 }
 
 }  // namespace
@@ -175,35 +195,28 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
   h->KB = K / 256;
   h->NS = padded_n(N) / 16;
   h->max_R = max_R;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+  if (device_cus(&h->cus) != QGEMM_OK) {
     delete h;
     return QGEMM_EHIP;
   }
-  h->cus = cus;
-  for (int rt = 0; rt < 5; ++rt)
-    for (int nt = 0; nt < 5; ++nt) h->occ[rt][nt] = (rt && nt) ? stream_occupancy(rt, nt) : 0;
-  int rt_max = (max_R + 15) / 16;
-  h->xq_bytes = (size_t)rt_max * h->KB * 8192;
-  h->xs_bytes = (size_t)rt_max * h->KB * 512;
+  fill_occupancy(h->occ);
   size_t part = 0, cnt = 0;
   for (int R = 1; R <= max_R; ++R) {
-    Plan p = plan_stream(h->NS, h->KB, R, cus, h->occ);
+    Plan p = plan_stream(h->NS, h->KB, R, h->cus, h->occ);
+    if (!plan_fits(p)) {
+      delete h;
+      return QGEMM_ESHAPE;
+    }
     part = std::max(part, p.part_bytes);
     cnt = std::max(cnt, p.cnt_bytes);
   }
   h->part_bytes = part;
   h->cnt_bytes = cnt;
-  h->staged_R = -1;
-  bool ok = hipMalloc(&h->xq, h->xq_bytes) == hipSuccess && hipMalloc(&h->xs, h->xs_bytes) == hipSuccess;
-  if (ok && part) ok = hipMalloc(reinterpret_cast<void**>(&h->part), part) == hipSuccess;
-  if (ok && cnt) ok = hipMalloc(reinterpret_cast<void**>(&h->cnt), cnt) == hipSuccess &&
-                      hipMemset(h->cnt, 0, cnt) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  bool ok = hipMalloc(reinterpret_cast<void**>(&h->part), part) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&h->cnt), cnt) == hipSuccess &&
+            hipMemset(h->cnt, 0, cnt) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
-    if (h->xq) (void)hipFree(h->xq);
-    if (h->xs) (void)hipFree(h->xs);
     if (h->part) (void)hipFree(h->part);
     if (h->cnt) (void)hipFree(h->cnt);
     delete h;
@@ -225,26 +238,6 @@ int qgemm_run_path(qgemm_t h, const void* x_bf16, float* y, int R, int path, voi
 
 int qgemm_run(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
   return qgemm_run_path(h, x_bf16, y, R, QGEMM_PATH_AUTO, stream);
-}
-
-int qgemm_stage(qgemm_t h, const void* x_bf16, int R, void* stream) {
-  if (!valid_handle(h)) return QGEMM_EINVAL;
-  if (R < 0 || R > h->max_R) return QGEMM_ERANGE_R;
-  if (R == 0) return QGEMM_OK;
-  if (!x_bf16) return QGEMM_EINVAL;
-  if (!aligned16(x_bf16)) return QGEMM_EALIGN;
-  return stage_impl(h, x_bf16, R, reinterpret_cast<hipStream_t>(stream));
-}
-
-int qgemm_multiply(qgemm_t h, float* y, int R, int path, void* stream) {
-  if (!valid_handle(h)) return QGEMM_EINVAL;
-  if (R < 0 || R > h->max_R) return QGEMM_ERANGE_R;
-  if (path < QGEMM_PATH_AUTO || path > QGEMM_PATH_MFMA) return QGEMM_EINVAL;
-  if (R == 0) return QGEMM_OK;
-  if (R != h->staged_R) return QGEMM_ERANGE_R;
-  if (!y) return QGEMM_EINVAL;
-  if (!aligned16(y)) return QGEMM_EALIGN;
-  return multiply_impl(h, y, R, path, reinterpret_cast<hipStream_t>(stream));
 }
 
 int qgemm_dequantize(qgemm_t h, float* w_out, void* stream) {
@@ -275,8 +268,11 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   info->tiles = p.T;
   info->workgroups = p.P;
   info->steps = p.I;
-  info->kernels = p.kernels;
-  info->workspace_bytes = p.ws_bytes;
+  info->kernels = 1;
+  info->workspace_bytes = p.part_bytes + p.cnt_bytes;
+  info->ranges = p.V;
+  info->waves_per_workgroup = p.NW;
+  info->wave_columns = p.nwn;
   return QGEMM_OK;
 }
 
@@ -284,8 +280,6 @@ int qgemm_destroy(qgemm_t h) {
   if (!h) return QGEMM_OK;
   if (!valid_handle(h)) return QGEMM_EINVAL;
   (void)hipDeviceSynchronize();
-  if (h->xq) (void)hipFree(h->xq);
-  if (h->xs) (void)hipFree(h->xs);
   if (h->part) (void)hipFree(h->part);
   if (h->cnt) (void)hipFree(h->cnt);
   h->magic = 0;
@@ -297,10 +291,10 @@ int qgemm_destroy(qgemm_t h) {
 
 // ---- full weight pass --------------------------------------------------------
 
-struct GraphKey {
+struct SeqKey {
   int R;
   std::vector<uintptr_t> ptrs;
-  bool operator<(const GraphKey& o) const {
+  bool operator<(const SeqKey& o) const {
     if (R != o.R) return R < o.R;
     return ptrs < o.ptrs;
   }
@@ -308,25 +302,121 @@ struct GraphKey {
 
 struct qgemm_seq {
   uint32_t magic;
+  uint32_t flags;
   std::vector<qgemm_handle*> hs;
-  hipStream_t cap;
-  std::map<GraphKey, hipGraphExec_t> graphs;
+  hipStream_t cap;                                 // capture stream (graph mode)
+  std::map<SeqKey, hipGraphExec_t> graphs;         // per (R, pointer set) (graph mode)
+  int cus;
+  int occ[5];
+  // workspace shared by the GEMMs of a launch (they run one after another)
+  float* part;
+  uint32_t* cnt;     // per-tile counters
+  uint32_t* sync;    // count + 1 barrier counters
+  uint32_t* err;
+  size_t part_bytes, cnt_bytes;
+  std::map<SeqKey, GemmDesc*> descs;   // device descriptor arrays per (R, pointer set)
 };
+
+namespace {
+
+// one launch over all GEMMs of a sequence: the same (RT, NT, NW) and the same
+// P = V for all (every workgroup takes one range of every GEMM): P is the
+// smallest of the GEMMs' single-launch plans, and must still fit every GEMM's
+// activations (else the sequence cannot run persistent)
+Plan plan_seq(const qgemm_seq* s, int R, std::vector<Plan>* per, bool* fits) {
+  int64_t P = INT64_MAX;
+  for (const qgemm_handle* h : s->hs) P = std::min(P, plan_stream(h->NS, h->KB, R, s->cus, s->occ).P);
+  Plan all{};
+  int64_t Tmax = 1;
+  size_t slot = 0;
+  *fits = true;
+  for (const qgemm_handle* h : s->hs) {
+    Plan p = plan_stream(h->NS, h->KB, R, s->cus, s->occ, P);
+    if (p.P != P) *fits = false;
+    p.P = p.V = P;
+    const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW);
+    if (std::min<int64_t>((p.I + P - 1) / P, h->KB) > cap) *fits = false;
+    if (per) per->push_back(p);
+    all = p;
+    Tmax = std::max(Tmax, p.T);
+    slot = std::max(slot, partial_slot_bytes(p.RT, p.NT, p.nwn));
+  }
+  all.P = all.V = P;
+  all.T = Tmax;
+  all.part_bytes = (size_t)(2 * P) * slot;
+  all.cnt_bytes = (size_t)Tmax * 4;
+  return all;
+}
+
+void seq_free(qgemm_seq* s) {
+  for (auto& kv : s->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (s->cap) (void)hipStreamDestroy(s->cap);
+  for (auto& kv : s->descs) (void)hipFree(kv.second);
+  if (s->part) (void)hipFree(s->part);
+  if (s->cnt) (void)hipFree(s->cnt);
+  if (s->sync) (void)hipFree(s->sync);
+  if (s->err) (void)hipFree(s->err);
+}
+
+}  // namespace
 
 extern "C" {
 
-int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count) {
-  if (!out || !handles || count < 1) return QGEMM_EINVAL;
+int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32_t flags) {
+  if (!out || !handles || count < 1 || (flags & ~(uint32_t)QGEMM_SEQ_PERSISTENT)) return QGEMM_EINVAL;
   *out = nullptr;
-  for (int i = 0; i < count; ++i)
+  int max_R = QGEMM_MAX_R;
+  for (int i = 0; i < count; ++i) {
     if (!valid_handle(handles[i])) return QGEMM_EINVAL;
+    max_R = std::min(max_R, handles[i]->max_R);
+  }
   qgemm_seq* s = new (std::nothrow) qgemm_seq{};
   if (!s) return QGEMM_ENOMEM;
   s->magic = SEQ_MAGIC;
+  s->flags = flags;
   s->hs.assign(handles, handles + count);
   if (hipStreamCreateWithFlags(&s->cap, hipStreamNonBlocking) != hipSuccess) {
+    s->cap = nullptr;
     delete s;
     return QGEMM_EHIP;
+  }
+  if (device_cus(&s->cus) != QGEMM_OK) {
+    delete s;
+    return QGEMM_EHIP;
+  }
+  fill_occupancy(s->occ);
+  size_t part = 0, cnt = 0;
+  if (flags & QGEMM_SEQ_PERSISTENT)
+    for (int R = 1; R <= max_R; ++R) {
+      std::vector<Plan> per;
+      bool fits = true;
+      Plan p = plan_seq(s, R, &per, &fits);
+      for (const Plan& pi : per)
+        if (!plan_fits(pi)) fits = false;
+      if (!fits) {
+        (void)hipStreamDestroy(s->cap);
+        delete s;
+        return QGEMM_EPATH;
+      }
+      part = std::max(part, p.part_bytes);
+      cnt = std::max(cnt, p.cnt_bytes);
+    }
+  part = std::max<size_t>(part, 256);
+  cnt = std::max<size_t>(cnt, 256);
+  s->part_bytes = part;
+  s->cnt_bytes = cnt;
+  const size_t sync_bytes = (size_t)(count + 1) * 4;
+  bool ok = hipMalloc(reinterpret_cast<void**>(&s->part), part) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&s->cnt), cnt) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&s->sync), sync_bytes) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&s->err), 4) == hipSuccess &&
+            hipMemset(s->cnt, 0, cnt) == hipSuccess && hipMemset(s->sync, 0, sync_bytes) == hipSuccess &&
+            hipMemset(s->err, 0, 4) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    seq_free(s);
+    delete s;
+    return QGEMM_ENOMEM;
   }
   *out = s;
   return QGEMM_OK;
@@ -343,44 +433,91 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
   }
   if (R == 0) return QGEMM_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  GraphKey key{R, {}};
+  SeqKey key{R, {}};
   for (size_t i = 0; i < s->hs.size(); ++i) {
     key.ptrs.push_back(reinterpret_cast<uintptr_t>(xs[i]));
     key.ptrs.push_back(reinterpret_cast<uintptr_t>(ys[i]));
   }
-  key.ptrs.push_back(reinterpret_cast<uintptr_t>(argmax_idx));
-  auto it = s->graphs.find(key);
-  if (it == s->graphs.end()) {
-    if (hipStreamBeginCapture(s->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return QGEMM_EHIP;
-    int rc = QGEMM_OK;
-    for (size_t i = 0; i < s->hs.size() && rc == QGEMM_OK; ++i)
-      rc = run_impl(s->hs[i], xs[i], ys[i], R, QGEMM_PATH_AUTO, s->cap);
-    if (rc == QGEMM_OK && argmax_idx) {
-      qgemm_handle* last = s->hs.back();
-      if (launch_argmax(ys[s->hs.size() - 1], R, last->N, argmax_idx, s->cap) != hipSuccess) rc = QGEMM_EHIP;
+  if (!(s->flags & QGEMM_SEQ_PERSISTENT)) {
+    // one launch per GEMM, in order, captured once into a graph and replayed
+    key.ptrs.push_back(reinterpret_cast<uintptr_t>(argmax_idx));
+    auto g = s->graphs.find(key);
+    if (g == s->graphs.end()) {
+      if (hipStreamBeginCapture(s->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return QGEMM_EHIP;
+      int rc = QGEMM_OK;
+      for (size_t i = 0; i < s->hs.size() && rc == QGEMM_OK; ++i)
+        rc = run_impl(s->hs[i], xs[i], ys[i], R, QGEMM_PATH_AUTO, s->cap);
+      if (rc == QGEMM_OK && argmax_idx &&
+          launch_argmax(ys[s->hs.size() - 1], R, s->hs.back()->N, argmax_idx, s->cap) != hipSuccess)
+        rc = QGEMM_EHIP;
+      hipGraph_t graph = nullptr;
+      const hipError_t e = hipStreamEndCapture(s->cap, &graph);
+      if (rc != QGEMM_OK || e != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc != QGEMM_OK ? rc : QGEMM_EHIP;
+      }
+      hipGraphExec_t exec = nullptr;
+      const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) return QGEMM_EHIP;
+      g = s->graphs.emplace(key, exec).first;
     }
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(s->cap, &g);
-    if (rc != QGEMM_OK) {
-      if (g) (void)hipGraphDestroy(g);
-      return rc;
-    }
-    if (e != hipSuccess || !g) return QGEMM_EHIP;
-    hipGraphExec_t ex = nullptr;
-    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (e != hipSuccess) return QGEMM_EHIP;
-    it = s->graphs.emplace(key, ex).first;
+    return hipGraphLaunch(g->second, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
   }
-  return hipGraphLaunch(it->second, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+  std::vector<Plan> per;
+  bool fits = true;
+  const Plan p = plan_seq(s, R, &per, &fits);
+  if (!fits) return QGEMM_EPATH;
+  auto it = s->descs.find(key);
+  if (it == s->descs.end()) {
+    std::vector<GemmDesc> host(s->hs.size());
+    for (size_t i = 0; i < s->hs.size(); ++i) host[i] = make_desc(s->hs[i], xs[i], ys[i], per[i]);
+    GemmDesc* dev = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&dev), host.size() * sizeof(GemmDesc)) != hipSuccess) {
+      (void)hipGetLastError();
+      return QGEMM_ENOMEM;
+    }
+    if (hipMemcpy(dev, host.data(), host.size() * sizeof(GemmDesc), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(dev);
+      return QGEMM_EHIP;
+    }
+    it = s->descs.emplace(key, dev).first;
+  }
+  StreamArgs a{};
+  a.descs = it->second;
+  a.part = s->part;
+  a.cnt = s->cnt;
+  a.sync = s->sync;
+  a.err = s->err;
+  a.G = (int32_t)s->hs.size();
+  a.R = R;
+  a.P = (int32_t)p.P;
+  a.RT = p.RT;
+  a.NT = p.NT;
+  a.NW = p.NW;
+  if (launch_stream(a, true, st) != hipSuccess) return QGEMM_EHIP;
+  if (argmax_idx) {
+    const qgemm_handle* last = s->hs.back();
+    if (launch_argmax(ys[s->hs.size() - 1], R, last->N, argmax_idx, st) != hipSuccess) return QGEMM_EHIP;
+  }
+  return QGEMM_OK;
+}
+
+int qgemm_seq_errors(qgemm_seq_t s, uint32_t* timeouts) {
+  if (!s || s->magic != SEQ_MAGIC || !timeouts) return QGEMM_EINVAL;
+  uint32_t v = 0;
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&v, s->err, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(s->err, 0, 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return QGEMM_EHIP;
+  *timeouts = v;
+  return QGEMM_OK;
 }
 
 int qgemm_seq_destroy(qgemm_seq_t s) {
   if (!s) return QGEMM_OK;
   if (s->magic != SEQ_MAGIC) return QGEMM_EINVAL;
   (void)hipDeviceSynchronize();
-  for (auto& kv : s->graphs) (void)hipGraphExecDestroy(kv.second);
-  (void)hipStreamDestroy(s->cap);
+  seq_free(s);
   s->magic = 0;
   delete s;
   return QGEMM_OK;

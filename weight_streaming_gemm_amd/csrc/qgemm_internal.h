@@ -1,33 +1,58 @@
-// qgemm_internal.h — launch wrappers shared by the kernel and API translation
-// units of the library (not part of the C ABI).
+// qgemm_internal.h — kernel arguments and launch wrappers shared by the kernel
+// and API translation units of the library (not part of the C ABI).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qg {
 
-struct StreamArgs {
-  const uint8_t* packed;
-  int64_t hdr_off;       // byte offset of the header region
-  uint32_t quant_bytes;  // sizes of the two regions (< 2^31)
+// One GEMM of a launch: y[R x N] = x[R x K] . W^T over packed weights.
+struct GemmDesc {
+  const uint8_t* packed;   // quant region (quant_bytes), then the header region (hdr_bytes)
+  const uint16_t* x;       // bf16 activations, R x K row-major
+  float* y;                // fp32 outputs, R x N row-major
+  uint32_t quant_bytes;    // < 2^31
   uint32_t hdr_bytes;
-  const void* xq;        // binary16 operand layout (layout.h)
-  const void* xs;        // fp32 sub-block sums
-  float* y;              // output [R][N]
-  float* part;           // partial tiles, 2 per workgroup
-  uint32_t* cnt;         // per tile arrival counters, zero between launches
-  int64_t N, NS;
-  int KB, R;
-  int64_t T;             // tiles of 4 * NT sub-tiles
-  int64_t I;             // T * KB steps
-  int64_t P;             // workgroups (<= I)
-  int RT, NT;
+  int32_t N, NS, KB;       // outputs, 16-output sub-tiles, 256-weight blocks
+  int32_t nwn;             // waves of a workgroup side by side along N (the other
+                           // NW / nwn split each range along K)
+  int32_t T;               // output tiles of nwn * NT sub-tiles
+  int32_t I;               // T * KB (tile, block) steps
+  int32_t V;               // equal contiguous step ranges (P <= V <= I); workgroup p
+                           // takes ranges p, p + P, p + 2P, ...
+  int32_t pad_;
 };
 
+// A launch of the streaming kernel: G GEMMs run one after another (GEMM g + 1
+// starts after every workgroup has finished GEMM g).
+struct StreamArgs {
+  GemmDesc d0;             // the GEMM when G == 1
+  const GemmDesc* descs;   // device array of G GEMMs when G > 1
+  float* part;             // 2 V partial-tile slots of nwn * NT * RT KiB
+  uint32_t* cnt;           // per-tile arrival counters, zero between launches
+  uint32_t* sync;          // G + 1 barrier counters, zero between launches (G > 1)
+  uint32_t* err;           // set to 1 when a barrier wait gave up
+  int32_t G, R, P;
+  int32_t RT, NT, NW;
+};
+
+// Kernel variants: (row tiles RT, sub-tiles per tile NT, waves per workgroup NW).
+// A workgroup (one per CU) holds in LDS the partial tiles of its waves (two per
+// wave) and the activations of the blocks its current range touches, R * 512
+// bytes per block, in what is left of 160 KiB.
+constexpr int LDS_BYTES = 160 * 1024;
+constexpr int LDS_RESERVED = 1024;              // flags and a zero operand
+inline constexpr int piece_bytes(int RT, int NT, int NW) { return NW * 2 * NT * RT * 1024; }
+inline constexpr int x_area_bytes(int RT, int NT, int NW) { return LDS_BYTES - LDS_RESERVED - piece_bytes(RT, NT, NW); }
+inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (R * 512); }
+inline int waves_for(int RT) { return RT <= 2 ? 8 : 4; }
+inline int subtiles_for(int RT) { (void)RT; return 1; }
+inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }
+
 hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K, hipStream_t st);
-hipError_t launch_xprep(const uint16_t* x, void* xq, void* xs, int R, int64_t K, int RT, hipStream_t st);
-hipError_t launch_stream(const StreamArgs& a, hipStream_t st);
-int stream_occupancy(int RT, int NT);   // resident workgroups per CU
+hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
+bool stream_variant_exists(int RT, int NT, int NW);
+int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_argmax(const float* y, int R, int64_t N, int32_t* idx, hipStream_t st);
 

@@ -7,20 +7,21 @@
 //
 //   y[r, n] = sum_k w[n, k] x[r, k],  w[n, k] = d sc_s q_k - dmin m_s
 //
-// computed as, per 256-weight block (d, dmin, sc_s, m_s of output n):
+// computed per 256-weight block (d, dmin, sc_s, m_s of output n) as
 //
-//   y[r, n] += d * sum_k (sc_s q_k) x[r, k]  -  sum_s (dmin m_s) X_s[r]
+//   y[r, n] += d * sum_k (sc_s q_k) x[r, k]  -  dmin * sum_k m_s x[r, k]
 //
-// where X_s[r] is the sum of x[r, k] over sub-block s.  sc_s q_k is an integer
-// <= 945, exact in binary16, so the first sum runs on the fp16 matrix cores
-// (v_mfma_f32_16x16x32_f16, fp32 accumulate) with exact products; dmin m_s is
-// exact in fp32 and the second sum runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32).  x enters the fp16 matrix core as binary16, which
-// holds every bf16 value of magnitude in [2^-17, 65504] exactly.
+// sc_s q_k (<= 945) and m_s (<= 63) are integers, exact in binary16, so both
+// sums run on the fp16 matrix cores (v_mfma_f32_16x16x32_f16) with exact
+// products and fp32 accumulation; d and dmin are applied in fp32 once per
+// block.  x enters the matrix cores as binary16, which holds every bf16 value
+// of magnitude in [2^-17, 65504] exactly.
 //
 // Layouts: layout.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "layout.h"
 #include "operand.h"
@@ -30,8 +31,8 @@
 namespace qg {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ WConst header_consts(u32x4 h, int g) { return header_consts(h.x, h.y, h.z, h.w, g); }
 
@@ -80,273 +81,483 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 activations -> matrix-core operand layout + sub-block sums.
-// One thread per (row tile, block, lane): 64 contiguous x values of its row.
-__global__ void __launch_bounds__(256)
-xprep_kernel(const uint16_t* __restrict__ x, f16x8* __restrict__ xq, f32x2* __restrict__ xs,
-             int R, int64_t K, int64_t KB, int RT) {
-  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t total = (int64_t)RT * KB * 64;
-  if (tid >= total) return;
-  int lane = (int)(tid & 63);
-  int64_t rj = tid >> 6;               // rt * KB + j
-  int rt = (int)(rj / KB);
-  int64_t j = rj % KB;
-  int g = lane >> 4, rr = lane & 15;
-  int r = rt * 16 + rr;
-  float vals[64];
-  if (r < R) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)r * K + j * SB_W + 64 * g);
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = src[i];
-      for (int b = 0; b < 4; ++b) {
-        vals[8 * i + 2 * b] = bitcast<float>(v[b] << 16);
-        vals[8 * i + 2 * b + 1] = bitcast<float>(v[b] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    for (int i = 0; i < 64; ++i) vals[i] = 0.0f;
-  }
-  // vals[32 hbit + c] = x[r, 256 j + 64 g + 32 hbit + c]
-  for (int t = 0; t < 8; ++t) {
-    f16x8 o;
-    for (int e = 0; e < 8; ++e) o[e] = (_Float16)vals[32 * (e & 1) + 4 * t + (e >> 1)];
-    xq[(rj * 8 + t) * 64 + lane] = o;
-  }
-  float s0 = 0.0f, s1 = 0.0f;
-  for (int c = 0; c < 32; ++c) s0 += vals[c];
-  for (int c = 0; c < 32; ++c) s1 += vals[32 + c];
-  xs[rj * 64 + lane] = f32x2{s0, s1};
-}
 
 // ---------------------------------------------------------------------------
-// Matrix-core streaming GEMM (stream-K over the whole matrix).
+// The streaming kernel.
 //
-// Work: a tile is 4 waves x NT sub-tiles x 16 outputs; tile t needs KB block
-// steps.  The T*KB (tile, block) steps are cut into P equal contiguous ranges,
-// one per workgroup, so every CU gets the same number of bytes to stream
-// whatever the shape.  A range that starts or ends inside a tile leaves a
-// partial result; the last workgroup to finish a tile sums its partials in
-// workgroup order (fixed: results are deterministic) with no waiting.
+// Work.  The NW waves of a workgroup form an nwn x (NW / nwn) grid: nwn side by
+// side along N, NW / nwn along K (nwn is chosen per GEMM).  A tile is nwn * NT
+// 16-output sub-tiles; tile t needs KB block steps.  The T * KB (tile, block)
+// steps of a GEMM are cut into V equal contiguous ranges; workgroup p (one per
+// CU) takes ranges p, p + P, ..., so every CU streams the same number of bytes
+// whatever the matrix shape.  Inside a range, each row of nwn waves takes an
+// equal contiguous sub-range, each wave its NT sub-tiles of every tile.
 //
-// Per block step each wave reads, for each of its NT sub-tiles, one 2 KiB
-// quant chunk and its outputs' 16-byte headers (raw buffer loads, streaming
-// hint), three steps deep in a register ring; the x operands of the step are
-// shared by the four waves through a two-slot LDS ring.  Loads past the end of
-// a range address beyond the buffer's size and return zeros without memory
-// traffic, so the tail needs no branches.
-constexpr int NWAVE = 4;
-constexpr uint32_t OOB = 0x80000000u;   // beyond every buffer (sizes < 2^31)
+// Sums.  A wave writes a tile it covers alone straight to y.  The pieces of a
+// tile shared by several waves meet in LDS and are added, after the range, in
+// wave order.  A tile shared with other ranges leaves the workgroup's sum in a
+// global partial slot; the last range to finish the tile adds the slots in
+// range order.  Every sum has a fixed order, so results are deterministic.
+//
+// Streams.  At the start of a range the workgroup converts the activations of
+// the blocks the range touches (R rows x 256 bf16 each) into the matrix-core
+// operand layout in LDS; the steps then read only weights from memory: per
+// step and sub-tile the 2 KiB quant chunk and the outputs' 16-byte headers,
+// with raw buffer loads (streaming hint), RING steps ahead in a register ring
+// (each slot refilled right after its step), across range and GEMM ends.
+// Loads past the end of the work address beyond the buffer and return zeros
+// without memory traffic.
+//
+// With G > 1 all workgroups are resident (cooperative launch) and GEMM g + 1
+// starts only after every workgroup has finished GEMM g, as in a model where
+// each projection's input depends on the previous output; the weights of the
+// next GEMM are already in flight while a workgroup waits.
+constexpr int RING = 4;                        // weight ring depth, steps
+constexpr uint32_t OOB = 0x80000000u;          // beyond every buffer (sizes < 2^31)
+constexpr uint32_t SPIN_LIMIT = 1u << 21;      // barrier polls before giving up
+constexpr int SC1 = 16;                        // cache policy: coherent across the device
 
 // aux 2 = streaming (non-temporal) hint for data read once; 0 for shared data
 template <class T, int AUX>
 __device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX));
 }
+__device__ __forceinline__ void bstore_sc1(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, SC1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// the value of the first active lane: for values that are uniform by
+// construction, so that the compiler keeps them (and branches on them) scalar
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <int NT>
 struct WStage {
   u32x4 qa[NT], qb[NT], hd[NT];
 };
 
-template <int RT, int NT>
-__global__ void __launch_bounds__(256)
-stream_kernel(StreamArgs a) {
-  __shared__ u32x4 xl[2][RT][8 * 64];
-  __shared__ u32x4 xsl[2][RT][32];
-  __shared__ uint32_t s_last;
+// where a wave stands in its sequence of steps (uniform across the wave)
+struct Cursor {
+  int g;          // GEMM index; >= G when past the end
+  int v;          // range index
+  int A, B;       // the range's steps
+  int it, it1;    // current step and end of this wave's sub-range
+  int t, j;       // tile and block of step it
+  int KB, NS, I, V;
+  int nwn, wn, wk, nwk;            // wave grid of GEMM g and this wave's place in it
+  __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions of GEMM g (load cursor)
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, nl = lane & 15;
-  const int64_t p = blockIdx.x;
-  const int64_t I = a.I;
-  const int64_t it0 = range_first(p, a.P, I), it1 = range_first(p + 1, a.P, I);
-  const int KB = a.KB;
+template <int RT, int NT, int NW, bool MULTI>
+__global__ void __launch_bounds__(NW * 64, NW / 4)
+stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
+  constexpr int NTHR = NW * 64;
+  constexpr int XAREA = x_area_bytes(RT, NT, NW);
+  constexpr int XZERO = XAREA;                    // 16 zero bytes: the operand of rows >= R
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[XAREA + 16];
+  __shared__ f32x4 pieces[NW * 2 * NT * RT * 64];
+  __shared__ uint32_t s_flag;
 
-  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)a.packed, 0, (int)a.quant_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.packed + a.hdr_off), 0, (int)a.hdr_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, (int)(RT * KB * 8192), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xsr = __builtin_amdgcn_make_buffer_rsrc((void*)a.xs, 0, (int)(RT * KB * 512), 0x00020000);
+  const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
+  const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
+  const int SB = R * 512;                         // LDS bytes of one block's activations
 
-  // (tile, block) of the current step and the two steps ahead
-  int64_t t_c = it0 / KB;
-  int j_c = (int)(it0 - t_c * KB);
-  const int j_first = j_c;
-
-  auto load_w = [&](WStage<NT>& st, int64_t it, int64_t t, int j) {
-    for (int u = 0; u < NT; ++u) {
-      int64_t ns = (t * NWAVE + w) * NT + u;
-      bool ok = it < it1 && ns < a.NS;
-      uint32_t qo = ok ? (uint32_t)((ns * KB + j) * CHUNK_Q) + lane * 16 : OOB;
-      uint32_t ho = ok ? (uint32_t)((ns * KB + j) * CHUNK_H) + nl * 16 : OOB;
-      st.qa[u] = bload<u32x4, 2>(qr, qo);
-      st.qb[u] = bload<u32x4, 2>(qr, qo + 1024);
-      st.hd[u] = bload<u32x4, 2>(hr, ho);
+  // descriptor of GEMM g; fields of the device table are made explicitly
+  // wave-uniform so that buffer resources built from them stay scalar
+  auto get_desc = [&](int g) __attribute__((always_inline)) -> GemmDesc {
+    if constexpr (MULTI) {
+      typedef const GemmDesc __attribute__((address_space(4)))* const_desc_ptr;
+      const const_desc_ptr src = (const_desc_ptr)(descs + g);
+      GemmDesc d;
+      d.packed = uniform_ptr(src->packed);
+      d.x = uniform_ptr(src->x);
+      d.y = uniform_ptr(src->y);
+      d.quant_bytes = (uint32_t)uni((int)src->quant_bytes);
+      d.hdr_bytes = (uint32_t)uni((int)src->hdr_bytes);
+      d.N = uni(src->N);
+      d.NS = uni(src->NS);
+      d.KB = uni(src->KB);
+      d.nwn = uni(src->nwn);
+      d.T = uni(src->T);
+      d.I = uni(src->I);
+      d.V = uni(src->V);
+      return d;
+    } else {
+      return a.d0;
     }
   };
-  u32x4 xv[RT][2], xsv_g[RT];
-  auto load_x = [&](int64_t it, int j) {
-    bool ok = it < it1;
-    for (int rt = 0; rt < RT; ++rt) {
-      uint32_t base = (uint32_t)((rt * KB + j) * 8192);
-      xv[rt][0] = bload<u32x4, 0>(xr, ok ? base + tid * 16 : OOB);
-      xv[rt][1] = bload<u32x4, 0>(xr, ok ? base + 4096 + tid * 16 : OOB);
-      xsv_g[rt] = bload<u32x4, 0>(xsr, (ok && tid < 32) ? (uint32_t)((rt * KB + j) * 512) + tid * 16 : OOB);
-    }
+  // range v of the cursor's GEMM and this wave's sub-range of it
+  auto set_range = [&](Cursor& c) __attribute__((always_inline)) {
+    c.A = uni((int)range_first<uint32_t>(c.v, c.V, c.I));
+    c.B = uni((int)range_first<uint32_t>(c.v + 1, c.V, c.I));
+    c.it = uni(c.A + (int)range_first<uint32_t>(c.wk, c.nwk, c.B - c.A));
+    c.it1 = uni(c.A + (int)range_first<uint32_t>(c.wk + 1, c.nwk, c.B - c.A));
+    c.t = uni(c.it / c.KB);
+    c.j = uni(c.it - c.t * c.KB);
   };
-  auto store_x = [&](int slot) {
-    for (int rt = 0; rt < RT; ++rt) {
-      xl[slot][rt][tid] = xv[rt][0];
-      xl[slot][rt][256 + tid] = xv[rt][1];
-      if (tid < 32) xsl[slot][rt][tid] = xsv_g[rt];
-    }
-  };
-
-  f32x4 acc[NT][RT], macc[NT][RT];
-  auto zero_acc = [&]() {
-    for (int u = 0; u < NT; ++u)
-      for (int rt = 0; rt < RT; ++rt) {
-        acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        macc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-  };
-  zero_acc();
-
-  auto advance = [](int64_t& t, int& j, int KB_) {
-    if (++j == KB_) { j = 0; ++t; }
-  };
-
-  // prologue: x of step it0 into slot 0; weights of it0, it0+1; x of it0+1 in flight
-  int64_t t_n1 = t_c, t_n2;
-  int j_n1 = j_c, j_n2;
-  advance(t_n1, j_n1, KB);
-  t_n2 = t_n1; j_n2 = j_n1;
-  advance(t_n2, j_n2, KB);
-  load_x(it0, j_c);
-  store_x(0);
-  WStage<NT> W0, W1, W2;
-  load_w(W0, it0, t_c, j_c);
-  load_w(W1, it0 + 1, t_n1, j_n1);
-  load_x(it0 + 1, j_n1);
-  __syncthreads();
-
-  int64_t it = it0;
-  int slot = 0;
-
-  auto finish_segment = [&](int64_t t, int ja) {
-    // segment [ja, j_c] of tile t is complete
-    const bool full = (ja == 0) && (j_c == KB - 1);
-    if (full) {
-      for (int u = 0; u < NT; ++u) {
-        int64_t n = ((t * NWAVE + w) * NT + u) * TILE_N + nl;
-        if (n >= a.N) continue;
-        for (int rt = 0; rt < RT; ++rt)
-          for (int i = 0; i < 4; ++i) {
-            int r = rt * 16 + 4 * g + i;
-            if (r < a.R) a.y[(int64_t)r * a.N + n] = acc[u][rt][i] + macc[u][rt][i];
-          }
-      }
+  auto enter = [&](Cursor& c, int g) __attribute__((always_inline)) {
+    c.g = g;
+    if (g >= G) {
+      c.v = 0; c.V = 1; c.A = c.B = 0;
+      c.it = 1; c.it1 = 0;
+      c.t = 0; c.j = 0; c.KB = 1; c.NS = 0; c.I = 0;
+      c.nwn = 1; c.wn = 0; c.wk = w; c.nwk = NW;
+      c.qr = make_rsrc(nullptr, 0);
+      c.hr = make_rsrc(nullptr, 0);
       return;
     }
-    const int64_t pslot = partial_slot(p, t, KB, a.P, I);
-    float* dst = a.part + (pslot * NWAVE + w) * (NT * RT * 256);
+    const GemmDesc d = get_desc(g);
+    c.v = p;
+    c.V = d.V;
+    c.KB = d.KB;
+    c.NS = d.NS;
+    c.I = d.I;
+    c.nwn = d.nwn;
+    c.nwk = uni(NW / d.nwn);
+    c.wn = uni(w % d.nwn);
+    c.wk = uni(w / d.nwn);
+    c.qr = make_rsrc(d.packed, d.quant_bytes);
+    c.hr = make_rsrc(d.packed + d.quant_bytes, d.hdr_bytes);
+    set_range(c);
+  };
+  // the load cursor's next step: within the sub-range, else this wave's
+  // sub-range of the workgroup's next range (skipping empty ones), else the
+  // next GEMM's first range (p < P <= V, so it exists)
+  auto next = [&](Cursor& c) __attribute__((always_inline)) {
+    c.it = uni(c.it + 1);
+    c.j = uni(c.j + 1);
+    if (c.j == c.KB) { c.j = 0; c.t = uni(c.t + 1); }
+  };
+
+  // ---- weights: RING steps ahead -----------------------------------------------
+  auto load_w = [&](WStage<NT>& st, const Cursor& c) __attribute__((always_inline)) {
+    for (int u = 0; u < NT; ++u) {
+      const int ns = (c.t * c.nwn + c.wn) * NT + u;
+      const bool ok = c.it < c.it1 && ns < c.NS;
+      const uint32_t qo = ok ? (uint32_t)(ns * c.KB + c.j) * CHUNK_Q + lane * 16 : OOB;
+      const uint32_t ho = ok ? (uint32_t)(ns * c.KB + c.j) * CHUNK_H + nl * 16 : OOB;
+      st.qa[u] = bload<u32x4, 2>(c.qr, qo);
+      st.qb[u] = bload<u32x4, 2>(c.qr, qo + 1024);
+      st.hd[u] = bload<u32x4, 2>(c.hr, ho);
+    }
+  };
+
+  // ---- activations of a range: block j = (j0 + b) mod KB goes to slot b; row r
+  // of slot b, lane group gg, step t is the A operand of lane 16 gg + r % 16 of
+  // row tile r / 16, built from x[r, 256 j + 64 gg + 4 t + {0..3}] and the same
+  // 32 further on.  32 threads per (slot, row); XB rows in flight per thread. ---
+  auto convert_x = [&](const GemmDesc& d, int j0, int nslots) __attribute__((always_inline)) {
+    constexpr int GROUPS = NTHR / 32, XB = 8;
+    const int sub = tid & 31, gg = sub >> 3, t = sub & 7;
+    const int K = d.KB * SB_W;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
+    const int rows = nslots * R;
+    for (int base = tid >> 5; base < rows; base += XB * GROUPS) {
+      u32x2 lo[XB], hi[XB];
+      for (int k = 0; k < XB; ++k) {
+        const int rb = base + k * GROUPS;
+        const int b = rb / R, r = rb - b * R;
+        int j = j0 + b;
+        if (j >= d.KB) j -= d.KB;
+        const uint32_t off = (uint32_t)((r * K + j * SB_W + 64 * gg + 4 * t) * 2);
+        lo[k] = bload<u32x2, 0>(xr, rb < rows ? off : OOB);
+        hi[k] = bload<u32x2, 0>(xr, rb < rows ? off + 64 : OOB);
+      }
+      for (int k = 0; k < XB; ++k) {
+        const int rb = base + k * GROUPS;
+        if (rb >= rows) break;
+        const int b = rb / R, r = rb - b * R;
+        *reinterpret_cast<f16x8*>(xlds + b * SB + ((t * 4 + gg) * R + r) * 16) =
+            build_a(lo[k].x, lo[k].y, hi[k].x, hi[k].y);
+      }
+    }
+  };
+  // this lane's A-operand offsets inside a slot, per row tile (-1: row >= R)
+  int xoff[RT];
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + nl;
+    xoff[rt] = (r < R) ? (g4 * R + r) * 16 : -1;
+  }
+
+  f32x4 acc[NT][RT];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+    for (int u = 0; u < NT; ++u)
+      for (int rt = 0; rt < RT; ++rt) acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto compute = [&](const WStage<NT>& st, int slot) __attribute__((always_inline)) {
+    WConst c[NT];
+    f16x8 bm[NT];
+    f32x4 ds[NT][RT], ms[NT][RT];
+    for (int u = 0; u < NT; ++u) {
+      c[u] = header_consts(st.hd[u], g4);
+      bm[u] = build_m(c[u]);
+      for (int rt = 0; rt < RT; ++rt) {
+        ds[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ms[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const int base = slot * SB;
+    for (int t = 0; t < 8; ++t) {
+      f16x8 xa[RT];
+      for (int rt = 0; rt < RT; ++rt) {
+        const int addr = xoff[rt] >= 0 ? base + t * 64 * R + xoff[rt] : XZERO;
+        xa[rt] = *reinterpret_cast<const f16x8*>(xlds + addr);
+      }
+      for (int u = 0; u < NT; ++u) {
+        const uint32_t wd = (t < 4) ? st.qa[u][t] : st.qb[u][t - 4];
+        const f16x8 b = build_b(wd, c[u]);
+        for (int rt = 0; rt < RT; ++rt) {
+          ds[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[u][rt], 0, 0, 0);
+          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], bm[u], ms[u][rt], 0, 0, 0);
+        }
+      }
+    }
+    // acc += d * ds - dmin * ms, two fused multiply-adds per element
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt)
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(dst + ((u * RT + rt) * 4 + i) * 64 + lane, acc[u][rt][i] + macc[u][rt][i],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // workgroups that hold a piece of tile t: those containing steps tKB .. tKB+KB-1
-    const int64_t q_lo = tile_first_owner(t, KB, a.P, I);
-    const int64_t q_hi = tile_last_owner(t, KB, a.P, I);
-    if (tid == 0) {
-      uint32_t prev = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == (uint32_t)(q_hi - q_lo)) ? 1u : 0u;
+        for (int i = 0; i < 4; ++i) {
+          acc[u][rt][i] = __builtin_fmaf(c[u].d, ds[u][rt][i], acc[u][rt][i]);
+          acc[u][rt][i] = __builtin_fmaf(c[u].nmin, ms[u][rt][i], acc[u][rt][i]);
+        }
+  };
+
+  // ---- outputs ------------------------------------------------------------------
+  // sub-tiles (t * nwn + wn) * NT + u of tile t belong to the waves of column wn
+  auto write_y = [&](const GemmDesc& d, int t, int wn, const f32x4 (&v)[NT][RT]) __attribute__((always_inline)) {
+    for (int u = 0; u < NT; ++u) {
+      const int n = ((t * d.nwn + wn) * NT + u) * TILE_N + nl;
+      if (n >= d.N) continue;
+      for (int rt = 0; rt < RT; ++rt)
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * g4 + i;
+          if (r < R) d.y[(int64_t)r * d.N + n] = v[u][rt][i];
+        }
     }
-    __syncthreads();
-    if (!s_last) return;
+  };
+  // LDS piece (sub-range wk, slot sl, column wn): one per wave and slot
+  auto piece_at = [&](int nwn, int wk, int sl, int wn, int u, int rt) __attribute__((always_inline)) -> f32x4& {
+    return pieces[(((((wk * 2 + sl) * nwn + wn) * NT + u) * RT + rt) * 64) + lane];
+  };
+  // a wave's segment of tile C.t ends: y if it covers the tile, else a piece in
+  // LDS slot 0 (the segment starts inside the tile) or 1
+  auto finish_segment = [&](const Cursor& c, const GemmDesc& d, int ja, int a_w) __attribute__((always_inline)) {
+    if (ja == 0 && c.j == c.KB - 1) {
+      write_y(d, c.t, c.wn, acc);
+      return;
+    }
+    const int sl = (a_w > c.t * c.KB) ? 0 : 1;
+    for (int u = 0; u < NT; ++u)
+      for (int rt = 0; rt < RT; ++rt) piece_at(c.nwn, c.wk, sl, c.wn, u, rt) = acc[u][rt];
+  };
+
+  // the partial slots of the current GEMM: 2 V of nwn * NT * RT KiB
+  auto part_rsrc = [&](const Cursor& c) __attribute__((always_inline)) {
+    return make_rsrc(a.part, (uint32_t)(2 * c.V * c.nwn * NT * RT * 1024));
+  };
+  auto gslot_off = [&](const Cursor& c, int slot, int wn, int u, int rt) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(((((slot * c.nwn + wn) * NT + u) * RT + rt) * 64 + lane) * 16);
+  };
+  // the last range to arrive at tile t adds the tile's global partial slots in
+  // range order and writes y (column wn of the tile)
+  auto global_fixup = [&](const Cursor& c, const GemmDesc& d, int t, int wn) __attribute__((always_inline)) {
+    const int q_lo = (int)tile_first_owner<uint32_t>(t, c.KB, c.V, c.I);
+    const int q_hi = (int)tile_last_owner<uint32_t>(t, c.KB, c.V, c.I);
+    const __amdgpu_buffer_rsrc_t pr = part_rsrc(c);
     f32x4 sum[NT][RT];
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt) sum[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t q = q_lo; q <= q_hi; ++q) {
-      const int64_t qslot = partial_slot(q, t, KB, a.P, I);
-      const float* src = a.part + (qslot * NWAVE + w) * (NT * RT * 256);
+    for (int q = q_lo; q <= q_hi; ++q) {
+      const int qs = (int)partial_slot<uint32_t>(q, t, c.KB, c.V, c.I);
       for (int u = 0; u < NT; ++u)
-        for (int rt = 0; rt < RT; ++rt)
-          for (int i = 0; i < 4; ++i)
-            sum[u][rt][i] += __hip_atomic_load(src + ((u * RT + rt) * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int rt = 0; rt < RT; ++rt) sum[u][rt] += bload<f32x4, SC1>(pr, gslot_off(c, qs, wn, u, rt));
     }
-    for (int u = 0; u < NT; ++u) {
-      int64_t n = ((t * NWAVE + w) * NT + u) * TILE_N + nl;
-      if (n >= a.N) continue;
-      for (int rt = 0; rt < RT; ++rt)
-        for (int i = 0; i < 4; ++i) {
-          int r = rt * 16 + 4 * g + i;
-          if (r < a.R) a.y[(int64_t)r * a.N + n] = sum[u][rt][i];
+    write_y(d, t, wn, sum);
+  };
+
+  // ---- end of a range: add the pieces of shared tiles (sub-range order), then
+  // the tiles shared with other ranges (range order) ------------------------------
+  auto close_range = [&](const Cursor& c, const GemmDesc& d) __attribute__((always_inline)) {
+    __syncthreads();                              // every piece is in LDS
+    const int A = c.A, B = c.B, KB = c.KB, L = B - A, nwn = c.nwn, nwk = c.nwk;
+    const int tA = A / KB, tB = (B - 1) / KB;
+    const bool cross_a = tA * KB < A, cross_b = (tB + 1) * KB > B;
+    // (tile, column) pairs, spread over the waves
+    for (int pi = w; pi < (tB - tA + 1) * nwn; pi += NW) {
+      const int t = tA + pi / nwn, wn = pi % nwn;
+      const int s0 = (t * KB > A ? t * KB : A) - A;                   // the tile's steps in the range,
+      const int s1 = ((t + 1) * KB < B ? (t + 1) * KB : B) - A;       // local [s0, s1)
+      const int k_lo = (int)range_owner<uint32_t>(s0, nwk, L);
+      const int k_hi = (int)range_owner<uint32_t>(s1 - 1, nwk, L);
+      const bool crossing = (t == tA && cross_a) || (t == tB && cross_b);
+      if (k_lo == k_hi && !crossing) continue;    // one sub-range covered it: already in y
+      f32x4 sum[NT][RT];
+      for (int u = 0; u < NT; ++u)
+        for (int rt = 0; rt < RT; ++rt) sum[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = k_lo; kk <= k_hi; ++kk) {
+        const int a_k = A + (int)range_first<uint32_t>(kk, nwk, L);
+        const int b_k = A + (int)range_first<uint32_t>(kk + 1, nwk, L);
+        if (a_k == b_k) continue;                 // an empty sub-range holds no piece
+        const int sl = (a_k > t * KB) ? 0 : 1;
+        for (int u = 0; u < NT; ++u)
+          for (int rt = 0; rt < RT; ++rt) sum[u][rt] += piece_at(nwn, kk, sl, wn, u, rt);
+      }
+      if (!crossing) {
+        write_y(d, t, wn, sum);
+      } else {
+        const int gs = (int)partial_slot<uint32_t>(c.v, t, KB, c.V, c.I);
+        const __amdgpu_buffer_rsrc_t pr = part_rsrc(c);
+        for (int u = 0; u < NT; ++u)
+          for (int rt = 0; rt < RT; ++rt) bstore_sc1(sum[u][rt], pr, gslot_off(c, gs, wn, u, rt));
+      }
+    }
+    if (cross_a || cross_b) {
+      __builtin_amdgcn_s_waitcnt(0);              // this thread's partial stores are complete
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t last = 0;
+        if (cross_a) {
+          const uint32_t owners = tile_last_owner<uint32_t>(tA, KB, c.V, c.I) - tile_first_owner<uint32_t>(tA, KB, c.V, c.I);
+          if (__hip_atomic_fetch_add(a.cnt + tA, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == owners) last |= 1u;
         }
-    }
-    if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-
-  auto compute = [&](const WStage<NT>& st) {
-    f16x8 xa[RT][8];
-    f32x2 xs2[RT];
-    for (int rt = 0; rt < RT; ++rt) {
-      for (int t = 0; t < 8; ++t) xa[rt][t] = __builtin_bit_cast(f16x8, xl[slot][rt][t * 64 + lane]);
-      xs2[rt] = reinterpret_cast<const f32x2*>(&xsl[slot][rt][0])[lane];
-    }
-    for (int u = 0; u < NT; ++u) {
-      WConst c = header_consts(st.hd[u], g);
-      f32x4 dsum[RT];
-      for (int rt = 0; rt < RT; ++rt) dsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int t = 0; t < 8; ++t) {
-        uint32_t wd = (t < 4) ? st.qa[u][t] : st.qb[u][t - 4];
-        f16x8 b = build_b(wd, c);
-        for (int rt = 0; rt < RT; ++rt)
-          dsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt][t], b, dsum[rt], 0, 0, 0);
+        if (cross_b && !(cross_a && tB == tA)) {
+          const uint32_t owners = tile_last_owner<uint32_t>(tB, KB, c.V, c.I) - tile_first_owner<uint32_t>(tB, KB, c.V, c.I);
+          if (__hip_atomic_fetch_add(a.cnt + tB, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == owners) last |= 2u;
+        }
+        s_flag = last;
       }
-      for (int rt = 0; rt < RT; ++rt) {
-        acc[u][rt] += c.d * dsum[rt];
-        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs2[rt][0], c.bm0, macc[u][rt], 0, 0, 0);
-        macc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs2[rt][1], c.bm1, macc[u][rt], 0, 0, 0);
+      __syncthreads();
+      const uint32_t last = s_flag;
+      // the waves of the first nwn columns add the tile's slots (column w)
+      if (w < nwn) {
+        if (last & 1u) global_fixup(c, d, tA, w);
+        if (last & 2u) global_fixup(c, d, tB, w);
+      }
+      // re-arm the counters for the next launch, after every column has read
+      __syncthreads();
+      if (tid == 0) {
+        if (last & 1u) __hip_atomic_store(a.cnt + tA, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last & 2u) __hip_atomic_store(a.cnt + tB, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    __syncthreads();                              // pieces and activations may be reused
   };
 
-  int ja = j_first;   // first block of the current segment
-  // one step: prefetch weights two steps ahead into `ahead`, compute `cur`,
-  // stage the next step's x into the other LDS slot, then close the segment if
-  // the step ends a tile or the range
-  auto step = [&](WStage<NT>& cur, WStage<NT>& ahead) -> bool {
-    load_w(ahead, it + 2, t_n2, j_n2);
-    compute(cur);
-    store_x(slot ^ 1);
-    int64_t t_n3 = t_n2;
-    int j_n3 = j_n2;
-    advance(t_n3, j_n3, KB);
-    load_x(it + 2, j_n2);
+  // ---- all workgroups finished GEMM g (bounded wait; a timeout sets err) -----
+  auto grid_barrier = [&](int g) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool last = (it + 1 == it1);
-    if (j_c == KB - 1 || last) {
-      finish_segment(t_c, ja);
+    if (tid == 0) {
+      __hip_atomic_fetch_add(a.sync + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t n = 0;
+      while (__hip_atomic_load(a.sync + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)P) {
+        if (++n > SPIN_LIMIT) {
+          __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- prologue: the load cursor starts RING steps ahead -------------------------
+  if (tid == 0) *reinterpret_cast<u32x4*>(xlds + XZERO) = u32x4{0u, 0u, 0u, 0u};
+  Cursor L, C;
+  enter(L, 0);
+  C = L;
+  WStage<NT> W[RING];
+  for (int s = 0; s < RING; ++s) {
+    load_w(W[s], L);
+    next(L);
+  }
+  GemmDesc D = get_desc(0);
+  int xs = 0;                                     // activation slot of C's step
+  int ja = 0;                                     // first block of the current segment
+  int a_w = 0;                                    // first step of this wave's sub-range
+
+  // one step at ring position s; true at the end of this wave's sub-range
+  auto step = [&](auto S) __attribute__((always_inline)) -> bool {
+    constexpr int s = decltype(S)::value;
+    compute(W[s], xs);
+    load_w(W[s], L);                              // the slot takes the step RING ahead
+    next(L);
+    const bool tile_end = C.j == C.KB - 1;
+    const bool sub_end = C.it + 1 == C.it1;
+    if (tile_end || sub_end) {
+      finish_segment(C, D, ja, a_w);
       zero_acc();
       ja = 0;
     }
-    ++it;
-    slot ^= 1;
-    t_c = t_n1; j_c = j_n1;
-    t_n1 = t_n2; j_n1 = j_n2;
-    t_n2 = t_n3; j_n2 = j_n3;
-    return !last;
+    if (sub_end) return true;
+    C.it = uni(C.it + 1);
+    C.j = uni(C.j + 1);
+    if (C.j == C.KB) { C.j = 0; C.t = uni(C.t + 1); }
+    xs = uni(xs + 1);
+    if (xs == C.KB) xs = 0;
+    return false;
   };
+  static_assert(RING == 4, "the loop below unrolls RING steps");
 
-  while (it < it1) {
-    if (!step(W0, W2)) break;
-    if (!step(W1, W0)) break;
-    if (!step(W2, W1)) break;
+  // One range per workgroup and GEMM (the host sizes V = P): the ring keeps its
+  // position from one GEMM to the next only through a full drain, so each wave
+  // starts every GEMM at ring position 0.
+  for (;;) {
+    convert_x(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB));
+    __syncthreads();
+    if (C.it < C.it1) {
+      xs = uni((C.it - C.A) % C.KB);
+      ja = C.j;
+      a_w = C.it;
+      zero_acc();
+      for (;;) {
+        if (step(std::integral_constant<int, 0>{})) break;
+        if (step(std::integral_constant<int, 1>{})) break;
+        if (step(std::integral_constant<int, 2>{})) break;
+        if (step(std::integral_constant<int, 3>{})) break;
+      }
+    }
+    close_range(C, D);
+    if constexpr (!MULTI) {
+      break;
+    } else {
+      if (C.g + 1 >= G) break;
+      grid_barrier(C.g);
+      enter(C, C.g + 1);
+      D = get_desc(C.g);
+      // the load cursor stopped at the end of this wave's sub-range: refill
+      L = C;
+      for (int s = 0; s < RING; ++s) {
+        load_w(W[s], L);
+        next(L);
+      }
+    }
+  }
+
+  if constexpr (MULTI) {
+    // the last workgroup out re-arms the barrier counters for the next launch
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(a.sync + G, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = (prev == (uint32_t)P - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_flag)
+      for (int i = tid; i <= G; i += NTHR) __hip_atomic_store(a.sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -428,36 +639,47 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_xprep(const uint16_t* x, void* xq, void* xs, int R, int64_t K, int RT, hipStream_t st) {
-  int64_t KB = K / SB_W;
-  int64_t total = (int64_t)RT * KB * 64;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(xprep_kernel, dim3(blocks_for(total, 256)), dim3(256), 0, st, x,
-                     reinterpret_cast<f16x8*>(xq), reinterpret_cast<f32x2*>(xs), R, K, KB, RT);
-  return hipGetLastError();
+#define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(1, 1, 12) X(2, 1, 8) X(3, 1, 4) X(4, 1, 4)
+
+template <int RT, int NT, int NW>
+static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
+  if (a.G == 1 && !cooperative) {
+    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, false>), dim3((unsigned)a.P), dim3(NW * 64), 0, st, a,
+                       (const GemmDesc*)nullptr);
+    return hipGetLastError();
+  }
+  StreamArgs args = a;
+  const GemmDesc* descs = a.descs;
+  void* params[] = {&args, &descs};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true>),
+                                    dim3((unsigned)a.P), dim3(NW * 64), params, 0, st);
 }
 
-template <int RT, int NT>
-static hipError_t launch_stream_t(const StreamArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((stream_kernel<RT, NT>), dim3((unsigned)a.P), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-#define QG_STREAM_VARIANTS(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(3, 1) X(4, 1)
-
-hipError_t launch_stream(const StreamArgs& a, hipStream_t st) {
-#define QG_CASE(rt, nt) \
-  if (a.RT == rt && a.NT == nt) return launch_stream_t<rt, nt>(a, st);
+hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st) {
+#define QG_CASE(rt, nt, nw) \
+  if (a.RT == rt && a.NT == nt && a.NW == nw) return launch_stream_t<rt, nt, nw>(a, cooperative, st);
   QG_STREAM_VARIANTS(QG_CASE)
 #undef QG_CASE
   return hipErrorInvalidValue;
 }
 
-int stream_occupancy(int RT, int NT) {
+bool stream_variant_exists(int RT, int NT, int NW) {
+#define QG_CASE(rt, nt, nw) \
+  if (RT == rt && NT == nt && NW == nw) return true;
+  QG_STREAM_VARIANTS(QG_CASE)
+#undef QG_CASE
+  return false;
+}
+
+// resident workgroups per CU of the multi-GEMM variant (the single-GEMM
+// variant has the same LDS footprint)
+int stream_occupancy(int RT, int NT, int NW) {
   int blocks = 0;
-#define QG_CASE(rt, nt) \
-  if (RT == rt && NT == nt) { \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt>, 256, 0) != hipSuccess) return 0; \
+#define QG_CASE(rt, nt, nw) \
+  if (RT == rt && NT == nt && NW == nw) { \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true>, nw * 64, 0) != \
+        hipSuccess) \
+      return 0; \
     return blocks; \
   }
   QG_STREAM_VARIANTS(QG_CASE)

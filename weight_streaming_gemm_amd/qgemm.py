@@ -16,14 +16,14 @@ LIB_PATH = os.path.join(HERE, "libqgemm.so")
 QGEMM_OK, QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN = 0, -1, -2, -3
 QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH = -4, -5, -6, -7
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+SEQ_PERSISTENT = 1
 MAX_R = 64
 
 # every symbol include/qgemm.h declares
 EXPORTS = (
     "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
-    "qgemm_stage", "qgemm_multiply",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_query", "qgemm_destroy",
-    "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_destroy", "qgemm_status_string",
+    "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_errors", "qgemm_seq_destroy", "qgemm_status_string",
 )
 
 
@@ -36,7 +36,8 @@ class QGemmError(RuntimeError):
 class Info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("row_tiles", ctypes.c_int), ("subtiles_per_wave", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("steps", ctypes.c_int64),
-                ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("ranges", ctypes.c_int64),
+                ("waves_per_workgroup", ctypes.c_int), ("wave_columns", ctypes.c_int)]
 
 
 _lib = None
@@ -57,14 +58,13 @@ def lib():
             "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
             "qgemm_run": [vp, vp, vp, i32, vp],
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
-            "qgemm_stage": [vp, vp, i32, vp],
-            "qgemm_multiply": [vp, vp, i32, i32, vp],
             "qgemm_dequantize": [vp, vp, vp],
             "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
             "qgemm_query": [vp, i32, i32, ctypes.POINTER(Info)],
             "qgemm_destroy": [vp],
-            "qgemm_seq_create": [ctypes.POINTER(vp), ctypes.POINTER(vp), i32],
+            "qgemm_seq_create": [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.c_uint32],
             "qgemm_seq_run": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp],
+            "qgemm_seq_errors": [vp, ctypes.POINTER(ctypes.c_uint32)],
             "qgemm_seq_destroy": [vp],
         }
         for name, args in sig.items():
@@ -130,14 +130,6 @@ class QGemm:
         _check(lib().qgemm_run_path(self.h, _ptr(x), _ptr(y), R, path, _stream(stream)), "qgemm_run")
         return y
 
-    def stage(self, x, R: int | None = None, stream=None):
-        R = x.shape[0] if R is None else R
-        _check(lib().qgemm_stage(self.h, _ptr(x), R, _stream(stream)), "qgemm_stage")
-
-    def multiply(self, y, R: int, path: int = PATH_AUTO, stream=None):
-        _check(lib().qgemm_multiply(self.h, _ptr(y), R, path, _stream(stream)), "qgemm_multiply")
-        return y
-
     def dequantize(self, w, stream=None):
         _check(lib().qgemm_dequantize(self.h, _ptr(w), _stream(stream)), "qgemm_dequantize")
         return w
@@ -160,13 +152,15 @@ class QGemm:
 
 
 class Seq:
-    """A full weight pass: handles run back to back (graph-captured per R)."""
+    """A full weight pass: the GEMMs run in order, as a replayed graph of one launch
+    per GEMM, or (persistent=True) as one cooperative launch."""
 
-    def __init__(self, gemms):
+    def __init__(self, gemms, persistent: bool = False):
         self.gemms = list(gemms)
         arr = (ctypes.c_void_p * len(self.gemms))(*[g.h.value for g in self.gemms])
         s = ctypes.c_void_p()
-        _check(lib().qgemm_seq_create(ctypes.byref(s), arr, len(self.gemms)), "qgemm_seq_create")
+        flags = SEQ_PERSISTENT if persistent else 0
+        _check(lib().qgemm_seq_create(ctypes.byref(s), arr, len(self.gemms), flags), "qgemm_seq_create")
         self.s = s
 
     def run(self, xs, ys, R: int, argmax_idx=None, stream=None):
@@ -174,6 +168,12 @@ class Seq:
         xa = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
         ya = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
         _check(lib().qgemm_seq_run(self.s, xa, ya, R, _ptr(argmax_idx), _stream(stream)), "qgemm_seq_run")
+
+    def errors(self) -> int:
+        """Barrier waits that gave up since the last call (synchronises the device)."""
+        n = ctypes.c_uint32()
+        _check(lib().qgemm_seq_errors(self.s, ctypes.byref(n)), "qgemm_seq_errors")
+        return n.value
 
     def close(self):
         if getattr(self, "s", None) is not None and self.s.value:
