@@ -89,6 +89,8 @@ typedef struct {
     int waves_per_workgroup;
     int wave_columns;       /* waves of a workgroup side by side along N; the others
                                split each step range along K */
+    int whole_tile_ranges;  /* 1: each step range is whole output tiles (no partial
+                               sums cross workgroups); 0: equal ranges (stream-K) */
 } qgemm_info;
 
 /* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights

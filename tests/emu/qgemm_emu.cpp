@@ -94,10 +94,12 @@ void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, 
         }
 }
 
-// the A operand of lane (row tile rt, lane) at step t from slot b
+// the A operand of lane (row tile rt, lane) at step t from slot b; rows >= R
+// of a row tile read row R - 1 (their products are never stored)
 f16x8 a_operand(const std::vector<f16x8>& slots, int R, int64_t b, int rt, int t, int lane) {
-  const int r = rt * 16 + (lane & 15), gg = lane >> 4;
-  if (r >= R) return f16x8{};
+  int r = rt * 16 + (lane & 15);
+  const int gg = lane >> 4;
+  if (r >= R) r = R - 1;
   return slots[(size_t)((b * 8 + t) * 4 + gg) * R + r];
 }
 
@@ -153,7 +155,7 @@ struct EmuGemm {
   const uint16_t* x;
   float* y;
   int64_t N, K, KB, NS, T, I, V, hdr_off;
-  int nwn;
+  int nwn, aligned;
 };
 
 }  // namespace
@@ -172,7 +174,7 @@ extern "C" {
 // counter is left armed, -3 on an inconsistent activation slot.
 int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const int64_t* Ks,
                    const uint16_t* const* xs, float* const* ys, int R, int NT, int NW, const int* nwns,
-                   const int64_t* Vs, uint64_t order_seed) {
+                   const int64_t* Vs, const int* aligned, uint64_t order_seed) {
   const int RT = (R + 15) / 16;
   std::vector<EmuGemm> gs((size_t)G);
   int64_t Tmax = 0, Vslots = 0;
@@ -180,11 +182,12 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
     EmuGemm& e = gs[(size_t)g];
     e.N = Ns[g]; e.K = Ks[g]; e.KB = e.K / SB_W; e.NS = padded_n(e.N) / TILE_N;
     e.nwn = nwns[g];
+    e.aligned = aligned[g];
     if (e.nwn < 1 || NW % e.nwn) return -1;
     e.T = (e.NS + (int64_t)e.nwn * NT - 1) / ((int64_t)e.nwn * NT);
     e.I = e.T * e.KB;
     e.V = Vs[g];
-    if (e.V > e.I || e.V < 1) return -1;
+    if (e.V > (e.aligned ? e.T : e.I) || e.V < 1) return -1;
     e.packed.resize((size_t)packed_bytes(e.N, e.K));
     pack(canon[g], e.packed.data(), e.N, e.K);
     e.hdr_off = quant_region_bytes(e.N, e.K);
@@ -218,7 +221,10 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
     for (int64_t v = 0; v < e.V; ++v) order[(size_t)v] = v;
     std::shuffle(order.begin(), order.end(), rng);
     for (int64_t v : order) {
-      const int64_t A = range_first(v, e.V, e.I), B = range_first(v + 1, e.V, e.I), L = B - A;
+      // equal step ranges, or ranges of whole tiles
+      const int64_t A = e.aligned ? KB * range_first(v, e.V, e.T) : range_first(v, e.V, e.I);
+      const int64_t B = e.aligned ? KB * range_first(v + 1, e.V, e.T) : range_first(v + 1, e.V, e.I);
+      const int64_t L = B - A;
       const int64_t j0 = A % KB;
       convert_x(e.x, R, e.K, j0, x_slots(A, B, KB), xslots);
       // pieces[wk][slot][wn][tile_f4]
@@ -293,8 +299,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
 }
 
 int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int NW, int nwn,
-               int64_t V, uint64_t order_seed, float* y) {
-  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, order_seed);
+               int64_t V, int aligned, uint64_t order_seed, float* y) {
+  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, &aligned, order_seed);
 }
 
 int emu_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {

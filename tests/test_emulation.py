@@ -97,6 +97,22 @@ def test_wave_grid_matches_oracle_any_order(orc, N, K, R, NW, nwn, V):
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("N,K,R,NW,V", [
+    (640, 1024, 12, 8, 16),        # 40 tiles over 16 ranges: 2 or 3 whole tiles each
+    (300, 2048, 5, 8, 7),          # ragged last tile
+    (48, 5120, 1, 8, 3),           # one tile per range, 20 blocks each
+    (1000, 512, 20, 8, 63),        # two row tiles, 63 tiles over 63 ranges
+    (700, 256, 48, 4, 11),         # three row tiles, one block per tile
+])
+def test_whole_tile_ranges_match_oracle(orc, N, K, R, NW, V):
+    """Ranges of whole tiles: no tile is shared between workgroups."""
+    canon = synth.matrix_rows(5, 2, N, K)
+    x = synth.x_bf16(5, 3, R, K, outlier_p=0.01)
+    m = assert_parity(emu.stream(canon, N, K, x, NT=1, NW=NW, V=V, aligned=1), orc.gemm(canon, N, K, x),
+                      f"tile ranges N={N} K={K} R={R} V={V}")
+    assert m["rel_l2"] < 2e-6
+
+
 def test_sequence_shares_workspace_across_gemms(orc):
     """Several GEMMs of different shapes in one launch reuse the partial slots and
     tile counters; each result still matches the oracle and no counter stays armed."""
@@ -106,12 +122,13 @@ def test_sequence_shares_workspace_across_gemms(orc):
     xs = [synth.x_bf16(6, 50 + i, R, K) for i, (N, K) in enumerate(shapes)]
     Vs = [5, 5, 5, 5]
     nwns = [1, 2, 4, 1]            # each GEMM its own wave grid
-    ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns)
-    for (canon, N, K), x, y, V, nwn in zip(mats, xs, ys, Vs, nwns):
+    aligned = [0, 0, 1, 0]         # and its own kind of range
+    ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns, aligned=aligned)
+    for (canon, N, K), x, y, V, nwn, al in zip(mats, xs, ys, Vs, nwns, aligned):
         m = assert_parity(y, orc.gemm(canon, N, K, x), f"seq N={N} K={K}")
         assert m["rel_l2"] < 2e-6
         # the same GEMM alone in its own launch gives the same bits
-        alone = emu.stream(canon, N, K, x, NT=2, NW=4, V=V, order_seed=11, nwn=nwn)
+        alone = emu.stream(canon, N, K, x, NT=2, NW=4, V=V, order_seed=11, nwn=nwn, aligned=al)
         assert np.array_equal(alone.view(np.uint32), y.view(np.uint32))
 
 

@@ -116,7 +116,7 @@ def test_gemm_small_workload_all_R(orc, small, R):
 
 
 @pytest.mark.parametrize("N,K,R", [(40, 8192, 12), (1000, 25600, 3), (17, 5120, 7), (5120, 1024, 12),
-                                   (33, 256, 1), (4000, 2048, 48)])
+                                   (33, 256, 1), (4000, 2048, 48), (4100, 512, 12), (8200, 256, 1)])
 def test_gemm_ragged_and_split(orc, N, K, R):
     _flush(f"gemm N={N} K={K} R={R}")
     canon, g = G.make(1, 5, N, K, max_R=R)
@@ -125,6 +125,16 @@ def test_gemm_ragged_and_split(orc, N, K, R):
     y = G.run(g, x)
     assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} wgs={info['workgroups']}")
     g.close()
+
+
+def test_plan_kinds_are_exercised():
+    """The shapes above reach both kinds of range: whole tiles and stream-K."""
+    kinds = {}
+    for N, K, R in [(4100, 512, 12), (40, 8192, 12), (4000, 2048, 48)]:
+        _, g = G.make(1, 5, N, K, max_R=R)
+        kinds[(N, K, R)] = g.query(R)["whole_tile_ranges"]
+        g.close()
+    assert kinds[(4100, 512, 12)] == 1 and kinds[(40, 8192, 12)] == 0 and kinds[(4000, 2048, 48)] == 0
 
 
 def test_edge_blocks_large_R(orc):
@@ -209,7 +219,7 @@ def test_argmax_ties_and_nan():
 def test_seq_matches_oracle_and_repeats_bitwise(orc, persistent):
     import torch
     import weight_streaming_gemm_amd as wsg
-    shapes = [(300, 1024), (64, 2048), (1000, 1024), (40, 3072), (151, 512)]
+    shapes = [(300, 1024), (64, 2048), (4100, 512), (1000, 1024), (40, 3072), (151, 512)]
     R = 12
     mats = [G.make(9, i, N, K, max_R=12) for i, (N, K) in enumerate(shapes)]
     xs_np = [synth.x_bf16(9, 100 + i, R, K) for i, (N, K) in enumerate(shapes)]

@@ -61,6 +61,19 @@ QG_HD WConst header_consts(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, i
   return c;
 }
 
+// (a & mask) | c in one instruction.  The compiler would otherwise split it in
+// two: the three-operand form takes no literal and at most one scalar operand,
+// so the constant c is passed in a vector register.
+QG_HD uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+#else
+  return (a & mask) | c;
+#endif
+}
+
 // Eight weights of one packed dword as the B operand, each equal to sc * q.
 // Nibble positions (0,4) and (2,6) become 1024 + q in the binary16 mantissa,
 // positions (1,5) and (3,7) become 1024 + 16 q; one fused multiply-add per
@@ -69,10 +82,10 @@ QG_HD WConst header_consts(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, i
 QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
   const uint32_t magic = 0x64006400u;
   uint32_t w8 = w >> 8;
-  f16x2 p0 = bitcast<f16x2>((w & 0x000F000Fu) | magic);
-  f16x2 p1 = bitcast<f16x2>((w & 0x00F000F0u) | magic);
-  f16x2 p2 = bitcast<f16x2>((w8 & 0x000F000Fu) | magic);
-  f16x2 p3 = bitcast<f16x2>((w8 & 0x00F000F0u) | magic);
+  f16x2 p0 = bitcast<f16x2>(and_or(w, 0x000F000Fu, magic));
+  f16x2 p1 = bitcast<f16x2>(and_or(w, 0x00F000F0u, magic));
+  f16x2 p2 = bitcast<f16x2>(and_or(w8, 0x000F000Fu, magic));
+  f16x2 p3 = bitcast<f16x2>(and_or(w8, 0x00F000F0u, magic));
   f16x2 o0 = fma2(p0, c.sc, c.b1);
   f16x2 o1 = fma2(p1, c.sc16, c.b16);
   f16x2 o2 = fma2(p2, c.sc, c.b1);

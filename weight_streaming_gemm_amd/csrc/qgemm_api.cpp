@@ -36,7 +36,7 @@ namespace {
 
 struct Plan {
   int path;
-  int RT, NT, NW, nwn;
+  int RT, NT, NW, nwn, aligned;
   int64_t T, I, V, P;
   size_t part_bytes, cnt_bytes;
 };
@@ -70,6 +70,25 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
   int64_t resident = (int64_t)cus * std::max(1, occ[p.RT]);
   if (P_cap > 0) resident = std::min(resident, P_cap);
   const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW);
+  // Ranges of whole tiles need no partial sums across workgroups (whose
+  // exchange costs a few memory round trips at the end of a range, worth about
+  // FIXUP_STEPS steps); they are taken when every workgroup gets a tile, a
+  // whole tile row of activations fits in LDS, and the uneven split costs less.
+  constexpr int64_t FIXUP_STEPS = 32;
+  const int64_t T1 = (NS + p.NT - 1) / p.NT;
+  if (KB <= cap && T1 >= resident) {
+    const int64_t V = resident;
+    if (((T1 + V - 1) / V) * KB <= (T1 * KB + V - 1) / V + FIXUP_STEPS) {
+      p.nwn = 1;
+      p.aligned = 1;
+      p.T = T1;
+      p.I = T1 * KB;
+      p.V = p.P = V;
+      p.part_bytes = 0;
+      p.cnt_bytes = (size_t)p.T * 4;
+      return p;
+    }
+  }
   for (int nwn = 1; nwn <= p.NW; nwn *= 2) {
     if (p.NW % nwn) break;
     p.nwn = nwn;
@@ -110,6 +129,7 @@ GemmDesc make_desc(const qgemm_handle* h, const void* x, float* y, const Plan& p
   d.T = (int32_t)p.T;
   d.I = (int32_t)p.I;
   d.V = (int32_t)p.V;
+  d.aligned = p.aligned;
   return d;
 }
 
@@ -210,6 +230,7 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
     part = std::max(part, p.part_bytes);
     cnt = std::max(cnt, p.cnt_bytes);
   }
+  part = std::max<size_t>(part, 256);
   h->part_bytes = part;
   h->cnt_bytes = cnt;
   bool ok = hipMalloc(reinterpret_cast<void**>(&h->part), part) == hipSuccess &&
@@ -273,6 +294,7 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   info->ranges = p.V;
   info->waves_per_workgroup = p.NW;
   info->wave_columns = p.nwn;
+  info->whole_tile_ranges = p.aligned;
   return QGEMM_OK;
 }
 

@@ -18,9 +18,11 @@ struct GemmDesc {
                            // NW / nwn split each range along K)
   int32_t T;               // output tiles of nwn * NT sub-tiles
   int32_t I;               // T * KB (tile, block) steps
-  int32_t V;               // equal contiguous step ranges (P <= V <= I); workgroup p
-                           // takes ranges p, p + P, p + 2P, ...
-  int32_t pad_;
+  int32_t V;               // contiguous step ranges (P <= V <= I); workgroup p takes
+                           // ranges p, p + P, p + 2P, ...
+  int32_t aligned;         // 0: V equal ranges of steps; 1: V ranges of whole tiles
+                           // (tiles [floor(v T / V), floor((v + 1) T / V))), so that
+                           // no tile is shared between ranges
 };
 
 // A launch of the streaming kernel: G GEMMs run one after another (GEMM g + 1
@@ -38,13 +40,13 @@ struct StreamArgs {
 
 // Kernel variants: (row tiles RT, sub-tiles per tile NT, waves per workgroup NW).
 // A workgroup (one per CU) holds in LDS the partial tiles of its waves (two per
-// wave) and the activations of the blocks its current range touches, R * 512
-// bytes per block, in what is left of 160 KiB.
+// wave) and the activations of the blocks its current range touches, 8 (64 R +
+// 16) bytes per block, in what is left of 160 KiB.
 constexpr int LDS_BYTES = 160 * 1024;
-constexpr int LDS_RESERVED = 1024;              // flags and a zero operand
+constexpr int LDS_RESERVED = 1024;              // flags
 inline constexpr int piece_bytes(int RT, int NT, int NW) { return NW * 2 * NT * RT * 1024; }
 inline constexpr int x_area_bytes(int RT, int NT, int NW) { return LDS_BYTES - LDS_RESERVED - piece_bytes(RT, NT, NW); }
-inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (R * 512); }
+inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (8 * (64 * R + 16)); }
 inline int waves_for(int RT) { return RT <= 2 ? 8 : 4; }
 inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }

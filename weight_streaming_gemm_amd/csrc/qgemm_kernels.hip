@@ -112,7 +112,11 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 // starts only after every workgroup has finished GEMM g, as in a model where
 // each projection's input depends on the previous output; the weights of the
 // next GEMM are already in flight while a workgroup waits.
-constexpr int RING = 4;                        // weight ring depth, steps
+#ifndef QG_RING
+#define QG_RING 4
+#endif
+constexpr int RING = QG_RING;                  // weight ring depth, steps (4, 6 or 8)
+static_assert(RING == 4 || RING == 6 || RING == 8, "the main loop unrolls 4, 6 or 8 steps");
 constexpr uint32_t OOB = 0x80000000u;          // beyond every buffer (sizes < 2^31)
 constexpr uint32_t SPIN_LIMIT = 1u << 21;      // barrier polls before giving up
 constexpr int SC1 = 16;                        // cache policy: coherent across the device
@@ -157,7 +161,8 @@ struct Cursor {
   int A, B;       // the range's steps
   int it, it1;    // current step and end of this wave's sub-range
   int t, j;       // tile and block of step it
-  int KB, NS, I, V;
+  int KB, NS, I, V, T;
+  int aligned;
   int nwn, wn, wk, nwk;            // wave grid of GEMM g and this wave's place in it
   __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions of GEMM g (load cursor)
 };
@@ -167,14 +172,15 @@ __global__ void __launch_bounds__(NW * 64, NW / 4)
 stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   constexpr int NTHR = NW * 64;
   constexpr int XAREA = x_area_bytes(RT, NT, NW);
-  constexpr int XZERO = XAREA;                    // 16 zero bytes: the operand of rows >= R
-  __shared__ __attribute__((aligned(16))) uint8_t xlds[XAREA + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[XAREA];
   __shared__ f32x4 pieces[NW * 2 * NT * RT * 64];
   __shared__ uint32_t s_flag;
+  __shared__ uint32_t s_last[2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
-  const int SB = R * 512;                         // LDS bytes of one block's activations
+  const int XT = 64 * R + 16;                     // LDS bytes of one step's activations
+  const int SB = 8 * XT;                          // LDS bytes of one block's activations
 
   // descriptor of GEMM g; fields of the device table are made explicitly
   // wave-uniform so that buffer resources built from them stay scalar
@@ -195,6 +201,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       d.T = uni(src->T);
       d.I = uni(src->I);
       d.V = uni(src->V);
+      d.aligned = uni(src->aligned);
       return d;
     } else {
       return a.d0;
@@ -202,8 +209,13 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   };
   // range v of the cursor's GEMM and this wave's sub-range of it
   auto set_range = [&](Cursor& c) __attribute__((always_inline)) {
-    c.A = uni((int)range_first<uint32_t>(c.v, c.V, c.I));
-    c.B = uni((int)range_first<uint32_t>(c.v + 1, c.V, c.I));
+    if (c.aligned) {
+      c.A = uni(c.KB * (int)range_first<uint32_t>(c.v, c.V, c.T));
+      c.B = uni(c.KB * (int)range_first<uint32_t>(c.v + 1, c.V, c.T));
+    } else {
+      c.A = uni((int)range_first<uint32_t>(c.v, c.V, c.I));
+      c.B = uni((int)range_first<uint32_t>(c.v + 1, c.V, c.I));
+    }
     c.it = uni(c.A + (int)range_first<uint32_t>(c.wk, c.nwk, c.B - c.A));
     c.it1 = uni(c.A + (int)range_first<uint32_t>(c.wk + 1, c.nwk, c.B - c.A));
     c.t = uni(c.it / c.KB);
@@ -214,7 +226,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     if (g >= G) {
       c.v = 0; c.V = 1; c.A = c.B = 0;
       c.it = 1; c.it1 = 0;
-      c.t = 0; c.j = 0; c.KB = 1; c.NS = 0; c.I = 0;
+      c.t = 0; c.j = 0; c.KB = 1; c.NS = 0; c.I = 0; c.T = 0; c.aligned = 0;
       c.nwn = 1; c.wn = 0; c.wk = w; c.nwk = NW;
       c.qr = make_rsrc(nullptr, 0);
       c.hr = make_rsrc(nullptr, 0);
@@ -226,6 +238,8 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     c.KB = d.KB;
     c.NS = d.NS;
     c.I = d.I;
+    c.T = d.T;
+    c.aligned = d.aligned;
     c.nwn = d.nwn;
     c.nwk = uni(NW / d.nwn);
     c.wn = uni(w % d.nwn);
@@ -234,13 +248,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     c.hr = make_rsrc(d.packed + d.quant_bytes, d.hdr_bytes);
     set_range(c);
   };
-  // the load cursor's next step: within the sub-range, else this wave's
-  // sub-range of the workgroup's next range (skipping empty ones), else the
-  // next GEMM's first range (p < P <= V, so it exists)
+  // the load cursor's next step: the next one of this wave's sub-range; past its
+  // end, in a launch of several GEMMs, the first step of this wave's sub-range of
+  // the next GEMM that gives it any, so that the weights of GEMM g + 1 stream
+  // while GEMM g finishes; past the last GEMM, none (the loads return zeros)
+  auto skip_done = [&](Cursor& c) __attribute__((always_inline)) {
+    if constexpr (MULTI)
+      while (c.it >= c.it1 && c.g < G) enter(c, c.g + 1);
+  };
   auto next = [&](Cursor& c) __attribute__((always_inline)) {
     c.it = uni(c.it + 1);
     c.j = uni(c.j + 1);
     if (c.j == c.KB) { c.j = 0; c.t = uni(c.t + 1); }
+    skip_done(c);
   };
 
   // ---- weights: RING steps ahead -----------------------------------------------
@@ -256,41 +276,76 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     }
   };
 
-  // ---- activations of a range: block j = (j0 + b) mod KB goes to slot b; row r
-  // of slot b, lane group gg, step t is the A operand of lane 16 gg + r % 16 of
-  // row tile r / 16, built from x[r, 256 j + 64 gg + 4 t + {0..3}] and the same
-  // 32 further on.  32 threads per (slot, row); XB rows in flight per thread. ---
-  auto convert_x = [&](const GemmDesc& d, int j0, int nslots) __attribute__((always_inline)) {
-    constexpr int GROUPS = NTHR / 32, XB = 8;
+  // ---- activations of a range: block j = (j0 + b) mod KB goes to slot b.  A slot
+  // holds 8 steps t of XT = 64 R + 16 bytes (the pad puts consecutive steps on
+  // different LDS banks); in step t, lane group gg and row r hold the A operand
+  // of lane 16 gg + r % 16 of row tile r / 16, built from x[r, 256 j + 64 gg +
+  // 4 t + {0..3}] and the same 32 further on.  32 threads per (slot, row), XB
+  // rows in flight per thread, the rows taken in an order rotated by the
+  // workgroup index (all workgroups read the same activations).  The loads of
+  // the first batch are issued on their own (x_load) so that the kernel can
+  // queue them ahead of the weight ring. ---
+  constexpr int XGROUPS = NTHR / 32, XB = 16;
+  u32x2 xlo[XB], xhi[XB];
+  // (slot, row) of this thread's k-th row of the batch at base, rows = nslots R;
+  // slots rotated by the workgroup index.  Walked incrementally: one division.
+  struct XRow { int b, r; };
+  auto x_rows = [&](int nslots, int base, XRow (&o)[XB]) __attribute__((always_inline)) {
+    const int qg = XGROUPS / R, mg = XGROUPS - qg * R;
+    int b = base / R, r = base - b * R;
+    b += p % nslots;
+    for (int k = 0; k < XB; ++k) {
+      o[k].b = b >= nslots ? b - nslots : b;     // b < 2 nslots while the row is valid
+      o[k].r = r;
+      r += mg;
+      b += qg;
+      if (r >= R) { r -= R; ++b; }
+    }
+  };
+  auto x_load = [&](const GemmDesc& d, int j0, int nslots, int base) __attribute__((always_inline)) {
     const int sub = tid & 31, gg = sub >> 3, t = sub & 7;
     const int K = d.KB * SB_W;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
     const int rows = nslots * R;
-    for (int base = tid >> 5; base < rows; base += XB * GROUPS) {
-      u32x2 lo[XB], hi[XB];
-      for (int k = 0; k < XB; ++k) {
-        const int rb = base + k * GROUPS;
-        const int b = rb / R, r = rb - b * R;
-        int j = j0 + b;
-        if (j >= d.KB) j -= d.KB;
-        const uint32_t off = (uint32_t)((r * K + j * SB_W + 64 * gg + 4 * t) * 2);
-        lo[k] = bload<u32x2, 0>(xr, rb < rows ? off : OOB);
-        hi[k] = bload<u32x2, 0>(xr, rb < rows ? off + 64 : OOB);
-      }
-      for (int k = 0; k < XB; ++k) {
-        const int rb = base + k * GROUPS;
-        if (rb >= rows) break;
-        const int b = rb / R, r = rb - b * R;
-        *reinterpret_cast<f16x8*>(xlds + b * SB + ((t * 4 + gg) * R + r) * 16) =
-            build_a(lo[k].x, lo[k].y, hi[k].x, hi[k].y);
-      }
+    XRow rw[XB];
+    x_rows(nslots, base, rw);
+    for (int k = 0; k < XB; ++k) {
+      const int rb = base + k * XGROUPS;
+      int j = j0 + rw[k].b;
+      if (j >= d.KB) j -= d.KB;
+      const uint32_t off = (uint32_t)((rw[k].r * K + j * SB_W + 64 * gg + 4 * t) * 2);
+      xlo[k] = bload<u32x2, 0>(xr, rb < rows ? off : OOB);
+      xhi[k] = bload<u32x2, 0>(xr, rb < rows ? off + 64 : OOB);
     }
   };
-  // this lane's A-operand offsets inside a slot, per row tile (-1: row >= R)
+  auto x_store = [&](int nslots, int base) __attribute__((always_inline)) {
+    const int sub = tid & 31, gg = sub >> 3, t = sub & 7;
+    const int rows = nslots * R;
+    XRow rw[XB];
+    x_rows(nslots, base, rw);
+    for (int k = 0; k < XB; ++k) {
+      const int rb = base + k * XGROUPS;
+      if (rb >= rows) break;
+      *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + t * XT + (gg * R + rw[k].r) * 16) =
+          build_a(xlo[k].x, xlo[k].y, xhi[k].x, xhi[k].y);
+    }
+  };
+  // the rest of a range's conversion once its first batch is loaded
+  auto x_convert_rest = [&](const GemmDesc& d, int j0, int nslots) __attribute__((always_inline)) {
+    const int rows = nslots * R;
+    x_store(nslots, tid >> 5);
+    for (int base = (tid >> 5) + XB * XGROUPS; base < rows; base += XB * XGROUPS) {
+      x_load(d, j0, nslots, base);
+      x_store(nslots, base);
+    }
+  };
+  // this lane's A-operand offsets inside a slot, per row tile.  A row >= R of a
+  // row tile takes row R - 1's operand: a row of A only reaches the same row of
+  // the product, and rows >= R are never stored.
   int xoff[RT];
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + nl;
-    xoff[rt] = (r < R) ? (g4 * R + r) * 16 : -1;
+    xoff[rt] = (g4 * R + (r < R ? r : R - 1)) * 16;
   }
 
   f32x4 acc[NT][RT];
@@ -315,7 +370,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     for (int t = 0; t < 8; ++t) {
       f16x8 xa[RT];
       for (int rt = 0; rt < RT; ++rt) {
-        const int addr = xoff[rt] >= 0 ? base + t * 64 * R + xoff[rt] : XZERO;
+        const int addr = base + t * XT + xoff[rt];
         xa[rt] = *reinterpret_cast<const f16x8*>(xlds + addr);
       }
       for (int u = 0; u < NT; ++u) {
@@ -338,14 +393,18 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
 
   // ---- outputs ------------------------------------------------------------------
   // sub-tiles (t * nwn + wn) * NT + u of tile t belong to the waves of column wn
+  // (through a global-space pointer: a generic store would also count as an LDS
+  // access and make every later LDS wait conservative)
   auto write_y = [&](const GemmDesc& d, int t, int wn, const f32x4 (&v)[NT][RT]) __attribute__((always_inline)) {
+    typedef float __attribute__((address_space(1))) global_float;
+    global_float* const y = (global_float*)d.y;
     for (int u = 0; u < NT; ++u) {
       const int n = ((t * d.nwn + wn) * NT + u) * TILE_N + nl;
       if (n >= d.N) continue;
       for (int rt = 0; rt < RT; ++rt)
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * g4 + i;
-          if (r < R) d.y[(int64_t)r * d.N + n] = v[u][rt][i];
+          if (r < R) y[(int64_t)r * d.N + n] = v[u][rt][i];
         }
     }
   };
@@ -381,10 +440,21 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     f32x4 sum[NT][RT];
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt) sum[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q = q_lo; q <= q_hi; ++q) {
-      const int qs = (int)partial_slot<uint32_t>(q, t, c.KB, c.V, c.I);
-      for (int u = 0; u < NT; ++u)
-        for (int rt = 0; rt < RT; ++rt) sum[u][rt] += bload<f32x4, SC1>(pr, gslot_off(c, qs, wn, u, rt));
+    // FB slots in flight at a time, added in range order
+    constexpr int FB = RT == 1 ? 8 : (RT == 2 ? 4 : 2);
+    for (int q0 = q_lo; q0 <= q_hi; q0 += FB) {
+      f32x4 v[FB][NT][RT];
+      for (int k = 0; k < FB; ++k) {
+        const int q = q0 + k;
+        const int qs = q <= q_hi ? (int)partial_slot<uint32_t>(q, t, c.KB, c.V, c.I) : 0;
+        for (int u = 0; u < NT; ++u)
+          for (int rt = 0; rt < RT; ++rt)
+            v[k][u][rt] = bload<f32x4, SC1>(pr, q <= q_hi ? gslot_off(c, qs, wn, u, rt) : OOB);
+      }
+      for (int k = 0; k < FB; ++k)
+        if (q0 + k <= q_hi)
+          for (int u = 0; u < NT; ++u)
+            for (int rt = 0; rt < RT; ++rt) sum[u][rt] += v[k][u][rt];
     }
     write_y(d, t, wn, sum);
   };
@@ -428,20 +498,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     if (cross_a || cross_b) {
       __builtin_amdgcn_s_waitcnt(0);              // this thread's partial stores are complete
       __syncthreads();
-      if (tid == 0) {
-        uint32_t last = 0;
-        if (cross_a) {
-          const uint32_t owners = tile_last_owner<uint32_t>(tA, KB, c.V, c.I) - tile_first_owner<uint32_t>(tA, KB, c.V, c.I);
-          if (__hip_atomic_fetch_add(a.cnt + tA, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == owners) last |= 1u;
+      // lanes 0 and 1 arrive at tiles tA and tB with one atomic instruction
+      if (tid < 2) {
+        const bool mine = tid == 0 ? cross_a : (cross_b && !(cross_a && tB == tA));
+        const int t = tid == 0 ? tA : tB;
+        uint32_t is_last = 0;
+        if (mine) {
+          const uint32_t owners = tile_last_owner<uint32_t>(t, KB, c.V, c.I) - tile_first_owner<uint32_t>(t, KB, c.V, c.I);
+          is_last = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == owners;
         }
-        if (cross_b && !(cross_a && tB == tA)) {
-          const uint32_t owners = tile_last_owner<uint32_t>(tB, KB, c.V, c.I) - tile_first_owner<uint32_t>(tB, KB, c.V, c.I);
-          if (__hip_atomic_fetch_add(a.cnt + tB, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == owners) last |= 2u;
-        }
-        s_flag = last;
+        s_last[tid] = is_last;
       }
       __syncthreads();
-      const uint32_t last = s_flag;
+      const uint32_t last = s_last[0] | (s_last[1] << 1);
       // the waves of the first nwn columns add the tile's slots (column w)
       if (w < nwn) {
         if (last & 1u) global_fixup(c, d, tA, w);
@@ -475,17 +544,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     __syncthreads();
   };
 
-  // ---- prologue: the load cursor starts RING steps ahead -------------------------
-  if (tid == 0) *reinterpret_cast<u32x4*>(xlds + XZERO) = u32x4{0u, 0u, 0u, 0u};
+  // ---- prologue: the first activation batch, then the weight ring (the load
+  // cursor starts RING steps ahead) ---------------------------------------------
   Cursor L, C;
-  enter(L, 0);
-  C = L;
+  enter(C, 0);
+  GemmDesc D = get_desc(0);
+  x_load(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
+  L = C;
+  skip_done(L);
   WStage<NT> W[RING];
   for (int s = 0; s < RING; ++s) {
     load_w(W[s], L);
     next(L);
   }
-  GemmDesc D = get_desc(0);
   int xs = 0;                                     // activation slot of C's step
   int ja = 0;                                     // first block of the current segment
   int a_w = 0;                                    // first step of this wave's sub-range
@@ -511,39 +582,73 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     if (xs == C.KB) xs = 0;
     return false;
   };
-  static_assert(RING == 4, "the loop below unrolls RING steps");
 
-  // One range per workgroup and GEMM (the host sizes V = P): the ring keeps its
-  // position from one GEMM to the next only through a full drain, so each wave
-  // starts every GEMM at ring position 0.
-  for (;;) {
-    convert_x(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB));
+  // One range per workgroup and GEMM (the host sizes V = P).
+  // (the first activation batch is already in flight)
+  auto start_range = [&]() __attribute__((always_inline)) {
+    x_convert_rest(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB));
     __syncthreads();
+    xs = uni((C.it - C.A) % C.KB);
+    ja = C.j;
+    a_w = C.it;
+    zero_acc();
+  };
+  if constexpr (!MULTI) {
+    start_range();
     if (C.it < C.it1) {
-      xs = uni((C.it - C.A) % C.KB);
-      ja = C.j;
-      a_w = C.it;
-      zero_acc();
       for (;;) {
         if (step(std::integral_constant<int, 0>{})) break;
         if (step(std::integral_constant<int, 1>{})) break;
         if (step(std::integral_constant<int, 2>{})) break;
         if (step(std::integral_constant<int, 3>{})) break;
+        if constexpr (RING > 4) {
+          if (step(std::integral_constant<int, 4 % RING>{})) break;
+          if (step(std::integral_constant<int, 5 % RING>{})) break;
+        }
+        if constexpr (RING > 6) {
+          if (step(std::integral_constant<int, 6 % RING>{})) break;
+          if (step(std::integral_constant<int, 7 % RING>{})) break;
+        }
       }
     }
     close_range(C, D);
-    if constexpr (!MULTI) {
-      break;
-    } else {
-      if (C.g + 1 >= G) break;
-      grid_barrier(C.g);
-      enter(C, C.g + 1);
-      D = get_desc(C.g);
-      // the load cursor stopped at the end of this wave's sub-range: refill
-      L = C;
-      for (int s = 0; s < RING; ++s) {
-        load_w(W[s], L);
-        next(L);
+  } else {
+    // Several GEMMs: the ring runs on from one GEMM into the next (the load
+    // cursor is already in GEMM g + 1 while GEMM g finishes), so the GEMM
+    // boundary is handled inside the step loop and the loop never restarts.
+    // boundary(): close GEMM g, wait for all workgroups, start this wave's next
+    // non-empty sub-range; false when the launch is done.
+    auto boundary = [&]() __attribute__((always_inline)) -> bool {
+      for (;;) {
+        close_range(C, D);
+        if (C.g + 1 >= G) return false;
+        grid_barrier(C.g);
+        enter(C, C.g + 1);
+        D = get_desc(C.g);
+        x_load(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
+        start_range();
+        if (C.it < C.it1) return true;
+      }
+    };
+    auto mstep = [&](auto S) __attribute__((always_inline)) -> bool {
+      if (!step(S)) return false;
+      return !boundary();
+    };
+    start_range();
+    if (C.it < C.it1 || boundary()) {
+      for (;;) {
+        if (mstep(std::integral_constant<int, 0>{})) break;
+        if (mstep(std::integral_constant<int, 1>{})) break;
+        if (mstep(std::integral_constant<int, 2>{})) break;
+        if (mstep(std::integral_constant<int, 3>{})) break;
+        if constexpr (RING > 4) {
+          if (mstep(std::integral_constant<int, 4 % RING>{})) break;
+          if (mstep(std::integral_constant<int, 5 % RING>{})) break;
+        }
+        if constexpr (RING > 6) {
+          if (mstep(std::integral_constant<int, 6 % RING>{})) break;
+          if (mstep(std::integral_constant<int, 7 % RING>{})) break;
+        }
       }
     }
   }
@@ -639,7 +744,7 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
   return hipGetLastError();
 }
 
-#define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(1, 1, 12) X(2, 1, 8) X(3, 1, 4) X(4, 1, 4)
+#define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(2, 1, 8) X(3, 1, 4) X(4, 1, 4)
 
 template <int RT, int NT, int NW>
 static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {

@@ -37,7 +37,8 @@ class Info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("row_tiles", ctypes.c_int), ("subtiles_per_wave", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("steps", ctypes.c_int64),
                 ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("ranges", ctypes.c_int64),
-                ("waves_per_workgroup", ctypes.c_int), ("wave_columns", ctypes.c_int)]
+                ("waves_per_workgroup", ctypes.c_int), ("wave_columns", ctypes.c_int),
+                ("whole_tile_ranges", ctypes.c_int)]
 
 
 _lib = None
