@@ -73,12 +73,15 @@ void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
 
 int64_t x_slot_of_emu(int64_t j, int64_t j0, int64_t KB) { return (j - j0 + KB) % KB; }
 
-// Activation staging of one range: the kernel's convert_x, slot b <- block
-// (j0 + b) mod KB for b < nslots; slot layout [b][t][gg][r < R] of 16-byte A
-// operands (R rows stored), rows >= R read as zeros.
-void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, std::vector<f16x8>& slots) {
+// Activation staging of one range: the kernel's x_load / x_store, slot b <-
+// block (j0 + b) mod KB for b < nslots; slot layout [b][t][gg][r < R] of
+// 16-byte A operands, and per (b, gg, r) the min-term operand from the sums of
+// sub-blocks 2 gg and 2 gg + 1.
+void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, std::vector<f16x8>& slots,
+               std::vector<f16x8>& sums) {
   const int64_t KB = K / SB_W;
   slots.assign((size_t)nslots * 8 * 4 * R, f16x8{});
+  sums.assign((size_t)nslots * 4 * R, f16x8{});
   for (int64_t b = 0; b < nslots; ++b)
     for (int r = 0; r < R; ++r)
       for (int gg = 0; gg < 4; ++gg)
@@ -92,6 +95,23 @@ void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, 
           const uint32_t d3 = (uint32_t)lo[34] | ((uint32_t)lo[35] << 16);
           slots[(size_t)((b * 8 + t) * 4 + gg) * R + r] = build_a(d0, d1, d2, d3);
         }
+  // sub-block sums: thread t adds its four bf16 values of each run (the kernel
+  // uses two bf16 dot products with ones, which may round differently), then the
+  // eight threads' partial sums are added in the kernel's tree order
+  for (int64_t b = 0; b < nslots; ++b)
+    for (int r = 0; r < R; ++r)
+      for (int gg = 0; gg < 4; ++gg) {
+        int64_t j = j0 + b;
+        if (j >= KB) j -= KB;
+        float p0[8], p1[8];
+        for (int t = 0; t < 8; ++t) {
+          const uint16_t* lo = x + (int64_t)r * K + j * SB_W + 64 * gg + 4 * t;
+          auto f = [](uint16_t v) { return bitcast<float>((uint32_t)v << 16); };
+          p0[t] = ((f(lo[0]) + f(lo[1])) + f(lo[2])) + f(lo[3]);
+          p1[t] = ((f(lo[32]) + f(lo[33])) + f(lo[34])) + f(lo[35]);
+        }
+        sums[(size_t)(b * 4 + gg) * R + r] = build_s(tree8(p0), tree8(p1));
+      }
 }
 
 // the A operand of lane (row tile rt, lane) at step t from slot b; rows >= R
@@ -102,12 +122,20 @@ f16x8 a_operand(const std::vector<f16x8>& slots, int R, int64_t b, int rt, int t
   if (r >= R) r = R - 1;
   return slots[(size_t)((b * 8 + t) * 4 + gg) * R + r];
 }
+// the min-term A operand of lane (row tile rt, lane) from slot b
+f16x8 s_operand(const std::vector<f16x8>& sums, int R, int64_t b, int rt, int lane) {
+  int r = rt * 16 + (lane & 15);
+  const int gg = lane >> 4;
+  if (r >= R) r = R - 1;
+  return sums[(size_t)(b * 4 + gg) * R + r];
+}
 
 // One step of a wave at sub-tiles ns0 .. ns0 + NT - 1, block j (activation
 // slot b): the kernel's compute() for its NT sub-tiles and all 64 lanes,
 // accumulating into acc[NT][RT][64].
 void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int64_t NS, int64_t j, int64_t KB,
-               const std::vector<f16x8>& slots, int R, int64_t b, int RT, f32x4* acc) {
+               const std::vector<f16x8>& slots, const std::vector<f16x8>& sums, int R, int64_t b, int RT,
+               f32x4* acc) {
   for (int u = 0; u < NT; ++u) {
     const int64_t ns = ns0 + u;
     WConst c[64];
@@ -129,6 +157,9 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 ds[64], ms[64];
       for (int l = 0; l < 64; ++l) ds[l] = ms[l] = f32x4{0, 0, 0, 0};
+      f16x8 sv[64];
+      for (int lane = 0; lane < 64; ++lane) sv[lane] = s_operand(sums, R, b, rt, lane);
+      mfma_16x16x32(sv, bm, ms);
       for (int tt = 0; tt < 8; ++tt) {
         f16x8 av[64], bb[64];
         for (int lane = 0; lane < 64; ++lane) {
@@ -136,7 +167,6 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
           bb[lane] = build_b(qd[lane][tt], c[lane]);
         }
         mfma_16x16x32(av, bb, ds);
-        mfma_16x16x32(av, bm, ms);
       }
       f32x4* ac = acc + (size_t)(u * RT + rt) * 64;
       for (int lane = 0; lane < 64; ++lane)
@@ -199,7 +229,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
   const size_t tile_f4 = (size_t)NT * RT * 64;            // f32x4 per wave piece (one column of a tile)
   std::vector<f32x4> part((size_t)2 * Vslots * tile_f4, f32x4{NAN, NAN, NAN, NAN});
   std::vector<uint32_t> cnt((size_t)Tmax, 0);
-  std::vector<f16x8> xslots;
+  std::vector<f16x8> xslots, xsums;
   std::mt19937_64 rng(order_seed);
   for (int g = 0; g < G; ++g) {
     EmuGemm& e = gs[(size_t)g];
@@ -226,7 +256,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
       const int64_t B = e.aligned ? KB * range_first(v + 1, e.V, e.T) : range_first(v + 1, e.V, e.I);
       const int64_t L = B - A;
       const int64_t j0 = A % KB;
-      convert_x(e.x, R, e.K, j0, x_slots(A, B, KB), xslots);
+      convert_x(e.x, R, e.K, j0, x_slots(A, B, KB), xslots, xsums);
       // pieces[wk][slot][wn][tile_f4]
       auto piece = [&](int64_t wk, int sl, int wn) { return (size_t)((wk * 2 + sl) * nwn + wn) * tile_f4; };
       std::vector<f32x4> pieces((size_t)NW * 2 * tile_f4, f32x4{NAN, NAN, NAN, NAN});
@@ -239,7 +269,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
           const int64_t t = it / KB, j = it % KB;
           const int64_t b = (it - A) % KB;
           if (b != x_slot_of_emu(j, j0, KB)) return -3;
-          wave_step(e.packed.data(), e.hdr_off, (t * nwn + wn) * NT, NT, e.NS, j, KB, xslots, R, b, RT, acc.data());
+          wave_step(e.packed.data(), e.hdr_off, (t * nwn + wn) * NT, NT, e.NS, j, KB, xslots, xsums, R, b, RT,
+                    acc.data());
           const bool sub_end = it + 1 == b_w;
           if (j != KB - 1 && !sub_end) continue;
           if (ja == 0 && j == KB - 1) {

@@ -4,9 +4,8 @@
 //
 // For lane group g (sub-blocks 2g, 2g+1 of a block) the B operand element e of
 // step t is sc_{2g + (e & 1)} * q_k for k = operand_k(g, t, e) (layout.h): an
-// integer <= 63 * 15 = 945, exact in binary16.  The min term uses a second B
-// operand whose element e is m_{2g + (e & 1)} (<= 63, exact), the same for
-// every step t of the block.
+// integer <= 63 * 15 = 945, exact in binary16.  The min term is one more
+// product per block, of the sub-block sums of x with the mins (build_m, build_s).
 #pragma once
 #include <stdint.h>
 
@@ -93,9 +92,28 @@ QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
   return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
 }
 
-// the min-term B operand: (m_{2g}, m_{2g+1}) in every pair
+// The min term of a block, sum over k of m_sub(k) x_k, is sum over s of m_s X_s
+// with X_s the sum of x over sub-block s: one matrix-core product per block.
+// Lane group g holds sub-blocks 2g and 2g+1; each sum is split into a binary16
+// head and tail, X = hi + lo (exact to 2^-22 relative), and the operands are
+//   A (per row):    (hi(X_2g), hi(X_2g+1), lo(X_2g), lo(X_2g+1), 0, 0, 0, 0)
+//   B (per output): (m_2g,     m_2g+1,     m_2g,     m_2g+1,     0, 0, 0, 0)
 QG_HD f16x8 build_m(const WConst& c) {
-  return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1]};
+  const _Float16 z = (_Float16)0.0f;
+  return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], z, z, z, z};
+}
+
+// the sum of the 8 per-step partial sums of a sub-block, in a fixed tree order
+QG_HD float tree8(const float p[8]) {
+  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// the A operand of the min-term product from the sums of sub-blocks 2g (s0) and 2g+1 (s1)
+QG_HD f16x8 build_s(float s0, float s1) {
+  const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
+  const _Float16 l0 = (_Float16)(s0 - (float)h0), l1 = (_Float16)(s1 - (float)h1);
+  const _Float16 z = (_Float16)0.0f;
+  return f16x8{h0, h1, l0, l1, z, z, z, z};
 }
 
 // Eight activations of one matrix-core A operand from two runs of four bf16

@@ -41,12 +41,12 @@ struct StreamArgs {
 // Kernel variants: (row tiles RT, sub-tiles per tile NT, waves per workgroup NW).
 // A workgroup (one per CU) holds in LDS the partial tiles of its waves (two per
 // wave) and the activations of the blocks its current range touches, 8 (64 R +
-// 16) bytes per block, in what is left of 160 KiB.
+// 16) + 64 R bytes per block, in what is left of 160 KiB.
 constexpr int LDS_BYTES = 160 * 1024;
 constexpr int LDS_RESERVED = 1024;              // flags
 inline constexpr int piece_bytes(int RT, int NT, int NW) { return NW * 2 * NT * RT * 1024; }
 inline constexpr int x_area_bytes(int RT, int NT, int NW) { return LDS_BYTES - LDS_RESERVED - piece_bytes(RT, NT, NW); }
-inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (8 * (64 * R + 16)); }
+inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (8 * (64 * R + 16) + 64 * R); }
 inline int waves_for(int RT) { return RT <= 2 ? 8 : 4; }
 inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }

@@ -137,6 +137,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
+// the sum of four bf16 values (two dwords) in fp32, with two dot products against ones
+__device__ __forceinline__ float sum4_bf16(uint32_t d0, uint32_t d1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  const float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), one, 0.0f, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), one, s, false);
+}
+
+// v from the lane picked by the data-parallel-primitive control CTRL
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 template <class T>
 __device__ __forceinline__ T* uniform_ptr(T* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -180,7 +194,8 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
   const int XT = 64 * R + 16;                     // LDS bytes of one step's activations
-  const int SB = 8 * XT;                          // LDS bytes of one block's activations
+  const int XS = 8 * XT;                          // offset of a block's sub-block sums
+  const int SB = XS + 64 * R;                     // LDS bytes of one block's activations
 
   // descriptor of GEMM g; fields of the device table are made explicitly
   // wave-uniform so that buffer resources built from them stay scalar
@@ -285,7 +300,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // workgroup index (all workgroups read the same activations).  The loads of
   // the first batch are issued on their own (x_load) so that the kernel can
   // queue them ahead of the weight ring. ---
-  constexpr int XGROUPS = NTHR / 32, XB = 16;
+  constexpr int XGROUPS = NTHR / 32, XB = MULTI ? 8 : 16;
   u32x2 xlo[XB], xhi[XB];
   // (slot, row) of this thread's k-th row of the batch at base, rows = nslots R;
   // slots rotated by the workgroup index.  Walked incrementally: one division.
@@ -326,8 +341,16 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     for (int k = 0; k < XB; ++k) {
       const int rb = base + k * XGROUPS;
       if (rb >= rows) break;
-      *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + t * XT + (gg * R + rw[k].r) * 16) =
-          build_a(xlo[k].x, xlo[k].y, xhi[k].x, xhi[k].y);
+      const f16x8 op = build_a(xlo[k].x, xlo[k].y, xhi[k].x, xhi[k].y);
+      *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + t * XT + (gg * R + rw[k].r) * 16) = op;
+      // sub-block sums: the 8 threads t of lane group gg (8 consecutive lanes) add
+      // their run sums as ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
+      float s0 = sum4_bf16(xlo[k].x, xlo[k].y), s1 = sum4_bf16(xhi[k].x, xhi[k].y);
+      s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
+      s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
+      s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
+      if (t == 0)
+        *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 16) = build_s(s0, s1);
     }
   };
   // the rest of a range's conversion once its first batch is loaded
@@ -367,6 +390,11 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       }
     }
     const int base = slot * SB;
+    for (int rt = 0; rt < RT; ++rt) {
+      const f16x8 xsum = *reinterpret_cast<const f16x8*>(xlds + base + XS + xoff[rt]);
+      for (int u = 0; u < NT; ++u)
+        ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xsum, bm[u], ms[u][rt], 0, 0, 0);
+    }
     for (int t = 0; t < 8; ++t) {
       f16x8 xa[RT];
       for (int rt = 0; rt < RT; ++rt) {
@@ -376,10 +404,8 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       for (int u = 0; u < NT; ++u) {
         const uint32_t wd = (t < 4) ? st.qa[u][t] : st.qb[u][t - 4];
         const f16x8 b = build_b(wd, c[u]);
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RT; ++rt)
           ds[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[u][rt], 0, 0, 0);
-          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], bm[u], ms[u][rt], 0, 0, 0);
-        }
       }
     }
     // acc += d * ds - dmin * ms, two fused multiply-adds per element
