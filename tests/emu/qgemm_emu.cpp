@@ -135,7 +135,7 @@ f16x8 s_operand(const std::vector<f16x8>& sums, int R, int64_t b, int rt, int la
 // accumulating into acc[NT][RT][64].
 void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int64_t NS, int64_t j, int64_t KB,
                const std::vector<f16x8>& slots, const std::vector<f16x8>& sums, int R, int64_t b, int RT,
-               f32x4* acc) {
+               bool msum, f32x4* acc) {
   for (int u = 0; u < NT; ++u) {
     const int64_t ns = ns0 + u;
     WConst c[64];
@@ -152,14 +152,16 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
         memset(qd[lane], 0, sizeof(qd[lane]));   // loads past the end return zeros
       }
       c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
-      bm[lane] = build_m(c[lane]);
+      bm[lane] = msum ? build_m(c[lane]) : build_m_full(c[lane]);
     }
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 ds[64], ms[64];
       for (int l = 0; l < 64; ++l) ds[l] = ms[l] = f32x4{0, 0, 0, 0};
-      f16x8 sv[64];
-      for (int lane = 0; lane < 64; ++lane) sv[lane] = s_operand(sums, R, b, rt, lane);
-      mfma_16x16x32(sv, bm, ms);
+      if (msum) {
+        f16x8 sv[64];
+        for (int lane = 0; lane < 64; ++lane) sv[lane] = s_operand(sums, R, b, rt, lane);
+        mfma_16x16x32(sv, bm, ms);
+      }
       for (int tt = 0; tt < 8; ++tt) {
         f16x8 av[64], bb[64];
         for (int lane = 0; lane < 64; ++lane) {
@@ -167,6 +169,7 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
           bb[lane] = build_b(qd[lane][tt], c[lane]);
         }
         mfma_16x16x32(av, bb, ds);
+        if (!msum) mfma_16x16x32(av, bm, ms);
       }
       f32x4* ac = acc + (size_t)(u * RT + rt) * 64;
       for (int lane = 0; lane < 64; ++lane)
@@ -185,7 +188,7 @@ struct EmuGemm {
   const uint16_t* x;
   float* y;
   int64_t N, K, KB, NS, T, I, V, hdr_off;
-  int nwn, aligned;
+  int nwn, aligned, msum;
 };
 
 }  // namespace
@@ -204,7 +207,7 @@ extern "C" {
 // counter is left armed, -3 on an inconsistent activation slot.
 int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const int64_t* Ks,
                    const uint16_t* const* xs, float* const* ys, int R, int NT, int NW, const int* nwns,
-                   const int64_t* Vs, const int* aligned, uint64_t order_seed) {
+                   const int64_t* Vs, const int* aligned, const int* msums, uint64_t order_seed) {
   const int RT = (R + 15) / 16;
   std::vector<EmuGemm> gs((size_t)G);
   int64_t Tmax = 0, Vslots = 0;
@@ -213,6 +216,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
     e.N = Ns[g]; e.K = Ks[g]; e.KB = e.K / SB_W; e.NS = padded_n(e.N) / TILE_N;
     e.nwn = nwns[g];
     e.aligned = aligned[g];
+    e.msum = msums[g];
     if (e.nwn < 1 || NW % e.nwn) return -1;
     e.T = (e.NS + (int64_t)e.nwn * NT - 1) / ((int64_t)e.nwn * NT);
     e.I = e.T * e.KB;
@@ -270,7 +274,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
           const int64_t b = (it - A) % KB;
           if (b != x_slot_of_emu(j, j0, KB)) return -3;
           wave_step(e.packed.data(), e.hdr_off, (t * nwn + wn) * NT, NT, e.NS, j, KB, xslots, xsums, R, b, RT,
-                    acc.data());
+                    e.msum != 0, acc.data());
           const bool sub_end = it + 1 == b_w;
           if (j != KB - 1 && !sub_end) continue;
           if (ja == 0 && j == KB - 1) {
@@ -330,8 +334,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
 }
 
 int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int NW, int nwn,
-               int64_t V, int aligned, uint64_t order_seed, float* y) {
-  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, &aligned, order_seed);
+               int64_t V, int aligned, int msum, uint64_t order_seed, float* y) {
+  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, &aligned, &msum, order_seed);
 }
 
 int emu_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {

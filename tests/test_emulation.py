@@ -39,12 +39,14 @@ def test_packed_size_and_padding():
     (16, 512, 5, 1, 8, 1),        # 2 steps for 8 waves: empty sub-ranges
     (48, 1024, 7, 1, 8, 5),       # ranges of 2-3 steps over 8 waves
 ])
-def test_gemm_data_flow_matches_oracle(orc, N, K, R, NT, NW, V):
+@pytest.mark.parametrize("msum", [1, 0])
+def test_gemm_data_flow_matches_oracle(orc, N, K, R, NT, NW, V, msum):
+    """Both forms of the min term: from staged sub-block sums, or per step."""
     canon = synth.matrix_rows(0, 3, N, K)
     x = synth.x_bf16(0, 5, R, K, outlier_p=0.01)
-    y = emu.stream(canon, N, K, x, NT=NT, NW=NW, V=V)
+    y = emu.stream(canon, N, K, x, NT=NT, NW=NW, V=V, msum=msum)
     ref = orc.gemm(canon, N, K, x)
-    m = assert_parity(y, ref, f"emu N={N} K={K} R={R}")
+    m = assert_parity(y, ref, f"emu N={N} K={K} R={R} msum={msum}")
     assert m["rel_l2"] < 2e-6
 
 
@@ -123,12 +125,13 @@ def test_sequence_shares_workspace_across_gemms(orc):
     Vs = [5, 5, 5, 5]
     nwns = [1, 2, 4, 1]            # each GEMM its own wave grid
     aligned = [0, 0, 1, 0]         # and its own kind of range
-    ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns, aligned=aligned)
-    for (canon, N, K), x, y, V, nwn, al in zip(mats, xs, ys, Vs, nwns, aligned):
+    msums = [1, 0, 1, 0]           # and its own form of the min term
+    ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns, aligned=aligned, msums=msums)
+    for (canon, N, K), x, y, V, nwn, al, ms in zip(mats, xs, ys, Vs, nwns, aligned, msums):
         m = assert_parity(y, orc.gemm(canon, N, K, x), f"seq N={N} K={K}")
         assert m["rel_l2"] < 2e-6
         # the same GEMM alone in its own launch gives the same bits
-        alone = emu.stream(canon, N, K, x, NT=2, NW=4, V=V, order_seed=11, nwn=nwn, aligned=al)
+        alone = emu.stream(canon, N, K, x, NT=2, NW=4, V=V, order_seed=11, nwn=nwn, aligned=al, msum=ms)
         assert np.array_equal(alone.view(np.uint32), y.view(np.uint32))
 
 

@@ -102,6 +102,11 @@ QG_HD f16x8 build_m(const WConst& c) {
   const _Float16 z = (_Float16)0.0f;
   return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], z, z, z, z};
 }
+// Without the sums, the min term is the product of each step's activation
+// operand with B = (m_2g, m_2g+1) in every pair (eight products per block).
+QG_HD f16x8 build_m_full(const WConst& c) {
+  return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1], c.m[0], c.m[1]};
+}
 
 // the sum of the 8 per-step partial sums of a sub-block, in a fixed tree order
 QG_HD float tree8(const float p[8]) {

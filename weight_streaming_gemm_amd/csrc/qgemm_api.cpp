@@ -36,7 +36,7 @@ namespace {
 
 struct Plan {
   int path;
-  int RT, NT, NW, nwn, aligned;
+  int RT, NT, NW, nwn, aligned, msum;
   int64_t T, I, V, P;
   size_t part_bytes, cnt_bytes;
 };
@@ -54,6 +54,15 @@ bool valid_shape(int64_t N, int64_t K) {
 
 bool valid_handle(const qgemm_handle* h) { return h && h->magic == HANDLE_MAGIC; }
 
+// The min term from staged sub-block sums costs work per staged block and saves
+// seven products per step: taken when a range has at least 4 steps per block
+// (and the sums fit in LDS).
+void choose_msum(Plan& p, int64_t KB, int R) {
+  const int64_t steps = p.aligned ? ((p.T + p.V - 1) / p.V) * KB : (p.I + p.V - 1) / p.V;
+  const int64_t slots = std::min(steps, KB);
+  p.msum = steps >= 4 * slots && slots <= x_slot_capacity(R, p.RT, p.NT, p.NW, true);
+}
+
 // Matrix-core plan for one GEMM: 16-row tiles, NW waves per workgroup in an
 // nwn x (NW / nwn) grid, tiles of nwn * NT 16-output sub-tiles, one workgroup
 // per CU, one range of (tile, block) steps per workgroup.  V = P ranges: as
@@ -69,7 +78,7 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
   p.NT = subtiles_for(p.RT);
   int64_t resident = (int64_t)cus * std::max(1, occ[p.RT]);
   if (P_cap > 0) resident = std::min(resident, P_cap);
-  const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW);
+  const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW, false);
   // Ranges of whole tiles need no partial sums across workgroups (whose
   // exchange costs a few memory round trips at the end of a range, worth about
   // FIXUP_STEPS steps); they are taken when every workgroup gets a tile, a
@@ -86,6 +95,7 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
       p.V = p.P = V;
       p.part_bytes = 0;
       p.cnt_bytes = (size_t)p.T * 4;
+      choose_msum(p, KB, R);
       return p;
     }
   }
@@ -102,6 +112,7 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
   p.P = p.V;
   p.part_bytes = (size_t)(2 * p.V) * partial_slot_bytes(p.RT, p.NT, p.nwn);
   p.cnt_bytes = (size_t)p.T * 4;
+  choose_msum(p, KB, R);
   return p;
 }
 
@@ -150,6 +161,7 @@ int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStrea
   a.RT = p.RT;
   a.NT = p.NT;
   a.NW = p.NW;
+  a.msum = p.msum;
   return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
@@ -341,8 +353,9 @@ struct qgemm_seq {
 
 namespace {
 
-// one launch over all GEMMs of a sequence: the same (RT, NT, NW) and the same
-// P = V for all (every workgroup takes one range of every GEMM): P is the
+// one launch over all GEMMs of a sequence: the same (RT, NT, NW), the same form
+// of the min term and the same P = V for all (every workgroup takes one range
+// of every GEMM): P is the
 // smallest of the GEMMs' single-launch plans, and must still fit every GEMM's
 // activations (else the sequence cannot run persistent)
 Plan plan_seq(const qgemm_seq* s, int R, std::vector<Plan>* per, bool* fits) {
@@ -356,7 +369,8 @@ Plan plan_seq(const qgemm_seq* s, int R, std::vector<Plan>* per, bool* fits) {
     Plan p = plan_stream(h->NS, h->KB, R, s->cus, s->occ, P);
     if (p.P != P) *fits = false;
     p.P = p.V = P;
-    const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW);
+    p.msum = 0;                    // one kernel for all GEMMs: the min term per step
+    const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW, p.msum != 0);
     if (std::min<int64_t>((p.I + P - 1) / P, h->KB) > cap) *fits = false;
     if (per) per->push_back(p);
     all = p;

@@ -36,17 +36,23 @@ struct StreamArgs {
   uint32_t* err;           // set to 1 when a barrier wait gave up
   int32_t G, R, P;
   int32_t RT, NT, NW;
+  int32_t msum;            // 1: min term from sub-block sums staged with the
+                           // activations (one product per step); 0: from the
+                           // activations themselves (eight products per step)
 };
 
 // Kernel variants: (row tiles RT, sub-tiles per tile NT, waves per workgroup NW).
 // A workgroup (one per CU) holds in LDS the partial tiles of its waves (two per
-// wave) and the activations of the blocks its current range touches, 8 (64 R +
-// 16) + 64 R bytes per block, in what is left of 160 KiB.
+// wave) and the activations of the blocks its current range touches (and their
+// sub-block sums when they are used), in what is left of 160 KiB.
 constexpr int LDS_BYTES = 160 * 1024;
 constexpr int LDS_RESERVED = 1024;              // flags
 inline constexpr int piece_bytes(int RT, int NT, int NW) { return NW * 2 * NT * RT * 1024; }
 inline constexpr int x_area_bytes(int RT, int NT, int NW) { return LDS_BYTES - LDS_RESERVED - piece_bytes(RT, NT, NW); }
-inline int x_slot_capacity(int R, int RT, int NT, int NW) { return x_area_bytes(RT, NT, NW) / (8 * (64 * R + 16) + 64 * R); }
+inline int x_slot_bytes(int R, bool msum) { return 8 * (64 * R + 16) + (msum ? 64 * R : 0); }
+inline int x_slot_capacity(int R, int RT, int NT, int NW, bool msum) {
+  return x_area_bytes(RT, NT, NW) / x_slot_bytes(R, msum);
+}
 inline int waves_for(int RT) { return RT <= 2 ? 8 : 4; }
 inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }

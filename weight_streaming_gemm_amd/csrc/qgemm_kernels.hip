@@ -181,7 +181,7 @@ struct Cursor {
   __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions of GEMM g (load cursor)
 };
 
-template <int RT, int NT, int NW, bool MULTI>
+template <int RT, int NT, int NW, bool MULTI, bool MSUM>
 __global__ void __launch_bounds__(NW * 64, NW / 4)
 stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   constexpr int NTHR = NW * 64;
@@ -195,7 +195,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
   const int XT = 64 * R + 16;                     // LDS bytes of one step's activations
   const int XS = 8 * XT;                          // offset of a block's sub-block sums
-  const int SB = XS + 64 * R;                     // LDS bytes of one block's activations
+  const int SB = XS + (MSUM ? 64 * R : 0);        // LDS bytes of one block's activations
 
   // descriptor of GEMM g; fields of the device table are made explicitly
   // wave-uniform so that buffer resources built from them stay scalar
@@ -343,14 +343,18 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       if (rb >= rows) break;
       const f16x8 op = build_a(xlo[k].x, xlo[k].y, xhi[k].x, xhi[k].y);
       *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + t * XT + (gg * R + rw[k].r) * 16) = op;
-      // sub-block sums: the 8 threads t of lane group gg (8 consecutive lanes) add
-      // their run sums as ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
-      float s0 = sum4_bf16(xlo[k].x, xlo[k].y), s1 = sum4_bf16(xhi[k].x, xhi[k].y);
-      s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
-      s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
-      s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
-      if (t == 0)
-        *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 16) = build_s(s0, s1);
+      if constexpr (MSUM) {
+        // sub-block sums: the 8 threads t of lane group gg (8 consecutive lanes) add
+        // their run sums as ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
+        float s0 = sum4_bf16(xlo[k].x, xlo[k].y), s1 = sum4_bf16(xhi[k].x, xhi[k].y);
+        s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
+        s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
+        s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
+        if (t == 0)
+          *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 16) = build_s(s0, s1);
+        // one row at a time: few values live while the weight ring is in flight
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   // the rest of a range's conversion once its first batch is loaded
@@ -377,24 +381,22 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       for (int rt = 0; rt < RT; ++rt) acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
+  // MSUM: the min term from the staged sub-block sums (one product), else from
+  // the activation operands of the 8 steps (eight products)
   auto compute = [&](const WStage<NT>& st, int slot) __attribute__((always_inline)) {
+    constexpr bool msum = MSUM;
     WConst c[NT];
     f16x8 bm[NT];
     f32x4 ds[NT][RT], ms[NT][RT];
     for (int u = 0; u < NT; ++u) {
       c[u] = header_consts(st.hd[u], g4);
-      bm[u] = build_m(c[u]);
+      bm[u] = msum ? build_m(c[u]) : build_m_full(c[u]);
       for (int rt = 0; rt < RT; ++rt) {
         ds[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         ms[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     const int base = slot * SB;
-    for (int rt = 0; rt < RT; ++rt) {
-      const f16x8 xsum = *reinterpret_cast<const f16x8*>(xlds + base + XS + xoff[rt]);
-      for (int u = 0; u < NT; ++u)
-        ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xsum, bm[u], ms[u][rt], 0, 0, 0);
-    }
     for (int t = 0; t < 8; ++t) {
       f16x8 xa[RT];
       for (int rt = 0; rt < RT; ++rt) {
@@ -404,10 +406,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       for (int u = 0; u < NT; ++u) {
         const uint32_t wd = (t < 4) ? st.qa[u][t] : st.qb[u][t - 4];
         const f16x8 b = build_b(wd, c[u]);
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
           ds[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[u][rt], 0, 0, 0);
+          if constexpr (!msum)
+            ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], bm[u], ms[u][rt], 0, 0, 0);
+        }
       }
     }
+    if constexpr (msum)
+      for (int rt = 0; rt < RT; ++rt) {
+        const f16x8 xsum = *reinterpret_cast<const f16x8*>(xlds + base + XS + xoff[rt]);
+        for (int u = 0; u < NT; ++u)
+          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xsum, bm[u], ms[u][rt], 0, 0, 0);
+      }
     // acc += d * ds - dmin * ms, two fused multiply-adds per element
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt)
@@ -578,11 +589,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   x_load(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
   L = C;
   skip_done(L);
+  // The ring's first loads go out before the activations are staged, so that
+  // they land meanwhile; with sub-block sums (MSUM) they go out after: the
+  // compiler then keeps the ring slots in fixed registers through the step
+  // loop, where across the longer staging code it copies them on every pass
+  // (which waits for every load in flight).
   WStage<NT> W[RING];
-  for (int s = 0; s < RING; ++s) {
-    load_w(W[s], L);
-    next(L);
-  }
+  auto ring_fill = [&]() __attribute__((always_inline)) {
+    for (int s = 0; s < RING; ++s) {
+      load_w(W[s], L);
+      next(L);
+    }
+  };
+  if constexpr (MULTI || !MSUM) ring_fill();
   int xs = 0;                                     // activation slot of C's step
   int ja = 0;                                     // first block of the current segment
   int a_w = 0;                                    // first step of this wave's sub-range
@@ -591,6 +610,10 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   auto step = [&](auto S) __attribute__((always_inline)) -> bool {
     constexpr int s = decltype(S)::value;
     compute(W[s], xs);
+    // keep the refill after the step's last use of the slot, so that the load
+    // writes the slot's own registers (a load hoisted above would need other
+    // registers and a copy, which waits for every load in flight)
+    __builtin_amdgcn_sched_barrier(0);
     load_w(W[s], L);                              // the slot takes the step RING ahead
     next(L);
     const bool tile_end = C.j == C.KB - 1;
@@ -619,23 +642,28 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     a_w = C.it;
     zero_acc();
   };
+  // the unrolled step loop (ring slots 0 .. RING-1); true from STEP ends it
+  auto run_ring = [&](auto STEP) __attribute__((always_inline)) {
+    for (;;) {
+      if (STEP(std::integral_constant<int, 0>{})) break;
+      if (STEP(std::integral_constant<int, 1>{})) break;
+      if (STEP(std::integral_constant<int, 2>{})) break;
+      if (STEP(std::integral_constant<int, 3>{})) break;
+      if constexpr (RING > 4) {
+        if (STEP(std::integral_constant<int, 4 % RING>{})) break;
+        if (STEP(std::integral_constant<int, 5 % RING>{})) break;
+      }
+      if constexpr (RING > 6) {
+        if (STEP(std::integral_constant<int, 6 % RING>{})) break;
+        if (STEP(std::integral_constant<int, 7 % RING>{})) break;
+      }
+    }
+  };
   if constexpr (!MULTI) {
     start_range();
+    if constexpr (MSUM) ring_fill();
     if (C.it < C.it1) {
-      for (;;) {
-        if (step(std::integral_constant<int, 0>{})) break;
-        if (step(std::integral_constant<int, 1>{})) break;
-        if (step(std::integral_constant<int, 2>{})) break;
-        if (step(std::integral_constant<int, 3>{})) break;
-        if constexpr (RING > 4) {
-          if (step(std::integral_constant<int, 4 % RING>{})) break;
-          if (step(std::integral_constant<int, 5 % RING>{})) break;
-        }
-        if constexpr (RING > 6) {
-          if (step(std::integral_constant<int, 6 % RING>{})) break;
-          if (step(std::integral_constant<int, 7 % RING>{})) break;
-        }
-      }
+      run_ring([&](auto S) __attribute__((always_inline)) { return step(S); });
     }
     close_range(C, D);
   } else {
@@ -656,26 +684,9 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
         if (C.it < C.it1) return true;
       }
     };
-    auto mstep = [&](auto S) __attribute__((always_inline)) -> bool {
-      if (!step(S)) return false;
-      return !boundary();
-    };
     start_range();
     if (C.it < C.it1 || boundary()) {
-      for (;;) {
-        if (mstep(std::integral_constant<int, 0>{})) break;
-        if (mstep(std::integral_constant<int, 1>{})) break;
-        if (mstep(std::integral_constant<int, 2>{})) break;
-        if (mstep(std::integral_constant<int, 3>{})) break;
-        if constexpr (RING > 4) {
-          if (mstep(std::integral_constant<int, 4 % RING>{})) break;
-          if (mstep(std::integral_constant<int, 5 % RING>{})) break;
-        }
-        if constexpr (RING > 6) {
-          if (mstep(std::integral_constant<int, 6 % RING>{})) break;
-          if (mstep(std::integral_constant<int, 7 % RING>{})) break;
-        }
-      }
+      run_ring([&](auto S) __attribute__((always_inline)) { return step(S) && !boundary(); });
     }
   }
 
@@ -772,18 +783,23 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
 
 #define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(2, 1, 8) X(3, 1, 4) X(4, 1, 4)
 
-template <int RT, int NT, int NW>
-static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
+template <int RT, int NT, int NW, bool MSUM>
+static hipError_t launch_stream_m(const StreamArgs& a, bool cooperative, hipStream_t st) {
   if (a.G == 1 && !cooperative) {
-    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, false>), dim3((unsigned)a.P), dim3(NW * 64), 0, st, a,
+    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, false, MSUM>), dim3((unsigned)a.P), dim3(NW * 64), 0, st, a,
                        (const GemmDesc*)nullptr);
     return hipGetLastError();
   }
   StreamArgs args = a;
   const GemmDesc* descs = a.descs;
   void* params[] = {&args, &descs};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true>),
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true, MSUM>),
                                     dim3((unsigned)a.P), dim3(NW * 64), params, 0, st);
+}
+template <int RT, int NT, int NW>
+static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
+  return a.msum ? launch_stream_m<RT, NT, NW, true>(a, cooperative, st)
+                : launch_stream_m<RT, NT, NW, false>(a, cooperative, st);
 }
 
 hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st) {
@@ -808,7 +824,7 @@ int stream_occupancy(int RT, int NT, int NW) {
   int blocks = 0;
 #define QG_CASE(rt, nt, nw) \
   if (RT == rt && NT == nt && NW == nw) { \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true>, nw * 64, 0) != \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true, true>, nw * 64, 0) != \
         hipSuccess) \
       return 0; \
     return blocks; \
