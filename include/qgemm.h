@@ -91,6 +91,8 @@ typedef struct {
                                split each step range along K */
     int whole_tile_ranges;  /* 1: each step range is whole output tiles (no partial
                                sums cross workgroups); 0: equal ranges (stream-K) */
+    int k_chunks;           /* K split in this many chunks (when a tile row of
+                               activations does not fit in LDS); 1: whole K */
 } qgemm_info;
 
 /* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights

@@ -35,11 +35,11 @@ def lib():
         L.emu_stream_seq.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                     ctypes.c_uint64]
+                                     ctypes.c_void_p, ctypes.c_uint64]
         L.emu_stream.restype = ctypes.c_int
         L.emu_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                                 ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p]
         L.emu_dequant.restype = ctypes.c_int
         L.emu_dequant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.emu_pack.restype = ctypes.c_int
@@ -48,22 +48,22 @@ def lib():
     return _lib
 
 
-def stream(canon, N, K, x_bits, NT=2, NW=4, V=8, order_seed=0, nwn=1, aligned=0, msum=1):
+def stream(canon, N, K, x_bits, NT=2, NW=4, V=8, order_seed=0, nwn=1, aligned=0, msum=1, chunks=1):
     """One GEMM through the emulated streaming kernel (NW waves in an nwn x NW/nwn
     grid, NT sub-tiles per wave, V ranges: equal step ranges, or whole-tile ranges
-    when aligned; min term from sub-block sums when msum)."""
+    when aligned; min term from sub-block sums when msum; K in `chunks` chunks)."""
     canon = np.ascontiguousarray(canon, dtype=np.uint8)
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     R = x_bits.shape[0]
     y = np.empty((R, N), dtype=np.float32)
     rc = lib().emu_stream(canon.ctypes.data, N, K, x_bits.ctypes.data, R, NT, NW, nwn, V, aligned,
-                             msum, order_seed, y.ctypes.data)
+                             msum, chunks, order_seed, y.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"emu_stream failed ({rc})")
     return y
 
 
-def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None, aligned=None, msums=None):
+def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None, aligned=None, msums=None, chunks=None):
     """Several GEMMs in one emulated launch; mats = [(canon, N, K)], xs = [bf16 bits (R x K)]."""
     G = len(mats)
     canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
@@ -77,10 +77,11 @@ def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None, aligned=N
     nwns = np.array(nwns if nwns is not None else [1] * G, dtype=np.int32)
     aligned = np.array(aligned if aligned is not None else [0] * G, dtype=np.int32)
     msums = np.array(msums if msums is not None else [1] * G, dtype=np.int32)
+    chunks = np.array(chunks if chunks is not None else [1] * G, dtype=np.int32)
     rc = lib().emu_stream_seq(G, P_(*[c.ctypes.data for c in canons]), Ns.ctypes.data, Ks.ctypes.data,
                               P_(*[x.ctypes.data for x in xs]), P_(*[y.ctypes.data for y in ys]), R, NT, NW,
                               nwns.ctypes.data, Vs.ctypes.data, aligned.ctypes.data, msums.ctypes.data,
-                              order_seed)
+                              chunks.ctypes.data, order_seed)
     if rc != 0:
         raise RuntimeError(f"emu_stream_seq failed ({rc})")
     return ys

@@ -77,9 +77,9 @@ int64_t x_slot_of_emu(int64_t j, int64_t j0, int64_t KB) { return (j - j0 + KB) 
 // block (j0 + b) mod KB for b < nslots; slot layout [b][t][gg][r < R] of
 // 16-byte A operands, and per (b, gg, r) the min-term operand from the sums of
 // sub-blocks 2 gg and 2 gg + 1.
-void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, std::vector<f16x8>& slots,
-               std::vector<f16x8>& sums) {
-  const int64_t KB = K / SB_W;
+void convert_x(const uint16_t* x, int R, int64_t K, int64_t jbase, int64_t kbv, int64_t j0, int64_t nslots,
+               std::vector<f16x8>& slots, std::vector<f16x8>& sums) {
+  const int64_t KB = kbv;   // blocks of the step order's tile (a chunk's with K in chunks)
   slots.assign((size_t)nslots * 8 * 4 * R, f16x8{});
   sums.assign((size_t)nslots * 4 * R, f16x8{});
   for (int64_t b = 0; b < nslots; ++b)
@@ -88,6 +88,7 @@ void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, 
         for (int t = 0; t < 8; ++t) {
           int64_t j = j0 + b;
           if (j >= KB) j -= KB;
+          j += jbase;
           const uint16_t* lo = x + (int64_t)r * K + j * SB_W + 64 * gg + 4 * t;
           const uint32_t d0 = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
           const uint32_t d1 = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
@@ -103,6 +104,7 @@ void convert_x(const uint16_t* x, int R, int64_t K, int64_t j0, int64_t nslots, 
       for (int gg = 0; gg < 4; ++gg) {
         int64_t j = j0 + b;
         if (j >= KB) j -= KB;
+        j += jbase;
         float p0[8], p1[8];
         for (int t = 0; t < 8; ++t) {
           const uint16_t* lo = x + (int64_t)r * K + j * SB_W + 64 * gg + 4 * t;
@@ -188,6 +190,7 @@ struct EmuGemm {
   const uint16_t* x;
   float* y;
   int64_t N, K, KB, NS, T, I, V, hdr_off;
+  int64_t S, KBv, Treal;   // K in S chunks of KBv blocks; T = S Treal virtual tiles
   int nwn, aligned, msum;
 };
 
@@ -207,7 +210,8 @@ extern "C" {
 // counter is left armed, -3 on an inconsistent activation slot.
 int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const int64_t* Ks,
                    const uint16_t* const* xs, float* const* ys, int R, int NT, int NW, const int* nwns,
-                   const int64_t* Vs, const int* aligned, const int* msums, uint64_t order_seed) {
+                   const int64_t* Vs, const int* aligned, const int* msums, const int* chunks,
+                   uint64_t order_seed) {
   const int RT = (R + 15) / 16;
   std::vector<EmuGemm> gs((size_t)G);
   int64_t Tmax = 0, Vslots = 0;
@@ -218,26 +222,32 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
     e.aligned = aligned[g];
     e.msum = msums[g];
     if (e.nwn < 1 || NW % e.nwn) return -1;
-    e.T = (e.NS + (int64_t)e.nwn * NT - 1) / ((int64_t)e.nwn * NT);
-    e.I = e.T * e.KB;
+    e.Treal = (e.NS + (int64_t)e.nwn * NT - 1) / ((int64_t)e.nwn * NT);
+    e.S = chunks[g];
+    if (e.S < 1 || e.KB % e.S) return -1;
+    e.KBv = e.KB / e.S;
+    e.T = e.S * e.Treal;
+    e.I = e.T * e.KBv;
     e.V = Vs[g];
     if (e.V > (e.aligned ? e.T : e.I) || e.V < 1) return -1;
+    // K in chunks: ranges of whole tiles of one chunk each
+    if (e.S > 1 && (!e.aligned || e.V % e.S || e.nwn != 1)) return -1;
     e.packed.resize((size_t)packed_bytes(e.N, e.K));
     pack(canon[g], e.packed.data(), e.N, e.K);
     e.hdr_off = quant_region_bytes(e.N, e.K);
     e.x = xs[g];
     e.y = ys[g];
-    Tmax = std::max(Tmax, e.T);
-    Vslots = std::max(Vslots, e.V * e.nwn);
+    Tmax = std::max(Tmax, e.Treal);
+    Vslots = std::max(Vslots, std::max(2 * e.V * e.nwn, e.T * e.nwn));
   }
   const size_t tile_f4 = (size_t)NT * RT * 64;            // f32x4 per wave piece (one column of a tile)
-  std::vector<f32x4> part((size_t)2 * Vslots * tile_f4, f32x4{NAN, NAN, NAN, NAN});
+  std::vector<f32x4> part((size_t)Vslots * tile_f4, f32x4{NAN, NAN, NAN, NAN});
   std::vector<uint32_t> cnt((size_t)Tmax, 0);
   std::vector<f16x8> xslots, xsums;
   std::mt19937_64 rng(order_seed);
   for (int g = 0; g < G; ++g) {
     EmuGemm& e = gs[(size_t)g];
-    const int64_t KB = e.KB;
+    const int64_t KB = e.KBv;   // blocks per tile of the step order
     const int nwn = e.nwn, nwk = NW / e.nwn;
     for (int64_t i = 0; i < (int64_t)R * e.N; ++i) e.y[i] = std::nanf("");
     // column wn of tile t: sub-tiles (t nwn + wn) NT + u
@@ -251,6 +261,14 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
               if (n < e.N && r < R) e.y[(int64_t)r * e.N + n] = v[(size_t)(u * RT + rt) * 64 + lane][i];
             }
     };
+    // a full tile's result: y, or with K in chunks the chunk's partial (slot vt)
+    auto tile_result = [&](int64_t vt, int wn, const f32x4* v) {
+      if (e.S == 1) {
+        write_y(vt, wn, v);
+      } else {
+        std::copy(v, v + tile_f4, part.begin() + (size_t)(vt * nwn + wn) * tile_f4);
+      }
+    };
     std::vector<int64_t> order((size_t)e.V);
     for (int64_t v = 0; v < e.V; ++v) order[(size_t)v] = v;
     std::shuffle(order.begin(), order.end(), rng);
@@ -260,7 +278,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
       const int64_t B = e.aligned ? KB * range_first(v + 1, e.V, e.T) : range_first(v + 1, e.V, e.I);
       const int64_t L = B - A;
       const int64_t j0 = A % KB;
-      convert_x(e.x, R, e.K, j0, x_slots(A, B, KB), xslots, xsums);
+      const int64_t jbase = (A / KB / e.Treal) * KB;          // the range's chunk
+      convert_x(e.x, R, e.K, jbase, KB, j0, x_slots(A, B, KB), xslots, xsums);
       // pieces[wk][slot][wn][tile_f4]
       auto piece = [&](int64_t wk, int sl, int wn) { return (size_t)((wk * 2 + sl) * nwn + wn) * tile_f4; };
       std::vector<f32x4> pieces((size_t)NW * 2 * tile_f4, f32x4{NAN, NAN, NAN, NAN});
@@ -273,12 +292,14 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
           const int64_t t = it / KB, j = it % KB;
           const int64_t b = (it - A) % KB;
           if (b != x_slot_of_emu(j, j0, KB)) return -3;
-          wave_step(e.packed.data(), e.hdr_off, (t * nwn + wn) * NT, NT, e.NS, j, KB, xslots, xsums, R, b, RT,
+          const int64_t tr = t % e.Treal, jr = (t / e.Treal) * KB + j;   // output tile, block
+          if ((t / e.Treal) * KB != jbase) return -3;
+          wave_step(e.packed.data(), e.hdr_off, (tr * nwn + wn) * NT, NT, e.NS, jr, e.KB, xslots, xsums, R, b, RT,
                     e.msum != 0, acc.data());
           const bool sub_end = it + 1 == b_w;
           if (j != KB - 1 && !sub_end) continue;
           if (ja == 0 && j == KB - 1) {
-            write_y(t, wn, acc.data());
+            tile_result(t, wn, acc.data());
           } else {
             const int sl = (a_w > t * KB) ? 0 : 1;
             std::copy(acc.begin(), acc.end(), pieces.begin() + piece(wk, sl, wn));
@@ -304,7 +325,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
             for (size_t k = 0; k < tile_f4; ++k) sum[k] += pieces[piece(kk, sl, wn) + k];
           }
           if (!crossing) {
-            write_y(t, wn, sum.data());
+            tile_result(t, wn, sum.data());
           } else {
             const int64_t gsl = partial_slot(v, t, KB, e.V, e.I);
             std::copy(sum.begin(), sum.end(), part.begin() + (size_t)(gsl * nwn + wn) * tile_f4);
@@ -326,6 +347,21 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
       };
       if (cross_a) arrive(tA);
       if (cross_b && !(cross_a && tB == tA)) arrive(tB);
+      if (e.S > 1 && A < B) {
+        // K in chunks: arrive at the range's output tiles; the last of the S
+        // chunks adds the partials in chunk order
+        for (int64_t t = tA; t <= tB; ++t) {
+          const int64_t tr = t % e.Treal;
+          if (++cnt[(size_t)tr] != (uint32_t)e.S) continue;
+          for (int wn = 0; wn < nwn; ++wn) {
+            std::vector<f32x4> sum(tile_f4, f32x4{0, 0, 0, 0});
+            for (int64_t c = 0; c < e.S; ++c)
+              for (size_t k = 0; k < tile_f4; ++k) sum[k] += part[(size_t)((c * e.Treal + tr) * nwn + wn) * tile_f4 + k];
+            write_y(tr, wn, sum.data());
+          }
+          cnt[(size_t)tr] = 0;
+        }
+      }
     }
     for (int64_t t = 0; t < Tmax; ++t)
       if (cnt[(size_t)t] != 0) return -2;   // a counter was left armed
@@ -334,8 +370,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
 }
 
 int emu_stream(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int NT, int NW, int nwn,
-               int64_t V, int aligned, int msum, uint64_t order_seed, float* y) {
-  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, &aligned, &msum, order_seed);
+               int64_t V, int aligned, int msum, int chunks, uint64_t order_seed, float* y) {
+  return emu_stream_seq(1, &canon, &N, &K, &x, &y, R, NT, NW, &nwn, &V, &aligned, &msum, &chunks, order_seed);
 }
 
 int emu_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {

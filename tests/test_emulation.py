@@ -115,6 +115,26 @@ def test_whole_tile_ranges_match_oracle(orc, N, K, R, NW, V):
     assert m["rel_l2"] < 2e-6
 
 
+@pytest.mark.parametrize("N,K,R,NW,chunks,V,msum", [
+    (640, 5120, 48, 4, 4, 16, 0),     # K in 4 chunks of 5 blocks, 4 ranges per chunk
+    (320, 8192, 48, 4, 8, 16, 1),     # 8 chunks of 4 blocks, 2 ranges per chunk
+    (300, 2048, 24, 8, 2, 6, 0),      # ragged last tile
+    (40, 1536, 33, 4, 3, 3, 1),       # one range per chunk, 3 tiles
+])
+def test_k_chunks_match_oracle_any_order(orc, N, K, R, NW, chunks, V, msum):
+    """K in chunks: each chunk of a tile leaves a partial; the last chunk to
+    arrive adds them in chunk order (same bits in any arrival order)."""
+    canon = synth.matrix_rows(8, 1, N, K)
+    x = synth.x_bf16(8, 2, R, K, outlier_p=0.01)
+    ref = orc.gemm(canon, N, K, x)
+    ys = [emu.stream(canon, N, K, x, NT=1, NW=NW, V=V, aligned=1, msum=msum, chunks=chunks, order_seed=s)
+          for s in range(2)]
+    for y in ys:
+        m = assert_parity(y, ref, f"chunks N={N} K={K} R={R} S={chunks}")
+        assert m["rel_l2"] < 2e-6
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+
+
 def test_sequence_shares_workspace_across_gemms(orc):
     """Several GEMMs of different shapes in one launch reuse the partial slots and
     tile counters; each result still matches the oracle and no counter stays armed."""
@@ -127,6 +147,12 @@ def test_sequence_shares_workspace_across_gemms(orc):
     aligned = [0, 0, 1, 0]         # and its own kind of range
     msums = [1, 0, 1, 0]           # and its own form of the min term
     ys = emu.stream_seq(mats, xs, NT=2, NW=4, Vs=Vs, order_seed=3, nwns=nwns, aligned=aligned, msums=msums)
+    # a GEMM with K in chunks between two others, sharing the workspace
+    chunked = emu.stream_seq([mats[0], (synth.matrix_rows(6, 9, 600, 2048), 600, 2048), mats[2]],
+                             [xs[0], synth.x_bf16(6, 59, R, 2048), xs[2]], NT=1, NW=4, Vs=[5, 8, 5],
+                             order_seed=4, nwns=[1, 1, 4], aligned=[0, 1, 1], msums=[1, 0, 1], chunks=[1, 4, 1])
+    assert_parity(chunked[1], orc.gemm(synth.matrix_rows(6, 9, 600, 2048), 600, 2048, synth.x_bf16(6, 59, R, 2048)),
+                  "seq chunked")
     for (canon, N, K), x, y, V, nwn, al, ms in zip(mats, xs, ys, Vs, nwns, aligned, msums):
         m = assert_parity(y, orc.gemm(canon, N, K, x), f"seq N={N} K={K}")
         assert m["rel_l2"] < 2e-6

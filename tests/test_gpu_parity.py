@@ -116,7 +116,8 @@ def test_gemm_small_workload_all_R(orc, small, R):
 
 
 @pytest.mark.parametrize("N,K,R", [(40, 8192, 12), (1000, 25600, 3), (17, 5120, 7), (5120, 1024, 12),
-                                   (33, 256, 1), (4000, 2048, 48), (4100, 512, 12), (8200, 256, 1)])
+                                   (33, 256, 1), (4000, 2048, 48), (4100, 512, 12), (8200, 256, 1),
+                                   (600, 5120, 64), (1000, 8192, 24), (16390, 2048, 48), (16384, 1024, 64)])
 def test_gemm_ragged_and_split(orc, N, K, R):
     _flush(f"gemm N={N} K={K} R={R}")
     canon, g = G.make(1, 5, N, K, max_R=R)
@@ -128,13 +129,17 @@ def test_gemm_ragged_and_split(orc, N, K, R):
 
 
 def test_plan_kinds_are_exercised():
-    """The shapes above reach both kinds of range: whole tiles and stream-K."""
-    kinds = {}
-    for N, K, R in [(4100, 512, 12), (40, 8192, 12), (4000, 2048, 48)]:
+    """The shapes above reach every kind of plan: whole-tile ranges, stream-K
+    ranges, and K in chunks (activations of a tile row larger than LDS)."""
+    info = {}
+    for N, K, R in [(4100, 512, 12), (40, 8192, 12), (16390, 2048, 48), (16384, 1024, 64)]:
         _, g = G.make(1, 5, N, K, max_R=R)
-        kinds[(N, K, R)] = g.query(R)["whole_tile_ranges"]
+        info[(N, K, R)] = g.query(R)
         g.close()
-    assert kinds[(4100, 512, 12)] == 1 and kinds[(40, 8192, 12)] == 0 and kinds[(4000, 2048, 48)] == 0
+    assert info[(4100, 512, 12)]["whole_tile_ranges"] == 1 and info[(4100, 512, 12)]["k_chunks"] == 1
+    assert info[(40, 8192, 12)]["whole_tile_ranges"] == 0
+    assert info[(16390, 2048, 48)]["k_chunks"] == 2
+    assert info[(16384, 1024, 64)]["k_chunks"] == 2
 
 
 def test_edge_blocks_large_R(orc):

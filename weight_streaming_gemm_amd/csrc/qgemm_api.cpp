@@ -37,6 +37,7 @@ namespace {
 struct Plan {
   int path;
   int RT, NT, NW, nwn, aligned, msum;
+  int64_t S, kbv, treal;   // K in S chunks of kbv blocks (S = 1: kbv = KB) over treal output tiles
   int64_t T, I, V, P;
   size_t part_bytes, cnt_bytes;
 };
@@ -73,6 +74,8 @@ void choose_msum(Plan& p, int64_t KB, int R) {
 Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64_t P_cap = 0) {
   Plan p{};
   p.path = QGEMM_PATH_MFMA;
+  p.S = 1;
+  p.kbv = KB;
   p.RT = (R + 15) / 16;
   p.NW = waves_for(p.RT);
   p.NT = subtiles_for(p.RT);
@@ -93,23 +96,46 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
       p.T = T1;
       p.I = T1 * KB;
       p.V = p.P = V;
+      p.treal = p.T;
       p.part_bytes = 0;
       p.cnt_bytes = (size_t)p.T * 4;
       choose_msum(p, KB, R);
       return p;
     }
   }
+  bool one_round = false;
   for (int nwn = 1; nwn <= p.NW; nwn *= 2) {
     if (p.NW % nwn) break;
     p.nwn = nwn;
     p.T = (NS + (int64_t)nwn * p.NT - 1) / ((int64_t)nwn * p.NT);
     p.I = p.T * KB;
     p.V = std::max<int64_t>(1, std::min(resident, p.I));
-    if (std::min((p.I + p.V - 1) / p.V, KB) <= cap) break;   // one round
-    if (2 * nwn > p.NW || p.NW % (2 * nwn))                  // the widest grid: rounds of
-      p.V = std::min(p.I, std::max(p.V, (p.I + cap - 1) / cap));   // at most cap steps
+    if (std::min((p.I + p.V - 1) / p.V, KB) <= cap) { one_round = true; break; }
+  }
+  if (!one_round) {
+    // No wave grid fits a range's activations in one round: K in S chunks of
+    // kbv blocks (the largest divisor of KB that fits), resident / S ranges of
+    // whole tiles per chunk; each chunk of a tile leaves a partial result.
+    int64_t kc = std::max<int64_t>(1, std::min(cap, KB));
+    while (KB % kc) --kc;
+    p.nwn = 1;
+    p.aligned = 1;
+    p.S = KB / kc;
+    p.kbv = kc;
+    p.treal = T1;
+    // (a range's tiles arrive one thread each: at most NW * 64 tiles per range)
+    const int64_t vc = std::max((T1 + p.NW * 64 - 1) / (p.NW * 64),
+                                std::min(T1, std::max<int64_t>(1, resident / p.S)));
+    p.T = p.S * T1;
+    p.I = p.T * kc;
+    p.V = p.P = p.S * vc;
+    p.part_bytes = (size_t)p.T * partial_slot_bytes(p.RT, p.NT, 1);
+    p.cnt_bytes = (size_t)T1 * 4;
+    choose_msum(p, kc, R);
+    return p;
   }
   p.P = p.V;
+  p.treal = p.T;
   p.part_bytes = (size_t)(2 * p.V) * partial_slot_bytes(p.RT, p.NT, p.nwn);
   p.cnt_bytes = (size_t)p.T * 4;
   choose_msum(p, KB, R);
@@ -135,12 +161,15 @@ GemmDesc make_desc(const qgemm_handle* h, const void* x, float* y, const Plan& p
   d.hdr_bytes = (uint32_t)(packed_bytes(h->N, h->K) - d.quant_bytes);
   d.N = (int32_t)h->N;
   d.NS = (int32_t)h->NS;
-  d.KB = (int32_t)h->KB;
   d.nwn = (int32_t)p.nwn;
   d.T = (int32_t)p.T;
   d.I = (int32_t)p.I;
   d.V = (int32_t)p.V;
   d.aligned = p.aligned;
+  d.KB = (int32_t)p.kbv;                 // blocks per tile of the step order (a chunk's)
+  d.S = (int32_t)p.S;
+  d.kbr = (int32_t)h->KB;
+  d.treal = (int32_t)p.treal;
   return d;
 }
 
@@ -307,6 +336,7 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   info->waves_per_workgroup = p.NW;
   info->wave_columns = p.nwn;
   info->whole_tile_ranges = p.aligned;
+  info->k_chunks = (int)p.S;
   return QGEMM_OK;
 }
 

@@ -23,6 +23,12 @@ struct GemmDesc {
   int32_t aligned;         // 0: V equal ranges of steps; 1: V ranges of whole tiles
                            // (tiles [floor(v T / V), floor((v + 1) T / V))), so that
                            // no tile is shared between ranges
+  // K in S chunks (S > 1 when a tile row of activations does not fit in LDS):
+  // tile t above is then chunk t / treal of output tile t mod treal, KB above is
+  // the chunk's blocks and kbr the row's; each chunk of a tile leaves a partial
+  // result, and the last chunk to arrive adds the S of them in chunk order.
+  int32_t S, kbr, treal;
+  int32_t pad_;
 };
 
 // A launch of the streaming kernel: G GEMMs run one after another (GEMM g + 1

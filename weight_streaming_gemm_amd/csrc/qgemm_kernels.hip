@@ -175,8 +175,9 @@ struct Cursor {
   int A, B;       // the range's steps
   int it, it1;    // current step and end of this wave's sub-range
   int t, j;       // tile and block of step it
+  int tr, jb;     // output tile and first block of tile t's chunk (K in chunks)
   int KB, NS, I, V, T;
-  int aligned;
+  int aligned, S, kbr, treal;
   int nwn, wn, wk, nwk;            // wave grid of GEMM g and this wave's place in it
   __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions of GEMM g (load cursor)
 };
@@ -190,6 +191,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   __shared__ f32x4 pieces[NW * 2 * NT * RT * 64];
   __shared__ uint32_t s_flag;
   __shared__ uint32_t s_last[2];
+  __shared__ uint8_t s_chunk_last[NTHR];         // K in chunks: last arrivals of a range's tiles
 
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
@@ -217,6 +219,9 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       d.I = uni(src->I);
       d.V = uni(src->V);
       d.aligned = uni(src->aligned);
+      d.S = uni(src->S);
+      d.kbr = uni(src->kbr);
+      d.treal = uni(src->treal);
       return d;
     } else {
       return a.d0;
@@ -235,6 +240,15 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     c.it1 = uni(c.A + (int)range_first<uint32_t>(c.wk + 1, c.nwk, c.B - c.A));
     c.t = uni(c.it / c.KB);
     c.j = uni(c.it - c.t * c.KB);
+    const int cc = uni(c.t / c.treal);
+    c.tr = uni(c.t - cc * c.treal);
+    c.jb = uni(cc * c.KB);
+  };
+  // the cursor's tile advances by one (and into the next chunk after the last tile)
+  auto next_tile = [&](Cursor& c) __attribute__((always_inline)) {
+    c.t = uni(c.t + 1);
+    c.tr = uni(c.tr + 1);
+    if (c.tr == c.treal) { c.tr = 0; c.jb = uni(c.jb + c.KB); }
   };
   auto enter = [&](Cursor& c, int g) __attribute__((always_inline)) {
     c.g = g;
@@ -242,6 +256,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       c.v = 0; c.V = 1; c.A = c.B = 0;
       c.it = 1; c.it1 = 0;
       c.t = 0; c.j = 0; c.KB = 1; c.NS = 0; c.I = 0; c.T = 0; c.aligned = 0;
+      c.tr = 0; c.jb = 0; c.S = 1; c.kbr = 1; c.treal = 1;
       c.nwn = 1; c.wn = 0; c.wk = w; c.nwk = NW;
       c.qr = make_rsrc(nullptr, 0);
       c.hr = make_rsrc(nullptr, 0);
@@ -255,6 +270,9 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     c.I = d.I;
     c.T = d.T;
     c.aligned = d.aligned;
+    c.S = d.S;
+    c.kbr = d.kbr;
+    c.treal = d.treal;
     c.nwn = d.nwn;
     c.nwk = uni(NW / d.nwn);
     c.wn = uni(w % d.nwn);
@@ -274,17 +292,17 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   auto next = [&](Cursor& c) __attribute__((always_inline)) {
     c.it = uni(c.it + 1);
     c.j = uni(c.j + 1);
-    if (c.j == c.KB) { c.j = 0; c.t = uni(c.t + 1); }
+    if (c.j == c.KB) { c.j = 0; next_tile(c); }
     skip_done(c);
   };
 
   // ---- weights: RING steps ahead -----------------------------------------------
   auto load_w = [&](WStage<NT>& st, const Cursor& c) __attribute__((always_inline)) {
     for (int u = 0; u < NT; ++u) {
-      const int ns = (c.t * c.nwn + c.wn) * NT + u;
+      const int ns = (c.tr * c.nwn + c.wn) * NT + u;
       const bool ok = c.it < c.it1 && ns < c.NS;
-      const uint32_t qo = ok ? (uint32_t)(ns * c.KB + c.j) * CHUNK_Q + lane * 16 : OOB;
-      const uint32_t ho = ok ? (uint32_t)(ns * c.KB + c.j) * CHUNK_H + nl * 16 : OOB;
+      const uint32_t qo = ok ? (uint32_t)(ns * c.kbr + c.jb + c.j) * CHUNK_Q + lane * 16 : OOB;
+      const uint32_t ho = ok ? (uint32_t)(ns * c.kbr + c.jb + c.j) * CHUNK_H + nl * 16 : OOB;
       st.qa[u] = bload<u32x4, 2>(c.qr, qo);
       st.qb[u] = bload<u32x4, 2>(c.qr, qo + 1024);
       st.hd[u] = bload<u32x4, 2>(c.hr, ho);
@@ -317,9 +335,9 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       if (r >= R) { r -= R; ++b; }
     }
   };
-  auto x_load = [&](const GemmDesc& d, int j0, int nslots, int base) __attribute__((always_inline)) {
+  auto x_load = [&](const GemmDesc& d, int jbase, int j0, int nslots, int base) __attribute__((always_inline)) {
     const int sub = tid & 31, gg = sub >> 3, t = sub & 7;
-    const int K = d.KB * SB_W;
+    const int K = d.kbr * SB_W;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
     const int rows = nslots * R;
     XRow rw[XB];
@@ -328,7 +346,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       const int rb = base + k * XGROUPS;
       int j = j0 + rw[k].b;
       if (j >= d.KB) j -= d.KB;
-      const uint32_t off = (uint32_t)((rw[k].r * K + j * SB_W + 64 * gg + 4 * t) * 2);
+      const uint32_t off = (uint32_t)((rw[k].r * K + (jbase + j) * SB_W + 64 * gg + 4 * t) * 2);
       xlo[k] = bload<u32x2, 0>(xr, rb < rows ? off : OOB);
       xhi[k] = bload<u32x2, 0>(xr, rb < rows ? off + 64 : OOB);
     }
@@ -358,11 +376,11 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     }
   };
   // the rest of a range's conversion once its first batch is loaded
-  auto x_convert_rest = [&](const GemmDesc& d, int j0, int nslots) __attribute__((always_inline)) {
+  auto x_convert_rest = [&](const GemmDesc& d, int jbase, int j0, int nslots) __attribute__((always_inline)) {
     const int rows = nslots * R;
     x_store(nslots, tid >> 5);
     for (int base = (tid >> 5) + XB * XGROUPS; base < rows; base += XB * XGROUPS) {
-      x_load(d, j0, nslots, base);
+      x_load(d, jbase, j0, nslots, base);
       x_store(nslots, base);
     }
   };
@@ -445,6 +463,19 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
         }
     }
   };
+  // the result of tile t (column wn) of the cursor's GEMM: y, or with K in
+  // chunks the chunk's partial result, in slot t of the partial buffer
+  auto tile_result = [&](const Cursor& c, const GemmDesc& d, int t, int wn, const f32x4 (&v)[NT][RT])
+      __attribute__((always_inline)) {
+    if (c.S == 1) {
+      write_y(d, t, wn, v);
+    } else {
+      const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, (uint32_t)(c.T * c.nwn * NT * RT * 1024));
+      for (int u = 0; u < NT; ++u)
+        for (int rt = 0; rt < RT; ++rt)
+          bstore_sc1(v[u][rt], pr, (uint32_t)(((((t * c.nwn + wn) * NT + u) * RT + rt) * 64 + lane) * 16));
+    }
+  };
   // LDS piece (sub-range wk, slot sl, column wn): one per wave and slot
   auto piece_at = [&](int nwn, int wk, int sl, int wn, int u, int rt) __attribute__((always_inline)) -> f32x4& {
     return pieces[(((((wk * 2 + sl) * nwn + wn) * NT + u) * RT + rt) * 64) + lane];
@@ -453,7 +484,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // LDS slot 0 (the segment starts inside the tile) or 1
   auto finish_segment = [&](const Cursor& c, const GemmDesc& d, int ja, int a_w) __attribute__((always_inline)) {
     if (ja == 0 && c.j == c.KB - 1) {
-      write_y(d, c.t, c.wn, acc);
+      tile_result(c, d, c.t, c.wn, acc);
       return;
     }
     const int sl = (a_w > c.t * c.KB) ? 0 : 1;
@@ -524,7 +555,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
           for (int rt = 0; rt < RT; ++rt) sum[u][rt] += piece_at(nwn, kk, sl, wn, u, rt);
       }
       if (!crossing) {
-        write_y(d, t, wn, sum);
+        tile_result(c, d, t, wn, sum);
       } else {
         const int gs = (int)partial_slot<uint32_t>(c.v, t, KB, c.V, c.I);
         const __amdgpu_buffer_rsrc_t pr = part_rsrc(c);
@@ -560,6 +591,47 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
         if (last & 2u) __hip_atomic_store(a.cnt + tB, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    if (c.S > 1 && A < B) {
+      // K in chunks: the range holds whole tiles of one chunk.  Arrive at each of
+      // their output tiles (one thread per tile); the last of the S chunks to
+      // arrive adds the S partial results in chunk order and writes y.
+      __builtin_amdgcn_s_waitcnt(0);              // this thread's partial stores are complete
+      __syncthreads();
+      const int cc = tA / c.treal, r0 = tA - cc * c.treal, count = tB - tA + 1;
+      if (tid < count) {
+        const uint32_t old = __hip_atomic_fetch_add(a.cnt + r0 + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_chunk_last[tid] = old == (uint32_t)(c.S - 1) ? 1 : 0;
+      }
+      __syncthreads();
+      const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, (uint32_t)(c.T * nwn * NT * RT * 1024));
+      constexpr int FB = RT == 1 ? 8 : (RT == 2 ? 4 : 2);
+      for (int pi = w; pi < count * nwn; pi += NW) {
+        const int i = pi / nwn, wn = pi - i * nwn;
+        if (!s_chunk_last[i]) continue;
+        const int tr = r0 + i;
+        f32x4 sum[NT][RT];
+        for (int u = 0; u < NT; ++u)
+          for (int rt = 0; rt < RT; ++rt) sum[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < c.S; q0 += FB) {
+          f32x4 v[FB][NT][RT];
+          for (int k = 0; k < FB; ++k) {
+            const int vt = (q0 + k) * c.treal + tr;
+            for (int u = 0; u < NT; ++u)
+              for (int rt = 0; rt < RT; ++rt)
+                v[k][u][rt] = bload<f32x4, SC1>(
+                    pr, q0 + k < c.S ? (uint32_t)(((((vt * nwn + wn) * NT + u) * RT + rt) * 64 + lane) * 16) : OOB);
+          }
+          for (int k = 0; k < FB; ++k)
+            if (q0 + k < c.S)
+              for (int u = 0; u < NT; ++u)
+                for (int rt = 0; rt < RT; ++rt) sum[u][rt] += v[k][u][rt];
+        }
+        write_y(d, tr, wn, sum);
+      }
+      __syncthreads();
+      if (tid < count && s_chunk_last[tid])
+        __hip_atomic_store(a.cnt + r0 + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();                              // pieces and activations may be reused
   };
 
@@ -586,7 +658,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   Cursor L, C;
   enter(C, 0);
   GemmDesc D = get_desc(0);
-  x_load(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
+  x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
   L = C;
   skip_done(L);
   // The ring's first loads go out before the activations are staged, so that
@@ -626,7 +698,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     if (sub_end) return true;
     C.it = uni(C.it + 1);
     C.j = uni(C.j + 1);
-    if (C.j == C.KB) { C.j = 0; C.t = uni(C.t + 1); }
+    if (C.j == C.KB) { C.j = 0; next_tile(C); }
     xs = uni(xs + 1);
     if (xs == C.KB) xs = 0;
     return false;
@@ -635,7 +707,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // One range per workgroup and GEMM (the host sizes V = P).
   // (the first activation batch is already in flight)
   auto start_range = [&]() __attribute__((always_inline)) {
-    x_convert_rest(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB));
+    x_convert_rest(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB));
     __syncthreads();
     xs = uni((C.it - C.A) % C.KB);
     ja = C.j;
@@ -679,7 +751,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
         grid_barrier(C.g);
         enter(C, C.g + 1);
         D = get_desc(C.g);
-        x_load(D, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
+        x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
         start_range();
         if (C.it < C.it1) return true;
       }
