@@ -231,7 +231,8 @@ def main():
     bytes_per_launch = pass_bytes / len(gemms)
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
     info = gemms[0].query(args.R)
-    kname = f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}>"
+    kname = (f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}, {info['waves_per_workgroup']}, "
+             f"false, *> (both min-term variants, all 257 GEMMs)")
     log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
         f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
 
