@@ -113,6 +113,40 @@ def time_dominant_kernel(gemms, xs, ys, R: int, reps: int):
     return e0.elapsed_time(e1) / launches, launches
 
 
+def time_paths(gemms, xs, ys, Rs, reps: int = 5):
+    """ms per pass (the 257 streaming kernels, no argmax) on each kernel path for
+    each R: the measurement behind the automatic choice between the vector-unit
+    and matrix-core kernels.  One graph of the pass per (path, R), replayed."""
+    import torch
+    from weight_streaming_gemm_amd import qgemm as Q
+    out = {}
+    for R in Rs:
+        rec = {}
+        for name, path in (("valu", Q.PATH_VALU), ("mfma", Q.PATH_MFMA)):
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                for g, x, y in zip(gemms, xs, ys):
+                    g.run(x[:R], y[:R], R, path=path)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for g, x, y in zip(gemms, xs, ys):
+                    g.run(x[:R], y[:R], R, path=path)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            rec[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+            del graph
+        rec["auto"] = "valu" if gemms[0].query(R)["path"] == Q.PATH_VALU else "mfma"
+        out[str(R)] = rec
+    return out
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP library's sources: identifies the kernel a counter run measured."""
     import hashlib
@@ -236,6 +270,11 @@ def main():
     log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
         f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
 
+    paths = time_paths(gemms, xs, ys, [r for r in (1, 2, 3, 4) if r <= R_max])
+    for R, rec in paths.items():
+        log(f"[paths] R={R}: vector-unit {rec['valu_ms']:.4f} ms/pass, matrix-core {rec['mfma_ms']:.4f} "
+            f"ms/pass, automatic choice {rec['auto']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.seed)
@@ -265,6 +304,7 @@ def main():
             "rows_tok_per_s": round(args.R * 1000 / ms, 1),
             "ms_per_pass_by_R": {str(k): round(v, 5) for k, v in results.items()},
             "flatness_t12_over_t1": round(results[12] / results[1], 4) if 1 in results and 12 in results else None,
+            "kernel_paths_ms_per_pass_by_R": paths,
         },
         "roofline": {
             "bound": "hbm",

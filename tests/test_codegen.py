@@ -10,7 +10,11 @@ the product path, that each group of matrix-core instructions in the step loop
 is preceded by a wait that leaves the later stages in flight, and that no
 streaming kernel spills to scratch (the offline packer keeps a block in private
 memory; it is not on the timed path).  The persistent variant with two row
-tiles is left out: its loop still copies ring slots (a known slow spot).
+tiles is left out: its loop still copies ring slots (a known slow spot).  The
+vector-unit variants (one per row count 1..4) are checked the same way on
+their groups of dot-product instructions; there the compiler issues the
+refill of a stage before the stage's dot products, so the wait may count the
+refill's loads as well, but it must still leave the later stages in flight.
 """
 from __future__ import annotations
 
@@ -36,15 +40,15 @@ def asm(tmp_path_factory):
     return out.read_text()
 
 
-def _kernel_body(asm: str, rt: int, nw: int, multi: bool, msum: bool) -> str:
-    name = (f"_ZN2qg13stream_kernelILi{rt}ELi1ELi{nw}ELb{int(multi)}ELb{int(msum)}"
+def _kernel_body(asm: str, rt: int, nw: int, multi: bool, msum: bool, vr: int = 0) -> str:
+    name = (f"_ZN2qg13stream_kernelILi{rt}ELi1ELi{nw}ELb{int(multi)}ELb{int(msum)}ELi{vr}"
             "EEEvNS_10StreamArgsEPKNS_8GemmDescE")
     start = asm.index(name + ":")
     return asm[start:asm.index("s_endpgm", start)]
 
 
-def _mfma_groups(body: str):
-    """(wait before the group, group size) for each run of MFMAs with no vmcnt wait inside."""
+def _mfma_groups(body: str, op: str = "v_mfma"):
+    """(wait before the group, group size) for each run of `op` instructions with no vmcnt wait inside."""
     groups, last_wait, n = [], None, 0
     for line in body.splitlines():
         s = line.strip()
@@ -53,7 +57,7 @@ def _mfma_groups(body: str):
                 groups.append((last_wait, n))
                 n = 0
             last_wait = int(re.search(r"vmcnt\((\d+)\)", s).group(1))
-        elif s.startswith("v_mfma"):
+        elif re.match(op, s):
             n += 1
     if n:
         groups.append((last_wait, n))
@@ -91,4 +95,16 @@ def test_persistent_step_loop_keeps_ring_in_flight(asm, rt, nw):
 @pytest.mark.parametrize("msum", [False, True])
 def test_stream_kernels_do_not_spill(asm, rt, nw, multi, msum):
     body = _kernel_body(asm, rt, nw, multi, msum)
+    assert "scratch_store" not in body and "scratch_load" not in body
+
+
+@pytest.mark.parametrize("vr", [1, 2, 3, 4])
+def test_vector_unit_step_loop_keeps_ring_in_flight(asm, vr):
+    body = _kernel_body(asm, 1, 8, False, True, vr)
+    per_step = 32 * vr                                   # 8 operand pairs x 4 dot products per row
+    steps = [(w, n) for w, n in _mfma_groups(body, r"v_dot2c?_f32_f16") if n >= per_step]
+    assert len(steps) >= RING, steps
+    for w, n in steps:
+        assert n == per_step, f"{n} dot products under one wait"
+        assert (RING - 1) * LOADS_PER_STAGE <= w <= RING * LOADS_PER_STAGE, f"step waits vmcnt({w})"
     assert "scratch_store" not in body and "scratch_load" not in body

@@ -56,6 +56,47 @@ def test_layer_matrix_sampled(orc, which, R):
     g.close()
 
 
+@pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
+def test_layer_matrix_sampled_vector_unit(orc, which):
+    """The vector-unit kernel on the full layer shapes, R = 1 and 3."""
+    from weight_streaming_gemm_amd import qgemm as Q
+    import weight_streaming_gemm_amd as wsg
+    seed = W.SEED_LAYER
+    m = {mm.name: mm for mm in W.layer_mats(0)}[which]
+    canon = fused_canon(seed, m)
+    packed = G.upload_packed(canon, m.N, m.K)
+    g = wsg.QGemm(packed, m.N, m.K, max_R=4)
+    for R in (1, 3):
+        print(f"valu layer {which} N={m.N} K={m.K} R={R}", flush=True)
+        x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+        y = G.run(g, x, path=Q.PATH_VALU)
+        ns = sample_ns(m.N, 96, R)
+        ref = orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, x)
+        assert_parity(y[:, ns], ref, f"valu {which} R={R}")
+    g.close()
+
+
+def test_vector_unit_k_chunks_sampled(orc):
+    """A shape whose step ranges outgrow LDS at R = 4 even with 8 wave columns:
+    the vector-unit kernel runs K in two chunks."""
+    from weight_streaming_gemm_amd import qgemm as Q
+    import weight_streaming_gemm_amd as wsg
+    N, K, R = 32768, 16384, 4
+    print(f"valu chunks N={N} K={K} R={R}", flush=True)
+    canon = synth.matrix_rows(11, 2, N, K)
+    packed = G.upload_packed(canon, N, K)
+    g = wsg.QGemm(packed, N, K, max_R=R)
+    info = g.query(R, Q.PATH_VALU)
+    assert info["k_chunks"] == 2, info
+    x = synth.x_bf16(11, 3, R, K, outlier_p=0.01)
+    y = G.run(g, x, path=Q.PATH_VALU)
+    ns = sample_ns(N, 96, 5)
+    rows = np.concatenate([synth.matrix_rows(11, 2, N, K, n0=n, n1=n + 1) for n in ns])
+    ref = orc.gemm(rows, len(ns), K, x)
+    assert_parity(y[:, ns], ref, "valu chunks")
+    g.close()
+
+
 def test_output_head_argmax_and_sampled_parity(orc):
     import torch
     import weight_streaming_gemm_amd as wsg

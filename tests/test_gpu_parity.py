@@ -196,6 +196,56 @@ def test_row_count_zero_and_errors(small):
     assert float(y.abs().sum()) == 0.0
 
 
+# ---- vector-unit path (R <= 4) -------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(256, 1024), (33, 256), (17, 5120), (40, 8192), (4100, 512), (8200, 256),
+                                 (5120, 1024), (1000, 25600)])
+def test_vector_unit_path(orc, N, K):
+    from weight_streaming_gemm_amd import qgemm as Q
+    canon, g = G.make(3, 7, N, K, max_R=4)
+    for R in (1, 2, 3, 4):
+        _flush(f"valu N={N} K={K} R={R}")
+        info = g.query(R, Q.PATH_VALU)
+        assert info["path"] == Q.PATH_VALU and info["row_tiles"] == 0
+        x = synth.x_bf16(3, 10 + R, R, K, outlier_p=0.01)
+        assert_parity(G.run(g, x, path=Q.PATH_VALU), orc.gemm(canon, N, K, x),
+                      f"valu N={N} K={K} R={R} wgs={info['workgroups']}")
+    g.close()
+
+
+def test_vector_unit_path_edge_blocks_and_determinism(orc):
+    from weight_streaming_gemm_amd import qgemm as Q
+    N, K = 512, 2048
+    canon, g = G.make(4, 0, N, K, max_R=4, edge_mode=1)
+    for R in (1, 4):
+        _flush(f"valu edge R={R}")
+        x = synth.x_bf16(4, 50 + R, R, K)
+        y1 = G.run(g, x, path=Q.PATH_VALU)
+        assert_parity(y1, orc.gemm(canon, N, K, x), f"valu edge R={R}")
+        y2 = G.run(g, x, path=Q.PATH_VALU)
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    g.close()
+
+
+def test_vector_unit_path_plan_kinds_and_errors(small):
+    """Whole-tile and stream-K ranges both reach the vector-unit kernel; it
+    serves R <= 4 only."""
+    import torch
+    from weight_streaming_gemm_amd import qgemm as Q
+    for N, K, aligned in [(4100, 512, 1), (40, 8192, 0)]:
+        _, g = G.make(1, 5, N, K, max_R=4)
+        assert g.query(4, Q.PATH_VALU)["whole_tile_ranges"] == aligned
+        g.close()
+    canon, g = small
+    x = torch.zeros((5, 1024), dtype=torch.int16, device="cuda")
+    y = torch.zeros((5, 256), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert Q.lib().qgemm_run_path(g.h, x.data_ptr(), y.data_ptr(), 5, Q.PATH_VALU, st) == Q.QGEMM_EPATH
+    assert Q.lib().qgemm_query(g.h, 5, Q.PATH_VALU, ctypes.byref(Q.Info())) == Q.QGEMM_EPATH
+    torch.cuda.synchronize()
+    assert float(y.abs().sum()) == 0.0
+
+
 # ---- argmax -------------------------------------------------------------------
 
 def test_argmax_ties_and_nan():

@@ -27,12 +27,9 @@
 // Size: NS * KB * (2048 + 256) = Np * KB * 144 bytes, i.e. the canonical size
 // of the padded matrix (padding rows are all-zero blocks).
 //
-// Activation operand layout (written by the staging kernel from bf16 x):
-//   xq  (binary16): element (rt, j, t, l, e), l = 16 g + r', row r = 16 rt + r',
-//       at ((rt*KB + j)*8 + t)*64*8 + l*8 + e, slot e = 2v + hbit holds
-//       x[r, 256 j + 64 g + 32 hbit + 4 t + v]; rows r >= R hold zero.
-//   xs  (fp32): element (rt, j, l, hbit) at ((rt*KB + j)*64 + l)*2 + hbit holds
-//       the sum of x[r, k] over sub-block 2g + hbit of block j.
+// Activation operands (staged by the streaming kernel into LDS, see there): for
+// row r, step t and lane group g, the binary16 A operand element e = 2v + hbit
+// holds x[r, 256 j + 64 g + 32 hbit + 4 t + v] (operand_k below).
 #pragma once
 #include <stdint.h>
 

@@ -71,9 +71,13 @@ void choose_msum(Plan& p, int64_t KB, int R) {
 // range's activations must fit the workgroup's LDS: nwn is the smallest wave
 // grid width for which they do (wider tiles mean fewer steps per range); if
 // none does, the widest grid runs ranges of at most cap steps in several rounds.
-Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64_t P_cap = 0) {
+//
+// valu: the same schedule for the vector-unit kernel (R <= VALU_MAX_R, one row
+// tile), which always takes the min term from the staged sub-block sums.
+Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64_t P_cap = 0,
+                 bool valu = false) {
   Plan p{};
-  p.path = QGEMM_PATH_MFMA;
+  p.path = valu ? QGEMM_PATH_VALU : QGEMM_PATH_MFMA;
   p.S = 1;
   p.kbv = KB;
   p.RT = (R + 15) / 16;
@@ -81,7 +85,13 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
   p.NT = subtiles_for(p.RT);
   int64_t resident = (int64_t)cus * std::max(1, occ[p.RT]);
   if (P_cap > 0) resident = std::min(resident, P_cap);
-  const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW, false);
+  const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW, valu);
+  auto min_term = [&](int64_t kb) {
+    if (valu)
+      p.msum = 1;
+    else
+      choose_msum(p, kb, R);
+  };
   // Ranges of whole tiles need no partial sums across workgroups (whose
   // exchange costs a few memory round trips at the end of a range, worth about
   // FIXUP_STEPS steps); they are taken when every workgroup gets a tile, a
@@ -99,7 +109,7 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
       p.treal = p.T;
       p.part_bytes = 0;
       p.cnt_bytes = (size_t)p.T * 4;
-      choose_msum(p, KB, R);
+      min_term(KB);
       return p;
     }
   }
@@ -131,24 +141,28 @@ Plan plan_stream(int64_t NS, int64_t KB, int R, int cus, const int occ[5], int64
     p.V = p.P = p.S * vc;
     p.part_bytes = (size_t)p.T * partial_slot_bytes(p.RT, p.NT, 1);
     p.cnt_bytes = (size_t)T1 * 4;
-    choose_msum(p, kc, R);
+    min_term(kc);
     return p;
   }
   p.P = p.V;
   p.treal = p.T;
   p.part_bytes = (size_t)(2 * p.V) * partial_slot_bytes(p.RT, p.NT, p.nwn);
   p.cnt_bytes = (size_t)p.T * 4;
-  choose_msum(p, KB, R);
+  min_term(KB);
   return p;
 }
 
 // the kernel's schedule arithmetic is 32-bit: (V + 1) * I must stay below 2^31
 bool plan_fits(const Plan& p) { return (p.V + 1) * (p.I + 1) < (int64_t(1) << 31); }
 
+// The R-dependent choice: the vector-unit kernel for R <= VALU_AUTO_MAX_R (the
+// measured crossover: below it the vector-unit kernel streams faster), the
+// matrix-core kernel above.
 int make_plan(const qgemm_handle* h, int R, int path, Plan* out) {
-  if (path == QGEMM_PATH_VALU) return QGEMM_EPATH;
-  if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA) return QGEMM_EINVAL;
-  *out = plan_stream(h->NS, h->KB, R, h->cus, h->occ);
+  if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA && path != QGEMM_PATH_VALU) return QGEMM_EINVAL;
+  if (path == QGEMM_PATH_VALU && R > VALU_MAX_R) return QGEMM_EPATH;
+  const bool valu = path == QGEMM_PATH_VALU || (path == QGEMM_PATH_AUTO && R <= VALU_AUTO_MAX_R);
+  *out = plan_stream(h->NS, h->KB, R, h->cus, h->occ, 0, valu);
   return plan_fits(*out) ? QGEMM_OK : QGEMM_ESHAPE;
 }
 
@@ -191,6 +205,7 @@ int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStrea
   a.NT = p.NT;
   a.NW = p.NW;
   a.msum = p.msum;
+  a.valu = p.path == QGEMM_PATH_VALU;
   return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
@@ -262,15 +277,16 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
   }
   fill_occupancy(h->occ);
   size_t part = 0, cnt = 0;
-  for (int R = 1; R <= max_R; ++R) {
-    Plan p = plan_stream(h->NS, h->KB, R, h->cus, h->occ);
-    if (!plan_fits(p)) {
-      delete h;
-      return QGEMM_ESHAPE;
+  for (int R = 1; R <= max_R; ++R)
+    for (int valu = 0; valu < (R <= VALU_MAX_R ? 2 : 1); ++valu) {
+      Plan p = plan_stream(h->NS, h->KB, R, h->cus, h->occ, 0, valu != 0);
+      if (!plan_fits(p)) {
+        delete h;
+        return QGEMM_ESHAPE;
+      }
+      part = std::max(part, p.part_bytes);
+      cnt = std::max(cnt, p.cnt_bytes);
     }
-    part = std::max(part, p.part_bytes);
-    cnt = std::max(cnt, p.cnt_bytes);
-  }
   part = std::max<size_t>(part, 256);
   h->part_bytes = part;
   h->cnt_bytes = cnt;
@@ -325,7 +341,7 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
   info->path = p.path;
-  info->row_tiles = p.RT;
+  info->row_tiles = p.path == QGEMM_PATH_VALU ? 0 : p.RT;
   info->subtiles_per_wave = p.NT;
   info->tiles = p.T;
   info->workgroups = p.P;

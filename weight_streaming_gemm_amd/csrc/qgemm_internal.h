@@ -45,7 +45,10 @@ struct StreamArgs {
   int32_t msum;            // 1: min term from sub-block sums staged with the
                            // activations (one product per step); 0: from the
                            // activations themselves (eight products per step)
+  int32_t valu;            // 1: vector-unit variant (R <= 4, msum = 1, one GEMM)
 };
+constexpr int VALU_MAX_R = 4;       // rows the vector-unit kernel serves
+constexpr int VALU_AUTO_MAX_R = 0;  // rows for which the automatic choice takes it
 
 // Kernel variants: (row tiles RT, sub-tiles per tile NT, waves per workgroup NW).
 // A workgroup (one per CU) holds in LDS the partial tiles of its waves (two per

@@ -182,9 +182,17 @@ struct Cursor {
   __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions of GEMM g (load cursor)
 };
 
-template <int RT, int NT, int NW, bool MULTI, bool MSUM>
+// VR > 0: the vector-unit variant for exactly VR rows (RT = NT = 1, MSUM): dot
+// products of the binary16 operands on the vector units instead of the matrix
+// cores, one lane per (output, lane group), reduced over the 4 lane groups at
+// the end of each segment into the matrix-core accumulator layout.
+constexpr int VROWS = 4;
+
+template <int RT, int NT, int NW, bool MULTI, bool MSUM, int VR = 0>
 __global__ void __launch_bounds__(NW * 64, NW / 4)
 stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
+  constexpr bool VALU = VR > 0;
+  static_assert(VR <= VROWS && (!VALU || (RT == 1 && NT == 1 && MSUM && !MULTI)), "vector-unit variant: one row tile");
   constexpr int NTHR = NW * 64;
   constexpr int XAREA = x_area_bytes(RT, NT, NW);
   __shared__ __attribute__((aligned(16))) uint8_t xlds[XAREA];
@@ -394,9 +402,59 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   }
 
   f32x4 acc[NT][RT];
+  float vacc[VR > 0 ? VR : 1];                    // vector-unit variant: row r of this lane's output
   auto zero_acc = [&]() __attribute__((always_inline)) {
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt) acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (VALU)
+      for (int r = 0; r < VR; ++r) vacc[r] = 0.f;
+  };
+  // vector-unit variant, end of a segment: add the 4 lane groups' sums of each
+  // row ((g0 + g1) + (g2 + g3) in every lane) and take the matrix-core layout:
+  // lane (g, n) holds rows 4g .. 4g + 3 of output n
+  auto vacc_to_acc = [&]() __attribute__((always_inline)) {
+    float tot[VR > 0 ? VR : 1];
+    for (int r = 0; r < VR; ++r) {
+      float v = vacc[r];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      tot[r] = v;
+    }
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+      for (int r = 0; r < VR; ++r)
+        if (r == 4 * g4 + i) v = tot[r];
+      acc[0][0][i] = v;
+    }
+  };
+
+  // the vector-unit step: for each row r < R, the lane's 64 weights (sub-blocks
+  // 2g, 2g + 1 of output n) times x as binary16 pairs (v_dot2_f32_f16: exact
+  // products, fp32 sums), then d and the min term from the sub-block sums
+  auto compute_valu = [&](const WStage<NT>& st, int slot) __attribute__((always_inline)) {
+    const WConst c = header_consts(st.hd[0], g4);
+    float ds[VR > 0 ? VR : 1];
+    for (int r = 0; r < VR; ++r) ds[r] = 0.f;
+    const int base = slot * SB;
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t wd = (t < 4) ? st.qa[0][t] : st.qb[0][t - 4];
+      const f16x8 b = build_b(wd, c);
+      for (int r = 0; r < VR; ++r) {
+        const f16x8 x8 = *reinterpret_cast<const f16x8*>(xlds + base + t * XT + (g4 * R + r) * 16);
+        float v = ds[r];
+        for (int e = 0; e < 8; e += 2)
+          v = __builtin_amdgcn_fdot2(f16x2{b[e], b[e + 1]}, f16x2{x8[e], x8[e + 1]}, v, false);
+        ds[r] = v;
+      }
+    }
+    for (int r = 0; r < VR; ++r) {
+      const f16x8 sm = *reinterpret_cast<const f16x8*>(xlds + base + XS + (g4 * R + r) * 16);
+      // min term of the lane's two sub-blocks: m_2g (hi + lo of X_2g) + m_2g+1 (hi + lo of X_2g+1)
+      const float x0 = (float)sm[0] + (float)sm[2], x1 = (float)sm[1] + (float)sm[3];
+      const float mt = __builtin_fmaf((float)c.m[0], x0, (float)c.m[1] * x1);
+      vacc[r] = __builtin_fmaf(c.d, ds[r], vacc[r]);
+      vacc[r] = __builtin_fmaf(c.nmin, mt, vacc[r]);
+    }
   };
 
   // MSUM: the min term from the staged sub-block sums (one product), else from
@@ -681,7 +739,10 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // one step at ring position s; true at the end of this wave's sub-range
   auto step = [&](auto S) __attribute__((always_inline)) -> bool {
     constexpr int s = decltype(S)::value;
-    compute(W[s], xs);
+    if constexpr (VALU)
+      compute_valu(W[s], xs);
+    else
+      compute(W[s], xs);
     // keep the refill after the step's last use of the slot, so that the load
     // writes the slot's own registers (a load hoisted above would need other
     // registers and a copy, which waits for every load in flight)
@@ -691,6 +752,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     const bool tile_end = C.j == C.KB - 1;
     const bool sub_end = C.it + 1 == C.it1;
     if (tile_end || sub_end) {
+      if constexpr (VALU) vacc_to_acc();
       finish_segment(C, D, ja, a_w);
       zero_acc();
       ja = 0;
@@ -870,6 +932,21 @@ static hipError_t launch_stream_m(const StreamArgs& a, bool cooperative, hipStre
 }
 template <int RT, int NT, int NW>
 static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
+  if constexpr (RT == 1 && NT == 1 && NW == 8) {
+    if (a.valu) {
+      if (a.G != 1 || cooperative || !a.msum || a.R < 1 || a.R > VROWS) return hipErrorInvalidValue;
+      const dim3 grid((unsigned)a.P), block(NW * 64);
+      const GemmDesc* nd = nullptr;
+      switch (a.R) {
+        case 1: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 1>), grid, block, 0, st, a, nd); break;
+        case 2: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 2>), grid, block, 0, st, a, nd); break;
+        case 3: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 3>), grid, block, 0, st, a, nd); break;
+        default: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 4>), grid, block, 0, st, a, nd); break;
+      }
+      return hipGetLastError();
+    }
+  }
+  if (a.valu) return hipErrorInvalidValue;
   return a.msum ? launch_stream_m<RT, NT, NW, true>(a, cooperative, st)
                 : launch_stream_m<RT, NT, NW, false>(a, cooperative, st);
 }
