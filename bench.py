@@ -147,6 +147,143 @@ def time_paths(gemms, xs, ys, Rs, reps: int = 5):
     return out
 
 
+def graph_ms(calls, reps: int = 5) -> float:
+    """ms per replay of a graph of the given launches (captured once, warmed once)."""
+    import torch
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / reps
+
+
+def layer_report(seed: int, edge: int, Rs, copies: int):
+    """One layer's four GEMMs (Q|K|V, O, gate|up, down), `copies` rotating weight
+    copies so that no replay is served from the 256 MB Infinity Cache: per-matrix
+    and per-layer time, GB/s and % of 8 TB/s for each R, on the matrix-core path
+    and (R <= 4) on the vector-unit path; useful TFLOP/s against the fp16 dense
+    matrix-core peak."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import workloads as W
+    import weight_streaming_gemm_amd as wsg
+    from weight_streaming_gemm_amd import qgemm as Q
+    from weight_streaming_gemm_amd import roofline as RF
+    dev = torch.device("cuda:0")
+    R_max = max(Rs)
+    mats = W.layer_mats(0)
+    per = []
+    for m in mats:
+        canon = np.concatenate([synth.matrix_rows(seed, mid, n, m.K, edge_mode=edge) for mid, n in zip(m.mids, m.splits)])
+        cd = torch.from_numpy(canon).to(dev)
+        pk = torch.empty(wsg.packed_size(m.N, m.K), dtype=torch.uint8, device=dev)
+        wsg.pack(cd, pk, m.N, m.K)
+        torch.cuda.synchronize()
+        del cd
+        pks = [pk] + [pk.clone() for _ in range(copies - 1)]
+        gs = [wsg.QGemm(q, m.N, m.K, max_R=R_max) for q in pks]
+        x = torch.from_numpy(synth.x_bf16(seed, W.X_STREAM[m.K], R_max, m.K).view(np.int16)).to(dev)
+        y = torch.empty((R_max, m.N), dtype=torch.float32, device=dev)
+        per.append((m, pks, gs, x, y))
+    layer_bytes = sum(m.packed_bytes for m in mats)
+    out = {}
+    for R in Rs:
+        rec = {}
+        for pname, path in (("mfma", Q.PATH_MFMA), ("valu", Q.PATH_VALU)):
+            if path == Q.PATH_VALU and R > 4:
+                continue
+            prec = {}
+            for m, pks, gs, x, y in per:
+                us = graph_ms([lambda g=g, x=x, y=y: g.run(x[:R], y[:R], R, path=path) for g in gs]) / copies * 1e3
+                prec[m.name] = {"us": round(us, 2), "GB_s": round(m.packed_bytes / us / 1e3, 1),
+                                "pct_hbm_peak": round(m.packed_bytes / us / 1e3 / RF.HBM_PEAK_GBS * 100, 1)}
+                if pname == "mfma":
+                    prec[m.name]["useful_tflop_s"] = round(2 * R * m.N * m.K / us / 1e6, 1)
+            calls = []
+            for c in range(copies):
+                for m, pks, gs, x, y in per:
+                    calls.append(lambda g=gs[c], x=x, y=y: g.run(x[:R], y[:R], R, path=path))
+            us = graph_ms(calls) / copies * 1e3
+            prec["layer"] = {"us": round(us, 2), "GB_s": round(layer_bytes / us / 1e3, 1),
+                             "pct_hbm_peak": round(layer_bytes / us / 1e3 / RF.HBM_PEAK_GBS * 100, 1)}
+            if pname == "mfma":
+                flops = sum(2 * R * m.N * m.K for m in mats)
+                prec["layer"]["useful_tflop_s"] = round(flops / us / 1e6, 1)
+                prec["layer"]["pct_fp16_mfma_peak"] = round(flops / us / 1e6 / RF.MFMA_F16_DENSE_TFLOPS * 100, 2)
+            rec[pname] = prec
+            log(f"[layer seed={seed} edge={edge}] R={R:2d} {pname}: " +
+                ", ".join(f"{k} {v['us']:.1f} us" for k, v in prec.items()))
+        out[str(R)] = rec
+    for m, pks, gs, x, y in per:
+        for g in gs:
+            g.close()
+    return {"seed": seed, "edge_blocks": bool(edge), "copies": copies, "layer_packed_bytes": layer_bytes,
+            "by_R": out}
+
+
+def ragged_report(seed: int, steps: int):
+    """The full pass under a seeded schedule of active agents: step t runs R_t =
+    3 * a_t rows (a_t uniform in 1..4), with fresh activations per step (1 % of
+    them scaled by 50).  Each step is one graph replay of the 257 GEMMs and the
+    head's argmax; every step's graph is captured before timing."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import workloads as W
+    import weight_streaming_gemm_amd as wsg
+    from weight_streaming_gemm_amd import roofline as RF
+    sched = W.ragged_schedule(seed, steps)
+    mats, gemms, packed, _, ys, idx = build_pass(max(sched), seed)
+    dev = torch.device("cuda:0")
+    xs_t = []
+    for t, R in enumerate(sched):
+        by_w = {w: torch.from_numpy(synth.x_bf16(seed, 1000 * (t + 1) + sid, R, w, outlier_p=0.01).view(np.int16))
+                .to(dev) for w, sid in W.X_STREAM.items()}
+        xs_t.append([by_w[m.K] for m in mats])
+    seq = wsg.Seq(gemms)
+    for t, R in enumerate(sched):                                  # capture every step's graph
+        seq.run(xs_t[t], [y[:R] for y in ys], R, argmax_idx=idx)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sched]
+    t0 = time.perf_counter()
+    for t, R in enumerate(sched):
+        ev[t][0].record()
+        seq.run(xs_t[t], [y[:R] for y in ys], R, argmax_idx=idx)
+        ev[t][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pass_bytes = W.pass_bytes()
+    by_r = {str(R): round(float(ms[np.array(sched) == R].mean()), 4) for R in sorted(set(sched))}
+    seq.close()
+    for g in gemms:
+        g.close()
+    return {"seed": seed, "steps": steps, "rows_by_step": sched,
+            "ms_per_step": {"mean": round(float(ms.mean()), 4), "median": round(float(np.median(ms)), 4),
+                            "min": round(float(ms.min()), 4), "max": round(float(ms.max()), 4),
+                            "p90": round(float(np.percentile(ms, 90)), 4)},
+            "ms_per_step_by_R": by_r,
+            "GB_s_mean": round(pass_bytes / ms.mean() / 1e6, 1),
+            "pct_hbm_peak_mean": round(pass_bytes / ms.mean() / 1e6 / RF.HBM_PEAK_GBS * 100, 2),
+            "rows_tok_per_s": round(sum(sched) / (ms.sum() / 1e3), 1),
+            "wall_s": round(wall, 3)}
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP library's sources: identifies the kernel a counter run measured."""
     import hashlib
@@ -216,6 +353,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB three times: a kernel of known "
                          "traffic for scaling the HBM byte counters of a profiler run")
+    ap.add_argument("--report", choices=["layer", "ragged"],
+                    help="instead of the pass: 'layer' = one layer's GEMMs per matrix and R on both kernel paths "
+                         "(plain weights, seed 1, R in 1,2,3,4,12,24,48; then edge-block weights, seed 4, R in "
+                         "24,48); 'ragged' = 100 passes under the seeded 1..4-agent schedule (seed 3)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -229,6 +370,15 @@ def main():
     from synth import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.report == "layer":
+        rep = {"report": "layer", "unit": "us per GEMM (graph replay over rotating weight copies)",
+               "layer": layer_report(W.SEED_LAYER, 0, [1, 2, 3, 4, 12, 24, 48], copies=6),
+               "large_R_edge_blocks": layer_report(W.SEED_LARGE_R, 2, [24, 48], copies=6)}
+        print(json.dumps(rep), flush=True)
+        return
+    if args.report == "ragged":
+        print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
+        return
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
     R_max = max(sweep)
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)

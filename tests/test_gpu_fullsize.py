@@ -97,6 +97,46 @@ def test_vector_unit_k_chunks_sampled(orc):
     g.close()
 
 
+def test_ragged_schedule_sampled_steps(orc):
+    """The agent schedule (R_t = 3 a_t, fresh activations with 1 % outliers per
+    step) through one graph-mode sequence over layer 0's GEMMs: R changes from
+    step to step; sampled outputs of every step are checked, and a repeated step
+    gives the same bits."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    seed = W.SEED_RAGGED
+    sched = W.ragged_schedule(seed, 100)
+    steps = [sched.index(R) for R in (3, 6, 9, 12)] + [10, 11]
+    mats = W.layer_mats(0)
+    gs, canons = [], []
+    for m in mats:
+        canon = fused_canon(seed, m)
+        gs.append(wsg.QGemm(G.upload_packed(canon, m.N, m.K), m.N, m.K, max_R=12))
+        canons.append(canon)
+    seq = wsg.Seq(gs)
+    ys = [torch.empty((12, m.N), dtype=torch.float32, device="cuda") for m in mats]
+    first = {}
+    for t in steps + steps[:1]:
+        R = sched[t]
+        print(f"ragged step {t} R={R}", flush=True)
+        xs_np = [synth.x_bf16(seed, 1000 * (t + 1) + W.X_STREAM[m.K], R, m.K, outlier_p=0.01) for m in mats]
+        seq.run([G.to_dev(x) for x in xs_np], [y[:R] for y in ys], R)
+        torch.cuda.synchronize()
+        got = [y[:R].cpu().numpy() for y in ys]
+        if t in first:
+            for a, b in zip(got, first[t]):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+            continue
+        first[t] = got
+        for i, m in enumerate(mats):
+            ns = sample_ns(m.N, 48, t)
+            canon_rows = canons[i].reshape(m.N, -1)[ns].ravel()
+            assert_parity(got[i][:, ns], orc.gemm(canon_rows, len(ns), m.K, xs_np[i]), f"ragged t={t} {m.name}")
+    seq.close()
+    for g in gs:
+        g.close()
+
+
 def test_output_head_argmax_and_sampled_parity(orc):
     import torch
     import weight_streaming_gemm_amd as wsg
