@@ -65,7 +65,7 @@ def _mfma_groups(body: str, op: str = "v_mfma"):
 
 
 # (RT, waves) of the product variants, single-GEMM and persistent, both min-term forms
-VARIANTS = [(1, 8), (2, 8), (3, 4), (4, 4)]
+VARIANTS = [(1, 8), (2, 8), (3, 8), (4, 8)]
 
 
 @pytest.mark.parametrize("rt,nw", VARIANTS)
@@ -80,7 +80,7 @@ def test_single_gemm_step_loop_keeps_ring_in_flight(asm, rt, nw, msum):
         assert w == (RING - 1) * LOADS_PER_STAGE, f"step waits vmcnt({w})"
 
 
-@pytest.mark.parametrize("rt,nw", [(1, 8), (3, 4), (4, 4)])
+@pytest.mark.parametrize("rt,nw", [(1, 8), (3, 8), (4, 8)])
 def test_persistent_step_loop_keeps_ring_in_flight(asm, rt, nw):
     body = _kernel_body(asm, rt, nw, True, False)
     per_step = 16 * rt

@@ -62,7 +62,7 @@ inline int x_slot_bytes(int R, bool msum) { return 8 * (64 * R + 16) + (msum ? 6
 inline int x_slot_capacity(int R, int RT, int NT, int NW, bool msum) {
   return x_area_bytes(RT, NT, NW) / x_slot_bytes(R, msum);
 }
-inline int waves_for(int RT) { return RT <= 2 ? 8 : 4; }
+inline int waves_for(int RT) { (void)RT; return 8; }   // two waves per SIMD at every row count
 inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }
 

@@ -872,34 +872,60 @@ dequant_kernel(const uint8_t* __restrict__ packed, float* __restrict__ w, int64_
 }
 
 // ---------------------------------------------------------------------------
-// per-row argmax, lowest index among equal maxima; NaN never wins
+// per-row argmax, lowest index among equal maxima; NaN never wins.  One
+// workgroup per row; the row is read as 16-byte vectors (after a scalar head up
+// to 16-byte alignment), four independent loads in flight per thread, so one
+// workgroup streams its row at close to a CU's load bandwidth.  Which thread
+// sees which element does not matter: (value, lowest index) is the same maximum
+// in any order.
 __global__ void __launch_bounds__(1024)
 argmax_kernel(const float* __restrict__ y, int64_t N, int32_t* __restrict__ idx) {
-  __shared__ float sv[1024];
-  __shared__ int64_t si[1024];
+  constexpr int NT = 1024, U = 4;
+  __shared__ float sv[NT / 64];
+  __shared__ int64_t si[NT / 64];
   const int64_t r = blockIdx.x;
   const float* row = y + r * N;
+  const int tid = threadIdx.x;
   float bv = -__builtin_inff();
   int64_t bi = N;                      // N = "none yet"
-  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
-    float v = row[n];
-    if (v > bv || (bi == N && v == bv)) { bv = v; bi = n; }
-  }
-  sv[threadIdx.x] = bv;
-  si[threadIdx.x] = bi;
-  __syncthreads();
-  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
-    if ((int)threadIdx.x < st) {
-      float ov = sv[threadIdx.x + st];
-      int64_t oi = si[threadIdx.x + st];
-      float mv = sv[threadIdx.x];
-      int64_t mi = si[threadIdx.x];
-      bool take = (oi != N) && (mi == N || ov > mv || (ov == mv && oi < mi));
-      if (take) { sv[threadIdx.x] = ov; si[threadIdx.x] = oi; }
+  auto take = [&](float v, int64_t n) {
+    if (v > bv || (v == bv && n < bi)) { bv = v; bi = n; }
+  };
+  const int64_t mis = (int64_t)((16u - ((uintptr_t)row & 15u)) & 15u) / 4;
+  const int64_t head = mis < N ? mis : N;
+  if (tid < head) take(row[tid], tid);
+  const int64_t nvec = (N - head) / 4;
+  const float4* vrow = reinterpret_cast<const float4*>(row + head);
+  for (int64_t i0 = 0; i0 < nvec; i0 += (int64_t)NT * U) {
+    float4 v[U];
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT + tid;
+      v[u] = i < nvec ? vrow[i] : make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                              __builtin_nanf(""));
     }
-    __syncthreads();
+    for (int u = 0; u < U; ++u) {
+      const int64_t n = head + 4 * (i0 + (int64_t)u * NT + tid);
+      take(v[u].x, n);
+      take(v[u].y, n + 1);
+      take(v[u].z, n + 2);
+      take(v[u].w, n + 3);
+    }
   }
-  if (threadIdx.x == 0) idx[r] = (int32_t)(si[0] == N ? 0 : si[0]);
+  for (int64_t n = head + 4 * nvec + tid; n < N; n += NT) take(row[n], n);
+  // wave, then workgroup: keep the larger value, the lower index on ties; "none"
+  // (index N) loses to anything
+  auto merge = [&](float ov, int64_t oi) {
+    if (oi != N && (bi == N || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+  };
+  for (int off = 32; off > 0; off >>= 1) merge(__shfl_xor(bv, off), __shfl_xor(bi, off));
+  if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
+  __syncthreads();
+  if (tid < 64) {
+    bv = tid < NT / 64 ? sv[tid] : -__builtin_inff();
+    bi = tid < NT / 64 ? si[tid] : N;
+    for (int off = 32; off > 0; off >>= 1) merge(__shfl_xor(bv, off), __shfl_xor(bi, off));
+    if (tid == 0) idx[r] = (int32_t)(bi == N ? 0 : bi);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -915,7 +941,7 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
   return hipGetLastError();
 }
 
-#define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(2, 1, 8) X(3, 1, 4) X(4, 1, 4)
+#define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(2, 1, 8) X(3, 1, 8) X(4, 1, 8)
 
 template <int RT, int NT, int NW, bool MSUM>
 static hipError_t launch_stream_m(const StreamArgs& a, bool cooperative, hipStream_t st) {
