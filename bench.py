@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB three times: a kernel of known "
                          "traffic for scaling the HBM byte counters of a profiler run")
+    ap.add_argument("--no-paths", action="store_true",
+                    help="skip timing the pass on each kernel path for R = 1..4 (for profiler runs of one R)")
     ap.add_argument("--report", choices=["layer", "ragged"],
                     help="instead of the pass: 'layer' = one layer's GEMMs per matrix and R on both kernel paths "
                          "(plain weights, seed 1, R in 1,2,3,4,12,24,48; then edge-block weights, seed 4, R in "
@@ -416,12 +418,12 @@ def main():
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
     info = gemms[0].query(args.R)
     kname = (f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}, {info['waves_per_workgroup']}, "
-             f"false, *> (both min-term variants, all 257 GEMMs)")
+             f"false, *, 0> (both min-term variants, all 257 GEMMs)")
     log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
         f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
 
-    paths = time_paths(gemms, xs, ys, [r for r in (1, 2, 3, 4) if r <= R_max])
-    for R, rec in paths.items():
+    paths = None if args.no_paths else time_paths(gemms, xs, ys, [r for r in (1, 2, 3, 4) if r <= R_max])
+    for R, rec in (paths or {}).items():
         log(f"[paths] R={R}: vector-unit {rec['valu_ms']:.4f} ms/pass, matrix-core {rec['mfma_ms']:.4f} "
             f"ms/pass, automatic choice {rec['auto']}")
 
