@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB three times: a kernel of known "
                          "traffic for scaling the HBM byte counters of a profiler run")
+    ap.add_argument("--rows", default="",
+                    help="with --report layer: only these row counts (comma-separated), e.g. for counter runs")
     ap.add_argument("--no-paths", action="store_true",
                     help="skip timing the pass on each kernel path for R = 1..4 (for profiler runs of one R)")
     ap.add_argument("--report", choices=["layer", "ragged"],
@@ -373,9 +375,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.report == "layer":
+        only = {int(v) for v in args.rows.split(",") if v}
+        plain = [r for r in (1, 2, 3, 4, 12, 24, 48) if not only or r in only]
+        edge = [r for r in (24, 48) if not only or r in only]
         rep = {"report": "layer", "unit": "us per GEMM (graph replay over rotating weight copies)",
-               "layer": layer_report(W.SEED_LAYER, 0, [1, 2, 3, 4, 12, 24, 48], copies=6),
-               "large_R_edge_blocks": layer_report(W.SEED_LARGE_R, 2, [24, 48], copies=6)}
+               "layer": layer_report(W.SEED_LAYER, 0, plain, copies=6) if plain else None,
+               "large_R_edge_blocks": layer_report(W.SEED_LARGE_R, 2, edge, copies=6) if edge else None}
         print(json.dumps(rep), flush=True)
         return
     if args.report == "ragged":
