@@ -240,7 +240,8 @@ def ragged_report(seed: int, steps: int):
     """The full pass under a seeded schedule of active agents: step t runs R_t =
     3 * a_t rows (a_t uniform in 1..4), with fresh activations per step (1 % of
     them scaled by 50).  Each step is one graph replay of the 257 GEMMs and the
-    head's argmax; every step's graph is captured before timing."""
+    head's argmax (one graph per row count, captured before timing); the timed
+    events bracket the pass only, not the copy of the step's activations."""
     import numpy as np
     import torch
     import synth
@@ -250,21 +251,30 @@ def ragged_report(seed: int, steps: int):
     sched = W.ragged_schedule(seed, steps)
     mats, gemms, packed, _, ys, idx = build_pass(max(sched), seed)
     dev = torch.device("cuda:0")
-    xs_t = []
-    for t, R in enumerate(sched):
-        by_w = {w: torch.from_numpy(synth.x_bf16(seed, 1000 * (t + 1) + sid, R, w, outlier_p=0.01).view(np.int16))
-                .to(dev) for w, sid in W.X_STREAM.items()}
-        xs_t.append([by_w[m.K] for m in mats])
+    # every step's activations, resident; before its pass a step's are copied
+    # into the fixed input buffers of its row count (outside the timed events),
+    # so that the sequence replays one graph per row count
+    xs_t = [{w: torch.from_numpy(synth.x_bf16(seed, 1000 * (t + 1) + sid, R, w, outlier_p=0.01).view(np.int16))
+             .to(dev) for w, sid in W.X_STREAM.items()} for t, R in enumerate(sched)]
+    xbuf = {R: {w: torch.empty((R, w), dtype=torch.int16, device=dev) for w in W.X_STREAM} for R in set(sched)}
     seq = wsg.Seq(gemms)
-    for t, R in enumerate(sched):                                  # capture every step's graph
-        seq.run(xs_t[t], [y[:R] for y in ys], R, argmax_idx=idx)
+
+    def one_step(t, R, ev=None):
+        for w in W.X_STREAM:
+            xbuf[R][w].copy_(xs_t[t][w])
+        if ev:
+            ev[0].record()
+        seq.run([xbuf[R][m.K] for m in mats], [y[:R] for y in ys], R, argmax_idx=idx)
+        if ev:
+            ev[1].record()
+
+    for t, R in enumerate(sched):                                  # warm: one graph per row count
+        one_step(t, R)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sched]
     t0 = time.perf_counter()
     for t, R in enumerate(sched):
-        ev[t][0].record()
-        seq.run(xs_t[t], [y[:R] for y in ys], R, argmax_idx=idx)
-        ev[t][1].record()
+        one_step(t, R, ev[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in ev])

@@ -175,7 +175,11 @@ int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32
  * already streams the next GEMM's weights while it waits; the first run for a
  * given (R, pointer set) uploads a descriptor table (synchronous).  Do not
  * capture a persistent run into a graph (cooperative launch).  Runs of one
- * sequence share workspace: one stream at a time.
+ * sequence share workspace: one stream at a time.  Without the flag, the first
+ * run for a given (R, pointer set, argmax_idx) captures the launches into a
+ * graph that later runs replay.  The sequence keeps at most 64 such graphs (and
+ * 64 descriptor tables); a run that needs one more first waits for the device
+ * and drops all of them.
  * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays, QGEMM_ENOMEM. */
 int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
                   int32_t *argmax_idx, void *stream);

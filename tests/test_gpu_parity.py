@@ -246,6 +246,34 @@ def test_vector_unit_path_plan_kinds_and_errors(small):
     assert float(y.abs().sum()) == 0.0
 
 
+def test_seq_graph_cache_bound(orc):
+    """More (R, pointer set) combinations than a sequence caches graphs for: the
+    cache is dropped and rebuilt, and every run still gives the oracle's result."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    shapes = [(64, 512), (40, 256)]
+    mats = [G.make(12, i, N, K, max_R=4) for i, (N, K) in enumerate(shapes)]
+    seq = wsg.Seq([g for _, g in mats])
+    R = 2
+    xs_np = [synth.x_bf16(12, 30 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    xs = [G.to_dev(x) for x in xs_np]
+    refs = [orc.gemm(c, N, K, x) for (c, _), (N, K), x in zip(mats, shapes, xs_np)]
+    outs = [[torch.empty((R, N), dtype=torch.float32, device="cuda") for N, K in shapes] for _ in range(70)]
+    for rep in range(2):
+        _flush(f"seq cache pass {rep}")
+        for ys in outs:
+            for y in ys:
+                y.fill_(-3.0)
+            seq.run(xs, ys, R)
+        torch.cuda.synchronize()
+        for ys in outs:
+            for y, ref in zip(ys, refs):
+                assert_parity(y.cpu().numpy(), ref, "seq cache")
+    seq.close()
+    for _, g in mats:
+        g.close()
+
+
 # ---- argmax -------------------------------------------------------------------
 
 def test_argmax_ties_and_nan():

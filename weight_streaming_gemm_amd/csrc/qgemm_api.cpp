@@ -430,6 +430,23 @@ Plan plan_seq(const qgemm_seq* s, int R, std::vector<Plan>* per, bool* fits) {
   return all;
 }
 
+// Cached graphs and descriptor tables per (R, pointer set): at most this many
+// of each; a run that needs another waits for the device and drops them all
+// (a graph or table may still be in use by work in flight).
+constexpr size_t SEQ_CACHE_MAX = 64;
+
+void seq_drop_graphs(qgemm_seq* s) {
+  (void)hipDeviceSynchronize();
+  for (auto& kv : s->graphs) (void)hipGraphExecDestroy(kv.second);
+  s->graphs.clear();
+}
+
+void seq_drop_descs(qgemm_seq* s) {
+  (void)hipDeviceSynchronize();
+  for (auto& kv : s->descs) (void)hipFree(kv.second);
+  s->descs.clear();
+}
+
 void seq_free(qgemm_seq* s) {
   for (auto& kv : s->graphs) (void)hipGraphExecDestroy(kv.second);
   if (s->cap) (void)hipStreamDestroy(s->cap);
@@ -525,6 +542,7 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
     key.ptrs.push_back(reinterpret_cast<uintptr_t>(argmax_idx));
     auto g = s->graphs.find(key);
     if (g == s->graphs.end()) {
+      if (s->graphs.size() >= SEQ_CACHE_MAX) seq_drop_graphs(s);
       if (hipStreamBeginCapture(s->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return QGEMM_EHIP;
       int rc = QGEMM_OK;
       for (size_t i = 0; i < s->hs.size() && rc == QGEMM_OK; ++i)
@@ -552,6 +570,7 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
   if (!fits) return QGEMM_EPATH;
   auto it = s->descs.find(key);
   if (it == s->descs.end()) {
+    if (s->descs.size() >= SEQ_CACHE_MAX) seq_drop_descs(s);
     std::vector<GemmDesc> host(s->hs.size());
     for (size_t i = 0; i < s->hs.size(); ++i) host[i] = make_desc(s->hs[i], xs[i], ys[i], per[i]);
     GemmDesc* dev = nullptr;
