@@ -295,15 +295,21 @@ def ragged_report(seed: int, steps: int):
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the HIP library's sources: identifies the kernel a counter run measured."""
+    """sha256 over the HIP library's sources with comments and blank space
+    removed: identifies the code a counter run measured (a comment edit does
+    not make the counters stale; any code change does)."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "weight_streaming_gemm_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # the sources hold no "//" or "/*" in literals
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -88,16 +88,27 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 // Work.  The NW waves of a workgroup form an nwn x (NW / nwn) grid: nwn side by
 // side along N, NW / nwn along K (nwn is chosen per GEMM).  A tile is nwn * NT
 // 16-output sub-tiles; tile t needs KB block steps.  The T * KB (tile, block)
-// steps of a GEMM are cut into V equal contiguous ranges; workgroup p (one per
-// CU) takes ranges p, p + P, ..., so every CU streams the same number of bytes
-// whatever the matrix shape.  Inside a range, each row of nwn waves takes an
-// equal contiguous sub-range, each wave its NT sub-tiles of every tile.
+// steps of a GEMM are cut into V = P contiguous ranges, one per workgroup (one
+// workgroup per CU): equal ranges (stream-K: every CU streams the same bytes
+// whatever the matrix shape), or ranges of whole tiles when the host finds the
+// uneven split cheaper than sharing tiles.  When a tile row of activations does
+// not fit in LDS, K is cut into S chunks of KB blocks and the ranges hold whole
+// tiles of one chunk ("virtual" tiles c * treal + t).  Inside a range, each row
+// of nwn waves takes an equal contiguous sub-range, each wave its NT sub-tiles
+// of every tile.
 //
 // Sums.  A wave writes a tile it covers alone straight to y.  The pieces of a
 // tile shared by several waves meet in LDS and are added, after the range, in
 // wave order.  A tile shared with other ranges leaves the workgroup's sum in a
 // global partial slot; the last range to finish the tile adds the slots in
-// range order.  Every sum has a fixed order, so results are deterministic.
+// range order (with K chunks: the chunks' partial tiles, in chunk order).
+// Every sum has a fixed order, so results are deterministic.
+//
+// Min term.  Either eight more matrix-core products per step with B = m_s
+// (MSUM = false), or, when a range uses each block for several steps, one
+// product per step of the sub-block sums of x, staged with the activations
+// (MSUM = true).  The vector-unit variant (VR = R <= 4 rows) replaces the
+// products by dot products on the vector units and always uses the sums.
 //
 // Streams.  At the start of a range the workgroup converts the activations of
 // the blocks the range touches (R rows x 256 bf16 each) into the matrix-core
