@@ -56,6 +56,9 @@ class Oracle:
         lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_verify_greedy.restype = ctypes.c_int
+        lib.oracle_verify_greedy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_argmax_rows.restype = ctypes.c_int
         lib.oracle_argmax_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_void_p]
@@ -113,6 +116,20 @@ class Oracle:
         idx = np.empty(R, dtype=np.int32)
         self._check(self.lib.oracle_argmax_rows(y.ctypes.data, R, N, idx.ctypes.data), "argmax")
         return idx
+
+
+    def verify_greedy(self, argmax_rows, drafts, drafts_per_agent: int):
+        """(tokens [A, D + 1] int32, -1 past n_new; n_new [A] int32) for argmax rows
+        [A (D + 1)] and drafts [A, D]."""
+        D = int(drafts_per_agent)
+        am = np.ascontiguousarray(argmax_rows, dtype=np.int32).ravel()
+        A = am.size // (D + 1)
+        dr = np.ascontiguousarray(drafts, dtype=np.int32).reshape(A, D) if D > 0 else np.zeros((A, 0), np.int32)
+        tokens = np.empty((A, D + 1), dtype=np.int32)
+        n_new = np.empty(A, dtype=np.int32)
+        self._check(self.lib.oracle_verify_greedy(am.ctypes.data, am.size, dr.ctypes.data if D > 0 else None, D,
+                                                  tokens.ctypes.data, n_new.ctypes.data), "verify")
+        return tokens, n_new
 
 
 _default = None

@@ -29,6 +29,7 @@
  *   5. the fp32 dequantised weight is the double w rounded once to nearest-even
  *      (C's double -> float conversion under the default rounding mode);
  *   6. per-row argmax over y, lowest index on ties.
+ *   7. greedy verification of the agents' draft tokens against the argmax rows.
  *
  * Build-time switch ORACLE_MUTANT (default 0) plants one deliberate mistake so
  * that the pin tests can show they would catch it; release builds never set it.
@@ -222,6 +223,47 @@ int oracle_gemm(const uint8_t *canon, int64_t N, int64_t K, const uint16_t *x, i
     for (int t = 1; t < nthreads; t++) pthread_join(th[t], 0);
     for (int t = 0; t < nthreads; t++)
         if (jobs[t].rc) return jobs[t].rc;
+    return ORACLE_OK;
+}
+
+/* 7. Greedy verification of the draft tokens of each agent.  Agent a owns rows
+ * a (D + 1) .. a (D + 1) + D of the pass: its current token, then its D draft
+ * tokens drafts[a D + i] (OpenJet multi-agent serving page, section on moving
+ * the weights only once: every agent contributes its next token plus drafts,
+ * and the drafts are checked in the same round).  Row i's argmax p_i is the
+ * model's choice for the position after row i's input, so draft i (the input of
+ * row i + 1) stands iff it equals p_i, and p_{i+1} is then valid too.  The agent
+ * emits p_0, then p_{i+1} for each draft accepted in order, stopping at the
+ * first rejected one: n_new[a] = 1 + (number of drafts accepted); tokens[a (D +
+ * 1) + j] holds the j-th emitted token, -1 past n_new[a]. */
+int oracle_verify_greedy(const int32_t *argmax, int64_t R, const int32_t *drafts, int64_t D,
+                         int32_t *tokens, int32_t *n_new)
+{
+    if (!argmax || !tokens || !n_new || D < 0 || R < 0 || R % (D + 1) != 0) return ORACLE_EARG;
+    if (D > 0 && !drafts) return ORACLE_EARG;
+    const int64_t A = R / (D + 1);
+    for (int64_t a = 0; a < A; a++) {
+        const int64_t base = a * (D + 1);
+        for (int64_t j = 0; j <= D; j++) tokens[base + j] = -1;
+        int64_t n = 0;
+        tokens[base + n++] = argmax[base];
+        for (int64_t i = 0; i < D; i++) {
+#if ORACLE_MUTANT == 6
+            if (argmax[base + i + 1] != drafts[a * D + i]) break;     /* mutant: checked against the wrong row */
+#else
+            if (argmax[base + i] != drafts[a * D + i]) break;
+#endif
+            tokens[base + n++] = argmax[base + i + 1];
+        }
+#if ORACLE_MUTANT == 7
+        /* mutant: a rejected draft does not stop the later ones */
+        n = 1;
+        for (int64_t j = 1; j <= D; j++) tokens[base + j] = -1;
+        for (int64_t i = 0; i < D; i++)
+            if (argmax[base + i] == drafts[a * D + i]) tokens[base + n++] = argmax[base + i + 1];
+#endif
+        n_new[a] = (int32_t)n;
+    }
     return ORACLE_OK;
 }
 

@@ -243,9 +243,60 @@ def test_page_pins():
 
 # --- planted mistakes --------------------------------------------------------
 
+# ---- greedy draft verification ------------------------------------------------
+# Hand-derived cases of the rule: row i's argmax p_i stands for the position after
+# row i's input; draft i (row i + 1's input) is accepted iff it equals p_i, in
+# order, stopping at the first rejection; the agent emits p_0 and then p_{i+1} for
+# each accepted draft.  Two drafts per agent (three rows) unless stated.
+VERIFY_CASES = [
+    # argmax rows,            drafts,            D, tokens,                          n_new
+    ([10, 20, 30],            [[10, 20]],        2, [[10, 20, 30]],                  [3]),   # both drafts stand
+    ([5, 6, 7],               [[9, 6]],          2, [[5, -1, -1]],                   [1]),   # first draft wrong: later match ignored
+    ([4, 8, 1],               [[4, 2]],          2, [[4, 8, -1]],                    [2]),   # second draft wrong
+    ([3, 3, 3],               [[3, 3]],          2, [[3, 3, 3]],                     [3]),   # repeated token
+    ([7, 1, 2, 9, 9, 9],      [[7, 1], [8, 9]],  2, [[7, 1, 2], [9, -1, -1]],        [3, 1]),
+    ([11, 12, 13, 14],        [],                0, [[11], [12], [13], [14]],        [1, 1, 1, 1]),  # no drafts
+    ([2, 5, 6, 2, 5],         [[2, 5, 7, 9]],    4, [[2, 5, 6, -1, -1]],             [3]),   # four drafts, third wrong
+    ([2, 5, 6, 2, 5],         [[2, 5, 6, 9]],    4, [[2, 5, 6, 2, -1]],              [4]),   # four drafts, fourth wrong
+]
+
+
+@pytest.mark.parametrize("case", range(len(VERIFY_CASES)))
+def test_verify_greedy_hand_cases(orc, case):
+    am, dr, D, tok, n = VERIFY_CASES[case]
+    t, nn = orc.verify_greedy(am, dr, D)
+    assert t.tolist() == tok and nn.tolist() == n
+
+
+def test_verify_greedy_invariants(orc):
+    """Drafts that copy the argmax of the row before them all stand; one changed
+    draft cuts the agent's tokens right there; n_new is always in 1 .. D + 1 and
+    the emitted tokens are the argmax rows in order."""
+    rng = np.random.default_rng(5)
+    for D in (1, 2, 3, 5):
+        A = 7
+        am = rng.integers(0, 50, size=A * (D + 1)).astype(np.int32)
+        good = np.stack([am[a * (D + 1): a * (D + 1) + D] for a in range(A)])
+        t, n = orc.verify_greedy(am, good, D)
+        assert (n == D + 1).all()
+        assert np.array_equal(t.ravel(), am)
+        for cut in range(D):
+            bad = good.copy()
+            bad[:, cut] += 1
+            t, n = orc.verify_greedy(am, bad, D)
+            assert (n == cut + 1).all()
+            for a in range(A):
+                assert t[a, :cut + 1].tolist() == am[a * (D + 1): a * (D + 1) + cut + 1].tolist()
+                assert (t[a, cut + 1:] == -1).all()
+
+
 def _pins_fail(o: oracle.Oracle) -> bool:
     """Run a subset of the pins against an oracle; True when any pin fails."""
     try:
+        for am, dr, D, tok, n in VERIFY_CASES:
+            t, nn = o.verify_greedy(am, dr, D)
+            if t.tolist() != tok or nn.tolist() != n:
+                return True
         for rec in load_golden():
             w = o.dequant_block(golden_bytes(rec))
             if [Fraction(float(v)) for v in w] != golden_expect(rec):
@@ -264,7 +315,7 @@ def _pins_fail(o: oracle.Oracle) -> bool:
     return False
 
 
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7])
 def test_planted_mistakes_are_caught(tmp_path, mutant):
     path = str(tmp_path / f"liboracle_m{mutant}.so")
     oracle.build(force=True, mutant=mutant, path=path)
