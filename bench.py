@@ -4,7 +4,8 @@
 A step is one full decode-step weight pass: 64 transformer layers of four
 projections (Q|K|V fused, O, gate|up fused, down; hidden 5120, 64 query heads
 and 8 key/value heads of 128, MLP 25600) and a 5120 -> 151936 output head with
-its row argmax, for R stacked activation rows (4 agents x (1 token + 2 drafts)
+its row argmax and the greedy check of each agent's two draft tokens, for R
+stacked activation rows (4 agents x (1 token + 2 drafts)
 = 12 by default).  Weights are streamed once per step; 17,990,737,920 packed
 bytes (144 B per 256 weights).  Inputs are seeded synthetic data of those
 shapes and distributions, resident in HBM before timing.
@@ -74,19 +75,41 @@ def build_pass(R_max: int, seed: int):
     return mats, gemms, packed, xs, ys, idx
 
 
+def draft_check(R: int, seed: int):
+    """Device buffers for the step's draft check: R rows as agents of a token and
+    two drafts (when R is a multiple of 3, else no drafts); seeded draft tokens."""
+    import numpy as np
+    import torch
+    from synth import workloads as W
+    D = W.ROWS_PER_AGENT - 1 if R % W.ROWS_PER_AGENT == 0 else 0
+    A = R // (D + 1)
+    rng = np.random.default_rng(seed)
+    drafts = torch.from_numpy(rng.integers(0, W.VOCAB, size=(A, max(D, 1))).astype(np.int32)[:, :D].copy()).cuda()
+    tokens = torch.empty((A, D + 1), dtype=torch.int32, device="cuda")
+    n_new = torch.empty(A, dtype=torch.int32, device="cuda")
+    return D, drafts, tokens, n_new
+
+
 def time_pass(seq, xs, ys, idx, R: int, steps: int, warmup: int):
+    """ms per decode step: the 257 GEMMs, the head's row argmax and the greedy
+    check of the agents' drafts (one graph replay)."""
     import torch
     xr = [x[:R] for x in xs]
     yr = [y[:R] for y in ys]
+    D, drafts, tokens, n_new = draft_check(R, 7)
+
+    def one():
+        seq.run_verify(xr, yr, R, idx, drafts, D, tokens, n_new)
+
     for _ in range(warmup):
-        seq.run(xr, yr, R, argmax_idx=idx)
+        one()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(st)
     for _ in range(steps):
-        seq.run(xr, yr, R, argmax_idx=idx)
+        one()
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -472,6 +495,7 @@ def main():
                         "257 GEMMs + row argmax",
             "R": args.R,
             "pass_launch": "persistent" if args.persistent else "graph",
+            "step_epilogue": "head row argmax (chunked) + greedy check of 2 drafts per agent",
             "packed_bytes": pass_bytes,
             "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),
             "rows_tok_per_s": round(args.R * 1000 / ms, 1),

@@ -143,6 +143,38 @@ int qgemm_dequantize(qgemm_t h, float *w_out, void *stream);
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE (N < 1), QGEMM_ERANGE_R (R < 0), QGEMM_EHIP. */
 int qgemm_argmax_rows(const float *y, int R, int64_t N, int32_t *idx, void *stream);
 
+/* Bytes of the workspace qgemm_argmax_rows_ws needs for R rows of N columns.
+ * Errors: QGEMM_EINVAL (bytes NULL), QGEMM_ERANGE_R, QGEMM_ESHAPE (N < 1 or
+ * N > 2^31 - 1). */
+int qgemm_argmax_workspace_size(int R, int64_t N, size_t *bytes);
+
+/* As qgemm_argmax_rows (the same result), spread over many workgroups: each
+ * takes a chunk of up to 8192 columns of one row; the last chunk of a row to
+ * finish combines the chunks' maxima in chunk order.  workspace: device,
+ * caller-owned, at least qgemm_argmax_workspace_size bytes, 16-byte aligned,
+ * zero-filled before its first use; every run leaves it ready for the next (its
+ * counters back at zero).  Runs sharing a workspace must not overlap.
+ * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_ESHAPE, QGEMM_EHIP. */
+int qgemm_argmax_rows_ws(const float *y, int R, int64_t N, int32_t *idx, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Greedy verification of draft tokens (OpenJet multi-agent serving page,
+ * section on moving the weights only once: each agent contributes its next token
+ * and draft tokens as rows of one pass, and the drafts are checked in the same
+ * round).  The R rows are R / (D + 1) agents of D + 1 consecutive rows (D =
+ * drafts_per_agent): the agent's current token, then its D drafts.  argmax_idx
+ * (device int32 [R]) is the row argmax of the output head; drafts (device int32
+ * [agents x D], may be NULL when D = 0) the draft tokens.  Draft i stands iff it
+ * equals the argmax of row i, in order, up to the first rejection.  Writes
+ * n_new[a] = 1 + accepted drafts (device int32 [agents]) and tokens[a (D + 1) + j]
+ * = the j-th emitted token: the argmax of row 0, then of row i + 1 for each
+ * accepted draft i; -1 past n_new[a] (device int32 [agents x (D + 1)]).  One small
+ * kernel on `stream`.
+ * Errors: QGEMM_EINVAL (R not a multiple of D + 1, D < 0, NULL pointers),
+ * QGEMM_ERANGE_R, QGEMM_EHIP. */
+int qgemm_verify_greedy(const int32_t *argmax_idx, int R, const int32_t *drafts, int drafts_per_agent,
+                        int32_t *tokens, int32_t *n_new, void *stream);
+
 /* Describe the launch plan for (R, path) without running it.
  * Errors: QGEMM_EINVAL, QGEMM_ERANGE_R, QGEMM_EPATH. */
 int qgemm_query(qgemm_t h, int R, int path, qgemm_info *info);
@@ -169,7 +201,8 @@ int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32
  * (arrays of `count` device pointers, shapes as for qgemm_run); GEMM i + 1
  * starts after GEMM i has finished, as when each projection's input depends on
  * the previous output.  If argmax_idx is not NULL, the row argmax of the LAST
- * GEMM's output is written to it (device int32 [R]) by one more kernel.
+ * GEMM's output is written to it (device int32 [R]) by one more kernel (the
+ * chunked argmax of qgemm_argmax_rows_ws, on the sequence's own workspace).
  * With QGEMM_SEQ_PERSISTENT, one cooperative launch runs all GEMMs: every
  * workgroup is resident, waits at a device-wide barrier between GEMMs and
  * already streams the next GEMM's weights while it waits; the first run for a
@@ -183,6 +216,15 @@ int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32
  * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays, QGEMM_ENOMEM. */
 int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
                   int32_t *argmax_idx, void *stream);
+
+/* As qgemm_seq_run with argmax_idx, and the greedy verification of
+ * qgemm_verify_greedy on that argmax in the same epilogue kernel (the last row
+ * to finish its argmax runs it): the whole decode step's weight pass, head argmax
+ * and draft check in one call.
+ * Errors: as qgemm_seq_run and qgemm_verify_greedy. */
+int qgemm_seq_run_verify(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
+                         int32_t *argmax_idx, const int32_t *drafts, int drafts_per_agent,
+                         int32_t *tokens, int32_t *n_new, void *stream);
 
 /* Waits for the device, then stores in *timeouts how many barrier waits of the
  * sequence's launches since the previous call gave up (a bounded wait: a

@@ -67,6 +67,23 @@ def test_host_validation_codes():
     assert L.qgemm_argmax_rows(vp(4096), 2, 0, vp(4096), None) == Q.QGEMM_ESHAPE
     assert L.qgemm_argmax_rows(None, 2, 10, vp(4096), None) == Q.QGEMM_EINVAL
     assert L.qgemm_argmax_rows(None, 0, 10, None, None) == Q.QGEMM_OK        # R = 0: no-op
+    # chunked argmax and draft verification: size arithmetic and argument checks (no GPU call)
+    assert wsg.argmax_workspace_size(12, 151936) == 1888          # 12 x 19 chunks x 8 B + 13 counters, 16 B multiple
+    assert wsg.argmax_workspace_size(1, 1) == 16
+    sz = ctypes.c_size_t()
+    assert L.qgemm_argmax_workspace_size(65, 10, ctypes.byref(sz)) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_argmax_workspace_size(2, 0, ctypes.byref(sz)) == Q.QGEMM_ESHAPE
+    assert L.qgemm_argmax_workspace_size(2, 10, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_argmax_rows_ws(vp(4096), 2, 10, vp(4096), vp(4096), 8, None) == Q.QGEMM_EINVAL   # too small
+    assert L.qgemm_argmax_rows_ws(vp(4096), 2, 10, vp(4096), vp(4104), 4096, None) == Q.QGEMM_EALIGN
+    assert L.qgemm_argmax_rows_ws(None, 0, 10, None, None, 0, None) == Q.QGEMM_OK
+    assert L.qgemm_verify_greedy(vp(4096), 10, vp(4096), 2, vp(4096), vp(4096), None) == Q.QGEMM_EINVAL  # 10 % 3
+    assert L.qgemm_verify_greedy(vp(4096), 12, None, 2, vp(4096), vp(4096), None) == Q.QGEMM_EINVAL      # no drafts
+    assert L.qgemm_verify_greedy(vp(4096), 12, vp(4096), -1, vp(4096), vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_verify_greedy(vp(4096), 65, vp(4096), 0, vp(4096), vp(4096), None) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_verify_greedy(None, 0, None, 0, vp(4096), vp(4096), None) == Q.QGEMM_OK
+    assert L.qgemm_seq_run_verify(None, None, None, 12, vp(4096), vp(4096), 2, vp(4096), vp(4096),
+                                  None) == Q.QGEMM_EINVAL
     s = vp()
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 0) == Q.QGEMM_EINVAL
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 4) == Q.QGEMM_EINVAL

@@ -327,6 +327,106 @@ def test_argmax_unaligned_rows_ties_and_nan(N):
         assert got[r] == int(np.flatnonzero(v == v.max())[0]), (r, got[r])
 
 
+@pytest.mark.parametrize("N", [1, 5, 1001, 8193, 65537, 151936])
+def test_argmax_chunked_matches_rule_and_reuses_workspace(N):
+    """The chunked argmax (workspace, last chunk of a row combines) gives the same
+    index as the rule on rows with ties across chunks, NaN and an all-NaN row;
+    three runs on one workspace (its counters must come back to zero)."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    rng = np.random.default_rng(N + 7)
+    R = 9
+    y = rng.standard_normal((R, N)).astype(np.float32)
+    top = np.float32(10.0)
+    for r, n in enumerate([0, N - 1, N // 2, min(8191, N - 1), min(8192, N - 1)]):
+        y[r, n] = top
+    y[1, 0] = top                                  # tie across the first and last chunk
+    y[5, :] = np.nan
+    y[6, ::3] = np.nan
+    y[7, :] = -np.inf                              # all -inf: index 0
+    yd = torch.from_numpy(y).cuda()
+    ws = torch.zeros(wsg.argmax_workspace_size(R, N), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        _flush(f"argmax ws N={N} rep {rep}")
+        idx = torch.full((R,), -5, dtype=torch.int32, device="cuda")
+        wsg.argmax_rows_ws(yd, idx, ws)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(R):
+            row = y[r]
+            if np.isnan(row).all():
+                assert got[r] == 0
+                continue
+            v = np.where(np.isnan(row), -np.inf, row)
+            assert got[r] == int(np.flatnonzero(v == v.max())[0]), (r, got[r])
+    counters = ws.view(torch.int32)[(R * ((N + 8191) // 8192) * 8) // 4:][: R + 1].cpu().numpy()
+    assert (counters == 0).all()
+
+
+@pytest.mark.parametrize("D", [0, 1, 2, 3])
+def test_verify_greedy_matches_oracle(orc, D):
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    rng = np.random.default_rng(D)
+    A = 64 // (D + 1)
+    R = A * (D + 1)
+    am = rng.integers(0, 6, size=R).astype(np.int32)            # few values: many accidental matches
+    drafts = rng.integers(0, 6, size=(A, max(D, 1))).astype(np.int32)[:, :D]
+    for a in range(0, A, 3):                                   # every third agent: all drafts copy the argmax
+        drafts[a] = am[a * (D + 1): a * (D + 1) + D]
+    tok_ref, n_ref = orc.verify_greedy(am, drafts, D)
+    tokens = torch.full((A, D + 1), 99, dtype=torch.int32, device="cuda")
+    n_new = torch.full((A,), 99, dtype=torch.int32, device="cuda")
+    dd = torch.from_numpy(np.ascontiguousarray(drafts)).cuda() if D > 0 else None
+    wsg.verify_greedy(torch.from_numpy(am).cuda(), dd, D, tokens, n_new)
+    torch.cuda.synchronize()
+    assert np.array_equal(tokens.cpu().numpy(), tok_ref) and np.array_equal(n_new.cpu().numpy(), n_ref)
+
+
+def test_seq_run_verify_matches_oracle(orc):
+    """Weight pass, head argmax and draft check in one call: 4 agents x (token + 2
+    drafts) = 12 rows; drafts planted against the oracle's argmax (all stand, the
+    first stands, none stands, random); repeated runs give the same bits."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    shapes = [(300, 1024), (1000, 512)]
+    R, D = 12, 2
+    A = R // (D + 1)
+    mats = [G.make(14, i, N, K, max_R=R) for i, (N, K) in enumerate(shapes)]
+    xs_np = [synth.x_bf16(14, 40 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    ref_y = orc.gemm(mats[-1][0], shapes[-1][0], shapes[-1][1], xs_np[-1])
+    ref_idx = orc.argmax_rows(ref_y)
+    drafts = np.zeros((A, D), np.int32)
+    drafts[0] = ref_idx[0:2]                           # both stand
+    drafts[1] = [ref_idx[3], ref_idx[4] + 1]           # first stands
+    drafts[2] = [ref_idx[6] + 1, ref_idx[7]]           # none (second match ignored)
+    drafts[3] = [5, 7]
+    tok_ref, n_ref = orc.verify_greedy(ref_idx, drafts, D)
+    seq = wsg.Seq([g for _, g in mats])
+    xs = [G.to_dev(x) for x in xs_np]
+    ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for N, K in shapes]
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    tokens = torch.empty((A, D + 1), dtype=torch.int32, device="cuda")
+    n_new = torch.empty(A, dtype=torch.int32, device="cuda")
+    dd = torch.from_numpy(drafts).cuda()
+    top2 = np.sort(ref_y, axis=1)[:, -2:]
+    for rep in range(3):
+        _flush(f"seq verify rep {rep}")
+        tokens.fill_(77)
+        seq.run_verify(xs, ys, R, idx, dd, D, tokens, n_new)
+        torch.cuda.synchronize()
+        got_y = ys[-1].cpu().numpy()
+        assert_parity(got_y, ref_y, "seq verify head")
+        margin = top2[:, 1] - top2[:, 0]
+        assert (margin > 10 * np.abs(got_y - ref_y).max()).all(), "argmax ambiguous within the error bound"
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        assert np.array_equal(tokens.cpu().numpy(), tok_ref) and np.array_equal(n_new.cpu().numpy(), n_ref)
+    assert n_ref.tolist()[:3] == [3, 2, 1]
+    seq.close()
+    for _, g in mats:
+        g.close()
+
+
 # ---- full weight pass machinery (one cooperative launch over several GEMMs) ----
 
 @pytest.mark.parametrize("persistent", [False, True])

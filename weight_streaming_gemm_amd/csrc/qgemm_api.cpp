@@ -15,6 +15,7 @@
 #include "qgemm_internal.h"
 
 using namespace qg;
+static_assert(MAX_ROWS == QGEMM_MAX_R, "row limit of the kernels and of the ABI");
 
 struct qgemm_handle {
   uint32_t magic;
@@ -54,6 +55,11 @@ bool valid_shape(int64_t N, int64_t K) {
 }
 
 bool valid_handle(const qgemm_handle* h) { return h && h->magic == HANDLE_MAGIC; }
+
+// R rows = agents of D + 1 rows each (current token and D drafts)
+bool verify_args_ok(int R, const int32_t* drafts, int D, const int32_t* tokens, const int32_t* n_new) {
+  return D >= 0 && R % (D + 1) == 0 && (D == 0 || drafts) && tokens && n_new;
+}
 
 // The min term from staged sub-block sums costs work per staged block and saves
 // seven products per step: taken when a range has at least 4 steps per block
@@ -334,6 +340,37 @@ int qgemm_argmax_rows(const float* y, int R, int64_t N, int32_t* idx, void* stre
   return e == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
+int qgemm_argmax_workspace_size(int R, int64_t N, size_t* bytes) {
+  if (!bytes) return QGEMM_EINVAL;
+  if (R < 0 || R > QGEMM_MAX_R) return QGEMM_ERANGE_R;
+  if (N < 1 || N > INT32_MAX) return QGEMM_ESHAPE;
+  *bytes = argmax_ws_bytes(R, N);
+  return QGEMM_OK;
+}
+
+int qgemm_argmax_rows_ws(const float* y, int R, int64_t N, int32_t* idx, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (R < 0 || R > QGEMM_MAX_R) return QGEMM_ERANGE_R;
+  if (N < 1 || N > INT32_MAX) return QGEMM_ESHAPE;
+  if (R == 0) return QGEMM_OK;
+  if (!y || !idx || !workspace || workspace_bytes < argmax_ws_bytes(R, N)) return QGEMM_EINVAL;
+  if (!aligned16(workspace)) return QGEMM_EALIGN;
+  hipError_t e = launch_argmax_split(y, R, N, idx, workspace, nullptr, 0, nullptr, nullptr,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+}
+
+int qgemm_verify_greedy(const int32_t* argmax_idx, int R, const int32_t* drafts, int drafts_per_agent,
+                        int32_t* tokens, int32_t* n_new, void* stream) {
+  if (R < 0 || R > QGEMM_MAX_R) return QGEMM_ERANGE_R;
+  if (!verify_args_ok(R, drafts, drafts_per_agent, tokens, n_new)) return QGEMM_EINVAL;
+  if (R == 0) return QGEMM_OK;
+  if (!argmax_idx) return QGEMM_EINVAL;
+  hipError_t e = launch_verify(argmax_idx, R, drafts, drafts_per_agent, tokens, n_new,
+                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+}
+
 int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   if (!valid_handle(h) || !info) return QGEMM_EINVAL;
   if (R < 1 || R > h->max_R) return QGEMM_ERANGE_R;
@@ -395,6 +432,8 @@ struct qgemm_seq {
   uint32_t* err;
   size_t part_bytes, cnt_bytes;
   std::map<SeqKey, GemmDesc*> descs;   // device descriptor arrays per (R, pointer set)
+  void* am_ws;       // argmax (and verification) workspace for the last GEMM's output
+  int max_R;
 };
 
 namespace {
@@ -455,6 +494,7 @@ void seq_free(qgemm_seq* s) {
   if (s->cnt) (void)hipFree(s->cnt);
   if (s->sync) (void)hipFree(s->sync);
   if (s->err) (void)hipFree(s->err);
+  if (s->am_ws) (void)hipFree(s->am_ws);
 }
 
 }  // namespace
@@ -505,7 +545,10 @@ int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32
   s->part_bytes = part;
   s->cnt_bytes = cnt;
   const size_t sync_bytes = (size_t)(count + 1) * 4;
-  bool ok = hipMalloc(reinterpret_cast<void**>(&s->part), part) == hipSuccess &&
+  s->max_R = max_R;
+  const size_t am_bytes = argmax_ws_bytes(max_R, s->hs.back()->N);
+  bool ok = hipMalloc(&s->am_ws, am_bytes) == hipSuccess && hipMemset(s->am_ws, 0, am_bytes) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&s->part), part) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->cnt), cnt) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->sync), sync_bytes) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->err), 4) == hipSuccess &&
@@ -521,8 +564,14 @@ int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32
   return QGEMM_OK;
 }
 
-int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, int32_t* argmax_idx,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// the whole sequence, then (argmax_idx) the last output's row argmax and
+// (tokens) the greedy verification of D drafts per agent, in one epilogue kernel
+int seq_run_impl(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, int32_t* argmax_idx,
+                 const int32_t* drafts, int D, int32_t* tokens, int32_t* n_new, void* stream) {
   if (!s || s->magic != SEQ_MAGIC || !xs || !ys) return QGEMM_EINVAL;
   if (R < 0) return QGEMM_ERANGE_R;
   for (size_t i = 0; i < s->hs.size(); ++i) {
@@ -540,6 +589,10 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
   if (!(s->flags & QGEMM_SEQ_PERSISTENT)) {
     // one launch per GEMM, in order, captured once into a graph and replayed
     key.ptrs.push_back(reinterpret_cast<uintptr_t>(argmax_idx));
+    key.ptrs.push_back(reinterpret_cast<uintptr_t>(drafts));
+    key.ptrs.push_back(reinterpret_cast<uintptr_t>(tokens));
+    key.ptrs.push_back(reinterpret_cast<uintptr_t>(n_new));
+    key.ptrs.push_back((uintptr_t)D);
     auto g = s->graphs.find(key);
     if (g == s->graphs.end()) {
       if (s->graphs.size() >= SEQ_CACHE_MAX) seq_drop_graphs(s);
@@ -548,7 +601,8 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
       for (size_t i = 0; i < s->hs.size() && rc == QGEMM_OK; ++i)
         rc = run_impl(s->hs[i], xs[i], ys[i], R, QGEMM_PATH_AUTO, s->cap);
       if (rc == QGEMM_OK && argmax_idx &&
-          launch_argmax(ys[s->hs.size() - 1], R, s->hs.back()->N, argmax_idx, s->cap) != hipSuccess)
+          launch_argmax_split(ys[s->hs.size() - 1], R, s->hs.back()->N, argmax_idx, s->am_ws, drafts, D, tokens,
+                              n_new, s->cap) != hipSuccess)
         rc = QGEMM_EHIP;
       hipGraph_t graph = nullptr;
       const hipError_t e = hipStreamEndCapture(s->cap, &graph);
@@ -599,9 +653,27 @@ int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R,
   if (launch_stream(a, true, st) != hipSuccess) return QGEMM_EHIP;
   if (argmax_idx) {
     const qgemm_handle* last = s->hs.back();
-    if (launch_argmax(ys[s->hs.size() - 1], R, last->N, argmax_idx, st) != hipSuccess) return QGEMM_EHIP;
+    if (launch_argmax_split(ys[s->hs.size() - 1], R, last->N, argmax_idx, s->am_ws, drafts, D, tokens, n_new, st) !=
+        hipSuccess)
+      return QGEMM_EHIP;
   }
   return QGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_seq_run(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, int32_t* argmax_idx,
+                  void* stream) {
+  return seq_run_impl(s, xs, ys, R, argmax_idx, nullptr, 0, nullptr, nullptr, stream);
+}
+
+int qgemm_seq_run_verify(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, int32_t* argmax_idx,
+                         const int32_t* drafts, int drafts_per_agent, int32_t* tokens, int32_t* n_new,
+                         void* stream) {
+  if (!argmax_idx || !verify_args_ok(R, drafts, drafts_per_agent, tokens, n_new)) return QGEMM_EINVAL;
+  return seq_run_impl(s, xs, ys, R, argmax_idx, drafts, drafts_per_agent, tokens, n_new, stream);
 }
 
 int qgemm_seq_errors(qgemm_seq_t s, uint32_t* timeouts) {

@@ -47,6 +47,7 @@ struct StreamArgs {
                            // activations themselves (eight products per step)
   int32_t valu;            // 1: vector-unit variant (R <= 4, msum = 1, one GEMM)
 };
+constexpr int MAX_ROWS = 64;        // rows of a run (QGEMM_MAX_R)
 constexpr int VALU_MAX_R = 4;       // rows the vector-unit kernel serves
 constexpr int VALU_AUTO_MAX_R = 0;  // rows for which the automatic choice takes it
 
@@ -72,5 +73,19 @@ bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_argmax(const float* y, int R, int64_t N, int32_t* idx, hipStream_t st);
+// Row argmax over column chunks with a workspace of argmax_ws_bytes(R, N) bytes
+// (chunk partials, then R + 1 arrival counters that start and end at zero);
+// with tokens != null the kernel also runs the greedy draft verification.
+inline int argmax_chunks(int64_t N) {
+  const int64_t c = (N + 8191) / 8192;
+  return (int)(c < 1 ? 1 : (c > 1024 ? 1024 : c));
+}
+inline size_t argmax_ws_bytes(int R, int64_t N) {
+  return (((size_t)R * argmax_chunks(N) * 8 + (size_t)(R + 1) * 4) + 15) / 16 * 16;
+}
+hipError_t launch_argmax_split(const float* y, int R, int64_t N, int32_t* idx, void* ws, const int32_t* drafts,
+                               int D, int32_t* tokens, int32_t* n_new, hipStream_t st);
+hipError_t launch_verify(const int32_t* idx, int R, const int32_t* drafts, int D, int32_t* tokens, int32_t* n_new,
+                         hipStream_t st);
 
 }  // namespace qg

@@ -940,6 +940,129 @@ argmax_kernel(const float* __restrict__ y, int64_t N, int32_t* __restrict__ idx)
 }
 
 // ---------------------------------------------------------------------------
+// Greedy verification of draft tokens.  Agent a owns rows a (D + 1) .. a (D + 1)
+// + D of the pass: its current token and its D drafts (OpenJet multi-agent
+// serving page, section on moving the weights only once: the drafts are checked
+// in the same round).  Row i's argmax p_i is the choice for the position after
+// row i's input, so draft i (row i + 1's input) stands iff it equals p_i; the
+// agent emits p_0 and p_{i+1} for each draft accepted in order, up to the first
+// rejection.  One thread per agent; argmax rows read through `load`.
+template <class Load>
+__device__ __forceinline__ void verify_agent(int a, int D, Load load, const int32_t* __restrict__ drafts,
+                                             int32_t* __restrict__ tokens, int32_t* __restrict__ n_new) {
+  const int base = a * (D + 1);
+  int n = 1;
+  tokens[base] = load(base);
+  bool open = true;
+  for (int i = 0; i < D; ++i) {
+    open = open && load(base + i) == drafts[a * D + i];
+    tokens[base + i + 1] = open ? load(base + i + 1) : -1;
+    n += open ? 1 : 0;
+  }
+  n_new[a] = n;
+}
+
+__global__ void __launch_bounds__(64)
+verify_kernel(const int32_t* __restrict__ idx, int A, int D, const int32_t* __restrict__ drafts,
+              int32_t* __restrict__ tokens, int32_t* __restrict__ n_new) {
+  const int a = threadIdx.x;
+  if (a < A) verify_agent(a, D, [&](int r) { return idx[r]; }, drafts, tokens, n_new);
+}
+
+// Row argmax over column chunks, with a workspace (the same result as
+// argmax_kernel: the largest value, lowest index among equal maxima, NaN never
+// wins).  Grid (C, R): workgroup (c, r) takes columns [c chunk, (c + 1) chunk) of
+// row r, publishes its (value, index) in part[r C + c] and arrives at cnt[r];
+// the last of row r's C arrivals adds the partials in chunk order, writes idx[r]
+// and arrives at cnt[R]; the last row to finish runs the draft verification when
+// drafts are given.  Every arrival counter it uses is back at zero when the
+// kernel ends.
+__global__ void __launch_bounds__(256)
+argmax_split_kernel(const float* __restrict__ y, int R, int64_t N, int64_t chunk, int C,
+                    unsigned long long* __restrict__ part, uint32_t* __restrict__ cnt, int32_t* __restrict__ idx,
+                    const int32_t* __restrict__ drafts, int D, int32_t* __restrict__ tokens,
+                    int32_t* __restrict__ n_new) {
+  constexpr int NT = 256, U = 4;
+  constexpr uint32_t NONE = 0xFFFFFFFFu;
+  __shared__ float sv[NT / 64];
+  __shared__ int64_t si[NT / 64];
+  __shared__ uint32_t s_last;
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int64_t n0 = (int64_t)c * chunk, n1 = n0 + chunk < N ? n0 + chunk : N;
+  const float* row = y + (int64_t)r * N;
+  float bv = -__builtin_inff();
+  int64_t bi = N;                                 // N = "none yet"
+  auto take = [&](float v, int64_t n) {
+    if (v > bv || (v == bv && n < bi)) { bv = v; bi = n; }
+  };
+  // scalar head up to 16-byte alignment, 16-byte vectors, scalar tail
+  const int64_t mis = (int64_t)((16u - ((uintptr_t)(row + n0) & 15u)) & 15u) / 4;
+  const int64_t h1 = n0 + mis < n1 ? n0 + mis : n1;
+  if (n0 + tid < h1) take(row[n0 + tid], n0 + tid);
+  const int64_t nvec = (n1 - h1) / 4;
+  const float4* vrow = reinterpret_cast<const float4*>(row + h1);
+  for (int64_t i0 = 0; i0 < nvec; i0 += (int64_t)NT * U) {
+    float4 v[U];
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT + tid;
+      v[u] = i < nvec ? vrow[i] : make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                              __builtin_nanf(""));
+    }
+    for (int u = 0; u < U; ++u) {
+      const int64_t n = h1 + 4 * (i0 + (int64_t)u * NT + tid);
+      take(v[u].x, n);
+      take(v[u].y, n + 1);
+      take(v[u].z, n + 2);
+      take(v[u].w, n + 3);
+    }
+  }
+  for (int64_t n = h1 + 4 * nvec + tid; n < n1; n += NT) take(row[n], n);
+  auto merge = [&](float ov, int64_t oi) {
+    if (oi != N && (bi == N || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+  };
+  for (int off = 32; off > 0; off >>= 1) merge(__shfl_xor(bv, off), __shfl_xor(bi, off));
+  if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < NT / 64; ++k) merge(sv[k], si[k]);
+    const unsigned long long key =
+        ((unsigned long long)__builtin_bit_cast(uint32_t, bv) << 32) | (bi == N ? NONE : (uint32_t)bi);
+    __hip_atomic_store(part + (int64_t)r * C + c, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the row's last arrival: every thread takes some chunks' partials, then the
+  // workgroup reduces them (the maximum with the lowest index does not depend
+  // on the order in which partials meet)
+  bv = -__builtin_inff();
+  bi = N;
+  for (int k = tid; k < C; k += NT) {
+    const unsigned long long key = __hip_atomic_load(part + (int64_t)r * C + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ki = (uint32_t)key;
+    if (ki != NONE) merge(__builtin_bit_cast(float, (uint32_t)(key >> 32)), (int64_t)ki);
+  }
+  for (int off = 32; off > 0; off >>= 1) merge(__shfl_xor(bv, off), __shfl_xor(bi, off));
+  __syncthreads();                                // the first reduction's LDS reads are done
+  if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < NT / 64; ++k) merge(sv[k], si[k]);
+    __hip_atomic_store(idx + r, (int32_t)(bi == N ? 0 : bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cnt + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = __hip_atomic_fetch_add(cnt + R, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(R - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the last row: draft verification, one thread per agent, argmax rows staged in LDS
+  __shared__ int32_t s_idx[MAX_ROWS];
+  if (tid < R) s_idx[tid] = __hip_atomic_load(idx + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(cnt + R, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tokens && tid < R / (D + 1)) verify_agent(tid, D, [&](int q) { return s_idx[q]; }, drafts, tokens, n_new);
+}
+
+// ---------------------------------------------------------------------------
 // launch wrappers
 
 static inline unsigned blocks_for(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
@@ -1032,6 +1155,25 @@ hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K,
 hipError_t launch_argmax(const float* y, int R, int64_t N, int32_t* idx, hipStream_t st) {
   if (R == 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)R), dim3(1024), 0, st, y, N, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_split(const float* y, int R, int64_t N, int32_t* idx, void* ws, const int32_t* drafts,
+                               int D, int32_t* tokens, int32_t* n_new, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  const int C = argmax_chunks(N);
+  const int64_t chunk = (N + C - 1) / C;
+  unsigned long long* part = reinterpret_cast<unsigned long long*>(ws);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(part + (int64_t)R * C);
+  hipLaunchKernelGGL(argmax_split_kernel, dim3((unsigned)C, (unsigned)R), dim3(256), 0, st, y, R, N, chunk, C, part,
+                     cnt, idx, drafts, D, tokens, n_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const int32_t* idx, int R, const int32_t* drafts, int D, int32_t* tokens, int32_t* n_new,
+                         hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(64), 0, st, idx, R / (D + 1), D, drafts, tokens, n_new);
   return hipGetLastError();
 }
 

@@ -22,8 +22,10 @@ MAX_R = 64
 # every symbol include/qgemm.h declares
 EXPORTS = (
     "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
-    "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_query", "qgemm_destroy",
-    "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_errors", "qgemm_seq_destroy", "qgemm_status_string",
+    "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_argmax_workspace_size", "qgemm_argmax_rows_ws",
+    "qgemm_verify_greedy", "qgemm_query", "qgemm_destroy",
+    "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_run_verify", "qgemm_seq_errors", "qgemm_seq_destroy",
+    "qgemm_status_string",
 )
 
 
@@ -61,10 +63,14 @@ def lib():
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
             "qgemm_dequantize": [vp, vp, vp],
             "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
+            "qgemm_argmax_workspace_size": [i32, i64, ctypes.POINTER(ctypes.c_size_t)],
+            "qgemm_argmax_rows_ws": [vp, i32, i64, vp, vp, ctypes.c_size_t, vp],
+            "qgemm_verify_greedy": [vp, i32, vp, i32, vp, vp, vp],
             "qgemm_query": [vp, i32, i32, ctypes.POINTER(Info)],
             "qgemm_destroy": [vp],
             "qgemm_seq_create": [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.c_uint32],
             "qgemm_seq_run": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp],
+            "qgemm_seq_run_verify": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp, i32, vp, vp, vp],
             "qgemm_seq_errors": [vp, ctypes.POINTER(ctypes.c_uint32)],
             "qgemm_seq_destroy": [vp],
         }
@@ -114,6 +120,28 @@ def argmax_rows(y, idx, R: int | None = None, stream=None):
     N = y.shape[1]
     _check(lib().qgemm_argmax_rows(_ptr(y), R, N, _ptr(idx), _stream(stream)), "qgemm_argmax_rows")
     return idx
+
+
+def argmax_workspace_size(R: int, N: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().qgemm_argmax_workspace_size(R, N, ctypes.byref(out)), "qgemm_argmax_workspace_size")
+    return out.value
+
+
+def argmax_rows_ws(y, idx, workspace, R: int | None = None, stream=None):
+    R = y.shape[0] if R is None else R
+    N = y.shape[1]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().qgemm_argmax_rows_ws(_ptr(y), R, N, _ptr(idx), _ptr(workspace), nbytes, _stream(stream)),
+           "qgemm_argmax_rows_ws")
+    return idx
+
+
+def verify_greedy(argmax_idx, drafts, drafts_per_agent: int, tokens, n_new, R: int | None = None, stream=None):
+    R = argmax_idx.shape[0] if R is None else R
+    _check(lib().qgemm_verify_greedy(_ptr(argmax_idx), R, _ptr(drafts), drafts_per_agent, _ptr(tokens), _ptr(n_new),
+                                     _stream(stream)), "qgemm_verify_greedy")
+    return tokens, n_new
 
 
 class QGemm:
@@ -169,6 +197,13 @@ class Seq:
         xa = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
         ya = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
         _check(lib().qgemm_seq_run(self.s, xa, ya, R, _ptr(argmax_idx), _stream(stream)), "qgemm_seq_run")
+
+    def run_verify(self, xs, ys, R: int, argmax_idx, drafts, drafts_per_agent: int, tokens, n_new, stream=None):
+        n = len(self.gemms)
+        xa = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+        ya = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+        _check(lib().qgemm_seq_run_verify(self.s, xa, ya, R, _ptr(argmax_idx), _ptr(drafts), drafts_per_agent,
+                                          _ptr(tokens), _ptr(n_new), _stream(stream)), "qgemm_seq_run_verify")
 
     def errors(self) -> int:
         """Barrier waits that gave up since the last call (synchronises the device)."""
