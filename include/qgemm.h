@@ -236,6 +236,31 @@ int qgemm_seq_errors(qgemm_seq_t s, uint32_t *timeouts);
 /* Free the sequence and its workspace (not the handles).  NULL is a no-op. */
 int qgemm_seq_destroy(qgemm_seq_t s);
 
+/* Decode attention of the agents' step rows over their own KV caches
+ * (OpenJet multi-agent serving page, section on moving the weights only once:
+ * every agent reads its own KV cache, and attention grows with the agents).
+ * Agent a's step has `rows` (1..4) query rows (its token and drafts) at
+ * positions L_a .. L_a + rows - 1 of its sequence, L_a = lengths[a] (device
+ * int32 [agents], clamped to [0, max_len]); their keys and values must already
+ * be in the caches at those positions.  Row i sees positions 0 .. L_a + i.
+ *   q_bf16   device bf16 [agents][rows][q_heads][head_dim]
+ *   k_cache, v_cache  device bf16 [agents][cap][kv_heads][head_dim]
+ *   out      device fp32 [agents][rows][q_heads][head_dim], overwritten:
+ *            softmax(q.k / sqrt(head_dim)) . v, query head hq reading
+ *            key/value head hq / (q_heads / kv_heads)
+ * head_dim must be 128 and q_heads = 8 kv_heads; cap >= max_len + rows; q and
+ * the caches below 2 GiB each.  Keys and queries enter the matrix cores as
+ * bf16 (exact); the weights and the values as binary16 (values above 65504 in
+ * magnitude are out of range).  workspace: device, caller-owned, at least
+ * qgemm_attention_workspace_size bytes, 16-byte aligned (partial results of
+ * the sequence splits).  Two kernels on `stream`.
+ * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_EHIP. */
+int qgemm_attention_workspace_size(int agents, int rows, int kv_heads, int max_len, size_t *bytes);
+int qgemm_decode_attention(const void *q_bf16, const void *k_cache, const void *v_cache,
+                           const int32_t *lengths, int agents, int rows, int q_heads, int kv_heads,
+                           int head_dim, int cap, int max_len, float *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *qgemm_status_string(int status);
 

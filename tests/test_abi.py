@@ -84,6 +84,21 @@ def test_host_validation_codes():
     assert L.qgemm_verify_greedy(None, 0, None, 0, vp(4096), vp(4096), None) == Q.QGEMM_OK
     assert L.qgemm_seq_run_verify(None, None, None, 12, vp(4096), vp(4096), 2, vp(4096), vp(4096),
                                   None) == Q.QGEMM_EINVAL
+    # decode attention: workspace arithmetic and shape checks (no GPU call)
+    assert wsg.attention_workspace_size(4, 3, 8, 23000) == 4 * 8 * 23 * 32 * 130 * 4
+    assert L.qgemm_attention_workspace_size(4, 5, 8, 100, ctypes.byref(sz)) == Q.QGEMM_ESHAPE
+    att = lambda **kw: L.qgemm_decode_attention(  # noqa: E731
+        vp(4096), vp(4096), vp(4096), vp(4096), kw.get("A", 2), kw.get("rows", 3), kw.get("hq", 16),
+        kw.get("hkv", 2), kw.get("d", 128), kw.get("cap", 100), kw.get("max_len", 50), vp(4096),
+        vp(kw.get("ws", 4096)), kw.get("ws_bytes", 1 << 30), None)
+    assert att(d=64) == Q.QGEMM_ESHAPE
+    assert att(hq=12) == Q.QGEMM_ESHAPE
+    assert att(rows=5) == Q.QGEMM_ESHAPE
+    assert att(cap=52) == Q.QGEMM_ESHAPE                      # cap < max_len + rows
+    assert att(A=64, cap=1 << 20, max_len=100) == Q.QGEMM_ESHAPE  # caches beyond 2 GiB
+    assert att(ws_bytes=16) == Q.QGEMM_EINVAL
+    assert att(ws=4104) == Q.QGEMM_EALIGN
+    assert att(A=0) == Q.QGEMM_OK
     s = vp()
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 0) == Q.QGEMM_EINVAL
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 4) == Q.QGEMM_EINVAL

@@ -1,0 +1,267 @@
+// attention.hip — gfx950 decode attention of the agents' step rows over their
+// own KV caches (split over the sequence, then one combine pass).
+//
+// OpenJet multi-agent serving page, section on moving the weights only once:
+// the stacked rows share every weight read, but each agent reads its own KV
+// cache, and attention grows with the number of agents.  An agent's step has
+// `rows` query rows (its current token and its drafts) at positions L, L + 1,
+// ... of its sequence; their keys and values are already in its cache.  Row i
+// sees positions 0 .. L + i.  Query head hq reads key/value head hq / 8
+// (groups of 8 query heads); head size 128; scores q.k / sqrt(128).
+//
+// Split kernel: workgroup (s, h, a) takes positions [s SPLIT, (s + 1) SPLIT) of
+// agent a's cache for key/value head h, for all rows x 8 query heads of the
+// group at once (at most 32 query vectors: the rows of one 16 x 16 matrix-core
+// tile pair).  Each of its 4 waves takes every 4th tile of 32 positions:
+//   S = Q K^T       bf16 matrix-core products, fp32 (exact products)
+//   online softmax  fp32, base-2 exponent with log2(e) / sqrt(128) folded in
+//   O += P V        P as a binary16 head + tail pair (P in [0, 1]: the pair
+//                   holds it to about 2^-22), V converted bf16 -> binary16
+//                   (exact), two fp16 matrix-core products, fp32 accumulation
+// P and V reach their operand layouts through a small LDS area per wave (P from
+// the product layout to the A layout, V transposed).  The waves' (max, sum, O)
+// are merged in LDS and written as the split's partial result (O not yet
+// divided by the sum).  Combine kernel: per (agent, row, query head), the
+// splits' partials rescaled to the common maximum and divided by the sum.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemm_internal.h"
+
+namespace qg {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t w32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int AD = ATTN_HEAD_DIM;       // 128
+constexpr int GRP = ATTN_GROUP;         // 8 query heads per key/value head
+constexpr int SPLIT = ATTN_SPLIT;       // positions per workgroup
+constexpr int TK = 32;                  // positions per wave step
+constexpr int NWAVE = 4;
+constexpr uint32_t AOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
+
+// per-wave LDS: P's head and tail [32 rows][32 positions] and V^T [128 dims][32
+// positions], as binary16, rows padded to 80 bytes
+constexpr int PSTRIDE = 80, PBYTES = 32 * PSTRIDE, VBYTES = AD * PSTRIDE;
+constexpr int WAVE_LDS = 2 * PBYTES + VBYTES;
+// merge area: per wave (max, sum) of 32 rows and O [32][128] fp32
+constexpr int MERGE_LDS = NWAVE * (32 * 2 * 4 + 32 * AD * 4);
+constexpr int ATTN_LDS = (NWAVE * WAVE_LDS > MERGE_LDS) ? NWAVE * WAVE_LDS : MERGE_LDS;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes >= 0x80000000ull ? 0x80000000u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ w32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(w32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+}  // namespace
+
+__global__ void __launch_bounds__(NWAVE * 64)
+attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[ATTN_LDS];
+  const int s = blockIdx.x, h = blockIdx.y, ag = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, nl = lane & 15;
+  const int rows = a.rows, nq = rows * GRP;                 // query vectors of the group
+  const int L0 = a.lengths[ag];
+  const int L = L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0);
+  const int total = L + rows;                               // positions the last row sees
+  const int p_begin = s * SPLIT;
+  if (p_begin >= total) return;                             // the combine reads only splits below total
+  const int p_end = p_begin + SPLIT < total ? p_begin + SPLIT : total;
+  const int Hq = a.Hkv * GRP;
+  const uint64_t cache_bytes = (uint64_t)a.A * a.cap * a.Hkv * AD * 2;
+  const __amdgpu_buffer_rsrc_t kr = rsrc(a.k, cache_bytes), vr = rsrc(a.v, cache_bytes);
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q, (uint64_t)a.A * rows * Hq * AD * 2);
+
+  // A operands of Q: row tile rt, k-step c: query vector 16 rt + nl (row i =
+  // vector / 8, head h * 8 + vector % 8), dims 32 c + 8 g .. + 7
+  b16x8 qa[2][4];
+  for (int rt = 0; rt < 2; ++rt) {
+    const int qv = 16 * rt + nl;
+    const uint32_t base = qv < nq ? (uint32_t)((((ag * rows + qv / GRP) * Hq + h * GRP + qv % GRP) * AD) * 2) : AOOB;
+    for (int c = 0; c < 4; ++c)
+      qa[rt][c] = __builtin_bit_cast(b16x8, load16(qr, base == AOOB ? AOOB : base + (32 * c + 8 * g) * 2));
+  }
+
+  const float NEG = -__builtin_inff();
+  float mrow[2][4], lrow[2][4];
+  f32x4 o[2][8];
+  for (int rt = 0; rt < 2; ++rt)
+    for (int i = 0; i < 4; ++i) { mrow[rt][i] = NEG; lrow[rt][i] = 0.f; }
+  for (int rt = 0; rt < 2; ++rt)
+    for (int dt = 0; dt < 8; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* pbuf = lds + w * WAVE_LDS;                        // P head
+  uint8_t* plbuf = pbuf + PBYTES;                           // P tail
+  uint8_t* vbuf = plbuf + PBYTES;
+  // byte offset of (position p, head h, dim d) in a cache
+  auto coff = [&](int p, int d) { return (uint32_t)((((uint64_t)ag * a.cap + p) * a.Hkv + h) * AD + d) * 2; };
+
+  for (int t0 = p_begin + TK * w; t0 < p_end; t0 += TK * NWAVE) {
+    // K: B operands, position 16 kt + nl of the step, dims 32 c + 8 g .. + 7
+    b16x8 kb[2][4];
+    for (int kt = 0; kt < 2; ++kt) {
+      const int p = t0 + 16 * kt + nl;
+      for (int c = 0; c < 4; ++c)
+        kb[kt][c] = __builtin_bit_cast(b16x8, load16(kr, p < p_end ? coff(p, 32 * c + 8 * g) : AOOB));
+    }
+    // V: the step's 32 positions x 128 dims as 512 chunks of 16 bytes, 8 per lane
+    w32x4 vc[8];
+    for (int it = 0; it < 8; ++it) {
+      const int cid = it * 64 + lane, pp = t0 + (cid >> 4);
+      vc[it] = load16(vr, pp < p_end ? coff(pp, 8 * (cid & 15)) : AOOB);
+    }
+    // S = Q K^T; lane (g, nl) holds S[16 rt + 4 g + i][16 kt + nl]
+    f32x4 sc[2][2];
+    for (int rt = 0; rt < 2; ++rt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][c], kb[kt][c], acc, 0, 0, 0);
+        sc[rt][kt] = acc;
+      }
+    // mask, scale, online softmax (row statistics shared by the 16 lanes of a group)
+    float pv[2][2][4];
+    for (int rt = 0; rt < 2; ++rt)
+      for (int i = 0; i < 4; ++i) {
+        const int qv = 16 * rt + 4 * g + i;
+        const int last = L + qv / GRP;                          // row qv / 8 sees positions <= last
+        float x[2];
+        for (int kt = 0; kt < 2; ++kt) {
+          const int p = t0 + 16 * kt + nl;
+          x[kt] = (qv < nq && p < p_end && p <= last) ? sc[rt][kt][i] * a.scale_log2 : NEG;
+        }
+        float mx = x[0] > x[1] ? x[0] : x[1];
+        for (int off = 1; off < 16; off <<= 1) {
+          const float y = __shfl_xor(mx, off);
+          mx = y > mx ? y : mx;
+        }
+        const float mnew = mrow[rt][i] > mx ? mrow[rt][i] : mx;
+        float alpha = 1.f, sum = 0.f;
+        if (mnew != NEG) {
+          alpha = exp2f(mrow[rt][i] - mnew);
+          for (int kt = 0; kt < 2; ++kt) {
+            pv[rt][kt][i] = exp2f(x[kt] - mnew);
+            sum += pv[rt][kt][i];
+          }
+        } else {
+          pv[rt][0][i] = pv[rt][1][i] = 0.f;
+        }
+        for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+        mrow[rt][i] = mnew;
+        lrow[rt][i] = lrow[rt][i] * alpha + sum;
+        for (int dt = 0; dt < 8; ++dt) o[rt][dt][i] *= alpha;
+      }
+    // P (binary16) into the A layout, V (bf16 -> binary16) transposed
+    __asm__ volatile("" ::: "memory");
+    for (int rt = 0; rt < 2; ++rt)
+      for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 4; ++i) {
+          const int off = (16 * rt + 4 * g + i) * PSTRIDE + (16 * kt + nl) * 2;
+          const _Float16 hi = (_Float16)pv[rt][kt][i];
+          *reinterpret_cast<_Float16*>(pbuf + off) = hi;
+          *reinterpret_cast<_Float16*>(plbuf + off) = (_Float16)(pv[rt][kt][i] - (float)hi);
+        }
+    for (int it = 0; it < 8; ++it) {
+      const int cid = it * 64 + lane, pp = cid >> 4, d0 = 8 * (cid & 15);
+      const float e[8] = {bf16_lo(vc[it].x), bf16_hi(vc[it].x), bf16_lo(vc[it].y), bf16_hi(vc[it].y),
+                          bf16_lo(vc[it].z), bf16_hi(vc[it].z), bf16_lo(vc[it].w), bf16_hi(vc[it].w)};
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<_Float16*>(vbuf + (d0 + j) * PSTRIDE + pp * 2) = (_Float16)e[j];
+    }
+    __asm__ volatile("" ::: "memory");       // one wave's LDS accesses run in order
+    h16x8 pa[2], pl[2];
+    for (int rt = 0; rt < 2; ++rt) {
+      pa[rt] = *reinterpret_cast<const h16x8*>(pbuf + (16 * rt + nl) * PSTRIDE + 16 * g);
+      pl[rt] = *reinterpret_cast<const h16x8*>(plbuf + (16 * rt + nl) * PSTRIDE + 16 * g);
+    }
+    for (int dt = 0; dt < 8; ++dt) {
+      const h16x8 vb = *reinterpret_cast<const h16x8*>(vbuf + (16 * dt + nl) * PSTRIDE + 16 * g);
+      for (int rt = 0; rt < 2; ++rt) {
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], vb, o[rt][dt], 0, 0, 0);
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[rt], vb, o[rt][dt], 0, 0, 0);
+      }
+    }
+    __asm__ volatile("" ::: "memory");       // the next step's LDS writes come after these reads
+  }
+
+  // merge the 4 waves: (max, sum) per row, O rescaled to the common max
+  __syncthreads();                                          // the per-wave areas become the merge area
+  float* mlw = reinterpret_cast<float*>(lds);               // [wave][32 rows][2]
+  float* ow = mlw + NWAVE * 32 * 2;                         // [wave][32 rows][128]
+  for (int rt = 0; rt < 2; ++rt)
+    for (int i = 0; i < 4; ++i) {
+      const int qv = 16 * rt + 4 * g + i;
+      if (nl == 0) {
+        mlw[(w * 32 + qv) * 2] = mrow[rt][i];
+        mlw[(w * 32 + qv) * 2 + 1] = lrow[rt][i];
+      }
+      for (int dt = 0; dt < 8; ++dt) ow[(w * 32 + qv) * AD + 16 * dt + nl] = o[rt][dt][i];
+    }
+  __syncthreads();
+  const size_t item = ((size_t)ag * a.Hkv + h) * a.nsplit + s;
+  for (int e = tid; e < nq * AD; e += NWAVE * 64) {
+    const int qv = e / AD, d = e % AD;
+    float m = NEG;
+    for (int ww = 0; ww < NWAVE; ++ww) m = mlw[(ww * 32 + qv) * 2] > m ? mlw[(ww * 32 + qv) * 2] : m;
+    float acc = 0.f, l = 0.f;
+    if (m != NEG)
+      for (int ww = 0; ww < NWAVE; ++ww) {
+        const float f = exp2f(mlw[(ww * 32 + qv) * 2] - m);
+        acc += f * ow[(ww * 32 + qv) * AD + d];
+        l += f * mlw[(ww * 32 + qv) * 2 + 1];
+      }
+    a.part_o[(item * 32 + qv) * AD + d] = acc;
+    if (d == 0) {
+      a.part_ml[(item * 32 + qv) * 2] = m;
+      a.part_ml[(item * 32 + qv) * 2 + 1] = l;
+    }
+  }
+}
+
+// out[a][i][hq][d]: the splits of (agent, key/value head) rescaled to the common
+// maximum, summed in split order, divided by the summed weights
+__global__ void __launch_bounds__(AD)
+attn_combine_kernel(AttnArgs a, float* __restrict__ out) {
+  const int hq = blockIdx.x, i = blockIdx.y, ag = blockIdx.z, d = threadIdx.x;
+  const int h = hq / GRP, qv = i * GRP + hq % GRP, Hq = a.Hkv * GRP;
+  const int L0 = a.lengths[ag];
+  const int total = (L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0)) + a.rows;
+  const int ns = (total + SPLIT - 1) / SPLIT;               // <= nsplit (sized for max_len)
+  const size_t item0 = ((size_t)ag * a.Hkv + h) * a.nsplit;
+  float m = -__builtin_inff();
+  for (int s = 0; s < ns; ++s) {
+    const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
+    m = ms > m ? ms : m;
+  }
+  float acc = 0.f, l = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
+    if (ms == -__builtin_inff()) continue;
+    const float f = exp2f(ms - m);
+    acc += f * a.part_o[((item0 + s) * 32 + qv) * AD + d];
+    l += f * a.part_ml[((item0 + s) * 32 + qv) * 2 + 1];
+  }
+  out[(((size_t)ag * a.rows + i) * Hq + hq) * AD + d] = acc / l;
+}
+
+hipError_t launch_attention(const AttnArgs& a, float* out, hipStream_t st) {
+  if (a.A == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.A), dim3(NWAVE * 64),
+                     0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Hkv * GRP), (unsigned)a.rows, (unsigned)a.A), dim3(AD), 0,
+                     st, a, out);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -67,6 +67,26 @@ inline int waves_for(int RT) { (void)RT; return 8; }   // two waves per SIMD at 
 inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }
 
+// Decode attention of the agents' step rows (attention.hip).  q [A][rows][8 Hkv][128],
+// caches [A][cap][Hkv][128] (bf16), lengths [A] (cached positions before the
+// step's rows, clamped to [0, max_len]); partials per (agent, head, split).
+constexpr int ATTN_HEAD_DIM = 128, ATTN_GROUP = 8, ATTN_SPLIT = 1024, ATTN_MAX_ROWS = 4;
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* lengths;
+  float* part_o;           // [A][Hkv][nsplit][32][128]
+  float* part_ml;          // [A][Hkv][nsplit][32][2]: running max (base 2) and sum
+  int32_t A, rows, Hkv, cap, max_len, nsplit;
+  float scale_log2;        // log2(e) / sqrt(128)
+};
+inline int attn_splits(int max_len, int rows) { return (max_len + rows + ATTN_SPLIT - 1) / ATTN_SPLIT; }
+inline size_t attn_ws_bytes(int A, int Hkv, int rows, int max_len) {
+  return (size_t)A * Hkv * attn_splits(max_len, rows) * 32 * (ATTN_HEAD_DIM + 2) * 4;
+}
+hipError_t launch_attention(const AttnArgs& a, float* out, hipStream_t st);
+
 hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);

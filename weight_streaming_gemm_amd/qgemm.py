@@ -23,7 +23,8 @@ MAX_R = 64
 EXPORTS = (
     "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_argmax_workspace_size", "qgemm_argmax_rows_ws",
-    "qgemm_verify_greedy", "qgemm_query", "qgemm_destroy",
+    "qgemm_verify_greedy", "qgemm_attention_workspace_size", "qgemm_decode_attention", "qgemm_query",
+    "qgemm_destroy",
     "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_run_verify", "qgemm_seq_errors", "qgemm_seq_destroy",
     "qgemm_status_string",
 )
@@ -66,6 +67,8 @@ def lib():
             "qgemm_argmax_workspace_size": [i32, i64, ctypes.POINTER(ctypes.c_size_t)],
             "qgemm_argmax_rows_ws": [vp, i32, i64, vp, vp, ctypes.c_size_t, vp],
             "qgemm_verify_greedy": [vp, i32, vp, i32, vp, vp, vp],
+            "qgemm_attention_workspace_size": [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)],
+            "qgemm_decode_attention": [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, ctypes.c_size_t, vp],
             "qgemm_query": [vp, i32, i32, ctypes.POINTER(Info)],
             "qgemm_destroy": [vp],
             "qgemm_seq_create": [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.c_uint32],
@@ -142,6 +145,25 @@ def verify_greedy(argmax_idx, drafts, drafts_per_agent: int, tokens, n_new, R: i
     _check(lib().qgemm_verify_greedy(_ptr(argmax_idx), R, _ptr(drafts), drafts_per_agent, _ptr(tokens), _ptr(n_new),
                                      _stream(stream)), "qgemm_verify_greedy")
     return tokens, n_new
+
+
+def attention_workspace_size(agents: int, rows: int, kv_heads: int, max_len: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().qgemm_attention_workspace_size(agents, rows, kv_heads, max_len, ctypes.byref(out)),
+           "qgemm_attention_workspace_size")
+    return out.value
+
+
+def decode_attention(q, k_cache, v_cache, lengths, out, workspace, max_len: int, stream=None):
+    """q [A, rows, Hq, 128], caches [A, cap, Hkv, 128] (bf16 bit patterns on the device),
+    lengths [A] int32 on the device, out [A, rows, Hq, 128] fp32."""
+    A, rows, Hq, d = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().qgemm_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths), A, rows, Hq, Hkv, d,
+                                        cap, max_len, _ptr(out), _ptr(workspace), nbytes, _stream(stream)),
+           "qgemm_decode_attention")
+    return out
 
 
 class QGemm:
