@@ -317,6 +317,58 @@ def ragged_report(seed: int, steps: int):
             "wall_s": round(wall, 3)}
 
 
+def attention_report(seed: int, reps: int = 20):
+    """Decode attention of 4 agents x 3 step rows over about 23K cached positions
+    each (a length mix), 64 query heads over 8 key/value heads of 128: time per
+    step (split and combine kernels) over two rotating cache copies, the KV bytes
+    it must read, and the fp64 oracle on one agent beside it."""
+    import numpy as np
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    from oracle import attention as at
+    from weight_streaming_gemm_amd import roofline as RF
+    rng = np.random.default_rng(seed)
+    lengths = [23000, 21877, 23549, 20001]
+    A, rows, Hkv, d, cap = 4, 3, 8, 128, 23552
+    max_len = cap - rows
+
+    def bf(shape):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return ((x.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)  # noqa: E731
+    q = bf((A, rows, 8 * Hkv, d))
+    kv = [(t(bf((A, cap, Hkv, d))), t(bf((A, cap, Hkv, d)))) for _ in range(2)]
+    qd = t(q)
+    ln = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    out = torch.empty((A, rows, 8 * Hkv, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(wsg.attention_workspace_size(A, rows, Hkv, max_len), dtype=torch.uint8, device=dev)
+    for c in range(2):
+        wsg.decode_attention(qd, kv[c][0], kv[c][1], ln, out, ws, max_len)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        wsg.decode_attention(qd, kv[r % 2][0], kv[r % 2][1], ln, out, ws, max_len)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    kv_bytes = sum((L + rows) * Hkv * d * 2 * 2 for L in lengths)
+    # the oracle on agent 0 (a quarter of the work), all host cores via numpy
+    k0 = kv[0][0][:1].cpu().numpy().view(np.uint16)
+    v0 = kv[0][1][:1].cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    at.decode_attention(q[:1], k0, v0, lengths[:1])
+    cpu_s = time.perf_counter() - t0
+    cpu_bytes = (lengths[0] + rows) * Hkv * d * 2 * 2
+    return {"agents": A, "rows_per_agent": rows, "q_heads": 8 * Hkv, "kv_heads": Hkv, "head_dim": d,
+            "lengths": lengths, "us_per_step": round(us, 2), "kv_bytes": kv_bytes,
+            "GB_s": round(kv_bytes / us / 1e3, 1), "pct_hbm_peak": round(kv_bytes / us / 1e3 / RF.HBM_PEAK_GBS * 100, 1),
+            "cpu_baseline": {"value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+                             "sample": f"agent 0 ({lengths[0]} positions), fp64 numpy, {cpu_s:.2f}s"}}
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP library's sources with comments and blank space
     removed: identifies the code a counter run measured (a comment edit does
@@ -396,10 +448,11 @@ def main():
                     help="with --report layer: only these row counts (comma-separated), e.g. for counter runs")
     ap.add_argument("--no-paths", action="store_true",
                     help="skip timing the pass on each kernel path for R = 1..4 (for profiler runs of one R)")
-    ap.add_argument("--report", choices=["layer", "ragged"],
+    ap.add_argument("--report", choices=["layer", "ragged", "attention"],
                     help="instead of the pass: 'layer' = one layer's GEMMs per matrix and R on both kernel paths "
                          "(plain weights, seed 1, R in 1,2,3,4,12,24,48; then edge-block weights, seed 4, R in "
-                         "24,48); 'ragged' = 100 passes under the seeded 1..4-agent schedule (seed 3)")
+                         "24,48); 'ragged' = 100 passes under the seeded 1..4-agent schedule (seed 3); "
+                         "'attention' = decode attention of 4 agents x 3 rows over ~23K cached positions")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -421,6 +474,12 @@ def main():
                "layer": layer_report(W.SEED_LAYER, 0, plain, copies=6) if plain else None,
                "large_R_edge_blocks": layer_report(W.SEED_LARGE_R, 2, edge, copies=6) if edge else None}
         print(json.dumps(rep), flush=True)
+        return
+    if args.report == "attention":
+        rep = attention_report(args.seed)
+        log(f"[attention] {rep['us_per_step']:.1f} us per step, {rep['GB_s']:.0f} GB/s of KV "
+            f"({rep['pct_hbm_peak']:.1f} % of 8 TB/s)")
+        print(json.dumps({"report": "attention", **rep}), flush=True)
         return
     if args.report == "ragged":
         print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
