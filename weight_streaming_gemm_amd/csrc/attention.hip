@@ -115,12 +115,15 @@ attn_split_kernel(AttnArgs a) {
       for (int c = 0; c < 4; ++c)
         kb[kt][c] = __builtin_bit_cast(b16x8, load16(kr, p < p_end ? coff(p, 32 * c + 8 * g) : AOOB));
     }
-    // V: the step's 32 positions x 128 dims as 512 chunks of 16 bytes, 8 per lane
+    // V: the step's 32 positions x 128 dims as 512 chunks of 16 bytes; lane
+    // (dc, m) takes positions 2m and 2m + 1 of dim chunks 4 it + dc (8 dims each)
+    const int vm = lane & 15, vdc = lane >> 4;
     w32x4 vc[8];
-    for (int it = 0; it < 8; ++it) {
-      const int cid = it * 64 + lane, pp = t0 + (cid >> 4);
-      vc[it] = load16(vr, pp < p_end ? coff(pp, 8 * (cid & 15)) : AOOB);
-    }
+    for (int it = 0; it < 4; ++it)
+      for (int e = 0; e < 2; ++e) {
+        const int pp = t0 + 2 * vm + e;
+        vc[2 * it + e] = load16(vr, pp < p_end ? coff(pp, 8 * (4 * it + vdc)) : AOOB);
+      }
     // S = Q K^T; lane (g, nl) holds S[16 rt + 4 g + i][16 kt + nl]
     f32x4 sc[2][2];
     for (int rt = 0; rt < 2; ++rt)
@@ -148,9 +151,9 @@ attn_split_kernel(AttnArgs a) {
         const float mnew = mrow[rt][i] > mx ? mrow[rt][i] : mx;
         float alpha = 1.f, sum = 0.f;
         if (mnew != NEG) {
-          alpha = exp2f(mrow[rt][i] - mnew);
+          alpha = __builtin_amdgcn_exp2f(mrow[rt][i] - mnew);
           for (int kt = 0; kt < 2; ++kt) {
-            pv[rt][kt][i] = exp2f(x[kt] - mnew);
+            pv[rt][kt][i] = __builtin_amdgcn_exp2f(x[kt] - mnew);
             sum += pv[rt][kt][i];
           }
         } else {
@@ -171,11 +174,18 @@ attn_split_kernel(AttnArgs a) {
           *reinterpret_cast<_Float16*>(pbuf + off) = hi;
           *reinterpret_cast<_Float16*>(plbuf + off) = (_Float16)(pv[rt][kt][i] - (float)hi);
         }
-    for (int it = 0; it < 8; ++it) {
-      const int cid = it * 64 + lane, pp = cid >> 4, d0 = 8 * (cid & 15);
-      const float e[8] = {bf16_lo(vc[it].x), bf16_hi(vc[it].x), bf16_lo(vc[it].y), bf16_hi(vc[it].y),
-                          bf16_lo(vc[it].z), bf16_hi(vc[it].z), bf16_lo(vc[it].w), bf16_hi(vc[it].w)};
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<_Float16*>(vbuf + (d0 + j) * PSTRIDE + pp * 2) = (_Float16)e[j];
+    // V^T: one 4-byte write per dim holds positions 2m and 2m + 1 (16 lanes
+    // write 64 contiguous bytes of a row)
+    for (int it = 0; it < 4; ++it) {
+      const w32x4 a0 = vc[2 * it], a1 = vc[2 * it + 1];
+      const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
+      const int d0 = 8 * (4 * it + vdc);
+      for (int j = 0; j < 8; ++j) {
+        const float f0 = (j & 1) ? bf16_hi(w0[j >> 1]) : bf16_lo(w0[j >> 1]);
+        const float f1 = (j & 1) ? bf16_hi(w1[j >> 1]) : bf16_lo(w1[j >> 1]);
+        typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<h16x2*>(vbuf + (d0 + j) * PSTRIDE + vm * 4) = h16x2{(_Float16)f0, (_Float16)f1};
+      }
     }
     __asm__ volatile("" ::: "memory");       // one wave's LDS accesses run in order
     h16x8 pa[2], pl[2];
@@ -215,7 +225,7 @@ attn_split_kernel(AttnArgs a) {
     float acc = 0.f, l = 0.f;
     if (m != NEG)
       for (int ww = 0; ww < NWAVE; ++ww) {
-        const float f = exp2f(mlw[(ww * 32 + qv) * 2] - m);
+        const float f = __builtin_amdgcn_exp2f(mlw[(ww * 32 + qv) * 2] - m);
         acc += f * ow[(ww * 32 + qv) * AD + d];
         l += f * mlw[(ww * 32 + qv) * 2 + 1];
       }
@@ -246,7 +256,7 @@ attn_combine_kernel(AttnArgs a, float* __restrict__ out) {
   for (int s = 0; s < ns; ++s) {
     const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
     if (ms == -__builtin_inff()) continue;
-    const float f = exp2f(ms - m);
+    const float f = __builtin_amdgcn_exp2f(ms - m);
     acc += f * a.part_o[((item0 + s) * 32 + qv) * AD + d];
     l += f * a.part_ml[((item0 + s) * 32 + qv) * 2 + 1];
   }
