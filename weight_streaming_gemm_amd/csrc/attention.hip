@@ -107,23 +107,31 @@ attn_split_kernel(AttnArgs a) {
   // byte offset of (position p, head h, dim d) in a cache
   auto coff = [&](int p, int d) { return (uint32_t)((((uint64_t)ag * a.cap + p) * a.Hkv + h) * AD + d) * 2; };
 
-  for (int t0 = p_begin + TK * w; t0 < p_end; t0 += TK * NWAVE) {
-    // K: B operands, position 16 kt + nl of the step, dims 32 c + 8 g .. + 7
-    b16x8 kb[2][4];
+  // loads of one 32-position step: K as B operands (position 16 kt + nl, dims
+  // 32 c + 8 g .. + 7); V as 512 chunks of 16 bytes, lane (dc, m) taking
+  // positions 2m and 2m + 1 of dim chunks 4 it + dc.  The next step's loads go
+  // out as soon as this step's K (after S) and V (after its LDS copy) are used.
+  const int vm = lane & 15, vdc = lane >> 4;
+  b16x8 kb[2][4];
+  w32x4 vc[8];
+  auto load_k = [&](int t0) {
     for (int kt = 0; kt < 2; ++kt) {
       const int p = t0 + 16 * kt + nl;
       for (int c = 0; c < 4; ++c)
         kb[kt][c] = __builtin_bit_cast(b16x8, load16(kr, p < p_end ? coff(p, 32 * c + 8 * g) : AOOB));
     }
-    // V: the step's 32 positions x 128 dims as 512 chunks of 16 bytes; lane
-    // (dc, m) takes positions 2m and 2m + 1 of dim chunks 4 it + dc (8 dims each)
-    const int vm = lane & 15, vdc = lane >> 4;
-    w32x4 vc[8];
+  };
+  auto load_v = [&](int t0) {
     for (int it = 0; it < 4; ++it)
       for (int e = 0; e < 2; ++e) {
         const int pp = t0 + 2 * vm + e;
         vc[2 * it + e] = load16(vr, pp < p_end ? coff(pp, 8 * (4 * it + vdc)) : AOOB);
       }
+  };
+  load_k(p_begin + TK * w);
+  load_v(p_begin + TK * w);
+  for (int t0 = p_begin + TK * w; t0 < p_end; t0 += TK * NWAVE) {
+    const int tn = t0 + TK * NWAVE;                         // the next step (loads return zeros past p_end)
     // S = Q K^T; lane (g, nl) holds S[16 rt + 4 g + i][16 kt + nl]
     f32x4 sc[2][2];
     for (int rt = 0; rt < 2; ++rt)
@@ -132,6 +140,7 @@ attn_split_kernel(AttnArgs a) {
         for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][c], kb[kt][c], acc, 0, 0, 0);
         sc[rt][kt] = acc;
       }
+    load_k(tn);
     // mask, scale, online softmax (row statistics shared by the 16 lanes of a group)
     float pv[2][2][4];
     for (int rt = 0; rt < 2; ++rt)
@@ -187,6 +196,7 @@ attn_split_kernel(AttnArgs a) {
         *reinterpret_cast<h16x2*>(vbuf + (d0 + j) * PSTRIDE + vm * 4) = h16x2{(_Float16)f0, (_Float16)f1};
       }
     }
+    load_v(tn);
     __asm__ volatile("" ::: "memory");       // one wave's LDS accesses run in order
     h16x8 pa[2], pl[2];
     for (int rt = 0; rt < 2; ++rt) {
@@ -247,12 +257,15 @@ attn_combine_kernel(AttnArgs a, float* __restrict__ out) {
   const int total = (L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0)) + a.rows;
   const int ns = (total + SPLIT - 1) / SPLIT;               // <= nsplit (sized for max_len)
   const size_t item0 = ((size_t)ag * a.Hkv + h) * a.nsplit;
+  // (unrolled so that several splits' loads are in flight at once)
   float m = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
     m = ms > m ? ms : m;
   }
   float acc = 0.f, l = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
     if (ms == -__builtin_inff()) continue;
