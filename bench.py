@@ -403,6 +403,99 @@ def measured_traffic(R: int):
     return rec.get("bytes_per_launch")
 
 
+STREAM_KERNEL = "qg::stream_kernel<1, 1, 8, false"     # the R = 12 variants (both min-term forms)
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _read_csv(path: str):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find_csv(d: str, suffix: str) -> str:
+    for root, _, files in os.walk(d):
+        for name in files:
+            if name.endswith(suffix):
+                return os.path.join(root, name)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: int, R: int,
+                       commands: dict) -> dict:
+    """Turn one kernel-trace run and two counter runs (FETCH_SIZE, WRITE_SIZE in KiB per
+    dispatch) into profiles/traffic.json and a markdown summary.  The counters are
+    scaled so that the plain device copy of copy_mib MiB reads and writes exactly that
+    many bytes; the streaming kernel's figures are averages over its dispatches."""
+    stats = _read_csv(_find_csv(trace_dir, "kernel_stats.csv"))
+    per = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for row in _read_csv(_find_csv(d, "counter_collection.csv")):
+            if row["Counter_Name"] != name:
+                continue
+            k = per.setdefault(row["Kernel_Name"], {})
+            k.setdefault(name, []).append(float(row["Counter_Value"]))
+    copy_kib = copy_mib * 1024.0
+    cp = per[COPY_KERNEL]
+    # the copy runs three times; its largest dispatch is the full-size one
+    scale = {c: copy_kib / max(cp[c]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    fetch, write, n_disp = [], [], 0
+    for kname, v in per.items():
+        if kname.startswith(STREAM_KERNEL.replace("qg::", "void qg::")) or kname.startswith(STREAM_KERNEL):
+            fetch += v.get("FETCH_SIZE", [])
+            write += v.get("WRITE_SIZE", [])
+    fetch_b = sum(fetch) / len(fetch) * 1024 * scale["FETCH_SIZE"]
+    write_b = sum(write) / len(write) * 1024 * scale["WRITE_SIZE"]
+    calls = tot_ns = 0.0
+    for row in stats:
+        if STREAM_KERNEL in row["Name"]:
+            calls += float(row["Calls"])
+            tot_ns += float(row["TotalDurationNs"])
+    avg_us = tot_ns / calls / 1e3
+    rec = {
+        "kernel": "stream_kernel (all variants of the pass)",
+        "R": R,
+        "kernel_source_sha256": kernel_source_digest(),
+        "digest": "sha256 of the csrc sources with comments and blank space removed (bench.kernel_source_digest)",
+        "fetch_bytes_per_launch": int(round(fetch_b)),
+        "write_bytes_per_launch": int(round(write_b)),
+        "bytes_per_launch": int(round(fetch_b + write_b)),
+        "avg_launch_us_trace": round(avg_us, 3),
+        "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4), "WRITE_SIZE": round(scale["WRITE_SIZE"], 4),
+                  "from": f"{COPY_KERNEL} of {copy_mib} MiB"},
+        "summary": "profiles/stream_kernel_full_pass_R12.md",
+    }
+    alg = 17990737920 / 257
+    lines = [f"# Streaming kernel over the full 257-GEMM weight pass at R = {R}", "",
+             "Kernel-trace summary (`rocprofv3 --kernel-trace --stats`, run from /tmp with TMPDIR=/tmp):", "",
+             "```", commands["trace"], "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for row in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{row['Name'][:90]}` | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                     f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} | "
+                     f"{float(row['Percentage']):.1f} % |")
+    lines += ["", "Hardware counters, one `--pmc` pass per counter (KiB per dispatch, averaged over the "
+              "dispatches of each kernel):", "", "```", commands["fetch"], commands["write"], "```", "",
+              "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) |", "|---|---|---|---|"]
+    for kname, v in sorted(per.items()):
+        f_ = v.get("FETCH_SIZE", [0.0])
+        w_ = v.get("WRITE_SIZE", [0.0])
+        lines.append(f"| `{kname[:90]}` | {len(f_)} | {sum(f_) / len(f_):.1f} | {sum(w_) / len(w_):.1f} |")
+    lines += ["", "Reading the numbers (MI355X, one GPU):", "",
+              f"- The streaming kernel (both min-term variants) averages {avg_us:.2f} us per launch over "
+              f"{int(calls)} launches in the trace; a launch moves {alg / 1e6:.1f} MB of packed weights on average "
+              f"(17,990,737,920 B / 257), i.e. {alg / avg_us / 1e3:.0f} GB/s "
+              f"({alg / avg_us / 1e3 / 80:.1f} % of 8 TB/s).",
+              f"- Counter scale from the {copy_mib} MiB device copy ({COPY_KERNEL}): FETCH_SIZE x "
+              f"{scale['FETCH_SIZE']:.3f}, WRITE_SIZE x {scale['WRITE_SIZE']:.3f}.",
+              f"- Streaming kernel, scaled, per launch on average: {fetch_b / 1e6:.1f} MB fetched "
+              f"({fetch_b / alg:.3f}x the algorithmic weight bytes; the rest is activations and partial tiles), "
+              f"{write_b / 1e6:.2f} MB written (outputs and partial tiles).", ""]
+    rec["summary_text"] = "\n".join(lines)
+    return rec
+
+
 def cpu_baseline(seed: int):
     """The fp64 oracle as it stands, on layer 0's four GEMMs at R=12 (a bounded
     sample of the pass: one of its 64 layers), all host cores."""
@@ -453,7 +546,32 @@ def main():
                          "(plain weights, seed 1, R in 1,2,3,4,12,24,48; then edge-block weights, seed 4, R in "
                          "24,48); 'ragged' = 100 passes under the seeded 1..4-agent schedule (seed 3); "
                          "'attention' = decode attention of 4 agents x 3 rows over ~23K cached positions")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: read the rocprofv3 CSVs of a kernel-trace run and of the FETCH_SIZE and "
+                         "WRITE_SIZE counter runs (each made with --copy-calibration, size given by that flag) "
+                         "and rewrite profiles/traffic.json and profiles/stream_kernel_full_pass_R12.md")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        cmds = {
+            "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
+                     "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --sweep 12 --no-paths",
+            "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
+                     f"python3 bench.py --kernel-only --no-cpu-baseline --sweep 12 "
+                     f"--copy-calibration {args.copy_calibration}",
+            "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
+                     f"python3 bench.py --kernel-only --no-cpu-baseline --sweep 12 "
+                     f"--copy-calibration {args.copy_calibration}",
+        }
+        rec = summarize_profiles(*args.summarize_profiles, args.copy_calibration or 1024, args.R, cmds)
+        text = rec.pop("summary_text")
+        with open(os.path.join(ROOT, "profiles", "stream_kernel_full_pass_R12.md"), "w") as f:
+            f.write(text)
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the weight pass is not sharded across GPUs in this build "
