@@ -10,7 +10,9 @@ the product path, that each group of matrix-core instructions in the step loop
 is preceded by a wait that leaves the later stages in flight, and that no
 streaming kernel spills to scratch (the offline packer keeps a block in private
 memory; it is not on the timed path).  The persistent variant with two row
-tiles is left out: its loop still copies ring slots (a known slow spot).  The
+tiles is left out: one of its four steps waits for two of the three later
+stages (a known slow spot).  The persistent launch always forms the min term
+per step, so it has no sub-block-sum variant.  The
 vector-unit variants (one per row count 1..4) are checked the same way on
 their groups of dot-product instructions; there the compiler issues the
 refill of a stage before the stage's dot products, so the wait may count the
@@ -91,8 +93,7 @@ def test_persistent_step_loop_keeps_ring_in_flight(asm, rt, nw):
 
 
 @pytest.mark.parametrize("rt,nw", VARIANTS)
-@pytest.mark.parametrize("multi", [False, True])
-@pytest.mark.parametrize("msum", [False, True])
+@pytest.mark.parametrize("multi,msum", [(False, False), (False, True), (True, False)])
 def test_stream_kernels_do_not_spill(asm, rt, nw, multi, msum):
     body = _kernel_body(asm, rt, nw, multi, msum)
     assert "scratch_store" not in body and "scratch_load" not in body

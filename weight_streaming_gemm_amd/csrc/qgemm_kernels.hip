@@ -301,18 +301,11 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     set_range(c);
   };
   // the load cursor's next step: the next one of this wave's sub-range; past its
-  // end, in a launch of several GEMMs, the first step of this wave's sub-range of
-  // the next GEMM that gives it any, so that the weights of GEMM g + 1 stream
-  // while GEMM g finishes; past the last GEMM, none (the loads return zeros)
-  auto skip_done = [&](Cursor& c) __attribute__((always_inline)) {
-    if constexpr (MULTI)
-      while (c.it >= c.it1 && c.g < G) enter(c, c.g + 1);
-  };
+  // end none (the loads return zeros without memory traffic)
   auto next = [&](Cursor& c) __attribute__((always_inline)) {
     c.it = uni(c.it + 1);
     c.j = uni(c.j + 1);
     if (c.j == c.KB) { c.j = 0; next_tile(c); }
-    skip_done(c);
   };
 
   // ---- weights: RING steps ahead -----------------------------------------------
@@ -337,7 +330,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // workgroup index (all workgroups read the same activations).  The loads of
   // the first batch are issued on their own (x_load) so that the kernel can
   // queue them ahead of the weight ring. ---
-  constexpr int XGROUPS = NTHR / 32, XB = MULTI ? 8 : 16;
+  constexpr int XGROUPS = NTHR / 32, XB = (MULTI && RT > 2) ? 8 : 16;   // (registers)
   u32x2 xlo[XB], xhi[XB];
   // (slot, row) of this thread's k-th row of the batch at base, rows = nslots R;
   // slots rotated by the workgroup index.  Walked incrementally: one division.
@@ -705,11 +698,16 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   };
 
   // ---- all workgroups finished GEMM g (bounded wait; a timeout sets err) -----
-  auto grid_barrier = [&](int g) __attribute__((always_inline)) {
+  // Arrival waits only for this workgroup's own stores (the ring holds no loads
+  // then: its refills past the range end address nothing); the weights of the
+  // next GEMM are requested between arrival and the wait.
+  auto grid_arrive = [&](int g) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(a.sync + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto grid_wait = [&](int g) __attribute__((always_inline)) {
     if (tid == 0) {
-      __hip_atomic_fetch_add(a.sync + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       uint32_t n = 0;
       while (__hip_atomic_load(a.sync + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)P) {
         if (++n > SPIN_LIMIT) {
@@ -729,7 +727,6 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   GemmDesc D = get_desc(0);
   x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
   L = C;
-  skip_done(L);
   // The ring's first loads go out before the activations are staged, so that
   // they land meanwhile; with sub-block sums (MSUM) they go out after: the
   // compiler then keeps the ring slots in fixed registers through the step
@@ -742,7 +739,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       next(L);
     }
   };
-  if constexpr (MULTI || !MSUM) ring_fill();
+  if constexpr (!MSUM) ring_fill();
   int xs = 0;                                     // activation slot of C's step
   int ja = 0;                                     // first block of the current segment
   int a_w = 0;                                    // first step of this wave's sub-range
@@ -812,26 +809,26 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     }
     close_range(C, D);
   } else {
-    // Several GEMMs: the ring runs on from one GEMM into the next (the load
-    // cursor is already in GEMM g + 1 while GEMM g finishes), so the GEMM
-    // boundary is handled inside the step loop and the loop never restarts.
-    // boundary(): close GEMM g, wait for all workgroups, start this wave's next
-    // non-empty sub-range; false when the launch is done.
-    auto boundary = [&]() __attribute__((always_inline)) -> bool {
-      for (;;) {
-        close_range(C, D);
-        if (C.g + 1 >= G) return false;
-        grid_barrier(C.g);
-        enter(C, C.g + 1);
-        D = get_desc(C.g);
-        x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
-        start_range();
-        if (C.it < C.it1) return true;
-      }
-    };
+    // Several GEMMs, each as in a launch of one: the ring stops at the end of a
+    // wave's sub-range (its last refills address nothing), the range closes, the
+    // workgroup arrives at the grid barrier, requests the first RING steps of
+    // its next sub-range (weights do not depend on the previous output), then
+    // waits for every workgroup and stages the activations.  The step loop
+    // restarts at ring slot 0 for every GEMM.
     start_range();
-    if (C.it < C.it1 || boundary()) {
-      run_ring([&](auto S) __attribute__((always_inline)) { return step(S) && !boundary(); });
+    for (;;) {
+      if (C.it < C.it1) run_ring([&](auto S) __attribute__((always_inline)) { return step(S); });
+      close_range(C, D);
+      if (C.g + 1 >= G) break;
+      grid_arrive(C.g);
+      const int g = C.g;
+      enter(C, g + 1);
+      D = get_desc(C.g);
+      L = C;
+      ring_fill();
+      grid_wait(g);
+      x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
+      start_range();
     }
   }
 
@@ -1084,11 +1081,16 @@ static hipError_t launch_stream_m(const StreamArgs& a, bool cooperative, hipStre
                        (const GemmDesc*)nullptr);
     return hipGetLastError();
   }
-  StreamArgs args = a;
-  const GemmDesc* descs = a.descs;
-  void* params[] = {&args, &descs};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true, MSUM>),
-                                    dim3((unsigned)a.P), dim3(NW * 64), params, 0, st);
+  // one launch over several GEMMs: the min term per step (no sub-block sums)
+  if constexpr (MSUM) {
+    return hipErrorInvalidValue;
+  } else {
+    StreamArgs args = a;
+    const GemmDesc* descs = a.descs;
+    void* params[] = {&args, &descs};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true, false>),
+                                      dim3((unsigned)a.P), dim3(NW * 64), params, 0, st);
+  }
 }
 template <int RT, int NT, int NW>
 static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
@@ -1133,7 +1135,7 @@ int stream_occupancy(int RT, int NT, int NW) {
   int blocks = 0;
 #define QG_CASE(rt, nt, nw) \
   if (RT == rt && NT == nt && NW == nw) { \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true, true>, nw * 64, 0) != \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true, false>, nw * 64, 0) != \
         hipSuccess) \
       return 0; \
     return blocks; \
