@@ -259,6 +259,66 @@ def layer_report(seed: int, edge: int, Rs, copies: int):
             "by_R": out}
 
 
+def prefill_report(seed: int, chunks, copies: int = 2):
+    """Prompt-chunk rows sharing the weight pass: one layer's four GEMMs at
+    R = 12 decode rows + P prompt rows through the row-tiled kernel
+    (qgemm_run_prefill), per matrix and per layer: time, useful TFLOP/s against
+    the fp16 dense matrix-core peak, and weight GB/s; next to the layer at the
+    12 decode rows alone on the streaming kernel."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import workloads as W
+    import weight_streaming_gemm_amd as wsg
+    from weight_streaming_gemm_amd import roofline as RF
+    dev = torch.device("cuda:0")
+    Rs = [12 + c for c in chunks]
+    R_max = max(Rs)
+    mats = W.layer_mats(0)
+    per = []
+    for m in mats:
+        canon = np.concatenate([synth.matrix_rows(seed, mid, n, m.K) for mid, n in zip(m.mids, m.splits)])
+        cd = torch.from_numpy(canon).to(dev)
+        pk = torch.empty(wsg.packed_size(m.N, m.K), dtype=torch.uint8, device=dev)
+        wsg.pack(cd, pk, m.N, m.K)
+        torch.cuda.synchronize()
+        del cd
+        pks = [pk] + [pk.clone() for _ in range(copies - 1)]
+        gs = [wsg.QGemm(q, m.N, m.K, max_R=12) for q in pks]
+        x = torch.from_numpy(synth.x_bf16(seed, W.X_STREAM[m.K], R_max, m.K).view(np.int16)).to(dev)
+        y = torch.empty((R_max, m.N), dtype=torch.float32, device=dev)
+        per.append((m, pks, gs, x, y))
+    layer_bytes = sum(m.packed_bytes for m in mats)
+    calls = [lambda g=gs[c], x=x, y=y: g.run(x[:12], y[:12], 12) for c in range(copies) for m, pks, gs, x, y in per]
+    base_us = graph_ms(calls) / copies * 1e3
+    log(f"[prefill] decode rows alone (R=12, streaming kernel): {base_us:.1f} us per layer")
+    out = {}
+    for P, R in zip(chunks, Rs):
+        rec = {}
+        for m, pks, gs, x, y in per:
+            us = graph_ms([lambda g=g, x=x, y=y: g.run_prefill(x[:R], y[:R], R) for g in gs]) / copies * 1e3
+            tf = 2 * R * m.N * m.K / us / 1e6
+            rec[m.name] = {"us": round(us, 2), "useful_tflop_s": round(tf, 1),
+                           "pct_fp16_mfma_peak": round(tf / RF.MFMA_F16_DENSE_TFLOPS * 100, 1),
+                           "weight_GB_s": round(m.packed_bytes / us / 1e3, 1)}
+        calls = [lambda g=gs[c], x=x, y=y: g.run_prefill(x[:R], y[:R], R)
+                 for c in range(copies) for m, pks, gs, x, y in per]
+        us = graph_ms(calls) / copies * 1e3
+        flops = sum(2 * R * m.N * m.K for m in mats)
+        rec["layer"] = {"us": round(us, 2), "useful_tflop_s": round(flops / us / 1e6, 1),
+                        "pct_fp16_mfma_peak": round(flops / us / 1e6 / RF.MFMA_F16_DENSE_TFLOPS * 100, 1),
+                        "weight_GB_s": round(layer_bytes / us / 1e3, 1),
+                        "prompt_rows_per_s_per_layer_pass": round(P / us * 1e6, 1)}
+        out[str(P)] = rec
+        log(f"[prefill] P={P:5d} (R={R}): " + ", ".join(f"{k} {v['us']:.1f} us {v['useful_tflop_s']:.0f} TF/s"
+                                                      for k, v in rec.items()))
+    for m, pks, gs, x, y in per:
+        for g in gs:
+            g.close()
+    return {"seed": seed, "copies": copies, "decode_rows": 12, "layer_packed_bytes": layer_bytes,
+            "decode_only_us_per_layer": round(base_us, 2), "by_prompt_rows": out}
+
+
 def ragged_report(seed: int, steps: int):
     """The full pass under a seeded schedule of active agents: step t runs R_t =
     3 * a_t rows (a_t uniform in 1..4), with fresh activations per step (1 % of
@@ -541,11 +601,13 @@ def main():
                     help="with --report layer: only these row counts (comma-separated), e.g. for counter runs")
     ap.add_argument("--no-paths", action="store_true",
                     help="skip timing the pass on each kernel path for R = 1..4 (for profiler runs of one R)")
-    ap.add_argument("--report", choices=["layer", "ragged", "attention"],
+    ap.add_argument("--report", choices=["layer", "ragged", "attention", "prefill"],
                     help="instead of the pass: 'layer' = one layer's GEMMs per matrix and R on both kernel paths "
                          "(plain weights, seed 1, R in 1,2,3,4,12,24,48; then edge-block weights, seed 4, R in "
                          "24,48); 'ragged' = 100 passes under the seeded 1..4-agent schedule (seed 3); "
-                         "'attention' = decode attention of 4 agents x 3 rows over ~23K cached positions")
+                         "'attention' = decode attention of 4 agents x 3 rows over ~23K cached positions; "
+                         "'prefill' = one layer at 12 decode rows + a prompt chunk of 64..2048 rows on the "
+                         "row-tiled kernel")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 CSVs of a kernel-trace run and of the FETCH_SIZE and "
                          "WRITE_SIZE counter runs (each made with --copy-calibration, size given by that flag) "
@@ -592,6 +654,10 @@ def main():
                "layer": layer_report(W.SEED_LAYER, 0, plain, copies=6) if plain else None,
                "large_R_edge_blocks": layer_report(W.SEED_LARGE_R, 2, edge, copies=6) if edge else None}
         print(json.dumps(rep), flush=True)
+        return
+    if args.report == "prefill":
+        rep = prefill_report(1, [64, 128, 256, 512, 1024, 2048])
+        print(json.dumps({"report": "prefill", **rep}))
         return
     if args.report == "attention":
         rep = attention_report(args.seed)

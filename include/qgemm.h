@@ -130,6 +130,23 @@ int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
  * serve (R > 4). */
 int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, void *stream);
 
+/* Prompt-chunk rows sharing the weight pass (OpenJet multi-agent serving page,
+ * section on what the design buys: another agent's long prefill runs while the
+ * others decode, so a chunk of prompt rows and the agents' decode rows go
+ * through the same weights): y = x . W^T for R rows, 0 <= R <= QGEMM_MAX_PREFILL_R,
+ * with a kernel that tiles rows as well as outputs (128 x 128 per workgroup,
+ * every weight read serving a 128-row tile; bound by the matrix cores at
+ * hundreds of rows).  Same operands and result as qgemm_run: x device bf16
+ * [R x K], y device fp32 [R x N] (overwritten), both row-major and 16-byte
+ * aligned; the same arithmetic per 256-weight block (exact binary16 products
+ * of sc*q with x, fp32 sums, then d and the min term).  Needs no workspace and
+ * does not depend on the handle's max_R; it may run on several streams at once.
+ * Enqueues one kernel on `stream`; R = 0 is a no-op.
+ * Errors: QGEMM_EINVAL (bad handle, null x or y), QGEMM_EALIGN,
+ * QGEMM_ERANGE_R (R < 0, R > QGEMM_MAX_PREFILL_R, or R*K*2 >= 2^31), QGEMM_EHIP. */
+#define QGEMM_MAX_PREFILL_R 8192
+int qgemm_run_prefill(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
+
 /* The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
  * 16-byte aligned): w_out[n, k] is the binary32 value nearest to
  * d*sc_s*q_k - dmin*m_s (one rounding; bit-exact), decoded from the packed

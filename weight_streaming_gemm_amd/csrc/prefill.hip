@@ -1,0 +1,209 @@
+// prefill.hip — the same fused dequantise-and-multiply for many rows: a prompt
+// chunk (tens to thousands of rows) together with the agents' decode rows.
+//
+// The OpenJet page's claim that a long prompt need not stall decode (section on
+// what the design buys: another agent's 20K-token prefill running while the
+// others decode) needs the prompt's rows to go through the same weight pass.
+// With hundreds of rows a weight is used hundreds of times, so the product is
+// bound by the matrix cores, not by the weight stream: this kernel tiles rows
+// as well as outputs, and every weight read serves a 128-row tile.
+//
+//   y[r, n] = sum_k w[n, k] x[r, k],  w[n, k] = d sc_s q_k - dmin m_s
+//
+// is computed per 256-weight block exactly as in the streaming kernel:
+// ds = sum_k (sc_s q_k) x[r, k] and ms = sum_s m_s X_s on the fp16 matrix
+// cores (exact integer B operands, fp32 sums), then acc += d ds - dmin ms.
+//
+// Work: one workgroup of 4 waves per (128-row tile, 128-output tile), over the
+// whole of K (no split, so every output is written once, in a fixed order).
+// Waves form a 2 x 2 grid; a wave owns 64 rows (4 row tiles of 16) x 64 outputs
+// (4 sub-tiles of 16): 16 accumulator tiles.  Per block the workgroup stages
+// its 128 rows of x as binary16 operands (and the 8 sub-block sums per row) in
+// LDS, double-buffered: the next block's activations and weights are in flight
+// while the current block is multiplied.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+#include "operand.h"
+#include "qgemm_internal.h"
+
+namespace qg {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PF_RT = 4;                       // row tiles per wave
+constexpr int PF_U = 4;                        // output sub-tiles per wave
+constexpr int PF_TILES = 2 * PF_RT;            // row tiles per workgroup (128 rows)
+constexpr int PF_CHUNK = 64 * 16;              // one (row tile, step) operand chunk: 64 lanes x 16 B
+constexpr int PF_X = PF_TILES * 8 * PF_CHUNK;  // activations of one block: 64 KiB
+constexpr int PF_S = PF_TILES * PF_CHUNK;      // their sub-block sums: 8 KiB
+constexpr int PF_BUF = PF_X + PF_S;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+}
+
+// s plus the eight bf16 values of a 16-byte load, each widened exactly to fp32
+// (a bf16 is the high half of a binary32), added in order.  (A chain of bf16
+// dot products against ones over the four dwords of one vector was compiled to
+// four reads of the first dword on gfx950, so plain adds are used.)
+__device__ __forceinline__ float sum8_bf16(u32x4 v, float s) {
+  for (int i = 0; i < 4; ++i) {
+    s += __builtin_bit_cast(float, v[i] << 16);
+    s += __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+  }
+  return s;
+}
+
+}  // namespace
+
+// grid (row tiles of 128, output tiles of 128); 256 threads
+__global__ void __launch_bounds__(256, 1)
+prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_t hdr_bytes,
+               const uint16_t* __restrict__ x, float* __restrict__ y, int R, int N, int NS, int KB) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, nl = lane & 15;
+  const int wm = w & 1, wn = w >> 1;                 // the wave's place in the 2 x 2 grid
+  const int m0 = blockIdx.x * (PF_TILES * 16);       // first row of the workgroup
+  const int ns0 = (blockIdx.y * 2 + wn) * PF_U;      // first sub-tile of the wave
+  const int K = KB * SB_W;
+
+  const __amdgpu_buffer_rsrc_t qr = rsrc(packed, quant_bytes);
+  const __amdgpu_buffer_rsrc_t hr = rsrc(packed + quant_bytes, hdr_bytes);
+  const __amdgpu_buffer_rsrc_t xr = rsrc(x, (uint32_t)R * (uint32_t)K * 2u);
+  constexpr uint32_t OOB = 0x80000000u;
+
+  // ---- weights of block j for the wave's sub-tiles (past N: no traffic, zeros) ----
+  struct WB { u32x4 qa[PF_U], qb[PF_U], hd[PF_U]; };
+  auto load_w = [&](WB& b, int j) __attribute__((always_inline)) {
+    for (int u = 0; u < PF_U; ++u) {
+      const int ns = ns0 + u;
+      const bool ok = ns < NS;
+      const uint32_t qo = ok ? (uint32_t)(ns * KB + j) * CHUNK_Q + lane * 16 : OOB;
+      const uint32_t ho = ok ? (uint32_t)(ns * KB + j) * CHUNK_H + nl * 16 : OOB;
+      b.qa[u] = load16<2>(qr, qo);
+      b.qb[u] = load16<2>(qr, qo + 1024);
+      b.hd[u] = load16<2>(hr, ho);
+    }
+  };
+
+  // ---- activations of block j: thread (wave w, lane 16 g + r) converts, for row
+  // tiles w and w + 4, row 16 rt + r's 64 values of sub-blocks 2g and 2g + 1
+  // (one 128-byte line) into the 8 operands of lane 16 g + r, and the two sums.
+  // Rows past R load nothing and stage zeros. ---
+  struct XB { u32x4 v[2][8]; };
+  auto load_x = [&](XB& b, int j) __attribute__((always_inline)) {
+    for (int i = 0; i < 2; ++i) {
+      const int row = m0 + (w + 4 * i) * 16 + nl;
+      const uint32_t base = row < R ? (uint32_t)((row * K + j * SB_W + 64 * g4) * 2) : OOB;
+      for (int c = 0; c < 8; ++c) b.v[i][c] = load16<0>(xr, base == OOB ? OOB : base + 16 * c);
+    }
+  };
+  auto store_x = [&](const XB& b, int buf) __attribute__((always_inline)) {
+    uint8_t* const X = lds + buf * PF_BUF;
+    for (int i = 0; i < 2; ++i) {
+      const int rt = w + 4 * i;
+      // b.v[i][c] holds k = 64 g + 8 c .. 8 c + 7: c < 4 sub-block 2g, c >= 4 sub-block 2g + 1
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 lo = b.v[i][t >> 1], hi = b.v[i][4 + (t >> 1)];
+        const int o = (t & 1) * 2;       // dwords of k = 4 t .. 4 t + 3 within the 8-value load
+        const f16x8 op = build_a(lo[o], lo[o + 1], hi[o], hi[o + 1]);
+        *reinterpret_cast<f16x8*>(X + (rt * 8 + t) * PF_CHUNK + lane * 16) = op;
+      }
+      float s0 = 0.f, s1 = 0.f;
+      for (int c = 0; c < 4; ++c) s0 = sum8_bf16(b.v[i][c], s0);
+      for (int c = 4; c < 8; ++c) s1 = sum8_bf16(b.v[i][c], s1);
+      *reinterpret_cast<f16x8*>(X + PF_X + rt * PF_CHUNK + lane * 16) = build_s(s0, s1);
+    }
+  };
+
+  f32x4 acc[PF_RT][PF_U];
+  for (int rt = 0; rt < PF_RT; ++rt)
+    for (int u = 0; u < PF_U; ++u) acc[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- one block: ds on the matrix cores over its 8 steps, then the min term ----
+  auto compute = [&](const WB& b, int buf) __attribute__((always_inline)) {
+    const uint8_t* const X = lds + buf * PF_BUF;
+    WConst c[PF_U];
+    for (int u = 0; u < PF_U; ++u) c[u] = header_consts(b.hd[u].x, b.hd[u].y, b.hd[u].z, b.hd[u].w, g4);
+    f32x4 ds[PF_RT][PF_U];
+    for (int rt = 0; rt < PF_RT; ++rt)
+      for (int u = 0; u < PF_U; ++u) ds[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) {
+      f16x8 a[PF_RT];
+      for (int rt = 0; rt < PF_RT; ++rt)
+        a[rt] = *reinterpret_cast<const f16x8*>(X + ((wm * PF_RT + rt) * 8 + t) * PF_CHUNK + lane * 16);
+      for (int u = 0; u < PF_U; ++u) {
+        const uint32_t wd = t < 4 ? b.qa[u][t] : b.qb[u][t - 4];
+        const f16x8 bo = build_b(wd, c[u]);
+        for (int rt = 0; rt < PF_RT; ++rt)
+          ds[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], bo, ds[rt][u], 0, 0, 0);
+      }
+    }
+    for (int rt = 0; rt < PF_RT; ++rt) {
+      const f16x8 sx = *reinterpret_cast<const f16x8*>(X + PF_X + (wm * PF_RT + rt) * PF_CHUNK + lane * 16);
+      for (int u = 0; u < PF_U; ++u) {
+        const f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(sx, build_m(c[u]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          acc[rt][u][i] = __builtin_fmaf(c[u].d, ds[rt][u][i], acc[rt][u][i]);
+          acc[rt][u][i] = __builtin_fmaf(c[u].nmin, ms[i], acc[rt][u][i]);
+        }
+      }
+    }
+  };
+
+  // ---- the K loop, two blocks per pass so that the register buffers alternate
+  // without copies; block j + 1's loads are in flight during block j ----
+  WB wa, wb;
+  XB xb;
+  load_w(wa, 0);
+  load_x(xb, 0);
+  store_x(xb, 0);
+  __syncthreads();
+  for (int j = 0; j < KB; j += 2) {
+    const bool more1 = j + 1 < KB, more2 = j + 2 < KB;
+    if (more1) { load_w(wb, j + 1); load_x(xb, j + 1); }
+    compute(wa, 0);
+    if (more1) store_x(xb, 1);
+    __syncthreads();
+    if (!more1) break;
+    if (more2) { load_w(wa, j + 2); load_x(xb, j + 2); }
+    compute(wb, 1);
+    if (more2) store_x(xb, 0);
+    __syncthreads();
+  }
+
+  // ---- outputs: lane (g, nl) of tile (rt, u) holds rows 4 g .. 4 g + 3 of output nl ----
+  typedef float __attribute__((address_space(1))) global_float;
+  global_float* const yg = (global_float*)y;
+  for (int u = 0; u < PF_U; ++u) {
+    const int n = (ns0 + u) * TILE_N + nl;
+    if (n >= N) continue;
+    for (int rt = 0; rt < PF_RT; ++rt)
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + (wm * PF_RT + rt) * 16 + 4 * g4 + i;
+        if (row < R) yg[(int64_t)row * N + n] = acc[rt][u][i];
+      }
+  }
+}
+
+hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,
+                          hipStream_t st) {
+  const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
+  const uint32_t qb = (uint32_t)quant_region_bytes(N, K);
+  const uint32_t hb = (uint32_t)(packed_bytes(N, K) - quant_region_bytes(N, K));
+  const dim3 grid((unsigned)((R + PF_TILES * 16 - 1) / (PF_TILES * 16)), (unsigned)((NS + 2 * PF_U - 1) / (2 * PF_U)));
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, packed, qb, hb, reinterpret_cast<const uint16_t*>(x), y,
+                     R, (int)N, (int)NS, (int)KB);
+  return hipGetLastError();
+}
+
+}  // namespace qg

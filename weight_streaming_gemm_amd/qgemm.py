@@ -18,10 +18,11 @@ QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH = -4, -5, -6, -7
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 SEQ_PERSISTENT = 1
 MAX_R = 64
+MAX_PREFILL_R = 8192
 
 # every symbol include/qgemm.h declares
 EXPORTS = (
-    "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path",
+    "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path", "qgemm_run_prefill",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_argmax_workspace_size", "qgemm_argmax_rows_ws",
     "qgemm_verify_greedy", "qgemm_attention_workspace_size", "qgemm_decode_attention", "qgemm_query",
     "qgemm_destroy",
@@ -62,6 +63,7 @@ def lib():
             "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
             "qgemm_run": [vp, vp, vp, i32, vp],
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
+            "qgemm_run_prefill": [vp, vp, vp, i32, vp],
             "qgemm_dequantize": [vp, vp, vp],
             "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
             "qgemm_argmax_workspace_size": [i32, i64, ctypes.POINTER(ctypes.c_size_t)],
@@ -179,6 +181,12 @@ class QGemm:
     def run(self, x, y, R: int | None = None, path: int = PATH_AUTO, stream=None):
         R = x.shape[0] if R is None else R
         _check(lib().qgemm_run_path(self.h, _ptr(x), _ptr(y), R, path, _stream(stream)), "qgemm_run")
+        return y
+
+    def run_prefill(self, x, y, R: int | None = None, stream=None):
+        """Many rows (a prompt chunk with the decode rows): the row-tiled kernel."""
+        R = x.shape[0] if R is None else R
+        _check(lib().qgemm_run_prefill(self.h, _ptr(x), _ptr(y), R, _stream(stream)), "qgemm_run_prefill")
         return y
 
     def dequantize(self, w, stream=None):
