@@ -287,21 +287,24 @@ def prefill_report(seed: int, chunks, copies: int = 2):
         gs = [wsg.QGemm(q, m.N, m.K, max_R=12) for q in pks]
         x = torch.from_numpy(synth.x_bf16(seed, W.X_STREAM[m.K], R_max, m.K).view(np.int16)).to(dev)
         y = torch.empty((R_max, m.N), dtype=torch.float32, device=dev)
-        per.append((m, pks, gs, x, y))
+        # one K-chunk workspace per matrix, sized for the largest need over the row counts
+        ws = torch.empty(max(16, max(gs[0].prefill_workspace_size(R) for R in Rs)), dtype=torch.uint8, device=dev)
+        per.append((m, pks, gs, x, (y, ws)))
     layer_bytes = sum(m.packed_bytes for m in mats)
-    calls = [lambda g=gs[c], x=x, y=y: g.run(x[:12], y[:12], 12) for c in range(copies) for m, pks, gs, x, y in per]
+    calls = [lambda g=gs[c], x=x, y=y: g.run(x[:12], y[0][:12], 12) for c in range(copies) for m, pks, gs, x, y in per]
     base_us = graph_ms(calls) / copies * 1e3
     log(f"[prefill] decode rows alone (R=12, streaming kernel): {base_us:.1f} us per layer")
     out = {}
     for P, R in zip(chunks, Rs):
         rec = {}
         for m, pks, gs, x, y in per:
-            us = graph_ms([lambda g=g, x=x, y=y: g.run_prefill(x[:R], y[:R], R) for g in gs]) / copies * 1e3
+            us = graph_ms([lambda g=g, x=x, y=y: g.run_prefill(x[:R], y[0][:R], R, workspace=y[1])
+                           for g in gs]) / copies * 1e3
             tf = 2 * R * m.N * m.K / us / 1e6
             rec[m.name] = {"us": round(us, 2), "useful_tflop_s": round(tf, 1),
                            "pct_fp16_mfma_peak": round(tf / RF.MFMA_F16_DENSE_TFLOPS * 100, 1),
                            "weight_GB_s": round(m.packed_bytes / us / 1e3, 1)}
-        calls = [lambda g=gs[c], x=x, y=y: g.run_prefill(x[:R], y[:R], R)
+        calls = [lambda g=gs[c], x=x, y=y: g.run_prefill(x[:R], y[0][:R], R, workspace=y[1])
                  for c in range(copies) for m, pks, gs, x, y in per]
         us = graph_ms(calls) / copies * 1e3
         flops = sum(2 * R * m.N * m.K for m in mats)

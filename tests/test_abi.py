@@ -61,7 +61,8 @@ def test_host_validation_codes():
     assert L.qgemm_create(None, vp(4096), 16, 256, 12, 0) == Q.QGEMM_EINVAL
     assert L.qgemm_run(None, vp(4096), vp(4096), 1, None) == Q.QGEMM_EINVAL
     assert L.qgemm_run_path(None, vp(4096), vp(4096), 1, 2, None) == Q.QGEMM_EINVAL
-    assert L.qgemm_run_prefill(None, vp(4096), vp(4096), 100, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_run_prefill(None, vp(4096), vp(4096), 100, None, 0, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_prefill_workspace_size(None, 100, ctypes.byref(sz0 := ctypes.c_size_t())) == Q.QGEMM_EINVAL
     assert L.qgemm_dequantize(None, vp(4096), None) == Q.QGEMM_EINVAL
     assert L.qgemm_query(None, 1, 0, None) == Q.QGEMM_EINVAL
     assert L.qgemm_argmax_rows(vp(4096), -1, 10, vp(4096), None) == Q.QGEMM_ERANGE_R

@@ -34,7 +34,10 @@ def run_prefill(g, x_bits):
 # (N, K, R): one tile; ragged rows and outputs over several tiles; one row; a
 # single output sub-tile; an odd number of blocks (the K loop's last pass is half)
 SHAPES = [(128, 256, 128), (300, 1024, 76), (1000, 2048, 200), (4100, 512, 129), (40, 3072, 524),
-          (256, 1280, 1), (16, 768, 300), (520, 256, 65)]
+          (256, 1280, 1), (16, 768, 300), (520, 256, 65),
+          # few tiles and long K: K cut into chunks (4 of 8 blocks; 8 of 13 with a last of 9;
+          # an odd R x N, so the chunks' partial slices are padded)
+          (300, 8192, 76), (520, 25600, 20), (301, 8192, 75)]
 
 
 @pytest.mark.parametrize("N,K,R", SHAPES)
@@ -91,21 +94,52 @@ def test_prefill_agrees_with_streaming_kernel(orc):
 
 
 def test_prefill_argument_errors():
+    import ctypes
     import torch
-    import weight_streaming_gemm_amd as wsg
     from weight_streaming_gemm_amd import qgemm as Q
-    _, g = G.make(25, 1, 64, 256, max_R=1)
-    x = torch.zeros((4, 256), dtype=torch.int16, device=G.dev())
+    _, g = G.make(25, 1, 64, 8192, max_R=1)
+    x = torch.zeros((4, 8192), dtype=torch.int16, device=G.dev())
     y = torch.zeros((4, 64), dtype=torch.float32, device=G.dev())
     L = Q.lib()
     st = torch.cuda.current_stream().cuda_stream
-    assert L.qgemm_run_prefill(g.h, x.data_ptr(), y.data_ptr(), 0, st) == Q.QGEMM_OK
-    assert L.qgemm_run_prefill(g.h, x.data_ptr(), y.data_ptr(), -1, st) == Q.QGEMM_ERANGE_R
-    assert L.qgemm_run_prefill(g.h, x.data_ptr(), y.data_ptr(), Q.MAX_PREFILL_R + 1, st) == Q.QGEMM_ERANGE_R
-    assert L.qgemm_run_prefill(g.h, x.data_ptr() + 2, y.data_ptr(), 4, st) == Q.QGEMM_EALIGN
-    assert L.qgemm_run_prefill(g.h, None, y.data_ptr(), 4, st) == Q.QGEMM_EINVAL
+    need = g.prefill_workspace_size(4)
+    assert need > 0                                      # one tile, 32 blocks: K in chunks
+    ws = torch.zeros(need, dtype=torch.uint8, device=G.dev())
+    run = lambda xp, R, wsp=ws.data_ptr(), nb=need: L.qgemm_run_prefill(  # noqa: E731
+        g.h, xp, y.data_ptr(), R, wsp, nb, st)
+    assert run(x.data_ptr(), 0) == Q.QGEMM_OK
+    assert run(x.data_ptr(), -1) == Q.QGEMM_ERANGE_R
+    assert run(x.data_ptr(), Q.MAX_PREFILL_R + 1) == Q.QGEMM_ERANGE_R
+    assert run(x.data_ptr() + 2, 4) == Q.QGEMM_EALIGN
+    assert run(None, 4) == Q.QGEMM_EINVAL
+    assert run(x.data_ptr(), 4, None, 0) == Q.QGEMM_EINVAL          # workspace needed
+    assert run(x.data_ptr(), 4, ws.data_ptr(), need - 16) == Q.QGEMM_EINVAL
+    assert run(x.data_ptr(), 4, ws.data_ptr() + 8, need) == Q.QGEMM_EALIGN
+    sz = ctypes.c_size_t()
+    assert L.qgemm_prefill_workspace_size(g.h, Q.MAX_PREFILL_R + 1, ctypes.byref(sz)) == Q.QGEMM_ERANGE_R
+    assert run(x.data_ptr(), 4) == Q.QGEMM_OK
     torch.cuda.synchronize()
-    assert wsg.QGemm is not None
+    assert float(y.abs().max()) == 0.0                   # zero activations, zero outputs
+    g.close()
+
+
+def test_prefill_full_size_down_k_chunks_sampled(orc):
+    """down of one layer (25600 -> 5120) at 12 decode rows + 64 prompt rows: 40
+    output tiles, so K runs in chunks; sampled outputs of every row."""
+    import weight_streaming_gemm_amd as wsg
+    from tests.test_gpu_fullsize import fused_canon, sample_ns, sampled_rows
+    seed = W.SEED_LAYER
+    m = {mm.name: mm for mm in W.layer_mats(0)}["down"]
+    R = 12 + 64
+    _flush(f"prefill full size down N={m.N} K={m.K} R={R}")
+    packed = G.upload_packed(fused_canon(seed, m), m.N, m.K)
+    g = wsg.QGemm(packed, m.N, m.K, max_R=1)
+    assert g.prefill_workspace_size(R) > 0
+    x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+    y = run_prefill(g, x)
+    ns = sample_ns(m.N, 48, 6)
+    ref = orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, x)
+    assert_parity(y[:, ns], ref, "prefill down sampled")
     g.close()
 
 

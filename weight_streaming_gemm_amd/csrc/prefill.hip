@@ -67,7 +67,8 @@ __device__ __forceinline__ float sum8_bf16(u32x4 v, float s) {
 // grid (row tiles of 128, output tiles of 128); 256 threads
 __global__ void __launch_bounds__(256, 1)
 prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_t hdr_bytes,
-               const uint16_t* __restrict__ x, float* __restrict__ y, int R, int N, int NS, int KB) {
+               const uint16_t* __restrict__ x, float* __restrict__ y, int R, int N, int NS, int KB, int kc,
+               int64_t slice) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, nl = lane & 15;
@@ -75,6 +76,11 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   const int m0 = blockIdx.x * (PF_TILES * 16);       // first row of the workgroup
   const int ns0 = (blockIdx.y * 2 + wn) * PF_U;      // first sub-tile of the wave
   const int K = KB * SB_W;
+  // K in gridDim.z chunks of kc blocks: chunk z covers blocks jb .. je - 1 and
+  // writes its partial sums to slice z (R x N, `slice` floats apart) of y; with
+  // one chunk, y itself
+  const int jb = blockIdx.z * kc, je = jb + kc < KB ? jb + kc : KB;
+  y += (int64_t)blockIdx.z * slice;
 
   const __amdgpu_buffer_rsrc_t qr = rsrc(packed, quant_bytes);
   const __amdgpu_buffer_rsrc_t hr = rsrc(packed + quant_bytes, hdr_bytes);
@@ -164,12 +170,12 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   // without copies; block j + 1's loads are in flight during block j ----
   WB wa, wb;
   XB xb;
-  load_w(wa, 0);
-  load_x(xb, 0);
+  load_w(wa, jb);
+  load_x(xb, jb);
   store_x(xb, 0);
   __syncthreads();
-  for (int j = 0; j < KB; j += 2) {
-    const bool more1 = j + 1 < KB, more2 = j + 2 < KB;
+  for (int j = jb; j < je; j += 2) {
+    const bool more1 = j + 1 < je, more2 = j + 2 < je;
     if (more1) { load_w(wb, j + 1); load_x(xb, j + 1); }
     compute(wa, 0);
     if (more1) store_x(xb, 1);
@@ -195,14 +201,46 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   }
 }
 
+// y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order
+__global__ void __launch_bounds__(256)
+prefill_reduce_kernel(const float* __restrict__ part, float* __restrict__ y, int64_t count, int64_t slice, int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float s = part[i];
+  for (int z = 1; z < S; ++z) s += part[z * slice + i];
+  y[i] = s;
+}
+
+PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus) {
+  PrefillPlan p{};
+  const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
+  p.mt = (R + PF_TILES * 16 - 1) / (PF_TILES * 16);
+  p.nt = (NS + 2 * PF_U - 1) / (2 * PF_U);
+  // chunks of K while the grid is below the CU count, at least 8 blocks a chunk
+  int64_t S = 1;
+  while (p.mt * p.nt * S * 2 <= cus && KB / (S * 2) >= 8) S *= 2;
+  p.kc = (KB + S - 1) / S;
+  p.S = (KB + p.kc - 1) / p.kc;
+  // partial slices of R x N fp32, each rounded up to 16 bytes
+  p.slice = ((int64_t)R * N + 3) / 4 * 4;
+  p.ws_bytes = p.S > 1 ? (size_t)p.S * (size_t)p.slice * 4 : 0;
+  return p;
+}
+
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,
-                          hipStream_t st) {
+                          const PrefillPlan& p, void* ws, hipStream_t st) {
   const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
   const uint32_t qb = (uint32_t)quant_region_bytes(N, K);
   const uint32_t hb = (uint32_t)(packed_bytes(N, K) - quant_region_bytes(N, K));
-  const dim3 grid((unsigned)((R + PF_TILES * 16 - 1) / (PF_TILES * 16)), (unsigned)((NS + 2 * PF_U - 1) / (2 * PF_U)));
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, packed, qb, hb, reinterpret_cast<const uint16_t*>(x), y,
-                     R, (int)N, (int)NS, (int)KB);
+  const dim3 grid((unsigned)p.mt, (unsigned)p.nt, (unsigned)p.S);
+  float* out = p.S > 1 ? reinterpret_cast<float*>(ws) : y;
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, packed, qb, hb, reinterpret_cast<const uint16_t*>(x),
+                     out, R, (int)N, (int)NS, (int)KB, (int)p.kc, p.S > 1 ? p.slice : (int64_t)0);
+  if (p.S > 1) {
+    const int64_t count = (int64_t)R * N;
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, out, y, count,
+                       p.slice, (int)p.S);
+  }
   return hipGetLastError();
 }
 

@@ -324,14 +324,28 @@ int qgemm_run(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
   return qgemm_run_path(h, x_bf16, y, R, QGEMM_PATH_AUTO, stream);
 }
 
-int qgemm_run_prefill(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
+int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t* bytes) {
+  if (!valid_handle(h) || !bytes) return QGEMM_EINVAL;
+  if (R < 0 || R > QGEMM_MAX_PREFILL_R) return QGEMM_ERANGE_R;
+  *bytes = R == 0 ? 0 : prefill_plan(h->N, h->K, R, h->cus).ws_bytes;
+  return QGEMM_OK;
+}
+
+int qgemm_run_prefill(qgemm_t h, const void* x_bf16, float* y, int R, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (!valid_handle(h)) return QGEMM_EINVAL;
   if (R < 0 || R > QGEMM_MAX_PREFILL_R) return QGEMM_ERANGE_R;
   if ((int64_t)R * h->K * 2 >= (int64_t(1) << 31)) return QGEMM_ERANGE_R;   // x is addressed with 32-bit offsets
   if (R == 0) return QGEMM_OK;
   if (!x_bf16 || !y) return QGEMM_EINVAL;
   if (!aligned16(x_bf16) || !aligned16(y)) return QGEMM_EALIGN;
-  return launch_prefill(h->packed, h->N, h->K, x_bf16, y, R, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+  const PrefillPlan p = prefill_plan(h->N, h->K, R, h->cus);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return QGEMM_EINVAL;
+    if (!aligned16(workspace)) return QGEMM_EALIGN;
+  }
+  return launch_prefill(h->packed, h->N, h->K, x_bf16, y, R, p, workspace, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? QGEMM_OK
              : QGEMM_EHIP;
 }

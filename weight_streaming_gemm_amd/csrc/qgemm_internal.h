@@ -91,9 +91,17 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
 hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
-// rows tiled as well as outputs (prefill.hip): x [R x K] bf16, y [R x N] fp32, any R
+// rows tiled as well as outputs (prefill.hip): x [R x K] bf16, y [R x N] fp32, any R.
+// Grid: mt row tiles x nt output tiles x S chunks of K (kc blocks each); with
+// S > 1 the chunks' partial outputs go to a workspace of ws_bytes and a second
+// kernel adds them in chunk order.
+struct PrefillPlan {
+  int64_t mt, nt, S, kc, slice;
+  size_t ws_bytes;
+};
+PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus);
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,
-                          hipStream_t st);
+                          const PrefillPlan& p, void* ws, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_argmax(const float* y, int R, int64_t N, int32_t* idx, hipStream_t st);
 // Row argmax over column chunks with a workspace of argmax_ws_bytes(R, N) bytes

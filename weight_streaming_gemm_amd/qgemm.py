@@ -23,6 +23,7 @@ MAX_PREFILL_R = 8192
 # every symbol include/qgemm.h declares
 EXPORTS = (
     "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path", "qgemm_run_prefill",
+    "qgemm_prefill_workspace_size",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_argmax_workspace_size", "qgemm_argmax_rows_ws",
     "qgemm_verify_greedy", "qgemm_attention_workspace_size", "qgemm_decode_attention", "qgemm_query",
     "qgemm_destroy",
@@ -63,7 +64,8 @@ def lib():
             "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
             "qgemm_run": [vp, vp, vp, i32, vp],
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
-            "qgemm_run_prefill": [vp, vp, vp, i32, vp],
+            "qgemm_run_prefill": [vp, vp, vp, i32, vp, ctypes.c_size_t, vp],
+            "qgemm_prefill_workspace_size": [vp, i32, ctypes.POINTER(ctypes.c_size_t)],
             "qgemm_dequantize": [vp, vp, vp],
             "qgemm_argmax_rows": [vp, i32, i64, vp, vp],
             "qgemm_argmax_workspace_size": [i32, i64, ctypes.POINTER(ctypes.c_size_t)],
@@ -183,10 +185,23 @@ class QGemm:
         _check(lib().qgemm_run_path(self.h, _ptr(x), _ptr(y), R, path, _stream(stream)), "qgemm_run")
         return y
 
-    def run_prefill(self, x, y, R: int | None = None, stream=None):
-        """Many rows (a prompt chunk with the decode rows): the row-tiled kernel."""
+    def prefill_workspace_size(self, R: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().qgemm_prefill_workspace_size(self.h, R, ctypes.byref(n)), "qgemm_prefill_workspace_size")
+        return n.value
+
+    def run_prefill(self, x, y, R: int | None = None, workspace=None, stream=None):
+        """Many rows (a prompt chunk with the decode rows): the row-tiled kernel.
+        workspace: a device buffer of at least prefill_workspace_size(R) bytes
+        (torch allocates one here when none is given and one is needed)."""
         R = x.shape[0] if R is None else R
-        _check(lib().qgemm_run_prefill(self.h, _ptr(x), _ptr(y), R, _stream(stream)), "qgemm_run_prefill")
+        need = self.prefill_workspace_size(R)
+        if need and workspace is None:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().qgemm_run_prefill(self.h, _ptr(x), _ptr(y), R, _ptr(workspace), nbytes, _stream(stream)),
+               "qgemm_run_prefill")
         return y
 
     def dequantize(self, w, stream=None):
