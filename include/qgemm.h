@@ -139,17 +139,18 @@ int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, voi
  * hundreds of rows).  Same operands and result as qgemm_run: x device bf16
  * [R x K], y device fp32 [R x N] (overwritten), both row-major and 16-byte
  * aligned; the same arithmetic per 256-weight block (exact binary16 products
- * of sc*q with x, fp32 sums, then d and the min term).  When the row and
- * output tiles are fewer than the GPU's compute units, K is cut into chunks
- * whose partial outputs go to `workspace` (device, caller-owned, 16-byte
- * aligned, at least the size qgemm_prefill_workspace_size gives; may be null
- * when that size is 0) and a second kernel adds them in chunk order, so the
+ * of sc*q with x, fp32 sums, then d and the min term).  `workspace` (device,
+ * caller-owned, 16-byte aligned, at least qgemm_prefill_workspace_size bytes)
+ * receives x converted once into the kernel's LDS image (binary16 operands and
+ * sub-block sums per 128-row tile and block, 1.125x the padded x in bytes)
+ * and, when the row and output tiles are fewer than the GPU's compute units,
+ * the partial outputs of K chunks, which a last kernel adds in chunk order: the
  * result is the same bits on every run.  Does not use the handle's workspace
  * or max_R: calls with their own workspaces may run on several streams at once.
- * Enqueues one kernel (two with K chunks) on `stream`; R = 0 is a no-op.
+ * Enqueues two kernels (three with K chunks) on `stream`; R = 0 is a no-op.
  * Errors: QGEMM_EINVAL (bad handle, null x or y, workspace missing or too
- * small), QGEMM_EALIGN, QGEMM_ERANGE_R (R < 0, R > QGEMM_MAX_PREFILL_R, or
- * R*K*2 >= 2^31), QGEMM_EHIP. */
+ * small), QGEMM_EALIGN, QGEMM_ERANGE_R (R < 0, R > QGEMM_MAX_PREFILL_R,
+ * R*K*2 >= 2^31, or an activation image of 2 GiB or more), QGEMM_EHIP. */
 #define QGEMM_MAX_PREFILL_R 8192
 int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t *bytes);
 int qgemm_run_prefill(qgemm_t h, const void *x_bf16, float *y, int R, void *workspace,

@@ -17,10 +17,13 @@
 // Work: one workgroup of 4 waves per (128-row tile, 128-output tile), over the
 // whole of K (no split, so every output is written once, in a fixed order).
 // Waves form a 2 x 2 grid; a wave owns 64 rows (4 row tiles of 16) x 64 outputs
-// (4 sub-tiles of 16): 16 accumulator tiles.  Per block the workgroup stages
-// its 128 rows of x as binary16 operands (and the 8 sub-block sums per row) in
-// LDS, double-buffered: the next block's activations and weights are in flight
-// while the current block is multiplied.
+// (4 sub-tiles of 16): 16 accumulator tiles.  A first kernel converts x once
+// into the LDS image of every (128-row tile, block): binary16 operands in the
+// matrix-core lane layout plus the 8 sub-block sums per row (72 KiB).  The main
+// kernel copies each block's image straight into LDS with buffer loads that
+// write LDS directly (no registers, no vector instructions), double-buffered:
+// the next block's activations and weights are in flight while the current
+// block is multiplied.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,15 +70,14 @@ __device__ __forceinline__ float sum8_bf16(u32x4 v, float s) {
 // grid (row tiles of 128, output tiles of 128); 256 threads
 __global__ void __launch_bounds__(256, 1)
 prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_t hdr_bytes,
-               const uint16_t* __restrict__ x, float* __restrict__ y, int R, int N, int NS, int KB, int kc,
-               int64_t slice) {
+               const uint8_t* __restrict__ ximg, uint32_t img_bytes, float* __restrict__ y, int R, int N, int NS,
+               int KB, int kc, int64_t slice) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, nl = lane & 15;
   const int wm = w & 1, wn = w >> 1;                 // the wave's place in the 2 x 2 grid
   const int m0 = blockIdx.x * (PF_TILES * 16);       // first row of the workgroup
   const int ns0 = (blockIdx.y * 2 + wn) * PF_U;      // first sub-tile of the wave
-  const int K = KB * SB_W;
   // K in gridDim.z chunks of kc blocks: chunk z covers blocks jb .. je - 1 and
   // writes its partial sums to slice z (R x N, `slice` floats apart) of y; with
   // one chunk, y itself
@@ -84,7 +86,6 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
 
   const __amdgpu_buffer_rsrc_t qr = rsrc(packed, quant_bytes);
   const __amdgpu_buffer_rsrc_t hr = rsrc(packed + quant_bytes, hdr_bytes);
-  const __amdgpu_buffer_rsrc_t xr = rsrc(x, (uint32_t)R * (uint32_t)K * 2u);
   constexpr uint32_t OOB = 0x80000000u;
 
   // ---- weights of block j for the wave's sub-tiles (past N: no traffic, zeros) ----
@@ -101,33 +102,17 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
     }
   };
 
-  // ---- activations of block j: thread (wave w, lane 16 g + r) converts, for row
-  // tiles w and w + 4, row 16 rt + r's 64 values of sub-blocks 2g and 2g + 1
-  // (one 128-byte line) into the 8 operands of lane 16 g + r, and the two sums.
-  // Rows past R load nothing and stage zeros. ---
-  struct XB { u32x4 v[2][8]; };
-  auto load_x = [&](XB& b, int j) __attribute__((always_inline)) {
-    for (int i = 0; i < 2; ++i) {
-      const int row = m0 + (w + 4 * i) * 16 + nl;
-      const uint32_t base = row < R ? (uint32_t)((row * K + j * SB_W + 64 * g4) * 2) : OOB;
-      for (int c = 0; c < 8; ++c) b.v[i][c] = load16<0>(xr, base == OOB ? OOB : base + 16 * c);
-    }
-  };
-  auto store_x = [&](const XB& b, int buf) __attribute__((always_inline)) {
-    uint8_t* const X = lds + buf * PF_BUF;
-    for (int i = 0; i < 2; ++i) {
-      const int rt = w + 4 * i;
-      // b.v[i][c] holds k = 64 g + 8 c .. 8 c + 7: c < 4 sub-block 2g, c >= 4 sub-block 2g + 1
-      for (int t = 0; t < 8; ++t) {
-        const u32x4 lo = b.v[i][t >> 1], hi = b.v[i][4 + (t >> 1)];
-        const int o = (t & 1) * 2;       // dwords of k = 4 t .. 4 t + 3 within the 8-value load
-        const f16x8 op = build_a(lo[o], lo[o + 1], hi[o], hi[o + 1]);
-        *reinterpret_cast<f16x8*>(X + (rt * 8 + t) * PF_CHUNK + lane * 16) = op;
-      }
-      float s0 = 0.f, s1 = 0.f;
-      for (int c = 0; c < 4; ++c) s0 = sum8_bf16(b.v[i][c], s0);
-      for (int c = 4; c < 8; ++c) s1 = sum8_bf16(b.v[i][c], s1);
-      *reinterpret_cast<f16x8*>(X + PF_X + rt * PF_CHUNK + lane * 16) = build_s(s0, s1);
+  // ---- activations of block j: its 72 one-KiB chunks of the image, 18 per wave,
+  // copied into LDS buffer `buf` by buffer loads that write LDS (lane l's 16
+  // bytes land at the chunk's base + 16 l) ----
+  const __amdgpu_buffer_rsrc_t ir = rsrc(ximg, img_bytes);
+  auto stage_x = [&](int j, int buf) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(blockIdx.x * KB + j) * (uint32_t)PF_BUF;
+    for (int i = 0; i < PF_BUF / PF_CHUNK / 4; ++i) {
+      const int c = w * (PF_BUF / PF_CHUNK / 4) + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ir, (__attribute__((address_space(3))) void*)(lds + buf * PF_BUF + c * PF_CHUNK), 16,
+          base + (uint32_t)(c * PF_CHUNK + lane * 16), 0, 0, 0);
     }
   };
 
@@ -169,21 +154,17 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   // ---- the K loop, two blocks per pass so that the register buffers alternate
   // without copies; block j + 1's loads are in flight during block j ----
   WB wa, wb;
-  XB xb;
+  stage_x(jb, 0);
   load_w(wa, jb);
-  load_x(xb, jb);
-  store_x(xb, 0);
   __syncthreads();
   for (int j = jb; j < je; j += 2) {
     const bool more1 = j + 1 < je, more2 = j + 2 < je;
-    if (more1) { load_w(wb, j + 1); load_x(xb, j + 1); }
+    if (more1) { stage_x(j + 1, 1); load_w(wb, j + 1); }
     compute(wa, 0);
-    if (more1) store_x(xb, 1);
     __syncthreads();
     if (!more1) break;
-    if (more2) { load_w(wa, j + 2); load_x(xb, j + 2); }
+    if (more2) { stage_x(j + 2, 0); load_w(wa, j + 2); }
     compute(wb, 1);
-    if (more2) store_x(xb, 0);
     __syncthreads();
   }
 
@@ -199,6 +180,43 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
         if (row < R) yg[(int64_t)row * N + n] = acc[rt][u][i];
       }
   }
+}
+
+// The LDS image of x: for 128-row tile m and block j, at (m KB + j) * 72 KiB,
+// chunk (row tile rt, step t) at 1 KiB (8 rt + t) holds lane 16 g + r's binary16
+// A operand of row 128 m + 16 rt + r (k = 256 j + 64 g + 32 (e & 1) + 4 t + (e >> 1)
+// for element e), and chunk 64 + rt the sub-block sums of those rows (two per
+// lane group, as binary16 head and tail).  Rows past R are zeros.  One thread per
+// (m, j, rt, lane): it reads the row's 64 values of sub-blocks 2g, 2g + 1 (one
+// 128-byte line) and writes 8 operands and one sum entry.
+__global__ void __launch_bounds__(256)
+prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, int R, int KB, int64_t total) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= total) return;
+  const int lane = (int)(id & 63), g = lane >> 4, r = lane & 15;
+  const int64_t q = id >> 6;                       // (m KB + j) * 8 + rt
+  const int rt = (int)(q & 7);
+  const int64_t mj = q >> 3;
+  const int64_t m = mj / KB, j = mj - m * KB;
+  const int64_t row = m * (PF_TILES * 16) + rt * 16 + r;
+  u32x4 v[8];
+  if (row < R) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + row * (int64_t)KB * SB_W + j * SB_W + 64 * g);
+    for (int c = 0; c < 8; ++c) v[c] = src[c];
+  } else {
+    for (int c = 0; c < 8; ++c) v[c] = u32x4{0u, 0u, 0u, 0u};
+  }
+  uint8_t* const dst = img + mj * PF_BUF;
+  // v[c] holds k = 64 g + 8 c .. 8 c + 7: c < 4 sub-block 2g, c >= 4 sub-block 2g + 1
+  for (int t = 0; t < 8; ++t) {
+    const u32x4 lo = v[t >> 1], hi = v[4 + (t >> 1)];
+    const int o = (t & 1) * 2;                     // dwords of k = 4 t .. 4 t + 3 within the 8-value load
+    *reinterpret_cast<f16x8*>(dst + (rt * 8 + t) * PF_CHUNK + lane * 16) = build_a(lo[o], lo[o + 1], hi[o], hi[o + 1]);
+  }
+  float s0 = 0.f, s1 = 0.f;
+  for (int c = 0; c < 4; ++c) s0 = sum8_bf16(v[c], s0);
+  for (int c = 4; c < 8; ++c) s1 = sum8_bf16(v[c], s1);
+  *reinterpret_cast<f16x8*>(dst + PF_X + rt * PF_CHUNK + lane * 16) = build_s(s0, s1);
 }
 
 // y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order
@@ -221,9 +239,11 @@ PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus) {
   while (p.mt * p.nt * S * 2 <= cus && KB / (S * 2) >= 8) S *= 2;
   p.kc = (KB + S - 1) / S;
   p.S = (KB + p.kc - 1) / p.kc;
-  // partial slices of R x N fp32, each rounded up to 16 bytes
+  // the activations' LDS image, then (with K chunks) the partial slices of R x N
+  // fp32, each rounded up to 16 bytes
+  p.img_bytes = (size_t)p.mt * (size_t)KB * PF_BUF;
   p.slice = ((int64_t)R * N + 3) / 4 * 4;
-  p.ws_bytes = p.S > 1 ? (size_t)p.S * (size_t)p.slice * 4 : 0;
+  p.ws_bytes = p.img_bytes + (p.S > 1 ? (size_t)p.S * (size_t)p.slice * 4 : 0);
   return p;
 }
 
@@ -232,10 +252,14 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const voi
   const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
   const uint32_t qb = (uint32_t)quant_region_bytes(N, K);
   const uint32_t hb = (uint32_t)(packed_bytes(N, K) - quant_region_bytes(N, K));
+  uint8_t* const img = reinterpret_cast<uint8_t*>(ws);
+  const int64_t total = p.mt * KB * 8 * 64;
+  hipLaunchKernelGGL(prefill_image_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(x), img, R, (int)KB, total);
   const dim3 grid((unsigned)p.mt, (unsigned)p.nt, (unsigned)p.S);
-  float* out = p.S > 1 ? reinterpret_cast<float*>(ws) : y;
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, packed, qb, hb, reinterpret_cast<const uint16_t*>(x),
-                     out, R, (int)N, (int)NS, (int)KB, (int)p.kc, p.S > 1 ? p.slice : (int64_t)0);
+  float* out = p.S > 1 ? reinterpret_cast<float*>(img + p.img_bytes) : y;
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, packed, qb, hb, img, (uint32_t)p.img_bytes, out, R,
+                     (int)N, (int)NS, (int)KB, (int)p.kc, p.S > 1 ? p.slice : (int64_t)0);
   if (p.S > 1) {
     const int64_t count = (int64_t)R * N;
     hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, out, y, count,

@@ -327,7 +327,13 @@ int qgemm_run(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
 int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t* bytes) {
   if (!valid_handle(h) || !bytes) return QGEMM_EINVAL;
   if (R < 0 || R > QGEMM_MAX_PREFILL_R) return QGEMM_ERANGE_R;
-  *bytes = R == 0 ? 0 : prefill_plan(h->N, h->K, R, h->cus).ws_bytes;
+  if (R == 0) {
+    *bytes = 0;
+    return QGEMM_OK;
+  }
+  const PrefillPlan p = prefill_plan(h->N, h->K, R, h->cus);
+  if (p.img_bytes >= (size_t(1) << 31)) return QGEMM_ERANGE_R;
+  *bytes = p.ws_bytes;
   return QGEMM_OK;
 }
 
@@ -340,10 +346,9 @@ int qgemm_run_prefill(qgemm_t h, const void* x_bf16, float* y, int R, void* work
   if (!x_bf16 || !y) return QGEMM_EINVAL;
   if (!aligned16(x_bf16) || !aligned16(y)) return QGEMM_EALIGN;
   const PrefillPlan p = prefill_plan(h->N, h->K, R, h->cus);
-  if (p.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < p.ws_bytes) return QGEMM_EINVAL;
-    if (!aligned16(workspace)) return QGEMM_EALIGN;
-  }
+  if (p.img_bytes >= (size_t(1) << 31)) return QGEMM_ERANGE_R;     // the image is addressed with 32-bit offsets
+  if (!workspace || workspace_bytes < p.ws_bytes) return QGEMM_EINVAL;
+  if (!aligned16(workspace)) return QGEMM_EALIGN;
   return launch_prefill(h->packed, h->N, h->K, x_bf16, y, R, p, workspace, reinterpret_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? QGEMM_OK

@@ -92,12 +92,13 @@ hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 // rows tiled as well as outputs (prefill.hip): x [R x K] bf16, y [R x N] fp32, any R.
-// Grid: mt row tiles x nt output tiles x S chunks of K (kc blocks each); with
-// S > 1 the chunks' partial outputs go to a workspace of ws_bytes and a second
-// kernel adds them in chunk order.
+// Grid: mt row tiles x nt output tiles x S chunks of K (kc blocks each).  The
+// workspace (ws_bytes) holds the activations' LDS image (img_bytes, written by a
+// first kernel) and, with S > 1, the chunks' partial outputs, which a last
+// kernel adds in chunk order.
 struct PrefillPlan {
   int64_t mt, nt, S, kc, slice;
-  size_t ws_bytes;
+  size_t img_bytes, ws_bytes;
 };
 PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus);
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,

@@ -193,7 +193,7 @@ class QGemm:
     def run_prefill(self, x, y, R: int | None = None, workspace=None, stream=None):
         """Many rows (a prompt chunk with the decode rows): the row-tiled kernel.
         workspace: a device buffer of at least prefill_workspace_size(R) bytes
-        (torch allocates one here when none is given and one is needed)."""
+        (torch allocates one here when none is given)."""
         R = x.shape[0] if R is None else R
         need = self.prefill_workspace_size(R)
         if need and workspace is None:
