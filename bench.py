@@ -432,8 +432,13 @@ def attention_report(seed: int, reps: int = 20):
                              "sample": f"agent 0 ({lengths[0]} positions), fp64 numpy, {cpu_s:.2f}s"}}
 
 
+# the sources the streaming kernel and its launches are built from (the decode
+# attention and the row-tiled prompt kernel live in files of their own)
+STREAM_SOURCES = ("layout.h", "operand.h", "qgemm_api.cpp", "qgemm_internal.h", "qgemm_kernels.hip", "stream_sched.h")
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP library's sources with comments and blank space
+    """sha256 over the streaming kernel's sources with comments and blank space
     removed: identifies the code a counter run measured (a comment edit does
     not make the counters stale; any code change does)."""
     import hashlib
@@ -441,7 +446,7 @@ def kernel_source_digest() -> str:
     csrc = os.path.join(ROOT, "weight_streaming_gemm_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name in STREAM_SOURCES:
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 text = f.read()
             text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # the sources hold no "//" or "/*" in literals
@@ -519,7 +524,8 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib:
         "kernel": "stream_kernel (all variants of the pass)",
         "R": R,
         "kernel_source_sha256": kernel_source_digest(),
-        "digest": "sha256 of the csrc sources with comments and blank space removed (bench.kernel_source_digest)",
+        "digest": "sha256 of the streaming kernel's csrc sources with comments and blank space removed "
+                  "(bench.kernel_source_digest)",
         "fetch_bytes_per_launch": int(round(fetch_b)),
         "write_bytes_per_launch": int(round(write_b)),
         "bytes_per_launch": int(round(fetch_b + write_b)),
