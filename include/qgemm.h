@@ -134,7 +134,7 @@ int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, voi
  * section on what the design buys: another agent's long prefill runs while the
  * others decode, so a chunk of prompt rows and the agents' decode rows go
  * through the same weights): y = x . W^T for R rows, 0 <= R <= QGEMM_MAX_PREFILL_R,
- * with a kernel that tiles rows as well as outputs (128 x 128 per workgroup,
+ * with a kernel that tiles rows as well as outputs (128 rows x 128 or 192 per workgroup,
  * every weight read serving a 128-row tile; bound by the matrix cores at
  * hundreds of rows).  Same operands and result as qgemm_run: x device bf16
  * [R x K], y device fp32 [R x N] (overwritten), both row-major and 16-byte
