@@ -227,15 +227,21 @@ def layer_report(seed: int, edge: int, Rs, copies: int):
     out = {}
     for R in Rs:
         rec = {}
-        for pname, path in (("mfma", Q.PATH_MFMA), ("valu", Q.PATH_VALU)):
+        for pname, path in (("mfma", Q.PATH_MFMA), ("valu", Q.PATH_VALU), ("auto", Q.PATH_AUTO)):
             if path == Q.PATH_VALU and R > 4:
                 continue
+            if path == Q.PATH_AUTO and R < Q.TILED_MIN_R:
+                continue          # the automatic choice is the streaming kernel here
+            if path == Q.PATH_AUTO:
+                log(f"[layer] R={R} automatic choice: " +
+                    ", ".join(f"{m.name} {'tiled' if gs[0].query(R)['path'] == Q.PATH_TILED else 'streaming'}"
+                              for m, pks, gs, x, y in per))
             prec = {}
             for m, pks, gs, x, y in per:
                 us = graph_ms([lambda g=g, x=x, y=y: g.run(x[:R], y[:R], R, path=path) for g in gs]) / copies * 1e3
                 prec[m.name] = {"us": round(us, 2), "GB_s": round(m.packed_bytes / us / 1e3, 1),
                                 "pct_hbm_peak": round(m.packed_bytes / us / 1e3 / RF.HBM_PEAK_GBS * 100, 1)}
-                if pname == "mfma":
+                if pname != "valu":
                     prec[m.name]["useful_tflop_s"] = round(2 * R * m.N * m.K / us / 1e6, 1)
             calls = []
             for c in range(copies):
@@ -244,7 +250,7 @@ def layer_report(seed: int, edge: int, Rs, copies: int):
             us = graph_ms(calls) / copies * 1e3
             prec["layer"] = {"us": round(us, 2), "GB_s": round(layer_bytes / us / 1e3, 1),
                              "pct_hbm_peak": round(layer_bytes / us / 1e3 / RF.HBM_PEAK_GBS * 100, 1)}
-            if pname == "mfma":
+            if pname != "valu":
                 flops = sum(2 * R * m.N * m.K for m in mats)
                 prec["layer"]["useful_tflop_s"] = round(flops / us / 1e6, 1)
                 prec["layer"]["pct_fp16_mfma_peak"] = round(flops / us / 1e6 / RF.MFMA_F16_DENSE_TFLOPS * 100, 2)

@@ -66,8 +66,16 @@ typedef enum {
 typedef enum {
     QGEMM_PATH_AUTO = 0,  /* the library's choice for (R, N, K) */
     QGEMM_PATH_VALU = 1,  /* vector-ALU bandwidth path (small R only) */
-    QGEMM_PATH_MFMA = 2   /* matrix-core path (any R) */
+    QGEMM_PATH_MFMA = 2,  /* matrix-core streaming path (any R) */
+    QGEMM_PATH_TILED = 3  /* row-tiled matrix-core path (the kernel of
+                             qgemm_run_prefill, with the handle's workspace):
+                             handles created with max_R >= QGEMM_TILED_MIN_R */
 } qgemm_path;
+
+/* The automatic choice takes the row-tiled path from this many rows on for
+ * matrices of at least 2^26 weights, and at QGEMM_MAX_R rows for all (the
+ * measured crossover against the streaming kernel on one MI355X). */
+#define QGEMM_TILED_MIN_R 48
 
 typedef struct qgemm_handle *qgemm_t;
 typedef struct qgemm_seq *qgemm_seq_t;
@@ -77,7 +85,9 @@ typedef struct qgemm_seq *qgemm_seq_t;
  * the `steps` = tiles * K/256 (tile, block) steps into `ranges` equal
  * contiguous ranges and deals them round-robin to `workgroups` workgroups. */
 typedef struct {
-    int path;               /* QGEMM_PATH_VALU or QGEMM_PATH_MFMA */
+    int path;               /* QGEMM_PATH_VALU, QGEMM_PATH_MFMA or QGEMM_PATH_TILED
+                               (for the row-tiled path only path, tiles (output tiles),
+                               workgroups, kernels, k_chunks and workspace_bytes are set) */
     int row_tiles;          /* 16-row tiles on the matrix-core path (0 on the VALU path) */
     int subtiles_per_wave;  /* 16-output sub-tiles per wave */
     int64_t tiles;          /* output tiles */
@@ -110,7 +120,8 @@ int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, vo
 /* Create a handle over packed weights.  The handle BORROWS packed_dev (it must
  * stay valid and unchanged until qgemm_destroy) and OWNS a device workspace
  * sized for up to max_R rows (partial output tiles and per-tile arrival
- * counters).  flags
+ * counters; with max_R >= QGEMM_TILED_MIN_R also the row-tiled path's
+ * activation image and K-chunk partials).  flags
  * must be 0.  Synchronous.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_ERANGE_R,
  * QGEMM_ENOMEM, QGEMM_EHIP. */
@@ -119,15 +130,18 @@ int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int
 
 /* y = x . W^T for R rows on `stream`, with the R-dependent kernel choice.
  * x: device bf16 [R x K], y: device fp32 [R x N], both 16-byte aligned.
- * Enqueues exactly one kernel, which reads every packed weight byte once,
- * converts x itself and writes y.  R = 0 is a no-op.  Runs of one handle share
- * its workspace: do not run one handle on two streams at once.
+ * On the streaming paths enqueues exactly one kernel, which reads every packed
+ * weight byte once, converts x itself and writes y; on the row-tiled path
+ * (large R, see QGEMM_TILED_MIN_R) two or three kernels (activation image,
+ * product, and the sum of K chunks).  R = 0 is a no-op.  Runs of one handle
+ * share its workspace: do not run one handle on two streams at once.
  * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_EHIP. */
 int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
 
 /* As qgemm_run with an explicit path (QGEMM_PATH_AUTO = qgemm_run).
  * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not
- * serve (R > 4). */
+ * serve (R > 4), or the row-tiled path of a handle created with
+ * max_R < QGEMM_TILED_MIN_R. */
 int qgemm_run_path(qgemm_t h, const void *x_bf16, float *y, int R, int path, void *stream);
 
 /* Prompt-chunk rows sharing the weight pass (OpenJet multi-agent serving page,

@@ -119,22 +119,46 @@ def test_gemm_small_workload_all_R(orc, small, R):
                                    (33, 256, 1), (4000, 2048, 48), (4100, 512, 12), (8200, 256, 1),
                                    (600, 5120, 64), (1000, 8192, 24), (16390, 2048, 48), (16384, 2048, 64)])
 def test_gemm_ragged_and_split(orc, N, K, R):
+    from weight_streaming_gemm_amd import qgemm as Q
     _flush(f"gemm N={N} K={K} R={R}")
     canon, g = G.make(1, 5, N, K, max_R=R)
     info = g.query(R)
     x = synth.x_bf16(1, 6, R, K, outlier_p=0.01)
-    y = G.run(g, x)
-    assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} wgs={info['workgroups']}")
+    ref = orc.gemm(canon, N, K, x)
+    assert_parity(G.run(g, x), ref, f"N={N} K={K} R={R} path={info['path']} wgs={info['workgroups']}")
+    if info["path"] != Q.PATH_MFMA:     # the automatic choice took the row-tiled kernel: the streaming one too
+        assert_parity(G.run(g, x, path=Q.PATH_MFMA), ref, f"N={N} K={K} R={R} streaming")
     g.close()
+
+
+def test_automatic_choice_of_the_row_tiled_kernel(orc):
+    """From 48 rows on, matrices of at least 2^26 weights take the row-tiled
+    kernel, and every matrix does at 64 rows; below, or on handles made for
+    fewer rows, the streaming kernel; an explicit request needs max_R >= 48."""
+    from weight_streaming_gemm_amd import qgemm as Q
+    _, big = G.make(1, 9, 32768, 2048, max_R=48)          # 2^26 weights
+    assert big.query(24)["path"] == Q.PATH_MFMA
+    assert big.query(48)["path"] == Q.PATH_TILED
+    assert big.query(48)["kernels"] in (2, 3)
+    big.close()
+    _, small = G.make(1, 9, 1000, 2048, max_R=64)
+    assert small.query(48)["path"] == Q.PATH_MFMA
+    assert small.query(64)["path"] == Q.PATH_TILED
+    assert small.query(12, Q.PATH_TILED)["path"] == Q.PATH_TILED
+    small.close()
+    canon, few = G.make(1, 9, 1000, 2048, max_R=12)
+    assert Q.lib().qgemm_query(few.h, 12, Q.PATH_TILED, ctypes.byref(Q.Info())) == Q.QGEMM_EPATH
+    few.close()
 
 
 def test_plan_kinds_are_exercised():
     """The shapes above reach every kind of plan: whole-tile ranges, stream-K
     ranges, and K in chunks (activations of a tile row larger than LDS)."""
     info = {}
+    from weight_streaming_gemm_amd import qgemm as Q
     for N, K, R in [(4100, 512, 12), (40, 8192, 12), (16390, 2048, 48), (16384, 2048, 64)]:
         _, g = G.make(1, 5, N, K, max_R=R)
-        info[(N, K, R)] = g.query(R)
+        info[(N, K, R)] = g.query(R, Q.PATH_MFMA)
         g.close()
     assert info[(4100, 512, 12)]["whole_tile_ranges"] == 1 and info[(4100, 512, 12)]["k_chunks"] == 1
     assert info[(40, 8192, 12)]["whole_tile_ranges"] == 0

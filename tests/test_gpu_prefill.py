@@ -38,8 +38,10 @@ SHAPES = [(128, 256, 128), (300, 1024, 76), (1000, 2048, 200), (4100, 512, 129),
           # few tiles and long K: K cut into chunks (4 of 8 blocks; 8 of 13 with a last of 9;
           # an odd R x N, so the chunks' partial slices are padded)
           (300, 8192, 76), (520, 25600, 20), (301, 8192, 75),
-          # many row and output tiles: the 12-wave kernel (192-output tiles) is taken
-          (4100, 512, 2060)]
+          # many row and output tiles: the 12-wave grid (192-output tiles) is taken
+          (4100, 512, 2060),
+          # few rows, many outputs: the 64-row grid (1 x 8 waves, 256-output tiles) is taken
+          (40000, 256, 40)]
 
 
 @pytest.mark.parametrize("N,K,R", SHAPES)

@@ -40,11 +40,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int PF_RT = 4;                       // row tiles per wave
 constexpr int PF_U = 2;                        // output sub-tiles per wave
-constexpr int PF_TILES = 2 * PF_RT;            // row tiles per workgroup (128 rows)
 constexpr int PF_CHUNK = 64 * 16;              // one (row tile, step) operand chunk: 64 lanes x 16 B
-constexpr int PF_X = PF_TILES * 8 * PF_CHUNK;  // activations of one block: 64 KiB
-constexpr int PF_S = PF_TILES * PF_CHUNK;      // their sub-block sums: 8 KiB
-constexpr int PF_BUF = PF_X + PF_S;
+// LDS image of one block for MT row tiles: MT x 8 operand chunks, then MT chunks of sums
+__host__ __device__ constexpr int pf_buf(int MT) { return 9 * MT * PF_CHUNK; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
@@ -68,19 +66,20 @@ __device__ __forceinline__ float sum8_bf16(u32x4 v, float s) {
 
 }  // namespace
 
-// grid (row tiles of 128, output tiles of 32 WN, K chunks); 2 x WN waves:
-// two along the rows, WN side by side along the outputs
-template <int WN>
-__global__ void __launch_bounds__(128 * WN, 1)
+// grid (row tiles of 64 WM, output tiles of 32 WN, K chunks); WM x WN waves:
+// WM along the rows, WN side by side along the outputs
+template <int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN, 1)
 prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_t hdr_bytes,
                const uint8_t* __restrict__ ximg, uint32_t img_bytes, float* __restrict__ y, int R, int N, int NS,
                int KB, int kc, int64_t slice) {
-  constexpr int PF_WN = WN, PF_WAVES = 2 * WN;
+  constexpr int PF_WN = WN, PF_WAVES = WM * WN, MT = WM * PF_RT;
+  constexpr int PF_BUF = pf_buf(MT), PF_X = MT * 8 * PF_CHUNK, NCH = PF_BUF / PF_CHUNK;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, nl = lane & 15;
-  const int wm = w & 1, wn = w >> 1;                 // the wave's place in the 2 x PF_WN grid
-  const int m0 = blockIdx.x * (PF_TILES * 16);       // first row of the workgroup
+  const int wm = w % WM, wn = w / WM;                // the wave's place in the WM x WN grid
+  const int m0 = blockIdx.x * (MT * 16);             // first row of the workgroup
   const int ns0 = (blockIdx.y * PF_WN + wn) * PF_U;  // first sub-tile of the wave
   // K in gridDim.z chunks of kc blocks: chunk z covers blocks jb .. je - 1 and
   // writes its partial sums to slice z (R x N, `slice` floats apart) of y; with
@@ -112,8 +111,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   const __amdgpu_buffer_rsrc_t ir = rsrc(ximg, img_bytes);
   auto stage_x = [&](int j, int buf) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(blockIdx.x * KB + j) * (uint32_t)PF_BUF;
-    for (int i = 0; i < PF_BUF / PF_CHUNK / PF_WAVES; ++i) {
-      const int c = w * (PF_BUF / PF_CHUNK / PF_WAVES) + i;
+    for (int c = w; c < NCH; c += PF_WAVES) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ir, (__attribute__((address_space(3))) void*)(lds + buf * PF_BUF + c * PF_CHUNK), 16,
           base + (uint32_t)(c * PF_CHUNK + lane * 16), 0, 0, 0);
@@ -186,23 +184,25 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   }
 }
 
-// The LDS image of x: for 128-row tile m and block j, at (m KB + j) * 72 KiB,
-// chunk (row tile rt, step t) at 1 KiB (8 rt + t) holds lane 16 g + r's binary16
-// A operand of row 128 m + 16 rt + r (k = 256 j + 64 g + 32 (e & 1) + 4 t + (e >> 1)
-// for element e), and chunk 64 + rt the sub-block sums of those rows (two per
+// The LDS image of x for workgroups of MT row tiles: for row tile group m and
+// block j, at (m KB + j) * 9 MT KiB, chunk (row tile rt, step t) at 1 KiB (8 rt + t)
+// holds lane 16 g + r's binary16 A operand of row 16 (MT m + rt) + r (k = 256 j +
+// 64 g + 32 (e & 1) + 4 t + (e >> 1) for element e), and chunk 8 MT + rt the
+// sub-block sums of those rows (two per
 // lane group, as binary16 head and tail).  Rows past R are zeros.  One thread per
 // (m, j, rt, lane): it reads the row's 64 values of sub-blocks 2g, 2g + 1 (one
 // 128-byte line) and writes 8 operands and one sum entry.
 __global__ void __launch_bounds__(256)
-prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, int R, int KB, int64_t total) {
+prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, int R, int KB, int MT, int64_t total) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= total) return;
   const int lane = (int)(id & 63), g = lane >> 4, r = lane & 15;
-  const int64_t q = id >> 6;                       // (m KB + j) * 8 + rt
-  const int rt = (int)(q & 7);
-  const int64_t mj = q >> 3;
+  const int64_t q = id >> 6;                       // (m KB + j) * MT + rt
+  const int rt = (int)(q % MT);
+  const int64_t mj = q / MT;
   const int64_t m = mj / KB, j = mj - m * KB;
-  const int64_t row = m * (PF_TILES * 16) + rt * 16 + r;
+  const int64_t row = m * (MT * 16) + rt * 16 + r;
+  const int PF_BUF = pf_buf(MT), PF_X = MT * 8 * PF_CHUNK;
   u32x4 v[8];
   if (row < R) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + row * (int64_t)KB * SB_W + j * SB_W + 64 * g);
@@ -233,34 +233,38 @@ prefill_reduce_kernel(const float* __restrict__ part, float* __restrict__ y, int
   y[i] = s;
 }
 
-// The plan for (N, K, R): 8 or 12 waves per workgroup (output tiles of 128 or
-// 192), and K in chunks (of at least 8 blocks) while the grid is below the CU
-// count.  Of the two wave counts the one with the lower estimated time is
-// taken: rounds of workgroups over the CUs times the work of one, the 12-wave
-// kernel doing the same work 1.12x faster (measured at 2048 prompt rows).
+// The plan for (N, K, R): the wave grid (WM x WN: 64 WM rows x 32 WN outputs
+// per workgroup; 2 x 4, 2 x 6 or 1 x 8 waves, two or three per SIMD)
+// and K in chunks (of at least 8 blocks) while the grid is below the CU count.
+// The grid with the lowest estimated time is taken: rounds of workgroups over
+// the CUs times the work of one (WM WN waves x kc blocks), the 12-wave grid
+// doing it 1.12x faster (measured at 2048 prompt rows).
 PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus) {
   const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
   PrefillPlan best{};
   double best_cost = 0.0;
-  for (int wn : {4, 6}) {
+  const int grids[3][2] = {{2, 4}, {2, 6}, {1, 8}};
+  for (int gi = 0; gi < 3; ++gi) {
+    const int wm = grids[gi][0], wn = grids[gi][1];
     PrefillPlan p{};
+    p.wm = wm;
     p.wn = wn;
-    p.mt = (R + PF_TILES * 16 - 1) / (PF_TILES * 16);
+    p.mt = (R + wm * PF_RT * 16 - 1) / (wm * PF_RT * 16);
     p.nt = (NS + wn * PF_U - 1) / (wn * PF_U);
     int64_t S = 1;
     while (p.mt * p.nt * S * 2 <= cus && KB / (S * 2) >= 8) S *= 2;
     p.kc = (KB + S - 1) / S;
     p.S = (KB + p.kc - 1) / p.kc;
     const int64_t rounds = (p.mt * p.nt * p.S + cus - 1) / cus;
-    const double cost = (double)rounds * (double)(wn * p.kc) / (wn == 6 ? 1.12 : 1.0);
-    if (wn == 4 || cost < best_cost) {
+    const double cost = (double)rounds * (double)(wm * wn * p.kc) / (wm * wn == 12 ? 1.12 : 1.0);
+    if (gi == 0 || cost < best_cost) {
       best = p;
       best_cost = cost;
     }
   }
   // the activations' LDS image, then (with K chunks) the partial slices of R x N
   // fp32, each rounded up to 16 bytes
-  best.img_bytes = (size_t)best.mt * (size_t)KB * PF_BUF;
+  best.img_bytes = (size_t)best.mt * (size_t)KB * (size_t)pf_buf(best.wm * PF_RT);
   best.slice = ((int64_t)R * N + 3) / 4 * 4;
   best.ws_bytes = best.img_bytes + (best.S > 1 ? (size_t)best.S * (size_t)best.slice * 4 : 0);
   return best;
@@ -272,18 +276,23 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const voi
   const uint32_t qb = (uint32_t)quant_region_bytes(N, K);
   const uint32_t hb = (uint32_t)(packed_bytes(N, K) - quant_region_bytes(N, K));
   uint8_t* const img = reinterpret_cast<uint8_t*>(ws);
-  const int64_t total = p.mt * KB * 8 * 64;
+  const int MT = p.wm * PF_RT;
+  const int64_t total = p.mt * KB * MT * 64;
   hipLaunchKernelGGL(prefill_image_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint16_t*>(x), img, R, (int)KB, total);
+                     reinterpret_cast<const uint16_t*>(x), img, R, (int)KB, MT, total);
   const dim3 grid((unsigned)p.mt, (unsigned)p.nt, (unsigned)p.S);
   float* out = p.S > 1 ? reinterpret_cast<float*>(img + p.img_bytes) : y;
   const int64_t slice = p.S > 1 ? p.slice : 0;
-  if (p.wn == 6)
-    hipLaunchKernelGGL(prefill_kernel<6>, grid, dim3(768), 0, st, packed, qb, hb, img, (uint32_t)p.img_bytes, out, R,
-                       (int)N, (int)NS, (int)KB, (int)p.kc, slice);
+#define QG_PF_LAUNCH(WM_, WN_)                                                                               \
+  hipLaunchKernelGGL((prefill_kernel<WM_, WN_>), grid, dim3(64 * WM_ * WN_), 0, st, packed, qb, hb, img,         \
+                     (uint32_t)p.img_bytes, out, R, (int)N, (int)NS, (int)KB, (int)p.kc, slice)
+  if (p.wm == 2 && p.wn == 6)
+    QG_PF_LAUNCH(2, 6);
+  else if (p.wm == 1 && p.wn == 8)
+    QG_PF_LAUNCH(1, 8);
   else
-    hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(512), 0, st, packed, qb, hb, img, (uint32_t)p.img_bytes, out, R,
-                       (int)N, (int)NS, (int)KB, (int)p.kc, slice);
+    QG_PF_LAUNCH(2, 4);
+#undef QG_PF_LAUNCH
   if (p.S > 1) {
     const int64_t count = (int64_t)R * N;
     hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, out, y, count,

@@ -28,6 +28,8 @@ struct qgemm_handle {
   float* part;
   uint32_t* cnt;
   size_t part_bytes, cnt_bytes;
+  void* tiled_ws;           // the row-tiled path's image and partials (max_R >= QGEMM_TILED_MIN_R)
+  size_t tiled_ws_bytes;
 };
 
 static const uint32_t HANDLE_MAGIC = 0x51474D32u;  // "QGM2"
@@ -164,9 +166,25 @@ bool plan_fits(const Plan& p) { return (p.V + 1) * (p.I + 1) < (int64_t(1) << 31
 // The R-dependent choice: the vector-unit kernel for R <= VALU_AUTO_MAX_R (the
 // measured crossover: below it the vector-unit kernel streams faster), the
 // matrix-core kernel above.
+// The row-tiled kernel from QGEMM_TILED_MIN_R rows on for matrices of at least
+// 2^26 weights (gate|up, down: there the streaming kernel's K chunks and
+// re-staged activations cost more than the row tile's idle rows), and at
+// QGEMM_MAX_R rows for all (measured per matrix over R = 12..64 on one layer).
+bool auto_tiled(const qgemm_handle* h, int R) {
+  if (h->max_R < QGEMM_TILED_MIN_R || R < QGEMM_TILED_MIN_R) return false;
+  return R >= QGEMM_MAX_R || h->N * h->K >= (int64_t(1) << 26);
+}
+
 int make_plan(const qgemm_handle* h, int R, int path, Plan* out) {
-  if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA && path != QGEMM_PATH_VALU) return QGEMM_EINVAL;
+  if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_MFMA && path != QGEMM_PATH_VALU && path != QGEMM_PATH_TILED)
+    return QGEMM_EINVAL;
   if (path == QGEMM_PATH_VALU && R > VALU_MAX_R) return QGEMM_EPATH;
+  if (path == QGEMM_PATH_TILED && h->max_R < QGEMM_TILED_MIN_R) return QGEMM_EPATH;
+  if (path == QGEMM_PATH_TILED || (path == QGEMM_PATH_AUTO && auto_tiled(h, R))) {
+    *out = Plan{};
+    out->path = QGEMM_PATH_TILED;
+    return QGEMM_OK;
+  }
   const bool valu = path == QGEMM_PATH_VALU || (path == QGEMM_PATH_AUTO && R <= VALU_AUTO_MAX_R);
   *out = plan_stream(h->NS, h->KB, R, h->cus, h->occ, 0, valu);
   return plan_fits(*out) ? QGEMM_OK : QGEMM_ESHAPE;
@@ -197,6 +215,11 @@ int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStrea
   Plan p;
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
+  if (p.path == QGEMM_PATH_TILED) {
+    const PrefillPlan tp = prefill_plan(h->N, h->K, R, h->cus);
+    if (tp.ws_bytes > h->tiled_ws_bytes) return QGEMM_EHIP;      // sized at create for every R <= max_R
+    return launch_prefill(h->packed, h->N, h->K, x, y, R, tp, h->tiled_ws, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+  }
   StreamArgs a{};
   a.d0 = make_desc(h, x, y, p);
   a.descs = nullptr;
@@ -296,13 +319,19 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
   part = std::max<size_t>(part, 256);
   h->part_bytes = part;
   h->cnt_bytes = cnt;
+  size_t tiled = 0;
+  if (max_R >= QGEMM_TILED_MIN_R)
+    for (int R = 1; R <= max_R; ++R) tiled = std::max(tiled, prefill_plan(N, K, R, h->cus).ws_bytes);
+  h->tiled_ws_bytes = tiled;
   bool ok = hipMalloc(reinterpret_cast<void**>(&h->part), part) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&h->cnt), cnt) == hipSuccess &&
+            (tiled == 0 || hipMalloc(&h->tiled_ws, tiled) == hipSuccess) &&
             hipMemset(h->cnt, 0, cnt) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     if (h->part) (void)hipFree(h->part);
     if (h->cnt) (void)hipFree(h->cnt);
+    if (h->tiled_ws) (void)hipFree(h->tiled_ws);
     delete h;
     return QGEMM_ENOMEM;
   }
@@ -313,7 +342,7 @@ int qgemm_create(qgemm_t* out, const void* packed_dev, int64_t N, int64_t K, int
 int qgemm_run_path(qgemm_t h, const void* x_bf16, float* y, int R, int path, void* stream) {
   if (!valid_handle(h)) return QGEMM_EINVAL;
   if (R < 0 || R > h->max_R) return QGEMM_ERANGE_R;
-  if (path < QGEMM_PATH_AUTO || path > QGEMM_PATH_MFMA) return QGEMM_EINVAL;
+  if (path < QGEMM_PATH_AUTO || path > QGEMM_PATH_TILED) return QGEMM_EINVAL;
   if (R == 0) return QGEMM_OK;
   if (!x_bf16 || !y) return QGEMM_EINVAL;
   if (!aligned16(x_bf16) || !aligned16(y)) return QGEMM_EALIGN;
@@ -447,6 +476,17 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   Plan p;
   int rc = make_plan(h, R, path, &p);
   if (rc) return rc;
+  if (p.path == QGEMM_PATH_TILED) {
+    const PrefillPlan tp = prefill_plan(h->N, h->K, R, h->cus);
+    *info = qgemm_info{};
+    info->path = QGEMM_PATH_TILED;
+    info->tiles = tp.mt * tp.nt;
+    info->workgroups = tp.mt * tp.nt * tp.S;
+    info->kernels = tp.S > 1 ? 3 : 2;
+    info->k_chunks = (int)tp.S;
+    info->workspace_bytes = tp.ws_bytes;
+    return QGEMM_OK;
+  }
   info->path = p.path;
   info->row_tiles = p.path == QGEMM_PATH_VALU ? 0 : p.RT;
   info->subtiles_per_wave = p.NT;
@@ -469,6 +509,7 @@ int qgemm_destroy(qgemm_t h) {
   (void)hipDeviceSynchronize();
   if (h->part) (void)hipFree(h->part);
   if (h->cnt) (void)hipFree(h->cnt);
+  if (h->tiled_ws) (void)hipFree(h->tiled_ws);
   h->magic = 0;
   delete h;
   return QGEMM_OK;

@@ -92,12 +92,12 @@ hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 // rows tiled as well as outputs (prefill.hip): x [R x K] bf16, y [R x N] fp32, any R.
-// Grid: mt row tiles x nt output tiles (32 wn outputs) x S chunks of K (kc blocks each).  The
+// Grid: mt row tiles (64 wm rows) x nt output tiles (32 wn outputs) x S chunks of K (kc blocks each).  The
 // workspace (ws_bytes) holds the activations' LDS image (img_bytes, written by a
 // first kernel) and, with S > 1, the chunks' partial outputs, which a last
 // kernel adds in chunk order.
 struct PrefillPlan {
-  int wn;                  // waves side by side along the outputs (4 or 6; two along the rows)
+  int wm, wn;              // waves along the rows (2: 128-row tiles, 1: 64) and along the outputs
   int64_t mt, nt, S, kc, slice;
   size_t img_bytes, ws_bytes;
 };
