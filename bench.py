@@ -601,7 +601,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--R", type=int, default=12)
-    ap.add_argument("--sweep", default="1,3,12", help="extra row counts timed for the flatness report")
+    ap.add_argument("--sweep", default="1,3,12,24,48",
+                    help="extra row counts timed over the full pass (flatness; 24 and 48 rows = 8 and 16 agents)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--persistent", action="store_true",
@@ -684,6 +685,10 @@ def main():
         print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
         return
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
+    if args.persistent and max(sweep) > 12:
+        # one cooperative launch runs the streaming kernel only, whose large-R plans need K chunks
+        sweep = [r for r in sweep if r <= max(12, args.R)]
+        log(f"[pass] persistent launch: row counts {sweep}")
     R_max = max(sweep)
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)
     seq = wsg.Seq(gemms, persistent=args.persistent)
@@ -758,6 +763,12 @@ def main():
             "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),
             "rows_tok_per_s": round(args.R * 1000 / ms, 1),
             "ms_per_pass_by_R": {str(k): round(v, 5) for k, v in results.items()},
+            "GB_s_by_R": {str(k): round(pass_bytes / v / 1e6, 1) for k, v in results.items()},
+            "pct_hbm_peak_by_R": {str(k): round(pass_bytes / v / 1e6 / RF.HBM_PEAK_GBS * 100, 2)
+                                  for k, v in results.items()},
+            "rows_tok_per_s_by_R": {str(k): round(k * 1000 / v, 1) for k, v in results.items()},
+            "row_tiled_gemms_by_R": {str(k): sum(1 for g in gemms if g.query(k)["path"] == wsg.PATH_TILED)
+                                     for k in results},
             "flatness_t12_over_t1": round(results[12] / results[1], 4) if 1 in results and 12 in results else None,
             "kernel_paths_ms_per_pass_by_R": paths,
         },
