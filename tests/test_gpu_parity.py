@@ -491,3 +491,34 @@ def test_seq_matches_oracle_and_repeats_bitwise(orc, persistent):
     seq.close()
     for _, g in mats:
         g.close()
+
+
+def test_seq_with_row_tiled_gemms_matches_oracle(orc):
+    """A graph-replayed sequence at 64 rows, where every GEMM takes the row-tiled
+    kernel (activation image, product, K-chunk sums), and at 24 rows on the
+    streaming kernel through the same handles; repeats are bitwise equal."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    from weight_streaming_gemm_amd import qgemm as Q
+    shapes = [(300, 1024), (5120, 2048), (40, 8192)]
+    mats = [G.make(11, i, N, K, max_R=64) for i, (N, K) in enumerate(shapes)]
+    assert all(g.query(64)["path"] == Q.PATH_TILED for _, g in mats)
+    assert all(g.query(24)["path"] == Q.PATH_MFMA for _, g in mats)
+    seq = wsg.Seq([g for _, g in mats])
+    for R in (64, 24):
+        _flush(f"seq row-tiled R={R}")
+        xs_np = [synth.x_bf16(11, 200 + i, R, K) for i, (N, K) in enumerate(shapes)]
+        xs = [G.to_dev(x) for x in xs_np]
+        ys = [torch.full((R, N), -7.0, dtype=torch.float32, device="cuda") for N, K in shapes]
+        seq.run(xs, ys, R)
+        torch.cuda.synchronize()
+        first = [y.cpu().numpy() for y in ys]
+        for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+            assert_parity(first[i], orc.gemm(canon, N, K, xs_np[i]), f"seq R={R} gemm {i}")
+        seq.run(xs, ys, R)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), first[i].view(np.uint32))
+    seq.close()
+    for _, g in mats:
+        g.close()
