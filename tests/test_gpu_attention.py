@@ -36,8 +36,9 @@ def _run(q, k, v, lengths, max_len):
 
 @pytest.mark.parametrize("rows", [1, 2, 3, 4])
 def test_attention_small_ragged_lengths(rows):
-    """Lengths around the split size (1024) and the 32-position steps, an empty
-    cache, two key/value heads."""
+    """Lengths around a split boundary (6 agents x 2 heads: splits of 128
+    positions, 1024 a boundary) and the 32-position steps, an empty cache, two
+    key/value heads."""
     rng = np.random.default_rng(rows)
     lengths = [0, 31, 1023, 1024, 1025, 2500]
     A, Hkv, d = len(lengths), 2, 128

@@ -9,7 +9,7 @@
 // sees positions 0 .. L + i.  Query head hq reads key/value head hq / 8
 // (groups of 8 query heads); head size 128; scores q.k / sqrt(128).
 //
-// Split kernel: workgroup (s, h, a) takes positions [s SPLIT, (s + 1) SPLIT) of
+// Split kernel: workgroup (s, h, a) takes positions [s split, (s + 1) split) of
 // agent a's cache for key/value head h, for all rows x 8 query heads of the
 // group at once (at most 32 query vectors: the rows of one 16 x 16 matrix-core
 // tile pair).  Each of its 4 waves takes every 4th tile of 32 positions:
@@ -39,7 +39,6 @@ typedef uint32_t w32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AD = ATTN_HEAD_DIM;       // 128
 constexpr int GRP = ATTN_GROUP;         // 8 query heads per key/value head
-constexpr int SPLIT = ATTN_SPLIT;       // positions per workgroup
 constexpr int TK = 32;                  // positions per wave step
 constexpr int NWAVE = 4;
 constexpr uint32_t AOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
@@ -75,6 +74,7 @@ attn_split_kernel(AttnArgs a) {
   const int L0 = a.lengths[ag];
   const int L = L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0);
   const int total = L + rows;                               // positions the last row sees
+  const int SPLIT = a.split;                                // positions per workgroup
   const int p_begin = s * SPLIT;
   if (p_begin >= total) return;                             // the combine reads only splits below total
   const int p_end = p_begin + SPLIT < total ? p_begin + SPLIT : total;
@@ -255,7 +255,7 @@ attn_combine_kernel(AttnArgs a, float* __restrict__ out) {
   const int h = hq / GRP, qv = i * GRP + hq % GRP, Hq = a.Hkv * GRP;
   const int L0 = a.lengths[ag];
   const int total = (L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0)) + a.rows;
-  const int ns = (total + SPLIT - 1) / SPLIT;               // <= nsplit (sized for max_len)
+  const int ns = (total + a.split - 1) / a.split;           // <= nsplit (sized for max_len)
   const size_t item0 = ((size_t)ag * a.Hkv + h) * a.nsplit;
   // (unrolled so that several splits' loads are in flight at once)
   float m = -__builtin_inff();

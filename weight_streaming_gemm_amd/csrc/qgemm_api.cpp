@@ -463,7 +463,8 @@ int qgemm_decode_attention(const void* q_bf16, const void* k_cache, const void* 
   a.Hkv = kv_heads;
   a.cap = cap;
   a.max_len = max_len;
-  a.nsplit = attn_splits(max_len, rows);
+  a.split = attn_split_len(agents, kv_heads, max_len, rows);
+  a.nsplit = attn_splits(agents, kv_heads, max_len, rows);
   a.part_o = reinterpret_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)agents * kv_heads * a.nsplit * 32 * ATTN_HEAD_DIM;
   a.scale_log2 = (float)(1.4426950408889634 / 11.313708498984761);   // log2(e) / sqrt(128)
