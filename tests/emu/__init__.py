@@ -15,7 +15,7 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 def build(force: bool = False) -> str:
     src = os.path.join(HERE, "qgemm_emu.cpp")
     deps = [src] + [os.path.join(HERE, "..", "..", "weight_streaming_gemm_amd", "csrc", f)
-                    for f in ("layout.h", "operand.h", "stream_sched.h")]
+                    for f in ("layout.h", "operand.h", "stream_sched.h", "prefill_plan.h")]
     if force or not os.path.exists(LIB) or any(os.path.getmtime(d) > os.path.getmtime(LIB) for d in deps):
         tmp = LIB + ".tmp"
         subprocess.check_call([CLANG, "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
@@ -44,8 +44,30 @@ def lib():
         L.emu_dequant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.emu_pack.restype = ctypes.c_int
         L.emu_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]
+        L.emu_prefill_plan.restype = ctypes.c_int
+        L.emu_prefill_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_prefill.restype = ctypes.c_int
+        L.emu_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
         _lib = L
     return _lib
+
+
+PLAN_FIELDS = ("wm", "wn", "mt", "nt", "S", "kc", "img_bytes", "ws_bytes")
+
+
+def prefill_plan(N, K, R, cus=256):
+    out = np.zeros(8, np.int64)
+    lib().emu_prefill_plan(N, K, R, cus, out.ctypes.data)
+    return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
+
+
+def prefill(canon, N, K, x_bits, cus=256):
+    R = x_bits.shape[0]
+    y = np.zeros((R, N), np.float32)
+    xb = np.ascontiguousarray(x_bits.view(np.uint16))
+    lib().emu_prefill(np.ascontiguousarray(canon).ctypes.data, N, K, xb.ctypes.data, R, cus, y.ctypes.data)
+    return y
 
 
 def stream(canon, N, K, x_bits, NT=2, NW=4, V=8, order_seed=0, nwn=1, aligned=0, msum=1, chunks=1):

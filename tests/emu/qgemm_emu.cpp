@@ -16,6 +16,7 @@
 #include "../../weight_streaming_gemm_amd/csrc/layout.h"
 #include "../../weight_streaming_gemm_amd/csrc/operand.h"
 #include "../../weight_streaming_gemm_amd/csrc/stream_sched.h"
+#include "../../weight_streaming_gemm_amd/csrc/prefill_plan.h"
 #include <algorithm>
 #include <cmath>
 #include <random>
@@ -69,6 +70,45 @@ void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
           memcpy(packed + quant_region_bytes(N, K) + header_chunk_off(ns, j, KB) + nl * 16, hd, 16);
         }
       }
+}
+
+
+// ---- the row-tiled kernel (prefill.hip): plan, activation image, product ----
+
+// the image, as prefill_image_kernel writes it: per (row tile group m, block j,
+// row tile rt, lane 16 g + r) the row's 64 values of sub-blocks 2g, 2g + 1 as 8
+// A operands and the two sums (bf16 widened to fp32, added in k order)
+void prefill_image(const uint16_t* x, int R, int64_t KB, int MT, int64_t mt, std::vector<uint8_t>& img) {
+  img.assign((size_t)mt * KB * pf_buf(MT), 0);
+  for (int64_t m = 0; m < mt; ++m)
+    for (int64_t j = 0; j < KB; ++j)
+      for (int rt = 0; rt < MT; ++rt)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int g = lane >> 4, r = lane & 15;
+          const int64_t row = m * MT * 16 + rt * 16 + r;
+          uint32_t v[32];                       // 64 bf16 values as 32 dwords
+          for (int i = 0; i < 32; ++i) {
+            uint32_t d = 0;
+            if (row < R) memcpy(&d, x + row * KB * SB_W + j * SB_W + 64 * g + 2 * i, 4);
+            v[i] = d;
+          }
+          for (int t = 0; t < 8; ++t) {
+            const int lo = 2 * t, hi = 16 + 2 * t;   // dwords of k = 4 t .. 4 t + 3 and 32 further on
+            const f16x8 op = build_a(v[lo], v[lo + 1], v[hi], v[hi + 1]);
+            memcpy(img.data() + pf_chunk_off(m, j, KB, MT, pf_operand_chunk(rt, t)) + lane * 16, &op, 16);
+          }
+          float s0 = 0.f, s1 = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            s0 += bitcast<float>(v[i] << 16);
+            s0 += bitcast<float>(v[i] & 0xFFFF0000u);
+          }
+          for (int i = 16; i < 32; ++i) {
+            s1 += bitcast<float>(v[i] << 16);
+            s1 += bitcast<float>(v[i] & 0xFFFF0000u);
+          }
+          const f16x8 sv = build_s(s0, s1);
+          memcpy(img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, rt)) + lane * 16, &sv, 16);
+        }
 }
 
 int64_t x_slot_of_emu(int64_t j, int64_t j0, int64_t KB) { return (j - j0 + KB) % KB; }
@@ -408,6 +448,100 @@ int emu_dequant(const uint8_t* canon, int64_t N, int64_t K, float* w) {
             w[n * K + j * SB_W + slot_k(g, t, p)] = std::fma(A[hb], qq, -B[hb]);
           }
       }
+  return 0;
+}
+
+
+// The row-tiled kernel's plan (wm, wn, mt, nt, S, kc, img_bytes, ws_bytes).
+int emu_prefill_plan(int64_t N, int64_t K, int R, int cus, int64_t* out) {
+  const PrefillPlan p = prefill_plan(N, K, R, cus);
+  const int64_t v[8] = {p.wm, p.wn, p.mt, p.nt, p.S, p.kc, (int64_t)p.img_bytes, (int64_t)p.ws_bytes};
+  memcpy(out, v, sizeof(v));
+  return 0;
+}
+
+// Replay of the row-tiled path: the plan, the image, every workgroup's waves
+// (row tiles wm PF_RT .., sub-tiles (tile WN + wn) PF_U ..) over its K chunk with
+// the matrix-core products emulated, the per-block d / dmin update, and with K
+// chunks the partial slices added in chunk order.  y: R x N fp32.
+int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int cus, float* y) {
+  const PrefillPlan p = prefill_plan(N, K, R, cus);
+  const int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
+  const int MT = p.wm * PF_RT;
+  std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
+  pack(canon, packed.data(), N, K);
+  const int64_t hdr_off = quant_region_bytes(N, K);
+  std::vector<uint8_t> img;
+  prefill_image(x, R, KB, MT, p.mt, img);
+  std::vector<float> part((size_t)p.S * p.slice, 0.f);
+  for (int64_t z = 0; z < p.S; ++z)
+    for (int64_t m = 0; m < p.mt; ++m)
+      for (int64_t nt = 0; nt < p.nt; ++nt)
+        for (int wm = 0; wm < p.wm; ++wm)
+          for (int wn = 0; wn < p.wn; ++wn) {
+            const int64_t jb = z * p.kc, je = std::min<int64_t>(jb + p.kc, KB);
+            f32x4 acc[PF_RT][PF_U][64] = {};
+            for (int64_t j = jb; j < je; ++j) {
+              WConst c[PF_U][64];
+              uint32_t q[PF_U][64][8];
+              for (int u = 0; u < PF_U; ++u) {
+                const int64_t ns = (nt * p.wn + wn) * PF_U + u;
+                for (int lane = 0; lane < 64; ++lane) {
+                  const int g = lane >> 4, nl = lane & 15;
+                  uint32_t h[4] = {0, 0, 0, 0};
+                  for (int t = 0; t < 8; ++t) q[u][lane][t] = 0;
+                  if (ns < NS) {
+                    const uint8_t* qp = packed.data() + quant_chunk_off(ns, j, KB) + lane * 16;
+                    memcpy(q[u][lane], qp, 16);
+                    memcpy(q[u][lane] + 4, qp + 1024, 16);
+                    memcpy(h, packed.data() + hdr_off + header_chunk_off(ns, j, KB) + nl * 16, 16);
+                  }
+                  c[u][lane] = header_consts(h[0], h[1], h[2], h[3], g);
+                }
+              }
+              f32x4 ds[PF_RT][PF_U][64] = {};
+              for (int t = 0; t < 8; ++t)
+                for (int rt = 0; rt < PF_RT; ++rt) {
+                  f16x8 a[64];
+                  memcpy(a, img.data() + pf_chunk_off(m, j, KB, MT, pf_operand_chunk(wm * PF_RT + rt, t)), 1024);
+                  for (int u = 0; u < PF_U; ++u) {
+                    f16x8 b[64];
+                    for (int lane = 0; lane < 64; ++lane) b[lane] = build_b(q[u][lane][t], c[u][lane]);
+                    mfma_16x16x32(a, b, ds[rt][u]);
+                  }
+                }
+              for (int rt = 0; rt < PF_RT; ++rt) {
+                f16x8 sx[64];
+                memcpy(sx, img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, wm * PF_RT + rt)), 1024);
+                for (int u = 0; u < PF_U; ++u) {
+                  f16x8 bm[64];
+                  for (int lane = 0; lane < 64; ++lane) bm[lane] = build_m(c[u][lane]);
+                  f32x4 ms[64] = {};
+                  mfma_16x16x32(sx, bm, ms);
+                  for (int lane = 0; lane < 64; ++lane)
+                    for (int i = 0; i < 4; ++i) {
+                      acc[rt][u][lane][i] = std::fma(c[u][lane].d, ds[rt][u][lane][i], acc[rt][u][lane][i]);
+                      acc[rt][u][lane][i] = std::fma(c[u][lane].nmin, ms[lane][i], acc[rt][u][lane][i]);
+                    }
+                }
+              }
+            }
+            for (int rt = 0; rt < PF_RT; ++rt)
+              for (int u = 0; u < PF_U; ++u)
+                for (int lane = 0; lane < 64; ++lane) {
+                  const int64_t n = ((nt * p.wn + wn) * PF_U + u) * TILE_N + (lane & 15);
+                  if (n >= N) continue;
+                  for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m * MT * 16 + (wm * PF_RT + rt) * 16 + 4 * (lane >> 4) + i;
+                    if (row < R) part[(size_t)(z * p.slice + row * N + n)] = acc[rt][u][lane][i];
+                  }
+                }
+          }
+  for (int64_t i = 0; i < (int64_t)R * N; ++i) {
+    float s = part[(size_t)i];
+    for (int64_t z = 1; z < p.S; ++z) s += part[(size_t)(z * p.slice + i)];
+    y[i] = s;
+  }
   return 0;
 }
 

@@ -190,3 +190,69 @@ def test_stream_schedule_slots_unique():
             assert owners == list(range(q_lo, q_hi + 1))
             slots = [s for s, tt in used.items() if tt == t]
             assert len(slots) == (len(owners) if len(owners) > 1 else 0)
+
+
+# ---- the row-tiled path (prompt-chunk rows, and large R) ----------------------
+
+@pytest.mark.parametrize("N,K", [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600), (151936, 5120),
+                                 (300, 1024), (16, 256)])
+@pytest.mark.parametrize("R", [1, 12, 48, 64, 76, 524, 2060])
+def test_prefill_plan_covers_the_problem(N, K, R):
+    """Every row, output and block is in exactly one workgroup's share; K chunks
+    hold at least 8 blocks (or there is one); the workspace holds the image and
+    the chunks' partial slices."""
+    p = emu.prefill_plan(N, K, R)
+    KB, NS = K // 256, (N + 15) // 16
+    rows, subtiles = 16 * 4 * p["wm"], 2 * p["wn"]
+    assert (p["wm"], p["wn"]) in ((2, 4), (2, 6), (1, 8))
+    assert p["mt"] * rows >= R > (p["mt"] - 1) * rows
+    assert p["nt"] * subtiles >= NS > (p["nt"] - 1) * subtiles
+    assert p["S"] * p["kc"] >= KB > (p["S"] - 1) * p["kc"]
+    assert p["S"] == 1 or p["kc"] >= 8
+    img = p["mt"] * KB * 9 * 4 * p["wm"] * 1024
+    assert p["img_bytes"] == img
+    slice_ = (R * N + 3) // 4 * 4
+    assert p["ws_bytes"] == img + (p["S"] * slice_ * 4 if p["S"] > 1 else 0)
+
+
+def test_prefill_plan_choices_on_the_layer():
+    """The choices the measurements rest on: gate|up at 48 rows on the 64-row
+    grid (one round), down at 76 rows in K chunks (40 output tiles), and the
+    12-wave grid at 2060 rows."""
+    assert (emu.prefill_plan(51200, 5120, 48)["wm"], emu.prefill_plan(51200, 5120, 48)["wn"]) == (1, 8)
+    assert emu.prefill_plan(5120, 25600, 76)["S"] > 1
+    p = emu.prefill_plan(51200, 5120, 2060)
+    assert (p["wm"], p["wn"]) == (2, 6)
+
+
+# (N, K, R, CUs): each wave grid, K in chunks (4 of 8 blocks; 4 of 9 with a last of 6),
+# ragged rows and outputs, one row
+PREFILL_CASES = [(400, 512, 130, 4, (2, 4), 1), (400, 512, 200, 3, (2, 6), 1), (400, 512, 130, 2, (1, 8), 1),
+                 (300, 8192, 76, 64, (2, 4), 4), (70, 8448, 5, 64, None, 4), (33, 256, 1, 256, None, 1)]
+
+
+@pytest.mark.parametrize("N,K,R,cus,grid,S", PREFILL_CASES)
+def test_prefill_replay_matches_oracle(orc, N, K, R, cus, grid, S):
+    """The row-tiled kernel's data flow replayed on the CPU (plan, activation image,
+    lane layouts, per-block scale update, K-chunk slices added in chunk order),
+    with emulated matrix-core products, against the fp64 oracle."""
+    p = emu.prefill_plan(N, K, R, cus)
+    if grid is not None:
+        assert (p["wm"], p["wn"]) == grid
+    assert p["S"] == S
+    canon = synth.matrix_rows(31, N, N, K)
+    x = synth.x_bf16(31, R, R, K, outlier_p=0.01)
+    assert_parity(emu.prefill(canon, N, K, x, cus), orc.gemm(canon, N, K, x), f"replay N={N} K={K} R={R}")
+
+
+def test_prefill_replay_catches_a_wrong_image_chunk(orc):
+    """A planted mistake: rows of the image shifted by one row tile must fail."""
+    N, K, R = 64, 512, 40
+    canon = synth.matrix_rows(32, 1, N, K)
+    x = synth.x_bf16(32, 2, R, K)
+    y = emu.prefill(canon, N, K, x)
+    ref = orc.gemm(canon, N, K, x)
+    assert_parity(y, ref, "replay")
+    wrong = emu.prefill(canon, N, K, np.roll(x, 16, axis=0))
+    with pytest.raises(AssertionError):
+        assert_parity(wrong, ref, "shifted rows")

@@ -30,6 +30,7 @@
 
 #include "layout.h"
 #include "operand.h"
+#include "prefill_plan.h"
 #include "qgemm_internal.h"
 
 namespace qg {
@@ -38,11 +39,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int PF_RT = 4;                       // row tiles per wave
-constexpr int PF_U = 2;                        // output sub-tiles per wave
-constexpr int PF_CHUNK = 64 * 16;              // one (row tile, step) operand chunk: 64 lanes x 16 B
-// LDS image of one block for MT row tiles: MT x 8 operand chunks, then MT chunks of sums
-__host__ __device__ constexpr int pf_buf(int MT) { return 9 * MT * PF_CHUNK; }
+
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
@@ -74,7 +71,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
                const uint8_t* __restrict__ ximg, uint32_t img_bytes, float* __restrict__ y, int R, int N, int NS,
                int KB, int kc, int64_t slice) {
   constexpr int PF_WN = WN, PF_WAVES = WM * WN, MT = WM * PF_RT;
-  constexpr int PF_BUF = pf_buf(MT), PF_X = MT * 8 * PF_CHUNK, NCH = PF_BUF / PF_CHUNK;
+  constexpr int PF_BUF = pf_buf(MT), NCH = PF_BUF / PF_CHUNK;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, nl = lane & 15;
@@ -110,7 +107,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
   // bytes land at the chunk's base + 16 l) ----
   const __amdgpu_buffer_rsrc_t ir = rsrc(ximg, img_bytes);
   auto stage_x = [&](int j, int buf) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)(blockIdx.x * KB + j) * (uint32_t)PF_BUF;
+    const uint32_t base = (uint32_t)pf_chunk_off(blockIdx.x, j, KB, MT, 0);
     for (int c = w; c < NCH; c += PF_WAVES) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ir, (__attribute__((address_space(3))) void*)(lds + buf * PF_BUF + c * PF_CHUNK), 16,
@@ -133,7 +130,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
     for (int t = 0; t < 8; ++t) {
       f16x8 a[PF_RT];
       for (int rt = 0; rt < PF_RT; ++rt)
-        a[rt] = *reinterpret_cast<const f16x8*>(X + ((wm * PF_RT + rt) * 8 + t) * PF_CHUNK + lane * 16);
+        a[rt] = *reinterpret_cast<const f16x8*>(X + pf_operand_chunk(wm * PF_RT + rt, t) * PF_CHUNK + lane * 16);
       for (int u = 0; u < PF_U; ++u) {
         const uint32_t wd = t < 4 ? b.qa[u][t] : b.qb[u][t - 4];
         const f16x8 bo = build_b(wd, c[u]);
@@ -142,7 +139,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
       }
     }
     for (int rt = 0; rt < PF_RT; ++rt) {
-      const f16x8 sx = *reinterpret_cast<const f16x8*>(X + PF_X + (wm * PF_RT + rt) * PF_CHUNK + lane * 16);
+      const f16x8 sx = *reinterpret_cast<const f16x8*>(X + pf_sum_chunk(MT, wm * PF_RT + rt) * PF_CHUNK + lane * 16);
       for (int u = 0; u < PF_U; ++u) {
         const f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(sx, build_m(c[u]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         for (int i = 0; i < 4; ++i) {
@@ -202,7 +199,6 @@ prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, 
   const int64_t mj = q / MT;
   const int64_t m = mj / KB, j = mj - m * KB;
   const int64_t row = m * (MT * 16) + rt * 16 + r;
-  const int PF_BUF = pf_buf(MT), PF_X = MT * 8 * PF_CHUNK;
   u32x4 v[8];
   if (row < R) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + row * (int64_t)KB * SB_W + j * SB_W + 64 * g);
@@ -210,17 +206,18 @@ prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, 
   } else {
     for (int c = 0; c < 8; ++c) v[c] = u32x4{0u, 0u, 0u, 0u};
   }
-  uint8_t* const dst = img + mj * PF_BUF;
+  uint8_t* const dst = img + pf_chunk_off(m, j, KB, MT, 0);
   // v[c] holds k = 64 g + 8 c .. 8 c + 7: c < 4 sub-block 2g, c >= 4 sub-block 2g + 1
   for (int t = 0; t < 8; ++t) {
     const u32x4 lo = v[t >> 1], hi = v[4 + (t >> 1)];
     const int o = (t & 1) * 2;                     // dwords of k = 4 t .. 4 t + 3 within the 8-value load
-    *reinterpret_cast<f16x8*>(dst + (rt * 8 + t) * PF_CHUNK + lane * 16) = build_a(lo[o], lo[o + 1], hi[o], hi[o + 1]);
+    *reinterpret_cast<f16x8*>(dst + pf_operand_chunk(rt, t) * PF_CHUNK + lane * 16) =
+        build_a(lo[o], lo[o + 1], hi[o], hi[o + 1]);
   }
   float s0 = 0.f, s1 = 0.f;
   for (int c = 0; c < 4; ++c) s0 = sum8_bf16(v[c], s0);
   for (int c = 4; c < 8; ++c) s1 = sum8_bf16(v[c], s1);
-  *reinterpret_cast<f16x8*>(dst + PF_X + rt * PF_CHUNK + lane * 16) = build_s(s0, s1);
+  *reinterpret_cast<f16x8*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) = build_s(s0, s1);
 }
 
 // y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order
@@ -231,43 +228,6 @@ prefill_reduce_kernel(const float* __restrict__ part, float* __restrict__ y, int
   float s = part[i];
   for (int z = 1; z < S; ++z) s += part[z * slice + i];
   y[i] = s;
-}
-
-// The plan for (N, K, R): the wave grid (WM x WN: 64 WM rows x 32 WN outputs
-// per workgroup; 2 x 4, 2 x 6 or 1 x 8 waves, two or three per SIMD)
-// and K in chunks (of at least 8 blocks) while the grid is below the CU count.
-// The grid with the lowest estimated time is taken: rounds of workgroups over
-// the CUs times the work of one (WM WN waves x kc blocks), the 12-wave grid
-// doing it 1.12x faster (measured at 2048 prompt rows).
-PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus) {
-  const int64_t NS = padded_n(N) / TILE_N, KB = K / SB_W;
-  PrefillPlan best{};
-  double best_cost = 0.0;
-  const int grids[3][2] = {{2, 4}, {2, 6}, {1, 8}};
-  for (int gi = 0; gi < 3; ++gi) {
-    const int wm = grids[gi][0], wn = grids[gi][1];
-    PrefillPlan p{};
-    p.wm = wm;
-    p.wn = wn;
-    p.mt = (R + wm * PF_RT * 16 - 1) / (wm * PF_RT * 16);
-    p.nt = (NS + wn * PF_U - 1) / (wn * PF_U);
-    int64_t S = 1;
-    while (p.mt * p.nt * S * 2 <= cus && KB / (S * 2) >= 8) S *= 2;
-    p.kc = (KB + S - 1) / S;
-    p.S = (KB + p.kc - 1) / p.kc;
-    const int64_t rounds = (p.mt * p.nt * p.S + cus - 1) / cus;
-    const double cost = (double)rounds * (double)(wm * wn * p.kc) / (wm * wn == 12 ? 1.12 : 1.0);
-    if (gi == 0 || cost < best_cost) {
-      best = p;
-      best_cost = cost;
-    }
-  }
-  // the activations' LDS image, then (with K chunks) the partial slices of R x N
-  // fp32, each rounded up to 16 bytes
-  best.img_bytes = (size_t)best.mt * (size_t)KB * (size_t)pf_buf(best.wm * PF_RT);
-  best.slice = ((int64_t)R * N + 3) / 4 * 4;
-  best.ws_bytes = best.img_bytes + (best.S > 1 ? (size_t)best.S * (size_t)best.slice * 4 : 0);
-  return best;
 }
 
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,

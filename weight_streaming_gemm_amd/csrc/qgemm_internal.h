@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "prefill_plan.h"
+
 namespace qg {
 
 // One GEMM of a launch: y[R x N] = x[R x K] . W^T over packed weights.
@@ -107,17 +109,8 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
 hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
-// rows tiled as well as outputs (prefill.hip): x [R x K] bf16, y [R x N] fp32, any R.
-// Grid: mt row tiles (64 wm rows) x nt output tiles (32 wn outputs) x S chunks of K (kc blocks each).  The
-// workspace (ws_bytes) holds the activations' LDS image (img_bytes, written by a
-// first kernel) and, with S > 1, the chunks' partial outputs, which a last
-// kernel adds in chunk order.
-struct PrefillPlan {
-  int wm, wn;              // waves along the rows (2: 128-row tiles, 1: 64) and along the outputs
-  int64_t mt, nt, S, kc, slice;
-  size_t img_bytes, ws_bytes;
-};
-PrefillPlan prefill_plan(int64_t N, int64_t K, int R, int cus);
+// rows tiled as well as outputs (prefill.hip; plan and image layout in prefill_plan.h):
+// x [R x K] bf16, y [R x N] fp32, any R
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const void* x, float* y, int R,
                           const PrefillPlan& p, void* ws, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* packed, float* w, int64_t N, int64_t K, hipStream_t st);
