@@ -73,9 +73,10 @@ typedef enum {
 } qgemm_path;
 
 /* The automatic choice takes the row-tiled path from this many rows on for
- * matrices of at least 2^26 weights, and at QGEMM_MAX_R rows for all (the
- * measured crossover against the streaming kernel on one MI355X). */
-#define QGEMM_TILED_MIN_R 48
+ * matrices of at least 32768 outputs, from 48 rows on for matrices of at least
+ * 2^26 weights, and at QGEMM_MAX_R rows for all (the measured crossovers
+ * against the streaming kernel on one MI355X). */
+#define QGEMM_TILED_MIN_R 24
 
 typedef struct qgemm_handle *qgemm_t;
 typedef struct qgemm_seq *qgemm_seq_t;

@@ -53,11 +53,11 @@ def lib():
     return _lib
 
 
-PLAN_FIELDS = ("wm", "wn", "mt", "nt", "S", "kc", "img_bytes", "ws_bytes")
+PLAN_FIELDS = ("wm", "wn", "mt", "nt", "S", "kc", "img_bytes", "ws_bytes", "rtw")
 
 
 def prefill_plan(N, K, R, cus=256):
-    out = np.zeros(8, np.int64)
+    out = np.zeros(9, np.int64)
     lib().emu_prefill_plan(N, K, R, cus, out.ctypes.data)
     return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
 

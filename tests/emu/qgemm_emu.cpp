@@ -452,22 +452,22 @@ int emu_dequant(const uint8_t* canon, int64_t N, int64_t K, float* w) {
 }
 
 
-// The row-tiled kernel's plan (wm, wn, mt, nt, S, kc, img_bytes, ws_bytes).
+// The row-tiled kernel's plan (wm, wn, mt, nt, S, kc, img_bytes, ws_bytes, rtw).
 int emu_prefill_plan(int64_t N, int64_t K, int R, int cus, int64_t* out) {
   const PrefillPlan p = prefill_plan(N, K, R, cus);
-  const int64_t v[8] = {p.wm, p.wn, p.mt, p.nt, p.S, p.kc, (int64_t)p.img_bytes, (int64_t)p.ws_bytes};
+  const int64_t v[9] = {p.wm, p.wn, p.mt, p.nt, p.S, p.kc, (int64_t)p.img_bytes, (int64_t)p.ws_bytes, p.rtw};
   memcpy(out, v, sizeof(v));
   return 0;
 }
 
 // Replay of the row-tiled path: the plan, the image, every workgroup's waves
-// (row tiles wm PF_RT .., sub-tiles (tile WN + wn) PF_U ..) over its K chunk with
+// (row tiles wm RTW .., sub-tiles (tile WN + wn) PF_U ..) over its K chunk with
 // the matrix-core products emulated, the per-block d / dmin update, and with K
 // chunks the partial slices added in chunk order.  y: R x N fp32.
 int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, int R, int cus, float* y) {
   const PrefillPlan p = prefill_plan(N, K, R, cus);
   const int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
-  const int MT = p.wm * PF_RT;
+  const int RTW = p.rtw, MT = p.wm * RTW;
   std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
   pack(canon, packed.data(), N, K);
   const int64_t hdr_off = quant_region_bytes(N, K);
@@ -480,7 +480,7 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
         for (int wm = 0; wm < p.wm; ++wm)
           for (int wn = 0; wn < p.wn; ++wn) {
             const int64_t jb = z * p.kc, je = std::min<int64_t>(jb + p.kc, KB);
-            f32x4 acc[PF_RT][PF_U][64] = {};
+            f32x4 acc[4][PF_U][64] = {};
             for (int64_t j = jb; j < je; ++j) {
               WConst c[PF_U][64];
               uint32_t q[PF_U][64][8];
@@ -499,20 +499,20 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
                   c[u][lane] = header_consts(h[0], h[1], h[2], h[3], g);
                 }
               }
-              f32x4 ds[PF_RT][PF_U][64] = {};
+              f32x4 ds[4][PF_U][64] = {};
               for (int t = 0; t < 8; ++t)
-                for (int rt = 0; rt < PF_RT; ++rt) {
+                for (int rt = 0; rt < RTW; ++rt) {
                   f16x8 a[64];
-                  memcpy(a, img.data() + pf_chunk_off(m, j, KB, MT, pf_operand_chunk(wm * PF_RT + rt, t)), 1024);
+                  memcpy(a, img.data() + pf_chunk_off(m, j, KB, MT, pf_operand_chunk(wm * RTW + rt, t)), 1024);
                   for (int u = 0; u < PF_U; ++u) {
                     f16x8 b[64];
                     for (int lane = 0; lane < 64; ++lane) b[lane] = build_b(q[u][lane][t], c[u][lane]);
                     mfma_16x16x32(a, b, ds[rt][u]);
                   }
                 }
-              for (int rt = 0; rt < PF_RT; ++rt) {
+              for (int rt = 0; rt < RTW; ++rt) {
                 f16x8 sx[64];
-                memcpy(sx, img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, wm * PF_RT + rt)), 1024);
+                memcpy(sx, img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, wm * RTW + rt)), 1024);
                 for (int u = 0; u < PF_U; ++u) {
                   f16x8 bm[64];
                   for (int lane = 0; lane < 64; ++lane) bm[lane] = build_m(c[u][lane]);
@@ -526,13 +526,13 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
                 }
               }
             }
-            for (int rt = 0; rt < PF_RT; ++rt)
+            for (int rt = 0; rt < RTW; ++rt)
               for (int u = 0; u < PF_U; ++u)
                 for (int lane = 0; lane < 64; ++lane) {
                   const int64_t n = ((nt * p.wn + wn) * PF_U + u) * TILE_N + (lane & 15);
                   if (n >= N) continue;
                   for (int i = 0; i < 4; ++i) {
-                    const int64_t row = m * MT * 16 + (wm * PF_RT + rt) * 16 + 4 * (lane >> 4) + i;
+                    const int64_t row = m * MT * 16 + (wm * RTW + rt) * 16 + 4 * (lane >> 4) + i;
                     if (row < R) part[(size_t)(z * p.slice + row * N + n)] = acc[rt][u][lane][i];
                   }
                 }

@@ -203,13 +203,13 @@ def test_prefill_plan_covers_the_problem(N, K, R):
     the chunks' partial slices."""
     p = emu.prefill_plan(N, K, R)
     KB, NS = K // 256, (N + 15) // 16
-    rows, subtiles = 16 * 4 * p["wm"], 2 * p["wn"]
-    assert (p["wm"], p["wn"]) in ((2, 4), (2, 6), (1, 8))
+    rows, subtiles = 16 * p["rtw"] * p["wm"], 2 * p["wn"]
+    assert (p["wm"], p["wn"], p["rtw"]) in ((2, 4, 4), (2, 6, 4), (1, 8, 4), (1, 8, 2))
     assert p["mt"] * rows >= R > (p["mt"] - 1) * rows
     assert p["nt"] * subtiles >= NS > (p["nt"] - 1) * subtiles
     assert p["S"] * p["kc"] >= KB > (p["S"] - 1) * p["kc"]
     assert p["S"] == 1 or p["kc"] >= 8
-    img = p["mt"] * KB * 9 * 4 * p["wm"] * 1024
+    img = p["mt"] * KB * 9 * p["rtw"] * p["wm"] * 1024
     assert p["img_bytes"] == img
     slice_ = (R * N + 3) // 4 * 4
     assert p["ws_bytes"] == img + (p["S"] * slice_ * 4 if p["S"] > 1 else 0)

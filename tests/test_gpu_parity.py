@@ -132,11 +132,16 @@ def test_gemm_ragged_and_split(orc, N, K, R):
 
 
 def test_automatic_choice_of_the_row_tiled_kernel(orc):
-    """From 48 rows on, matrices of at least 2^26 weights take the row-tiled
-    kernel, and every matrix does at 64 rows; below, or on handles made for
-    fewer rows, the streaming kernel; an explicit request needs max_R >= 48."""
+    """Matrices of at least 32768 outputs take the row-tiled kernel from 24 rows
+    on, matrices of at least 2^26 weights from 48 rows on, every matrix at 64
+    rows; below, or on handles made for fewer rows, the streaming kernel; an
+    explicit request needs max_R >= 24."""
     from weight_streaming_gemm_amd import qgemm as Q
-    _, big = G.make(1, 9, 32768, 2048, max_R=48)          # 2^26 weights
+    _, wide = G.make(1, 9, 32768, 512, max_R=24)           # 2^24 weights, 32768 outputs
+    assert wide.query(16)["path"] == Q.PATH_MFMA
+    assert wide.query(24)["path"] == Q.PATH_TILED
+    wide.close()
+    _, big = G.make(1, 9, 16384, 4096, max_R=48)          # 2^26 weights, 16384 outputs
     assert big.query(24)["path"] == Q.PATH_MFMA
     assert big.query(48)["path"] == Q.PATH_TILED
     assert big.query(48)["kernels"] in (2, 3)

@@ -65,12 +65,12 @@ __device__ __forceinline__ float sum8_bf16(u32x4 v, float s) {
 
 // grid (row tiles of 64 WM, output tiles of 32 WN, K chunks); WM x WN waves:
 // WM along the rows, WN side by side along the outputs
-template <int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, 1)
+template <int WM, int WN, int RTW>
+__global__ void __launch_bounds__(64 * WM * WN, RTW == 2 ? 2 : 1)
 prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_t hdr_bytes,
                const uint8_t* __restrict__ ximg, uint32_t img_bytes, float* __restrict__ y, int R, int N, int NS,
                int KB, int kc, int64_t slice) {
-  constexpr int PF_WN = WN, PF_WAVES = WM * WN, MT = WM * PF_RT;
+  constexpr int PF_WN = WN, PF_WAVES = WM * WN, PF_RT = RTW, MT = WM * PF_RT;
   constexpr int PF_BUF = pf_buf(MT), NCH = PF_BUF / PF_CHUNK;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PF_BUF];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,22 +236,24 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const voi
   const uint32_t qb = (uint32_t)quant_region_bytes(N, K);
   const uint32_t hb = (uint32_t)(packed_bytes(N, K) - quant_region_bytes(N, K));
   uint8_t* const img = reinterpret_cast<uint8_t*>(ws);
-  const int MT = p.wm * PF_RT;
+  const int MT = p.wm * p.rtw;
   const int64_t total = p.mt * KB * MT * 64;
   hipLaunchKernelGGL(prefill_image_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t*>(x), img, R, (int)KB, MT, total);
   const dim3 grid((unsigned)p.mt, (unsigned)p.nt, (unsigned)p.S);
   float* out = p.S > 1 ? reinterpret_cast<float*>(img + p.img_bytes) : y;
   const int64_t slice = p.S > 1 ? p.slice : 0;
-#define QG_PF_LAUNCH(WM_, WN_)                                                                               \
-  hipLaunchKernelGGL((prefill_kernel<WM_, WN_>), grid, dim3(64 * WM_ * WN_), 0, st, packed, qb, hb, img,         \
+#define QG_PF_LAUNCH(WM_, WN_, RT_)                                                                          \
+  hipLaunchKernelGGL((prefill_kernel<WM_, WN_, RT_>), grid, dim3(64 * WM_ * WN_), 0, st, packed, qb, hb, img,    \
                      (uint32_t)p.img_bytes, out, R, (int)N, (int)NS, (int)KB, (int)p.kc, slice)
   if (p.wm == 2 && p.wn == 6)
-    QG_PF_LAUNCH(2, 6);
+    QG_PF_LAUNCH(2, 6, 4);
+  else if (p.wm == 1 && p.wn == 8 && p.rtw == 2)
+    QG_PF_LAUNCH(1, 8, 2);
   else if (p.wm == 1 && p.wn == 8)
-    QG_PF_LAUNCH(1, 8);
+    QG_PF_LAUNCH(1, 8, 4);
   else
-    QG_PF_LAUNCH(2, 4);
+    QG_PF_LAUNCH(2, 4, 4);
 #undef QG_PF_LAUNCH
   if (p.S > 1) {
     const int64_t count = (int64_t)R * N;

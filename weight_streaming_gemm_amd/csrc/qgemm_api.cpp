@@ -166,13 +166,14 @@ bool plan_fits(const Plan& p) { return (p.V + 1) * (p.I + 1) < (int64_t(1) << 31
 // The R-dependent choice: the vector-unit kernel for R <= VALU_AUTO_MAX_R (the
 // measured crossover: below it the vector-unit kernel streams faster), the
 // matrix-core kernel above.
-// The row-tiled kernel from QGEMM_TILED_MIN_R rows on for matrices of at least
-// 2^26 weights (gate|up, down: there the streaming kernel's K chunks and
-// re-staged activations cost more than the row tile's idle rows), and at
-// QGEMM_MAX_R rows for all (measured per matrix over R = 12..64 on one layer).
+// The row-tiled kernel (measured per matrix over R = 12..64 on one layer): from
+// QGEMM_TILED_MIN_R rows on for wide matrices (N >= 32768: gate|up, the output
+// head; there its 32-row grid with two workgroups per CU beats the streaming
+// kernel's re-staged activations), from 48 rows on for matrices of at least 2^26
+// weights (down as well), and at QGEMM_MAX_R rows for all.
 bool auto_tiled(const qgemm_handle* h, int R) {
   if (h->max_R < QGEMM_TILED_MIN_R || R < QGEMM_TILED_MIN_R) return false;
-  return R >= QGEMM_MAX_R || h->N * h->K >= (int64_t(1) << 26);
+  return R >= QGEMM_MAX_R || h->N >= 32768 || (R >= 48 && h->N * h->K >= (int64_t(1) << 26));
 }
 
 int make_plan(const qgemm_handle* h, int R, int path, Plan* out) {

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libqgemm.so")
 QGEMM_OK, QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN = 0, -1, -2, -3
 QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH = -4, -5, -6, -7
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_TILED = 0, 1, 2, 3
-TILED_MIN_R = 48
+TILED_MIN_R = 24
 SEQ_PERSISTENT = 1
 MAX_R = 64
 MAX_PREFILL_R = 8192
