@@ -75,8 +75,8 @@ inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn *
 constexpr int ATTN_HEAD_DIM = 128, ATTN_GROUP = 8, ATTN_MAX_ROWS = 4;
 // Sequence splits: as many workgroups as stay resident in one round on an
 // MI355X (256 CUs x 2 workgroups of the split kernel), each split a multiple of
-// 128 positions (4 waves x 32-position tiles).
-constexpr int ATTN_RESIDENT = 512, ATTN_SPLIT_UNIT = 128;
+// the 32-position step.
+constexpr int ATTN_RESIDENT = 512, ATTN_SPLIT_UNIT = 32;
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
