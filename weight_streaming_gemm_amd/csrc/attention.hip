@@ -26,7 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "qgemm_internal.h"
+#include "../../include/qgemm.h"
+#include "attention.h"
 
 namespace qg {
 
@@ -288,3 +289,54 @@ hipError_t launch_attention(const AttnArgs& a, float* out, hipStream_t st) {
 }
 
 }  // namespace qg
+
+// ---- C ABI (include/qgemm.h) ------------------------------------------------
+namespace {
+bool attn_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+using namespace qg;
+
+extern "C" {
+
+int qgemm_attention_workspace_size(int agents, int rows, int kv_heads, int max_len, size_t* bytes) {
+  if (!bytes) return QGEMM_EINVAL;
+  if (agents < 0 || kv_heads < 1 || max_len < 0 || rows < 1 || rows > ATTN_MAX_ROWS) return QGEMM_ESHAPE;
+  *bytes = attn_ws_bytes(agents, kv_heads, rows, max_len);
+  return QGEMM_OK;
+}
+
+int qgemm_decode_attention(const void* q_bf16, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                           int agents, int rows, int q_heads, int kv_heads, int head_dim, int cap, int max_len,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (agents < 0 || kv_heads < 1 || rows < 1 || rows > ATTN_MAX_ROWS || head_dim != ATTN_HEAD_DIM ||
+      q_heads != ATTN_GROUP * kv_heads || max_len < 0 || cap < max_len + rows)
+    return QGEMM_ESHAPE;
+  // every offset into q, the caches and the workspace must fit the kernels' 32-bit buffer offsets
+  const uint64_t cache_bytes = (uint64_t)agents * cap * kv_heads * ATTN_HEAD_DIM * 2;
+  const uint64_t q_bytes = (uint64_t)agents * rows * q_heads * ATTN_HEAD_DIM * 2;
+  if (cache_bytes >= (uint64_t(1) << 31) || q_bytes >= (uint64_t(1) << 31)) return QGEMM_ESHAPE;
+  if (agents == 0) return QGEMM_OK;
+  if (!q_bf16 || !k_cache || !v_cache || !lengths || !out || !workspace) return QGEMM_EINVAL;
+  if (workspace_bytes < attn_ws_bytes(agents, kv_heads, rows, max_len)) return QGEMM_EINVAL;
+  if (!attn_aligned16(q_bf16) || !attn_aligned16(k_cache) || !attn_aligned16(v_cache) || !attn_aligned16(out) || !attn_aligned16(workspace))
+    return QGEMM_EALIGN;
+  AttnArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q_bf16);
+  a.k = reinterpret_cast<const uint16_t*>(k_cache);
+  a.v = reinterpret_cast<const uint16_t*>(v_cache);
+  a.lengths = lengths;
+  a.A = agents;
+  a.rows = rows;
+  a.Hkv = kv_heads;
+  a.cap = cap;
+  a.max_len = max_len;
+  a.split = attn_split_len(agents, kv_heads, max_len, rows);
+  a.nsplit = attn_splits(agents, kv_heads, max_len, rows);
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)agents * kv_heads * a.nsplit * 32 * ATTN_HEAD_DIM;
+  a.scale_log2 = (float)(1.4426950408889634 / 11.313708498984761);   // log2(e) / sqrt(128)
+  return launch_attention(a, out, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+}
+
+}  // extern "C"
