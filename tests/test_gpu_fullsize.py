@@ -137,15 +137,20 @@ def test_ragged_schedule_sampled_steps(orc):
         g.close()
 
 
-def test_output_head_argmax_and_sampled_parity(orc):
+@pytest.mark.parametrize("R", [W.R_DEFAULT, 24])
+def test_output_head_argmax_and_sampled_parity(orc, R):
+    """All 151936 outputs against the oracle and the row argmax; at 24 rows (8
+    agents) the head takes the row-tiled kernel."""
     import torch
     import weight_streaming_gemm_amd as wsg
-    seed, R = W.SEED_PASS, W.R_DEFAULT
+    from weight_streaming_gemm_amd import qgemm as Q
+    seed = W.SEED_PASS
     m = W.lm_head()
     print(f"lm_head N={m.N} K={m.K} R={R}", flush=True)
     canon = fused_canon(seed, m)
     packed = G.upload_packed(canon, m.N, m.K)
     g = wsg.QGemm(packed, m.N, m.K, max_R=R)
+    assert g.query(R)["path"] == (Q.PATH_TILED if R >= 24 else Q.PATH_MFMA)
     x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
     xd = G.to_dev(x)
     y = torch.empty((R, m.N), dtype=torch.float32, device="cuda")
@@ -160,10 +165,16 @@ def test_output_head_argmax_and_sampled_parity(orc):
     top2 = np.sort(ref, axis=1)[:, -2:]
     margin = top2[:, 1] - top2[:, 0]
     err = np.abs(yh - ref).max()
+    got_idx = idx.cpu().numpy()
+    clear = margin > 10 * err
     for r in range(R):
-        print(f"row {r}: argmax {ref_idx[r]} margin {margin[r]:.3e} vs max|dy| {err:.3e}", flush=True)
-        assert margin[r] > 10 * err, f"row {r} argmax ambiguous within the error bound"
-    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        print(f"row {r}: argmax {ref_idx[r]} margin {margin[r]:.3e} vs max|dy| {err:.3e}"
+              f"{'' if clear[r] else ' (ambiguous within the error bound)'}", flush=True)
+    if R == W.R_DEFAULT:
+        assert clear.all(), "an argmax of the 12-row step is ambiguous within the error bound"
+    assert clear.mean() >= 0.9
+    # exact wherever the oracle's top two are apart by more than 10x the observed error
+    assert np.array_equal(got_idx[clear], ref_idx[clear])
     g.close()
 
 

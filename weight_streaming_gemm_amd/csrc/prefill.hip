@@ -220,13 +220,22 @@ prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, 
   *reinterpret_cast<f16x8*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) = build_s(s0, s1);
 }
 
-// y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order
+// y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order;
+// up to 16 chunks' loads are issued before the adds (the planner makes at most
+// KB / 8 chunks, and more than 16 only for K > 32768)
 __global__ void __launch_bounds__(256)
 prefill_reduce_kernel(const float* __restrict__ part, float* __restrict__ y, int64_t count, int64_t slice, int S) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
-  float s = part[i];
-  for (int z = 1; z < S; ++z) s += part[z * slice + i];
+  float s = 0.f;
+  for (int z0 = 0; z0 < S; z0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = z0 + k < S ? part[(z0 + k) * slice + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (z0 + k < S) s = (z0 + k == 0) ? v[k] : s + v[k];
+  }
   y[i] = s;
 }
 
