@@ -115,14 +115,16 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 // operand layout in LDS; the steps then read only weights from memory: per
 // step and sub-tile the 2 KiB quant chunk and the outputs' 16-byte headers,
 // with raw buffer loads (streaming hint), RING steps ahead in a register ring
-// (each slot refilled right after its step), across range and GEMM ends.
-// Loads past the end of the work address beyond the buffer and return zeros
-// without memory traffic.
+// (each slot refilled right after its step) up to the end of the wave's
+// sub-range.  Loads past the end of the work address beyond the buffer and
+// return zeros without memory traffic.
 //
 // With G > 1 all workgroups are resident (cooperative launch) and GEMM g + 1
 // starts only after every workgroup has finished GEMM g, as in a model where
-// each projection's input depends on the previous output; the weights of the
-// next GEMM are already in flight while a workgroup waits.
+// each projection's input depends on the previous output: a workgroup closes
+// its range, arrives at the grid barrier (waiting only for its own stores),
+// requests the first RING steps of its next range (weights do not depend on
+// the previous output), and then waits.
 #ifndef QG_RING
 #define QG_RING 4
 #endif
