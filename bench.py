@@ -652,8 +652,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the weight pass is not sharded across GPUs in this build "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the weight pass runs on a single GPU and is not sharded "
+              "across GPUs; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
