@@ -249,30 +249,52 @@ attn_split_kernel(AttnArgs a) {
 }
 
 // out[a][i][hq][d]: the splits of (agent, key/value head) rescaled to the common
-// maximum, summed in split order, divided by the summed weights
+// maximum, summed in split order, divided by the summed weights.  The splits are
+// read 16 at a time with all their loads in flight together (the partials come
+// from other dies' caches: each round trip is long); the running maximum moves
+// from one group of 16 to the next, and with at most 16 splits there is one
+// group, so every split is scaled by the overall maximum directly.
 __global__ void __launch_bounds__(AD)
 attn_combine_kernel(AttnArgs a, float* __restrict__ out) {
+  constexpr int CH = 16;
+  constexpr float NEG_INF = -__builtin_inff();
   const int hq = blockIdx.x, i = blockIdx.y, ag = blockIdx.z, d = threadIdx.x;
   const int h = hq / GRP, qv = i * GRP + hq % GRP, Hq = a.Hkv * GRP;
   const int L0 = a.lengths[ag];
   const int total = (L0 < 0 ? 0 : (L0 > a.max_len ? a.max_len : L0)) + a.rows;
   const int ns = (total + a.split - 1) / a.split;           // <= nsplit (sized for max_len)
   const size_t item0 = ((size_t)ag * a.Hkv + h) * a.nsplit;
-  // (unrolled so that several splits' loads are in flight at once)
-  float m = -__builtin_inff();
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
-    m = ms > m ? ms : m;
-  }
-  float acc = 0.f, l = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const float ms = a.part_ml[((item0 + s) * 32 + qv) * 2];
-    if (ms == -__builtin_inff()) continue;
-    const float f = __builtin_amdgcn_exp2f(ms - m);
-    acc += f * a.part_o[((item0 + s) * 32 + qv) * AD + d];
-    l += f * a.part_ml[((item0 + s) * 32 + qv) * 2 + 1];
+  float m = NEG_INF, acc = 0.f, l = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    float mv[CH], lv[CH], ov[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      // past the last split, the last split's address (loaded and not used): the
+      // loads carry no branches and issue back to back
+      const bool ok = s0 + u < ns;
+      const size_t it = (item0 + (ok ? s0 + u : ns - 1)) * 32 + qv;
+      const float mu = a.part_ml[it * 2], lu = a.part_ml[it * 2 + 1], ou = a.part_o[it * AD + d];
+      mv[u] = ok ? mu : NEG_INF;
+      lv[u] = ok ? lu : 0.f;
+      ov[u] = ok ? ou : 0.f;
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) mc = mv[u] > mc ? mv[u] : mc;
+    if (mc == NEG_INF) continue;                              // no position of these splits is visible
+    if (m != NEG_INF) {                                       // earlier groups to the new maximum
+      const float sc = __builtin_amdgcn_exp2f(m - mc);
+      acc *= sc;
+      l *= sc;
+    }
+    m = mc;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (mv[u] == NEG_INF) continue;
+      const float f = __builtin_amdgcn_exp2f(mv[u] - m);
+      acc += f * ov[u];
+      l += f * lv[u];
+    }
   }
   out[(((size_t)ag * a.rows + i) * Hq + hq) * AD + d] = acc / l;
 }
