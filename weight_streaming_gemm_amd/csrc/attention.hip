@@ -61,6 +61,31 @@ __device__ __forceinline__ w32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_bit_cast(w32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// v of the lane that the data-parallel-primitive control CTRL picks within the
+// lane's row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// maximum and sum over the 16 lanes of a row, the same in every lane: lanes
+// paired as lane ^ 1, lane ^ 2 (quad permutations), then the other quad of the
+// half row and the other half of the row (mirrors).  The sum is associated as
+// ((q0 + q1) + (q2 + q3)) over the four quads' sums in every lane.
+__device__ __forceinline__ float row16_max(float v) {
+  float y = row_dpp<0xB1>(v); v = y > v ? y : v;      // quad_perm [1, 0, 3, 2]
+  y = row_dpp<0x4E>(v); v = y > v ? y : v;            // quad_perm [2, 3, 0, 1]
+  y = row_dpp<0x141>(v); v = y > v ? y : v;           // row_half_mirror
+  y = row_dpp<0x140>(v); v = y > v ? y : v;           // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_dpp<0xB1>(v);
+  v += row_dpp<0x4E>(v);
+  v += row_dpp<0x141>(v);
+  v += row_dpp<0x140>(v);
+  return v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -153,11 +178,7 @@ attn_split_kernel(AttnArgs a) {
           const int p = t0 + 16 * kt + nl;
           x[kt] = (qv < nq && p < p_end && p <= last) ? sc[rt][kt][i] * a.scale_log2 : NEG;
         }
-        float mx = x[0] > x[1] ? x[0] : x[1];
-        for (int off = 1; off < 16; off <<= 1) {
-          const float y = __shfl_xor(mx, off);
-          mx = y > mx ? y : mx;
-        }
+        const float mx = row16_max(x[0] > x[1] ? x[0] : x[1]);
         const float mnew = mrow[rt][i] > mx ? mrow[rt][i] : mx;
         float alpha = 1.f, sum = 0.f;
         if (mnew != NEG) {
@@ -169,7 +190,7 @@ attn_split_kernel(AttnArgs a) {
         } else {
           pv[rt][0][i] = pv[rt][1][i] = 0.f;
         }
-        for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+        sum = row16_sum(sum);
         mrow[rt][i] = mnew;
         lrow[rt][i] = lrow[rt][i] * alpha + sum;
         for (int dt = 0; dt < 8; ++dt) o[rt][dt][i] *= alpha;
