@@ -296,7 +296,7 @@ int qgemm_seq_destroy(qgemm_seq_t s);
  * qgemm_attention_workspace_size bytes, 16-byte aligned (partial results of
  * the sequence splits: each (agent, key/value head) cut into splits of a
  * multiple of 32 positions, as many in all as workgroups stay resident in one
- * round, 512).  Two kernels on `stream`.
+ * round, 256).  Two kernels on `stream`.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_EHIP. */
 int qgemm_attention_workspace_size(int agents, int rows, int kv_heads, int max_len, size_t *bytes);
 int qgemm_decode_attention(const void *q_bf16, const void *k_cache, const void *v_cache,

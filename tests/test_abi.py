@@ -87,9 +87,9 @@ def test_host_validation_codes():
     assert L.qgemm_seq_run_verify(None, None, None, 12, vp(4096), vp(4096), 2, vp(4096), vp(4096),
                                   None) == Q.QGEMM_EINVAL
     # decode attention: workspace arithmetic and shape checks (no GPU call)
-    # 4 agents x 8 heads: 16 splits each at most (512 in all), of 1440 positions (23003 / 16 rounded up to
-    # 32), so 16 splits
-    assert wsg.attention_workspace_size(4, 3, 8, 23000) == 4 * 8 * 16 * 32 * 130 * 4
+    # 4 agents x 8 heads: 8 splits each at most (256 in all), of 2880 positions (23003 / 8 rounded up to
+    # 32), so 8 splits
+    assert wsg.attention_workspace_size(4, 3, 8, 23000) == 4 * 8 * 8 * 32 * 130 * 4
     assert wsg.attention_workspace_size(1, 1, 1, 0) == 1 * 1 * 1 * 32 * 130 * 4
     assert L.qgemm_attention_workspace_size(4, 5, 8, 100, ctypes.byref(sz)) == Q.QGEMM_ESHAPE
     att = lambda **kw: L.qgemm_decode_attention(  # noqa: E731

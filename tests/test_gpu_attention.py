@@ -36,7 +36,7 @@ def _run(q, k, v, lengths, max_len):
 
 @pytest.mark.parametrize("rows", [1, 2, 3, 4])
 def test_attention_small_ragged_lengths(rows):
-    """Lengths around split boundaries (6 agents x 2 heads: splits of 64
+    """Lengths around split boundaries (6 agents x 2 heads: splits of 128
     positions, 1024 a boundary) and the 32-position steps, an empty cache, two
     key/value heads."""
     rng = np.random.default_rng(rows)

@@ -12,9 +12,9 @@ namespace qg {
 // step's rows, clamped to [0, max_len]); partials per (agent, head, split).
 constexpr int ATTN_HEAD_DIM = 128, ATTN_GROUP = 8, ATTN_MAX_ROWS = 4;
 // Sequence splits: as many workgroups as stay resident in one round on an
-// MI355X (256 CUs x 2 workgroups of the split kernel), each split a multiple of
-// the 32-position step.
-constexpr int ATTN_RESIDENT = 512, ATTN_SPLIT_UNIT = 32;
+// MI355X (256 CUs, one workgroup of the split kernel each: its registers leave
+// room for one wave per SIMD), each split a multiple of the 32-position step.
+constexpr int ATTN_RESIDENT = 256, ATTN_SPLIT_UNIT = 32;
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -11,17 +11,20 @@
 //
 // Split kernel: workgroup (s, h, a) takes positions [s split, (s + 1) split) of
 // agent a's cache for key/value head h, for all rows x 8 query heads of the
-// group at once (at most 32 query vectors: the rows of one 16 x 16 matrix-core
-// tile pair).  Each of its 4 waves takes every 4th tile of 32 positions:
-//   S = Q K^T       bf16 matrix-core products, fp32 (exact products)
-//   online softmax  fp32, base-2 exponent with log2(e) / sqrt(128) folded in
-//   O += P V        P as a binary16 head + tail pair (P in [0, 1]: the pair
-//                   holds it to about 2^-22), V converted bf16 -> binary16
-//                   (exact), two fp16 matrix-core products, fp32 accumulation
-// P and V reach their operand layouts through a small LDS area per wave (P from
-// the product layout to the A layout, V transposed).  The waves' (max, sum, O)
-// are merged in LDS and written as the split's partial result (O not yet
-// divided by the sum).  Combine kernel: per (agent, row, query head), the
+// group at once (at most 32 query vectors: the columns of two 16 x 16
+// matrix-core tiles).  Each of its 4 waves takes every 4th tile of 32 positions:
+//   S^T = K Q^T     bf16 matrix-core products, fp32 (exact products); a lane
+//                   holds 8 scores of one query vector
+//   online softmax  fp32, base-2 exponent with log2(e) / sqrt(128) folded in;
+//                   a vector's maximum and sum over its 4 lanes
+//   O^T += V^T P^T  P as a binary16 head + tail pair (P in [0, 1]: the pair
+//                   holds it to about 2^-22) straight from the softmax's
+//                   registers, V converted bf16 -> binary16 (exact), two fp16
+//                   matrix-core products, fp32 accumulation
+// V reaches its operand layout through a small LDS area per wave (transposed,
+// its positions placed in the k slots where the lanes hold P).  The waves'
+// (max, sum, O) are merged in LDS and written as the split's partial result (O
+// not yet divided by the sum).  Combine kernel: per (agent, row, query head), the
 // splits' partials rescaled to the common maximum and divided by the sum.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,10 +47,9 @@ constexpr int TK = 32;                  // positions per wave step
 constexpr int NWAVE = 4;
 constexpr uint32_t AOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
 
-// per-wave LDS: P's head and tail [32 rows][32 positions] and V^T [128 dims][32
-// positions], as binary16, rows padded to 80 bytes
-constexpr int PSTRIDE = 80, PBYTES = 32 * PSTRIDE, VBYTES = AD * PSTRIDE;
-constexpr int WAVE_LDS = 2 * PBYTES + VBYTES;
+// per-wave LDS: V^T [128 dims][32 positions] as binary16, rows padded to 80 bytes
+constexpr int PSTRIDE = 80, VBYTES = AD * PSTRIDE;
+constexpr int WAVE_LDS = VBYTES;
 // merge area: per wave (max, sum) of 32 rows and O [32][128] fp32
 constexpr int MERGE_LDS = NWAVE * (32 * 2 * 4 + 32 * AD * 4);
 constexpr int ATTN_LDS = (NWAVE * WAVE_LDS > MERGE_LDS) ? NWAVE * WAVE_LDS : MERGE_LDS;
@@ -71,11 +73,12 @@ __device__ __forceinline__ float row_dpp(float v) {
 // paired as lane ^ 1, lane ^ 2 (quad permutations), then the other quad of the
 // half row and the other half of the row (mirrors).  The sum is associated as
 // ((q0 + q1) + (q2 + q3)) over the four quads' sums in every lane.
+// (scores are never NaN: the maximum needs no NaN rule)
 __device__ __forceinline__ float row16_max(float v) {
-  float y = row_dpp<0xB1>(v); v = y > v ? y : v;      // quad_perm [1, 0, 3, 2]
-  y = row_dpp<0x4E>(v); v = y > v ? y : v;            // quad_perm [2, 3, 0, 1]
-  y = row_dpp<0x141>(v); v = y > v ? y : v;           // row_half_mirror
-  y = row_dpp<0x140>(v); v = y > v ? y : v;           // row_mirror
+  v = __builtin_fmaxf(v, row_dpp<0xB1>(v));           // quad_perm [1, 0, 3, 2]
+  v = __builtin_fmaxf(v, row_dpp<0x4E>(v));           // quad_perm [2, 3, 0, 1]
+  v = __builtin_fmaxf(v, row_dpp<0x141>(v));          // row_half_mirror
+  v = __builtin_fmaxf(v, row_dpp<0x140>(v));          // row_mirror
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
@@ -119,35 +122,33 @@ attn_split_kernel(AttnArgs a) {
       qa[rt][c] = __builtin_bit_cast(b16x8, load16(qr, base == AOOB ? AOOB : base + (32 * c + 8 * g) * 2));
   }
 
+  // softmax state of query vector 16 rt + nl (the same in the 4 lane groups)
   const float NEG = -__builtin_inff();
-  float mrow[2][4], lrow[2][4];
-  f32x4 o[2][8];
-  for (int rt = 0; rt < 2; ++rt)
-    for (int i = 0; i < 4; ++i) { mrow[rt][i] = NEG; lrow[rt][i] = 0.f; }
+  float mrow[2], lrow[2];
+  f32x4 o[2][8];                                            // O[16 rt + nl][16 dt + 4 g + i]
+  for (int rt = 0; rt < 2; ++rt) { mrow[rt] = NEG; lrow[rt] = 0.f; }
   for (int rt = 0; rt < 2; ++rt)
     for (int dt = 0; dt < 8; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint8_t* pbuf = lds + w * WAVE_LDS;                        // P head
-  uint8_t* plbuf = pbuf + PBYTES;                           // P tail
-  uint8_t* vbuf = plbuf + PBYTES;
+  uint8_t* vbuf = lds + w * WAVE_LDS;                        // V^T of the wave's step
   // byte offset of (position p, head h, dim d) in a cache
   auto coff = [&](int p, int d) { return (uint32_t)((((uint64_t)ag * a.cap + p) * a.Hkv + h) * AD + d) * 2; };
 
-  // loads of one 32-position step: K as B operands (position 16 kt + nl, dims
+  // loads of one 32-position step: K as A operands (position 16 kt + nl, dims
   // 32 c + 8 g .. + 7); V as 512 chunks of 16 bytes, lane (dc, m) taking
   // positions 2m and 2m + 1 of dim chunks 4 it + dc.  The next step's loads go
   // out as soon as this step's K (after S) and V (after its LDS copy) are used.
   const int vm = lane & 15, vdc = lane >> 4;
   b16x8 kb[2][4];
   w32x4 vc[8];
-  auto load_k = [&](int t0) {
+  auto load_k = [&](int t0) __attribute__((always_inline)) {
     for (int kt = 0; kt < 2; ++kt) {
       const int p = t0 + 16 * kt + nl;
       for (int c = 0; c < 4; ++c)
         kb[kt][c] = __builtin_bit_cast(b16x8, load16(kr, p < p_end ? coff(p, 32 * c + 8 * g) : AOOB));
     }
   };
-  auto load_v = [&](int t0) {
+  auto load_v = [&](int t0) __attribute__((always_inline)) {
     for (int it = 0; it < 4; ++it)
       for (int e = 0; e < 2; ++e) {
         const int pp = t0 + 2 * vm + e;
@@ -158,55 +159,57 @@ attn_split_kernel(AttnArgs a) {
   load_v(p_begin + TK * w);
   for (int t0 = p_begin + TK * w; t0 < p_end; t0 += TK * NWAVE) {
     const int tn = t0 + TK * NWAVE;                         // the next step (loads return zeros past p_end)
-    // S = Q K^T; lane (g, nl) holds S[16 rt + 4 g + i][16 kt + nl]
+    // S^T = K Q^T; lane (g, nl) holds S[16 rt + nl][16 kt + 4 g + i]: the lane's
+    // query vector is its column, the same in all the products below
     f32x4 sc[2][2];
     for (int rt = 0; rt < 2; ++rt)
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][c], kb[kt][c], acc, 0, 0, 0);
+        for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kt][c], qa[rt][c], acc, 0, 0, 0);
         sc[rt][kt] = acc;
       }
     load_k(tn);
-    // mask, scale, online softmax (row statistics shared by the 16 lanes of a group)
-    float pv[2][2][4];
-    for (int rt = 0; rt < 2; ++rt)
-      for (int i = 0; i < 4; ++i) {
-        const int qv = 16 * rt + 4 * g + i;
-        const int last = L + qv / GRP;                          // row qv / 8 sees positions <= last
-        float x[2];
-        for (int kt = 0; kt < 2; ++kt) {
-          const int p = t0 + 16 * kt + nl;
-          x[kt] = (qv < nq && p < p_end && p <= last) ? sc[rt][kt][i] * a.scale_log2 : NEG;
-        }
-        const float mx = row16_max(x[0] > x[1] ? x[0] : x[1]);
-        const float mnew = mrow[rt][i] > mx ? mrow[rt][i] : mx;
-        float alpha = 1.f, sum = 0.f;
-        if (mnew != NEG) {
-          alpha = __builtin_amdgcn_exp2f(mrow[rt][i] - mnew);
-          for (int kt = 0; kt < 2; ++kt) {
-            pv[rt][kt][i] = __builtin_amdgcn_exp2f(x[kt] - mnew);
-            sum += pv[rt][kt][i];
-          }
-        } else {
-          pv[rt][0][i] = pv[rt][1][i] = 0.f;
-        }
-        sum = row16_sum(sum);
-        mrow[rt][i] = mnew;
-        lrow[rt][i] = lrow[rt][i] * alpha + sum;
-        for (int dt = 0; dt < 8; ++dt) o[rt][dt][i] *= alpha;
-      }
-    // P (binary16) into the A layout, V (bf16 -> binary16) transposed
-    __asm__ volatile("" ::: "memory");
-    for (int rt = 0; rt < 2; ++rt)
+    // mask, scale, online softmax: a vector's 32 scores sit 8 per lane in the 4
+    // lanes nl, nl + 16, nl + 32, nl + 48
+    h16x8 pb[2], pl[2];                                     // P^T as B operands: head and tail
+    for (int rt = 0; rt < 2; ++rt) {
+      const int qv = 16 * rt + nl;
+      const int last = L + qv / GRP;                        // vector qv's row sees positions <= last
+      float x[2][4];
+      float mx = NEG;
       for (int kt = 0; kt < 2; ++kt)
         for (int i = 0; i < 4; ++i) {
-          const int off = (16 * rt + 4 * g + i) * PSTRIDE + (16 * kt + nl) * 2;
-          const _Float16 hi = (_Float16)pv[rt][kt][i];
-          *reinterpret_cast<_Float16*>(pbuf + off) = hi;
-          *reinterpret_cast<_Float16*>(plbuf + off) = (_Float16)(pv[rt][kt][i] - (float)hi);
+          const int p = t0 + 16 * kt + 4 * g + i;
+          x[kt][i] = (qv < nq && p < p_end && p <= last) ? sc[rt][kt][i] * a.scale_log2 : NEG;
+          mx = __builtin_fmaxf(mx, x[kt][i]);
         }
-    // V^T: one 4-byte write per dim holds positions 2m and 2m + 1 (16 lanes
-    // write 64 contiguous bytes of a row)
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = __builtin_fmaxf(mrow[rt], mx);
+      // a vector with no visible position yet keeps alpha = 1 and P = 0
+      const bool live = mnew != NEG;
+      const float alpha = live ? __builtin_amdgcn_exp2f(mrow[rt] - mnew) : 1.f;
+      float sum = 0.f;
+      for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 4; ++i) {
+          // k slot 8 g + 4 kt + i of the product holds position 16 kt + 4 g + i
+          const float pv = live ? __builtin_amdgcn_exp2f(x[kt][i] - mnew) : 0.f;
+          sum += pv;
+          const _Float16 hi = (_Float16)pv;
+          pb[rt][4 * kt + i] = hi;
+          pl[rt][4 * kt + i] = (_Float16)(pv - (float)hi);
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      mrow[rt] = mnew;
+      lrow[rt] = lrow[rt] * alpha + sum;
+      for (int dt = 0; dt < 8; ++dt) o[rt][dt] *= alpha;
+    }
+    // V^T (bf16 -> binary16) with its positions in the k slots of P^T: one 4-byte
+    // write per dim holds positions 2m and 2m + 1
+    __asm__ volatile("" ::: "memory");
+    const int pos = 2 * vm;
+    const int slot = pos < 16 ? 8 * (pos >> 2) + (pos & 3) : 8 * ((pos - 16) >> 2) + 4 + (pos & 3);
     for (int it = 0; it < 4; ++it) {
       const w32x4 a0 = vc[2 * it], a1 = vc[2 * it + 1];
       const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
@@ -215,21 +218,17 @@ attn_split_kernel(AttnArgs a) {
         const float f0 = (j & 1) ? bf16_hi(w0[j >> 1]) : bf16_lo(w0[j >> 1]);
         const float f1 = (j & 1) ? bf16_hi(w1[j >> 1]) : bf16_lo(w1[j >> 1]);
         typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<h16x2*>(vbuf + (d0 + j) * PSTRIDE + vm * 4) = h16x2{(_Float16)f0, (_Float16)f1};
+        *reinterpret_cast<h16x2*>(vbuf + (d0 + j) * PSTRIDE + slot * 2) = h16x2{(_Float16)f0, (_Float16)f1};
       }
     }
     load_v(tn);
     __asm__ volatile("" ::: "memory");       // one wave's LDS accesses run in order
-    h16x8 pa[2], pl[2];
-    for (int rt = 0; rt < 2; ++rt) {
-      pa[rt] = *reinterpret_cast<const h16x8*>(pbuf + (16 * rt + nl) * PSTRIDE + 16 * g);
-      pl[rt] = *reinterpret_cast<const h16x8*>(plbuf + (16 * rt + nl) * PSTRIDE + 16 * g);
-    }
+    // O^T += V^T P^T (P as head + tail)
     for (int dt = 0; dt < 8; ++dt) {
-      const h16x8 vb = *reinterpret_cast<const h16x8*>(vbuf + (16 * dt + nl) * PSTRIDE + 16 * g);
+      const h16x8 va = *reinterpret_cast<const h16x8*>(vbuf + (16 * dt + nl) * PSTRIDE + 16 * g);
       for (int rt = 0; rt < 2; ++rt) {
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], vb, o[rt][dt], 0, 0, 0);
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[rt], vb, o[rt][dt], 0, 0, 0);
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rt], o[rt][dt], 0, 0, 0);
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl[rt], o[rt][dt], 0, 0, 0);
       }
     }
     __asm__ volatile("" ::: "memory");       // the next step's LDS writes come after these reads
@@ -239,15 +238,14 @@ attn_split_kernel(AttnArgs a) {
   __syncthreads();                                          // the per-wave areas become the merge area
   float* mlw = reinterpret_cast<float*>(lds);               // [wave][32 rows][2]
   float* ow = mlw + NWAVE * 32 * 2;                         // [wave][32 rows][128]
-  for (int rt = 0; rt < 2; ++rt)
-    for (int i = 0; i < 4; ++i) {
-      const int qv = 16 * rt + 4 * g + i;
-      if (nl == 0) {
-        mlw[(w * 32 + qv) * 2] = mrow[rt][i];
-        mlw[(w * 32 + qv) * 2 + 1] = lrow[rt][i];
-      }
-      for (int dt = 0; dt < 8; ++dt) ow[(w * 32 + qv) * AD + 16 * dt + nl] = o[rt][dt][i];
+  for (int rt = 0; rt < 2; ++rt) {
+    const int qv = 16 * rt + nl;
+    if (g == 0) {
+      mlw[(w * 32 + qv) * 2] = mrow[rt];
+      mlw[(w * 32 + qv) * 2 + 1] = lrow[rt];
     }
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(ow + (w * 32 + qv) * AD + 16 * dt + 4 * g) = o[rt][dt];
+  }
   __syncthreads();
   const size_t item = ((size_t)ag * a.Hkv + h) * a.nsplit + s;
   for (int e = tid; e < nq * AD; e += NWAVE * 64) {
