@@ -112,7 +112,7 @@ attn_split_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t kr = rsrc(a.k, cache_bytes), vr = rsrc(a.v, cache_bytes);
   const __amdgpu_buffer_rsrc_t qr = rsrc(a.q, (uint64_t)a.A * rows * Hq * AD * 2);
 
-  // A operands of Q: row tile rt, k-step c: query vector 16 rt + nl (row i =
+  // B operands of Q: row tile rt, k-step c: query vector 16 rt + nl (row i =
   // vector / 8, head h * 8 + vector % 8), dims 32 c + 8 g .. + 7
   b16x8 qa[2][4];
   for (int rt = 0; rt < 2; ++rt) {
