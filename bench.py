@@ -408,7 +408,7 @@ def attention_report(seed: int, reps: int = 20):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)  # noqa: E731
     q = bf((A, rows, 8 * Hkv, d))
-    kv = [(t(bf((A, cap, Hkv, d))), t(bf((A, cap, Hkv, d)))) for _ in range(2)]
+    kv = [(t(bf((A, Hkv, cap, d))), t(bf((A, Hkv, cap, d)))) for _ in range(2)]     # head-major caches
     qd = t(q)
     ln = torch.tensor(lengths, dtype=torch.int32, device=dev)
     out = torch.empty((A, rows, 8 * Hkv, d), dtype=torch.float32, device=dev)
@@ -425,8 +425,9 @@ def attention_report(seed: int, reps: int = 20):
     us = e0.elapsed_time(e1) / reps * 1e3
     kv_bytes = sum((L + rows) * Hkv * d * 2 * 2 for L in lengths)
     # the oracle on agent 0 (a quarter of the work), all host cores via numpy
-    k0 = kv[0][0][:1].cpu().numpy().view(np.uint16)
-    v0 = kv[0][1][:1].cpu().numpy().view(np.uint16)
+    # (the oracle takes [agent, position, head, dim])
+    k0 = np.ascontiguousarray(kv[0][0][:1].cpu().numpy().view(np.uint16).transpose(0, 2, 1, 3))
+    v0 = np.ascontiguousarray(kv[0][1][:1].cpu().numpy().view(np.uint16).transpose(0, 2, 1, 3))
     t0 = time.perf_counter()
     at.decode_attention(q[:1], k0, v0, lengths[:1])
     cpu_s = time.perf_counter() - t0

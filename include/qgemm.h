@@ -285,7 +285,8 @@ int qgemm_seq_destroy(qgemm_seq_t s);
  * int32 [agents], clamped to [0, max_len]); their keys and values must already
  * be in the caches at those positions.  Row i sees positions 0 .. L_a + i.
  *   q_bf16   device bf16 [agents][rows][q_heads][head_dim]
- *   k_cache, v_cache  device bf16 [agents][cap][kv_heads][head_dim]
+ *   k_cache, v_cache  device bf16 [agents][kv_heads][cap][head_dim] (head-major:
+ *            each head's positions contiguous)
  *   out      device fp32 [agents][rows][q_heads][head_dim], overwritten:
  *            softmax(q.k / sqrt(head_dim)) . v, query head hq reading
  *            key/value head hq / (q_heads / kv_heads)

@@ -20,10 +20,13 @@ def _bf(rng, shape, scale=1.0):
 
 
 def _run(q, k, v, lengths, max_len):
+    """q, k, v in the oracle's layout ([agent, position, head, dim] caches); the
+    entry point takes head-major caches ([agent, head, position, dim])."""
     import torch
     import weight_streaming_gemm_amd as wsg
     A, rows, Hq, d = q.shape
     Hkv = k.shape[2]
+    k, v = k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3)
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)  # noqa: E731
     out = torch.full((A, rows, Hq, d), float("nan"), dtype=torch.float32, device=dev)

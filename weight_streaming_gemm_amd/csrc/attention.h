@@ -8,7 +8,7 @@
 namespace qg {
 
 // Decode attention of the agents' step rows (attention.hip).  q [A][rows][8 Hkv][128],
-// caches [A][cap][Hkv][128] (bf16), lengths [A] (cached positions before the
+// caches [A][Hkv][cap][128] (bf16), lengths [A] (cached positions before the
 // step's rows, clamped to [0, max_len]); partials per (agent, head, split).
 constexpr int ATTN_HEAD_DIM = 128, ATTN_GROUP = 8, ATTN_MAX_ROWS = 4;
 // Sequence splits: as many workgroups as stay resident in one round on an

@@ -132,7 +132,8 @@ attn_split_kernel(AttnArgs a) {
 
   uint8_t* vbuf = lds + w * WAVE_LDS;                        // V^T of the wave's step
   // byte offset of (position p, head h, dim d) in a cache
-  auto coff = [&](int p, int d) { return (uint32_t)((((uint64_t)ag * a.cap + p) * a.Hkv + h) * AD + d) * 2; };
+  // (head-major: a head's positions are contiguous, a step's K or V one 8 KB run)
+  auto coff = [&](int p, int d) { return (uint32_t)((((uint64_t)ag * a.Hkv + h) * a.cap + p) * AD + d) * 2; };
 
   // loads of one 32-position step: K as A operands (position 16 kt + nl, dims
   // 32 c + 8 g .. + 7); V as 512 chunks of 16 bytes, lane (dc, m) taking

@@ -160,10 +160,10 @@ def attention_workspace_size(agents: int, rows: int, kv_heads: int, max_len: int
 
 
 def decode_attention(q, k_cache, v_cache, lengths, out, workspace, max_len: int, stream=None):
-    """q [A, rows, Hq, 128], caches [A, cap, Hkv, 128] (bf16 bit patterns on the device),
+    """q [A, rows, Hq, 128], caches [A, Hkv, cap, 128] (bf16 bit patterns on the device),
     lengths [A] int32 on the device, out [A, rows, Hq, 128] fp32."""
     A, rows, Hq, d = q.shape
-    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().qgemm_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths), A, rows, Hq, Hkv, d,
                                         cap, max_len, _ptr(out), _ptr(workspace), nbytes, _stream(stream)),
