@@ -37,7 +37,9 @@
  *     overwritten).  x enters the matrix cores as binary16: values with
  *     2^-17 <= |x| <= 65504 (and zero) are exact there; smaller magnitudes are
  *     rounded to a multiple of 2^-24 and larger ones are outside the supported
- *     range (they become infinities).
+ *     range (they become infinities).  Sums of x over 32-wide sub-blocks (used
+ *     for the min term) are kept in fp32, so every x in that range is served,
+ *     whatever its neighbours.
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -104,6 +106,9 @@ typedef struct {
                                sums cross workgroups); 0: equal ranges (stream-K) */
     int k_chunks;           /* K split in this many chunks (when a tile row of
                                activations does not fit in LDS); 1: whole K */
+    int min_term_sums;      /* 1: the min term dmin * sum_s m_s X_s is formed from fp32
+                               sums X_s of x over each 32-wide sub-block (staged once
+                               per block); 0: from the activations at every step */
 } qgemm_info;
 
 /* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights

@@ -48,6 +48,33 @@ void mfma_16x16x32(const f16x8* a, const f16x8* b, f32x4* c) {
   for (int l = 0; l < 64; ++l) c[l] = out[l];
 }
 
+// D = A x B + C on a 16 x 16 tile with K = 4 (fp32 in, fp32 out); per lane:
+// a[l] = A[l % 16][l / 16], b[l] = B[l / 16][l % 16], d[l][v] = D[4 (l / 16) + v][l % 16]
+void mfma_16x16x4_f32(const float* a, const float* b, f32x4* c) {
+  f32x4 out[64];
+  for (int l = 0; l < 64; ++l)
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * (l / 16) + v, j = l % 16;
+      double s = c[l][v];
+      for (int k = 0; k < 4; ++k) s += (double)a[16 * k + i] * (double)b[16 * k + j];
+      out[l][v] = (float)s;
+    }
+  for (int l = 0; l < 64; ++l) c[l] = out[l];
+}
+
+// the min term of a block from fp32 sub-block sums: xs[l] = (X_2g, X_2g+1) of
+// lane l's row, the mins of lane l's output from c[l]; two products of depth 4
+void min_term_f32(const float (*xs)[2], const WConst* c, f32x4* ms) {
+  for (int h = 0; h < 2; ++h) {
+    float a[64], b[64];
+    for (int l = 0; l < 64; ++l) {
+      a[l] = xs[l][h];
+      b[l] = min_operand(c[l], h);
+    }
+    mfma_16x16x4_f32(a, b, ms);
+  }
+}
+
 void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
   int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
   for (int64_t ns = 0; ns < NS; ++ns)
@@ -106,8 +133,8 @@ void prefill_image(const uint16_t* x, int R, int64_t KB, int MT, int64_t mt, std
             s1 += bitcast<float>(v[i] << 16);
             s1 += bitcast<float>(v[i] & 0xFFFF0000u);
           }
-          const f16x8 sv = build_s(s0, s1);
-          memcpy(img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, rt)) + lane * 16, &sv, 16);
+          const float sv[4] = {s0, s1, 0.f, 0.f};
+          memcpy(img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, rt)) + lane * 16, sv, 16);
         }
 }
 
@@ -115,13 +142,14 @@ int64_t x_slot_of_emu(int64_t j, int64_t j0, int64_t KB) { return (j - j0 + KB) 
 
 // Activation staging of one range: the kernel's x_load / x_store, slot b <-
 // block (j0 + b) mod KB for b < nslots; slot layout [b][t][gg][r < R] of
-// 16-byte A operands, and per (b, gg, r) the min-term operand from the sums of
-// sub-blocks 2 gg and 2 gg + 1.
+// 16-byte A operands, and per (b, gg, r) the fp32 sums of sub-blocks 2 gg and
+// 2 gg + 1.
+struct Sum2 { float v[2]; };
 void convert_x(const uint16_t* x, int R, int64_t K, int64_t jbase, int64_t kbv, int64_t j0, int64_t nslots,
-               std::vector<f16x8>& slots, std::vector<f16x8>& sums) {
+               std::vector<f16x8>& slots, std::vector<Sum2>& sums) {
   const int64_t KB = kbv;   // blocks of the step order's tile (a chunk's with K in chunks)
   slots.assign((size_t)nslots * 8 * 4 * R, f16x8{});
-  sums.assign((size_t)nslots * 4 * R, f16x8{});
+  sums.assign((size_t)nslots * 4 * R, Sum2{});
   for (int64_t b = 0; b < nslots; ++b)
     for (int r = 0; r < R; ++r)
       for (int gg = 0; gg < 4; ++gg)
@@ -152,7 +180,7 @@ void convert_x(const uint16_t* x, int R, int64_t K, int64_t jbase, int64_t kbv, 
           p0[t] = ((f(lo[0]) + f(lo[1])) + f(lo[2])) + f(lo[3]);
           p1[t] = ((f(lo[32]) + f(lo[33])) + f(lo[34])) + f(lo[35]);
         }
-        sums[(size_t)(b * 4 + gg) * R + r] = build_s(tree8(p0), tree8(p1));
+        sums[(size_t)(b * 4 + gg) * R + r] = Sum2{{tree8(p0), tree8(p1)}};
       }
 }
 
@@ -164,8 +192,8 @@ f16x8 a_operand(const std::vector<f16x8>& slots, int R, int64_t b, int rt, int t
   if (r >= R) r = R - 1;
   return slots[(size_t)((b * 8 + t) * 4 + gg) * R + r];
 }
-// the min-term A operand of lane (row tile rt, lane) from slot b
-f16x8 s_operand(const std::vector<f16x8>& sums, int R, int64_t b, int rt, int lane) {
+// the sub-block sums of lane (row tile rt, lane)'s row from slot b
+Sum2 s_operand(const std::vector<Sum2>& sums, int R, int64_t b, int rt, int lane) {
   int r = rt * 16 + (lane & 15);
   const int gg = lane >> 4;
   if (r >= R) r = R - 1;
@@ -176,7 +204,7 @@ f16x8 s_operand(const std::vector<f16x8>& sums, int R, int64_t b, int rt, int la
 // slot b): the kernel's compute() for its NT sub-tiles and all 64 lanes,
 // accumulating into acc[NT][RT][64].
 void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int64_t NS, int64_t j, int64_t KB,
-               const std::vector<f16x8>& slots, const std::vector<f16x8>& sums, int R, int64_t b, int RT,
+               const std::vector<f16x8>& slots, const std::vector<Sum2>& sums, int R, int64_t b, int RT,
                bool msum, f32x4* acc) {
   for (int u = 0; u < NT; ++u) {
     const int64_t ns = ns0 + u;
@@ -194,15 +222,19 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
         memset(qd[lane], 0, sizeof(qd[lane]));   // loads past the end return zeros
       }
       c[lane] = header_consts(h[0], h[1], h[2], h[3], lane >> 4);
-      bm[lane] = msum ? build_m(c[lane]) : build_m_full(c[lane]);
+      bm[lane] = build_m_full(c[lane]);
     }
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 ds[64], ms[64];
       for (int l = 0; l < 64; ++l) ds[l] = ms[l] = f32x4{0, 0, 0, 0};
       if (msum) {
-        f16x8 sv[64];
-        for (int lane = 0; lane < 64; ++lane) sv[lane] = s_operand(sums, R, b, rt, lane);
-        mfma_16x16x32(sv, bm, ms);
+        float sv[64][2];
+        for (int lane = 0; lane < 64; ++lane) {
+          const Sum2 sp = s_operand(sums, R, b, rt, lane);
+          sv[lane][0] = sp.v[0];
+          sv[lane][1] = sp.v[1];
+        }
+        min_term_f32(sv, c, ms);
       }
       for (int tt = 0; tt < 8; ++tt) {
         f16x8 av[64], bb[64];
@@ -283,7 +315,8 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
   const size_t tile_f4 = (size_t)NT * RT * 64;            // f32x4 per wave piece (one column of a tile)
   std::vector<f32x4> part((size_t)Vslots * tile_f4, f32x4{NAN, NAN, NAN, NAN});
   std::vector<uint32_t> cnt((size_t)Tmax, 0);
-  std::vector<f16x8> xslots, xsums;
+  std::vector<f16x8> xslots;
+  std::vector<Sum2> xsums;
   std::mt19937_64 rng(order_seed);
   for (int g = 0; g < G; ++g) {
     EmuGemm& e = gs[(size_t)g];
@@ -511,13 +544,15 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
                   }
                 }
               for (int rt = 0; rt < RTW; ++rt) {
-                f16x8 sx[64];
-                memcpy(sx, img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, wm * RTW + rt)), 1024);
+                float sx4[64][4], sx[64][2];
+                memcpy(sx4, img.data() + pf_chunk_off(m, j, KB, MT, pf_sum_chunk(MT, wm * RTW + rt)), 1024);
+                for (int lane = 0; lane < 64; ++lane) {
+                  sx[lane][0] = sx4[lane][0];
+                  sx[lane][1] = sx4[lane][1];
+                }
                 for (int u = 0; u < PF_U; ++u) {
-                  f16x8 bm[64];
-                  for (int lane = 0; lane < 64; ++lane) bm[lane] = build_m(c[u][lane]);
                   f32x4 ms[64] = {};
-                  mfma_16x16x32(sx, bm, ms);
+                  min_term_f32(sx, c[u], ms);
                   for (int lane = 0; lane < 64; ++lane)
                     for (int i = 0; i < 4; ++i) {
                       acc[rt][u][lane][i] = std::fma(c[u][lane].d, ds[rt][u][lane][i], acc[rt][u][lane][i]);

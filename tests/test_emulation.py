@@ -50,6 +50,40 @@ def test_gemm_data_flow_matches_oracle(orc, N, K, R, NT, NW, V, msum):
     assert m["rel_l2"] < 2e-6
 
 
+def _bf16_bits(v: float) -> int:
+    return int(np.array([v], np.float32).view(np.uint32)[0] >> 16)
+
+
+@pytest.mark.parametrize("big", [4096.0, 65280.0])
+@pytest.mark.parametrize("msum", [1, 0])
+def test_large_subblock_sums(orc, big, msum):
+    """Sub-blocks of 32 large activations: their sums (32 x 4096 = 131072, or
+    32 x 65280, the largest bf16 below binary16's limit) are far beyond
+    binary16's range.  The min term keeps them in fp32, so both forms of the
+    min term stay finite and match the oracle."""
+    N, K, R = 48, 1024, 12
+    canon = synth.matrix_rows(0, 3, N, K)
+    x = synth.x_bf16(0, 5, R, K).copy()
+    x[0, 32:64] = _bf16_bits(big)                 # sub-block 1 of block 0, row 0
+    x[5, 256 + 96:256 + 128] = _bf16_bits(-big)   # sub-block 3 of block 1, row 5
+    x[11, 1024 - 32:] = _bf16_bits(big)           # the last sub-block, the last row
+    y = emu.stream(canon, N, K, x, NT=1, NW=8, V=2, msum=msum)
+    assert np.isfinite(y).all()
+    assert_parity(y, orc.gemm(canon, N, K, x), f"big={big} msum={msum}")
+
+
+def test_large_subblock_sums_row_tiled(orc):
+    """The row-tiled kernel's activation image holds the same fp32 sums."""
+    N, K, R = 80, 512, 40
+    canon = synth.matrix_rows(0, 4, N, K)
+    x = synth.x_bf16(0, 6, R, K).copy()
+    x[3, 0:32] = _bf16_bits(65280.0)
+    x[39, 480:512] = _bf16_bits(-4096.0)
+    y = emu.prefill(canon, N, K, x)
+    assert np.isfinite(y).all()
+    assert_parity(y, orc.gemm(canon, N, K, x), "row-tiled sums")
+
+
 def test_edge_blocks_emulated(orc):
     N, K, R = 64, 1024, 24
     canon = synth.matrix_rows(4, 0, N, K, edge_mode=1)

@@ -1,7 +1,10 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
-times (R rows, automatic kernel choice).  The oracle recomputes sampled outputs
-one by one (regenerating only the sampled weight rows); the output head's row
-argmax is checked over all 151936 outputs."""
+times (R rows, automatic kernel choice).  The layer's four GEMMs and the output
+head are compared with the oracle on every output; the full 257-GEMM pass runs
+through the benchmark's own call (graph-replayed sequence with the head's row
+argmax and the draft check) and is compared on every output of layers 0 and 63
+and of the head, on sampled outputs of the other GEMMs (the oracle recomputes
+only the sampled weight rows), and on the argmax and the emitted tokens."""
 from __future__ import annotations
 
 import numpy as np
@@ -37,42 +40,46 @@ def sample_ns(N, count, seed):
     return np.array(sorted(n for n in ns if 0 <= n < N))
 
 
-@pytest.mark.parametrize("R", [1, 3, 12, 24, 48])
+LAYER_RS = (1, 3, 12, 24, 48)
+_layer_refs = {}
+
+
+def layer_ref(orc, which):
+    """(matrix, canonical bytes, x of 48 rows, oracle y of 48 rows) of one of layer
+    0's GEMMs.  The activation rows of a smaller R are the first rows of the
+    48-row x, and the oracle's rows are independent (pinned bitwise), so its
+    first R rows are the reference at R."""
+    if which not in _layer_refs:
+        _layer_refs.clear()                    # keep one matrix's reference on the host at a time
+        seed = W.SEED_LAYER
+        m = {mm.name: mm for mm in W.layer_mats(0)}[which]
+        canon = fused_canon(seed, m)
+        x = synth.x_bf16(seed, W.X_STREAM[m.K], max(LAYER_RS), m.K)
+        print(f"oracle {which} N={m.N} K={m.K} R={max(LAYER_RS)}", flush=True)
+        _layer_refs[which] = (m, canon, x, orc.gemm(canon, m.N, m.K, x))
+    return _layer_refs[which]
+
+
 @pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
-def test_layer_matrix_sampled(orc, which, R):
-    seed = W.SEED_LAYER
-    m = {mm.name: mm for mm in W.layer_mats(0)}[which]
-    print(f"layer {which} N={m.N} K={m.K} R={R}", flush=True)
-    canon = fused_canon(seed, m)
-    packed = G.upload_packed(canon, m.N, m.K)
+def test_layer_matrix_all_outputs(orc, which):
+    """Every output of the full-size layer GEMMs at R = 1, 3, 12, 24 and 48 on the
+    automatic choice (streaming kernel, whole-tile and stream-K ranges, K chunks,
+    and from 24 rows the row-tiled kernel), and at R = 1 and 3 on the vector-unit
+    kernel."""
     import weight_streaming_gemm_amd as wsg
-    g = wsg.QGemm(packed, m.N, m.K, max_R=R)
-    x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
-    y = G.run(g, x)
-    ns = sample_ns(m.N, 96, R)
-    ref = orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, x)
-    assert_parity(y[:, ns], ref, f"{which} R={R} wgs={g.query(R)['workgroups']}")
-    assert np.isfinite(y).all()
-    g.close()
-
-
-@pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
-def test_layer_matrix_sampled_vector_unit(orc, which):
-    """The vector-unit kernel on the full layer shapes, R = 1 and 3."""
     from weight_streaming_gemm_amd import qgemm as Q
-    import weight_streaming_gemm_amd as wsg
-    seed = W.SEED_LAYER
-    m = {mm.name: mm for mm in W.layer_mats(0)}[which]
-    canon = fused_canon(seed, m)
+    m, canon, x48, ref48 = layer_ref(orc, which)
     packed = G.upload_packed(canon, m.N, m.K)
-    g = wsg.QGemm(packed, m.N, m.K, max_R=4)
+    g = wsg.QGemm(packed, m.N, m.K, max_R=max(LAYER_RS))
+    for R in LAYER_RS:
+        info = g.query(R)
+        print(f"layer {which} N={m.N} K={m.K} R={R} path={info['path']} wgs={info['workgroups']} "
+              f"chunks={info['k_chunks']} sums={info['min_term_sums']}", flush=True)
+        y = G.run(g, x48[:R])
+        assert_parity(y, ref48[:R], f"{which} R={R} path={info['path']}")
     for R in (1, 3):
-        print(f"valu layer {which} N={m.N} K={m.K} R={R}", flush=True)
-        x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
-        y = G.run(g, x, path=Q.PATH_VALU)
-        ns = sample_ns(m.N, 96, R)
-        ref = orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, x)
-        assert_parity(y[:, ns], ref, f"valu {which} R={R}")
+        print(f"layer {which} R={R} vector-unit kernel", flush=True)
+        assert_parity(G.run(g, x48[:R], path=Q.PATH_VALU), ref48[:R], f"valu {which} R={R}")
     g.close()
 
 
@@ -100,8 +107,8 @@ def test_vector_unit_k_chunks_sampled(orc):
 def test_ragged_schedule_sampled_steps(orc):
     """The agent schedule (R_t = 3 a_t, fresh activations with 1 % outliers per
     step) through one graph-mode sequence over layer 0's GEMMs: R changes from
-    step to step; sampled outputs of every step are checked, and a repeated step
-    gives the same bits."""
+    step to step; every output of every checked step is compared with the oracle,
+    and a repeated step gives the same bits."""
     import torch
     import weight_streaming_gemm_amd as wsg
     seed = W.SEED_RAGGED
@@ -129,9 +136,7 @@ def test_ragged_schedule_sampled_steps(orc):
             continue
         first[t] = got
         for i, m in enumerate(mats):
-            ns = sample_ns(m.N, 48, t)
-            canon_rows = canons[i].reshape(m.N, -1)[ns].ravel()
-            assert_parity(got[i][:, ns], orc.gemm(canon_rows, len(ns), m.K, xs_np[i]), f"ragged t={t} {m.name}")
+            assert_parity(got[i], orc.gemm(canons[i], m.N, m.K, xs_np[i]), f"ragged t={t} {m.name}")
     seq.close()
     for g in gs:
         g.close()
@@ -200,3 +205,72 @@ def test_shared_tile_counters_rearm_over_repeats(orc):
     ns = sample_ns(m.N, 64, 1)
     assert_parity(first[:, ns], orc.gemm(sampled_rows(5, m, ns), len(ns), m.K, x), "down repeats")
     g.close()
+
+
+def test_full_pass_run_verify(orc):
+    """The benchmark's timed call itself: all 257 GEMMs of the pass resident (17.99
+    GB), one graph-replayed qgemm_seq_run_verify at 12 rows (4 agents x (token + 2
+    drafts)) with the head's row argmax and the greedy draft check.  Every output
+    of layers 0 and 63 and of the head is compared with the oracle, 16 sampled
+    outputs of every other GEMM, the argmax exactly, and the emitted tokens with
+    the oracle's greedy check.  The drafts are made from the oracle's argmax so
+    that agents accept two, one and none of their drafts."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    seed, R, D = W.SEED_PASS, W.R_DEFAULT, W.ROWS_PER_AGENT - 1
+    mats = W.full_pass()
+    print(f"full pass: {len(mats)} GEMMs, R={R}", flush=True)
+    gs, packs = [], []
+    for i, m in enumerate(mats):
+        packed = G.upload_packed(fused_canon(seed, m), m.N, m.K)
+        packs.append(packed)
+        gs.append(wsg.QGemm(packed, m.N, m.K, max_R=R))
+        if i % 64 == 0:
+            print(f"  resident {i + 1}/{len(mats)}", flush=True)
+    xs = {K: synth.x_bf16(seed, sid, R, K) for K, sid in W.X_STREAM.items()}
+    xd = {K: G.to_dev(x) for K, x in xs.items()}
+    ys = [torch.empty((R, m.N), dtype=torch.float32, device="cuda") for m in mats]
+    head = mats[-1]
+    print("oracle: head", flush=True)
+    head_canon = fused_canon(seed, head)
+    ref_head = orc.gemm(head_canon, head.N, head.K, xs[head.K])
+    ref_idx = orc.argmax_rows(ref_head)
+    A = R // (D + 1)
+    drafts = np.zeros((A, D), np.int32)
+    for a in range(A):
+        base = a * (D + 1)
+        accept = max(0, D - a)                       # agent 0 accepts 2, agent 1 one, agents 2, 3 none
+        for i in range(D):
+            drafts[a, i] = ref_idx[base + i] if i < accept else (ref_idx[base + i] + 1) % head.N
+    tok_ref, n_ref = orc.verify_greedy(ref_idx, drafts, D)
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    tokens = torch.empty((A, D + 1), dtype=torch.int32, device="cuda")
+    n_new = torch.empty(A, dtype=torch.int32, device="cuda")
+    seq = wsg.Seq(gs)
+    seq.run_verify([xd[m.K] for m in mats], ys, R, idx, G.to_dev(drafts), D, tokens, n_new)
+    torch.cuda.synchronize()
+    print("pass done; comparing", flush=True)
+    full = set(range(4)) | set(range(4 * 63, 4 * 64)) | {len(mats) - 1}
+    for i, m in enumerate(mats):
+        y = ys[i].cpu().numpy()
+        assert np.isfinite(y).all(), f"GEMM {i} {m.name}: non-finite output"
+        if i == len(mats) - 1:
+            assert_parity(y, ref_head, "head")
+        elif i in full:
+            print(f"oracle: GEMM {i} ({m.name}), all outputs", flush=True)
+            assert_parity(y, orc.gemm(fused_canon(seed, m), m.N, m.K, xs[m.K]), f"GEMM {i} {m.name}")
+        else:
+            ns = sample_ns(m.N, 16, i)
+            assert_parity(y[:, ns], orc.gemm(sampled_rows(seed, m, ns), len(ns), m.K, xs[m.K]),
+                          f"GEMM {i} {m.name} sampled")
+    top2 = np.sort(ref_head, axis=1)[:, -2:]
+    err = np.abs(ys[-1].cpu().numpy() - ref_head).max()
+    assert (top2[:, 1] - top2[:, 0] > 10 * err).all(), "an argmax is ambiguous within the error bound"
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.array_equal(tokens.cpu().numpy(), tok_ref) and np.array_equal(n_new.cpu().numpy(), n_ref)
+    assert sorted(n_ref.tolist()) == [1, 1, 2, 3]
+    seq.close()
+    for g in gs:
+        g.close()
+    del packs, ys
+    torch.cuda.empty_cache()

@@ -171,6 +171,37 @@ def test_plan_kinds_are_exercised():
     assert info[(16384, 2048, 64)]["k_chunks"] == 4
 
 
+def _bf16_bits(v: float) -> int:
+    return int(np.array([v], np.float32).view(np.uint32)[0] >> 16)
+
+
+@pytest.mark.parametrize("N,K,R,path", [
+    (32768, 1024, 12, "mfma"),    # streaming kernel, min term from the sub-block sums
+    (4096, 1024, 12, "mfma"),     # streaming kernel, min term per step
+    (4096, 1024, 3, "valu"),      # vector-unit kernel (always the sums)
+    (4096, 1024, 40, "tiled"),    # row-tiled kernel (sums in its activation image)
+])
+def test_large_subblock_sums(orc, N, K, R, path):
+    """Sub-blocks of 32 activations at 4096 and at 65280 (the largest bf16 below
+    binary16's limit): their sums leave binary16's range; every kernel path
+    must stay finite and match the oracle."""
+    from weight_streaming_gemm_amd import qgemm as Q
+    _flush(f"large sub-block sums N={N} K={K} R={R} path={path}")
+    canon, g = G.make(3, 7, N, K, max_R=max(R, 24))
+    pid = {"mfma": Q.PATH_MFMA, "valu": Q.PATH_VALU, "tiled": Q.PATH_TILED}[path]
+    info = g.query(R, pid)
+    if path == "mfma":
+        assert info["min_term_sums"] == (1 if N == 32768 else 0), info
+    x = synth.x_bf16(3, 8, R, K).copy()
+    x[0, 32:64] = _bf16_bits(4096.0)
+    x[R - 1, K - 32:] = _bf16_bits(65280.0)
+    x[R // 2, 256 + 96:256 + 128] = _bf16_bits(-65280.0)
+    y = G.run(g, x, path=pid)
+    assert np.isfinite(y).all()
+    assert_parity(y, orc.gemm(canon, N, K, x), f"N={N} K={K} R={R} path={path}")
+    g.close()
+
+
 def test_edge_blocks_large_R(orc):
     N, K = 512, 2048
     canon, g = G.make(4, 0, N, K, max_R=48, edge_mode=1)

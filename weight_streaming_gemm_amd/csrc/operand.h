@@ -4,8 +4,9 @@
 //
 // For lane group g (sub-blocks 2g, 2g+1 of a block) the B operand element e of
 // step t is sc_{2g + (e & 1)} * q_k for k = operand_k(g, t, e) (layout.h): an
-// integer <= 63 * 15 = 945, exact in binary16.  The min term is one more
-// product per block, of the sub-block sums of x with the mins (build_m, build_s).
+// integer <= 63 * 15 = 945, exact in binary16.  The min term is either a
+// product of the activation operands with the mins (build_m_full), or two fp32
+// products of the fp32 sub-block sums of x with the mins (min_operand).
 #pragma once
 #include <stdint.h>
 
@@ -93,15 +94,12 @@ QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
 }
 
 // The min term of a block, sum over k of m_sub(k) x_k, is sum over s of m_s X_s
-// with X_s the sum of x over sub-block s: one matrix-core product per block.
-// Lane group g holds sub-blocks 2g and 2g+1; each sum is split into a binary16
-// head and tail, X = hi + lo (exact to 2^-22 relative), and the operands are
-//   A (per row):    (hi(X_2g), hi(X_2g+1), lo(X_2g), lo(X_2g+1), 0, 0, 0, 0)
-//   B (per output): (m_2g,     m_2g+1,     m_2g,     m_2g+1,     0, 0, 0, 0)
-QG_HD f16x8 build_m(const WConst& c) {
-  const _Float16 z = (_Float16)0.0f;
-  return f16x8{c.m[0], c.m[1], c.m[0], c.m[1], z, z, z, z};
-}
+// with X_s the sum of x over sub-block s.  The sums stay in fp32: a bf16 sum of
+// 32 values reaches 32 * 65504, far beyond binary16's range, so they enter two
+// fp32 matrix-core products of depth 4 (v_mfma_f32_16x16x4_f32).  In product h
+// (0, 1) lane group g contributes X_{2g+h} of its row (A) and m_{2g+h} of its
+// output (B); the two products together cover the 8 sub-blocks.
+QG_HD float min_operand(const WConst& c, int h) { return (float)c.m[h]; }
 // Without the sums, the min term is the product of each step's activation
 // operand with B = (m_2g, m_2g+1) in every pair (eight products per block).
 QG_HD f16x8 build_m_full(const WConst& c) {
@@ -111,14 +109,6 @@ QG_HD f16x8 build_m_full(const WConst& c) {
 // the sum of the 8 per-step partial sums of a sub-block, in a fixed tree order
 QG_HD float tree8(const float p[8]) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-}
-
-// the A operand of the min-term product from the sums of sub-blocks 2g (s0) and 2g+1 (s1)
-QG_HD f16x8 build_s(float s0, float s1) {
-  const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
-  const _Float16 l0 = (_Float16)(s0 - (float)h0), l1 = (_Float16)(s1 - (float)h1);
-  const _Float16 z = (_Float16)0.0f;
-  return f16x8{h0, h1, l0, l1, z, z, z, z};
 }
 
 // Eight activations of one matrix-core A operand from two runs of four bf16

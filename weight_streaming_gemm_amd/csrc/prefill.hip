@@ -11,8 +11,9 @@
 //   y[r, n] = sum_k w[n, k] x[r, k],  w[n, k] = d sc_s q_k - dmin m_s
 //
 // is computed per 256-weight block exactly as in the streaming kernel:
-// ds = sum_k (sc_s q_k) x[r, k] and ms = sum_s m_s X_s on the fp16 matrix
-// cores (exact integer B operands, fp32 sums), then acc += d ds - dmin ms.
+// ds = sum_k (sc_s q_k) x[r, k] on the fp16 matrix cores (exact integer B
+// operands, fp32 sums) and ms = sum_s m_s X_s on the fp32 matrix cores (the
+// sub-block sums X_s kept in fp32), then acc += d ds - dmin ms.
 //
 // Work: one workgroup per (128-row tile, output tile of 32 WN), over the whole
 // of K (no split unless the grid is small, so every output is written once, in
@@ -20,7 +21,7 @@
 // the rows, WN along the outputs; a wave owns 64 rows (4 row tiles of 16) x 32
 // outputs (2 sub-tiles of 16): 8 accumulator tiles.  A first kernel converts x
 // once into the LDS image of every (128-row tile, block): binary16 operands in
-// the matrix-core lane layout plus the 8 sub-block sums per row (72 KiB).  The
+// the matrix-core lane layout plus the 8 fp32 sub-block sums per row (72 KiB).  The
 // main kernel copies each block's image straight into LDS with buffer loads
 // that write LDS directly (no registers, no vector instructions),
 // double-buffered: the next block's activations and weights are in flight
@@ -37,6 +38,7 @@ namespace qg {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 
@@ -139,9 +141,10 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
       }
     }
     for (int rt = 0; rt < PF_RT; ++rt) {
-      const f16x8 sx = *reinterpret_cast<const f16x8*>(X + pf_sum_chunk(MT, wm * PF_RT + rt) * PF_CHUNK + lane * 16);
+      const f32x2 sx = *reinterpret_cast<const f32x2*>(X + pf_sum_chunk(MT, wm * PF_RT + rt) * PF_CHUNK + lane * 16);
       for (int u = 0; u < PF_U; ++u) {
-        const f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(sx, build_m(c[u]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x4f32(sx.x, min_operand(c[u], 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(sx.y, min_operand(c[u], 1), ms, 0, 0, 0);
         for (int i = 0; i < 4; ++i) {
           acc[rt][u][i] = __builtin_fmaf(c[u].d, ds[rt][u][i], acc[rt][u][i]);
           acc[rt][u][i] = __builtin_fmaf(c[u].nmin, ms[i], acc[rt][u][i]);
@@ -185,8 +188,8 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
 // block j, at (m KB + j) * 9 MT KiB, chunk (row tile rt, step t) at 1 KiB (8 rt + t)
 // holds lane 16 g + r's binary16 A operand of row 16 (MT m + rt) + r (k = 256 j +
 // 64 g + 32 (e & 1) + 4 t + (e >> 1) for element e), and chunk 8 MT + rt the
-// sub-block sums of those rows (two per
-// lane group, as binary16 head and tail).  Rows past R are zeros.  One thread per
+// sub-block sums of those rows (lane 16 g + r: X_2g, X_2g+1 in fp32, then 8
+// zero bytes).  Rows past R are zeros.  One thread per
 // (m, j, rt, lane): it reads the row's 64 values of sub-blocks 2g, 2g + 1 (one
 // 128-byte line) and writes 8 operands and one sum entry.
 __global__ void __launch_bounds__(256)
@@ -217,7 +220,7 @@ prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, 
   float s0 = 0.f, s1 = 0.f;
   for (int c = 0; c < 4; ++c) s0 = sum8_bf16(v[c], s0);
   for (int c = 4; c < 8; ++c) s1 = sum8_bf16(v[c], s1);
-  *reinterpret_cast<f16x8*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) = build_s(s0, s1);
+  *reinterpret_cast<f32x4*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) = f32x4{s0, s1, 0.f, 0.f};
 }
 
 // y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order;

@@ -447,6 +447,7 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
     info->kernels = tp.S > 1 ? 3 : 2;
     info->k_chunks = (int)tp.S;
     info->workspace_bytes = tp.ws_bytes;
+    info->min_term_sums = 1;
     return QGEMM_OK;
   }
   info->path = p.path;
@@ -462,6 +463,7 @@ int qgemm_query(qgemm_t h, int R, int path, qgemm_info* info) {
   info->wave_columns = p.nwn;
   info->whole_tile_ranges = p.aligned;
   info->k_chunks = (int)p.S;
+  info->min_term_sums = p.msum;
   return QGEMM_OK;
 }
 

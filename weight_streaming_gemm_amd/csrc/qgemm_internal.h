@@ -61,7 +61,7 @@ constexpr int LDS_BYTES = 160 * 1024;
 constexpr int LDS_RESERVED = 1024;              // flags
 inline constexpr int piece_bytes(int RT, int NT, int NW) { return NW * 2 * NT * RT * 1024; }
 inline constexpr int x_area_bytes(int RT, int NT, int NW) { return LDS_BYTES - LDS_RESERVED - piece_bytes(RT, NT, NW); }
-inline int x_slot_bytes(int R, bool msum) { return 8 * (64 * R + 16) + (msum ? 64 * R : 0); }
+inline int x_slot_bytes(int R, bool msum) { return 8 * (64 * R + 16) + (msum ? 32 * R : 0); }
 inline int x_slot_capacity(int R, int RT, int NT, int NW, bool msum) {
   return x_area_bytes(RT, NT, NW) / x_slot_bytes(R, msum);
 }

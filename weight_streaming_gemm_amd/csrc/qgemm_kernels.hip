@@ -33,6 +33,7 @@ namespace qg {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ WConst header_consts(u32x4 h, int g) { return header_consts(h.x, h.y, h.z, h.w, g); }
 
@@ -106,8 +107,8 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 //
 // Min term.  Either eight more matrix-core products per step with B = m_s
 // (MSUM = false), or, when a range uses each block for several steps, one
-// product per step of the sub-block sums of x, staged with the activations
-// (MSUM = true).  The vector-unit variant (VR = R <= 4 rows) replaces the
+// pair of fp32 products per step of the sub-block sums of x (kept in fp32),
+// staged with the activations (MSUM = true).  The vector-unit variant (VR = R <= 4 rows) replaces the
 // products by dot products on the vector units and always uses the sums.
 //
 // Streams.  At the start of a range the workgroup converts the activations of
@@ -218,7 +219,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
   const int XT = 64 * R + 16;                     // LDS bytes of one step's activations
   const int XS = 8 * XT;                          // offset of a block's sub-block sums
-  const int SB = XS + (MSUM ? 64 * R : 0);        // LDS bytes of one block's activations
+  const int SB = XS + (MSUM ? 8 * 4 * R : 0);     // LDS bytes of one block's activations
 
   // descriptor of GEMM g; fields of the device table are made explicitly
   // wave-uniform so that buffer resources built from them stay scalar
@@ -383,7 +384,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
         s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
         s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
         if (t == 0)
-          *reinterpret_cast<f16x8*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 16) = build_s(s0, s1);
+          *reinterpret_cast<f32x2*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 8) = f32x2{s0, s1};
         // one row at a time: few values live while the weight ring is in flight
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -454,17 +455,16 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       }
     }
     for (int r = 0; r < VR; ++r) {
-      const f16x8 sm = *reinterpret_cast<const f16x8*>(xlds + base + XS + (g4 * R + r) * 16);
-      // min term of the lane's two sub-blocks: m_2g (hi + lo of X_2g) + m_2g+1 (hi + lo of X_2g+1)
-      const float x0 = (float)sm[0] + (float)sm[2], x1 = (float)sm[1] + (float)sm[3];
-      const float mt = __builtin_fmaf((float)c.m[0], x0, (float)c.m[1] * x1);
+      // min term of the lane's two sub-blocks: m_2g X_2g + m_2g+1 X_2g+1
+      const f32x2 sm = *reinterpret_cast<const f32x2*>(xlds + base + XS + (g4 * R + r) * 8);
+      const float mt = __builtin_fmaf(min_operand(c, 0), sm.x, min_operand(c, 1) * sm.y);
       vacc[r] = __builtin_fmaf(c.d, ds[r], vacc[r]);
       vacc[r] = __builtin_fmaf(c.nmin, mt, vacc[r]);
     }
   };
 
-  // MSUM: the min term from the staged sub-block sums (one product), else from
-  // the activation operands of the 8 steps (eight products)
+  // MSUM: the min term from the staged fp32 sub-block sums (two fp32 products),
+  // else from the activation operands of the 8 steps (eight products)
   auto compute = [&](const WStage<NT>& st, int slot) __attribute__((always_inline)) {
     constexpr bool msum = MSUM;
     WConst c[NT];
@@ -472,7 +472,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     f32x4 ds[NT][RT], ms[NT][RT];
     for (int u = 0; u < NT; ++u) {
       c[u] = header_consts(st.hd[u], g4);
-      bm[u] = msum ? build_m(c[u]) : build_m_full(c[u]);
+      if constexpr (!msum) bm[u] = build_m_full(c[u]);
       for (int rt = 0; rt < RT; ++rt) {
         ds[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         ms[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -497,9 +497,11 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     }
     if constexpr (msum)
       for (int rt = 0; rt < RT; ++rt) {
-        const f16x8 xsum = *reinterpret_cast<const f16x8*>(xlds + base + XS + xoff[rt]);
-        for (int u = 0; u < NT; ++u)
-          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xsum, bm[u], ms[u][rt], 0, 0, 0);
+        const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + XS + xoff[rt] / 2);
+        for (int u = 0; u < NT; ++u) {
+          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(c[u], 0), ms[u][rt], 0, 0, 0);
+          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(c[u], 1), ms[u][rt], 0, 0, 0);
+        }
       }
     // acc += d * ds - dmin * ms, two fused multiply-adds per element
     for (int u = 0; u < NT; ++u)

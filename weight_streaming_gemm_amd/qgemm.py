@@ -44,7 +44,8 @@ class Info(ctypes.Structure):
                 ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("steps", ctypes.c_int64),
                 ("kernels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("ranges", ctypes.c_int64),
                 ("waves_per_workgroup", ctypes.c_int), ("wave_columns", ctypes.c_int),
-                ("whole_tile_ranges", ctypes.c_int), ("k_chunks", ctypes.c_int)]
+                ("whole_tile_ranges", ctypes.c_int), ("k_chunks", ctypes.c_int),
+                ("min_term_sums", ctypes.c_int)]
 
 
 _lib = None
