@@ -61,7 +61,8 @@ typedef enum {
     QGEMM_ERANGE_R = -4,  /* R < 0, R > max_R of the handle, or max_R out of 1..QGEMM_MAX_R */
     QGEMM_ENOMEM = -5,    /* the library could not allocate its workspace */
     QGEMM_EHIP = -6,      /* a HIP call or kernel launch failed */
-    QGEMM_EPATH = -7      /* requested kernel path cannot serve this R */
+    QGEMM_EPATH = -7,     /* requested kernel path cannot serve this R */
+    QGEMM_ESCRATCH = -8   /* qgemm_run_static: the run needs more than its fixed scratch */
 } qgemm_status;
 
 /* Kernel paths (the R-dependent selection chooses between them). */
@@ -143,6 +144,28 @@ int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int
  * share its workspace: do not run one handle on two streams at once.
  * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_EHIP. */
 int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): qgemm_run
+ * without a handle, allocating nothing.  packed_dev holds the packed layout of
+ * an N x K matrix (qgemm_pack; borrowed for the call), x_bf16 [R x K] and y
+ * [R x N] as for qgemm_run; all three 16-byte aligned; 0 <= R <= QGEMM_MAX_R.
+ * Always the streaming matrix-core kernel (the row-tiled path's activation
+ * image would need an allocation), with the plan qgemm_run takes on that path:
+ * the same result bits.  Its partial output tiles and arrival counters live in
+ * a fixed device area of QGEMM_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; a run that would need more
+ * returns QGEMM_ESCRATCH (large R with stream-K partials on wide matrices).
+ * Enqueues two kernels on `stream`: one that zeroes the counters the run uses,
+ * then the GEMM.  Every call on one GPU shares that GPU's area: calls that
+ * overlap on one GPU (two streams, or two host threads) race and give wrong
+ * results.  The first call on a device reads the device's properties
+ * (synchronous, no allocation).
+ * Errors: QGEMM_EINVAL (NULL pointers), QGEMM_ESHAPE, QGEMM_EALIGN,
+ * QGEMM_ERANGE_R, QGEMM_ESCRATCH, QGEMM_EHIP. */
+#define QGEMM_STATIC_SCRATCH_BYTES (16u << 20)
+int qgemm_run_static(const void *packed_dev, int64_t N, int64_t K, const void *x_bf16, float *y,
+                     int R, void *stream);
 
 /* As qgemm_run with an explicit path (QGEMM_PATH_AUTO = qgemm_run).
  * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = wsg.status_string(code)
         assert s and s != "unknown status"
     assert wsg.status_string(-99) == "unknown status"
@@ -61,6 +61,16 @@ def test_host_validation_codes():
     assert L.qgemm_create(None, vp(4096), 16, 256, 12, 0) == Q.QGEMM_EINVAL
     assert L.qgemm_run(None, vp(4096), vp(4096), 1, None) == Q.QGEMM_EINVAL
     assert L.qgemm_run_path(None, vp(4096), vp(4096), 1, 2, None) == Q.QGEMM_EINVAL
+    # the allocation-free entry point rejects bad arguments before any HIP call
+    assert L.qgemm_run_static(None, 16, 256, vp(4096), vp(4096), 1, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_run_static(vp(4096), 16, 100, vp(4096), vp(4096), 1, None) == Q.QGEMM_ESHAPE
+    assert L.qgemm_run_static(vp(4096), 16, 256, vp(4096), vp(4096), 65, None) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_run_static(vp(4096), 16, 256, vp(4096), vp(4096), -1, None) == Q.QGEMM_ERANGE_R
+    assert L.qgemm_run_static(vp(4096), 16, 256, None, vp(4096), 1, None) == Q.QGEMM_EINVAL
+    assert L.qgemm_run_static(vp(4104), 16, 256, vp(4096), vp(4096), 1, None) == Q.QGEMM_EALIGN
+    assert L.qgemm_run_static(vp(4096), 16, 256, vp(4096), vp(4100), 1, None) == Q.QGEMM_EALIGN
+    assert L.qgemm_run_static(vp(4096), 16, 256, None, None, 0, None) == Q.QGEMM_OK      # R = 0: no-op
+    assert Q.STATIC_SCRATCH_BYTES == 16 << 20
     assert L.qgemm_run_prefill(None, vp(4096), vp(4096), 100, None, 0, None) == Q.QGEMM_EINVAL
     assert L.qgemm_prefill_workspace_size(None, 100, ctypes.byref(sz0 := ctypes.c_size_t())) == Q.QGEMM_EINVAL
     assert L.qgemm_dequantize(None, vp(4096), None) == Q.QGEMM_EINVAL

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -252,6 +253,34 @@ void fill_occupancy(int occ[5]) {
   for (int rt = 1; rt < 5; ++rt) occ[rt] = stream_occupancy(rt, subtiles_for(rt), waves_for(rt));
 }
 
+// Per-device facts for qgemm_run_static, gathered on its first call on a device
+// (with that device current) and kept: compute units, resident workgroups of
+// the streaming kernel, and the device address of the fixed scratch area.
+struct StaticDevice {
+  bool ready;
+  int cus;
+  int occ[5];
+  void* scratch;
+};
+
+int static_device(const StaticDevice** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static StaticDevice table[MAX_DEVICES] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return QGEMM_EHIP;
+  std::lock_guard<std::mutex> lock(mu);
+  StaticDevice& d = table[dev];
+  if (!d.ready) {
+    if (device_cus(&d.cus) != QGEMM_OK) return QGEMM_EHIP;
+    fill_occupancy(d.occ);
+    if (static_scratch_address(&d.scratch) != hipSuccess || !d.scratch) return QGEMM_EHIP;
+    d.ready = true;
+  }
+  *out = &d;
+  return QGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +295,7 @@ const char* qgemm_status_string(int status) {
     case QGEMM_ENOMEM: return "out of device memory";
     case QGEMM_EHIP: return "HIP call or kernel launch failed";
     case QGEMM_EPATH: return "kernel path cannot serve this row count";
+    case QGEMM_ESCRATCH: return "the run needs more than the fixed scratch area of qgemm_run_static";
     default: return "unknown status";
   }
 }
@@ -352,6 +382,50 @@ int qgemm_run_path(qgemm_t h, const void* x_bf16, float* y, int R, int path, voi
 
 int qgemm_run(qgemm_t h, const void* x_bf16, float* y, int R, void* stream) {
   return qgemm_run_path(h, x_bf16, y, R, QGEMM_PATH_AUTO, stream);
+}
+
+int qgemm_run_static(const void* packed_dev, int64_t N, int64_t K, const void* x_bf16, float* y, int R,
+                     void* stream) {
+  if (!packed_dev) return QGEMM_EINVAL;
+  if (!valid_shape(N, K)) return QGEMM_ESHAPE;
+  if (R < 0 || R > QGEMM_MAX_R) return QGEMM_ERANGE_R;
+  if (R == 0) return QGEMM_OK;
+  if (!x_bf16 || !y) return QGEMM_EINVAL;
+  if (!aligned16(packed_dev) || !aligned16(x_bf16) || !aligned16(y)) return QGEMM_EALIGN;
+  const StaticDevice* sd = nullptr;
+  if (static_device(&sd) != QGEMM_OK) return QGEMM_EHIP;
+  // a handle on the stack: borrowed weights, no workspace of its own
+  qgemm_handle h{};
+  h.magic = HANDLE_MAGIC;
+  h.packed = reinterpret_cast<const uint8_t*>(packed_dev);
+  h.N = N;
+  h.K = K;
+  h.KB = K / 256;
+  h.NS = padded_n(N) / 16;
+  h.max_R = R;
+  h.cus = sd->cus;
+  const Plan p = plan_stream(h.NS, h.KB, R, sd->cus, sd->occ);
+  if (!plan_fits(p)) return QGEMM_ESHAPE;
+  const size_t cnt_bytes = (p.cnt_bytes + 255) / 256 * 256;
+  if (cnt_bytes + p.part_bytes > STATIC_SCRATCH_BYTES) return QGEMM_ESCRATCH;
+  uint8_t* const base = reinterpret_cast<uint8_t*>(sd->scratch);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the previous call's counters may not be zero if it did not complete: clear them
+  if (launch_zero_words(reinterpret_cast<uint32_t*>(base), (int64_t)(cnt_bytes / 4), st) != hipSuccess)
+    return QGEMM_EHIP;
+  StreamArgs a{};
+  a.d0 = make_desc(&h, x_bf16, y, p);
+  a.part = reinterpret_cast<float*>(base + cnt_bytes);
+  a.cnt = reinterpret_cast<uint32_t*>(base);
+  a.G = 1;
+  a.R = R;
+  a.P = (int32_t)p.P;
+  a.RT = p.RT;
+  a.NT = p.NT;
+  a.NW = p.NW;
+  a.msum = p.msum;
+  a.valu = 0;
+  return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
 int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t* bytes) {

@@ -94,4 +94,10 @@ hipError_t launch_argmax_split(const float* y, int R, int64_t N, int32_t* idx, v
 hipError_t launch_verify(const int32_t* idx, int R, const int32_t* drafts, int D, int32_t* tokens, int32_t* n_new,
                          hipStream_t st);
 
+// The allocation-free entry point's fixed device scratch (qgemm_run_static):
+// its bytes, its address on the current device, and a kernel that zeroes words.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(16) << 20;
+hipError_t static_scratch_address(void** out);
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st);
+
 }  // namespace qg

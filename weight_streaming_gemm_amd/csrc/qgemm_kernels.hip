@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "layout.h"
@@ -1180,6 +1181,46 @@ hipError_t launch_verify(const int32_t* idx, int R, const int32_t* drafts, int D
                          hipStream_t st) {
   if (R == 0) return hipSuccess;
   hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(64), 0, st, idx, R / (D + 1), D, drafts, tokens, n_new);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch of the allocation-free entry point (qgemm_run_static):
+// per-tile arrival counters, then partial output tiles.  Every GPU the library
+// runs on holds its own copy for the life of the process.  In host code the
+// array's name is not a device address: its address on the current device
+// comes from hipGetSymbolAddress, taken once per device and kept.
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch_address(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// n 32-bit words set to zero (a kernel rather than a memset node, so that a
+// captured graph replays it reliably)
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemm.so")
 
 QGEMM_OK, QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN = 0, -1, -2, -3
-QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH = -4, -5, -6, -7
+QGEMM_ERANGE_R, QGEMM_ENOMEM, QGEMM_EHIP, QGEMM_EPATH, QGEMM_ESCRATCH = -4, -5, -6, -7, -8
+STATIC_SCRATCH_BYTES = 16 << 20
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_TILED = 0, 1, 2, 3
 TILED_MIN_R = 24
 SEQ_PERSISTENT = 1
@@ -23,7 +24,8 @@ MAX_PREFILL_R = 8192
 
 # every symbol include/qgemm.h declares
 EXPORTS = (
-    "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path", "qgemm_run_prefill",
+    "qgemm_packed_size", "qgemm_pack", "qgemm_create", "qgemm_run", "qgemm_run_path", "qgemm_run_static",
+    "qgemm_run_prefill",
     "qgemm_prefill_workspace_size",
     "qgemm_dequantize", "qgemm_argmax_rows", "qgemm_argmax_workspace_size", "qgemm_argmax_rows_ws",
     "qgemm_verify_greedy", "qgemm_attention_workspace_size", "qgemm_decode_attention", "qgemm_query",
@@ -66,6 +68,7 @@ def lib():
             "qgemm_create": [ctypes.POINTER(vp), vp, i64, i64, i32, ctypes.c_uint32],
             "qgemm_run": [vp, vp, vp, i32, vp],
             "qgemm_run_path": [vp, vp, vp, i32, i32, vp],
+            "qgemm_run_static": [vp, i64, i64, vp, vp, i32, vp],
             "qgemm_run_prefill": [vp, vp, vp, i32, vp, ctypes.c_size_t, vp],
             "qgemm_prefill_workspace_size": [vp, i32, ctypes.POINTER(ctypes.c_size_t)],
             "qgemm_dequantize": [vp, vp, vp],
@@ -122,6 +125,13 @@ def packed_size(N: int, K: int) -> int:
 def pack(canon_dev, packed_dev, N: int, K: int, stream=None):
     _check(lib().qgemm_pack(_ptr(canon_dev), _ptr(packed_dev), N, K, _stream(stream)), "qgemm_pack")
     return packed_dev
+
+
+def run_static(packed_dev, N: int, K: int, x, y, R: int | None = None, stream=None):
+    """qgemm_run without a handle, on the library's fixed scratch (no allocation)."""
+    R = x.shape[0] if R is None else R
+    _check(lib().qgemm_run_static(_ptr(packed_dev), N, K, _ptr(x), _ptr(y), R, _stream(stream)),
+           "qgemm_run_static")
 
 
 def argmax_rows(y, idx, R: int | None = None, stream=None):
