@@ -686,9 +686,9 @@ def main():
         print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
         return
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
-    if args.persistent and max(sweep) > 12:
-        # one cooperative launch runs the streaming kernel only, whose large-R plans need K chunks
-        sweep = [r for r in sweep if r <= max(12, args.R)]
+    if args.persistent and max(sweep) > 16:
+        # the persistent pass kernel serves up to 16 rows (one row tile)
+        sweep = [r for r in sweep if r <= 16]
         log(f"[pass] persistent launch: row counts {sweep}")
     R_max = max(sweep)
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)

@@ -15,7 +15,7 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 def build(force: bool = False) -> str:
     src = os.path.join(HERE, "qgemm_emu.cpp")
     deps = [src] + [os.path.join(HERE, "..", "..", "weight_streaming_gemm_amd", "csrc", f)
-                    for f in ("layout.h", "operand.h", "stream_sched.h", "prefill_plan.h")]
+                    for f in ("layout.h", "operand.h", "stream_sched.h", "prefill_plan.h", "pass_sched.h")]
     if force or not os.path.exists(LIB) or any(os.path.getmtime(d) > os.path.getmtime(LIB) for d in deps):
         tmp = LIB + ".tmp"
         subprocess.check_call([CLANG, "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
@@ -46,6 +46,12 @@ def lib():
         L.emu_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]
         L.emu_prefill_plan.restype = ctypes.c_int
         L.emu_prefill_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_pass_coverage.restype = ctypes.c_int
+        L.emu_pass_coverage.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.emu_pass.restype = ctypes.c_int
+        L.emu_pass.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.emu_prefill.restype = ctypes.c_int
         L.emu_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_void_p]
@@ -106,6 +112,51 @@ def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None, aligned=N
                               chunks.ctypes.data, order_seed)
     if rc != 0:
         raise RuntimeError(f"emu_stream_seq failed ({rc})")
+    return ys
+
+
+# the persistent pass kernel's constants (qgemm_internal.h): compute waves per
+# workgroup, LDS bytes for activations, most K chunks
+PASS_NC = 8
+PASS_X_AREA = 160 * 1024 - 8 * 2 * 1024 - 256
+PASS_MAX_CHUNKS = 16
+
+
+def pass_coverage(shapes, R, P=256, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS):
+    """(per-GEMM step hit counts [NS * KB], chunks) of the pass kernel's schedule."""
+    G = len(shapes)
+    Ns = np.array([N for N, _ in shapes], np.int64)
+    Ks = np.array([K for _, K in shapes], np.int64)
+    sizes = [((N + 15) // 16) * (K // 256) for N, K in shapes]
+    counts = np.zeros(sum(sizes), np.int32)
+    chunks = np.zeros(G, np.int32)
+    rc = lib().emu_pass_coverage(G, Ns.ctypes.data, Ks.ctypes.data, R, P, PASS_NC, x_area, max_chunks,
+                                 counts.ctypes.data, chunks.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"emu_pass_coverage failed ({rc})")
+    out, o = [], 0
+    for n in sizes:
+        out.append(counts[o:o + n])
+        o += n
+    return out, chunks
+
+
+def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS):
+    """The pass kernel replayed over GEMMs mats = [(canon, N, K)] with activations
+    xs (bf16 bits, R x K each): the list of y."""
+    G = len(mats)
+    canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
+    xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
+    R = xs[0].shape[0]
+    ys = [np.full((R, N), np.nan, dtype=np.float32) for _, N, _ in mats]
+    P_ = ctypes.c_void_p * G
+    Ns = np.array([N for _, N, _ in mats], dtype=np.int64)
+    Ks = np.array([K for _, _, K in mats], dtype=np.int64)
+    rc = lib().emu_pass(G, P_(*[c.ctypes.data for c in canons]), Ns.ctypes.data, Ks.ctypes.data,
+                        P_(*[x.ctypes.data for x in xs]), P_(*[y.ctypes.data for y in ys]), R, P, PASS_NC, x_area,
+                        max_chunks)
+    if rc != 0:
+        raise RuntimeError(f"emu_pass failed ({rc})")
     return ys
 
 

@@ -17,6 +17,7 @@
 #include "../../weight_streaming_gemm_amd/csrc/operand.h"
 #include "../../weight_streaming_gemm_amd/csrc/stream_sched.h"
 #include "../../weight_streaming_gemm_amd/csrc/prefill_plan.h"
+#include "../../weight_streaming_gemm_amd/csrc/pass_sched.h"
 #include <algorithm>
 #include <cmath>
 #include <random>
@@ -576,6 +577,123 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
     float s = part[(size_t)i];
     for (int64_t z = 1; z < p.S; ++z) s += part[(size_t)(z * p.slice + i)];
     y[i] = s;
+  }
+  return 0;
+}
+
+// ---- the persistent pass kernel (pass.hip) -----------------------------------
+
+// Every compute wave's cursor over its share, as the kernel walks it: count
+// steps from packed step step0 at chunk block jj0, +1 per step and KB - kbc more
+// at a chunk's end.  counts[g][ns * KB + j] += 1 for every step taken.
+int emu_pass_coverage(int G, const int64_t* Ns, const int64_t* Ks, int R, int P, int NC, int x_area, int max_chunks,
+                      int32_t* counts, int32_t* chunks_out) {
+  int64_t off = 0;
+  for (int g = 0; g < G; ++g) {
+    const int KB = (int)(Ks[g] / SB_W), NS = (int)(padded_n(Ns[g]) / TILE_N);
+    const int S = pass_chunks(KB, R, P, x_area, max_chunks);
+    chunks_out[g] = S;
+    const int kbc = S ? KB / S : 1, rot = (int)((g * 37) % P);
+    for (int p = 0; p < P && S > 0; ++p)
+      for (int w = 0; w < NC; ++w) {
+        int count, step, jj;
+        pass_wave_share(p, w, NC, P, NS, KB, S, kbc, rot, &count, &step, &jj);
+        for (int i = 0; i < count; ++i) {
+          if (step < 0 || step >= NS * KB) return -2;
+          counts[off + step] += 1;
+          if (++jj == kbc) {
+            jj = 0;
+            step += KB - kbc + 1;
+          } else {
+            step += 1;
+          }
+        }
+      }
+    off += (int64_t)NS * KB;
+  }
+  return 0;
+}
+
+// Replay of the pass: per GEMM, every workgroup's compute waves walk their shares
+// with the streaming kernel's step arithmetic against the chunk's staged
+// activations and leave a piece at each unit end; helper 0 adds each unit's
+// pieces in wave order (waves from pass_step_owner, piece index from
+// pass_wave_first) and writes y, or with K chunks the chunk's partial tile; the
+// partial tiles of a sub-tile are added in chunk order.
+int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64_t* Ks, const uint16_t* const* xs,
+             float* const* ys, int R, int P, int NC, int x_area, int max_chunks) {
+  typedef std::vector<f32x4> Tile;   // 64 lanes
+  for (int g = 0; g < G; ++g) {
+    const int64_t N = Ns[g], K = Ks[g];
+    const int KB = (int)(K / SB_W), NS = (int)(padded_n(N) / TILE_N);
+    const int S = pass_chunks(KB, R, P, x_area, max_chunks);
+    if (S == 0) return -1;
+    const int kbc = KB / S, rot = (int)((g * 37) % P);
+    std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
+    pack(canons[g], packed.data(), N, K);
+    const int64_t hdr_off = quant_region_bytes(N, K);
+    std::vector<Tile> partial((size_t)S * NS, Tile(64, f32x4{0, 0, 0, 0}));
+    auto store_y = [&](int ns, const Tile& t) {
+      for (int lane = 0; lane < 64; ++lane) {
+        const int64_t n = (int64_t)ns * TILE_N + (lane & 15);
+        if (n >= N) continue;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * (lane >> 4) + i;
+          if (r < R) ys[g][(int64_t)r * N + n] = t[lane][i];
+        }
+      }
+    };
+    for (int p = 0; p < P; ++p) {
+      int c, ns0, ns1;
+      pass_units(p, S, P, NS, rot, &c, &ns0, &ns1);
+      if (ns1 == ns0) continue;
+      std::vector<f16x8> slots;
+      std::vector<Sum2> sums;
+      convert_x(xs[g], R, K, (int64_t)c * kbc, kbc, 0, kbc, slots, sums);
+      std::vector<std::vector<Tile>> pieces(NC);
+      for (int w = 0; w < NC; ++w) {
+        int count, step, jj;
+        pass_wave_share(p, w, NC, P, NS, KB, S, kbc, rot, &count, &step, &jj);
+        Tile acc(64, f32x4{0, 0, 0, 0});
+        for (int left = count; left > 0; --left) {
+          const int ns = step / KB, j = step % KB;
+          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, 1, true, acc.data());
+          if (jj == kbc - 1 || left == 1) {
+            pieces[w].push_back(acc);
+            acc.assign(64, f32x4{0, 0, 0, 0});
+          }
+          if (++jj == kbc) {
+            jj = 0;
+            step += KB - kbc + 1;
+          } else {
+            step += 1;
+          }
+        }
+      }
+      const int units = ns1 - ns0, n = units * kbc;
+      for (int u = 0; u < units; ++u) {
+        const int w_lo = pass_step_owner(u * kbc, NC, n), w_hi = pass_step_owner((u + 1) * kbc - 1, NC, n);
+        Tile sum(64, f32x4{0, 0, 0, 0});
+        for (int w = w_lo; w <= w_hi; ++w) {
+          const int a_w = pass_wave_first(w, NC, n);
+          if (a_w == pass_wave_first(w + 1, NC, n)) continue;   // an empty share leaves no piece
+          const int k = u - a_w / kbc;
+          if (k < 0 || k >= (int)pieces[w].size()) return -3;
+          for (int lane = 0; lane < 64; ++lane) sum[lane] += pieces[w][k][lane];
+        }
+        if (S == 1)
+          store_y(ns0 + u, sum);
+        else
+          partial[(size_t)c * NS + ns0 + u] = sum;
+      }
+    }
+    if (S > 1)
+      for (int ns = 0; ns < NS; ++ns) {
+        Tile sum = partial[ns];
+        for (int cc = 1; cc < S; ++cc)
+          for (int lane = 0; lane < 64; ++lane) sum[lane] += partial[(size_t)cc * NS + ns][lane];
+        store_y(ns, sum);
+      }
   }
   return 0;
 }

@@ -207,10 +207,12 @@ def test_shared_tile_counters_rearm_over_repeats(orc):
     g.close()
 
 
-def test_full_pass_run_verify(orc):
+@pytest.mark.parametrize("persistent", [False, True])
+def test_full_pass_run_verify(orc, persistent):
     """The benchmark's timed call itself: all 257 GEMMs of the pass resident (17.99
-    GB), one graph-replayed qgemm_seq_run_verify at 12 rows (4 agents x (token + 2
-    drafts)) with the head's row argmax and the greedy draft check.  Every output
+    GB), one qgemm_seq_run_verify at 12 rows (4 agents x (token + 2 drafts)) with
+    the head's row argmax and the greedy draft check, graph-replayed or as one
+    persistent launch.  Every output
     of layers 0 and 63 and of the head is compared with the oracle, 16 sampled
     outputs of every other GEMM, the argmax exactly, and the emitted tokens with
     the oracle's greedy check.  The drafts are made from the oracle's argmax so
@@ -219,7 +221,7 @@ def test_full_pass_run_verify(orc):
     import weight_streaming_gemm_amd as wsg
     seed, R, D = W.SEED_PASS, W.R_DEFAULT, W.ROWS_PER_AGENT - 1
     mats = W.full_pass()
-    print(f"full pass: {len(mats)} GEMMs, R={R}", flush=True)
+    print(f"full pass: {len(mats)} GEMMs, R={R}, persistent={persistent}", flush=True)
     gs, packs = [], []
     for i, m in enumerate(mats):
         packed = G.upload_packed(fused_canon(seed, m), m.N, m.K)
@@ -246,9 +248,10 @@ def test_full_pass_run_verify(orc):
     idx = torch.empty(R, dtype=torch.int32, device="cuda")
     tokens = torch.empty((A, D + 1), dtype=torch.int32, device="cuda")
     n_new = torch.empty(A, dtype=torch.int32, device="cuda")
-    seq = wsg.Seq(gs)
+    seq = wsg.Seq(gs, persistent=persistent)
     seq.run_verify([xd[m.K] for m in mats], ys, R, idx, G.to_dev(drafts), D, tokens, n_new)
     torch.cuda.synchronize()
+    assert seq.errors() == 0
     print("pass done; comparing", flush=True)
     full = set(range(4)) | set(range(4 * 63, 4 * 64)) | {len(mats) - 1}
     for i, m in enumerate(mats):

@@ -1,0 +1,80 @@
+"""The persistent pass kernel's schedule (pass_sched.h) and data flow, replayed
+on the CPU: every weight step of every GEMM is taken exactly once, the chunking
+of the pass's shapes is what the LDS area allows, and the replayed pass (cursor
+walk, pieces added in wave order, chunk partials added in chunk order) matches
+the fp64 oracle."""
+from __future__ import annotations
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from synth import workloads as W
+from tests import emu
+from tests.parity import assert_parity
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "weight_streaming_gemm_amd", "csrc")
+
+
+def test_replay_constants_match_the_kernel():
+    text = open(os.path.join(CSRC, "qgemm_internal.h")).read()
+    nc = int(re.search(r"constexpr int PASS_NC = (\d+);", text).group(1))
+    pieces = int(re.search(r"constexpr int PASS_PIECES = (\d+);", text).group(1))
+    chunks = int(re.search(r"constexpr int PASS_MAX_CHUNKS = (\d+);", text).group(1))
+    assert "PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256" in text
+    assert nc == emu.PASS_NC and chunks == emu.PASS_MAX_CHUNKS
+    assert emu.PASS_X_AREA == 160 * 1024 - nc * pieces * 1024 - 256
+
+
+PASS_SHAPES = [(m.N, m.K) for m in W.layer_mats(0)] + [(W.lm_head().N, W.lm_head().K)]
+
+
+@pytest.mark.parametrize("R", [1, 3, 12, 16])
+def test_pass_shapes_take_every_step_once(R):
+    counts, chunks = emu.pass_coverage(PASS_SHAPES, R, P=256)
+    for (N, K), c in zip(PASS_SHAPES, counts):
+        assert c.size == ((N + 15) // 16) * (K // 256)
+        assert (c == 1).all(), f"N={N} K={K} R={R}: steps taken {np.bincount(c)}"
+    if R == 12:
+        # Q|K|V, gate|up and the head in one chunk; O (K = 8192) in two, down (K = 25600) in five
+        assert chunks.tolist() == [1, 2, 1, 5, 1]
+    if R == 16:
+        assert chunks.tolist() == [2, 2, 2, 10, 2]
+
+
+@pytest.mark.parametrize("P", [1, 3, 7, 64, 250])
+def test_odd_shapes_take_every_step_once(P):
+    rng = np.random.default_rng(P)
+    shapes = [(int(rng.integers(1, 700)), 256 * int(rng.integers(1, 40))) for _ in range(12)] + [(1, 256), (17, 512)]
+    counts, chunks = emu.pass_coverage(shapes, 12, P=P, x_area=4 * 6656)
+    planned = 0
+    for (N, K), c, S in zip(shapes, counts, chunks):
+        if S == 0:                     # no chunking fits (the library refuses such a sequence)
+            KB = K // 256
+            assert not any(KB % S2 == 0 and KB // S2 <= 4 for S2 in range(1, min(P, 16, KB) + 1))
+            assert (c == 0).all()
+            continue
+        planned += 1
+        assert (K // 256) % S == 0 and K // 256 // S <= 4 and S <= min(P, 16)
+        assert (c == 1).all(), f"P={P} N={N} K={K} S={S}"
+    assert planned >= 2
+
+
+@pytest.mark.parametrize("P,x_blocks", [(7, 3), (16, 2), (5, 40), (1, 8)])
+def test_pass_replay_matches_oracle(orc, P, x_blocks):
+    """A 4-GEMM sequence on few workgroups (several units each, some with none),
+    with an LDS area of x_blocks blocks, so that some GEMMs run in K chunks."""
+    R = 12
+    shapes = [(300, 1024), (64, 2048), (520, 512), (33, 1536)]
+    mats, xs = [], []
+    for i, (N, K) in enumerate(shapes):
+        mats.append((synth.matrix_rows(6, 20 + i, N, K), N, K))
+        xs.append(synth.x_bf16(6, 30 + i, R, K, outlier_p=0.01))
+    x_area = x_blocks * (8 * (64 * R + 16) + 32 * R)
+    ys = emu.pass_run(mats, xs, P, x_area=x_area)
+    for (canon, N, K), x, y in zip(mats, xs, ys):
+        m = assert_parity(y, orc.gemm(canon, N, K, x), f"pass replay P={P} N={N} K={K}")
+        assert m["rel_l2"] < 2e-6

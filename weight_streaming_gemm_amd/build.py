@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["qgemm_kernels.hip", "attention.hip", "prefill.hip", "qgemm_api.cpp"]
+SOURCES = ["qgemm_kernels.hip", "pass.hip", "attention.hip", "prefill.hip", "qgemm_api.cpp"]
 
 
 def build(verbose: bool = False) -> str:

@@ -1,0 +1,552 @@
+// pass.hip — the whole weight pass (a sequence of GEMMs) in one persistent launch,
+// for up to 16 activation rows.
+//
+// The pages' decode step streams every quantised weight once and applies it to
+// all stacked rows (OpenJet multi-agent serving page, section on moving the
+// weights only once), with one persistent megakernel for the whole step (the
+// section on going from one session to four agents).  Here one cooperative
+// launch runs all GEMMs of the pass in order; GEMM g + 1 computes only after
+// every workgroup has finished GEMM g (each projection's input depends on the
+// previous output), but its weights are already in flight: the weight stream
+// does not stop at GEMM boundaries.
+//
+// Roles.  A workgroup (one per compute unit) has 8 compute waves and 4 helper
+// waves.  A compute wave streams its weight steps through a register ring of
+// RING steps that runs straight across GEMM boundaries, multiplies them on the
+// matrix cores against activations in LDS, and hands each finished partial
+// 16 x 16 tile ("piece") to LDS.  Compute waves issue only loads, so waiting for
+// a step's weights never waits for a store.  The helper waves stage each GEMM's
+// activations into LDS; helper 0 also adds the pieces of each unit in wave order,
+// stores y (or a chunk's partial tile), runs the K-chunk sums, and arrives at and
+// waits on the device-wide barrier between GEMMs.  Every wave executes exactly
+// one workgroup barrier per GEMM: after the activations of that GEMM are staged.
+//
+// Work (pass_sched.h): a GEMM is cut along K into S chunks of kbc blocks; chunk c
+// goes to a contiguous set of workgroups, which share its sub-tiles as runs of
+// whole units (a unit = one 16-output sub-tile over one chunk).  With S > 1 the
+// chunks' partial tiles of a sub-tile are added by the last chunk to arrive, in
+// chunk order; every sum has a fixed order, so results are bitwise repeatable.
+//
+// Per step (16 outputs x 256 weights of one block) the arithmetic is the
+// streaming kernel's: B = sc q exact in binary16, 8 v_mfma_f32_16x16x32_f16
+// against the activations, the min term from fp32 sub-block sums (two
+// v_mfma_f32_16x16x4_f32), then acc += d ds - dmin ms in fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "layout.h"
+#include "operand.h"
+#include "pass_sched.h"
+#include "qgemm_internal.h"
+
+namespace qg {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t OOB = 0x80000000u;          // beyond every buffer (sizes < 2^31)
+constexpr uint32_t SPIN_LIMIT = 1u << 21;      // polls of a device-wide wait before giving up
+constexpr uint32_t LDS_SPIN_LIMIT = 1u << 24;  // polls of a wait on another wave of the workgroup
+constexpr int SC1 = 16;                        // cache policy: coherent across the device
+// s_waitcnt with lgkmcnt(0) only (vmcnt and expcnt at their maxima): LDS done,
+// loads in flight untouched
+constexpr int WAIT_LGKM0 = 0xC07F;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <class T, int AUX>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX));
+}
+__device__ __forceinline__ void bstore_sc1(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, SC1);
+}
+__device__ __forceinline__ void bstore1_sc1(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, SC1);
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+// the sum of four bf16 values (two dwords) in fp32, with two dot products against ones
+__device__ __forceinline__ float sum4_bf16(uint32_t d0, uint32_t d1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  const float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), one, 0.0f, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), one, s, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// GEMM g's descriptor, read through the scalar unit (wave-uniform by construction)
+__device__ __forceinline__ PassGemm get_gemm(const PassGemm* __restrict__ t, int g) {
+  typedef const PassGemm __attribute__((address_space(4)))* cptr;
+  const cptr src = (cptr)(t + g);
+  PassGemm d;
+  d.qbase = uniform_ptr(src->qbase);
+  d.hbase = uniform_ptr(src->hbase);
+  d.qbytes = (uint32_t)uni((int)src->qbytes);
+  d.hbytes = (uint32_t)uni((int)src->hbytes);
+  d.x = uniform_ptr(src->x);
+  d.y = uniform_ptr(src->y);
+  d.N = uni(src->N);
+  d.NS = uni(src->NS);
+  d.KB = uni(src->KB);
+  d.S = uni(src->S);
+  d.kbc = uni(src->kbc);
+  d.rot = uni(src->rot);
+  d.pad_[0] = d.pad_[1] = 0;
+  return d;
+}
+__device__ __forceinline__ PassWave get_wave(const PassWave* __restrict__ t, int idx) {
+  typedef const PassWave __attribute__((address_space(4)))* cptr;
+  const cptr src = (cptr)(t + idx);
+  PassWave v;
+  v.count = uni(src->count);
+  v.step0 = uni(src->step0);
+  v.jj0 = uni(src->jj0);
+  v.next = uni(src->next);
+  return v;
+}
+
+// where a compute wave stands in the sequence (all wave-uniform)
+struct Span {
+  int g;                           // GEMM index; >= G past the end of the sequence
+  int KB, kbc;                     // blocks of a row, blocks of a chunk
+  int left;                        // steps of this GEMM left, the current one included
+  int step, jj;                    // packed step (sub-tile * KB + block), block within the chunk
+  int k;                           // pieces written in this GEMM (compute cursor)
+  __amdgpu_buffer_rsrc_t qr, hr;   // quant and header regions
+};
+
+}  // namespace
+
+template <int RING>
+__global__ void __launch_bounds__(PASS_THREADS, 1)
+pass_kernel(PassArgs a) {
+  static_assert(RING == 4 || RING == 6 || RING == 8, "the step loop unrolls 4, 6 or 8 steps");
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[PASS_X_AREA];
+  __shared__ f32x4 pieces[PASS_NC * PASS_PIECES * 64];
+  __shared__ uint32_t s_go;                     // GEMM whose activations the helpers may stage
+  __shared__ uint32_t s_written[PASS_NC];       // pieces each compute wave has written in this GEMM
+  __shared__ uint32_t s_consumed[PASS_NC];      // pieces of each compute wave helper 0 has added
+  __shared__ uint32_t s_last;                   // last workgroup out of the launch
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
+  const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
+  const PassGemm* __restrict__ gemms = a.gemms;
+  const int XT = pass_x_step_bytes(R), XS = 8 * XT, SB = pass_x_block_bytes(R);
+
+  if (wv < PASS_NC) {
+    // ======================= compute wave ======================================
+    const int w = wv;
+    int xoff = 0;                                // this lane's A-operand offset inside a step
+    {
+      const int r = nl < R ? nl : R - 1;         // rows >= R reuse row R - 1 (never stored)
+      xoff = (g4 * R + r) * 16;
+    }
+    const PassWave* __restrict__ waves = a.waves;
+    // the wave's share of GEMM g, or of the first later GEMM with steps for it
+    auto enter = [&](Span& s, int g) __attribute__((always_inline)) {
+      PassWave v = g < G ? get_wave(waves, (g * P + p) * PASS_NC + w) : PassWave{0, 0, 0, G};
+      if (v.count == 0 && v.next < G) {
+        g = v.next;
+        v = get_wave(waves, (g * P + p) * PASS_NC + w);
+      }
+      if (v.count == 0) g = G;
+      s.g = g;
+      s.left = v.count;
+      s.step = v.step0;
+      s.jj = v.jj0;
+      s.k = 0;
+      if (g < G) {
+        const PassGemm d = get_gemm(gemms, g);
+        s.KB = d.KB;
+        s.kbc = d.kbc;
+        s.qr = make_rsrc(d.qbase, d.qbytes);
+        s.hr = make_rsrc(d.hbase, d.hbytes);
+      } else {
+        s.KB = 1;
+        s.kbc = 1;
+        s.qr = make_rsrc(nullptr, 0);
+        s.hr = make_rsrc(nullptr, 0);
+      }
+    };
+    // the next step of a cursor; at the end of its share, the next GEMM's
+    auto advance = [&](Span& s) __attribute__((always_inline)) {
+      s.left = uni(s.left - 1);
+      if (s.left > 0) {
+        s.jj = uni(s.jj + 1);
+        s.step = uni(s.step + 1);
+        if (s.jj == s.kbc) {
+          s.jj = 0;
+          s.step = uni(s.step + s.KB - s.kbc);
+        }
+      } else {
+        enter(s, s.g + 1);
+      }
+    };
+    typedef struct { u32x4 qa, qb, hd; } Stage;
+    // the lane's offsets are fixed (lane 16 B into a quant half, output nl's 16 B of a
+    // header chunk); the step's offset is wave-uniform and goes in the scalar
+    // offset, so a refill needs no address registers and lands in the slot's own.
+    // Past the end of the sequence the resources have no records: the loads
+    // return zeros without touching memory.
+    const int qlane = lane * 16, hlane = nl * 16;
+    auto load_w = [&](Stage& st, const Span& s) __attribute__((always_inline)) {
+      st.qa = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.qr, qlane, s.step * CHUNK_Q, 2));
+      st.qb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.qr, qlane + 1024, s.step * CHUNK_Q, 2));
+      st.hd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.hr, hlane, s.step * CHUNK_H, 2));
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Stage& st, int slot) __attribute__((always_inline)) {
+      const WConst cst = header_consts(st.hd.x, st.hd.y, st.hd.z, st.hd.w, g4);
+      // d and -dmin as fp32 values of their own right away: folded into the final
+      // multiply-adds as binary16 operands, they would keep the header's registers
+      // alive past the slot's refill
+      float dd = cst.d, dm = cst.nmin;
+      asm volatile("" : "+v"(dd), "+v"(dm));
+      f32x4 ds = {0.f, 0.f, 0.f, 0.f}, ms = {0.f, 0.f, 0.f, 0.f};
+      const int base = slot * SB;
+      for (int t = 0; t < 8; ++t) {
+        const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + t * XT + xoff);
+        const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+        ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+      }
+      const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + XS + xoff / 2);
+      ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
+      ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = __builtin_fmaf(dd, ds[i], acc[i]);
+        acc[i] = __builtin_fmaf(dm, ms[i], acc[i]);
+      }
+    };
+    // piece k of this wave's sub-range (one per unit it touches) into slot k mod
+    // PASS_PIECES, once helper 0 has taken piece k - PASS_PIECES
+    auto put_piece = [&](Span& s) __attribute__((always_inline)) {
+      const uint32_t k = (uint32_t)s.k;
+      s.k = uni(s.k + 1);
+      if (k >= PASS_PIECES) {
+        uint32_t n = 0;
+        while (lds_load(&s_consumed[w]) + PASS_PIECES <= k) {
+          if (++n > LDS_SPIN_LIMIT) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      asm volatile("" ::: "memory");             // the slot is free before it is written
+      pieces[(w * PASS_PIECES + (int)(k % PASS_PIECES)) * 64 + lane] = acc;
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);    // the piece is in LDS before it is announced
+      asm volatile("" ::: "memory");
+      if (lane == 0) lds_store(&s_written[w], k + 1);
+    };
+
+    int passed = 0;                              // workgroup barriers passed (one per GEMM)
+    Span L, C;
+    enter(C, 0);
+    L = C;
+    Stage W[RING];
+    // the ring's first RING steps (unrolled: the slots must stay in registers)
+    auto fill = [&](auto SL) __attribute__((always_inline)) {
+      load_w(W[decltype(SL)::value], L);
+      advance(L);
+    };
+    fill(std::integral_constant<int, 0>{});
+    fill(std::integral_constant<int, 1>{});
+    fill(std::integral_constant<int, 2>{});
+    fill(std::integral_constant<int, 3>{});
+    if constexpr (RING > 4) {
+      fill(std::integral_constant<int, 4 % RING>{});
+      fill(std::integral_constant<int, 5 % RING>{});
+    }
+    if constexpr (RING > 6) {
+      fill(std::integral_constant<int, 6 % RING>{});
+      fill(std::integral_constant<int, 7 % RING>{});
+    }
+    // one step at ring slot s; true at the end of the sequence
+    auto step = [&](auto SL) __attribute__((always_inline)) -> bool {
+      constexpr int s = decltype(SL)::value;
+      compute(W[s], C.jj);
+      // the refill goes after the slot's last use, into the slot's own registers
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(W[s], L);
+      advance(L);
+      if (C.g < G && (C.jj == C.kbc - 1 || C.left == 1)) {      // the step ends a unit or the share
+        put_piece(C);
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      advance(C);
+      while (passed <= C.g && C.g < G) {         // the next step's GEMM: its activations are staged past this
+        __builtin_amdgcn_s_barrier();
+        passed = uni(passed + 1);
+      }
+      return C.g >= G;
+    };
+    while (passed <= C.g && C.g < G) {
+      __builtin_amdgcn_s_barrier();
+      passed = uni(passed + 1);
+    }
+    if (C.g < G)
+    for (;;) {
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+      if constexpr (RING > 4) {
+        step(std::integral_constant<int, 4 % RING>{});
+        step(std::integral_constant<int, 5 % RING>{});
+      }
+      if constexpr (RING > 6) {
+        step(std::integral_constant<int, 6 % RING>{});
+        step(std::integral_constant<int, 7 % RING>{});
+      }
+      if (C.g >= G) break;
+    }
+    while (passed < G) {                         // GEMMs past this wave's last step
+      __builtin_amdgcn_s_barrier();
+      passed = uni(passed + 1);
+    }
+    return;
+  }
+
+  // ========================= helper waves ========================================
+  const int h = wv - PASS_NC;                    // 0 .. PASS_NH - 1
+  const int htid = tid - PASS_NC * 64;           // 0 .. 64 PASS_NH - 1
+  uint32_t* const bar = a.bar;
+  const int groups = P < 8 ? P : 8;
+  const int grp = p % 8, members = (P - grp + 7) / 8;
+  bool dead = false;                             // a device-wide wait gave up: no more waiting
+
+  if (h == 0) {
+    if (lane < PASS_NC) {
+      s_written[lane] = 0u;
+      s_consumed[lane] = 0u;
+    }
+    if (lane == 0) s_go = 0u;
+  }
+
+  // ---- the activations of GEMM g for this workgroup's chunk: block c kbc + b of x
+  // goes to slot b.  A slot holds 8 steps of XT bytes (lane group gg, row r: the
+  // 16-byte binary16 A operand built from x[r, 256 j + 64 gg + 4 t + {0..3}] and the
+  // same 32 further on), then the fp32 sums of sub-blocks 2 gg and 2 gg + 1 per
+  // row.  32 threads per (slot, row); every (slot, row) of the chunk in one batch.
+  constexpr int HGROUPS = PASS_NH * 64 / 32;     // (slot, row) pairs per batch row
+  constexpr int XB = 16;                         // batch rows in flight per thread
+  auto stage = [&](const PassGemm& d, int c) __attribute__((always_inline)) {
+    const int sub = htid & 31, gg = sub >> 3, t = sub & 7, grp_id = htid >> 5;
+    const int K = d.KB * SB_W;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
+    const int pairs = d.kbc * R;
+    for (int base = 0; base < pairs; base += XB * HGROUPS) {
+      u32x2 lo[XB], hi[XB];
+#pragma unroll
+      for (int k = 0; k < XB; ++k) {
+        const int q = base + k * HGROUPS + grp_id;            // (slot, row) = (q / R, q % R)
+        const int b = q / R, r = q - b * R;
+        const uint32_t off = (uint32_t)((r * K + (c * d.kbc + b) * SB_W + 64 * gg + 4 * t) * 2);
+        lo[k] = bload<u32x2, 0>(xr, q < pairs ? off : OOB);
+        hi[k] = bload<u32x2, 0>(xr, q < pairs ? off + 64 : OOB);
+      }
+#pragma unroll
+      for (int k = 0; k < XB; ++k) {
+        const int q = base + k * HGROUPS + grp_id;
+        if (q >= pairs) continue;
+        const int b = q / R, r = q - b * R;
+        *reinterpret_cast<f16x8*>(xlds + b * SB + t * XT + (gg * R + r) * 16) =
+            build_a(lo[k].x, lo[k].y, hi[k].x, hi[k].y);
+        // sub-block sums: the 8 threads t of lane group gg add their run sums as
+        // ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
+        float s0 = sum4_bf16(lo[k].x, lo[k].y), s1 = sum4_bf16(hi[k].x, hi[k].y);
+        s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
+        s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
+        s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
+        if (t == 0) *reinterpret_cast<f32x2*>(xlds + b * SB + XS + (gg * R + r) * 8) = f32x2{s0, s1};
+      }
+    }
+  };
+
+  // ---- device-wide barrier after GEMM g (generation g + 1): arrive at the
+  // group counter of workgroups p mod 8; the group's last arrival arrives at the
+  // global counter.  Arrival waits only for helper 0's own stores.
+  auto grid_arrive = [&](int g) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      const uint32_t gen = (uint32_t)g + 1;
+      const uint32_t old = __hip_atomic_fetch_add(bar + 32 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == gen * (uint32_t)members)
+        __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto grid_wait = [&](int g) __attribute__((always_inline)) {
+    if (lane == 0 && !dead) {
+      const uint32_t target = ((uint32_t)g + 1) * (uint32_t)groups;
+      uint32_t n = 0;
+      while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++n > SPIN_LIMIT) {
+          __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          dead = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  };
+
+  // ---- helper 0: the units of GEMM g, in order: add each unit's pieces in wave
+  // order, then y (one chunk) or the chunk's partial tile; after the last unit the
+  // chunk sums of the sub-tiles whose last chunk this workgroup was.
+  auto finish = [&](const PassGemm& d, int c, int ns0, int ns1) __attribute__((always_inline)) {
+    const int units = ns1 - ns0, n = units * d.kbc;
+    // y goes out device-coherent: the next GEMM may run on any die
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
+    const uint32_t part_tile = (uint32_t)d.NS * 1024u;                 // bytes of one chunk's partials
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+    for (int u = 0; u < units; ++u) {
+      const int w_lo = pass_step_owner(u * d.kbc, PASS_NC, n);
+      const int w_hi = pass_step_owner((u + 1) * d.kbc - 1, PASS_NC, n);
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      for (int w = w_lo; w <= w_hi; ++w) {
+        const int a_w = pass_wave_first(w, PASS_NC, n);
+        if (a_w == pass_wave_first(w + 1, PASS_NC, n)) continue;   // an empty share leaves no piece
+        const int k = u - a_w / d.kbc;
+        uint32_t spins = 0;
+        while (lds_load(&s_written[w]) <= (uint32_t)k) {
+          if (++spins > LDS_SPIN_LIMIT) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");           // the piece is read after its announcement
+        sum += pieces[(w * PASS_PIECES + k % PASS_PIECES) * 64 + lane];
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // and before its slot is handed back
+        asm volatile("" ::: "memory");
+        if (lane == 0) lds_store(&s_consumed[w], (uint32_t)k + 1);
+      }
+      const int ns = ns0 + u;
+      if (d.S == 1) {
+        const int nn = ns * TILE_N + nl;
+        if (nn < d.N)
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
+          }
+      } else {
+        bstore_sc1(sum, pr, (uint32_t)c * part_tile + (uint32_t)ns * 1024u + lane * 16);
+      }
+    }
+    if (d.S == 1 || units == 0) return;
+    // every partial tile of this workgroup is stored; arrive at each unit's
+    // sub-tile counter (one lane per unit); the last of the S chunks to arrive adds
+    // the S partial tiles in chunk order and writes y
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int u0 = 0; u0 < units; u0 += 64) {
+      bool last = false;
+      if (u0 + lane < units) {
+        const uint32_t old = __hip_atomic_fetch_add(a.cnt + ns0 + u0 + lane, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (uint32_t)(d.S - 1);
+      }
+      uint64_t mask = __builtin_amdgcn_ballot_w64(last);
+      while (mask) {
+        // one sub-tile at a time, all its chunks' loads in flight together
+        const int uu = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int ns = ns0 + u0 + uu;
+        f32x4 v[PASS_MAX_CHUNKS];
+#pragma unroll
+        for (int cc = 0; cc < PASS_MAX_CHUNKS; ++cc)
+          v[cc] = bload<f32x4, SC1>(pr, cc < d.S ? (uint32_t)cc * part_tile + (uint32_t)ns * 1024u + lane * 16 : OOB);
+        f32x4 sum = v[0];
+#pragma unroll
+        for (int cc = 1; cc < PASS_MAX_CHUNKS; ++cc)
+          if (cc < d.S) sum += v[cc];
+        const int nn = ns * TILE_N + nl;
+        if (nn < d.N)
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
+          }
+        if (lane == 0) __hip_atomic_store(a.cnt + ns, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+
+  for (int g = 0; g < G; ++g) {
+    const PassGemm d = get_gemm(gemms, g);
+    int c, ns0, ns1;
+    pass_units(p, d.S, P, d.NS, d.rot, &c, &ns0, &ns1);
+    c = uni(c); ns0 = uni(ns0); ns1 = uni(ns1);
+    if (g > 0) {
+      if (h == 0) {
+        grid_wait(g - 1);
+        if (lane < PASS_NC) {
+          lds_store(&s_written[lane], 0u);
+          lds_store(&s_consumed[lane], 0u);
+        }
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+        if (lane == 0) lds_store(&s_go, (uint32_t)g);
+      } else {
+        uint32_t n = 0;
+        while (lds_load(&s_go) < (uint32_t)g) {
+          if (++n > LDS_SPIN_LIMIT) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
+    if (ns1 > ns0) stage(d, c);
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_s_barrier();                // the activations of GEMM g are in LDS
+    if (h == 0) {
+      finish(d, c, ns0, ns1);
+      if (g + 1 < G) grid_arrive(g);
+    }
+  }
+
+  // the last workgroup out re-arms the barrier counters for the next launch
+  if (h == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(bar + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)P - 1 ? 1u : 0u;
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    if (lds_load(&s_last) && lane < 10) {        // the global, exit and 8 group counters
+      const int i = lane == 0 ? 0 : (lane == 1 ? 16 : 32 + 32 * (lane - 2));
+      __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+hipError_t launch_pass(const PassArgs& a, hipStream_t st) {
+  PassArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&pass_kernel<PASS_RING>), dim3((unsigned)a.P),
+                                    dim3(PASS_THREADS), params, 0, st);
+}
+
+int pass_occupancy() {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pass_kernel<PASS_RING>, PASS_THREADS, 0) != hipSuccess)
+    return 0;
+  return blocks;
+}
+
+}  // namespace qg

@@ -1,0 +1,77 @@
+// pass_sched.h — the schedule of the persistent pass kernel (pass.hip) as pure
+// integer functions, compiled for host and device.
+//
+// One launch runs a sequence of GEMMs; every workgroup (one per compute unit, P
+// in all) takes part in every GEMM.  A GEMM with NS 16-output sub-tiles and KB
+// 256-weight blocks is cut along K into S chunks of kbc = KB / S blocks; a unit
+// is one sub-tile over one chunk (kbc block steps).  Chunk c is dealt to the
+// workgroups [first_cu(c), first_cu(c + 1)), which share its NS units as
+// contiguous runs of whole units (their counts differ by at most one; which
+// workgroups get the longer runs rotates from GEMM to GEMM).  So a workgroup
+// needs the activations of one chunk only, and a unit is never split between
+// workgroups: only the chunks of a sub-tile meet across workgroups.
+//
+// Inside a workgroup the compute waves split its steps (unit-major: step i is
+// block i mod kbc of unit i / kbc) into NC contiguous equal sub-ranges.  A wave
+// leaves one piece (its partial 16 x 16 tile) per unit its sub-range touches;
+// the pieces of a unit are added in wave order.
+#pragma once
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qg {
+
+// chunk of workgroup p (chunk c takes workgroups floor(c P / S) .. floor((c + 1) P / S) - 1)
+QG_HD int pass_chunk_of(int p, int S, int P) { return (int)(((int64_t)(p + 1) * S - 1) / P); }
+QG_HD int pass_first_cu(int c, int S, int P) { return (int)((int64_t)c * P / S); }
+
+// the units [*ns0, *ns1) of workgroup p in its chunk *c (sub-tiles of that chunk)
+QG_HD void pass_units(int p, int S, int P, int NS, int rot, int* c, int* ns0, int* ns1) {
+  const int cc = pass_chunk_of(p, S, P);
+  const int lo = pass_first_cu(cc, S, P), hi = pass_first_cu(cc + 1, S, P);
+  const int pc = hi - lo;                                  // workgroups of the chunk (>= 1 when S <= P)
+  const int q = (p - lo + pc - rot % pc) % pc;             // rotated place among them
+  const int base = NS / pc, extra = NS % pc;
+  const int a = q * base + (q < extra ? q : extra);
+  *c = cc;
+  *ns0 = a;
+  *ns1 = a + base + (q < extra ? 1 : 0);
+}
+
+// first step of wave w's sub-range when n steps are split over NC waves
+QG_HD int pass_wave_first(int w, int NC, int n) { return (int)((int64_t)n * w / NC); }
+// the wave whose sub-range holds step i (0 <= i < n)
+QG_HD int pass_step_owner(int i, int NC, int n) { return (int)((((int64_t)i + 1) * NC + n - 1) / n) - 1; }
+
+// LDS bytes of one block's activations for R rows: 8 steps of (64 R + 16)
+// bytes of binary16 operands (lane group, row; the 16-byte pad per step spreads
+// consecutive steps over the banks), then 8 R fp32 sub-block sums
+QG_HD int pass_x_step_bytes(int R) { return 64 * R + 16; }
+QG_HD int pass_x_block_bytes(int R) { return 8 * pass_x_step_bytes(R) + 32 * R; }
+
+// K chunks of a GEMM with KB blocks at R rows over P workgroups: the fewest
+// (dividing KB, at most max_chunks and at most P) whose activations fit x_area
+// bytes of LDS; 0 when none does
+QG_HD int pass_chunks(int KB, int R, int P, int x_area, int max_chunks) {
+  for (int S = 1; S <= max_chunks && S <= P && S <= KB; ++S)
+    if (KB % S == 0 && (int64_t)(KB / S) * pass_x_block_bytes(R) <= x_area) return S;
+  return 0;
+}
+
+// Compute wave w of workgroup p in a GEMM (NS sub-tiles, KB blocks, S chunks of
+// kbc, rotation rot): its count of steps, its first packed step (sub-tile * KB +
+// block) and first block within the chunk
+QG_HD void pass_wave_share(int p, int w, int NC, int P, int NS, int KB, int S, int kbc, int rot, int* count,
+                           int* step0, int* jj0) {
+  int c, ns0, ns1;
+  pass_units(p, S, P, NS, rot, &c, &ns0, &ns1);
+  const int n = (ns1 - ns0) * kbc;
+  const int a = pass_wave_first(w, NC, n), b = pass_wave_first(w + 1, NC, n);
+  *count = b - a;
+  const int ns = ns0 + a / kbc, jj = a % kbc;
+  *step0 = b > a ? ns * KB + c * kbc + jj : 0;
+  *jj0 = b > a ? jj : 0;
+}
+
+}  // namespace qg

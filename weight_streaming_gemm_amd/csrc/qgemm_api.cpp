@@ -13,6 +13,7 @@
 
 #include "../../include/qgemm.h"
 #include "layout.h"
+#include "pass_sched.h"
 #include "qgemm_internal.h"
 
 using namespace qg;
@@ -573,49 +574,90 @@ struct qgemm_seq {
   hipStream_t cap;                                 // capture stream (graph mode)
   std::map<SeqKey, hipGraphExec_t> graphs;         // per (R, pointer set) (graph mode)
   int cus;
-  int occ[5];
-  // workspace shared by the GEMMs of a launch (they run one after another)
-  float* part;
-  uint32_t* cnt;     // per-tile counters
-  uint32_t* sync;    // count + 1 barrier counters
+  // persistent mode (pass.hip): workspace shared by the GEMMs of a launch
+  float* part;       // chunk partial tiles
+  uint32_t* cnt;     // per-sub-tile chunk arrival counters
+  uint32_t* bar;     // barrier counters
   uint32_t* err;
   size_t part_bytes, cnt_bytes;
-  std::map<SeqKey, GemmDesc*> descs;   // device descriptor arrays per (R, pointer set)
+  std::map<SeqKey, PassGemm*> descs;   // device descriptor tables per (R, pointer set)
+  std::map<int, PassWave*> waves;      // device wave tables per R
   void* am_ws;       // argmax (and verification) workspace for the last GEMM's output
   int max_R;
 };
 
 namespace {
 
-// one launch over all GEMMs of a sequence: the same (RT, NT, NW), the same form
-// of the min term and the same P = V for all (every workgroup takes one range
-// of every GEMM): P is the
-// smallest of the GEMMs' single-launch plans, and must still fit every GEMM's
-// activations (else the sequence cannot run persistent)
-Plan plan_seq(const qgemm_seq* s, int R, std::vector<Plan>* per, bool* fits) {
-  int64_t P = INT64_MAX;
-  for (const qgemm_handle* h : s->hs) P = std::min(P, plan_stream(h->NS, h->KB, R, s->cus, s->occ).P);
-  Plan all{};
-  int64_t Tmax = 1;
-  size_t slot = 0;
-  *fits = true;
+// K chunks of one GEMM in the persistent pass at R rows: the fewest (dividing
+// the blocks of K, at most PASS_MAX_CHUNKS and at most one per workgroup) whose
+// activations fit the kernel's LDS area; 0 when none does.
+int pass_chunks_of(int64_t KB, int R, int P) {
+  return KB > INT32_MAX ? 0 : pass_chunks((int)KB, R, P, PASS_X_AREA, PASS_MAX_CHUNKS);
+}
+
+// The GEMMs' chunking and workspace needs at R rows; false if a GEMM cannot run
+bool pass_sizes(const qgemm_seq* s, int R, size_t* part, size_t* cnt) {
+  *part = *cnt = 0;
+  if (R < 1 || R > PASS_MAX_R) return false;
   for (const qgemm_handle* h : s->hs) {
-    Plan p = plan_stream(h->NS, h->KB, R, s->cus, s->occ, P);
-    if (p.P != P) *fits = false;
-    p.P = p.V = P;
-    p.msum = 0;                    // one kernel for all GEMMs: the min term per step
-    const int64_t cap = x_slot_capacity(R, p.RT, p.NT, p.NW, p.msum != 0);
-    if (std::min<int64_t>((p.I + P - 1) / P, h->KB) > cap) *fits = false;
-    if (per) per->push_back(p);
-    all = p;
-    Tmax = std::max(Tmax, p.T);
-    slot = std::max(slot, partial_slot_bytes(p.RT, p.NT, p.nwn));
+    const int S = pass_chunks_of(h->KB, R, s->cus);
+    if (S == 0) return false;
+    if (S > 1) {
+      *part = std::max(*part, (size_t)S * (size_t)h->NS * 1024);
+      *cnt = std::max(*cnt, (size_t)h->NS * 4);
+    }
   }
-  all.P = all.V = P;
-  all.T = Tmax;
-  all.part_bytes = (size_t)(2 * P) * slot;
-  all.cnt_bytes = (size_t)Tmax * 4;
-  return all;
+  return true;
+}
+
+// the descriptor table of one run (the GEMMs' weights, activations, outputs and
+// chunking at R rows); rot spreads the longer unit runs over the workgroups
+std::vector<PassGemm> pass_descs(const qgemm_seq* s, int R, const void* const* xs, float* const* ys) {
+  std::vector<PassGemm> t(s->hs.size());
+  for (size_t g = 0; g < s->hs.size(); ++g) {
+    const qgemm_handle* h = s->hs[g];
+    PassGemm& d = t[g];
+    const int64_t qb = quant_region_bytes(h->N, h->K);
+    d.qbase = h->packed;
+    d.hbase = h->packed + qb;
+    d.qbytes = (uint32_t)qb;
+    d.hbytes = (uint32_t)(packed_bytes(h->N, h->K) - qb);
+    d.x = reinterpret_cast<const uint16_t*>(xs[g]);
+    d.y = ys[g];
+    d.N = (int32_t)h->N;
+    d.NS = (int32_t)h->NS;
+    d.KB = (int32_t)h->KB;
+    d.S = pass_chunks_of(h->KB, R, s->cus);
+    d.kbc = (int32_t)(h->KB / d.S);
+    d.rot = (int32_t)((g * 37) % (size_t)s->cus);
+    d.pad_[0] = d.pad_[1] = 0;
+  }
+  return t;
+}
+
+// every compute wave's share of every GEMM (pass_sched.h), [G][P][PASS_NC]
+std::vector<PassWave> pass_waves(const std::vector<PassGemm>& t, int P) {
+  const int G = (int)t.size();
+  std::vector<PassWave> v((size_t)G * P * PASS_NC);
+  for (int g = 0; g < G; ++g) {
+    const PassGemm& d = t[g];
+    for (int p = 0; p < P; ++p)
+      for (int w = 0; w < PASS_NC; ++w) {
+        PassWave& e = v[((size_t)g * P + p) * PASS_NC + w];
+        pass_wave_share(p, w, PASS_NC, P, d.NS, d.KB, d.S, d.kbc, d.rot, &e.count, &e.step0, &e.jj0);
+      }
+  }
+  // next: the first later GEMM where the wave has steps
+  for (int p = 0; p < P; ++p)
+    for (int w = 0; w < PASS_NC; ++w) {
+      int next = G;
+      for (int g = G - 1; g >= 0; --g) {
+        PassWave& e = v[((size_t)g * P + p) * PASS_NC + w];
+        e.next = next;
+        if (e.count > 0) next = g;
+      }
+    }
+  return v;
 }
 
 // Cached graphs and descriptor tables per (R, pointer set): at most this many
@@ -639,11 +681,26 @@ void seq_free(qgemm_seq* s) {
   for (auto& kv : s->graphs) (void)hipGraphExecDestroy(kv.second);
   if (s->cap) (void)hipStreamDestroy(s->cap);
   for (auto& kv : s->descs) (void)hipFree(kv.second);
+  for (auto& kv : s->waves) (void)hipFree(kv.second);
   if (s->part) (void)hipFree(s->part);
   if (s->cnt) (void)hipFree(s->cnt);
-  if (s->sync) (void)hipFree(s->sync);
+  if (s->bar) (void)hipFree(s->bar);
   if (s->err) (void)hipFree(s->err);
   if (s->am_ws) (void)hipFree(s->am_ws);
+}
+
+template <class T>
+T* upload(const std::vector<T>& v) {
+  T* dev = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&dev), v.size() * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (hipMemcpy(dev, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    return nullptr;
+  }
+  return dev;
 }
 
 }  // namespace
@@ -669,39 +726,45 @@ int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32
     return QGEMM_EHIP;
   }
   if (device_cus(&s->cus) != QGEMM_OK) {
+    seq_free(s);
     delete s;
     return QGEMM_EHIP;
   }
-  fill_occupancy(s->occ);
   size_t part = 0, cnt = 0;
-  if (flags & QGEMM_SEQ_PERSISTENT)
-    for (int R = 1; R <= max_R; ++R) {
-      std::vector<Plan> per;
-      bool fits = true;
-      Plan p = plan_seq(s, R, &per, &fits);
-      for (const Plan& pi : per)
-        if (!plan_fits(pi)) fits = false;
-      if (!fits) {
-        (void)hipStreamDestroy(s->cap);
-        delete s;
-        return QGEMM_EPATH;
-      }
-      part = std::max(part, p.part_bytes);
-      cnt = std::max(cnt, p.cnt_bytes);
+  if (flags & QGEMM_SEQ_PERSISTENT) {
+    // one workgroup per compute unit, all resident
+    if (pass_occupancy() < 1) {
+      seq_free(s);
+      delete s;
+      return QGEMM_EPATH;
     }
+    bool any = false;
+    for (int R = 1; R <= std::min(max_R, PASS_MAX_R); ++R) {
+      size_t pr, cn;
+      if (!pass_sizes(s, R, &pr, &cn)) continue;
+      any = true;
+      part = std::max(part, pr);
+      cnt = std::max(cnt, cn);
+    }
+    if (!any) {
+      seq_free(s);
+      delete s;
+      return QGEMM_EPATH;
+    }
+  }
   part = std::max<size_t>(part, 256);
   cnt = std::max<size_t>(cnt, 256);
   s->part_bytes = part;
   s->cnt_bytes = cnt;
-  const size_t sync_bytes = (size_t)(count + 1) * 4;
+  const size_t bar_bytes = (size_t)PASS_BAR_WORDS * 4;
   s->max_R = max_R;
   const size_t am_bytes = argmax_ws_bytes(max_R, s->hs.back()->N);
   bool ok = hipMalloc(&s->am_ws, am_bytes) == hipSuccess && hipMemset(s->am_ws, 0, am_bytes) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->part), part) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->cnt), cnt) == hipSuccess &&
-            hipMalloc(reinterpret_cast<void**>(&s->sync), sync_bytes) == hipSuccess &&
+            hipMalloc(reinterpret_cast<void**>(&s->bar), bar_bytes) == hipSuccess &&
             hipMalloc(reinterpret_cast<void**>(&s->err), 4) == hipSuccess &&
-            hipMemset(s->cnt, 0, cnt) == hipSuccess && hipMemset(s->sync, 0, sync_bytes) == hipSuccess &&
+            hipMemset(s->cnt, 0, cnt) == hipSuccess && hipMemset(s->bar, 0, bar_bytes) == hipSuccess &&
             hipMemset(s->err, 0, 4) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
@@ -767,39 +830,34 @@ int seq_run_impl(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, 
     }
     return hipGraphLaunch(g->second, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
   }
-  std::vector<Plan> per;
-  bool fits = true;
-  const Plan p = plan_seq(s, R, &per, &fits);
-  if (!fits) return QGEMM_EPATH;
+  // one persistent launch over all GEMMs (pass.hip)
+  size_t part, cnt;
+  if (!pass_sizes(s, R, &part, &cnt) || part > s->part_bytes || cnt > s->cnt_bytes) return QGEMM_EPATH;
   auto it = s->descs.find(key);
   if (it == s->descs.end()) {
     if (s->descs.size() >= SEQ_CACHE_MAX) seq_drop_descs(s);
-    std::vector<GemmDesc> host(s->hs.size());
-    for (size_t i = 0; i < s->hs.size(); ++i) host[i] = make_desc(s->hs[i], xs[i], ys[i], per[i]);
-    GemmDesc* dev = nullptr;
-    if (hipMalloc(reinterpret_cast<void**>(&dev), host.size() * sizeof(GemmDesc)) != hipSuccess) {
-      (void)hipGetLastError();
-      return QGEMM_ENOMEM;
-    }
-    if (hipMemcpy(dev, host.data(), host.size() * sizeof(GemmDesc), hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(dev);
-      return QGEMM_EHIP;
-    }
+    PassGemm* dev = upload(pass_descs(s, R, xs, ys));
+    if (!dev) return QGEMM_ENOMEM;
     it = s->descs.emplace(key, dev).first;
   }
-  StreamArgs a{};
-  a.descs = it->second;
-  a.part = s->part;
-  a.cnt = s->cnt;
-  a.sync = s->sync;
-  a.err = s->err;
+  auto wt = s->waves.find(R);
+  if (wt == s->waves.end()) {
+    PassWave* dev = upload(pass_waves(pass_descs(s, R, xs, ys), s->cus));
+    if (!dev) return QGEMM_ENOMEM;
+    wt = s->waves.emplace(R, dev).first;
+  }
+  PassArgs a{};
+  a.gemms = it->second;
+  a.waves = wt->second;
   a.G = (int32_t)s->hs.size();
   a.R = R;
-  a.P = (int32_t)p.P;
-  a.RT = p.RT;
-  a.NT = p.NT;
-  a.NW = p.NW;
-  if (launch_stream(a, true, st) != hipSuccess) return QGEMM_EHIP;
+  a.P = s->cus;
+  a.part_bytes = (uint32_t)s->part_bytes;
+  a.part = s->part;
+  a.cnt = s->cnt;
+  a.bar = s->bar;
+  a.err = s->err;
+  if (launch_pass(a, st) != hipSuccess) return QGEMM_EHIP;
   if (argmax_idx) {
     const qgemm_handle* last = s->hs.back();
     if (launch_argmax_split(ys[s->hs.size() - 1], R, last->N, argmax_idx, s->am_ws, drafts, D, tokens, n_new, st) !=

@@ -94,6 +94,48 @@ hipError_t launch_argmax_split(const float* y, int R, int64_t N, int32_t* idx, v
 hipError_t launch_verify(const int32_t* idx, int R, const int32_t* drafts, int D, int32_t* tokens, int32_t* n_new,
                          hipStream_t st);
 
+// ---- the persistent pass kernel (pass.hip, schedule in pass_sched.h) ----------
+// One GEMM of the sequence, as the kernel reads it from a device table.
+struct PassGemm {
+  const uint8_t* qbase;    // quant region (qbytes), header region (hbytes) of the packed weights
+  const uint8_t* hbase;
+  uint32_t qbytes, hbytes;
+  const uint16_t* x;       // bf16 activations, R x K row-major
+  float* y;                // fp32 outputs, R x N row-major
+  int32_t N, NS, KB;       // outputs, 16-output sub-tiles, 256-weight blocks
+  int32_t S, kbc;          // K in S chunks of kbc blocks
+  int32_t rot;             // rotation of the deal of units to workgroups
+  int32_t pad_[2];
+};
+// A compute wave's share of one GEMM (pass_sched.h), precomputed on the host:
+// `count` steps starting at packed step `step0` (sub-tile * KB + block), at
+// block `jj0` of the chunk; `next` = the first later GEMM where the wave has
+// steps (G if none).
+struct PassWave {
+  int32_t count, step0, jj0, next;
+};
+struct PassArgs {
+  const PassGemm* gemms;   // device table of G GEMMs
+  const PassWave* waves;   // device table [G][P][PASS_NC]
+  int32_t G, R, P;         // GEMMs, rows (1..PASS_MAX_R), workgroups (all resident)
+  uint32_t part_bytes;     // bytes of `part`
+  float* part;             // chunk partial tiles: chunk c, sub-tile ns at (c NS + ns) KiB
+  uint32_t* cnt;           // per-sub-tile chunk arrival counters, zero between GEMMs
+  uint32_t* bar;           // PASS_BAR_WORDS barrier counters, zero between launches
+  uint32_t* err;           // set to 1 when a device-wide wait gave up
+};
+constexpr int PASS_MAX_R = 16;                   // one 16-row tile
+constexpr int PASS_NC = 8;                       // compute waves per workgroup
+constexpr int PASS_NH = 4;                       // helper waves per workgroup
+constexpr int PASS_THREADS = (PASS_NC + PASS_NH) * 64;
+constexpr int PASS_PIECES = 2;                   // LDS partial tiles per compute wave
+constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave
+constexpr int PASS_MAX_CHUNKS = 16;
+constexpr int PASS_BAR_WORDS = 512;
+constexpr int PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256;
+hipError_t launch_pass(const PassArgs& a, hipStream_t st);
+int pass_occupancy();                            // resident workgroups per CU (0: none)
+
 // The allocation-free entry point's fixed device scratch (qgemm_run_static):
 // its bytes, its address on the current device, and a kernel that zeroes words.
 constexpr size_t STATIC_SCRATCH_BYTES = size_t(16) << 20;
