@@ -261,9 +261,17 @@ int qgemm_destroy(qgemm_t h);
  *                         qgemm_run), captured into a HIP graph on the first
  *                         run for a given (R, pointer set) and replayed after;
  *   QGEMM_SEQ_PERSISTENT  one cooperative launch for all GEMMs (below).
+ * and, with QGEMM_SEQ_PERSISTENT, the form of the min term (dmin m_s X_s):
+ *   0                          eight more matrix-core products per weight block,
+ *                              of the activation operands with the mins;
+ *   QGEMM_SEQ_SUB_BLOCK_SUMS   the fp32 sub-block sums X_s of x, computed when
+ *                              the activations are staged, times the mins in
+ *                              two fp32 products per block.
+ * (Both give results within the stated tolerance; they round differently.)
  * Errors: QGEMM_EINVAL (also for unknown flags), QGEMM_ENOMEM, QGEMM_ESHAPE,
  * QGEMM_EHIP. */
 #define QGEMM_SEQ_PERSISTENT 1u
+#define QGEMM_SEQ_SUB_BLOCK_SUMS 2u
 int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32_t flags);
 
 /* Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]

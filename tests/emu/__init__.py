@@ -51,7 +51,10 @@ def lib():
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         L.emu_pass.restype = ctypes.c_int
         L.emu_pass.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int]
+        L.emu_pass_block_bytes.restype = ctypes.c_int
+        L.emu_pass_block_bytes.argtypes = [ctypes.c_int]
         L.emu_prefill.restype = ctypes.c_int
         L.emu_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_void_p]
@@ -141,9 +144,15 @@ def pass_coverage(shapes, R, P=256, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUN
     return out, chunks
 
 
-def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS):
+def pass_block_bytes(R):
+    """LDS bytes of one block's activations in the pass kernel at R rows."""
+    return lib().emu_pass_block_bytes(R)
+
+
+def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS, msum=False):
     """The pass kernel replayed over GEMMs mats = [(canon, N, K)] with activations
-    xs (bf16 bits, R x K each): the list of y."""
+    xs (bf16 bits, R x K each), the min term from sub-block sums (msum) or from
+    products with the mins: the list of y."""
     G = len(mats)
     canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
     xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
@@ -154,7 +163,7 @@ def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS):
     Ks = np.array([K for _, _, K in mats], dtype=np.int64)
     rc = lib().emu_pass(G, P_(*[c.ctypes.data for c in canons]), Ns.ctypes.data, Ks.ctypes.data,
                         P_(*[x.ctypes.data for x in xs]), P_(*[y.ctypes.data for y in ys]), R, P, PASS_NC, x_area,
-                        max_chunks)
+                        max_chunks, int(msum))
     if rc != 0:
         raise RuntimeError(f"emu_pass failed ({rc})")
     return ys

@@ -586,6 +586,9 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
 // Every compute wave's cursor over its share, as the kernel walks it: count
 // steps from packed step step0 at chunk block jj0, +1 per step and KB - kbc more
 // at a chunk's end.  counts[g][ns * KB + j] += 1 for every step taken.
+// LDS bytes of one block's activations in the pass kernel
+int emu_pass_block_bytes(int R) { return pass_x_block_bytes(R); }
+
 int emu_pass_coverage(int G, const int64_t* Ns, const int64_t* Ks, int R, int P, int NC, int x_area, int max_chunks,
                       int32_t* counts, int32_t* chunks_out) {
   int64_t off = 0;
@@ -621,7 +624,7 @@ int emu_pass_coverage(int G, const int64_t* Ns, const int64_t* Ks, int R, int P,
 // pass_wave_first) and writes y, or with K chunks the chunk's partial tile; the
 // partial tiles of a sub-tile are added in chunk order.
 int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64_t* Ks, const uint16_t* const* xs,
-             float* const* ys, int R, int P, int NC, int x_area, int max_chunks) {
+             float* const* ys, int R, int P, int NC, int x_area, int max_chunks, int msum) {
   typedef std::vector<f32x4> Tile;   // 64 lanes
   for (int g = 0; g < G; ++g) {
     const int64_t N = Ns[g], K = Ks[g];
@@ -657,7 +660,7 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
         Tile acc(64, f32x4{0, 0, 0, 0});
         for (int left = count; left > 0; --left) {
           const int ns = step / KB, j = step % KB;
-          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, 1, true, acc.data());
+          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, 1, msum != 0, acc.data());
           if (jj == kbc - 1 || left == 1) {
             pieces[w].push_back(acc);
             acc.assign(64, f32x4{0, 0, 0, 0});

@@ -489,40 +489,47 @@ def test_seq_run_verify_matches_oracle(orc):
 
 # ---- full weight pass machinery (one cooperative launch over several GEMMs) ----
 
-@pytest.mark.parametrize("persistent", [False, True])
-def test_seq_matches_oracle_and_repeats_bitwise(orc, persistent):
+@pytest.mark.parametrize("mode", ["graph", "persistent", "persistent_sums"])
+def test_seq_matches_oracle_and_repeats_bitwise(orc, mode):
+    """A six-GEMM sequence (ragged N, K of 2 to 12 blocks) at 12 rows: parity with
+    the oracle, bitwise-equal repeats with other work between them, the head
+    argmax; then 16, 7 and 1 rows through the same sequence (odd row counts
+    convert a missing last row in the persistent kernel's staging)."""
     import torch
     import weight_streaming_gemm_amd as wsg
+    persistent = mode != "graph"
     shapes = [(300, 1024), (64, 2048), (4100, 512), (1000, 1024), (40, 3072), (151, 512)]
-    R = 12
-    mats = [G.make(9, i, N, K, max_R=12) for i, (N, K) in enumerate(shapes)]
-    xs_np = [synth.x_bf16(9, 100 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    R, RM = 12, 16
+    mats = [G.make(9, i, N, K, max_R=RM) for i, (N, K) in enumerate(shapes)]
+    xs_np = [synth.x_bf16(9, 100 + i, RM, K) for i, (N, K) in enumerate(shapes)]
     xs = [G.to_dev(x) for x in xs_np]
-    ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for N, K in shapes]
-    idx = torch.empty(R, dtype=torch.int32, device="cuda")
-    seq = wsg.Seq([g for _, g in mats], persistent=persistent)
+    ys = [torch.empty((RM, N), dtype=torch.float32, device="cuda") for N, K in shapes]
+    idx = torch.empty(RM, dtype=torch.int32, device="cuda")
+    seq = wsg.Seq([g for _, g in mats], persistent=persistent, sub_block_sums=mode == "persistent_sums")
     first = None
     for rep in range(4):
-        _flush(f"seq persistent={persistent} rep {rep}")
+        _flush(f"seq {mode} rep {rep}")
         for y in ys:
             y.fill_(-7.0)
-        seq.run(xs, ys, R, argmax_idx=idx)
+        seq.run([x[:R] for x in xs], [y[:R] for y in ys], R, argmax_idx=idx)
         torch.cuda.synchronize()
         _ = (torch.ones(1000, device="cuda") * rep).sum().item()   # other work between launches
-        got = [y.cpu().numpy() for y in ys]
+        got = [y[:R].cpu().numpy() for y in ys]
         if first is None:
             first = got
             for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
-                assert_parity(got[i], orc.gemm(canon, N, K, xs_np[i]), f"seq gemm {i}")
+                assert_parity(got[i], orc.gemm(canon, N, K, xs_np[i][:R]), f"seq gemm {i}")
         for i in range(len(shapes)):
             assert np.array_equal(got[i].view(np.uint32), first[i].view(np.uint32)), (rep, i)
-        assert np.array_equal(idx.cpu().numpy(), np.argmax(got[-1], axis=1))
+        assert np.array_equal(idx[:R].cpu().numpy(), np.argmax(got[-1], axis=1))
     assert seq.errors() == 0
-    # fewer rows through the same sequence
-    seq.run([x[:3] for x in xs], [y[:3] for y in ys], 3)
-    torch.cuda.synchronize()
-    for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
-        assert_parity(ys[i][:3].cpu().numpy(), orc.gemm(canon, N, K, xs_np[i][:3]), f"seq R=3 gemm {i}")
+    # other row counts through the same sequence
+    for r in (16, 7, 1):
+        _flush(f"seq {mode} R={r}")
+        seq.run([x[:r] for x in xs], [y[:r] for y in ys], r)
+        torch.cuda.synchronize()
+        for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+            assert_parity(ys[i][:r].cpu().numpy(), orc.gemm(canon, N, K, xs_np[i][:r]), f"seq R={r} gemm {i}")
     assert seq.errors() == 0
     seq.close()
     for _, g in mats:

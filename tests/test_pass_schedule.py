@@ -63,18 +63,51 @@ def test_odd_shapes_take_every_step_once(P):
     assert planned >= 2
 
 
+@pytest.mark.parametrize("msum", [False, True])
 @pytest.mark.parametrize("P,x_blocks", [(7, 3), (16, 2), (5, 40), (1, 8)])
-def test_pass_replay_matches_oracle(orc, P, x_blocks):
+def test_pass_replay_matches_oracle(orc, P, x_blocks, msum):
     """A 4-GEMM sequence on few workgroups (several units each, some with none),
-    with an LDS area of x_blocks blocks, so that some GEMMs run in K chunks."""
+    with an LDS area of x_blocks blocks, so that some GEMMs run in K chunks; the
+    min term in either form."""
     R = 12
     shapes = [(300, 1024), (64, 2048), (520, 512), (33, 1536)]
     mats, xs = [], []
     for i, (N, K) in enumerate(shapes):
         mats.append((synth.matrix_rows(6, 20 + i, N, K), N, K))
         xs.append(synth.x_bf16(6, 30 + i, R, K, outlier_p=0.01))
-    x_area = x_blocks * (8 * (64 * R + 16) + 32 * R)
-    ys = emu.pass_run(mats, xs, P, x_area=x_area)
+    x_area = x_blocks * emu.pass_block_bytes(R)
+    ys = emu.pass_run(mats, xs, P, x_area=x_area, msum=msum)
     for (canon, N, K), x, y in zip(mats, xs, ys):
         m = assert_parity(y, orc.gemm(canon, N, K, x), f"pass replay P={P} N={N} K={K}")
         assert m["rel_l2"] < 2e-6
+
+
+@pytest.mark.parametrize("R", range(1, 17))
+def test_in_place_conversion_reads_every_raw_row_before_overwriting_it(R):
+    """The pass kernel converts a slot in place: the raw bf16 rows (512 bytes
+    each, in pairs) become 528-byte operand rows (a missing odd row included)
+    and the 8 R fp32 sums (at 528 times R rounded up to even).  Pairs go two at
+    a time from the last to the first (pair 0 twice when their number is odd),
+    both read before either is written.  Replayed byte by byte: nothing is
+    written over a raw row still to be read, and everything stays in the slot."""
+    sb = emu.pass_block_bytes(R)
+    row, pairs = 528, (R + 1) // 2
+    R2 = 2 * pairs
+    owner = np.full(sb, -1)                       # raw row whose bytes lie here
+    for r in range(R2):
+        owner[512 * r:512 * (r + 1)] = r
+    unread = set(range(R2))
+    for pp in range(pairs - 1, -1, -2):
+        qq = max(pp - 1, 0)
+        unread -= {2 * pp, 2 * pp + 1, 2 * qq, 2 * qq + 1}
+        for q in (pp, qq):
+            writes = []
+            for r in (2 * q, 2 * q + 1):
+                writes.append((row * r, row * r + 512))                      # operands of row r
+                if r < R:
+                    writes += [(row * R2 + (gg * R + r) * 8, row * R2 + (gg * R + r) * 8 + 8) for gg in range(4)]
+            for lo, hi in writes:
+                assert 0 <= lo and hi <= sb, f"R={R} pair {q}: write [{lo}, {hi}) outside the slot of {sb}"
+                hit = set(owner[lo:hi].tolist()) & unread
+                assert not hit, f"R={R} pair {q}: write [{lo}, {hi}) over unread raw rows {hit}"
+    assert not unread

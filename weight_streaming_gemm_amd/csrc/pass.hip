@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "layout.h"
 #include "operand.h"
@@ -56,6 +57,8 @@ constexpr int SC1 = 16;                        // cache policy: coherent across 
 // s_waitcnt with lgkmcnt(0) only (vmcnt and expcnt at their maxima): LDS done,
 // loads in flight untouched
 constexpr int WAIT_LGKM0 = 0xC07F;
+// s_waitcnt with vmcnt(0) only (lgkmcnt and expcnt at their maxima)
+constexpr int WAIT_VM0 = 0x0F70;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
@@ -127,7 +130,19 @@ __device__ __forceinline__ PassWave get_wave(const PassWave* __restrict__ t, int
   v.step0 = uni(src->step0);
   v.jj0 = uni(src->jj0);
   v.next = uni(src->next);
+  v.xblk = 0;
   return v;
+}
+
+__device__ __forceinline__ int xblk_of(const PassWave* __restrict__ t, int idx) {
+  typedef const PassWave __attribute__((address_space(4)))* cptr;
+  return uni(((cptr)(t + idx))->xblk);
+}
+
+// f(0), f(1), ..., f(n - 1) with compile-time indices (ring slots stay in registers)
+template <class F, int... I>
+__device__ __forceinline__ void for_each_slot(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
 
 // where a compute wave stands in the sequence (all wave-uniform)
@@ -142,34 +157,76 @@ struct Span {
 
 }  // namespace
 
-template <int RING>
+template <int RING, bool MSUM>
 __global__ void __launch_bounds__(PASS_THREADS, 1)
 pass_kernel(PassArgs a) {
-  static_assert(RING == 4 || RING == 6 || RING == 8, "the step loop unrolls 4, 6 or 8 steps");
+  static_assert(RING >= 2 && RING <= 12, "ring of 2 to 12 steps");
   __shared__ __attribute__((aligned(16))) uint8_t xlds[PASS_X_AREA];
   __shared__ f32x4 pieces[PASS_NC * PASS_PIECES * 64];
   __shared__ uint32_t s_go;                     // GEMM whose activations the helpers may stage
   __shared__ uint32_t s_written[PASS_NC];       // pieces each compute wave has written in this GEMM
-  __shared__ uint32_t s_consumed[PASS_NC];      // pieces of each compute wave helper 0 has added
+  __shared__ uint32_t s_consumed[PASS_NC][PASS_PIECES];  // times each piece slot has been added
+  __shared__ uint32_t s_done;                   // helpers through with their units (all GEMMs so far)
   __shared__ uint32_t s_last;                   // last workgroup out of the launch
 
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
   const PassGemm* __restrict__ gemms = a.gemms;
-  const int XT = pass_x_step_bytes(R), XS = 8 * XT, SB = pass_x_block_bytes(R);
+  const int XS = PASS_X_ROW * pass_x_rows(R), SB = pass_x_block_bytes(R);
+
+  // ---- the conversion of one block's raw bf16 rows into its image, in place.
+  // Rows go in pairs, 32 lanes (gg, t) per row: x[r, 64 gg + 4 t + {0..3}] and
+  // the same 32 further on make operand (gg, t).  Pairs are taken two at a time
+  // from the last to the first (pair 0 twice when their number is odd), both
+  // read before either is written.  Pair pp's operands go to 1056 pp and up,
+  // over raw pairs pp and pp + 1 only (1056 pp + 1040 <= 1024 (pp + 2) for
+  // pp < 16), and a wave's LDS reads and writes run in program order: every raw
+  // row is read before anything is written over it.
+  auto convert_block = [&](uint8_t* slot) __attribute__((always_inline)) {
+    const int half = lane >> 5, sub = lane & 31, gg = sub >> 3, t = sub & 7;
+    const uint8_t* const in = slot + half * 512 + (64 * gg + 4 * t) * 2;
+    uint8_t* const out = slot + half * PASS_X_ROW + sub * 16;
+    auto sums = [&](u32x2 lo, u32x2 hi, int r) __attribute__((always_inline)) {
+      if constexpr (MSUM) {
+        // sub-block sums: the 8 lanes t of lane group gg add their run sums as
+        // ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
+        float s0 = sum4_bf16(lo.x, lo.y), s1 = sum4_bf16(hi.x, hi.y);
+        s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
+        s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
+        s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
+        if (r < R && t == 0) *reinterpret_cast<f32x2*>(slot + XS + (gg * R + r) * 8) = f32x2{s0, s1};
+      }
+    };
+    for (int pp = ((R + 1) >> 1) - 1; pp >= 0; pp -= 2) {
+      const int qq = pp > 0 ? pp - 1 : 0;
+      const u32x2 lo0 = *reinterpret_cast<const u32x2*>(in + pp * 1024);
+      const u32x2 hi0 = *reinterpret_cast<const u32x2*>(in + pp * 1024 + 64);
+      const u32x2 lo1 = *reinterpret_cast<const u32x2*>(in + qq * 1024);
+      const u32x2 hi1 = *reinterpret_cast<const u32x2*>(in + qq * 1024 + 64);
+      *reinterpret_cast<f16x8*>(out + pp * 2 * PASS_X_ROW) = build_a(lo0.x, lo0.y, hi0.x, hi0.y);
+      sums(lo0, hi0, 2 * pp + half);
+      *reinterpret_cast<f16x8*>(out + qq * 2 * PASS_X_ROW) = build_a(lo1.x, lo1.y, hi1.x, hi1.y);
+      sums(lo1, hi1, 2 * qq + half);
+    }
+  };
+  // the conversion of a GEMM's xblk blocks is shared by all waves of the
+  // workgroup: wave v (compute waves 0 .. PASS_NC - 1, then the helpers) takes
+  // the blocks b = v mod (PASS_NC + PASS_NH)
+  auto convert_share = [&](int xblk, int v) __attribute__((always_inline)) {
+    for (int b = v; b < xblk; b += PASS_NC + PASS_NH) convert_block(xlds + b * SB);
+  };
 
   if (wv < PASS_NC) {
     // ======================= compute wave ======================================
     const int w = wv;
-    int xoff = 0;                                // this lane's A-operand offset inside a step
-    {
-      const int r = nl < R ? nl : R - 1;         // rows >= R reuse row R - 1 (never stored)
-      xoff = (g4 * R + r) * 16;
-    }
+    // this lane's A operands (step t at + 16 t) and sub-block sums inside a slot;
+    // rows >= R reuse row R - 1 (never stored)
+    const int xr = nl < R ? nl : R - 1;
+    const int xoff = xr * PASS_X_ROW + g4 * 128, soff = XS + (g4 * R + xr) * 8;
     const PassWave* __restrict__ waves = a.waves;
     // the wave's share of GEMM g, or of the first later GEMM with steps for it
     auto enter = [&](Span& s, int g) __attribute__((always_inline)) {
-      PassWave v = g < G ? get_wave(waves, (g * P + p) * PASS_NC + w) : PassWave{0, 0, 0, G};
+      PassWave v = g < G ? get_wave(waves, (g * P + p) * PASS_NC + w) : PassWave{0, 0, 0, G, 0};
       if (v.count == 0 && v.next < G) {
         g = v.next;
         v = get_wave(waves, (g * P + p) * PASS_NC + w);
@@ -229,27 +286,38 @@ pass_kernel(PassArgs a) {
       asm volatile("" : "+v"(dd), "+v"(dm));
       f32x4 ds = {0.f, 0.f, 0.f, 0.f}, ms = {0.f, 0.f, 0.f, 0.f};
       const int base = slot * SB;
-      for (int t = 0; t < 8; ++t) {
-        const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + t * XT + xoff);
-        const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
-        ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+      if constexpr (MSUM) {
+        for (int t = 0; t < 8; ++t) {
+          const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff + t * 16);
+          const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+          ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+        }
+        const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff);
+        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
+        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
+      } else {
+        const f16x8 bm = build_m_full(cst);
+        for (int t = 0; t < 8; ++t) {
+          const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff + t * 16);
+          const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+          ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+          ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bm, ms, 0, 0, 0);
+        }
       }
-      const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + XS + xoff / 2);
-      ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
-      ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
       for (int i = 0; i < 4; ++i) {
         acc[i] = __builtin_fmaf(dd, ds[i], acc[i]);
         acc[i] = __builtin_fmaf(dm, ms[i], acc[i]);
       }
     };
     // piece k of this wave's sub-range (one per unit it touches) into slot k mod
-    // PASS_PIECES, once helper 0 has taken piece k - PASS_PIECES
+    // PASS_PIECES, once a helper has taken piece k - PASS_PIECES from it (the
+    // slot's k / PASS_PIECES earlier pieces added)
     auto put_piece = [&](Span& s) __attribute__((always_inline)) {
       const uint32_t k = (uint32_t)s.k;
       s.k = uni(s.k + 1);
       if (k >= PASS_PIECES) {
         uint32_t n = 0;
-        while (lds_load(&s_consumed[w]) + PASS_PIECES <= k) {
+        while (lds_load(&s_consumed[w][k % PASS_PIECES]) < k / PASS_PIECES) {
           if (++n > LDS_SPIN_LIMIT) break;
           __builtin_amdgcn_s_sleep(1);
         }
@@ -261,7 +329,17 @@ pass_kernel(PassArgs a) {
       if (lane == 0) lds_store(&s_written[w], k + 1);
     };
 
-    int passed = 0;                              // workgroup barriers passed (one per GEMM)
+    // the wave's part in the staging of GEMM g: once the helpers' copies of the
+    // raw activations have landed, convert its share of the blocks; the GEMM's
+    // steps start after every wave's share is done
+    auto stage_gemm = [&](int g) __attribute__((always_inline)) {
+      const int xblk = uni(xblk_of(waves, (g * P + p) * PASS_NC + w));
+      __builtin_amdgcn_s_barrier();
+      convert_share(xblk, w);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_s_barrier();
+    };
+    int passed = 0;                              // GEMMs staged so far
     Span L, C;
     enter(C, 0);
     L = C;
@@ -271,18 +349,7 @@ pass_kernel(PassArgs a) {
       load_w(W[decltype(SL)::value], L);
       advance(L);
     };
-    fill(std::integral_constant<int, 0>{});
-    fill(std::integral_constant<int, 1>{});
-    fill(std::integral_constant<int, 2>{});
-    fill(std::integral_constant<int, 3>{});
-    if constexpr (RING > 4) {
-      fill(std::integral_constant<int, 4 % RING>{});
-      fill(std::integral_constant<int, 5 % RING>{});
-    }
-    if constexpr (RING > 6) {
-      fill(std::integral_constant<int, 6 % RING>{});
-      fill(std::integral_constant<int, 7 % RING>{});
-    }
+    for_each_slot(fill, std::make_integer_sequence<int, RING>{});
     // one step at ring slot s; true at the end of the sequence
     auto step = [&](auto SL) __attribute__((always_inline)) -> bool {
       constexpr int s = decltype(SL)::value;
@@ -296,34 +363,23 @@ pass_kernel(PassArgs a) {
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       advance(C);
-      while (passed <= C.g && C.g < G) {         // the next step's GEMM: its activations are staged past this
-        __builtin_amdgcn_s_barrier();
+      while (passed <= C.g && C.g < G) {         // the next step's GEMM: stage it first
+        stage_gemm(passed);
         passed = uni(passed + 1);
       }
       return C.g >= G;
     };
     while (passed <= C.g && C.g < G) {
-      __builtin_amdgcn_s_barrier();
+      stage_gemm(passed);
       passed = uni(passed + 1);
     }
     if (C.g < G)
     for (;;) {
-      step(std::integral_constant<int, 0>{});
-      step(std::integral_constant<int, 1>{});
-      step(std::integral_constant<int, 2>{});
-      step(std::integral_constant<int, 3>{});
-      if constexpr (RING > 4) {
-        step(std::integral_constant<int, 4 % RING>{});
-        step(std::integral_constant<int, 5 % RING>{});
-      }
-      if constexpr (RING > 6) {
-        step(std::integral_constant<int, 6 % RING>{});
-        step(std::integral_constant<int, 7 % RING>{});
-      }
+      for_each_slot(step, std::make_integer_sequence<int, RING>{});
       if (C.g >= G) break;
     }
     while (passed < G) {                         // GEMMs past this wave's last step
-      __builtin_amdgcn_s_barrier();
+      stage_gemm(passed);
       passed = uni(passed + 1);
     }
     return;
@@ -331,65 +387,47 @@ pass_kernel(PassArgs a) {
 
   // ========================= helper waves ========================================
   const int h = wv - PASS_NC;                    // 0 .. PASS_NH - 1
-  const int htid = tid - PASS_NC * 64;           // 0 .. 64 PASS_NH - 1
   uint32_t* const bar = a.bar;
   const int groups = P < 8 ? P : 8;
   const int grp = p % 8, members = (P - grp + 7) / 8;
   bool dead = false;                             // a device-wide wait gave up: no more waiting
 
   if (h == 0) {
-    if (lane < PASS_NC) {
-      s_written[lane] = 0u;
-      s_consumed[lane] = 0u;
+    if (lane < PASS_NC * PASS_PIECES) (&s_consumed[0][0])[lane] = 0u;
+    if (lane < PASS_NC) s_written[lane] = 0u;
+    if (lane == 0) {
+      s_go = 0u;
+      s_done = 0u;
     }
-    if (lane == 0) s_go = 0u;
   }
 
   // ---- the activations of GEMM g for this workgroup's chunk: block c kbc + b of x
-  // goes to slot b.  A slot holds 8 steps of XT bytes (lane group gg, row r: the
-  // 16-byte binary16 A operand built from x[r, 256 j + 64 gg + 4 t + {0..3}] and the
-  // same 32 further on), then the fp32 sums of sub-blocks 2 gg and 2 gg + 1 per
-  // row.  32 threads per (slot, row); every (slot, row) of the chunk in one batch.
-  constexpr int HGROUPS = PASS_NH * 64 / 32;     // (slot, row) pairs per batch row
-  constexpr int XB = 16;                         // batch rows in flight per thread
-  auto stage = [&](const PassGemm& d, int c) __attribute__((always_inline)) {
-    const int sub = htid & 31, gg = sub >> 3, t = sub & 7, grp_id = htid >> 5;
+  // goes to slot b, and helper h copies the blocks b = h mod PASS_NH: row r of
+  // the block (512 bytes of bf16) to slot + 512 r, two rows per load that
+  // writes LDS directly (lane l's 16 bytes land at the load's base + 16 l), all
+  // of the helper's loads in flight together.  All waves then convert the
+  // blocks in place (convert_share).
+  auto stage_raw = [&](const PassGemm& d, int c) __attribute__((always_inline)) {
     const int K = d.KB * SB_W;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
-    const int pairs = d.kbc * R;
-    for (int base = 0; base < pairs; base += XB * HGROUPS) {
-      u32x2 lo[XB], hi[XB];
-#pragma unroll
-      for (int k = 0; k < XB; ++k) {
-        const int q = base + k * HGROUPS + grp_id;            // (slot, row) = (q / R, q % R)
-        const int b = q / R, r = q - b * R;
-        const uint32_t off = (uint32_t)((r * K + (c * d.kbc + b) * SB_W + 64 * gg + 4 * t) * 2);
-        lo[k] = bload<u32x2, 0>(xr, q < pairs ? off : OOB);
-        hi[k] = bload<u32x2, 0>(xr, q < pairs ? off + 64 : OOB);
-      }
-#pragma unroll
-      for (int k = 0; k < XB; ++k) {
-        const int q = base + k * HGROUPS + grp_id;
-        if (q >= pairs) continue;
-        const int b = q / R, r = q - b * R;
-        *reinterpret_cast<f16x8*>(xlds + b * SB + t * XT + (gg * R + r) * 16) =
-            build_a(lo[k].x, lo[k].y, hi[k].x, hi[k].y);
-        // sub-block sums: the 8 threads t of lane group gg add their run sums as
-        // ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
-        float s0 = sum4_bf16(lo[k].x, lo[k].y), s1 = sum4_bf16(hi[k].x, hi[k].y);
-        s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
-        s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
-        s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
-        if (t == 0) *reinterpret_cast<f32x2*>(xlds + b * SB + XS + (gg * R + r) * 8) = f32x2{s0, s1};
+    const int RP = (R + 1) >> 1, half = lane >> 5;
+    for (int b = h; b < d.kbc; b += PASS_NH) {
+      const uint32_t blk = (uint32_t)((c * d.kbc + b) * SB_W * 2) + (uint32_t)(lane & 31) * 16u;
+      for (int pr = 0; pr < RP; ++pr) {
+        const int r = 2 * pr + half;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void*)(xlds + b * SB + pr * 1024), 16,
+            r < R ? (uint32_t)(r * K * 2) + blk : OOB, 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);        // the raw rows are in LDS
+    asm volatile("" ::: "memory");
   };
 
   // ---- device-wide barrier after GEMM g (generation g + 1): arrive at the
   // group counter of workgroups p mod 8; the group's last arrival arrives at the
-  // global counter.  Arrival waits only for helper 0's own stores.
+  // global counter.  Every helper's stores of GEMM g are complete by then.
   auto grid_arrive = [&](int g) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) {
       const uint32_t gen = (uint32_t)g + 1;
       const uint32_t old = __hip_atomic_fetch_add(bar + 32 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -412,16 +450,17 @@ pass_kernel(PassArgs a) {
     }
   };
 
-  // ---- helper 0: the units of GEMM g, in order: add each unit's pieces in wave
-  // order, then y (one chunk) or the chunk's partial tile; after the last unit the
-  // chunk sums of the sub-tiles whose last chunk this workgroup was.
+  // ---- the units of GEMM g, helper h taking units h, h + PASS_NH, ... in order:
+  // add each unit's pieces in wave order, then y (one chunk) or the chunk's
+  // partial tile; after its last unit the chunk sums of those of its sub-tiles
+  // whose last chunk this workgroup was.
   auto finish = [&](const PassGemm& d, int c, int ns0, int ns1) __attribute__((always_inline)) {
     const int units = ns1 - ns0, n = units * d.kbc;
     // y goes out device-coherent: the next GEMM may run on any die
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
     const uint32_t part_tile = (uint32_t)d.NS * 1024u;                 // bytes of one chunk's partials
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
-    for (int u = 0; u < units; ++u) {
+    for (int u = h; u < units; u += PASS_NH) {
       const int w_lo = pass_step_owner(u * d.kbc, PASS_NC, n);
       const int w_hi = pass_step_owner((u + 1) * d.kbc - 1, PASS_NC, n);
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
@@ -438,7 +477,7 @@ pass_kernel(PassArgs a) {
         sum += pieces[(w * PASS_PIECES + k % PASS_PIECES) * 64 + lane];
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // and before its slot is handed back
         asm volatile("" ::: "memory");
-        if (lane == 0) lds_store(&s_consumed[w], (uint32_t)k + 1);
+        if (lane == 0) lds_store(&s_consumed[w][k % PASS_PIECES], (uint32_t)(k / PASS_PIECES) + 1u);
       }
       const int ns = ns0 + u;
       if (d.S == 1) {
@@ -452,16 +491,17 @@ pass_kernel(PassArgs a) {
         bstore_sc1(sum, pr, (uint32_t)c * part_tile + (uint32_t)ns * 1024u + lane * 16);
       }
     }
-    if (d.S == 1 || units == 0) return;
-    // every partial tile of this workgroup is stored; arrive at each unit's
-    // sub-tile counter (one lane per unit); the last of the S chunks to arrive adds
-    // the S partial tiles in chunk order and writes y
+    const int mine = units > h ? (units - h + PASS_NH - 1) / PASS_NH : 0;   // this helper's units
+    if (d.S == 1 || mine == 0) return;
+    // every partial tile of this helper is stored; arrive at each unit's sub-tile
+    // counter (one lane per unit); the last of the S chunks to arrive adds the S
+    // partial tiles in chunk order and writes y
     __builtin_amdgcn_s_waitcnt(0);
-    for (int u0 = 0; u0 < units; u0 += 64) {
+    for (int u0 = 0; u0 < mine; u0 += 64) {
       bool last = false;
-      if (u0 + lane < units) {
-        const uint32_t old = __hip_atomic_fetch_add(a.cnt + ns0 + u0 + lane, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+      if (u0 + lane < mine) {
+        const int ns = ns0 + h + PASS_NH * (u0 + lane);
+        const uint32_t old = __hip_atomic_fetch_add(a.cnt + ns, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = old == (uint32_t)(d.S - 1);
       }
       uint64_t mask = __builtin_amdgcn_ballot_w64(last);
@@ -469,7 +509,7 @@ pass_kernel(PassArgs a) {
         // one sub-tile at a time, all its chunks' loads in flight together
         const int uu = __builtin_ctzll(mask);
         mask &= mask - 1;
-        const int ns = ns0 + u0 + uu;
+        const int ns = ns0 + h + PASS_NH * (u0 + uu);
         f32x4 v[PASS_MAX_CHUNKS];
 #pragma unroll
         for (int cc = 0; cc < PASS_MAX_CHUNKS; ++cc)
@@ -497,10 +537,8 @@ pass_kernel(PassArgs a) {
     if (g > 0) {
       if (h == 0) {
         grid_wait(g - 1);
-        if (lane < PASS_NC) {
-          lds_store(&s_written[lane], 0u);
-          lds_store(&s_consumed[lane], 0u);
-        }
+        if (lane < PASS_NC * PASS_PIECES) lds_store(&s_consumed[0][0] + lane, 0u);
+        if (lane < PASS_NC) lds_store(&s_written[lane], 0u);
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
         if (lane == 0) lds_store(&s_go, (uint32_t)g);
       } else {
@@ -511,18 +549,27 @@ pass_kernel(PassArgs a) {
         }
       }
     }
-    if (ns1 > ns0) stage(d, c);
+    if (ns1 > ns0) stage_raw(d, c);
+    __builtin_amdgcn_s_barrier();                // the raw activations of GEMM g are in LDS
+    convert_share(ns1 > ns0 ? d.kbc : 0, PASS_NC + h);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    __builtin_amdgcn_s_barrier();                // the activations of GEMM g are in LDS
-    if (h == 0) {
-      finish(d, c, ns0, ns1);
-      if (g + 1 < G) grid_arrive(g);
+    __builtin_amdgcn_s_barrier();                // and converted
+    finish(d, c, ns0, ns1);
+    __builtin_amdgcn_s_waitcnt(0);               // this helper's stores of GEMM g are complete
+    asm volatile("" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (h == 0 && g + 1 < G) {
+      uint32_t n = 0;
+      while (lds_load(&s_done) < (uint32_t)(PASS_NH * (g + 1))) {
+        if (++n > LDS_SPIN_LIMIT) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      grid_arrive(g);
     }
   }
 
   // the last workgroup out re-arms the barrier counters for the next launch
   if (h == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(bar + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == (uint32_t)P - 1 ? 1u : 0u;
@@ -535,18 +582,20 @@ pass_kernel(PassArgs a) {
   }
 }
 
-hipError_t launch_pass(const PassArgs& a, hipStream_t st) {
+hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st) {
   PassArgs args = a;
   void* params[] = {&args};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&pass_kernel<PASS_RING>), dim3((unsigned)a.P),
-                                    dim3(PASS_THREADS), params, 0, st);
+  const void* k = msum ? reinterpret_cast<const void*>(&pass_kernel<PASS_RING, true>)
+                       : reinterpret_cast<const void*>(&pass_kernel<PASS_RING, false>);
+  return hipLaunchCooperativeKernel(k, dim3((unsigned)a.P), dim3(PASS_THREADS), params, 0, st);
 }
 
 int pass_occupancy() {
-  int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pass_kernel<PASS_RING>, PASS_THREADS, 0) != hipSuccess)
+  int b0 = 0, b1 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, pass_kernel<PASS_RING, false>, PASS_THREADS, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, pass_kernel<PASS_RING, true>, PASS_THREADS, 0) != hipSuccess)
     return 0;
-  return blocks;
+  return b0 < b1 ? b0 : b1;
 }
 
 }  // namespace qg

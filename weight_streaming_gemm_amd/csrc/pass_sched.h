@@ -44,11 +44,16 @@ QG_HD int pass_wave_first(int w, int NC, int n) { return (int)((int64_t)n * w / 
 // the wave whose sub-range holds step i (0 <= i < n)
 QG_HD int pass_step_owner(int i, int NC, int n) { return (int)((((int64_t)i + 1) * NC + n - 1) / n) - 1; }
 
-// LDS bytes of one block's activations for R rows: 8 steps of (64 R + 16)
-// bytes of binary16 operands (lane group, row; the 16-byte pad per step spreads
-// consecutive steps over the banks), then 8 R fp32 sub-block sums
-QG_HD int pass_x_step_bytes(int R) { return 64 * R + 16; }
-QG_HD int pass_x_block_bytes(int R) { return 8 * pass_x_step_bytes(R) + 32 * R; }
+// LDS layout of one block's activations for R rows (a slot): rows are taken
+// in pairs (R2 = R rounded up to even; a missing last row is converted like the
+// others and never read).  Row r's 32 binary16 A operands sit at PASS_X_ROW r
+// (operand (gg, t) at 16 (8 gg + t); the 16-byte pad per row puts the rows of
+// one step on different banks), then the 8 R fp32 sub-block sums at
+// PASS_X_ROW R2.  The raw bf16 rows land in the same slot first (row r at
+// 512 r) and are converted in place.
+constexpr int PASS_X_ROW = 528;
+QG_HD int pass_x_rows(int R) { return R + (R & 1); }
+QG_HD int pass_x_block_bytes(int R) { return PASS_X_ROW * pass_x_rows(R) + 32 * R; }
 
 // K chunks of a GEMM with KB blocks at R rows over P workgroups: the fewest
 // (dividing KB, at most max_chunks and at most P) whose activations fit x_area

@@ -225,12 +225,8 @@ int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStrea
   }
   StreamArgs a{};
   a.d0 = make_desc(h, x, y, p);
-  a.descs = nullptr;
   a.part = h->part;
   a.cnt = h->cnt;
-  a.sync = nullptr;
-  a.err = nullptr;
-  a.G = 1;
   a.R = R;
   a.P = (int32_t)p.P;
   a.RT = p.RT;
@@ -238,7 +234,7 @@ int run_impl(qgemm_handle* h, const void* x, float* y, int R, int path, hipStrea
   a.NW = p.NW;
   a.msum = p.msum;
   a.valu = p.path == QGEMM_PATH_VALU;
-  return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+  return launch_stream(a, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
 int device_cus(int* cus) {
@@ -418,7 +414,6 @@ int qgemm_run_static(const void* packed_dev, int64_t N, int64_t K, const void* x
   a.d0 = make_desc(&h, x_bf16, y, p);
   a.part = reinterpret_cast<float*>(base + cnt_bytes);
   a.cnt = reinterpret_cast<uint32_t*>(base);
-  a.G = 1;
   a.R = R;
   a.P = (int32_t)p.P;
   a.RT = p.RT;
@@ -426,7 +421,7 @@ int qgemm_run_static(const void* packed_dev, int64_t N, int64_t K, const void* x
   a.NW = p.NW;
   a.msum = p.msum;
   a.valu = 0;
-  return launch_stream(a, false, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
+  return launch_stream(a, st) == hipSuccess ? QGEMM_OK : QGEMM_EHIP;
 }
 
 int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t* bytes) {
@@ -645,6 +640,9 @@ std::vector<PassWave> pass_waves(const std::vector<PassGemm>& t, int P) {
       for (int w = 0; w < PASS_NC; ++w) {
         PassWave& e = v[((size_t)g * P + p) * PASS_NC + w];
         pass_wave_share(p, w, PASS_NC, P, d.NS, d.KB, d.S, d.kbc, d.rot, &e.count, &e.step0, &e.jj0);
+        int c, ns0, ns1;
+        pass_units(p, d.S, P, d.NS, d.rot, &c, &ns0, &ns1);
+        e.xblk = ns1 > ns0 ? d.kbc : 0;
       }
   }
   // next: the first later GEMM where the wave has steps
@@ -708,7 +706,8 @@ T* upload(const std::vector<T>& v) {
 extern "C" {
 
 int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32_t flags) {
-  if (!out || !handles || count < 1 || (flags & ~(uint32_t)QGEMM_SEQ_PERSISTENT)) return QGEMM_EINVAL;
+  if (!out || !handles || count < 1 || (flags & ~(uint32_t)(QGEMM_SEQ_PERSISTENT | QGEMM_SEQ_SUB_BLOCK_SUMS)))
+    return QGEMM_EINVAL;
   *out = nullptr;
   int max_R = QGEMM_MAX_R;
   for (int i = 0; i < count; ++i) {
@@ -857,7 +856,7 @@ int seq_run_impl(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, 
   a.cnt = s->cnt;
   a.bar = s->bar;
   a.err = s->err;
-  if (launch_pass(a, st) != hipSuccess) return QGEMM_EHIP;
+  if (launch_pass(a, (s->flags & QGEMM_SEQ_SUB_BLOCK_SUMS) != 0, st) != hipSuccess) return QGEMM_EHIP;
   if (argmax_idx) {
     const qgemm_handle* last = s->hs.back();
     if (launch_argmax_split(ys[s->hs.size() - 1], R, last->N, argmax_idx, s->am_ws, drafts, D, tokens, n_new, st) !=

@@ -33,16 +33,12 @@ struct GemmDesc {
   int32_t pad_;
 };
 
-// A launch of the streaming kernel: G GEMMs run one after another (GEMM g + 1
-// starts after every workgroup has finished GEMM g).
+// A launch of the streaming kernel (one GEMM).
 struct StreamArgs {
-  GemmDesc d0;             // the GEMM when G == 1
-  const GemmDesc* descs;   // device array of G GEMMs when G > 1
+  GemmDesc d0;             // the GEMM
   float* part;             // 2 V partial-tile slots of nwn * NT * RT KiB
   uint32_t* cnt;           // per-tile arrival counters, zero between launches
-  uint32_t* sync;          // G + 1 barrier counters, zero between launches (G > 1)
-  uint32_t* err;           // set to 1 when a barrier wait gave up
-  int32_t G, R, P;
+  int32_t R, P;
   int32_t RT, NT, NW;
   int32_t msum;            // 1: min term from sub-block sums staged with the
                            // activations (one product per step); 0: from the
@@ -70,7 +66,7 @@ inline int subtiles_for(int RT) { (void)RT; return 1; }
 inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn * NT * RT * 1024; }
 
 hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K, hipStream_t st);
-hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st);
+hipError_t launch_stream(const StreamArgs& a, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 // rows tiled as well as outputs (prefill.hip; plan and image layout in prefill_plan.h):
@@ -112,7 +108,8 @@ struct PassGemm {
 // block `jj0` of the chunk; `next` = the first later GEMM where the wave has
 // steps (G if none).
 struct PassWave {
-  int32_t count, step0, jj0, next;
+  int32_t count, step0, jj0, next;   // steps, first packed step and block, next GEMM with steps
+  int32_t xblk;                      // activation blocks the workgroup stages (0: no units)
 };
 struct PassArgs {
   const PassGemm* gemms;   // device table of G GEMMs
@@ -133,7 +130,7 @@ constexpr int PASS_RING = 8;                     // weight steps in flight per c
 constexpr int PASS_MAX_CHUNKS = 16;
 constexpr int PASS_BAR_WORDS = 512;
 constexpr int PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256;
-hipError_t launch_pass(const PassArgs& a, hipStream_t st);
+hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st);
 int pass_occupancy();                            // resident workgroups per CU (0: none)
 
 // The allocation-free entry point's fixed device scratch (qgemm_run_static):

@@ -120,20 +120,12 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 // (each slot refilled right after its step) up to the end of the wave's
 // sub-range.  Loads past the end of the work address beyond the buffer and
 // return zeros without memory traffic.
-//
-// With G > 1 all workgroups are resident (cooperative launch) and GEMM g + 1
-// starts only after every workgroup has finished GEMM g, as in a model where
-// each projection's input depends on the previous output: a workgroup closes
-// its range, arrives at the grid barrier (waiting only for its own stores),
-// requests the first RING steps of its next range (weights do not depend on
-// the previous output), and then waits.
 #ifndef QG_RING
 #define QG_RING 4
 #endif
 constexpr int RING = QG_RING;                  // weight ring depth, steps (4, 6 or 8)
 static_assert(RING == 4 || RING == 6 || RING == 8, "the main loop unrolls 4, 6 or 8 steps");
 constexpr uint32_t OOB = 0x80000000u;          // beyond every buffer (sizes < 2^31)
-constexpr uint32_t SPIN_LIMIT = 1u << 21;      // barrier polls before giving up
 constexpr int SC1 = 16;                        // cache policy: coherent across the device
 
 // aux 2 = streaming (non-temporal) hint for data read once; 0 for shared data
@@ -185,7 +177,7 @@ struct WStage {
 
 // where a wave stands in its sequence of steps (uniform across the wave)
 struct Cursor {
-  int g;          // GEMM index; >= G when past the end
+  int g;          // 0 for the launch's GEMM; 1 past the end
   int v;          // range index
   int A, B;       // the range's steps
   int it, it1;    // current step and end of this wave's sub-range
@@ -203,53 +195,26 @@ struct Cursor {
 // the end of each segment into the matrix-core accumulator layout.
 constexpr int VROWS = 4;
 
-template <int RT, int NT, int NW, bool MULTI, bool MSUM, int VR = 0>
+template <int RT, int NT, int NW, bool MSUM, int VR = 0>
 __global__ void __launch_bounds__(NW * 64, NW / 4)
-stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
+stream_kernel(StreamArgs a) {
   constexpr bool VALU = VR > 0;
-  static_assert(VR <= VROWS && (!VALU || (RT == 1 && NT == 1 && MSUM && !MULTI)), "vector-unit variant: one row tile");
+  static_assert(VR <= VROWS && (!VALU || (RT == 1 && NT == 1 && MSUM)), "vector-unit variant: one row tile");
   constexpr int NTHR = NW * 64;
   constexpr int XAREA = x_area_bytes(RT, NT, NW);
   __shared__ __attribute__((aligned(16))) uint8_t xlds[XAREA];
   __shared__ f32x4 pieces[NW * 2 * NT * RT * 64];
-  __shared__ uint32_t s_flag;
   __shared__ uint32_t s_last[2];
   __shared__ uint8_t s_chunk_last[NTHR];         // K in chunks: last arrivals of a range's tiles
 
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
-  const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
+  const int p = blockIdx.x, P = a.P, R = a.R;
+  constexpr int G = 1;                            // one GEMM per launch
   const int XT = 64 * R + 16;                     // LDS bytes of one step's activations
   const int XS = 8 * XT;                          // offset of a block's sub-block sums
   const int SB = XS + (MSUM ? 8 * 4 * R : 0);     // LDS bytes of one block's activations
 
-  // descriptor of GEMM g; fields of the device table are made explicitly
-  // wave-uniform so that buffer resources built from them stay scalar
-  auto get_desc = [&](int g) __attribute__((always_inline)) -> GemmDesc {
-    if constexpr (MULTI) {
-      typedef const GemmDesc __attribute__((address_space(4)))* const_desc_ptr;
-      const const_desc_ptr src = (const_desc_ptr)(descs + g);
-      GemmDesc d;
-      d.packed = uniform_ptr(src->packed);
-      d.x = uniform_ptr(src->x);
-      d.y = uniform_ptr(src->y);
-      d.quant_bytes = (uint32_t)uni((int)src->quant_bytes);
-      d.hdr_bytes = (uint32_t)uni((int)src->hdr_bytes);
-      d.N = uni(src->N);
-      d.NS = uni(src->NS);
-      d.KB = uni(src->KB);
-      d.nwn = uni(src->nwn);
-      d.T = uni(src->T);
-      d.I = uni(src->I);
-      d.V = uni(src->V);
-      d.aligned = uni(src->aligned);
-      d.S = uni(src->S);
-      d.kbr = uni(src->kbr);
-      d.treal = uni(src->treal);
-      return d;
-    } else {
-      return a.d0;
-    }
-  };
+  auto get_desc = [&](int) __attribute__((always_inline)) -> GemmDesc { return a.d0; };
   // range v of the cursor's GEMM and this wave's sub-range of it
   auto set_range = [&](Cursor& c) __attribute__((always_inline)) {
     if (c.aligned) {
@@ -334,7 +299,7 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
   // workgroup index (all workgroups read the same activations).  The loads of
   // the first batch are issued on their own (x_load) so that the kernel can
   // queue them ahead of the weight ring. ---
-  constexpr int XGROUPS = NTHR / 32, XB = (MULTI && RT > 2) ? 8 : 16;   // (registers)
+  constexpr int XGROUPS = NTHR / 32, XB = 16;
   u32x2 xlo[XB], xhi[XB];
   // (slot, row) of this thread's k-th row of the batch at base, rows = nslots R;
   // slots rotated by the workgroup index.  Walked incrementally: one division.
@@ -702,29 +667,6 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
     __syncthreads();                              // pieces and activations may be reused
   };
 
-  // ---- all workgroups finished GEMM g (bounded wait; a timeout sets err) -----
-  // Arrival waits only for this workgroup's own stores (the ring holds no loads
-  // then: its refills past the range end address nothing); the weights of the
-  // next GEMM are requested between arrival and the wait.
-  auto grid_arrive = [&](int g) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(a.sync + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto grid_wait = [&](int g) __attribute__((always_inline)) {
-    if (tid == 0) {
-      uint32_t n = 0;
-      while (__hip_atomic_load(a.sync + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)P) {
-        if (++n > SPIN_LIMIT) {
-          __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    __syncthreads();
-  };
-
   // ---- prologue: the first activation batch, then the weight ring (the load
   // cursor starts RING steps ahead) ---------------------------------------------
   Cursor L, C;
@@ -806,48 +748,12 @@ stream_kernel(StreamArgs a, const GemmDesc* __restrict__ descs) {
       }
     }
   };
-  if constexpr (!MULTI) {
-    start_range();
-    if constexpr (MSUM) ring_fill();
-    if (C.it < C.it1) {
-      run_ring([&](auto S) __attribute__((always_inline)) { return step(S); });
-    }
-    close_range(C, D);
-  } else {
-    // Several GEMMs, each as in a launch of one: the ring stops at the end of a
-    // wave's sub-range (its last refills address nothing), the range closes, the
-    // workgroup arrives at the grid barrier, requests the first RING steps of
-    // its next sub-range (weights do not depend on the previous output), then
-    // waits for every workgroup and stages the activations.  The step loop
-    // restarts at ring slot 0 for every GEMM.
-    start_range();
-    for (;;) {
-      if (C.it < C.it1) run_ring([&](auto S) __attribute__((always_inline)) { return step(S); });
-      close_range(C, D);
-      if (C.g + 1 >= G) break;
-      grid_arrive(C.g);
-      const int g = C.g;
-      enter(C, g + 1);
-      D = get_desc(C.g);
-      L = C;
-      ring_fill();
-      grid_wait(g);
-      x_load(D, C.jb, C.A % C.KB, (int)x_slots<uint32_t>(C.A, C.B, C.KB), tid >> 5);
-      start_range();
-    }
+  start_range();
+  if constexpr (MSUM) ring_fill();
+  if (C.it < C.it1) {
+    run_ring([&](auto S) __attribute__((always_inline)) { return step(S); });
   }
-
-  if constexpr (MULTI) {
-    // the last workgroup out re-arms the barrier counters for the next launch
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.sync + G, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = (prev == (uint32_t)P - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_flag)
-      for (int i = tid; i <= G; i += NTHR) __hip_atomic_store(a.sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  close_range(C, D);
 }
 
 // ---------------------------------------------------------------------------
@@ -1079,48 +985,32 @@ hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t
 
 #define QG_STREAM_VARIANTS(X) X(1, 1, 8) X(2, 1, 8) X(3, 1, 8) X(4, 1, 8)
 
-template <int RT, int NT, int NW, bool MSUM>
-static hipError_t launch_stream_m(const StreamArgs& a, bool cooperative, hipStream_t st) {
-  if (a.G == 1 && !cooperative) {
-    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, false, MSUM>), dim3((unsigned)a.P), dim3(NW * 64), 0, st, a,
-                       (const GemmDesc*)nullptr);
-    return hipGetLastError();
-  }
-  // one launch over several GEMMs: the min term per step (no sub-block sums)
-  if constexpr (MSUM) {
-    return hipErrorInvalidValue;
-  } else {
-    StreamArgs args = a;
-    const GemmDesc* descs = a.descs;
-    void* params[] = {&args, &descs};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stream_kernel<RT, NT, NW, true, false>),
-                                      dim3((unsigned)a.P), dim3(NW * 64), params, 0, st);
-  }
-}
 template <int RT, int NT, int NW>
-static hipError_t launch_stream_t(const StreamArgs& a, bool cooperative, hipStream_t st) {
+static hipError_t launch_stream_t(const StreamArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.P), block(NW * 64);
   if constexpr (RT == 1 && NT == 1 && NW == 8) {
     if (a.valu) {
-      if (a.G != 1 || cooperative || !a.msum || a.R < 1 || a.R > VROWS) return hipErrorInvalidValue;
-      const dim3 grid((unsigned)a.P), block(NW * 64);
-      const GemmDesc* nd = nullptr;
+      if (!a.msum || a.R < 1 || a.R > VROWS) return hipErrorInvalidValue;
       switch (a.R) {
-        case 1: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 1>), grid, block, 0, st, a, nd); break;
-        case 2: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 2>), grid, block, 0, st, a, nd); break;
-        case 3: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 3>), grid, block, 0, st, a, nd); break;
-        default: hipLaunchKernelGGL((stream_kernel<1, 1, 8, false, true, 4>), grid, block, 0, st, a, nd); break;
+        case 1: hipLaunchKernelGGL((stream_kernel<1, 1, 8, true, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((stream_kernel<1, 1, 8, true, 2>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((stream_kernel<1, 1, 8, true, 3>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((stream_kernel<1, 1, 8, true, 4>), grid, block, 0, st, a); break;
       }
       return hipGetLastError();
     }
   }
   if (a.valu) return hipErrorInvalidValue;
-  return a.msum ? launch_stream_m<RT, NT, NW, true>(a, cooperative, st)
-                : launch_stream_m<RT, NT, NW, false>(a, cooperative, st);
+  if (a.msum)
+    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((stream_kernel<RT, NT, NW, false>), grid, block, 0, st, a);
+  return hipGetLastError();
 }
 
-hipError_t launch_stream(const StreamArgs& a, bool cooperative, hipStream_t st) {
+hipError_t launch_stream(const StreamArgs& a, hipStream_t st) {
 #define QG_CASE(rt, nt, nw) \
-  if (a.RT == rt && a.NT == nt && a.NW == nw) return launch_stream_t<rt, nt, nw>(a, cooperative, st);
+  if (a.RT == rt && a.NT == nt && a.NW == nw) return launch_stream_t<rt, nt, nw>(a, st);
   QG_STREAM_VARIANTS(QG_CASE)
 #undef QG_CASE
   return hipErrorInvalidValue;
@@ -1134,13 +1024,12 @@ bool stream_variant_exists(int RT, int NT, int NW) {
   return false;
 }
 
-// resident workgroups per CU of the multi-GEMM variant (the single-GEMM
-// variant has the same LDS footprint)
+// resident workgroups per CU of a variant (both min-term forms have the same LDS footprint)
 int stream_occupancy(int RT, int NT, int NW) {
   int blocks = 0;
 #define QG_CASE(rt, nt, nw) \
   if (RT == rt && NT == nt && NW == nw) { \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true, false>, nw * 64, 0) != \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<rt, nt, nw, true>, nw * 64, 0) != \
         hipSuccess) \
       return 0; \
     return blocks; \
