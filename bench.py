@@ -10,9 +10,14 @@ stacked activation rows (4 agents x (1 token + 2 drafts)
 bytes (144 B per 256 weights).  Inputs are seeded synthetic data of those
 shapes and distributions, resident in HBM before timing.
 
+A pass runs as one cooperative launch of the pass kernel where it serves the
+row count (up to 16 rows), else as a replayed graph of one streaming-kernel
+launch per GEMM (--launch picks one of them for every row count).
+
 Prints one JSON line (rank 0): effective weight GB/s and ms per pass, with a
-roofline record for the dominant kernel and the fp64 CPU oracle timed on a
-bounded sample beside it.  Extra detail goes to stderr.
+roofline record for the dominant kernel (and the device's practical read
+ceiling from a plain read kernel) and the fp64 CPU oracle timed on a bounded
+sample beside it.  Extra detail goes to stderr.
 """
 from __future__ import annotations
 
@@ -331,9 +336,10 @@ def prefill_report(seed: int, chunks, copies: int = 2):
 def ragged_report(seed: int, steps: int):
     """The full pass under a seeded schedule of active agents: step t runs R_t =
     3 * a_t rows (a_t uniform in 1..4), with fresh activations per step (1 % of
-    them scaled by 50).  Each step is one graph replay of the 257 GEMMs and the
-    head's argmax (one graph per row count, captured before timing); the timed
-    events bracket the pass only, not the copy of the step's activations."""
+    them scaled by 50).  Each step is one persistent launch of the 257 GEMMs
+    and the head's argmax (one descriptor table per row count, uploaded before
+    timing); the timed events bracket the pass only, not the copy of the step's
+    activations."""
     import numpy as np
     import torch
     import synth
@@ -349,7 +355,7 @@ def ragged_report(seed: int, steps: int):
     xs_t = [{w: torch.from_numpy(synth.x_bf16(seed, 1000 * (t + 1) + sid, R, w, outlier_p=0.01).view(np.int16))
              .to(dev) for w, sid in W.X_STREAM.items()} for t, R in enumerate(sched)]
     xbuf = {R: {w: torch.empty((R, w), dtype=torch.int16, device=dev) for w in W.X_STREAM} for R in set(sched)}
-    seq = wsg.Seq(gemms)
+    seq = wsg.Seq(gemms, persistent=max(sched) <= 16)   # one cooperative launch per step (rows <= 16)
 
     def one_step(t, R, ev=None):
         for w in W.X_STREAM:
@@ -441,45 +447,48 @@ def attention_report(seed: int, reps: int = 20):
 
 # the sources the streaming kernel and its launches are built from (the decode
 # attention and the row-tiled prompt kernel live in files of their own)
-STREAM_SOURCES = ("layout.h", "operand.h", "qgemm_api.cpp", "qgemm_internal.h", "qgemm_kernels.hip", "stream_sched.h")
+# the dominant kernel of each launch mode: (name prefix in traces, sources whose
+# code the counters describe, summary file under profiles/)
+KERNELS = {
+    "pass": ("qg::pass_kernel<", ("layout.h", "operand.h", "pass.hip", "pass_sched.h", "qgemm_api.cpp",
+                                  "qgemm_internal.h"), "pass_kernel_full_pass_R12.md"),
+    "stream": ("qg::stream_kernel<1, 1, 8", ("layout.h", "operand.h", "qgemm_api.cpp", "qgemm_internal.h",
+                                             "qgemm_kernels.hip", "stream_sched.h"), "stream_kernel_full_pass_R12.md"),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the streaming kernel's sources with comments and blank space
-    removed: identifies the code a counter run measured (a comment edit does
-    not make the counters stale; any code change does)."""
+def kernel_source_digest(kind: str) -> str:
+    """sha256 over a kernel's sources with comments and blank space removed:
+    identifies the code a counter run measured (a comment edit does not make the
+    counters stale; any code change does)."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "weight_streaming_gemm_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name in STREAM_SOURCES:
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                text = f.read()
-            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # the sources hold no "//" or "/*" in literals
-            text = re.sub(r"//[^\n]*", " ", text)
-            h.update(name.encode())
-            h.update(" ".join(text.split()).encode())
+    for name in sorted(KERNELS[kind][1]):
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # the sources hold no "//" or "/*" in literals
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
-def measured_traffic(R: int):
-    """HBM bytes per launch of the streaming kernel from the committed counter summary
+def measured_traffic(kind: str, R: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
     (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE runs, scaled by a copy kernel of known
-    size), or None when the kernel sources changed since the counters were taken."""
+    size), or None when the kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_digest() or rec.get("R") != R:
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_digest(kind) or rec.get("R") != R:
         return None
     return rec.get("bytes_per_launch")
-
-
-STREAM_KERNEL = "qg::stream_kernel<1, 1, 8, false"     # the R = 12 variants (both min-term forms)
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def _read_csv(path: str):
@@ -496,12 +505,14 @@ def _find_csv(d: str, suffix: str) -> str:
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: int, R: int,
+def summarize_profiles(kind: str, trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: int, R: int,
                        commands: dict) -> dict:
     """Turn one kernel-trace run and two counter runs (FETCH_SIZE, WRITE_SIZE in KiB per
-    dispatch) into profiles/traffic.json and a markdown summary.  The counters are
-    scaled so that the plain device copy of copy_mib MiB reads and writes exactly that
-    many bytes; the streaming kernel's figures are averages over its dispatches."""
+    dispatch) into a record for profiles/traffic.json and a markdown summary.  The
+    counters are scaled so that the plain device copy of copy_mib MiB reads and writes
+    exactly that many bytes; the dominant kernel's figures are averages over its
+    dispatches."""
+    prefix, _, summary = KERNELS[kind]
     stats = _read_csv(_find_csv(trace_dir, "kernel_stats.csv"))
     per = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -514,36 +525,40 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib:
     cp = per[COPY_KERNEL]
     # the copy runs three times; its largest dispatch is the full-size one
     scale = {c: copy_kib / max(cp[c]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
-    fetch, write, n_disp = [], [], 0
+    fetch, write = [], []
     for kname, v in per.items():
-        if kname.startswith(STREAM_KERNEL.replace("qg::", "void qg::")) or kname.startswith(STREAM_KERNEL):
+        if prefix in kname:
             fetch += v.get("FETCH_SIZE", [])
             write += v.get("WRITE_SIZE", [])
     fetch_b = sum(fetch) / len(fetch) * 1024 * scale["FETCH_SIZE"]
     write_b = sum(write) / len(write) * 1024 * scale["WRITE_SIZE"]
     calls = tot_ns = 0.0
     for row in stats:
-        if STREAM_KERNEL in row["Name"]:
+        if prefix in row["Name"]:
             calls += float(row["Calls"])
             tot_ns += float(row["TotalDurationNs"])
     avg_us = tot_ns / calls / 1e3
+    launch_bytes = 17990737920 if kind == "pass" else 17990737920 / 257
     rec = {
-        "kernel": "stream_kernel (all variants of the pass)",
+        "kernel": {"pass": "pass_kernel (one launch per pass: all 257 GEMMs)",
+                   "stream": "stream_kernel (all variants of the pass, one launch per GEMM)"}[kind],
         "R": R,
-        "kernel_source_sha256": kernel_source_digest(),
-        "digest": "sha256 of the streaming kernel's csrc sources with comments and blank space removed "
+        "kernel_source_sha256": kernel_source_digest(kind),
+        "digest": "sha256 of the kernel's csrc sources with comments and blank space removed "
                   "(bench.kernel_source_digest)",
         "fetch_bytes_per_launch": int(round(fetch_b)),
         "write_bytes_per_launch": int(round(write_b)),
         "bytes_per_launch": int(round(fetch_b + write_b)),
+        "algorithmic_bytes_per_launch": int(round(launch_bytes)),
         "avg_launch_us_trace": round(avg_us, 3),
         "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4), "WRITE_SIZE": round(scale["WRITE_SIZE"], 4),
                   "from": f"{COPY_KERNEL} of {copy_mib} MiB"},
-        "summary": "profiles/stream_kernel_full_pass_R12.md",
+        "summary": f"profiles/{summary}",
     }
-    alg = 17990737920 / 257
-    lines = [f"# Streaming kernel over the full 257-GEMM weight pass at R = {R}", "",
-             "Kernel-trace summary (`rocprofv3 --kernel-trace --stats`, run from /tmp with TMPDIR=/tmp):", "",
+    title = {"pass": f"Pass kernel (one cooperative launch per 257-GEMM weight pass) at R = {R}",
+             "stream": f"Streaming kernel over the full 257-GEMM weight pass at R = {R}"}[kind]
+    lines = [f"# {title}", "",
+             "Kernel-trace summary (`rocprofv3 --kernel-trace --stats`, run from the repository root with TMPDIR=/tmp):", "",
              "```", commands["trace"], "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
              "|---|---|---|---|---|---|"]
@@ -559,41 +574,148 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib:
         w_ = v.get("WRITE_SIZE", [0.0])
         lines.append(f"| `{kname[:90]}` | {len(f_)} | {sum(f_) / len(f_):.1f} | {sum(w_) / len(w_):.1f} |")
     lines += ["", "Reading the numbers (MI355X, one GPU):", "",
-              f"- The streaming kernel (both min-term variants) averages {avg_us:.2f} us per launch over "
-              f"{int(calls)} launches in the trace; a launch moves {alg / 1e6:.1f} MB of packed weights on average "
-              f"(17,990,737,920 B / 257), i.e. {alg / avg_us / 1e3:.0f} GB/s "
-              f"({alg / avg_us / 1e3 / 80:.1f} % of 8 TB/s).",
+              f"- The {kind} kernel averages {avg_us:.2f} us per launch over {int(calls)} launches in the trace; "
+              f"a launch moves {launch_bytes / 1e6:.1f} MB of packed weights, i.e. {launch_bytes / avg_us / 1e3:.0f} "
+              f"GB/s ({launch_bytes / avg_us / 1e3 / 80:.1f} % of 8 TB/s).",
               f"- Counter scale from the {copy_mib} MiB device copy ({COPY_KERNEL}): FETCH_SIZE x "
               f"{scale['FETCH_SIZE']:.3f}, WRITE_SIZE x {scale['WRITE_SIZE']:.3f}.",
-              f"- Streaming kernel, scaled, per launch on average: {fetch_b / 1e6:.1f} MB fetched "
-              f"({fetch_b / alg:.3f}x the algorithmic weight bytes; the rest is activations and partial tiles), "
-              f"{write_b / 1e6:.2f} MB written (outputs and partial tiles).", ""]
+              f"- Scaled, per launch on average: {fetch_b / 1e6:.1f} MB fetched "
+              f"({fetch_b / launch_bytes:.3f}x the algorithmic weight bytes; the rest is activations and partial "
+              f"tiles), {write_b / 1e6:.2f} MB written (outputs and partial tiles).", ""]
+    for row in stats:
+        if "read_probe_kernel" in row["Name"]:
+            nb = 4 << 30
+            rec["read_probe"] = {"bytes": nb, "avg_us_trace": round(float(row["AverageNs"]) / 1e3, 2),
+                                 "min_us_trace": round(float(row["MinNs"]) / 1e3, 2)}
+            lines[-1:-1] = [f"- Practical read ceiling: the plain read kernel (`read_probe_kernel`, the bench's "
+                            f"`roofline.practical_peak`) reads {nb} B in {float(row['AverageNs']) / 1e3:.1f} us on "
+                            f"average over {row['Calls']} calls ({nb / float(row['AverageNs']):.0f} GB/s; "
+                            f"{nb / float(row['MinNs']):.0f} GB/s at its fastest), against 8000 GB/s on paper."]
     rec["summary_text"] = "\n".join(lines)
     return rec
 
 
 def cpu_baseline(seed: int):
-    """The fp64 oracle as it stands, on layer 0's four GEMMs at R=12 (a bounded
-    sample of the pass: one of its 64 layers), all host cores."""
+    """The fp64 oracle as it stands on the host cores, on a bounded sample set.
+    All cores: the single matrix (256 x 1024) at R in 1, 3, 12, 24, 48; layer 0's
+    four GEMMs whole at R in 1, 3, 12 and cut to the first eighth of each
+    matrix's outputs at R in 24, 48; the output head's first eighth at R = 12.
+    One thread: the single matrix at every R and the first 1/64 of layer 0's
+    outputs per matrix at R = 12.  Cut samples are scaled to whole matrices by
+    bytes (the oracle's time is linear in the outputs) and labelled so; the full
+    pass at R = 12 is extrapolated (64 x layer 0 + the head); `value` is that
+    extrapolated all-core rate."""
+    import numpy as np
     import synth
     import oracle
     from synth import workloads as W
     o = oracle.get()
     threads = len(os.sched_getaffinity(0))
-    R = W.R_DEFAULT
-    total_bytes, total_t = 0, 0.0
-    for m in W.layer_mats(0):
-        parts = [synth.matrix_rows(seed, mid, n, m.K) for mid, n in zip(m.mids, m.splits)]
-        import numpy as np
-        canon = np.concatenate(parts)
-        x = synth.x_bf16(seed, W.X_STREAM[m.K], R, m.K)
+    Rs = (1, 3, 12, 24, 48)
+    t_start = time.perf_counter()
+
+    def timed(canon, N, K, x, th, frac=1):
+        rows = N if frac == 1 else max(1, N // frac)
         t0 = time.perf_counter()
-        o.gemm(canon, m.N, m.K, x, threads=threads)
-        total_t += time.perf_counter() - t0
-        total_bytes += m.packed_bytes
-    return {"value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"layer 0 of the pass (Q|K|V, O, gate|up, down; {total_bytes} packed bytes) at R={R}, "
-                      f"fp64 dequantize-then-dot, {total_t:.2f}s"}
+        o.gemm(canon[:rows * (K // 256) * 144], rows, K, x, threads=th)
+        return time.perf_counter() - t0, rows * (K // 256) * 144
+
+    def entry(t, nbytes, whole_bytes):
+        e = {"s": round(t, 5), "sample_bytes": nbytes, "GB_s": round(nbytes / t / 1e9, 5)}
+        if nbytes != whole_bytes:
+            e["whole_s_scaled"] = round(t * whole_bytes / nbytes, 3)
+        return e
+
+    sm = W.SMALL
+    one = W.Mat("single", sm["N"], sm["K"], (sm["mid"],), (sm["N"],))
+    c0 = synth.matrix_rows(sm["seed"], sm["mid"], one.N, one.K)
+    x0 = synth.x_bf16(sm["seed"], 0, max(Rs), one.K)
+    layer = [(m, np.concatenate([synth.matrix_rows(seed, mid, n, m.K) for mid, n in zip(m.mids, m.splits)]),
+              synth.x_bf16(seed, W.X_STREAM[m.K], max(Rs), m.K)) for m in W.layer_mats(0)]
+    layer_bytes = sum(m.packed_bytes for m, _, _ in layer)
+    rec = {"all_cores": {}, "one_thread": {}}
+    for R in Rs:
+        rec["all_cores"][f"single_matrix_R{R}"] = entry(*timed(c0, one.N, one.K, x0[:R], threads), one.packed_bytes)
+        rec["one_thread"][f"single_matrix_R{R}"] = entry(*timed(c0, one.N, one.K, x0[:R], 1), one.packed_bytes)
+
+    def layer_run(R, th, frac):
+        t = nb = 0
+        for m, c, x in layer:
+            dt, b = timed(c, m.N, m.K, x[:R], th, frac)
+            t += dt
+            nb += b
+        return t, nb
+
+    for R in Rs:
+        frac = 1 if R <= 12 else 8
+        rec["all_cores"][f"layer0_R{R}" + ("" if frac == 1 else "_first_eighth")] = entry(*layer_run(R, threads, frac),
+                                                                                        layer_bytes)
+    head = W.lm_head()
+    ch = np.concatenate([synth.matrix_rows(seed, mid, n, head.K) for mid, n in zip(head.mids, head.splits)])
+    xh = synth.x_bf16(seed, W.X_STREAM[head.K], 12, head.K)
+    th_, hb = timed(ch, head.N, head.K, xh, threads, 8)
+    rec["all_cores"]["head_R12_first_eighth"] = entry(th_, hb, head.packed_bytes)
+    t1, b1 = layer_run(12, 1, 64)
+    rec["one_thread"]["layer0_R12_first_64th"] = entry(t1, b1, layer_bytes)
+    t_layer = rec["all_cores"]["layer0_R12"]["s"]
+    t_head = th_ * head.packed_bytes / hb
+    full_s = 64 * t_layer + t_head
+    full_1t = (64 * layer_bytes + head.packed_bytes) / (b1 / t1)
+    rec["full_pass_R12_extrapolated"] = {
+        "all_cores_s": round(full_s, 2), "all_cores_GB_s": round(W.pass_bytes() / full_s / 1e9, 5),
+        "one_thread_s": round(full_1t, 1), "one_thread_GB_s": round(W.pass_bytes() / full_1t / 1e9, 5),
+        "how": "all cores: 64 x layer 0 at R=12 + the head at R=12 scaled from its first eighth; one thread: "
+               "the first-64th sample of layer 0 at R=12, scaled by bytes"}
+    spent = time.perf_counter() - t_start
+    return {"value": round(W.pass_bytes() / full_s / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 dequantize-then-dot on {threads} threads: single matrix 256x1024 at R in 1,3,12,24,48; "
+                      f"layer 0 (Q|K|V, O, gate|up, down) whole at R in 1,3,12 and its first eighth at R in 24,48; "
+                      f"the head's first eighth at R=12; one thread: single matrix at every R and layer 0's first "
+                      f"64th at R=12. value = full pass at R=12 extrapolated from layer 0 and the head "
+                      f"({spent:.1f}s of CPU work in all)",
+            "detail": rec}
+
+
+def read_ceiling(nbytes: int = 4 << 30, reps: int = 5):
+    """The practical HBM read ceiling: the library's plain read kernel over a
+    buffer far larger than the caches, best of `reps` (GB/s, ms)."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.empty(16384, dtype=torch.uint8, device="cuda")
+    wsg.read_probe(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    best = 1e9
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        wsg.read_probe(buf, nbytes, sink)
+        e1.record(st)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del buf, sink
+    return nbytes / best / 1e6, best
+
+
+def time_pass_kernel(seq, xs, ys, R: int, reps: int):
+    """Average duration of the persistent pass kernel (seq.run without the argmax
+    enqueues exactly one kernel: all 257 GEMMs), with HIP events on the stream it
+    runs on."""
+    import torch
+    xr = [x[:R] for x in xs]
+    yr = [y[:R] for y in ys]
+    seq.run(xr, yr, R)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        seq.run(xr, yr, R)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, reps
 
 
 def main():
@@ -606,11 +728,15 @@ def main():
                     help="extra row counts timed over the full pass (flatness; 24 and 48 rows = 8 and 16 agents)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--persistent", action="store_true",
-                    help="run the pass as one cooperative launch instead of a graph of one launch per GEMM")
+    ap.add_argument("--launch", choices=["auto", "persistent", "graph"], default="auto",
+                    help="how a pass is launched: one cooperative launch of the pass kernel (persistent, up to "
+                         "16 rows), a replayed graph of one streaming-kernel launch per GEMM (graph), or the "
+                         "persistent launch where it serves the row count and the graph elsewhere (auto)")
+    ap.add_argument("--persistent", action="store_true", help="same as --launch persistent")
     ap.add_argument("--kernel-only", action="store_true",
-                    help="skip the graph-replayed pass: only the back-to-back streaming-kernel launches (and "
-                         "the copy calibration), for hardware-counter runs")
+                    help="skip the timed passes: only the dominant kernel's launches at --R (the pass kernel, "
+                         "or the streaming kernels with --launch graph) and the copy calibration, for "
+                         "hardware-counter runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB three times: a kernel of known "
                          "traffic for scaling the HBM byte counters of a profiler run")
@@ -631,23 +757,37 @@ def main():
                          "and rewrite profiles/traffic.json and profiles/stream_kernel_full_pass_R12.md")
     args = ap.parse_args()
 
+    if args.persistent:
+        args.launch = "persistent"
+    kind = "stream" if args.launch == "graph" else "pass"
+
     if args.summarize_profiles:
+        lf = f"--launch {args.launch}"
         cmds = {
             "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
-                     "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --sweep 12 --no-paths",
+                     f"python3 bench.py {lf} --steps 5 --warmup 1 --no-cpu-baseline --sweep 12 --no-paths",
             "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
-                     f"python3 bench.py --kernel-only --no-cpu-baseline --sweep 12 "
+                     f"python3 bench.py {lf} --kernel-only --no-cpu-baseline --sweep 12 "
                      f"--copy-calibration {args.copy_calibration}",
             "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
-                     f"python3 bench.py --kernel-only --no-cpu-baseline --sweep 12 "
+                     f"python3 bench.py {lf} --kernel-only --no-cpu-baseline --sweep 12 "
                      f"--copy-calibration {args.copy_calibration}",
         }
-        rec = summarize_profiles(*args.summarize_profiles, args.copy_calibration or 1024, args.R, cmds)
+        rec = summarize_profiles(kind, *args.summarize_profiles, args.copy_calibration or 1024, args.R, cmds)
         text = rec.pop("summary_text")
-        with open(os.path.join(ROOT, "profiles", "stream_kernel_full_pass_R12.md"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", KERNELS[kind][2]), "w") as f:
             f.write(text)
-        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-            json.dump(rec, f, indent=1)
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            with open(path) as f:
+                allrec = json.load(f)
+            if "kernel_source_sha256" in allrec:           # a record of the older single-kernel form
+                allrec = {}
+        except (OSError, ValueError):
+            allrec = {}
+        allrec[kind] = rec
+        with open(path, "w") as f:
+            json.dump(allrec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
         return
@@ -686,13 +826,19 @@ def main():
         print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
         return
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
-    if args.persistent and max(sweep) > 16:
-        # the persistent pass kernel serves up to 16 rows (one row tile)
-        sweep = [r for r in sweep if r <= 16]
+    P_MAX = 16                                   # rows the persistent pass kernel serves (one row tile)
+    if args.launch == "persistent" and max(sweep) > P_MAX:
+        sweep = [r for r in sweep if r <= P_MAX]
         log(f"[pass] persistent launch: row counts {sweep}")
+
+    def mode_of(R):
+        return "persistent" if args.launch != "graph" and R <= P_MAX else "graph"
+
     R_max = max(sweep)
     mats, gemms, packed, xs, ys, idx = build_pass(R_max, args.seed)
-    seq = wsg.Seq(gemms, persistent=args.persistent)
+    seqs = {"graph": wsg.Seq(gemms)}
+    if any(mode_of(R) == "persistent" for R in sweep) or args.R <= P_MAX:
+        seqs["persistent"] = wsg.Seq(gemms, persistent=True)
     pass_bytes = W.pass_bytes()
     if args.copy_calibration > 0:
         nb = args.copy_calibration << 20
@@ -704,31 +850,53 @@ def main():
         log(f"[calib] copied {nb} bytes three times")
         del src, dst
 
+    head_mode = mode_of(args.R)
     if args.kernel_only:
-        kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=1)
+        if head_mode == "persistent":
+            kern_ms, launches = time_pass_kernel(seqs["persistent"], xs, ys, args.R, reps=2)
+            per_launch = pass_bytes
+        else:
+            kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=1)
+            per_launch = pass_bytes / len(gemms)
         log(f"[kernel] {launches} launches, {kern_ms * 1e3:.2f} us average")
-        print(json.dumps({"kernel_only": True, "R": args.R, "avg_launch_us": round(kern_ms * 1e3, 3),
-                          "bytes_per_launch": round(pass_bytes / len(gemms))}), flush=True)
+        print(json.dumps({"kernel_only": True, "R": args.R, "launch": head_mode,
+                          "avg_launch_us": round(kern_ms * 1e3, 3), "bytes_per_launch": round(per_launch)}),
+              flush=True)
         return
-    results = {}
+    results, modes = {}, {}
     for R in sweep:
-        ms, wall = time_pass(seq, xs, ys, idx, R, args.steps if R == args.R else max(5, args.steps // 2),
+        modes[R] = mode_of(R)
+        ms, wall = time_pass(seqs[modes[R]], xs, ys, idx, R, args.steps if R == args.R else max(5, args.steps // 2),
                              args.warmup)
         results[R] = ms
-        log(f"[pass] R={R:3d}: {ms:.4f} ms/pass, {pass_bytes / ms / 1e6:.1f} GB/s "
+        log(f"[pass] R={R:3d} ({modes[R]}): {ms:.4f} ms/pass, {pass_bytes / ms / 1e6:.1f} GB/s "
             f"({pass_bytes / ms / 1e6 / RF.HBM_PEAK_GBS * 100:.1f}% of 8 TB/s), "
             f"{R * 1000 / ms:.0f} rows*tok/s")
     ms = results[args.R]
     gbs = pass_bytes / ms / 1e6
+    # both launch modes at the headline row count
+    by_mode = {head_mode: round(ms, 5)}
+    for other in ("graph", "persistent"):
+        if other != head_mode and other in seqs:
+            o_ms, _ = time_pass(seqs[other], xs, ys, idx, args.R, max(5, args.steps // 2), args.warmup)
+            by_mode[other] = round(o_ms, 5)
+            log(f"[pass] R={args.R} ({other}): {o_ms:.4f} ms/pass")
 
-    kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=3)
-    bytes_per_launch = pass_bytes / len(gemms)
+    if head_mode == "persistent":
+        kern_ms, launches = time_pass_kernel(seqs["persistent"], xs, ys, args.R, reps=10)
+        bytes_per_launch = pass_bytes
+        kname = "pass_kernel<8, false> (one cooperative launch per pass: all 257 GEMMs)"
+    else:
+        kern_ms, launches = time_dominant_kernel(gemms, xs, ys, args.R, reps=3)
+        bytes_per_launch = pass_bytes / len(gemms)
+        info = gemms[0].query(args.R)
+        kname = (f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}, {info['waves_per_workgroup']}, "
+                 f"*, 0> (both min-term variants, all 257 GEMMs)")
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
-    info = gemms[0].query(args.R)
-    kname = (f"stream_kernel<{info['row_tiles']}, {info['subtiles_per_wave']}, {info['waves_per_workgroup']}, "
-             f"false, *, 0> (both min-term variants, all 257 GEMMs)")
     log(f"[kernel] {kname}: {kern_ms * 1e3:.2f} us average over {launches} launches, "
         f"{bytes_per_launch / 1e6:.2f} MB/launch, {achieved:.1f} GB/s")
+    ceiling, ceiling_ms = read_ceiling()
+    log(f"[ceiling] plain read kernel: {ceiling:.1f} GB/s ({ceiling / RF.HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
 
     paths = None if args.no_paths else time_paths(gemms, xs, ys, [r for r in (1, 2, 3, 4) if r <= R_max])
     for R, rec in (paths or {}).items():
@@ -758,7 +926,10 @@ def main():
                         "mlp 2x25600 / 25600) + lm-head 5120->151936, Q4_K-style 4.5 bit, "
                         "257 GEMMs + row argmax",
             "R": args.R,
-            "pass_launch": "persistent" if args.persistent else "graph",
+            "pass_launch": head_mode,
+            "pass_launch_by_R": {str(k): v for k, v in modes.items()},
+            "ms_per_pass_by_launch": by_mode,
+            "dependency_model": "each GEMM starts after the previous one has finished everywhere",
             "step_epilogue": "head row argmax (chunked) + greedy check of 2 drafts per agent",
             "packed_bytes": pass_bytes,
             "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),
@@ -768,8 +939,8 @@ def main():
             "pct_hbm_peak_by_R": {str(k): round(pass_bytes / v / 1e6 / RF.HBM_PEAK_GBS * 100, 2)
                                   for k, v in results.items()},
             "rows_tok_per_s_by_R": {str(k): round(k * 1000 / v, 1) for k, v in results.items()},
-            "row_tiled_gemms_by_R": {str(k): sum(1 for g in gemms if g.query(k)["path"] == wsg.PATH_TILED)
-                                     for k in results},
+            "row_tiled_gemms_by_R": {str(k): (sum(1 for g in gemms if g.query(k)["path"] == wsg.PATH_TILED)
+                                              if modes[k] == "graph" else 0) for k in results},
             "flatness_t12_over_t1": round(results[12] / results[1], 4) if 1 in results and 12 in results else None,
             "kernel_paths_ms_per_pass_by_R": paths,
         },
@@ -780,14 +951,19 @@ def main():
             "peak": RF.HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / RF.HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.R),
+            "traffic": measured_traffic(kind if head_mode == "persistent" else "stream", args.R),
             "avg_launch_us": round(kern_ms * 1e3, 3),
             "bytes_per_launch": round(bytes_per_launch),
+            "practical_peak": round(ceiling, 1),
+            "practical_peak_kernel": "read_probe_kernel: 4 GiB, one 512-thread workgroup per CU, 16-byte "
+                                     "nontemporal loads, best of 5",
+            "frac_of_practical_peak": round(achieved / ceiling, 4),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    seq.close()
+    for sq in seqs.values():
+        sq.close()
     for g in gemms:
         g.close()
 

@@ -341,6 +341,17 @@ int qgemm_decode_attention(const void *q_bf16, const void *k_cache, const void *
                            int head_dim, int cap, int max_len, float *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* Measurement aid (an interface of this library, not a step the pages
+ * describe): read `bytes` of device memory at `buf` once, as fast as the device
+ * allows, so that a caller can time the practical HBM read ceiling next to the
+ * weight pass.  One workgroup per compute unit, 16-byte nontemporal loads,
+ * four in flight per thread.  buf: device, 16-byte aligned; bytes: a multiple
+ * of 16, below 2^40.  sink: 16 KiB of device memory the kernel may write
+ * (contents unspecified).  One kernel on `stream`.
+ * Errors: QGEMM_EINVAL (NULL pointer, bytes not a multiple of 16 or too
+ * large), QGEMM_EALIGN, QGEMM_EHIP. */
+int qgemm_read_probe(const void *buf, uint64_t bytes, void *sink, void *stream);
+
 /* Static text for a status code. */
 const char *qgemm_status_string(int status);
 

@@ -17,7 +17,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# QG_ORACLE_LIB names a prebuilt copy to load instead (the sanitizer test's instrumented build)
+LIB_PATH = os.environ.get("QG_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 ORACLE_EARG, ORACLE_EINEXACT = -1, -2
 

@@ -13,7 +13,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# QG_SYNTH_LIB names a prebuilt copy to load instead (the sanitizer test's instrumented build)
+LIB_PATH = os.environ.get("QG_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
 SB_BYTES = 144
 SB_WEIGHTS = 256
 

@@ -13,6 +13,8 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 
 
 def build(force: bool = False) -> str:
+    if os.environ.get("QG_EMU_LIB"):                    # a prebuilt (instrumented) copy: load it as is
+        return os.environ["QG_EMU_LIB"]
     src = os.path.join(HERE, "qgemm_emu.cpp")
     deps = [src] + [os.path.join(HERE, "..", "..", "weight_streaming_gemm_amd", "csrc", f)
                     for f in ("layout.h", "operand.h", "stream_sched.h", "prefill_plan.h", "pass_sched.h")]

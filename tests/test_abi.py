@@ -71,6 +71,12 @@ def test_host_validation_codes():
     assert L.qgemm_run_static(vp(4096), 16, 256, vp(4096), vp(4100), 1, None) == Q.QGEMM_EALIGN
     assert L.qgemm_run_static(vp(4096), 16, 256, None, None, 0, None) == Q.QGEMM_OK      # R = 0: no-op
     assert Q.STATIC_SCRATCH_BYTES == 16 << 20
+    # the read probe checks its arguments before any HIP call
+    assert L.qgemm_read_probe(None, 4096, vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_read_probe(vp(4096), 4100, vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_read_probe(vp(4096), 1 << 40, vp(4096), None) == Q.QGEMM_EINVAL
+    assert L.qgemm_read_probe(vp(4104), 4096, vp(4096), None) == Q.QGEMM_EALIGN
+    assert L.qgemm_read_probe(vp(4096), 4096, None, None) == Q.QGEMM_EINVAL
     assert L.qgemm_run_prefill(None, vp(4096), vp(4096), 100, None, 0, None) == Q.QGEMM_EINVAL
     assert L.qgemm_prefill_workspace_size(None, 100, ctypes.byref(sz0 := ctypes.c_size_t())) == Q.QGEMM_EINVAL
     assert L.qgemm_dequantize(None, vp(4096), None) == Q.QGEMM_EINVAL

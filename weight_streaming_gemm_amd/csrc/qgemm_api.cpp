@@ -282,6 +282,16 @@ int static_device(const StaticDevice** out) {
 
 extern "C" {
 
+int qgemm_read_probe(const void* buf, uint64_t bytes, void* sink, void* stream) {
+  if (!buf || !sink || bytes % 16 != 0 || bytes >= (1ull << 40)) return QGEMM_EINVAL;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 16 != 0) return QGEMM_EALIGN;
+  int cus = 0;
+  if (const int rc = device_cus(&cus)) return rc;
+  if (bytes == 0) return QGEMM_OK;
+  return launch_read_probe(buf, bytes, sink, cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? QGEMM_OK
+                                                                                                       : QGEMM_EHIP;
+}
+
 const char* qgemm_status_string(int status) {
   switch (status) {
     case QGEMM_OK: return "ok";

@@ -67,6 +67,7 @@ inline size_t partial_slot_bytes(int RT, int NT, int nwn) { return (size_t)nwn *
 
 hipError_t launch_pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_stream(const StreamArgs& a, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, void* sink, int cus, hipStream_t st);
 bool stream_variant_exists(int RT, int NT, int NW);
 int stream_occupancy(int RT, int NT, int NW);   // resident workgroups per CU (0 if no such variant)
 // rows tiled as well as outputs (prefill.hip; plan and image layout in prefill_plan.h):

@@ -791,6 +791,36 @@ dequant_kernel(const uint8_t* __restrict__ packed, float* __restrict__ w, int64_
 }
 
 // ---------------------------------------------------------------------------
+// A plain read of n16 16-byte words: thread t of the grid reads words t,
+// t + stride, ..., four loads in flight (nontemporal hint), and folds them into
+// a value that is stored only if it equals a constant no real buffer is likely
+// to give (the loads must not be dropped).
+__global__ void __launch_bounds__(512) read_probe_kernel(const u32x4* __restrict__ p, uint64_t n16,
+                                                         u32x4* __restrict__ sink) {
+  constexpr int U = 4;
+  const uint64_t tid = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (uint64_t i = tid; i < n16; i += stride * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t k = i + (uint64_t)u * stride;
+      v[u] = k < n16 ? __builtin_nontemporal_load(p + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[tid & 1023] = acc;
+}
+
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, void* sink, int cus, hipStream_t st) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)cus), dim3(512), 0, st, reinterpret_cast<const u32x4*>(buf),
+                     bytes / 16, reinterpret_cast<u32x4*>(sink));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // per-row argmax, lowest index among equal maxima; NaN never wins.  One
 // workgroup per row; the row is read as 16-byte vectors (after a scalar head up
 // to 16-byte alignment), four independent loads in flight per thread, so one

@@ -32,6 +32,7 @@ EXPORTS = (
     "qgemm_verify_greedy", "qgemm_attention_workspace_size", "qgemm_decode_attention", "qgemm_query",
     "qgemm_destroy",
     "qgemm_seq_create", "qgemm_seq_run", "qgemm_seq_run_verify", "qgemm_seq_errors", "qgemm_seq_destroy",
+    "qgemm_read_probe",
     "qgemm_status_string",
 )
 
@@ -86,6 +87,7 @@ def lib():
             "qgemm_seq_run_verify": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, vp, i32, vp, vp, vp],
             "qgemm_seq_errors": [vp, ctypes.POINTER(ctypes.c_uint32)],
             "qgemm_seq_destroy": [vp],
+            "qgemm_read_probe": [vp, ctypes.c_uint64, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -133,6 +135,12 @@ def run_static(packed_dev, N: int, K: int, x, y, R: int | None = None, stream=No
     R = x.shape[0] if R is None else R
     _check(lib().qgemm_run_static(_ptr(packed_dev), N, K, _ptr(x), _ptr(y), R, _stream(stream)),
            "qgemm_run_static")
+
+
+def read_probe(buf, nbytes: int, sink, stream=None):
+    """Read nbytes of device memory at buf once at full speed (a measurement aid:
+    the practical HBM read ceiling); sink is 16 KiB of device scratch."""
+    _check(lib().qgemm_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "qgemm_read_probe")
 
 
 def argmax_rows(y, idx, R: int | None = None, stream=None):
