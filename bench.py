@@ -881,6 +881,16 @@ def main():
             o_ms, _ = time_pass(seqs[other], xs, ys, idx, args.R, max(5, args.steps // 2), args.warmup)
             by_mode[other] = round(o_ms, 5)
             log(f"[pass] R={args.R} ({other}): {o_ms:.4f} ms/pass")
+    # both dependency models of the persistent launch: every GEMM after the whole
+    # previous one (the headline), and down projections waiting only for the
+    # gate|up outputs they read
+    by_dep = None
+    if "persistent" in seqs and args.R <= P_MAX:
+        gated = wsg.Seq(gemms, persistent=True, gated_inputs=True)
+        g_ms, _ = time_pass(gated, xs, ys, idx, args.R, max(5, args.steps // 2), args.warmup)
+        gated.close()
+        by_dep = {"after_whole_previous_gemm": by_mode["persistent"], "gated_mlp_inputs": round(g_ms, 5)}
+        log(f"[pass] R={args.R} (persistent, gated inputs of the down projections): {g_ms:.4f} ms/pass")
 
     if head_mode == "persistent":
         kern_ms, launches = time_pass_kernel(seqs["persistent"], xs, ys, args.R, reps=10)
@@ -930,6 +940,7 @@ def main():
             "pass_launch_by_R": {str(k): v for k, v in modes.items()},
             "ms_per_pass_by_launch": by_mode,
             "dependency_model": "each GEMM starts after the previous one has finished everywhere",
+            "persistent_ms_per_pass_by_dependency_model": by_dep,
             "step_epilogue": "head row argmax (chunked) + greedy check of 2 drafts per agent",
             "packed_bytes": pass_bytes,
             "pct_hbm_peak": round(gbs / RF.HBM_PEAK_GBS * 100, 2),

@@ -268,10 +268,24 @@ int qgemm_destroy(qgemm_t h);
  *                              the activations are staged, times the mins in
  *                              two fp32 products per block.
  * (Both give results within the stated tolerance; they round differently.)
+ * and, with QGEMM_SEQ_PERSISTENT, the dependency between GEMMs:
+ *   0                          GEMM i + 1 starts after GEMM i has finished on
+ *                              every workgroup (its input depends on all of
+ *                              the previous output, as through a norm);
+ *   QGEMM_SEQ_GATED_INPUTS     where GEMM i has 2 K outputs and GEMM i + 1 has
+ *                              K inputs (K a multiple of 16; a fused gate|up
+ *                              feeding a down projection through an element-wise
+ *                              gate), input column j of GEMM i + 1 depends only
+ *                              on outputs j and K + j of GEMM i: each K chunk of
+ *                              GEMM i + 1 starts once the workgroups holding
+ *                              those outputs have finished GEMM i (not for two
+ *                              such GEMMs in a row; on up to 256 compute units).
+ *                              Results are the same as without the flag.
  * Errors: QGEMM_EINVAL (also for unknown flags), QGEMM_ENOMEM, QGEMM_ESHAPE,
  * QGEMM_EHIP. */
 #define QGEMM_SEQ_PERSISTENT 1u
 #define QGEMM_SEQ_SUB_BLOCK_SUMS 2u
+#define QGEMM_SEQ_GATED_INPUTS 4u
 int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32_t flags);
 
 /* Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]

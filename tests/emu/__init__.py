@@ -57,6 +57,10 @@ def lib():
                                ctypes.c_int]
         L.emu_pass_block_bytes.restype = ctypes.c_int
         L.emu_pass_block_bytes.argtypes = [ctypes.c_int]
+        L.emu_pass_units.restype = None
+        L.emu_pass_units.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p]
+        L.emu_pass_gated_mask.restype = None
+        L.emu_pass_gated_mask.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p]
         L.emu_prefill.restype = ctypes.c_int
         L.emu_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_void_p]
@@ -144,6 +148,20 @@ def pass_coverage(shapes, R, P=256, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUN
         out.append(counts[o:o + n])
         o += n
     return out, chunks
+
+
+def pass_units(p, S, P, NS, rot):
+    """(chunk, ns0, ns1) of workgroup p in the pass kernel's deal."""
+    out = np.zeros(3, np.int32)
+    lib().emu_pass_units(p, S, P, NS, rot, out.ctypes.data)
+    return tuple(int(v) for v in out)
+
+
+def pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p):
+    """The set of workgroups chunk c of a gated GEMM waits for."""
+    w = np.zeros(4, np.uint64)
+    lib().emu_pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p, w.ctypes.data)
+    return {q for q in range(256) if (int(w[q // 64]) >> (q % 64)) & 1}
 
 
 def pass_block_bytes(R):

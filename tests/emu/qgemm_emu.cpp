@@ -586,6 +586,14 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
 // Every compute wave's cursor over its share, as the kernel walks it: count
 // steps from packed step step0 at chunk block jj0, +1 per step and KB - kbc more
 // at a chunk's end.  counts[g][ns * KB + j] += 1 for every step taken.
+// the pass kernel's deal: workgroup p's chunk and units [ns0, ns1) (out[0..2])
+void emu_pass_units(int p, int S, int P, int NS, int rot, int* out) { pass_units(p, S, P, NS, rot, out, out + 1, out + 2); }
+
+// the workgroups a gated chunk waits for (pass_sched.h), 4 words
+void emu_pass_gated_mask(int c, int kbc, int half, int P, int NSp, int Sp, int rot_p, uint64_t* w) {
+  pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p, w);
+}
+
 // LDS bytes of one block's activations in the pass kernel
 int emu_pass_block_bytes(int R) { return pass_x_block_bytes(R); }
 

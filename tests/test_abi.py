@@ -123,6 +123,7 @@ def test_host_validation_codes():
     s = vp()
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 0) == Q.QGEMM_EINVAL
     assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 4) == Q.QGEMM_EINVAL
+    assert L.qgemm_seq_create(ctypes.byref(s), None, 1, 8) == Q.QGEMM_EINVAL
     assert L.qgemm_seq_run(None, None, None, 1, None, None) == Q.QGEMM_EINVAL
     assert L.qgemm_destroy(None) == Q.QGEMM_OK
     assert L.qgemm_seq_destroy(None) == Q.QGEMM_OK

@@ -273,6 +273,21 @@ def test_full_pass_run_verify(orc, persistent):
     assert np.array_equal(tokens.cpu().numpy(), tok_ref) and np.array_equal(n_new.cpu().numpy(), n_ref)
     assert sorted(n_ref.tolist()) == [1, 1, 2, 3]
     seq.close()
+    if persistent:
+        # with gated inputs (each down projection waits only for the gate|up
+        # outputs it reads) every output is bitwise the same
+        print("persistent pass with gated inputs", flush=True)
+        ys2 = [torch.empty_like(y) for y in ys]
+        idx2, tokens2, n_new2 = torch.empty_like(idx), torch.empty_like(tokens), torch.empty_like(n_new)
+        seq2 = wsg.Seq(gs, persistent=True, gated_inputs=True)
+        seq2.run_verify([xd[m.K] for m in mats], ys2, R, idx2, G.to_dev(drafts), D, tokens2, n_new2)
+        torch.cuda.synchronize()
+        assert seq2.errors() == 0
+        for i in range(len(mats)):
+            assert torch.equal(ys2[i].view(torch.int32), ys[i].view(torch.int32)), f"GEMM {i}"
+        assert torch.equal(idx2, idx) and torch.equal(tokens2, tokens) and torch.equal(n_new2, n_new)
+        seq2.close()
+        del ys2
     for g in gs:
         g.close()
     del packs, ys

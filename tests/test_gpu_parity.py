@@ -536,6 +536,37 @@ def test_seq_matches_oracle_and_repeats_bitwise(orc, mode):
         g.close()
 
 
+@pytest.mark.parametrize("R", [12, 16, 5])
+def test_seq_gated_inputs_match_oracle_and_ungated_bitwise(orc, R):
+    """Persistent sequences with gated inputs: GEMMs 2 (8192 inputs, two K chunks
+    at 12 or 16 rows) and 5 follow a GEMM of twice their input width, so each of
+    their chunks waits only for the workgroups holding the outputs it reads.
+    Results match the oracle and, bit for bit, the same sequence without the
+    flag; no wait gives up."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    shapes = [(300, 1024), (16384, 256), (80, 8192), (4100, 512), (512, 2048), (40, 256)]
+    mats = [G.make(11, i, N, K, max_R=16) for i, (N, K) in enumerate(shapes)]
+    xs_np = [synth.x_bf16(11, 200 + i, R, K) for i, (N, K) in enumerate(shapes)]
+    xs = [G.to_dev(x) for x in xs_np]
+    out = {}
+    for gated in (False, True):
+        _flush(f"seq gated={gated} R={R}")
+        ys = [torch.full((R, N), -7.0, dtype=torch.float32, device="cuda") for N, K in shapes]
+        seq = wsg.Seq([g for _, g in mats], persistent=True, gated_inputs=gated)
+        for _ in range(3):
+            seq.run(xs, ys, R)
+        torch.cuda.synchronize()
+        assert seq.errors() == 0
+        out[gated] = [y.cpu().numpy() for y in ys]
+        seq.close()
+    for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+        assert np.array_equal(out[True][i].view(np.uint32), out[False][i].view(np.uint32)), i
+        assert_parity(out[True][i], orc.gemm(canon, N, K, xs_np[i]), f"gated seq gemm {i}")
+    for _, g in mats:
+        g.close()
+
+
 def test_seq_with_row_tiled_gemms_matches_oracle(orc):
     """A graph-replayed sequence at 64 rows, where every GEMM takes the row-tiled
     kernel (activation image, product, K-chunk sums), and at 24 rows on the

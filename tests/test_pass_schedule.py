@@ -111,3 +111,29 @@ def test_in_place_conversion_reads_every_raw_row_before_overwriting_it(R):
                 hit = set(owner[lo:hi].tolist()) & unread
                 assert not hit, f"R={R} pair {q}: write [{lo}, {hi}) over unread raw rows {hit}"
     assert not unread
+
+
+@pytest.mark.parametrize("R,P", [(12, 256), (16, 256), (1, 256), (12, 100), (16, 37)])
+def test_gated_wait_sets_hold_exactly_the_producers(R, P):
+    """With gated inputs, K chunk c of down (25600 inputs) waits for the
+    workgroups holding gate|up outputs [256 kbc c, 256 kbc (c + 1)) and the same
+    + 25600: derived here from the deal of every workgroup's units, each chunk's
+    wait set must be exactly those holders."""
+    from synth import workloads as W
+    gu, dn = W.layer_mats(0)[2], W.layer_mats(0)[3]
+    x_area = emu.PASS_X_AREA
+    _, chunks = emu.pass_coverage([(gu.N, gu.K), (dn.N, dn.K)], R, P=P, x_area=x_area)
+    Sp, Sc = int(chunks[0]), int(chunks[1])
+    NSp, kbc, half = gu.N // 16, dn.K // 256 // Sc, dn.K // 16
+    rot_p = (2 * 37) % P                         # the gate|up GEMM's rotation at index 2 of a layer
+    holders = {}                                 # output sub-tile -> workgroups holding a unit of it
+    for q in range(P):
+        _, ns0, ns1 = emu.pass_units(q, Sp, P, NSp, rot_p)
+        for ns in range(ns0, ns1):
+            holders.setdefault(ns, set()).add(q)
+    assert sorted(holders) == list(range(NSp))
+    for c in range(Sc):
+        need = set()
+        for ns in list(range(16 * kbc * c, 16 * kbc * (c + 1))) + list(range(half + 16 * kbc * c, half + 16 * kbc * (c + 1))):
+            need |= holders[ns]
+        assert emu.pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p) == need, (R, P, c)

@@ -119,7 +119,7 @@ __device__ __forceinline__ PassGemm get_gemm(const PassGemm* __restrict__ t, int
   d.S = uni(src->S);
   d.kbc = uni(src->kbc);
   d.rot = uni(src->rot);
-  d.pad_[0] = d.pad_[1] = 0;
+  d.masks = uniform_ptr(src->masks);
   return d;
 }
 __device__ __forceinline__ PassWave get_wave(const PassWave* __restrict__ t, int idx) {
@@ -450,16 +450,51 @@ pass_kernel(PassArgs a) {
     }
   };
 
+  // ---- GEMM g with gated input, chunk c: wait only for the workgroups that hold
+  // the previous GEMM's outputs the chunk reads.  Each of them, once through the
+  // previous GEMM, adds one to the counter of every chunk of GEMM g that reads
+  // its outputs; the chunk's counter reaching the target in the table means all
+  // have (targets add up over the launch's gated GEMMs)
+  auto gated_wait = [&](const PassGemm& d, int c) __attribute__((always_inline)) {
+    if (lane != 0 || dead) return;
+    const uint32_t target = (uint32_t)d.masks[PASS_MASK_WORDS * c + 4];
+    uint32_t n = 0;
+    while (__hip_atomic_load(bar + PASS_DEP_WORD + PASS_DEP_STRIDE * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           target) {
+      if (++n > SPIN_LIMIT) {
+        __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dead = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  // ... and the producer's side, after its stores of the previous GEMM are
+  // complete: lane c' for chunk c' of the next GEMM dn
+  auto gated_signal = [&](const PassGemm& dn) __attribute__((always_inline)) {
+    if (lane < dn.S) {
+      const uint64_t w = dn.masks[PASS_MASK_WORDS * lane + (p >> 6)];
+      if ((w >> (p & 63)) & 1u)
+        __hip_atomic_fetch_add(bar + PASS_DEP_WORD + PASS_DEP_STRIDE * lane, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
   // ---- the units of GEMM g, helper h taking units h, h + PASS_NH, ... in order:
   // add each unit's pieces in wave order, then y (one chunk) or the chunk's
   // partial tile; after its last unit the chunk sums of those of its sub-tiles
   // whose last chunk this workgroup was.
-  auto finish = [&](const PassGemm& d, int c, int ns0, int ns1) __attribute__((always_inline)) {
+  auto finish = [&](const PassGemm& d, int g, int c, int ns0, int ns1) __attribute__((always_inline)) {
     const int units = ns1 - ns0, n = units * d.kbc;
     // y goes out device-coherent: the next GEMM may run on any die
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
     const uint32_t part_tile = (uint32_t)d.NS * 1024u;                 // bytes of one chunk's partials
-    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+    // GEMMs of even and odd index use separate halves of the partials and their
+    // counters: with gated inputs a workgroup may start GEMM g + 1 while others
+    // still finish GEMM g
+    const uint32_t half = (uint32_t)(g & 1);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part + half * (a.part_bytes / 8), a.part_bytes / 2);
+    uint32_t* const cnt = a.cnt + half * a.cnt_half;
     for (int u = h; u < units; u += PASS_NH) {
       const int w_lo = pass_step_owner(u * d.kbc, PASS_NC, n);
       const int w_hi = pass_step_owner((u + 1) * d.kbc - 1, PASS_NC, n);
@@ -501,7 +536,7 @@ pass_kernel(PassArgs a) {
       bool last = false;
       if (u0 + lane < mine) {
         const int ns = ns0 + h + PASS_NH * (u0 + lane);
-        const uint32_t old = __hip_atomic_fetch_add(a.cnt + ns, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(cnt + ns, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = old == (uint32_t)(d.S - 1);
       }
       uint64_t mask = __builtin_amdgcn_ballot_w64(last);
@@ -524,7 +559,7 @@ pass_kernel(PassArgs a) {
             const int r = 4 * g4 + i;
             if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
           }
-        if (lane == 0) __hip_atomic_store(a.cnt + ns, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(cnt + ns, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };
@@ -536,7 +571,10 @@ pass_kernel(PassArgs a) {
     c = uni(c); ns0 = uni(ns0); ns1 = uni(ns1);
     if (g > 0) {
       if (h == 0) {
-        grid_wait(g - 1);
+        if (d.masks)
+          gated_wait(d, c);
+        else
+          grid_wait(g - 1);
         if (lane < PASS_NC * PASS_PIECES) lds_store(&s_consumed[0][0] + lane, 0u);
         if (lane < PASS_NC) lds_store(&s_written[lane], 0u);
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
@@ -554,7 +592,7 @@ pass_kernel(PassArgs a) {
     convert_share(ns1 > ns0 ? d.kbc : 0, PASS_NC + h);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_s_barrier();                // and converted
-    finish(d, c, ns0, ns1);
+    finish(d, g, c, ns0, ns1);
     __builtin_amdgcn_s_waitcnt(0);               // this helper's stores of GEMM g are complete
     asm volatile("" ::: "memory");
     if (lane == 0) __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -564,6 +602,8 @@ pass_kernel(PassArgs a) {
         if (++n > LDS_SPIN_LIMIT) break;
         __builtin_amdgcn_s_sleep(1);
       }
+      const PassGemm dn = get_gemm(gemms, g + 1);
+      if (dn.masks) gated_signal(dn);
       grid_arrive(g);
     }
   }
@@ -575,9 +615,14 @@ pass_kernel(PassArgs a) {
       s_last = prev == (uint32_t)P - 1 ? 1u : 0u;
     }
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    if (lds_load(&s_last) && lane < 10) {        // the global, exit and 8 group counters
-      const int i = lane == 0 ? 0 : (lane == 1 ? 16 : 32 + 32 * (lane - 2));
-      __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lds_load(&s_last)) {
+      if (lane < 10) {                           // the global, exit and 8 group counters
+        const int i = lane == 0 ? 0 : (lane == 1 ? 16 : 32 + 32 * (lane - 2));
+        __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane < 16)                             // the gated-input counters
+        __hip_atomic_store(bar + PASS_DEP_WORD + PASS_DEP_STRIDE * lane, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

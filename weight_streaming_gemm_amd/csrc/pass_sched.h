@@ -79,4 +79,20 @@ QG_HD void pass_wave_share(int p, int w, int NC, int P, int NS, int KB, int S, i
   *jj0 = b > a ? jj : 0;
 }
 
+// Gated input: K chunk c (kbc blocks per chunk) of a GEMM whose input column j
+// depends on outputs j and half + j of the previous GEMM (half = K / 16 input
+// sub-tiles, i.e. the previous GEMM's sub-tiles [16 kbc c, 16 kbc (c + 1)) and
+// the same + half).  w[0..3] = bitmask of the workgroups (P <= 256) whose units
+// of the previous GEMM (NSp sub-tiles, Sp chunks, rotation rot_p) hold any of
+// them: the workgroups the chunk waits for.
+QG_HD void pass_gated_mask(int c, int kbc, int half, int P, int NSp, int Sp, int rot_p, uint64_t w[4]) {
+  const int lo = 16 * kbc * c, hi = 16 * kbc * (c + 1);
+  w[0] = w[1] = w[2] = w[3] = 0;
+  for (int q = 0; q < P && q < 256; ++q) {
+    int cq, ns0, ns1;
+    pass_units(q, Sp, P, NSp, rot_p, &cq, &ns0, &ns1);
+    if ((ns0 < hi && ns1 > lo) || (ns0 < hi + half && ns1 > lo + half)) w[q / 64] |= 1ull << (q % 64);
+  }
+}
+
 }  // namespace qg

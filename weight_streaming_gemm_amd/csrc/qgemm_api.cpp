@@ -587,6 +587,8 @@ struct qgemm_seq {
   size_t part_bytes, cnt_bytes;
   std::map<SeqKey, PassGemm*> descs;   // device descriptor tables per (R, pointer set)
   std::map<int, PassWave*> waves;      // device wave tables per R
+  std::vector<char> gated;             // GEMM g waits only for the producers of its inputs
+  std::map<int, uint64_t*> masks;      // device bitmasks of those producers per R (gated GEMMs)
   void* am_ws;       // argmax (and verification) workspace for the last GEMM's output
   int max_R;
 };
@@ -612,12 +614,58 @@ bool pass_sizes(const qgemm_seq* s, int R, size_t* part, size_t* cnt) {
       *cnt = std::max(*cnt, (size_t)h->NS * 4);
     }
   }
+  *part *= 2;        // halves for GEMMs of even and odd index
+  *cnt *= 2;
   return true;
+}
+
+// Gated inputs: GEMM g (g > 0) reads, for input column j, only the previous
+// GEMM's outputs j and K + j (a fused gate|up of 2 K outputs through an
+// element-wise gate).  Taken where the shapes say so, never for two GEMMs in a
+// row (so at most two GEMMs are in flight), and for at most PASS_MAX_GATED_P
+// workgroups.
+std::vector<char> gated_gemms(const qgemm_seq* s) {
+  std::vector<char> v(s->hs.size(), 0);
+  if (!(s->flags & QGEMM_SEQ_GATED_INPUTS) || s->cus > PASS_MAX_GATED_P) return v;
+  for (size_t g = 1; g < s->hs.size(); ++g)
+    v[g] = s->hs[g - 1]->N == 2 * s->hs[g]->K && s->hs[g]->K % TILE_N == 0 && !v[g - 1];
+  return v;
+}
+
+// per gated GEMM and chunk, PASS_MASK_WORDS words: a bitmask of the workgroups
+// whose units of the previous GEMM hold the outputs the chunk reads, then the
+// chunk counter's target; offsets[g] indexes the GEMM's first chunk (in words),
+// -1 if it waits for every workgroup
+std::vector<uint64_t> gated_masks(const qgemm_seq* s, int R, std::vector<int64_t>* offsets) {
+  std::vector<uint64_t> m;
+  offsets->assign(s->hs.size(), -1);
+  const int P = s->cus;
+  uint64_t target[16] = {};                                         // per chunk index, over the launch
+  for (size_t g = 1; g < s->hs.size(); ++g) {
+    if (!s->gated[g]) continue;
+    const qgemm_handle* prev = s->hs[g - 1];
+    const qgemm_handle* cur = s->hs[g];
+    const int Sp = pass_chunks_of(prev->KB, R, P), Sc = pass_chunks_of(cur->KB, R, P);
+    const int rot_p = (int)(((g - 1) * 37) % (size_t)P);
+    (*offsets)[g] = (int64_t)m.size();
+    for (int c = 0; c < Sc; ++c) {
+      uint64_t w[PASS_MASK_WORDS] = {};
+      pass_gated_mask(c, (int)(cur->KB / Sc), (int)(cur->K / TILE_N), P, (int)prev->NS, Sp, rot_p, w);
+      // the chunk counter's value once these workgroups are through (the counter
+      // keeps counting over the launch's gated GEMMs)
+      target[c] += (uint64_t)(__builtin_popcountll(w[0]) + __builtin_popcountll(w[1]) +
+                              __builtin_popcountll(w[2]) + __builtin_popcountll(w[3]));
+      w[4] = target[c];
+      m.insert(m.end(), w, w + PASS_MASK_WORDS);
+    }
+  }
+  return m;
 }
 
 // the descriptor table of one run (the GEMMs' weights, activations, outputs and
 // chunking at R rows); rot spreads the longer unit runs over the workgroups
-std::vector<PassGemm> pass_descs(const qgemm_seq* s, int R, const void* const* xs, float* const* ys) {
+std::vector<PassGemm> pass_descs(const qgemm_seq* s, int R, const void* const* xs, float* const* ys,
+                                  const uint64_t* masks_dev, const std::vector<int64_t>& mask_off) {
   std::vector<PassGemm> t(s->hs.size());
   for (size_t g = 0; g < s->hs.size(); ++g) {
     const qgemm_handle* h = s->hs[g];
@@ -635,7 +683,7 @@ std::vector<PassGemm> pass_descs(const qgemm_seq* s, int R, const void* const* x
     d.S = pass_chunks_of(h->KB, R, s->cus);
     d.kbc = (int32_t)(h->KB / d.S);
     d.rot = (int32_t)((g * 37) % (size_t)s->cus);
-    d.pad_[0] = d.pad_[1] = 0;
+    d.masks = mask_off[g] >= 0 ? masks_dev + mask_off[g] : nullptr;
   }
   return t;
 }
@@ -690,6 +738,7 @@ void seq_free(qgemm_seq* s) {
   if (s->cap) (void)hipStreamDestroy(s->cap);
   for (auto& kv : s->descs) (void)hipFree(kv.second);
   for (auto& kv : s->waves) (void)hipFree(kv.second);
+  for (auto& kv : s->masks) (void)hipFree(kv.second);
   if (s->part) (void)hipFree(s->part);
   if (s->cnt) (void)hipFree(s->cnt);
   if (s->bar) (void)hipFree(s->bar);
@@ -716,7 +765,8 @@ T* upload(const std::vector<T>& v) {
 extern "C" {
 
 int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32_t flags) {
-  if (!out || !handles || count < 1 || (flags & ~(uint32_t)(QGEMM_SEQ_PERSISTENT | QGEMM_SEQ_SUB_BLOCK_SUMS)))
+  if (!out || !handles || count < 1 ||
+      (flags & ~(uint32_t)(QGEMM_SEQ_PERSISTENT | QGEMM_SEQ_SUB_BLOCK_SUMS | QGEMM_SEQ_GATED_INPUTS)))
     return QGEMM_EINVAL;
   *out = nullptr;
   int max_R = QGEMM_MAX_R;
@@ -739,6 +789,7 @@ int qgemm_seq_create(qgemm_seq_t* out, const qgemm_t* handles, int count, uint32
     delete s;
     return QGEMM_EHIP;
   }
+  s->gated = gated_gemms(s);
   size_t part = 0, cnt = 0;
   if (flags & QGEMM_SEQ_PERSISTENT) {
     // one workgroup per compute unit, all resident
@@ -842,16 +893,24 @@ int seq_run_impl(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, 
   // one persistent launch over all GEMMs (pass.hip)
   size_t part, cnt;
   if (!pass_sizes(s, R, &part, &cnt) || part > s->part_bytes || cnt > s->cnt_bytes) return QGEMM_EPATH;
+  std::vector<int64_t> mask_off;
+  const std::vector<uint64_t> masks = gated_masks(s, R, &mask_off);
+  auto mt = s->masks.find(R);
+  if (mt == s->masks.end()) {
+    uint64_t* dev = upload(masks.empty() ? std::vector<uint64_t>(4, 0) : masks);
+    if (!dev) return QGEMM_ENOMEM;
+    mt = s->masks.emplace(R, dev).first;
+  }
   auto it = s->descs.find(key);
   if (it == s->descs.end()) {
     if (s->descs.size() >= SEQ_CACHE_MAX) seq_drop_descs(s);
-    PassGemm* dev = upload(pass_descs(s, R, xs, ys));
+    PassGemm* dev = upload(pass_descs(s, R, xs, ys, mt->second, mask_off));
     if (!dev) return QGEMM_ENOMEM;
     it = s->descs.emplace(key, dev).first;
   }
   auto wt = s->waves.find(R);
   if (wt == s->waves.end()) {
-    PassWave* dev = upload(pass_waves(pass_descs(s, R, xs, ys), s->cus));
+    PassWave* dev = upload(pass_waves(pass_descs(s, R, xs, ys, mt->second, mask_off), s->cus));
     if (!dev) return QGEMM_ENOMEM;
     wt = s->waves.emplace(R, dev).first;
   }
@@ -866,6 +925,7 @@ int seq_run_impl(qgemm_seq_t s, const void* const* xs, float* const* ys, int R, 
   a.cnt = s->cnt;
   a.bar = s->bar;
   a.err = s->err;
+  a.cnt_half = (uint32_t)(s->cnt_bytes / 8);
   if (launch_pass(a, (s->flags & QGEMM_SEQ_SUB_BLOCK_SUMS) != 0, st) != hipSuccess) return QGEMM_EHIP;
   if (argmax_idx) {
     const qgemm_handle* last = s->hs.back();

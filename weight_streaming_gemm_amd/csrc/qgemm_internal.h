@@ -102,7 +102,13 @@ struct PassGemm {
   int32_t N, NS, KB;       // outputs, 16-output sub-tiles, 256-weight blocks
   int32_t S, kbc;          // K in S chunks of kbc blocks
   int32_t rot;             // rotation of the deal of units to workgroups
-  int32_t pad_[2];
+  // gated input (the previous GEMM is a fused gate|up of 2 K outputs feeding this
+  // one through an element-wise gate): per chunk c, PASS_MASK_WORDS words: a
+  // 256-bit mask of the workgroups whose units of the previous GEMM hold the
+  // outputs the chunk reads, then the value the chunk's counter reaches once they
+  // have all finished (counts add up over the launch's gated GEMMs); a workgroup
+  // of chunk c waits only for that.  NULL: wait for every workgroup.
+  const uint64_t* masks;
 };
 // A compute wave's share of one GEMM (pass_sched.h), precomputed on the host:
 // `count` steps starting at packed step `step0` (sub-tile * KB + block), at
@@ -116,11 +122,14 @@ struct PassArgs {
   const PassGemm* gemms;   // device table of G GEMMs
   const PassWave* waves;   // device table [G][P][PASS_NC]
   int32_t G, R, P;         // GEMMs, rows (1..PASS_MAX_R), workgroups (all resident)
-  uint32_t part_bytes;     // bytes of `part`
-  float* part;             // chunk partial tiles: chunk c, sub-tile ns at (c NS + ns) KiB
-  uint32_t* cnt;           // per-sub-tile chunk arrival counters, zero between GEMMs
+  uint32_t part_bytes;     // bytes of `part` (two halves: GEMMs of even and odd index)
+  float* part;             // chunk partial tiles: chunk c, sub-tile ns at (c NS + ns) KiB of a half
+  uint32_t* cnt;           // per-sub-tile chunk arrival counters (two halves, as `part`), zero
+                           // between uses
   uint32_t* bar;           // PASS_BAR_WORDS barrier counters, zero between launches
   uint32_t* err;           // set to 1 when a device-wide wait gave up
+  uint32_t cnt_half;       // words of one half of `cnt`
+  uint32_t pad_;
 };
 constexpr int PASS_MAX_R = 16;                   // one 16-row tile
 constexpr int PASS_NC = 8;                       // compute waves per workgroup
@@ -129,7 +138,11 @@ constexpr int PASS_THREADS = (PASS_NC + PASS_NH) * 64;
 constexpr int PASS_PIECES = 2;                   // LDS partial tiles per compute wave
 constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave
 constexpr int PASS_MAX_CHUNKS = 16;
-constexpr int PASS_BAR_WORDS = 512;
+constexpr int PASS_DEP_WORD = 1024;              // bar[1024 + 256 c]: gated-input counter of chunk c
+constexpr int PASS_DEP_STRIDE = 256;             // (one KiB apart)
+constexpr int PASS_BAR_WORDS = PASS_DEP_WORD + 16 * PASS_DEP_STRIDE;
+constexpr int PASS_MAX_GATED_P = 256;            // workgroups a gated wait's bitmask covers
+constexpr int PASS_MASK_WORDS = 8;               // per gated chunk: 4 words of bitmask, the counter's target
 constexpr int PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256;
 hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st);
 int pass_occupancy();                            // resident workgroups per CU (0: none)

@@ -20,6 +20,7 @@ PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_TILED = 0, 1, 2, 3
 TILED_MIN_R = 24
 SEQ_PERSISTENT = 1
 SEQ_SUB_BLOCK_SUMS = 2
+SEQ_GATED_INPUTS = 4
 MAX_R = 64
 MAX_PREFILL_R = 8192
 
@@ -249,13 +250,16 @@ class QGemm:
 class Seq:
     """A full weight pass: the GEMMs run in order, as a replayed graph of one launch
     per GEMM, or (persistent=True) as one cooperative launch, whose min term comes
-    from products with the mins or (sub_block_sums=True) from staged sub-block sums."""
+    from products with the mins or (sub_block_sums=True) from staged sub-block sums,
+    and where (gated_inputs=True) a down projection after a fused gate|up waits only
+    for the outputs it reads."""
 
-    def __init__(self, gemms, persistent: bool = False, sub_block_sums: bool = False):
+    def __init__(self, gemms, persistent: bool = False, sub_block_sums: bool = False, gated_inputs: bool = False):
         self.gemms = list(gemms)
         arr = (ctypes.c_void_p * len(self.gemms))(*[g.h.value for g in self.gemms])
         s = ctypes.c_void_p()
-        flags = (SEQ_PERSISTENT if persistent else 0) | (SEQ_SUB_BLOCK_SUMS if sub_block_sums else 0)
+        flags = ((SEQ_PERSISTENT if persistent else 0) | (SEQ_SUB_BLOCK_SUMS if sub_block_sums else 0) |
+                 (SEQ_GATED_INPUTS if gated_inputs else 0))
         _check(lib().qgemm_seq_create(ctypes.byref(s), arr, len(self.gemms), flags), "qgemm_seq_create")
         self.s = s
 
