@@ -21,6 +21,10 @@
  *   [16,144) quants: byte i = q_{2i} | q_{2i+1} << 4.
  * Block (n, j) covers w[n, 256j .. 256j+255] at byte 144 * (n * K/256 + j).
  *
+ * The pages describe the method, not an interface: every call below is this
+ * library's own.  Each call's comment opens with the passage of the method it
+ * serves in brackets, or says that it is an interface of this library.
+ *
  * Conventions for every call:
  *   - Device pointers are hipMalloc'd (or torch) memory of the current device;
  *     the library never frees memory it did not allocate.
@@ -112,19 +116,22 @@ typedef struct {
                                per block); 0: from the activations at every step */
 } qgemm_info;
 
-/* Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights
+/* [Interface of this library: the pages fix no weight layout.]
+ * Bytes of the packed (GPU) layout of an N x K matrix: 144 B per 256 weights
  * of N rounded up to a multiple of 16 (the canonical size plus N-tail padding).
  * Errors: QGEMM_EINVAL (bytes NULL), QGEMM_ESHAPE. */
 int qgemm_packed_size(int64_t N, int64_t K, size_t *bytes);
 
-/* Rearrange canonical blocks (device, N*K/256*144 bytes, 16-byte aligned) into
+/* [Interface of this library: the pages fix no weight layout.]
+ * Rearrange canonical blocks (device, N*K/256*144 bytes, 16-byte aligned) into
  * the packed layout (device, qgemm_packed_size bytes, 16-byte aligned).  Both
  * buffers belong to the caller; canon may be freed once the stream has run the
  * work.  The packed bytes are a pure re-arrangement: no value is changed.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE, QGEMM_EALIGN, QGEMM_EHIP. */
 int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, void *stream);
 
-/* Create a handle over packed weights.  The handle BORROWS packed_dev (it must
+/* [Serves the multiply of the formula above (page: moving the weights only once).]
+ * Create a handle over packed weights.  The handle BORROWS packed_dev (it must
  * stay valid and unchanged until qgemm_destroy) and OWNS a device workspace
  * sized for up to max_R rows (partial output tiles and per-tile arrival
  * counters; with max_R >= QGEMM_TILED_MIN_R also the row-tiled path's
@@ -135,7 +142,9 @@ int qgemm_pack(const void *canon_dev, void *packed_dev, int64_t N, int64_t K, vo
 int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int max_R,
                  uint32_t flags);
 
-/* y = x . W^T for R rows on `stream`, with the R-dependent kernel choice.
+/* [The multiply of the formula above: every packed weight read once and applied
+ * to all R rows (page: moving the weights only once).]
+ * y = x . W^T for R rows on `stream`, with the R-dependent kernel choice.
  * x: device bf16 [R x K], y: device fp32 [R x N], both 16-byte aligned.
  * On the streaming paths enqueues exactly one kernel, which reads every packed
  * weight byte once, converts x itself and writes y; on the row-tiled path
@@ -145,7 +154,9 @@ int qgemm_create(qgemm_t *out, const void *packed_dev, int64_t N, int64_t K, int
  * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_ERANGE_R, QGEMM_EHIP. */
 int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
 
-/* For callers that cannot allocate device memory (code under HIP graph
+/* [For callers that cannot allocate: an interface of this library around the
+ * same multiply.]
+ * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): qgemm_run
  * without a handle, allocating nothing.  packed_dev holds the packed layout of
  * an N x K matrix (qgemm_pack; borrowed for the call), x_bf16 [R x K] and y
@@ -167,7 +178,8 @@ int qgemm_run(qgemm_t h, const void *x_bf16, float *y, int R, void *stream);
 int qgemm_run_static(const void *packed_dev, int64_t N, int64_t K, const void *x_bf16, float *y,
                      int R, void *stream);
 
-/* As qgemm_run with an explicit path (QGEMM_PATH_AUTO = qgemm_run).
+/* [The same multiply; the path choice is an interface of this library.]
+ * As qgemm_run with an explicit path (QGEMM_PATH_AUTO = qgemm_run).
  * Extra error: QGEMM_EPATH when the VALU path is asked for an R it does not
  * serve (R > 4), or the row-tiled path of a handle created with
  * max_R < QGEMM_TILED_MIN_R. */
@@ -199,25 +211,31 @@ int qgemm_prefill_workspace_size(qgemm_t h, int R, size_t *bytes);
 int qgemm_run_prefill(qgemm_t h, const void *x_bf16, float *y, int R, void *workspace,
                       size_t workspace_bytes, void *stream);
 
-/* The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
+/* [Interface of this library: the block formula above, as a check of the packed
+ * weights.]
+ * The dequantised weights, fp32 [N x K] row-major (device, caller-owned,
  * 16-byte aligned): w_out[n, k] is the binary32 value nearest to
  * d*sc_s*q_k - dmin*m_s (one rounding; bit-exact), decoded from the packed
  * layout by the same unpacking the GEMM kernels use.
  * Errors: QGEMM_EINVAL, QGEMM_EALIGN, QGEMM_EHIP. */
 int qgemm_dequantize(qgemm_t h, float *w_out, void *stream);
 
-/* idx[r] = the smallest n with y[r, n] = max over n of y[r, n], for r < R
+/* [The output head's next-token choice that the drafts are checked against
+ * (page: from one session to four agents).]
+ * idx[r] = the smallest n with y[r, n] = max over n of y[r, n], for r < R
  * (y: device fp32 [R x N]; idx: device int32 [R]).  NaN entries never win;
  * a row of NaNs gives 0.  The greedy pick over the output-head logits.
  * Errors: QGEMM_EINVAL, QGEMM_ESHAPE (N < 1), QGEMM_ERANGE_R (R < 0), QGEMM_EHIP. */
 int qgemm_argmax_rows(const float *y, int R, int64_t N, int32_t *idx, void *stream);
 
-/* Bytes of the workspace qgemm_argmax_rows_ws needs for R rows of N columns.
+/* [Interface of this library.]
+ * Bytes of the workspace qgemm_argmax_rows_ws needs for R rows of N columns.
  * Errors: QGEMM_EINVAL (bytes NULL), QGEMM_ERANGE_R, QGEMM_ESHAPE (N < 1 or
  * N > 2^31 - 1). */
 int qgemm_argmax_workspace_size(int R, int64_t N, size_t *bytes);
 
-/* As qgemm_argmax_rows (the same result), spread over many workgroups: each
+/* [As qgemm_argmax_rows (page: from one session to four agents).]
+ * As qgemm_argmax_rows (the same result), spread over many workgroups: each
  * takes a chunk of up to 8192 columns of one row; the last chunk of a row to
  * finish combines the chunks' maxima in chunk order.  workspace: device,
  * caller-owned, at least qgemm_argmax_workspace_size bytes, 16-byte aligned,
@@ -244,15 +262,20 @@ int qgemm_argmax_rows_ws(const float *y, int R, int64_t N, int32_t *idx, void *w
 int qgemm_verify_greedy(const int32_t *argmax_idx, int R, const int32_t *drafts, int drafts_per_agent,
                         int32_t *tokens, int32_t *n_new, void *stream);
 
-/* Describe the launch plan for (R, path) without running it.
+/* [Interface of this library.]
+ * Describe the launch plan for (R, path) without running it.
  * Errors: QGEMM_EINVAL, QGEMM_ERANGE_R, QGEMM_EPATH. */
 int qgemm_query(qgemm_t h, int R, int path, qgemm_info *info);
 
-/* Free the handle and its workspace (not the packed weights).  Waits for the
+/* [Interface of this library.]
+ * Free the handle and its workspace (not the packed weights).  Waits for the
  * device to finish work that may use the workspace.  NULL is a no-op. */
 int qgemm_destroy(qgemm_t h);
 
 /* ---- full weight pass -------------------------------------------------------
+ * [One decode step's weight pass (page: moving the weights only once); the
+ * persistent launch is the page's megakernel (section: from one session to four
+ * agents).]
  * A sequence of handles run back to back in the given (dependency) order, as
  * one decode step's weight pass: layer after layer of projections and then the
  * output head, each weight byte read once.  The sequence BORROWS the handles.
@@ -288,7 +311,10 @@ int qgemm_destroy(qgemm_t h);
 #define QGEMM_SEQ_GATED_INPUTS 4u
 int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32_t flags);
 
-/* Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]
+/* [One decode step's weight pass, weights read once (page: moving the weights
+ * only once); the one-launch form is the page's persistent megakernel (section:
+ * from one session to four agents).]
+ * Run the whole sequence for R rows: GEMM i reads xs[i] and writes ys[i]
  * (arrays of `count` device pointers, shapes as for qgemm_run); GEMM i + 1
  * starts after GEMM i has finished, as when each projection's input depends on
  * the previous output.  If argmax_idx is not NULL, the row argmax of the LAST
@@ -308,7 +334,9 @@ int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32
 int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
                   int32_t *argmax_idx, void *stream);
 
-/* As qgemm_seq_run with argmax_idx, and the greedy verification of
+/* [The step's pass with the draft check in the same round (page: from one
+ * session to four agents).]
+ * As qgemm_seq_run with argmax_idx, and the greedy verification of
  * qgemm_verify_greedy on that argmax in the same epilogue kernel (the last row
  * to finish its argmax runs it): the whole decode step's weight pass, head argmax
  * and draft check in one call.
@@ -317,14 +345,16 @@ int qgemm_seq_run_verify(qgemm_seq_t s, const void *const *xs, float *const *ys,
                          int32_t *argmax_idx, const int32_t *drafts, int drafts_per_agent,
                          int32_t *tokens, int32_t *n_new, void *stream);
 
-/* Waits for the device, then stores in *timeouts how many barrier waits of the
+/* [Interface of this library.]
+ * Waits for the device, then stores in *timeouts how many barrier waits of the
  * sequence's launches since the previous call gave up (a bounded wait: a
  * workgroup that waits about a second for the others proceeds and flags it;
  * results of such a launch are not reliable).  Resets the count.
  * Errors: QGEMM_EINVAL, QGEMM_EHIP. */
 int qgemm_seq_errors(qgemm_seq_t s, uint32_t *timeouts);
 
-/* Free the sequence and its workspace (not the handles).  NULL is a no-op. */
+/* [Interface of this library.]  Free the sequence and its workspace (not the
+ * handles).  NULL is a no-op. */
 int qgemm_seq_destroy(qgemm_seq_t s);
 
 /* Decode attention of the agents' step rows over their own KV caches
@@ -366,7 +396,7 @@ int qgemm_decode_attention(const void *q_bf16, const void *k_cache, const void *
  * large), QGEMM_EALIGN, QGEMM_EHIP. */
 int qgemm_read_probe(const void *buf, uint64_t bytes, void *sink, void *stream);
 
-/* Static text for a status code. */
+/* [Interface of this library.]  Static text for a status code. */
 const char *qgemm_status_string(int status);
 
 #ifdef __cplusplus
