@@ -39,10 +39,30 @@ QG_HD void pass_units(int p, int S, int P, int NS, int rot, int* c, int* ns0, in
   *ns1 = a + base + (q < extra ? 1 : 0);
 }
 
+// Share weights of the compute waves: waves w and w + NC/2 run on one SIMD,
+// where the older wave (lower index) is issued first and, with equal shares,
+// ends 1-5 us before the younger one; the first half of the waves takes
+// PASS_W_OLD parts of a workgroup's steps to PASS_W_YOUNG for the second half
+// (9 : 7 measured best of 1 : 1, 8 : 7, 11 : 9, 9 : 7, 7 : 5, 10 : 7, 5 : 3).
+#ifndef PASS_W_OLD
+#define PASS_W_OLD 9
+#define PASS_W_YOUNG 7
+#endif
 // first step of wave w's sub-range when n steps are split over NC waves
-QG_HD int pass_wave_first(int w, int NC, int n) { return (int)((int64_t)n * w / NC); }
-// the wave whose sub-range holds step i (0 <= i < n)
-QG_HD int pass_step_owner(int i, int NC, int n) { return (int)((((int64_t)i + 1) * NC + n - 1) / n) - 1; }
+QG_HD int pass_wave_first(int w, int NC, int n) {
+  const int h = NC / 2;
+  const int64_t cum = w <= h ? (int64_t)PASS_W_OLD * w : (int64_t)PASS_W_OLD * h + (int64_t)PASS_W_YOUNG * (w - h);
+  const int64_t total = (int64_t)PASS_W_OLD * h + (int64_t)PASS_W_YOUNG * (NC - h);
+  return (int)((int64_t)n * cum / total);
+}
+// the wave whose sub-range holds step i (0 <= i < n): the last wave whose
+// sub-range starts at or before i (waves with empty sub-ranges start where the
+// next one does)
+QG_HD int pass_step_owner(int i, int NC, int n) {
+  int w = NC - 1;
+  while (w > 0 && pass_wave_first(w, NC, n) > i) --w;
+  return w;
+}
 
 // LDS layout of one block's activations for R rows (a slot): rows are taken
 // in pairs (R2 = R rounded up to even; a missing last row is converted like the
