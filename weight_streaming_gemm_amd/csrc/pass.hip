@@ -480,12 +480,16 @@ pass_kernel(PassArgs a) {
     }
   };
 
-  // ---- the units of GEMM g, helper h taking units h, h + PASS_NH, ... in order:
-  // add each unit's pieces in wave order, then y (one chunk) or the chunk's
-  // partial tile; after its last unit the chunk sums of those of its sub-tiles
-  // whose last chunk this workgroup was.
+  // ---- the units of GEMM g.  A unit inside one compute wave's sub-range has
+  // one piece; helper h takes those of waves h and h + PASS_NH as they are
+  // written, and the units those two waves begin and later waves finish, adding
+  // their pieces in wave order.  The last wave's piece of such a unit is its
+  // first, written early: it is taken (and its slot handed back) as soon as it
+  // is written, so that no wave waits long for a free piece slot.  Then y (one
+  // chunk) or the chunk's partial tile; after its last unit the chunk sums of
+  // those of its sub-tiles whose last chunk this workgroup was.
   auto finish = [&](const PassGemm& d, int g, int c, int ns0, int ns1) __attribute__((always_inline)) {
-    const int units = ns1 - ns0, n = units * d.kbc;
+    const int units = ns1 - ns0, n = units * d.kbc, kbc = d.kbc;
     // y goes out device-coherent: the next GEMM may run on any die
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
     const uint32_t part_tile = (uint32_t)d.NS * 1024u;                 // bytes of one chunk's partials
@@ -495,25 +499,21 @@ pass_kernel(PassArgs a) {
     const uint32_t half = (uint32_t)(g & 1);
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part + half * (a.part_bytes / 8), a.part_bytes / 2);
     uint32_t* const cnt = a.cnt + half * a.cnt_half;
-    for (int u = h; u < units; u += PASS_NH) {
-      const int w_lo = pass_step_owner(u * d.kbc, PASS_NC, n);
-      const int w_hi = pass_step_owner((u + 1) * d.kbc - 1, PASS_NC, n);
-      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-      for (int w = w_lo; w <= w_hi; ++w) {
-        const int a_w = pass_wave_first(w, PASS_NC, n);
-        if (a_w == pass_wave_first(w + 1, PASS_NC, n)) continue;   // an empty share leaves no piece
-        const int k = u - a_w / d.kbc;
-        uint32_t spins = 0;
-        while (lds_load(&s_written[w]) <= (uint32_t)k) {
-          if (++spins > LDS_SPIN_LIMIT) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        asm volatile("" ::: "memory");           // the piece is read after its announcement
-        sum += pieces[(w * PASS_PIECES + k % PASS_PIECES) * 64 + lane];
-        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // and before its slot is handed back
-        asm volatile("" ::: "memory");
-        if (lane == 0) lds_store(&s_consumed[w][k % PASS_PIECES], (uint32_t)(k / PASS_PIECES) + 1u);
+    // piece j of wave w, once written; its slot is handed back
+    auto take = [&](int w, int j) __attribute__((always_inline)) -> f32x4 {
+      uint32_t spins = 0;
+      while (lds_load(&s_written[w]) <= (uint32_t)j) {
+        if (++spins > LDS_SPIN_LIMIT) break;
+        __builtin_amdgcn_s_sleep(1);
       }
+      asm volatile("" ::: "memory");             // the piece is read after its announcement
+      const f32x4 v = pieces[(w * PASS_PIECES + j % PASS_PIECES) * 64 + lane];
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);    // and before its slot is handed back
+      asm volatile("" ::: "memory");
+      if (lane == 0) lds_store(&s_consumed[w][j % PASS_PIECES], (uint32_t)(j / PASS_PIECES) + 1u);
+      return v;
+    };
+    auto put = [&](int u, const f32x4& sum) __attribute__((always_inline)) {
       const int ns = ns0 + u;
       if (d.S == 1) {
         const int nn = ns * TILE_N + nl;
@@ -525,18 +525,84 @@ pass_kernel(PassArgs a) {
       } else {
         bstore_sc1(sum, pr, (uint32_t)c * part_tile + (uint32_t)ns * 1024u + lane * 16);
       }
+    };
+    // waves h and h + PASS_NH: sub-range [a, b), units [f, l] touched (piece
+    // u - f of unit u), internal units [u, e), the unit it begins that later
+    // waves finish (ul, or -1) and the last of those waves (wl)
+    int wv2[2], a2[2], f2[2], u2[2], e2[2], ul2[2], wl2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int w = h + i * PASS_NH;
+      const int aw = pass_wave_first(w, PASS_NC, n), bw = pass_wave_first(w + 1, PASS_NC, n);
+      wv2[i] = w;
+      a2[i] = aw;
+      f2[i] = aw / kbc;
+      u2[i] = (aw + kbc - 1) / kbc;
+      e2[i] = aw < bw ? bw / kbc : u2[i];
+      const int ul = (bw - 1) / kbc;
+      const bool shared = aw < bw && ul * kbc >= aw && (ul + 1) * kbc > bw;
+      ul2[i] = shared ? ul : -1;
+      wl2[i] = shared ? pass_step_owner((ul + 1) * kbc - 1, PASS_NC, n) : w;
     }
-    const int mine = units > h ? (units - h + PASS_NH - 1) / PASS_NH : 0;   // this helper's units
-    if (d.S == 1 || mine == 0) return;
-    // every partial tile of this helper is stored; arrive at each unit's sub-tile
-    // counter (one lane per unit); the last of the S chunks to arrive adds the S
+    f32x4 hv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    bool have[2] = {ul2[0] < 0, ul2[1] < 0};
+    uint32_t spins = 0;
+    for (;;) {
+      bool moved = false, pending = false;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (u2[i] < e2[i]) {
+          const int j = u2[i] - f2[i];
+          if (lds_load(&s_written[wv2[i]]) > (uint32_t)j) {
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+            sum += take(wv2[i], j);
+            put(u2[i], sum);
+            u2[i] = uni(u2[i] + 1);
+            moved = true;
+          }
+          pending = pending || u2[i] < e2[i];
+        }
+        if (!have[i]) {                          // the last wave's (first) piece of the shared unit
+          if (lds_load(&s_written[wl2[i]]) > 0u) {
+            hv[i] = take(wl2[i], 0);
+            have[i] = true;
+            moved = true;
+          } else {
+            pending = true;
+          }
+        }
+      }
+      if (!pending) break;
+      if (!moved) {
+        if (++spins > LDS_SPIN_LIMIT) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // the shared units, their pieces in wave order (the last wave's taken above)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ul = ul2[i];
+      if (ul < 0) continue;
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      sum += take(wv2[i], ul - f2[i]);
+      for (int ww = wv2[i] + 1; ww < wl2[i]; ++ww) {
+        if (pass_wave_first(ww, PASS_NC, n) == pass_wave_first(ww + 1, PASS_NC, n)) continue;   // no piece
+        sum += take(ww, 0);                      // a middle wave's only piece
+      }
+      sum += hv[i];
+      put(ul, sum);
+    }
+    if (d.S == 1 || units == 0) return;
+    // every partial tile of this helper is stored; arrive at each of its units'
+    // sub-tile counters (one lane per unit: the units whose first step lies in
+    // wave h or h + PASS_NH); the last of the S chunks to arrive adds the S
     // partial tiles in chunk order and writes y
     __builtin_amdgcn_s_waitcnt(0);
-    for (int u0 = 0; u0 < mine; u0 += 64) {
+    for (int ub = 0; ub < units; ub += 64) {
       bool last = false;
-      if (u0 + lane < mine) {
-        const int ns = ns0 + h + PASS_NH * (u0 + lane);
-        const uint32_t old = __hip_atomic_fetch_add(cnt + ns, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int u = ub + lane;
+      if (u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt + ns0 + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = old == (uint32_t)(d.S - 1);
       }
       uint64_t mask = __builtin_amdgcn_ballot_w64(last);
@@ -544,7 +610,7 @@ pass_kernel(PassArgs a) {
         // one sub-tile at a time, all its chunks' loads in flight together
         const int uu = __builtin_ctzll(mask);
         mask &= mask - 1;
-        const int ns = ns0 + h + PASS_NH * (u0 + uu);
+        const int ns = ns0 + ub + uu;
         f32x4 v[PASS_MAX_CHUNKS];
 #pragma unroll
         for (int cc = 0; cc < PASS_MAX_CHUNKS; ++cc)
