@@ -57,6 +57,10 @@ def lib():
                                ctypes.c_int]
         L.emu_pass_block_bytes.restype = ctypes.c_int
         L.emu_pass_block_bytes.argtypes = [ctypes.c_int]
+        L.emu_pass_wave_first.restype = ctypes.c_int
+        L.emu_pass_wave_first.argtypes = [ctypes.c_int] * 3
+        L.emu_pass_step_owner.restype = ctypes.c_int
+        L.emu_pass_step_owner.argtypes = [ctypes.c_int] * 3
         L.emu_pass_units.restype = None
         L.emu_pass_units.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p]
         L.emu_pass_gated_mask.restype = None
@@ -162,6 +166,16 @@ def pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p):
     w = np.zeros(4, np.uint64)
     lib().emu_pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p, w.ctypes.data)
     return {q for q in range(256) if (int(w[q // 64]) >> (q % 64)) & 1}
+
+
+def pass_wave_first(w, NC, n):
+    """First step of compute wave w's sub-range when a workgroup's n steps are split over NC waves."""
+    return lib().emu_pass_wave_first(w, NC, n)
+
+
+def pass_step_owner(i, NC, n):
+    """The compute wave whose sub-range holds step i."""
+    return lib().emu_pass_step_owner(i, NC, n)
 
 
 def pass_block_bytes(R):

@@ -597,6 +597,10 @@ void emu_pass_gated_mask(int c, int kbc, int half, int P, int NSp, int Sp, int r
 // LDS bytes of one block's activations in the pass kernel
 int emu_pass_block_bytes(int R) { return pass_x_block_bytes(R); }
 
+// the pass kernel's split of a workgroup's n steps over NC compute waves (pass_sched.h)
+int emu_pass_wave_first(int w, int NC, int n) { return pass_wave_first(w, NC, n); }
+int emu_pass_step_owner(int i, int NC, int n) { return pass_step_owner(i, NC, n); }
+
 int emu_pass_coverage(int G, const int64_t* Ns, const int64_t* Ks, int R, int P, int NC, int x_area, int max_chunks,
                       int32_t* counts, int32_t* chunks_out) {
   int64_t off = 0;

@@ -137,3 +137,121 @@ def test_gated_wait_sets_hold_exactly_the_producers(R, P):
         for ns in list(range(16 * kbc * c, 16 * kbc * (c + 1))) + list(range(half + 16 * kbc * c, half + 16 * kbc * (c + 1))):
             need |= holders[ns]
         assert emu.pass_gated_mask(c, kbc, half, P, NSp, Sp, rot_p) == need, (R, P, c)
+
+
+def _replay_piece_protocol(n, kbc, seed, NC=8, NH=4, PIECES=2):
+    """The pass kernel's piece protocol for one workgroup's n steps in units of
+    kbc steps, replayed with its waits and a random interleaving: compute wave
+    w writes one piece per unit its sub-range touches, piece j into slot
+    j mod PIECES once piece j - PIECES has been taken; helper h takes the
+    single-piece units of waves h and h + NH as they are written and the first
+    piece of the last wave of each unit those two waves begin and later waves
+    finish, then adds each such unit's pieces in wave order.  Returns per unit
+    the waves whose pieces were added, in order, and per helper its units;
+    fails on a deadlock or a piece taken out of turn."""
+    rng = np.random.default_rng(seed)
+    first = [emu.pass_wave_first(w, NC, n) for w in range(NC + 1)]
+    owner = lambda i: emu.pass_step_owner(i, NC, n)
+    written = [0] * NC
+    taken = [[0] * PIECES for _ in range(NC)]
+    sums, mine = {}, {h: [] for h in range(NH)}
+
+    def take(w, j):
+        assert written[w] > j and taken[w][j % PIECES] == j // PIECES, (w, j)
+        taken[w][j % PIECES] = j // PIECES + 1
+
+    def wave(w):
+        a, b = first[w], first[w + 1]
+        for j in range(((b - 1) // kbc + 1 - a // kbc) if a < b else 0):
+            for _ in range(int(rng.integers(0, 3))):
+                yield "busy"
+            while j >= PIECES and taken[w][j % PIECES] < j // PIECES:
+                yield "blocked"
+            written[w] = j + 1
+            yield "progress"
+
+    def helper(h):
+        ws = [h, h + NH]
+        A, B = [first[w] for w in ws], [first[w + 1] for w in ws]
+        f = [a // kbc for a in A]
+        u = [(a + kbc - 1) // kbc for a in A]
+        e = [B[i] // kbc if A[i] < B[i] else u[i] for i in range(2)]
+        ul, wl = [], []
+        for i in range(2):
+            last = (B[i] - 1) // kbc
+            shared = A[i] < B[i] and last * kbc >= A[i] and (last + 1) * kbc > B[i]
+            ul.append(last if shared else -1)
+            wl.append(owner((last + 1) * kbc - 1) if shared else ws[i])
+        have = [x < 0 for x in ul]
+        while True:
+            moved = pending = False
+            for i in range(2):
+                if u[i] < e[i]:
+                    j = u[i] - f[i]
+                    if written[ws[i]] > j:
+                        take(ws[i], j)
+                        sums[u[i]] = [ws[i]]
+                        mine[h].append(u[i])
+                        u[i] += 1
+                        moved = True
+                    pending = pending or u[i] < e[i]
+                if not have[i]:
+                    if written[wl[i]] > 0:
+                        take(wl[i], 0)
+                        have[i] = moved = True
+                    else:
+                        pending = True
+            if not pending:
+                break
+            yield "progress" if moved else "blocked"
+        for i in range(2):
+            if ul[i] < 0:
+                continue
+            order, j = [ws[i]], ul[i] - f[i]
+            while written[ws[i]] <= j:
+                yield "blocked"
+            take(ws[i], j)
+            for ww in range(ws[i] + 1, wl[i]):
+                if first[ww] == first[ww + 1]:
+                    continue
+                while written[ww] <= 0:
+                    yield "blocked"
+                take(ww, 0)
+                order.append(ww)
+            order.append(wl[i])
+            sums[ul[i]] = order
+            mine[h].append(ul[i])
+            yield "progress"
+
+    live = [wave(w) for w in range(NC)] + [helper(h) for h in range(NH)]
+    while live:
+        moved = False
+        for k in rng.permutation(len(live)):
+            if live[k] is None:
+                continue
+            try:
+                moved = next(live[k]) != "blocked" or moved
+            except StopIteration:
+                live[k] = None
+                moved = True
+        live = [g for g in live if g is not None]
+        assert moved or not live, f"deadlock at n={n} kbc={kbc}"
+    return sums, mine
+
+
+@pytest.mark.parametrize("units,kbc", [(25, 10), (13, 20), (12, 20), (3, 20), (2, 20), (3, 16), (7, 20), (38, 20),
+                                       (1, 20), (7, 1), (8, 3), (1, 1), (1, 32), (125, 4), (5, 7)])
+def test_piece_protocol_takes_every_unit_once_in_wave_order(units, kbc):
+    """Every unit's pieces are added once, in wave order, whatever the
+    interleaving; no wave waits forever for a slot; and a helper's units are
+    the ones whose first step lies in its two waves (the units whose chunk
+    partials it arrives with)."""
+    n = units * kbc
+    for seed in range(6):
+        sums, mine = _replay_piece_protocol(n, kbc, seed)
+        assert sorted(sums) == list(range(units))
+        for u, order in sums.items():
+            touching = sorted({emu.pass_step_owner(i, 8, n) for i in range(u * kbc, (u + 1) * kbc)})
+            assert order == touching, (u, order, touching)
+        for h, us in mine.items():
+            assert sorted(us) == [u for u in range(units) if emu.pass_step_owner(u * kbc, 8, n) % 4 == h]
