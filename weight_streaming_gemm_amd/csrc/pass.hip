@@ -168,6 +168,7 @@ pass_kernel(PassArgs a) {
   __shared__ uint32_t s_consumed[PASS_NC][PASS_PIECES];  // times each piece slot has been added
   __shared__ uint32_t s_done;                   // helpers through with their units (all GEMMs so far)
   __shared__ uint32_t s_last;                   // last workgroup out of the launch
+  __shared__ uint32_t s_release;                // this workgroup's arrival completed the barrier
 
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6), g4 = lane >> 4, nl = lane & 15;
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
@@ -426,20 +427,31 @@ pass_kernel(PassArgs a) {
 
   // ---- device-wide barrier after GEMM g (generation g + 1): arrive at the
   // group counter of workgroups p mod 8; the group's last arrival arrives at the
-  // global counter.  Every helper's stores of GEMM g are complete by then.
+  // global counter, and the last arrival there writes the generation to every
+  // group's release word, which the group's workgroups wait on (32 waiters per
+  // word rather than all on one).  Every helper's stores of GEMM g are complete
+  // by then.
   auto grid_arrive = [&](int g) __attribute__((always_inline)) {
+    const uint32_t gen = (uint32_t)g + 1;
     if (lane == 0) {
-      const uint32_t gen = (uint32_t)g + 1;
+      uint32_t last = 0;
       const uint32_t old = __hip_atomic_fetch_add(bar + 32 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + 1 == gen * (uint32_t)members)
-        __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == gen * (uint32_t)members) {
+        const uint32_t all = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = all + 1 == gen * (uint32_t)groups ? 1u : 0u;
+      }
+      s_release = last;
     }
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    if (lds_load(&s_release) && lane < groups)
+      __hip_atomic_store(bar + PASS_RELEASE_WORD + 32 * lane, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto grid_wait = [&](int g) __attribute__((always_inline)) {
     if (lane == 0 && !dead) {
-      const uint32_t target = ((uint32_t)g + 1) * (uint32_t)groups;
+      const uint32_t target = (uint32_t)g + 1;
       uint32_t n = 0;
-      while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      while (__hip_atomic_load(bar + PASS_RELEASE_WORD + 32 * grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             target) {
         if (++n > SPIN_LIMIT) {
           __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           dead = true;
@@ -682,8 +694,11 @@ pass_kernel(PassArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     if (lds_load(&s_last)) {
-      if (lane < 10) {                           // the global, exit and 8 group counters
-        const int i = lane == 0 ? 0 : (lane == 1 ? 16 : 32 + 32 * (lane - 2));
+      if (lane < 18) {                           // the global, exit and 8 group counters, 8 release words
+        const int i = lane == 0 ? 0
+                      : lane == 1 ? 16
+                      : lane < 10 ? 32 + 32 * (lane - 2)
+                                  : PASS_RELEASE_WORD + 32 * (lane - 10);
         __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (lane < 16)                             // the gated-input counters

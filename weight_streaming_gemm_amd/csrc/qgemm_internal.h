@@ -138,6 +138,9 @@ constexpr int PASS_THREADS = (PASS_NC + PASS_NH) * 64;
 constexpr int PASS_PIECES = 2;                   // LDS partial tiles per compute wave
 constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave
 constexpr int PASS_MAX_CHUNKS = 16;
+// barrier words: bar[0] global counter, bar[16] exit counter, bar[32 + 32 k] group k's
+// counter, bar[512 + 32 k] group k's release word (k < 8)
+constexpr int PASS_RELEASE_WORD = 512;
 constexpr int PASS_DEP_WORD = 1024;              // bar[1024 + 256 c]: gated-input counter of chunk c
 constexpr int PASS_DEP_STRIDE = 256;             // (one KiB apart)
 constexpr int PASS_BAR_WORDS = PASS_DEP_WORD + 16 * PASS_DEP_STRIDE;
