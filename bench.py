@@ -505,13 +505,17 @@ def _find_csv(d: str, suffix: str) -> str:
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
+INST_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVES")
+
+
 def summarize_profiles(kind: str, trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: int, R: int,
-                       commands: dict) -> dict:
+                       commands: dict, inst_dir: str = None) -> dict:
     """Turn one kernel-trace run and two counter runs (FETCH_SIZE, WRITE_SIZE in KiB per
     dispatch) into a record for profiles/traffic.json and a markdown summary.  The
     counters are scaled so that the plain device copy of copy_mib MiB reads and writes
     exactly that many bytes; the dominant kernel's figures are averages over its
-    dispatches."""
+    dispatches.  With inst_dir, a run of INST_COUNTERS adds the instructions issued
+    per weight step (16 outputs x 256 weights: 2304 packed bytes)."""
     prefix, _, summary = KERNELS[kind]
     stats = _read_csv(_find_csv(trace_dir, "kernel_stats.csv"))
     per = {}
@@ -591,6 +595,24 @@ def summarize_profiles(kind: str, trace_dir: str, fetch_dir: str, write_dir: str
                             f"`roofline.practical_peak`) reads {nb} B in {float(row['AverageNs']) / 1e3:.1f} us on "
                             f"average over {row['Calls']} calls ({nb / float(row['AverageNs']):.0f} GB/s; "
                             f"{nb / float(row['MinNs']):.0f} GB/s at its fastest), against 8000 GB/s on paper."]
+    if inst_dir:
+        inst = {}
+        for row in _read_csv(_find_csv(inst_dir, "counter_collection.csv")):
+            if prefix in row["Kernel_Name"] and row["Counter_Name"] in INST_COUNTERS:
+                inst.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+        steps = launch_bytes / 2304
+        per_step = {c: round(sum(v) / len(v) / steps, 2) for c, v in inst.items() if c != "SQ_WAVES"}
+        rec["instructions_per_weight_step"] = per_step
+        lines += ["Instructions issued per weight step (wave instructions of all waves, the counters summed over "
+                  "the device per dispatch and averaged over the dispatches, divided by the "
+                  f"{steps:.0f} steps of a launch; SQ_INSTS_VALU counts the matrix-core instructions too):",
+                  "", "```", commands["inst"], "```", "",
+                  "| counter | per launch | per weight step |", "|---|---|---|"]
+        for c in INST_COUNTERS:
+            if c in inst:
+                v = sum(inst[c]) / len(inst[c])
+                lines.append(f"| {c} | {v:.4g} | {'-' if c == 'SQ_WAVES' else f'{v / steps:.1f}'} |")
+        lines.append("")
     rec["summary_text"] = "\n".join(lines)
     return rec
 
@@ -751,10 +773,12 @@ def main():
                          "'attention' = decode attention of 4 agents x 3 rows over ~23K cached positions; "
                          "'prefill' = one layer at 12 decode rows + a prompt chunk of 64..2048 rows on the "
                          "row-tiled kernel")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU work: read the rocprofv3 CSVs of a kernel-trace run and of the FETCH_SIZE and "
-                         "WRITE_SIZE counter runs (each made with --copy-calibration, size given by that flag) "
-                         "and rewrite profiles/traffic.json and profiles/stream_kernel_full_pass_R12.md")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="no GPU work: TRACE_DIR FETCH_DIR WRITE_DIR [INST_DIR]: read the rocprofv3 CSVs of a "
+                         "kernel-trace run, of the FETCH_SIZE and WRITE_SIZE counter runs (each made with "
+                         "--copy-calibration, size given by that flag) and optionally of a run of the "
+                         "instruction counters, and rewrite profiles/traffic.json and the dominant kernel's "
+                         "summary under profiles/")
     args = ap.parse_args()
 
     if args.persistent:
@@ -772,8 +796,14 @@ def main():
             "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
                      f"python3 bench.py {lf} --kernel-only --no-cpu-baseline --sweep 12 "
                      f"--copy-calibration {args.copy_calibration}",
+            "inst": f"rocprofv3 --pmc {' '.join(INST_COUNTERS)} --output-format csv -d gpurun_out/prof_inst -o bench -- "
+                    f"python3 bench.py {lf} --kernel-only --no-cpu-baseline --sweep 12",
         }
-        rec = summarize_profiles(kind, *args.summarize_profiles, args.copy_calibration or 1024, args.R, cmds)
+        dirs = args.summarize_profiles
+        if len(dirs) not in (3, 4):
+            ap.error("--summarize-profiles takes TRACE_DIR FETCH_DIR WRITE_DIR [INST_DIR]")
+        rec = summarize_profiles(kind, *dirs[:3], args.copy_calibration or 1024, args.R, cmds,
+                                 inst_dir=dirs[3] if len(dirs) == 4 else None)
         text = rec.pop("summary_text")
         with open(os.path.join(ROOT, "profiles", KERNELS[kind][2]), "w") as f:
             f.write(text)
