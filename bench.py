@@ -11,7 +11,7 @@ bytes (144 B per 256 weights).  Inputs are seeded synthetic data of those
 shapes and distributions, resident in HBM before timing.
 
 A pass runs as one cooperative launch of the pass kernel where it serves the
-row count (up to 16 rows), else as a replayed graph of one streaming-kernel
+row count (up to 48 rows), else as a replayed graph of one streaming-kernel
 launch per GEMM (--launch picks one of them for every row count).
 
 Prints one JSON line (rank 0): effective weight GB/s and ms per pass, with a
@@ -355,7 +355,7 @@ def ragged_report(seed: int, steps: int):
     xs_t = [{w: torch.from_numpy(synth.x_bf16(seed, 1000 * (t + 1) + sid, R, w, outlier_p=0.01).view(np.int16))
              .to(dev) for w, sid in W.X_STREAM.items()} for t, R in enumerate(sched)]
     xbuf = {R: {w: torch.empty((R, w), dtype=torch.int16, device=dev) for w in W.X_STREAM} for R in set(sched)}
-    seq = wsg.Seq(gemms, persistent=max(sched) <= 16)   # one cooperative launch per step (rows <= 16)
+    seq = wsg.Seq(gemms, persistent=max(sched) <= 48)   # one cooperative launch per step (rows <= 48)
 
     def one_step(t, R, ev=None):
         for w in W.X_STREAM:
@@ -752,7 +752,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", choices=["auto", "persistent", "graph"], default="auto",
                     help="how a pass is launched: one cooperative launch of the pass kernel (persistent, up to "
-                         "16 rows), a replayed graph of one streaming-kernel launch per GEMM (graph), or the "
+                         "48 rows), a replayed graph of one streaming-kernel launch per GEMM (graph), or the "
                          "persistent launch where it serves the row count and the graph elsewhere (auto)")
     ap.add_argument("--persistent", action="store_true", help="same as --launch persistent")
     ap.add_argument("--kernel-only", action="store_true",
@@ -856,7 +856,7 @@ def main():
         print(json.dumps({"report": "ragged", **ragged_report(W.SEED_RAGGED, 100)}), flush=True)
         return
     sweep = sorted({int(v) for v in args.sweep.split(",") if v} | {args.R})
-    P_MAX = 16                                   # rows the persistent pass kernel serves (one row tile)
+    P_MAX = 48                                   # rows the persistent pass kernel serves (three row tiles)
     if args.launch == "persistent" and max(sweep) > P_MAX:
         sweep = [r for r in sweep if r <= P_MAX]
         log(f"[pass] persistent launch: row counts {sweep}")

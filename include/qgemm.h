@@ -320,17 +320,20 @@ int qgemm_seq_create(qgemm_seq_t *out, const qgemm_t *handles, int count, uint32
  * the previous output.  If argmax_idx is not NULL, the row argmax of the LAST
  * GEMM's output is written to it (device int32 [R]) by one more kernel (the
  * chunked argmax of qgemm_argmax_rows_ws, on the sequence's own workspace).
- * With QGEMM_SEQ_PERSISTENT, one cooperative launch runs all GEMMs: every
- * workgroup is resident, waits at a device-wide barrier between GEMMs and
- * already streams the next GEMM's weights while it waits; the first run for a
- * given (R, pointer set) uploads a descriptor table (synchronous).  Do not
+ * With QGEMM_SEQ_PERSISTENT, one cooperative launch runs all GEMMs for 1 to 48
+ * rows (one to three 16-row tiles per weight step): every workgroup is
+ * resident, waits at a device-wide barrier between GEMMs and already streams
+ * the next GEMM's weights while it waits; the first run for a given (R,
+ * pointer set) uploads a descriptor table (synchronous).  Do not
  * capture a persistent run into a graph (cooperative launch).  Runs of one
  * sequence share workspace: one stream at a time.  Without the flag, the first
  * run for a given (R, pointer set, argmax_idx) captures the launches into a
  * graph that later runs replay.  The sequence keeps at most 64 such graphs (and
  * 64 descriptor tables); a run that needs one more first waits for the device
  * and drops all of them.
- * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays, QGEMM_ENOMEM. */
+ * Errors: as qgemm_run, plus QGEMM_EINVAL for NULL arrays, QGEMM_ENOMEM, and
+ * QGEMM_EPATH for a persistent sequence at more than 48 rows (or a GEMM whose
+ * K admits no chunking that fits the kernel's LDS). */
 int qgemm_seq_run(qgemm_seq_t s, const void *const *xs, float *const *ys, int R,
                   int32_t *argmax_idx, void *stream);
 

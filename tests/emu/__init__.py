@@ -129,14 +129,30 @@ def stream_seq(mats, xs, NT=2, NW=4, Vs=None, order_seed=0, nwns=None, aligned=N
 
 
 # the persistent pass kernel's constants (qgemm_internal.h): compute waves per
-# workgroup, LDS bytes for activations, most K chunks
+# workgroup, piece slots per wave, most K chunks, most rows; LDS bytes for
+# activations at R rows (row tiles of 16)
 PASS_NC = 8
-PASS_X_AREA = 160 * 1024 - 8 * 2 * 1024 - 256
-PASS_MAX_CHUNKS = 16
+PASS_PIECES = 2
+PASS_MAX_CHUNKS = 32
+PASS_MAX_R = 48
 
 
-def pass_coverage(shapes, R, P=256, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS):
-    """(per-GEMM step hit counts [NS * KB], chunks) of the pass kernel's schedule."""
+def pass_pieces(R):
+    """Piece slots per compute wave at R rows (one from two row tiles on)."""
+    return PASS_PIECES if R <= 16 else 1
+
+
+def pass_x_area(R):
+    return 160 * 1024 - PASS_NC * pass_pieces(R) * ((R + 15) // 16) * 1024 - 256
+
+
+PASS_X_AREA = pass_x_area(16)
+
+
+def pass_coverage(shapes, R, P=256, x_area=None, max_chunks=PASS_MAX_CHUNKS):
+    """(per-GEMM step hit counts [NS * KB], chunks) of the pass kernel's schedule
+    (x_area: the kernel's LDS area at R rows unless given)."""
+    x_area = pass_x_area(R) if x_area is None else x_area
     G = len(shapes)
     Ns = np.array([N for N, _ in shapes], np.int64)
     Ks = np.array([K for _, K in shapes], np.int64)
@@ -183,7 +199,7 @@ def pass_block_bytes(R):
     return lib().emu_pass_block_bytes(R)
 
 
-def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS, msum=False):
+def pass_run(mats, xs, P, x_area=None, max_chunks=PASS_MAX_CHUNKS, msum=False):
     """The pass kernel replayed over GEMMs mats = [(canon, N, K)] with activations
     xs (bf16 bits, R x K each), the min term from sub-block sums (msum) or from
     products with the mins: the list of y."""
@@ -191,6 +207,7 @@ def pass_run(mats, xs, P, x_area=PASS_X_AREA, max_chunks=PASS_MAX_CHUNKS, msum=F
     canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
     xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
     R = xs[0].shape[0]
+    x_area = pass_x_area(R) if x_area is None else x_area
     ys = [np.full((R, N), np.nan, dtype=np.float32) for _, N, _ in mats]
     P_ = ctypes.c_void_p * G
     Ns = np.array([N for _, N, _ in mats], dtype=np.int64)

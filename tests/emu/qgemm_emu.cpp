@@ -637,7 +637,8 @@ int emu_pass_coverage(int G, const int64_t* Ns, const int64_t* Ks, int R, int P,
 // partial tiles of a sub-tile are added in chunk order.
 int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64_t* Ks, const uint16_t* const* xs,
              float* const* ys, int R, int P, int NC, int x_area, int max_chunks, int msum) {
-  typedef std::vector<f32x4> Tile;   // 64 lanes
+  typedef std::vector<f32x4> Tile;   // RT row tiles x 64 lanes
+  const int RT = (R + 15) / 16;
   for (int g = 0; g < G; ++g) {
     const int64_t N = Ns[g], K = Ks[g];
     const int KB = (int)(K / SB_W), NS = (int)(padded_n(N) / TILE_N);
@@ -647,16 +648,17 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
     std::vector<uint8_t> packed((size_t)packed_bytes(N, K));
     pack(canons[g], packed.data(), N, K);
     const int64_t hdr_off = quant_region_bytes(N, K);
-    std::vector<Tile> partial((size_t)S * NS, Tile(64, f32x4{0, 0, 0, 0}));
+    std::vector<Tile> partial((size_t)S * NS, Tile((size_t)RT * 64, f32x4{0, 0, 0, 0}));
     auto store_y = [&](int ns, const Tile& t) {
-      for (int lane = 0; lane < 64; ++lane) {
-        const int64_t n = (int64_t)ns * TILE_N + (lane & 15);
-        if (n >= N) continue;
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * (lane >> 4) + i;
-          if (r < R) ys[g][(int64_t)r * N + n] = t[lane][i];
+      for (int rt = 0; rt < RT; ++rt)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int64_t n = (int64_t)ns * TILE_N + (lane & 15);
+          if (n >= N) continue;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * (lane >> 4) + i;
+            if (r < R) ys[g][(int64_t)r * N + n] = t[(size_t)rt * 64 + lane][i];
+          }
         }
-      }
     };
     for (int p = 0; p < P; ++p) {
       int c, ns0, ns1;
@@ -669,13 +671,13 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
       for (int w = 0; w < NC; ++w) {
         int count, step, jj;
         pass_wave_share(p, w, NC, P, NS, KB, S, kbc, rot, &count, &step, &jj);
-        Tile acc(64, f32x4{0, 0, 0, 0});
+        Tile acc((size_t)RT * 64, f32x4{0, 0, 0, 0});
         for (int left = count; left > 0; --left) {
           const int ns = step / KB, j = step % KB;
-          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, 1, msum != 0, acc.data());
+          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, RT, msum != 0, acc.data());
           if (jj == kbc - 1 || left == 1) {
             pieces[w].push_back(acc);
-            acc.assign(64, f32x4{0, 0, 0, 0});
+            acc.assign((size_t)RT * 64, f32x4{0, 0, 0, 0});
           }
           if (++jj == kbc) {
             jj = 0;
@@ -688,13 +690,13 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
       const int units = ns1 - ns0, n = units * kbc;
       for (int u = 0; u < units; ++u) {
         const int w_lo = pass_step_owner(u * kbc, NC, n), w_hi = pass_step_owner((u + 1) * kbc - 1, NC, n);
-        Tile sum(64, f32x4{0, 0, 0, 0});
+        Tile sum((size_t)RT * 64, f32x4{0, 0, 0, 0});
         for (int w = w_lo; w <= w_hi; ++w) {
           const int a_w = pass_wave_first(w, NC, n);
           if (a_w == pass_wave_first(w + 1, NC, n)) continue;   // an empty share leaves no piece
           const int k = u - a_w / kbc;
           if (k < 0 || k >= (int)pieces[w].size()) return -3;
-          for (int lane = 0; lane < 64; ++lane) sum[lane] += pieces[w][k][lane];
+          for (size_t l = 0; l < sum.size(); ++l) sum[l] += pieces[w][k][l];
         }
         if (S == 1)
           store_y(ns0 + u, sum);
@@ -706,7 +708,7 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
       for (int ns = 0; ns < NS; ++ns) {
         Tile sum = partial[ns];
         for (int cc = 1; cc < S; ++cc)
-          for (int lane = 0; lane < 64; ++lane) sum[lane] += partial[(size_t)cc * NS + ns][lane];
+          for (size_t l = 0; l < sum.size(); ++l) sum[l] += partial[(size_t)cc * NS + ns][l];
         store_y(ns, sum);
       }
   }

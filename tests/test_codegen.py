@@ -91,18 +91,24 @@ def test_single_gemm_step_loop_keeps_ring_in_flight(asm, rt, nw, msum):
         assert w == (RING - 1) * LOADS_PER_STAGE, f"step waits vmcnt({w})"
 
 
-def _pass_ring() -> int:
+def _pass_ring(rt: int) -> int:
+    """Ring depth of the pass kernel at rt row tiles (qgemm_internal.h: PASS_RING up to
+    some row tiles, a shallower ring beyond, where the registers run short)."""
     text = open(os.path.join(B.CSRC, "qgemm_internal.h")).read()
-    return int(re.search(r"constexpr int PASS_RING = (\d+);", text).group(1))
+    ring = int(re.search(r"constexpr int PASS_RING = (\d+);", text).group(1))
+    upto, deep = re.search(r"pass_ring\(int RT\) \{ return RT <= (\d+) \? PASS_RING : (\d+); \}", text).groups()
+    return ring if rt <= int(upto) else int(deep)
 
 
+@pytest.mark.parametrize("rt", [1, 2, 3])
 @pytest.mark.parametrize("msum", [False, True])
-def test_pass_step_loop_keeps_ring_in_flight(pass_asm, msum):
-    """The pass kernel's step loop (one 16-row tile): RING steps per ring turn,
-    each behind a wait that leaves the other RING - 1 stages in flight."""
-    ring = _pass_ring()
-    body = _body(pass_asm, f"_ZN2qg11pass_kernelILi{ring}ELb{int(msum)}EEEvNS_8PassArgsE")
-    per_step = 8 + (2 if msum else 8)
+def test_pass_step_loop_keeps_ring_in_flight(pass_asm, msum, rt):
+    """The pass kernel's step loop at rt 16-row tiles: RING steps per ring turn,
+    each behind a wait that leaves the other RING - 1 stages in flight, and no
+    spills to scratch."""
+    ring = _pass_ring(rt)
+    body = _body(pass_asm, f"_ZN2qg11pass_kernelILi{ring}ELb{int(msum)}ELi{rt}EEEvNS_8PassArgsE")
+    per_step = rt * (8 + (2 if msum else 8))
     steps = [(w, n) for w, n in _mfma_groups(body) if n >= per_step]
     assert len(steps) == ring, steps
     for w, n in steps:

@@ -536,6 +536,42 @@ def test_seq_matches_oracle_and_repeats_bitwise(orc, mode):
         g.close()
 
 
+@pytest.mark.parametrize("msum", [False, True])
+def test_seq_persistent_row_tiles_match_oracle_and_repeat_bitwise(orc, msum):
+    """Rows beyond 16 in the pass kernel: two or three 16-row tiles per weight
+    step.  A five-GEMM sequence whose K = 25600 GEMM runs in 20 K chunks at 24 rows
+    and 25 at 48 (the chunk partials of a sub-tile added in two batches), at 48,
+    33, 24 and 17 rows: parity with the oracle and a bitwise-equal repeat."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    shapes = [(300, 1024), (64, 25600), (4100, 512), (40, 8192), (151, 5120)]
+    RM = 48
+    mats = [G.make(11, i, N, K, max_R=RM) for i, (N, K) in enumerate(shapes)]
+    xs_np = [synth.x_bf16(11, 200 + i, RM, K) for i, (N, K) in enumerate(shapes)]
+    xs = [G.to_dev(x) for x in xs_np]
+    ys = [torch.empty((RM, N), dtype=torch.float32, device="cuda") for N, K in shapes]
+    seq = wsg.Seq([g for _, g in mats], persistent=True, sub_block_sums=msum)
+    for r in (48, 33, 24, 17):
+        first = None
+        for rep in range(2):
+            _flush(f"seq row tiles msum={msum} R={r} rep {rep}")
+            for y in ys:
+                y.fill_(-7.0)
+            seq.run([x[:r] for x in xs], [y[:r] for y in ys], r)
+            torch.cuda.synchronize()
+            got = [y[:r].cpu().numpy() for y in ys]
+            if first is None:
+                first = got
+                for i, ((canon, _), (N, K)) in enumerate(zip(mats, shapes)):
+                    assert_parity(got[i], orc.gemm(canon, N, K, xs_np[i][:r]), f"seq R={r} gemm {i}")
+            for i in range(len(shapes)):
+                assert np.array_equal(got[i].view(np.uint32), first[i].view(np.uint32)), (r, rep, i)
+    assert seq.errors() == 0
+    seq.close()
+    for _, g in mats:
+        g.close()
+
+
 @pytest.mark.parametrize("R", [12, 16, 5])
 def test_seq_gated_inputs_match_oracle_and_ungated_bitwise(orc, R):
     """Persistent sequences with gated inputs: GEMMs 2 (8192 inputs, two K chunks

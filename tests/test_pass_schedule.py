@@ -24,15 +24,21 @@ def test_replay_constants_match_the_kernel():
     nc = int(re.search(r"constexpr int PASS_NC = (\d+);", text).group(1))
     pieces = int(re.search(r"constexpr int PASS_PIECES = (\d+);", text).group(1))
     chunks = int(re.search(r"constexpr int PASS_MAX_CHUNKS = (\d+);", text).group(1))
-    assert "PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256" in text
-    assert nc == emu.PASS_NC and chunks == emu.PASS_MAX_CHUNKS
-    assert emu.PASS_X_AREA == 160 * 1024 - nc * pieces * 1024 - 256
+    rts = int(re.search(r"constexpr int PASS_MAX_RT = (\d+);", text).group(1))
+    assert "return 160 * 1024 - PASS_NC * pass_pieces(RT) * RT * 1024 - 256;" in text
+    assert "pass_pieces(int RT) { return RT == 1 ? PASS_PIECES : 1; }" in text
+    assert "PASS_MAX_R = 16 * PASS_MAX_RT;" in text
+    assert nc == emu.PASS_NC and pieces == emu.PASS_PIECES and chunks == emu.PASS_MAX_CHUNKS
+    assert emu.PASS_MAX_R == 16 * rts
+    for R in (1, 16, 17, 32, 33, 48):
+        rt = (R + 15) // 16
+        assert emu.pass_x_area(R) == 160 * 1024 - nc * (pieces if rt == 1 else 1) * rt * 1024 - 256
 
 
 PASS_SHAPES = [(m.N, m.K) for m in W.layer_mats(0)] + [(W.lm_head().N, W.lm_head().K)]
 
 
-@pytest.mark.parametrize("R", [1, 3, 12, 16])
+@pytest.mark.parametrize("R", [1, 3, 12, 16, 24, 33, 48])
 def test_pass_shapes_take_every_step_once(R):
     counts, chunks = emu.pass_coverage(PASS_SHAPES, R, P=256)
     for (N, K), c in zip(PASS_SHAPES, counts):
@@ -43,6 +49,11 @@ def test_pass_shapes_take_every_step_once(R):
         assert chunks.tolist() == [1, 2, 1, 5, 1]
     if R == 16:
         assert chunks.tolist() == [2, 2, 2, 10, 2]
+    if R == 24:
+        # two row tiles (one piece slot each): 10 blocks per chunk fit, down (100 blocks) goes in 10
+        assert chunks.tolist() == [2, 4, 2, 10, 2]
+    if R == 48:
+        assert chunks.tolist() == [4, 8, 4, 20, 4]
 
 
 @pytest.mark.parametrize("P", [1, 3, 7, 64, 250])
@@ -54,11 +65,11 @@ def test_odd_shapes_take_every_step_once(P):
     for (N, K), c, S in zip(shapes, counts, chunks):
         if S == 0:                     # no chunking fits (the library refuses such a sequence)
             KB = K // 256
-            assert not any(KB % S2 == 0 and KB // S2 <= 4 for S2 in range(1, min(P, 16, KB) + 1))
+            assert not any(KB % S2 == 0 and KB // S2 <= 4 for S2 in range(1, min(P, emu.PASS_MAX_CHUNKS, KB) + 1))
             assert (c == 0).all()
             continue
         planned += 1
-        assert (K // 256) % S == 0 and K // 256 // S <= 4 and S <= min(P, 16)
+        assert (K // 256) % S == 0 and K // 256 // S <= 4 and S <= min(P, emu.PASS_MAX_CHUNKS)
         assert (c == 1).all(), f"P={P} N={N} K={K} S={S}"
     assert planned >= 2
 
@@ -82,7 +93,22 @@ def test_pass_replay_matches_oracle(orc, P, x_blocks, msum):
         assert m["rel_l2"] < 2e-6
 
 
-@pytest.mark.parametrize("R", range(1, 17))
+@pytest.mark.parametrize("R,P,x_blocks", [(24, 7, 3), (33, 16, 2), (48, 5, 4), (17, 3, 6)])
+def test_pass_replay_with_row_tiles_matches_oracle(orc, R, P, x_blocks):
+    """Rows beyond 16 in two or three row tiles (each step feeds every tile, the
+    pieces and partial tiles carry all of them), some GEMMs in K chunks."""
+    shapes = [(300, 1024), (64, 2048), (40, 512)]
+    mats, xs = [], []
+    for i, (N, K) in enumerate(shapes):
+        mats.append((synth.matrix_rows(7, 60 + i, N, K), N, K))
+        xs.append(synth.x_bf16(7, 70 + i, R, K, outlier_p=0.01))
+    ys = emu.pass_run(mats, xs, P, x_area=x_blocks * emu.pass_block_bytes(R))
+    for (canon, N, K), x, y in zip(mats, xs, ys):
+        m = assert_parity(y, orc.gemm(canon, N, K, x), f"pass replay R={R} P={P} N={N} K={K}")
+        assert m["rel_l2"] < 2e-6
+
+
+@pytest.mark.parametrize("R", range(1, 49))
 def test_in_place_conversion_reads_every_raw_row_before_overwriting_it(R):
     """The pass kernel converts a slot in place: the raw bf16 rows (512 bytes
     each, in pairs) become 528-byte operand rows (a missing odd row included)
@@ -113,7 +139,7 @@ def test_in_place_conversion_reads_every_raw_row_before_overwriting_it(R):
     assert not unread
 
 
-@pytest.mark.parametrize("R,P", [(12, 256), (16, 256), (1, 256), (12, 100), (16, 37)])
+@pytest.mark.parametrize("R,P", [(12, 256), (16, 256), (1, 256), (12, 100), (16, 37), (24, 256), (48, 256), (48, 61)])
 def test_gated_wait_sets_hold_exactly_the_producers(R, P):
     """With gated inputs, K chunk c of down (25600 inputs) waits for the
     workgroups holding gate|up outputs [256 kbc c, 256 kbc (c + 1)) and the same
@@ -239,16 +265,17 @@ def _replay_piece_protocol(n, kbc, seed, NC=8, NH=4, PIECES=2):
     return sums, mine
 
 
+@pytest.mark.parametrize("pieces", [2, 1])
 @pytest.mark.parametrize("units,kbc", [(25, 10), (13, 20), (12, 20), (3, 20), (2, 20), (3, 16), (7, 20), (38, 20),
                                        (1, 20), (7, 1), (8, 3), (1, 1), (1, 32), (125, 4), (5, 7)])
-def test_piece_protocol_takes_every_unit_once_in_wave_order(units, kbc):
+def test_piece_protocol_takes_every_unit_once_in_wave_order(units, kbc, pieces):
     """Every unit's pieces are added once, in wave order, whatever the
-    interleaving; no wave waits forever for a slot; and a helper's units are
-    the ones whose first step lies in its two waves (the units whose chunk
-    partials it arrives with)."""
+    interleaving; no wave waits forever for a slot (two slots per wave at one
+    row tile, one from two on); and a helper's units are the ones whose first
+    step lies in its two waves (the units whose chunk partials it arrives with)."""
     n = units * kbc
     for seed in range(6):
-        sums, mine = _replay_piece_protocol(n, kbc, seed)
+        sums, mine = _replay_piece_protocol(n, kbc, seed, PIECES=pieces)
         assert sorted(sums) == list(range(units))
         for u, order in sums.items():
             touching = sorted({emu.pass_step_owner(i, 8, n) for i in range(u * kbc, (u + 1) * kbc)})

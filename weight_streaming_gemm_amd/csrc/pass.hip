@@ -139,6 +139,20 @@ __device__ __forceinline__ int xblk_of(const PassWave* __restrict__ t, int idx) 
   return uni(((cptr)(t + idx))->xblk);
 }
 
+// RT 16 x 16 tiles of one lane (a piece, a sum, a partial result)
+template <int RT>
+struct Tiles {
+  f32x4 v[RT];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) v[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void add(const Tiles& o) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) v[rt] += o.v[rt];
+  }
+};
+
 // f(0), f(1), ..., f(n - 1) with compile-time indices (ring slots stay in registers)
 template <class F, int... I>
 __device__ __forceinline__ void for_each_slot(F& f, std::integer_sequence<int, I...>) {
@@ -157,12 +171,16 @@ struct Span {
 
 }  // namespace
 
-template <int RING, bool MSUM>
+// RT row tiles of 16 rows (R <= 16 RT): every weight step feeds RT products
+// per activation operand; pieces and partial tiles hold RT 16 x 16 tiles
+template <int RING, bool MSUM, int RT>
 __global__ void __launch_bounds__(PASS_THREADS, 1)
 pass_kernel(PassArgs a) {
   static_assert(RING >= 2 && RING <= 12, "ring of 2 to 12 steps");
-  __shared__ __attribute__((aligned(16))) uint8_t xlds[PASS_X_AREA];
-  __shared__ f32x4 pieces[PASS_NC * PASS_PIECES * 64];
+  static_assert(RT >= 1 && RT <= PASS_MAX_RT, "one to PASS_MAX_RT row tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[pass_x_area(RT)];
+  constexpr int PC = pass_pieces(RT);           // piece slots per compute wave
+  __shared__ f32x4 pieces[PASS_NC * PC * RT * 64];
   __shared__ uint32_t s_go;                     // GEMM whose activations the helpers may stage
   __shared__ uint32_t s_written[PASS_NC];       // pieces each compute wave has written in this GEMM
   __shared__ uint32_t s_consumed[PASS_NC][PASS_PIECES];  // times each piece slot has been added
@@ -174,6 +192,7 @@ pass_kernel(PassArgs a) {
   const int p = blockIdx.x, P = a.P, R = a.R, G = a.G;
   const PassGemm* __restrict__ gemms = a.gemms;
   const int XS = PASS_X_ROW * pass_x_rows(R), SB = pass_x_block_bytes(R);
+  constexpr int GL = (16 / RT) * RT;            // partial tiles loaded together by a helper
 
   // ---- the conversion of one block's raw bf16 rows into its image, in place.
   // Rows go in pairs, 32 lanes (gg, t) per row: x[r, 64 gg + 4 t + {0..3}] and
@@ -181,7 +200,7 @@ pass_kernel(PassArgs a) {
   // from the last to the first (pair 0 twice when their number is odd), both
   // read before either is written.  Pair pp's operands go to 1056 pp and up,
   // over raw pairs pp and pp + 1 only (1056 pp + 1040 <= 1024 (pp + 2) for
-  // pp < 16), and a wave's LDS reads and writes run in program order: every raw
+  // pp < 32), and a wave's LDS reads and writes run in program order: every raw
   // row is read before anything is written over it.
   auto convert_block = [&](uint8_t* slot) __attribute__((always_inline)) {
     const int half = lane >> 5, sub = lane & 31, gg = sub >> 3, t = sub & 7;
@@ -220,10 +239,15 @@ pass_kernel(PassArgs a) {
   if (wv < PASS_NC) {
     // ======================= compute wave ======================================
     const int w = wv;
-    // this lane's A operands (step t at + 16 t) and sub-block sums inside a slot;
-    // rows >= R reuse row R - 1 (never stored)
-    const int xr = nl < R ? nl : R - 1;
-    const int xoff = xr * PASS_X_ROW + g4 * 128, soff = XS + (g4 * R + xr) * 8;
+    // this lane's A operands of row tile rt (step t at + 16 t) and sub-block sums
+    // inside a slot; rows >= R reuse row R - 1 (never stored)
+    int xoff[RT], soff[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int xr = 16 * rt + nl < R ? 16 * rt + nl : R - 1;
+      xoff[rt] = xr * PASS_X_ROW + g4 * 128;
+      soff[rt] = XS + (g4 * R + xr) * 8;
+    }
     const PassWave* __restrict__ waves = a.waves;
     // the wave's share of GEMM g, or of the first later GEMM with steps for it
     auto enter = [&](Span& s, int g) __attribute__((always_inline)) {
@@ -277,54 +301,108 @@ pass_kernel(PassArgs a) {
       st.qb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.qr, qlane + 1024, s.step * CHUNK_Q, 2));
       st.hd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.hr, hlane, s.step * CHUNK_H, 2));
     };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](const Stage& st, int slot) __attribute__((always_inline)) {
-      const WConst cst = header_consts(st.hd.x, st.hd.y, st.hd.z, st.hd.w, g4);
-      // d and -dmin as fp32 values of their own right away: folded into the final
-      // multiply-adds as binary16 operands, they would keep the header's registers
-      // alive past the slot's refill
-      float dd = cst.d, dm = cst.nmin;
-      asm volatile("" : "+v"(dd), "+v"(dm));
-      f32x4 ds = {0.f, 0.f, 0.f, 0.f}, ms = {0.f, 0.f, 0.f, 0.f};
-      const int base = slot * SB;
-      if constexpr (MSUM) {
-        for (int t = 0; t < 8; ++t) {
-          const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff + t * 16);
-          const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
-          ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
-        }
-        const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff);
-        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
-        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
+      if constexpr (RT == 1) {
+        const WConst cst = header_consts(st.hd.x, st.hd.y, st.hd.z, st.hd.w, g4);
+        // d and -dmin as fp32 values of their own right away: folded into the final
+        // multiply-adds as binary16 operands, they would keep the header's registers
+        // alive past the slot's refill
+        float dd = cst.d, dm = cst.nmin;
+        asm volatile("" : "+v"(dd), "+v"(dm));
+        f32x4 ds = {0.f, 0.f, 0.f, 0.f}, ms = {0.f, 0.f, 0.f, 0.f};
+        const int base = slot * SB;
+        if constexpr (MSUM) {
+          for (int t = 0; t < 8; ++t) {
+            const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff[0] + t * 16);
+            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+            ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+          }
+          const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[0]);
+          ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
+          ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
       } else {
-        const f16x8 bm = build_m_full(cst);
-        for (int t = 0; t < 8; ++t) {
-          const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff + t * 16);
-          const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
-          ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
-          ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bm, ms, 0, 0, 0);
+          const f16x8 bm = build_m_full(cst);
+          for (int t = 0; t < 8; ++t) {
+            const f16x8 xa = *reinterpret_cast<const f16x8*>(xlds + base + xoff[0] + t * 16);
+            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+            ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
+            ms = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bm, ms, 0, 0, 0);
+          }
         }
-      }
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = __builtin_fmaf(dd, ds[i], acc[i]);
-        acc[i] = __builtin_fmaf(dm, ms[i], acc[i]);
+        for (int i = 0; i < 4; ++i) {
+          acc[0][i] = __builtin_fmaf(dd, ds[i], acc[0][i]);
+          acc[0][i] = __builtin_fmaf(dm, ms[i], acc[0][i]);
+        }
+      } else {
+        // RT row tiles: the same B operand for every tile
+        const WConst cst = header_consts(st.hd.x, st.hd.y, st.hd.z, st.hd.w, g4);
+        // d and -dmin as fp32 values of their own right away: folded into the final
+        // multiply-adds as binary16 operands, they would keep the header's registers
+        // alive past the slot's refill
+        float dd = cst.d, dm = cst.nmin;
+        asm volatile("" : "+v"(dd), "+v"(dm));
+        f32x4 ds[RT], ms[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) ds[rt] = ms[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int base = slot * SB;
+        if constexpr (MSUM) {
+          for (int t = 0; t < 8; ++t) {
+            f16x8 xa[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const f16x8*>(xlds + base + xoff[rt] + t * 16);
+            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+            const f16x8 b = build_b(wd, cst);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[rt]);
+            ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms[rt], 0, 0, 0);
+            ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms[rt], 0, 0, 0);
+          }
+        } else {
+          const f16x8 bm = build_m_full(cst);
+          for (int t = 0; t < 8; ++t) {
+            f16x8 xa[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const f16x8*>(xlds + base + xoff[rt] + t * 16);
+            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+            const f16x8 b = build_b(wd, cst);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
+              ms[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], bm, ms[rt], 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          for (int i = 0; i < 4; ++i) {
+            acc[rt][i] = __builtin_fmaf(dd, ds[rt][i], acc[rt][i]);
+            acc[rt][i] = __builtin_fmaf(dm, ms[rt][i], acc[rt][i]);
+          }
       }
     };
     // piece k of this wave's sub-range (one per unit it touches) into slot k mod
-    // PASS_PIECES, once a helper has taken piece k - PASS_PIECES from it (the
-    // slot's k / PASS_PIECES earlier pieces added)
+    // PC, once a helper has taken piece k - PC from it (the slot's k / PC earlier
+    // pieces added)
     auto put_piece = [&](Span& s) __attribute__((always_inline)) {
       const uint32_t k = (uint32_t)s.k;
       s.k = uni(s.k + 1);
-      if (k >= PASS_PIECES) {
+      if (k >= PC) {
         uint32_t n = 0;
-        while (lds_load(&s_consumed[w][k % PASS_PIECES]) < k / PASS_PIECES) {
+        while (lds_load(&s_consumed[w][k % PC]) < k / PC) {
           if (++n > LDS_SPIN_LIMIT) break;
           __builtin_amdgcn_s_sleep(1);
         }
       }
       asm volatile("" ::: "memory");             // the slot is free before it is written
-      pieces[(w * PASS_PIECES + (int)(k % PASS_PIECES)) * 64 + lane] = acc;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pieces[((w * PC + (int)(k % PC)) * RT + rt) * 64 + lane] = acc[rt];
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);    // the piece is in LDS before it is announced
       asm volatile("" ::: "memory");
       if (lane == 0) lds_store(&s_written[w], k + 1);
@@ -361,7 +439,8 @@ pass_kernel(PassArgs a) {
       advance(L);
       if (C.g < G && (C.jj == C.kbc - 1 || C.left == 1)) {      // the step ends a unit or the share
         put_piece(C);
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       advance(C);
       while (passed <= C.g && C.g < G) {         // the next step's GEMM: stage it first
@@ -492,7 +571,7 @@ pass_kernel(PassArgs a) {
     }
   };
 
-  // ---- the units of GEMM g.  A unit inside one compute wave's sub-range has
+  // ---- the units of GEMM g at one row tile.  A unit inside one compute wave's sub-range has
   // one piece; helper h takes those of waves h and h + PASS_NH as they are
   // written, and the units those two waves begin and later waves finish, adding
   // their pieces in wave order.  The last wave's piece of such a unit is its
@@ -500,7 +579,7 @@ pass_kernel(PassArgs a) {
   // is written, so that no wave waits long for a free piece slot.  Then y (one
   // chunk) or the chunk's partial tile; after its last unit the chunk sums of
   // those of its sub-tiles whose last chunk this workgroup was.
-  auto finish = [&](const PassGemm& d, int g, int c, int ns0, int ns1) __attribute__((always_inline)) {
+  auto finish_one = [&](const PassGemm& d, int g, int c, int ns0, int ns1) __attribute__((always_inline)) {
     const int units = ns1 - ns0, n = units * d.kbc, kbc = d.kbc;
     // y goes out device-coherent: the next GEMM may run on any die
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
@@ -623,13 +702,13 @@ pass_kernel(PassArgs a) {
         const int uu = __builtin_ctzll(mask);
         mask &= mask - 1;
         const int ns = ns0 + ub + uu;
-        f32x4 v[PASS_MAX_CHUNKS];
+        f32x4 v[16];
 #pragma unroll
-        for (int cc = 0; cc < PASS_MAX_CHUNKS; ++cc)
+        for (int cc = 0; cc < 16; ++cc)
           v[cc] = bload<f32x4, SC1>(pr, cc < d.S ? (uint32_t)cc * part_tile + (uint32_t)ns * 1024u + lane * 16 : OOB);
         f32x4 sum = v[0];
 #pragma unroll
-        for (int cc = 1; cc < PASS_MAX_CHUNKS; ++cc)
+        for (int cc = 1; cc < 16; ++cc)
           if (cc < d.S) sum += v[cc];
         const int nn = ns * TILE_N + nl;
         if (nn < d.N)
@@ -638,6 +717,194 @@ pass_kernel(PassArgs a) {
             if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
           }
         if (lane == 0) __hip_atomic_store(cnt + ns, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+
+  // ---- the units of GEMM g.  A unit inside one compute wave's sub-range has
+  // one piece; helper h takes those of waves h and h + PASS_NH as they are
+  // written, and the units those two waves begin and later waves finish, adding
+  // their pieces in wave order.  The last wave's piece of such a unit is its
+  // first, written early: it is taken (and its slot handed back) as soon as it
+  // is written, so that no wave waits long for a free piece slot.  Then y (one
+  // chunk) or the chunk's partial tile; after its last unit the chunk sums of
+  // those of its sub-tiles whose last chunk this workgroup was.
+  auto finish_tiles = [&](const PassGemm& d, int g, int c, int ns0, int ns1) __attribute__((always_inline)) {
+    const int units = ns1 - ns0, n = units * d.kbc, kbc = d.kbc;
+    // y goes out device-coherent: the next GEMM may run on any die
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(d.y, (uint32_t)(R * d.N * 4));
+    // chunk c's partial result of sub-tile ns, row tile rt: at ((ns S + c) RT + rt) KiB, so that a
+    // sub-tile's S RT partial tiles lie together, in the order they are added
+    const uint32_t sub_tile = RT * 1024u;
+    // GEMMs of even and odd index use separate halves of the partials and their
+    // counters: with gated inputs a workgroup may start GEMM g + 1 while others
+    // still finish GEMM g
+    const uint32_t half = (uint32_t)(g & 1);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part + half * (a.part_bytes / 8), a.part_bytes / 2);
+    uint32_t* const cnt = a.cnt + half * a.cnt_half;
+    // piece j of wave w, once written; its slot is handed back
+    auto take = [&](int w, int j) __attribute__((always_inline)) -> Tiles<RT> {
+      uint32_t spins = 0;
+      while (lds_load(&s_written[w]) <= (uint32_t)j) {
+        if (++spins > LDS_SPIN_LIMIT) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");             // the piece is read after its announcement
+      Tiles<RT> v;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) v.v[rt] = pieces[((w * PC + j % PC) * RT + rt) * 64 + lane];
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);    // and before its slot is handed back
+      asm volatile("" ::: "memory");
+      if (lane == 0) lds_store(&s_consumed[w][j % PC], (uint32_t)(j / PC) + 1u);
+      return v;
+    };
+    // y of sub-tile ns: lane (g4, nl) holds rows 16 rt + 4 g4 + i of output 16 ns + nl
+    auto store_y = [&](int ns, const Tiles<RT>& sum) __attribute__((always_inline)) {
+      const int nn = ns * TILE_N + nl;
+      if (nn < d.N)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * g4 + i;
+            if (r < R) bstore1_sc1(sum.v[rt][i], yr, (uint32_t)((r * d.N + nn) * 4));
+          }
+    };
+    auto put = [&](int u, const Tiles<RT>& sum) __attribute__((always_inline)) {
+      const int ns = ns0 + u;
+      if (d.S == 1) {
+        store_y(ns, sum);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          bstore_sc1(sum.v[rt], pr, (uint32_t)(ns * d.S + c) * sub_tile + rt * 1024u + lane * 16);
+      }
+    };
+    // waves h and h + PASS_NH: sub-range [a, b), units [f, l] touched (piece
+    // u - f of unit u), internal units [u, e), the unit it begins that later
+    // waves finish (ul, or -1) and the last of those waves (wl)
+    int wv2[2], a2[2], f2[2], u2[2], e2[2], ul2[2], wl2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int w = h + i * PASS_NH;
+      const int aw = pass_wave_first(w, PASS_NC, n), bw = pass_wave_first(w + 1, PASS_NC, n);
+      wv2[i] = w;
+      a2[i] = aw;
+      f2[i] = aw / kbc;
+      u2[i] = (aw + kbc - 1) / kbc;
+      e2[i] = aw < bw ? bw / kbc : u2[i];
+      const int ul = (bw - 1) / kbc;
+      const bool shared = aw < bw && ul * kbc >= aw && (ul + 1) * kbc > bw;
+      ul2[i] = shared ? ul : -1;
+      wl2[i] = shared ? pass_step_owner((ul + 1) * kbc - 1, PASS_NC, n) : w;
+    }
+    Tiles<RT> hv[2];
+    hv[0].zero();
+    hv[1].zero();
+    bool have[2] = {ul2[0] < 0, ul2[1] < 0};
+    uint32_t spins = 0;
+    for (;;) {
+      bool moved = false, pending = false;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (u2[i] < e2[i]) {
+          const int j = u2[i] - f2[i];
+          if (lds_load(&s_written[wv2[i]]) > (uint32_t)j) {
+            Tiles<RT> sum;
+            sum.zero();
+            sum.add(take(wv2[i], j));
+            put(u2[i], sum);
+            u2[i] = uni(u2[i] + 1);
+            moved = true;
+          }
+          pending = pending || u2[i] < e2[i];
+        }
+        if (!have[i]) {                          // the last wave's (first) piece of the shared unit
+          if (lds_load(&s_written[wl2[i]]) > 0u) {
+            hv[i] = take(wl2[i], 0);
+            have[i] = true;
+            moved = true;
+          } else {
+            pending = true;
+          }
+        }
+      }
+      if (!pending) break;
+      if (!moved) {
+        if (++spins > LDS_SPIN_LIMIT) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // the shared units, their pieces in wave order (the last wave's taken above)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ul = ul2[i];
+      if (ul < 0) continue;
+      Tiles<RT> sum;
+      sum.zero();
+      sum.add(take(wv2[i], ul - f2[i]));
+      for (int ww = wv2[i] + 1; ww < wl2[i]; ++ww) {
+        if (pass_wave_first(ww, PASS_NC, n) == pass_wave_first(ww + 1, PASS_NC, n)) continue;   // no piece
+        sum.add(take(ww, 0));                    // a middle wave's only piece
+      }
+      sum.add(hv[i]);
+      put(ul, sum);
+    }
+    if (d.S == 1 || units == 0) return;
+    // every partial tile of this helper is stored; arrive at each of its units'
+    // sub-tile counters (one lane per unit: the units whose first step lies in
+    // wave h or h + PASS_NH); the last of the S chunks to arrive adds the S
+    // partial tiles in chunk order and writes y
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int ub = 0; ub < units; ub += 64) {
+      bool last = false;
+      const int u = ub + lane;
+      if (u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt + ns0 + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (uint32_t)(d.S - 1);
+      }
+      uint64_t mask = __builtin_amdgcn_ballot_w64(last);
+      // the sub-tiles this helper arrived last at: each one's S RT partial tiles
+      // (item k = c RT + rt) added per row tile in chunk order, GL loads in
+      // flight together: two sub-tiles per round when both fit, else rounds of
+      // GL items of one.  Addresses stay in vector registers (no scalar
+      // registers tied up across the kernel)
+      const int per = d.S * RT;
+      while (mask) {
+        const int ua = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        int ubb = -1;
+        if (2 * per <= GL && mask) {
+          ubb = __builtin_ctzll(mask);
+          mask &= mask - 1;
+        }
+        const bool two = ubb >= 0;
+        const int nsA = ns0 + ub + ua, nsB = two ? ns0 + ub + ubb : nsA;
+        Tiles<RT> sA, sB;
+        sA.zero();
+        sB.zero();
+        for (int k0 = 0; k0 < per; k0 += GL) {
+          uint32_t offA = (uint32_t)(nsA * per + k0) * 1024u + lane * 16;
+          uint32_t offB = (uint32_t)(nsB * per - per) * 1024u + lane * 16;   // item k - per of B at slot k
+          asm volatile("" : "+v"(offA), "+v"(offB));
+          f32x4 v[GL];
+#pragma unroll
+          for (int k = 0; k < GL; ++k) {
+            const bool inA = k0 + k < per, inB = two && k >= per && k < 2 * per;
+            v[k] = bload<f32x4, SC1>(pr, inA ? offA + k * 1024u : inB ? offB + k * 1024u : OOB);
+          }
+#pragma unroll
+          for (int k = 0; k < GL; ++k) {
+            const int rt = k % RT;                 // GL and per are multiples of RT
+            if (k0 + k < per) sA.v[rt] = k0 == 0 && k < RT ? v[k] : sA.v[rt] + v[k];
+            else if (two && k < 2 * per) sB.v[rt] = k < per + RT ? v[k] : sB.v[rt] + v[k];
+          }
+        }
+        store_y(nsA, sA);
+        if (two) store_y(nsB, sB);
+        if (lane == 0) {
+          __hip_atomic_store(cnt + nsA, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (two) __hip_atomic_store(cnt + nsB, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   };
@@ -670,7 +937,10 @@ pass_kernel(PassArgs a) {
     convert_share(ns1 > ns0 ? d.kbc : 0, PASS_NC + h);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_s_barrier();                // and converted
-    finish(d, g, c, ns0, ns1);
+    if constexpr (RT == 1)
+      finish_one(d, g, c, ns0, ns1);
+    else
+      finish_tiles(d, g, c, ns0, ns1);
     __builtin_amdgcn_s_waitcnt(0);               // this helper's stores of GEMM g are complete
     asm volatile("" ::: "memory");
     if (lane == 0) __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -701,27 +971,39 @@ pass_kernel(PassArgs a) {
                                   : PASS_RELEASE_WORD + 32 * (lane - 10);
         __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (lane < 16)                             // the gated-input counters
+      if (lane < PASS_MAX_CHUNKS)                // the gated-input counters
         __hip_atomic_store(bar + PASS_DEP_WORD + PASS_DEP_STRIDE * lane, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
+template <int RT>
+const void* pass_kernel_for(bool msum) {
+  constexpr int RING = pass_ring(RT);
+  return msum ? reinterpret_cast<const void*>(&pass_kernel<RING, true, RT>)
+              : reinterpret_cast<const void*>(&pass_kernel<RING, false, RT>);
+}
+
 hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st) {
+  const int RT = pass_row_tiles(a.R);
+  if (RT < 1 || RT > PASS_MAX_RT) return hipErrorInvalidValue;
   PassArgs args = a;
   void* params[] = {&args};
-  const void* k = msum ? reinterpret_cast<const void*>(&pass_kernel<PASS_RING, true>)
-                       : reinterpret_cast<const void*>(&pass_kernel<PASS_RING, false>);
+  const void* k = RT == 1 ? pass_kernel_for<1>(msum) : RT == 2 ? pass_kernel_for<2>(msum) : pass_kernel_for<3>(msum);
   return hipLaunchCooperativeKernel(k, dim3((unsigned)a.P), dim3(PASS_THREADS), params, 0, st);
 }
 
 int pass_occupancy() {
-  int b0 = 0, b1 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, pass_kernel<PASS_RING, false>, PASS_THREADS, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, pass_kernel<PASS_RING, true>, PASS_THREADS, 0) != hipSuccess)
-    return 0;
-  return b0 < b1 ? b0 : b1;
+  int lo = 1 << 30;
+  for (int RT = 1; RT <= PASS_MAX_RT; ++RT)
+    for (int m = 0; m < 2; ++m) {
+      const void* k = RT == 1 ? pass_kernel_for<1>(m) : RT == 2 ? pass_kernel_for<2>(m) : pass_kernel_for<3>(m);
+      int b = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, PASS_THREADS, 0) != hipSuccess) return 0;
+      lo = b < lo ? b : lo;
+    }
+  return lo;
 }
 
 }  // namespace qg

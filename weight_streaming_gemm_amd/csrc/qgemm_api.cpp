@@ -597,9 +597,10 @@ namespace {
 
 // K chunks of one GEMM in the persistent pass at R rows: the fewest (dividing
 // the blocks of K, at most PASS_MAX_CHUNKS and at most one per workgroup) whose
-// activations fit the kernel's LDS area; 0 when none does.
+// activations fit the kernel's LDS area at R's row tiles; 0 when none does.
 int pass_chunks_of(int64_t KB, int R, int P) {
-  return KB > INT32_MAX ? 0 : pass_chunks((int)KB, R, P, PASS_X_AREA, PASS_MAX_CHUNKS);
+  if (KB > INT32_MAX || R < 1 || R > PASS_MAX_R) return 0;
+  return pass_chunks((int)KB, R, P, pass_x_area(pass_row_tiles(R)), PASS_MAX_CHUNKS);
 }
 
 // The GEMMs' chunking and workspace needs at R rows; false if a GEMM cannot run
@@ -610,7 +611,7 @@ bool pass_sizes(const qgemm_seq* s, int R, size_t* part, size_t* cnt) {
     const int S = pass_chunks_of(h->KB, R, s->cus);
     if (S == 0) return false;
     if (S > 1) {
-      *part = std::max(*part, (size_t)S * (size_t)h->NS * 1024);
+      *part = std::max(*part, (size_t)S * (size_t)h->NS * 1024 * pass_row_tiles(R));
       *cnt = std::max(*cnt, (size_t)h->NS * 4);
     }
   }
@@ -640,7 +641,7 @@ std::vector<uint64_t> gated_masks(const qgemm_seq* s, int R, std::vector<int64_t
   std::vector<uint64_t> m;
   offsets->assign(s->hs.size(), -1);
   const int P = s->cus;
-  uint64_t target[16] = {};                                         // per chunk index, over the launch
+  uint64_t target[PASS_MAX_CHUNKS] = {};                            // per chunk index, over the launch
   for (size_t g = 1; g < s->hs.size(); ++g) {
     if (!s->gated[g]) continue;
     const qgemm_handle* prev = s->hs[g - 1];

@@ -131,22 +131,29 @@ struct PassArgs {
   uint32_t cnt_half;       // words of one half of `cnt`
   uint32_t pad_;
 };
-constexpr int PASS_MAX_R = 16;                   // one 16-row tile
+constexpr int PASS_MAX_RT = 3;                   // row tiles of 16 rows
+constexpr int PASS_MAX_R = 16 * PASS_MAX_RT;
+inline constexpr int pass_row_tiles(int R) { return (R + 15) / 16; }
 constexpr int PASS_NC = 8;                       // compute waves per workgroup
 constexpr int PASS_NH = 4;                       // helper waves per workgroup
 constexpr int PASS_THREADS = (PASS_NC + PASS_NH) * 64;
 constexpr int PASS_PIECES = 2;                   // LDS partial tiles per compute wave
-constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave
-constexpr int PASS_MAX_CHUNKS = 16;
+constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave (1-2 row tiles)
+inline constexpr int pass_ring(int RT) { return RT <= 2 ? PASS_RING : 6; }   // registers left at 3 row tiles
+constexpr int PASS_MAX_CHUNKS = 32;
 // barrier words: bar[0] global counter, bar[16] exit counter, bar[32 + 32 k] group k's
 // counter, bar[512 + 32 k] group k's release word (k < 8)
 constexpr int PASS_RELEASE_WORD = 512;
 constexpr int PASS_DEP_WORD = 1024;              // bar[1024 + 256 c]: gated-input counter of chunk c
 constexpr int PASS_DEP_STRIDE = 256;             // (one KiB apart)
-constexpr int PASS_BAR_WORDS = PASS_DEP_WORD + 16 * PASS_DEP_STRIDE;
+constexpr int PASS_BAR_WORDS = PASS_DEP_WORD + PASS_MAX_CHUNKS * PASS_DEP_STRIDE;
 constexpr int PASS_MAX_GATED_P = 256;            // workgroups a gated wait's bitmask covers
 constexpr int PASS_MASK_WORDS = 8;               // per gated chunk: 4 words of bitmask, the counter's target
-constexpr int PASS_X_AREA = 160 * 1024 - PASS_NC * PASS_PIECES * 1024 - 256;
+// piece slots per compute wave at RT row tiles (one slot from two row tiles on,
+// so that the activations keep the LDS of one row tile's two slots), and the LDS
+// bytes for activations: what the pieces (RT KiB each) and a few words leave of 160 KiB
+inline constexpr int pass_pieces(int RT) { return RT == 1 ? PASS_PIECES : 1; }
+inline constexpr int pass_x_area(int RT) { return 160 * 1024 - PASS_NC * pass_pieces(RT) * RT * 1024 - 256; }
 hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st);
 int pass_occupancy();                            // resident workgroups per CU (0: none)
 
