@@ -852,23 +852,38 @@ pass_kernel(PassArgs a) {
     if (d.S == 1 || units == 0) return;
     // every partial tile of this helper is stored; arrive at each of its units'
     // sub-tile counters (one lane per unit: the units whose first step lies in
-    // wave h or h + PASS_NH); the last of the S chunks to arrive adds the S
-    // partial tiles in chunk order and writes y
+    // wave h or h + PASS_NH).  Then the sub-tiles this workgroup adds up: of
+    // its units, those with ns mod S = c (so every sub-tile has one such
+    // workgroup, and the work is spread evenly rather than left to whichever
+    // chunk arrives last): once all S chunks have arrived, the S RT partial
+    // tiles (item k = c RT + rt) added per row tile in chunk order, GL loads in
+    // flight together, two sub-tiles per round when both fit, else rounds of
+    // GL items of one.  Addresses stay in vector registers (no scalar
+    // registers tied up across the kernel).
     __builtin_amdgcn_s_waitcnt(0);
     for (int ub = 0; ub < units; ub += 64) {
-      bool last = false;
       const int u = ub + lane;
-      if (u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h) {
-        const uint32_t old = __hip_atomic_fetch_add(cnt + ns0 + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = old == (uint32_t)(d.S - 1);
+      if (u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h)
+        __hip_atomic_fetch_add(cnt + ns0 + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int per = d.S * RT;
+    auto wait_all = [&](int ns) __attribute__((always_inline)) {
+      if (lane == 0 && !dead) {
+        uint32_t n_ = 0;
+        while (__hip_atomic_load(cnt + ns, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)d.S) {
+          if (++n_ > SPIN_LIMIT) {
+            __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dead = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
-      uint64_t mask = __builtin_amdgcn_ballot_w64(last);
-      // the sub-tiles this helper arrived last at: each one's S RT partial tiles
-      // (item k = c RT + rt) added per row tile in chunk order, GL loads in
-      // flight together: two sub-tiles per round when both fit, else rounds of
-      // GL items of one.  Addresses stay in vector registers (no scalar
-      // registers tied up across the kernel)
-      const int per = d.S * RT;
+    };
+    for (int ub = 0; ub < units; ub += 64) {
+      const int u = ub + lane;
+      const bool mine = u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h && (ns0 + u) % d.S == c;
+      uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
       while (mask) {
         const int ua = __builtin_ctzll(mask);
         mask &= mask - 1;
@@ -879,6 +894,9 @@ pass_kernel(PassArgs a) {
         }
         const bool two = ubb >= 0;
         const int nsA = ns0 + ub + ua, nsB = two ? ns0 + ub + ubb : nsA;
+        wait_all(nsA);
+        if (two) wait_all(nsB);
+        asm volatile("" ::: "memory");           // the partial tiles are read after the arrivals
         Tiles<RT> sA, sB;
         sA.zero();
         sB.zero();
