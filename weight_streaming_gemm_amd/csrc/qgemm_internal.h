@@ -139,7 +139,7 @@ constexpr int PASS_NH = 4;                       // helper waves per workgroup
 constexpr int PASS_THREADS = (PASS_NC + PASS_NH) * 64;
 constexpr int PASS_PIECES = 2;                   // LDS partial tiles per compute wave
 constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave (1-2 row tiles)
-inline constexpr int pass_ring(int RT) { return RT <= 2 ? PASS_RING : 6; }   // registers left at 3 row tiles
+inline constexpr int pass_ring(int RT) { return RT <= 2 ? PASS_RING : 7; }   // registers left at 3 row tiles
 constexpr int PASS_MAX_CHUNKS = 32;
 // barrier words: bar[0] global counter, bar[16] exit counter, bar[32 + 32 k] group k's
 // counter, bar[512 + 32 k] group k's release word (k < 8)
