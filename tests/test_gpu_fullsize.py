@@ -80,6 +80,20 @@ def test_layer_matrix_all_outputs(orc, which):
     for R in (1, 3):
         print(f"layer {which} R={R} vector-unit kernel", flush=True)
         assert_parity(G.run(g, x48[:R], path=Q.PATH_VALU), ref48[:R], f"valu {which} R={R}")
+    # the same GEMM in the persistent pass kernel: one, two and three row tiles, in K
+    # chunks from 24 rows on, with several of a helper's chunk sums added per round
+    import torch
+    seq = wsg.Seq([g], persistent=True)
+    xd = G.to_dev(x48)
+    y = torch.empty((max(LAYER_RS), m.N), dtype=torch.float32, device="cuda")
+    for R in (12, 24, 48):
+        print(f"layer {which} R={R} persistent pass kernel", flush=True)
+        y.fill_(-7.0)
+        seq.run([xd[:R]], [y[:R]], R)
+        torch.cuda.synchronize()
+        assert_parity(y[:R].cpu().numpy(), ref48[:R], f"persistent {which} R={R}")
+    assert seq.errors() == 0
+    seq.close()
     g.close()
 
 
