@@ -284,7 +284,9 @@ int qgemm_destroy(qgemm_t h);
  *                         qgemm_run), captured into a HIP graph on the first
  *                         run for a given (R, pointer set) and replayed after;
  *   QGEMM_SEQ_PERSISTENT  one cooperative launch for all GEMMs (below).
- * and, with QGEMM_SEQ_PERSISTENT, the form of the min term (dmin m_s X_s):
+ * and, with QGEMM_SEQ_PERSISTENT, the form of the min term (dmin m_s X_s) up to
+ * 16 rows (from 17 rows on, two or three 16-row tiles, the sums are always
+ * taken: measured faster there, as the products grow with the row tiles):
  *   0                          eight more matrix-core products per weight block,
  *                              of the activation operands with the mins;
  *   QGEMM_SEQ_SUB_BLOCK_SUMS   the fp32 sub-block sums X_s of x, computed when

@@ -201,8 +201,9 @@ def pass_block_bytes(R):
 
 def pass_run(mats, xs, P, x_area=None, max_chunks=PASS_MAX_CHUNKS, msum=False):
     """The pass kernel replayed over GEMMs mats = [(canon, N, K)] with activations
-    xs (bf16 bits, R x K each), the min term from sub-block sums (msum) or from
-    products with the mins: the list of y."""
+    xs (bf16 bits, R x K each), the min term from sub-block sums (msum, and
+    always beyond 16 rows, as in the kernel) or from products with the mins: the
+    list of y."""
     G = len(mats)
     canons = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _ in mats]
     xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]

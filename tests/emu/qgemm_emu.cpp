@@ -674,7 +674,7 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
         Tile acc((size_t)RT * 64, f32x4{0, 0, 0, 0});
         for (int left = count; left > 0; --left) {
           const int ns = step / KB, j = step % KB;
-          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, RT, msum != 0, acc.data());
+          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, RT, msum != 0 || RT > 1, acc.data());
           if (jj == kbc - 1 || left == 1) {
             pieces[w].push_back(acc);
             acc.assign((size_t)RT * 64, f32x4{0, 0, 0, 0});

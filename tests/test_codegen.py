@@ -100,12 +100,12 @@ def _pass_ring(rt: int) -> int:
     return ring if rt <= int(upto) else int(deep)
 
 
-@pytest.mark.parametrize("rt", [1, 2, 3])
-@pytest.mark.parametrize("msum", [False, True])
+@pytest.mark.parametrize("rt,msum", [(1, False), (1, True), (2, True), (3, True)])
 def test_pass_step_loop_keeps_ring_in_flight(pass_asm, msum, rt):
     """The pass kernel's step loop at rt 16-row tiles: RING steps per ring turn,
     each behind a wait that leaves the other RING - 1 stages in flight, and no
-    spills to scratch."""
+    spills to scratch.  From two row tiles on the kernel exists only with the
+    sub-block sums (the products form is not instantiated there)."""
     ring = _pass_ring(rt)
     body = _body(pass_asm, f"_ZN2qg11pass_kernelILi{ring}ELb{int(msum)}ELi{rt}EEEvNS_8PassArgsE")
     per_step = rt * (8 + (2 if msum else 8))

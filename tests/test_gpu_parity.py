@@ -539,7 +539,7 @@ def test_seq_matches_oracle_and_repeats_bitwise(orc, mode):
 @pytest.mark.parametrize("msum", [False, True])
 def test_seq_persistent_row_tiles_match_oracle_and_repeat_bitwise(orc, msum):
     """Rows beyond 16 in the pass kernel: two or three 16-row tiles per weight
-    step.  A five-GEMM sequence whose K = 25600 GEMM runs in 20 K chunks at 24 rows
+    step, the min term from the sub-block sums whatever the flag says.  A five-GEMM sequence whose K = 25600 GEMM runs in 20 K chunks at 24 rows
     and 25 at 48 (the chunk partials of a sub-tile added in two batches), at 48,
     33, 24 and 17 rows: parity with the oracle and a bitwise-equal repeat."""
     import torch

@@ -348,36 +348,21 @@ pass_kernel(PassArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) ds[rt] = ms[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int base = slot * SB;
-        if constexpr (MSUM) {
-          for (int t = 0; t < 8; ++t) {
-            f16x8 xa[RT];
+        static_assert(MSUM, "several row tiles take the min term from the sub-block sums");
+        for (int t = 0; t < 8; ++t) {
+          f16x8 xa[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const f16x8*>(xlds + base + xoff[rt] + t * 16);
-            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
-            const f16x8 b = build_b(wd, cst);
+          for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const f16x8*>(xlds + base + xoff[rt] + t * 16);
+          const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
+          const f16x8 b = build_b(wd, cst);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
-          }
+          for (int rt = 0; rt < RT; ++rt) ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
+        }
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[rt]);
-            ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms[rt], 0, 0, 0);
-            ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms[rt], 0, 0, 0);
-          }
-        } else {
-          const f16x8 bm = build_m_full(cst);
-          for (int t = 0; t < 8; ++t) {
-            f16x8 xa[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const f16x8*>(xlds + base + xoff[rt] + t * 16);
-            const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
-            const f16x8 b = build_b(wd, cst);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
-              ms[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], bm, ms[rt], 0, 0, 0);
-            }
-          }
+        for (int rt = 0; rt < RT; ++rt) {
+          const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[rt]);
+          ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms[rt], 0, 0, 0);
+          ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms[rt], 0, 0, 0);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -1078,8 +1063,15 @@ pass_kernel(PassArgs a) {
 template <int RT>
 const void* pass_kernel_for(bool msum) {
   constexpr int RING = pass_ring(RT);
-  return msum ? reinterpret_cast<const void*>(&pass_kernel<RING, true, RT>)
-              : reinterpret_cast<const void*>(&pass_kernel<RING, false, RT>);
+  if constexpr (RT > 1) {
+    // several row tiles take the sub-block sums whatever msum says: the
+    // products with the mins grow with the row tiles (8 per tile and step)
+    (void)msum;
+    return reinterpret_cast<const void*>(&pass_kernel<RING, true, RT>);
+  } else {
+    return msum ? reinterpret_cast<const void*>(&pass_kernel<RING, true, RT>)
+                : reinterpret_cast<const void*>(&pass_kernel<RING, false, RT>);
+  }
 }
 
 hipError_t launch_pass(const PassArgs& a, bool msum, hipStream_t st) {
