@@ -842,149 +842,92 @@ pass_kernel(PassArgs a) {
     // workgroup, and the work is spread evenly rather than left to whichever
     // chunk arrives last): once all S chunks have arrived, the S RT partial
     // tiles (item k = c RT + rt) added per row tile in chunk order, GL loads in
-    // flight together.  At two row tiles the counters of all pending sub-tiles
-    // are read at once and a round takes every ready sub-tile that fits (4 of
-    // 2 chunks, 2 of 3 or 4); at three, two sub-tiles per round when both fit.
-    // Else rounds of GL items of one.  Addresses and sub-tile indices stay in
-    // vector registers (no scalar registers tied up across the kernel).
+    // flight together.  The counters of all pending sub-tiles are read at once
+    // and a round takes the ready sub-tiles that fit: at two row tiles 16 loads
+    // (4 sub-tiles of 2 chunks, 2 of 3 or 4), at three 24 (2 sub-tiles of up
+    // to 4 chunks); a sub-tile of more items takes rounds of its own.
+    // Addresses and sub-tile indices stay in vector registers (no scalar
+    // registers tied up across the kernel).
     __builtin_amdgcn_s_waitcnt(0);
     for (int ub = 0; ub < units; ub += 64) {
       const int u = ub + lane;
       if (u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h)
         __hip_atomic_fetch_add(cnt + ns0 + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if constexpr (RT == 2) {
-      const int per = d.S * RT;
-      // one round over up to GL / PS of the ready sub-tiles in rdy, sub-tile j's items
-      // at slots j PS + i (PS >= per, or PS = GL with rounds of GL items of one)
-      auto gather = [&](auto PSC, uint64_t& rdy, int ub) __attribute__((always_inline)) {
-        constexpr int PS = decltype(PSC)::value, NB = GL / PS;
-        int nsj[NB];
-        uint32_t off[NB];
-  #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          nsj[j] = -1;
-          if (rdy) {
-            nsj[j] = ns0 + ub + __builtin_ctzll(rdy);
-            rdy &= rdy - 1;
-          }
-          asm volatile("" : "+v"(nsj[j]));        // in a vector register: no scalar registers held
+    constexpr int GLN = RT == 3 ? 8 * RT : GL;   // partial tiles in flight per round
+    const int per = d.S * RT;
+    // one round over up to GLN / PS of the ready sub-tiles in rdy, sub-tile j's items
+    // at slots j PS + i (PS >= per, or PS = GLN with rounds of GLN items of one)
+    auto gather = [&](auto PSC, uint64_t& rdy, int ub) __attribute__((always_inline)) {
+      constexpr int PS = decltype(PSC)::value, NB = GLN / PS;
+      int nsj[NB];
+      uint32_t off[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        nsj[j] = -1;
+        if (rdy) {
+          nsj[j] = ns0 + ub + __builtin_ctzll(rdy);
+          rdy &= rdy - 1;
         }
-        Tiles<RT> sj[NB];
-  #pragma unroll
-        for (int j = 0; j < NB; ++j) sj[j].zero();
-        for (int k0 = 0; k0 < per; k0 += GL) {     // several rounds only for one sub-tile of more than GL items
-  #pragma unroll
-          for (int j = 0; j < NB; ++j) off[j] = nsj[j] < 0 ? OOB : (uint32_t)(nsj[j] * per + k0) * 1024u + lane * 16;
-          f32x4 v[GL];
-  #pragma unroll
-          for (int k = 0; k < GL; ++k)             // slots past a sub-tile's items load what follows, unused
-            v[k] = bload<f32x4, SC1>(pr, off[k / PS] + (uint32_t)(k % PS) * 1024u);
-  #pragma unroll
-          for (int k = 0; k < GL; ++k) {
-            const int j = k / PS, i = k % PS, rt = i % RT;   // item k0 + i: chunk (k0 + i) / RT, row tile rt
-            if (k0 + i < per) sj[j].v[rt] = k0 + i < RT ? v[k] : sj[j].v[rt] + v[k];
-          }
-        }
-  #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if (nsj[j] < 0) continue;
-          store_y(nsj[j], sj[j]);
-          if (lane == 0) __hip_atomic_store(cnt + nsj[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      };
-      for (int ub = 0; ub < units; ub += 64) {
-        const int u = ub + lane;
-        const bool mine = u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h && (ns0 + u) % d.S == c;
-        uint64_t pend = __builtin_amdgcn_ballot_w64(mine);
-        uint32_t spins = 0;
-        while (pend) {
-          // the counters of all pending sub-tiles in one read; the complete ones are added up
-          bool ready = dead;
-          if (!dead && ((pend >> lane) & 1u))
-            ready = __hip_atomic_load(cnt + ns0 + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)d.S;
-          uint64_t rdy = __builtin_amdgcn_ballot_w64(ready) & pend;
-          if (!rdy) {
-            if (++spins > SPIN_LIMIT) {
-              if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              dead = true;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-          }
-          pend &= ~rdy;
-          asm volatile("" ::: "memory");           // the partial tiles are read after the arrivals
-          while (rdy) {
-            if constexpr (RT == 2) {               // several sub-tiles per round where 2 or 4 chunks' items fit
-              if (per <= 2 * RT)
-                gather(std::integral_constant<int, 2 * RT>{}, rdy, ub);
-              else if (per <= 4 * RT)
-                gather(std::integral_constant<int, 4 * RT>{}, rdy, ub);
-              else
-                gather(std::integral_constant<int, GL>{}, rdy, ub);
-            } else {
-              gather(std::integral_constant<int, GL>{}, rdy, ub);
-            }
-          }
+        asm volatile("" : "+v"(nsj[j]));        // in a vector register: no scalar registers held
+      }
+      Tiles<RT> sj[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sj[j].zero();
+      for (int k0 = 0; k0 < per; k0 += GLN) {    // several rounds only for one sub-tile of more than GLN items
+#pragma unroll
+        for (int j = 0; j < NB; ++j) off[j] = nsj[j] < 0 ? OOB : (uint32_t)(nsj[j] * per + k0) * 1024u + lane * 16;
+        f32x4 v[GLN];
+#pragma unroll
+        for (int k = 0; k < GLN; ++k)            // slots past a sub-tile's items load what follows, unused
+          v[k] = bload<f32x4, SC1>(pr, off[k / PS] + (uint32_t)(k % PS) * 1024u);
+#pragma unroll
+        for (int k = 0; k < GLN; ++k) {
+          const int j = k / PS, i = k % PS, rt = i % RT;   // item k0 + i: chunk (k0 + i) / RT, row tile rt
+          if (k0 + i < per) sj[j].v[rt] = k0 + i < RT ? v[k] : sj[j].v[rt] + v[k];
         }
       }
-    } else {
-      const int per = d.S * RT;
-      auto wait_all = [&](int ns) __attribute__((always_inline)) {
-        if (lane == 0 && !dead) {
-          uint32_t n_ = 0;
-          while (__hip_atomic_load(cnt + ns, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)d.S) {
-            if (++n_ > SPIN_LIMIT) {
-              __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              dead = true;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (nsj[j] < 0) continue;
+        store_y(nsj[j], sj[j]);
+        if (lane == 0) __hip_atomic_store(cnt + nsj[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    for (int ub = 0; ub < units; ub += 64) {
+      const int u = ub + lane;
+      const bool mine = u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h && (ns0 + u) % d.S == c;
+      uint64_t pend = __builtin_amdgcn_ballot_w64(mine);
+      uint32_t spins = 0;
+      while (pend) {
+        // the counters of all pending sub-tiles in one read; the complete ones are added up
+        bool ready = dead;
+        if (!dead && ((pend >> lane) & 1u))
+          ready = __hip_atomic_load(cnt + ns0 + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)d.S;
+        uint64_t rdy = __builtin_amdgcn_ballot_w64(ready) & pend;
+        if (!rdy) {
+          if (++spins > SPIN_LIMIT) {
+            if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dead = true;
           }
+          __builtin_amdgcn_s_sleep(1);
+          continue;
         }
-      };
-      for (int ub = 0; ub < units; ub += 64) {
-        const int u = ub + lane;
-        const bool mine = u < units && pass_step_owner(u * kbc, PASS_NC, n) % PASS_NH == h && (ns0 + u) % d.S == c;
-        uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
-        while (mask) {
-          const int ua = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          int ubb = -1;
-          if (2 * per <= GL && mask) {
-            ubb = __builtin_ctzll(mask);
-            mask &= mask - 1;
-          }
-          const bool two = ubb >= 0;
-          const int nsA = ns0 + ub + ua, nsB = two ? ns0 + ub + ubb : nsA;
-          wait_all(nsA);
-          if (two) wait_all(nsB);
-          asm volatile("" ::: "memory");           // the partial tiles are read after the arrivals
-          Tiles<RT> sA, sB;
-          sA.zero();
-          sB.zero();
-          for (int k0 = 0; k0 < per; k0 += GL) {
-            uint32_t offA = (uint32_t)(nsA * per + k0) * 1024u + lane * 16;
-            uint32_t offB = (uint32_t)(nsB * per - per) * 1024u + lane * 16;   // item k - per of B at slot k
-            asm volatile("" : "+v"(offA), "+v"(offB));
-            f32x4 v[GL];
-  #pragma unroll
-            for (int k = 0; k < GL; ++k) {
-              const bool inA = k0 + k < per, inB = two && k >= per && k < 2 * per;
-              v[k] = bload<f32x4, SC1>(pr, inA ? offA + k * 1024u : inB ? offB + k * 1024u : OOB);
-            }
-  #pragma unroll
-            for (int k = 0; k < GL; ++k) {
-              const int rt = k % RT;                 // GL and per are multiples of RT
-              if (k0 + k < per) sA.v[rt] = k0 == 0 && k < RT ? v[k] : sA.v[rt] + v[k];
-              else if (two && k < 2 * per) sB.v[rt] = k < per + RT ? v[k] : sB.v[rt] + v[k];
-            }
-          }
-          store_y(nsA, sA);
-          if (two) store_y(nsB, sB);
-          if (lane == 0) {
-            __hip_atomic_store(cnt + nsA, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (two) __hip_atomic_store(cnt + nsB, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pend &= ~rdy;
+        asm volatile("" ::: "memory");           // the partial tiles are read after the arrivals
+        while (rdy) {
+          if constexpr (RT == 2) {               // several sub-tiles per round where their items fit
+            if (per <= 2 * RT)
+              gather(std::integral_constant<int, 2 * RT>{}, rdy, ub);
+            else if (per <= 4 * RT)
+              gather(std::integral_constant<int, 4 * RT>{}, rdy, ub);
+            else
+              gather(std::integral_constant<int, GLN>{}, rdy, ub);
+          } else {
+            if (per <= GLN / 2)
+              gather(std::integral_constant<int, GLN / 2>{}, rdy, ub);
+            else
+              gather(std::integral_constant<int, GLN>{}, rdy, ub);
           }
         }
       }
