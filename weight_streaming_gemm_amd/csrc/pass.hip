@@ -672,7 +672,43 @@ pass_kernel(PassArgs a) {
     // every partial tile of this helper is stored; arrive at each of its units'
     // sub-tile counters (one lane per unit: the units whose first step lies in
     // wave h or h + PASS_NH); the last of the S chunks to arrive adds the S
-    // partial tiles in chunk order and writes y
+    // partial tiles in chunk order and writes y.  A round takes as many of those
+    // sub-tiles as 16 loads hold (8 of 2 chunks, 4 of up to 4, 2 of up to 8),
+    // all loads in flight together; sub-tile indices stay in vector registers.
+    auto gather = [&](auto PSC, uint64_t& mask, int ub) __attribute__((always_inline)) {
+      constexpr int PS = decltype(PSC)::value, NB = 16 / PS;
+      int nsj[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        nsj[j] = -1;
+        if (mask) {
+          nsj[j] = ns0 + ub + __builtin_ctzll(mask);
+          mask &= mask - 1;
+        }
+        asm volatile("" : "+v"(nsj[j]));
+      }
+      f32x4 v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int j = k / PS, cc = k % PS;
+        v[k] = bload<f32x4, SC1>(pr, nsj[j] >= 0 && cc < d.S ? (uint32_t)cc * part_tile + (uint32_t)nsj[j] * 1024u + lane * 16 : OOB);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (nsj[j] < 0) continue;
+        f32x4 sum = v[j * PS];
+#pragma unroll
+        for (int cc = 1; cc < PS; ++cc)
+          if (cc < d.S) sum += v[j * PS + cc];
+        const int nn = nsj[j] * TILE_N + nl;
+        if (nn < d.N)
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
+          }
+        if (lane == 0) __hip_atomic_store(cnt + nsj[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
     __builtin_amdgcn_s_waitcnt(0);
     for (int ub = 0; ub < units; ub += 64) {
       bool last = false;
@@ -683,25 +719,14 @@ pass_kernel(PassArgs a) {
       }
       uint64_t mask = __builtin_amdgcn_ballot_w64(last);
       while (mask) {
-        // one sub-tile at a time, all its chunks' loads in flight together
-        const int uu = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const int ns = ns0 + ub + uu;
-        f32x4 v[16];
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc)
-          v[cc] = bload<f32x4, SC1>(pr, cc < d.S ? (uint32_t)cc * part_tile + (uint32_t)ns * 1024u + lane * 16 : OOB);
-        f32x4 sum = v[0];
-#pragma unroll
-        for (int cc = 1; cc < 16; ++cc)
-          if (cc < d.S) sum += v[cc];
-        const int nn = ns * TILE_N + nl;
-        if (nn < d.N)
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            if (r < R) bstore1_sc1(sum[i], yr, (uint32_t)((r * d.N + nn) * 4));
-          }
-        if (lane == 0) __hip_atomic_store(cnt + ns, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d.S <= 2)
+          gather(std::integral_constant<int, 2>{}, mask, ub);
+        else if (d.S <= 4)
+          gather(std::integral_constant<int, 4>{}, mask, ub);
+        else if (d.S <= 8)
+          gather(std::integral_constant<int, 8>{}, mask, ub);
+        else
+          gather(std::integral_constant<int, 16>{}, mask, ub);
       }
     }
   };
