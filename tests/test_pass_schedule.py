@@ -109,34 +109,30 @@ def test_pass_replay_with_row_tiles_matches_oracle(orc, R, P, x_blocks):
 
 
 @pytest.mark.parametrize("R", range(1, 49))
-def test_in_place_conversion_reads_every_raw_row_before_overwriting_it(R):
-    """The pass kernel converts a slot in place: the raw bf16 rows (512 bytes
-    each, in pairs) become 528-byte operand rows (a missing odd row included)
-    and the 8 R fp32 sums (at 528 times R rounded up to even).  Pairs go two at
-    a time from the last to the first (pair 0 twice when their number is odd),
-    both read before either is written.  Replayed byte by byte: nothing is
-    written over a raw row still to be read, and everything stays in the slot."""
+def test_in_place_conversion_touches_only_its_own_raw_pair(R):
+    """The pass kernel converts a slot in place: raw row pair q (2 x 512 bytes of
+    bf16) lands at 1056 q, where its two 528-byte operand rows go (a missing odd
+    row included), and the 8 R fp32 sums go to 528 times R rounded up to even.
+    Pairs are dealt to all waves in any order, so replayed byte by byte: the
+    writes of pair q fall on no other pair's raw bytes, and everything stays in
+    the slot (the reads of a pair come before its writes, in one wave)."""
     sb = emu.pass_block_bytes(R)
     row, pairs = 528, (R + 1) // 2
     R2 = 2 * pairs
-    owner = np.full(sb, -1)                       # raw row whose bytes lie here
-    for r in range(R2):
-        owner[512 * r:512 * (r + 1)] = r
-    unread = set(range(R2))
-    for pp in range(pairs - 1, -1, -2):
-        qq = max(pp - 1, 0)
-        unread -= {2 * pp, 2 * pp + 1, 2 * qq, 2 * qq + 1}
-        for q in (pp, qq):
-            writes = []
-            for r in (2 * q, 2 * q + 1):
-                writes.append((row * r, row * r + 512))                      # operands of row r
-                if r < R:
-                    writes += [(row * R2 + (gg * R + r) * 8, row * R2 + (gg * R + r) * 8 + 8) for gg in range(4)]
-            for lo, hi in writes:
-                assert 0 <= lo and hi <= sb, f"R={R} pair {q}: write [{lo}, {hi}) outside the slot of {sb}"
-                hit = set(owner[lo:hi].tolist()) & unread
-                assert not hit, f"R={R} pair {q}: write [{lo}, {hi}) over unread raw rows {hit}"
-    assert not unread
+    owner = np.full(sb, -1)                       # raw pair whose bytes lie here
+    for q in range(pairs):
+        assert 1056 * q + 1024 <= sb
+        owner[1056 * q:1056 * q + 1024] = q
+    for q in range(pairs):
+        writes = []
+        for r in (2 * q, 2 * q + 1):
+            writes.append((row * r, row * r + 512))                          # operands of row r
+            if r < R:
+                writes += [(row * R2 + (gg * R + r) * 8, row * R2 + (gg * R + r) * 8 + 8) for gg in range(4)]
+        for lo, hi in writes:
+            assert 0 <= lo and hi <= sb, f"R={R} pair {q}: write [{lo}, {hi}) outside the slot of {sb}"
+            hit = set(owner[lo:hi].tolist()) - {-1, q}
+            assert not hit, f"R={R} pair {q}: write [{lo}, {hi}) over the raw bytes of pairs {hit}"
 
 
 @pytest.mark.parametrize("R,P", [(12, 256), (16, 256), (1, 256), (12, 100), (16, 37), (24, 256), (48, 256), (48, 61)])

@@ -194,19 +194,21 @@ pass_kernel(PassArgs a) {
   const int XS = PASS_X_ROW * pass_x_rows(R), SB = pass_x_block_bytes(R);
   constexpr int GL = (16 / RT) * RT;            // partial tiles loaded together by a helper
 
-  // ---- the conversion of one block's raw bf16 rows into its image, in place.
+  // ---- the conversion of the raw bf16 rows into the blocks' images, in place.
   // Rows go in pairs, 32 lanes (gg, t) per row: x[r, 64 gg + 4 t + {0..3}] and
-  // the same 32 further on make operand (gg, t).  Pairs are taken two at a time
-  // from the last to the first (pair 0 twice when their number is odd), both
-  // read before either is written.  Pair pp's operands go to 1056 pp and up,
-  // over raw pairs pp and pp + 1 only (1056 pp + 1040 <= 1024 (pp + 2) for
-  // pp < 32), and a wave's LDS reads and writes run in program order: every raw
-  // row is read before anything is written over it.
-  auto convert_block = [&](uint8_t* slot) __attribute__((always_inline)) {
+  // the same 32 further on make operand (gg, t).  Raw pair q lies at 1056 q, the
+  // place of its own operands (row 2 q + h at 1056 q + 512 h raw, 1056 q + 528 h
+  // converted), so a pair is read and written over by one wave and by nothing
+  // else (its reads come first: a wave's LDS accesses run in program order).
+  // With a block for every wave, wave v takes the blocks v mod (PASS_NC +
+  // PASS_NH); with fewer, the pairs of all blocks are dealt to all waves: the
+  // units (block, pair) u = v, v + PASS_NC + PASS_NH, ... go to wave v.
+  auto convert_share = [&](int xblk, int v) __attribute__((always_inline)) {
+    constexpr int NW = PASS_NC + PASS_NH;
+    const int RP = (R + 1) >> 1, units = xblk * RP;
     const int half = lane >> 5, sub = lane & 31, gg = sub >> 3, t = sub & 7;
-    const uint8_t* const in = slot + half * 512 + (64 * gg + 4 * t) * 2;
-    uint8_t* const out = slot + half * PASS_X_ROW + sub * 16;
-    auto sums = [&](u32x2 lo, u32x2 hi, int r) __attribute__((always_inline)) {
+    const int lin = half * 512 + (64 * gg + 4 * t) * 2, lout = half * PASS_X_ROW + sub * 16;
+    auto sums = [&](uint8_t* slot, u32x2 lo, u32x2 hi, int r) __attribute__((always_inline)) {
       if constexpr (MSUM) {
         // sub-block sums: the 8 lanes t of lane group gg add their run sums as
         // ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7))
@@ -217,23 +219,51 @@ pass_kernel(PassArgs a) {
         if (r < R && t == 0) *reinterpret_cast<f32x2*>(slot + XS + (gg * R + r) * 8) = f32x2{s0, s1};
       }
     };
-    for (int pp = ((R + 1) >> 1) - 1; pp >= 0; pp -= 2) {
-      const int qq = pp > 0 ? pp - 1 : 0;
-      const u32x2 lo0 = *reinterpret_cast<const u32x2*>(in + pp * 1024);
-      const u32x2 hi0 = *reinterpret_cast<const u32x2*>(in + pp * 1024 + 64);
-      const u32x2 lo1 = *reinterpret_cast<const u32x2*>(in + qq * 1024);
-      const u32x2 hi1 = *reinterpret_cast<const u32x2*>(in + qq * 1024 + 64);
-      *reinterpret_cast<f16x8*>(out + pp * 2 * PASS_X_ROW) = build_a(lo0.x, lo0.y, hi0.x, hi0.y);
-      sums(lo0, hi0, 2 * pp + half);
-      *reinterpret_cast<f16x8*>(out + qq * 2 * PASS_X_ROW) = build_a(lo1.x, lo1.y, hi1.x, hi1.y);
-      sums(lo1, hi1, 2 * qq + half);
+    // pairs q0 of block b0 and q1 of block b1 (when two), both read before either is written
+    auto convert2 = [&](int b0, int q0, int b1, int q1, bool two) __attribute__((always_inline)) {
+      uint8_t* const s0 = xlds + b0 * SB + q0 * 1056;
+      uint8_t* const s1 = xlds + b1 * SB + q1 * 1056;
+      const u32x2 lo0 = *reinterpret_cast<const u32x2*>(s0 + lin);
+      const u32x2 hi0 = *reinterpret_cast<const u32x2*>(s0 + lin + 64);
+      u32x2 lo1 = lo0, hi1 = hi0;
+      if (two) {
+        lo1 = *reinterpret_cast<const u32x2*>(s1 + lin);
+        hi1 = *reinterpret_cast<const u32x2*>(s1 + lin + 64);
+      }
+      *reinterpret_cast<f16x8*>(s0 + lout) = build_a(lo0.x, lo0.y, hi0.x, hi0.y);
+      sums(xlds + b0 * SB, lo0, hi0, 2 * q0 + half);
+      if (two) {
+        *reinterpret_cast<f16x8*>(s1 + lout) = build_a(lo1.x, lo1.y, hi1.x, hi1.y);
+        sums(xlds + b1 * SB, lo1, hi1, 2 * q1 + half);
+      }
+    };
+    if (xblk >= NW) {
+      // enough blocks for every wave: whole blocks, b = v mod NW
+      for (int bb = v; bb < xblk; bb += NW)
+        for (int q = 0; q < RP; q += 2) convert2(bb, q, bb, q + 1, q + 1 < RP);
+      return;
     }
-  };
-  // the conversion of a GEMM's xblk blocks is shared by all waves of the
-  // workgroup: wave v (compute waves 0 .. PASS_NC - 1, then the helpers) takes
-  // the blocks b = v mod (PASS_NC + PASS_NH)
-  auto convert_share = [&](int xblk, int v) __attribute__((always_inline)) {
-    for (int b = v; b < xblk; b += PASS_NC + PASS_NH) convert_block(xlds + b * SB);
+    // fewer: the units (block, pair) u = v, v + NW, ...
+    int b0 = 0, q0 = v;
+    while (q0 >= RP) {
+      q0 -= RP;
+      ++b0;
+    }
+    auto step = [&](int& bb, int& qq) __attribute__((always_inline)) {
+      qq += NW;
+      while (qq >= RP) {
+        qq -= RP;
+        ++bb;
+      }
+    };
+    for (int u = v; u < units; u += 2 * NW) {
+      int b1 = b0, q1 = q0;
+      step(b1, q1);
+      convert2(b0, q0, b1, q1, u + NW < units);
+      b0 = b1;
+      q0 = q1;
+      step(b0, q0);
+    }
   };
 
   if (wv < PASS_NC) {
@@ -467,11 +497,11 @@ pass_kernel(PassArgs a) {
   }
 
   // ---- the activations of GEMM g for this workgroup's chunk: block c kbc + b of x
-  // goes to slot b, and helper h copies the blocks b = h mod PASS_NH: row r of
-  // the block (512 bytes of bf16) to slot + 512 r, two rows per load that
+  // goes to slot b, and helper h copies the blocks b = h mod PASS_NH: row pair
+  // q of the block (2 x 512 bytes of bf16) to slot + 1056 q, one load that
   // writes LDS directly (lane l's 16 bytes land at the load's base + 16 l), all
   // of the helper's loads in flight together.  All waves then convert the
-  // blocks in place (convert_share).
+  // pairs in place (convert_share).
   auto stage_raw = [&](const PassGemm& d, int c) __attribute__((always_inline)) {
     const int K = d.KB * SB_W;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(d.x, (uint32_t)(R * K * 2));
@@ -481,7 +511,7 @@ pass_kernel(PassArgs a) {
       for (int pr = 0; pr < RP; ++pr) {
         const int r = 2 * pr + half;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xr, (__attribute__((address_space(3))) void*)(xlds + b * SB + pr * 1024), 16,
+            xr, (__attribute__((address_space(3))) void*)(xlds + b * SB + pr * 1056), 16,
             r < R ? (uint32_t)(r * K * 2) + blk : OOB, 0, 0, 0);
       }
     }

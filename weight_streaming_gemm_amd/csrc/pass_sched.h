@@ -69,8 +69,9 @@ QG_HD int pass_step_owner(int i, int NC, int n) {
 // others and never read).  Row r's 32 binary16 A operands sit at PASS_X_ROW r
 // (operand (gg, t) at 16 (8 gg + t); the 16-byte pad per row puts the rows of
 // one step on different banks), then the 8 R fp32 sub-block sums at
-// PASS_X_ROW R2.  The raw bf16 rows land in the same slot first (row r at
-// 512 r) and are converted in place.
+// PASS_X_ROW R2.  The raw bf16 rows land in the same slot first (row pair q
+// at 2 PASS_X_ROW q, row 2 q + h at 512 h further, under its own operands) and
+// each pair is converted in place.
 constexpr int PASS_X_ROW = 528;
 QG_HD int pass_x_rows(int R) { return R + (R & 1); }
 QG_HD int pass_x_block_bytes(int R) { return PASS_X_ROW * pass_x_rows(R) + 32 * R; }
