@@ -76,6 +76,36 @@ void min_term_f32(const float (*xs)[2], const WConst* c, f32x4* ms) {
   }
 }
 
+// The pass kernel's form of the same min term: X_s / 256 in two binary16 parts
+// (hi = f16(X_s / 256), lo = f16(X_s / 256 - hi)), lane group g's A holding
+// (hi_2g, hi_2g+1, lo_2g, lo_2g+1) of its row and B (m_2g, m_2g+1, m_2g, m_2g+1)
+// of its output, in one 16 x 16 x 16 product; the caller scales -dmin by 256.
+void min_term_parts(const float (*xs)[2], const WConst* c, f32x4* ms) {
+  float A[16][16], B[16][16];
+  for (int l = 0; l < 64; ++l) {
+    float part[4];
+    for (int h = 0; h < 2; ++h) {
+      const float a = xs[l][h] * (1.0f / 256.0f);
+      const _Float16 hi = (_Float16)a;
+      part[h] = (float)hi;
+      part[2 + h] = (float)(_Float16)(a - (float)hi);
+    }
+    for (int e = 0; e < 4; ++e) {
+      A[l % 16][4 * (l / 16) + e] = part[e];
+      B[4 * (l / 16) + e][l % 16] = (float)c[l].m[e & 1];
+    }
+  }
+  f32x4 out[64];
+  for (int l = 0; l < 64; ++l)
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * (l / 16) + v, j = l % 16;
+      double s = ms[l][v];
+      for (int k = 0; k < 16; ++k) s += (double)A[i][k] * (double)B[k][j];
+      out[l][v] = (float)s;
+    }
+  for (int l = 0; l < 64; ++l) ms[l] = out[l];
+}
+
 void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
   int64_t KB = K / SB_W, NS = padded_n(N) / TILE_N;
   for (int64_t ns = 0; ns < NS; ++ns)
@@ -206,7 +236,7 @@ Sum2 s_operand(const std::vector<Sum2>& sums, int R, int64_t b, int rt, int lane
 // accumulating into acc[NT][RT][64].
 void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int64_t NS, int64_t j, int64_t KB,
                const std::vector<f16x8>& slots, const std::vector<Sum2>& sums, int R, int64_t b, int RT,
-               bool msum, f32x4* acc) {
+               int msum, f32x4* acc) {
   for (int u = 0; u < NT; ++u) {
     const int64_t ns = ns0 + u;
     WConst c[64];
@@ -235,7 +265,10 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
           sv[lane][0] = sp.v[0];
           sv[lane][1] = sp.v[1];
         }
-        min_term_f32(sv, c, ms);
+        if (msum == 2)
+          min_term_parts(sv, c, ms);
+        else
+          min_term_f32(sv, c, ms);
       }
       for (int tt = 0; tt < 8; ++tt) {
         f16x8 av[64], bb[64];
@@ -251,7 +284,7 @@ void wave_step(const uint8_t* packed, int64_t hdr_off, int64_t ns0, int NT, int6
         for (int i = 0; i < 4; ++i) {
           float v = ac[lane][i];
           v = std::fma(c[lane].d, ds[lane][i], v);
-          v = std::fma(c[lane].nmin, ms[lane][i], v);
+          v = std::fma(msum == 2 ? c[lane].nmin * 256.0f : c[lane].nmin, ms[lane][i], v);
           ac[lane][i] = v;
         }
     }
@@ -674,7 +707,7 @@ int emu_pass(int G, const uint8_t* const* canons, const int64_t* Ns, const int64
         Tile acc((size_t)RT * 64, f32x4{0, 0, 0, 0});
         for (int left = count; left > 0; --left) {
           const int ns = step / KB, j = step % KB;
-          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, RT, msum != 0 || RT > 1, acc.data());
+          wave_step(packed.data(), hdr_off, ns, 1, NS, j, KB, slots, sums, R, jj, RT, msum != 0 || RT > 1 ? 2 : 0, acc.data());
           if (jj == kbc - 1 || left == 1) {
             pieces[w].push_back(acc);
             acc.assign((size_t)RT * 64, f32x4{0, 0, 0, 0});

@@ -202,6 +202,32 @@ def test_large_subblock_sums(orc, N, K, R, path):
     g.close()
 
 
+@pytest.mark.parametrize("R", [12, 40])
+def test_large_subblock_sums_persistent(orc, R):
+    """The same sub-blocks at 4096 and 65280 in the pass kernel with the min term
+    from the sub-block sums (two binary16 parts of X_s / 256 per sum): finite and
+    matching the oracle at one and at three row tiles."""
+    import torch
+    import weight_streaming_gemm_amd as wsg
+    N, K = 4096, 1024
+    _flush(f"large sub-block sums, pass kernel R={R}")
+    canon, g = G.make(3, 7, N, K, max_R=48)
+    x = synth.x_bf16(3, 8, R, K).copy()
+    x[0, 32:64] = _bf16_bits(4096.0)
+    x[R - 1, K - 32:] = _bf16_bits(65280.0)
+    x[R // 2, 256 + 96:256 + 128] = _bf16_bits(-65280.0)
+    seq = wsg.Seq([g], persistent=True, sub_block_sums=True)
+    y = torch.empty((R, N), dtype=torch.float32, device="cuda")
+    seq.run([G.to_dev(x)], [y], R)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_parity(got, orc.gemm(canon, N, K, x), f"pass kernel N={N} K={K} R={R}")
+    assert seq.errors() == 0
+    seq.close()
+    g.close()
+
+
 def test_edge_blocks_large_R(orc):
     N, K = 512, 2048
     canon, g = G.make(4, 0, N, K, max_R=48, edge_mode=1)

@@ -47,6 +47,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -91,6 +92,21 @@ __device__ __forceinline__ float sum4_bf16(uint32_t d0, uint32_t d1) {
   const float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), one, 0.0f, false);
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), one, s, false);
 }
+// The min term's fp32 sub-block sums as matrix-core A operands: X_s 2^-8 (in
+// binary16's range for |x| <= 65504: 32 x 65504 / 256 < 8192) in two binary16
+// parts, hi = f16(X_s 2^-8) and lo = f16(X_s 2^-8 - hi) (the difference is exact
+// in fp32), so that one v_mfma_f32_16x16x16_f16 against the mins (exact in
+// binary16) adds m_s (hi + lo) over the 8 sub-blocks; the 2^8 goes back into
+// -dmin (exact).  hi + lo holds X_s 2^-8 to 22 bits, or to 2^-25 absolute where
+// lo is subnormal.
+constexpr float SUM_SCALE = 1.0f / 256.0f, SUM_SCALE_INV = 256.0f;
+__device__ __forceinline__ f16x4 sum_parts(float s0, float s1) {
+  const float a0 = s0 * SUM_SCALE, a1 = s1 * SUM_SCALE;
+  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+  return f16x4{h0, h1, (_Float16)(a0 - (float)h0), (_Float16)(a1 - (float)h1)};
+}
+// B of that product for lane group g: (m_2g, m_2g+1) against both parts
+__device__ __forceinline__ f16x4 min_parts_b(const WConst& c) { return f16x4{c.m[0], c.m[1], c.m[0], c.m[1]}; }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -216,7 +232,7 @@ pass_kernel(PassArgs a) {
         s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
         s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
         s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
-        if (r < R && t == 0) *reinterpret_cast<f32x2*>(slot + XS + (gg * R + r) * 8) = f32x2{s0, s1};
+        if (r < R && t == 0) *reinterpret_cast<f16x4*>(slot + XS + (gg * R + r) * 8) = sum_parts(s0, s1);
       }
     };
     // pairs q0 of block b0 and q1 of block b1 (when two), both read before either is written
@@ -350,9 +366,9 @@ pass_kernel(PassArgs a) {
             const uint32_t wd = (t < 4) ? st.qa[t] : st.qb[t - 4];
             ds = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, build_b(wd, cst), ds, 0, 0, 0);
           }
-          const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[0]);
-          ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms, 0, 0, 0);
-          ms = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms, 0, 0, 0);
+          const f16x4 xs = *reinterpret_cast<const f16x4*>(xlds + base + soff[0]);
+          ms = __builtin_amdgcn_mfma_f32_16x16x16f16(xs, min_parts_b(cst), ms, 0, 0, 0);
+          dm *= SUM_SCALE_INV;
       } else {
           const f16x8 bm = build_m_full(cst);
           for (int t = 0; t < 8; ++t) {
@@ -388,12 +404,13 @@ pass_kernel(PassArgs a) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) ds[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rt], b, ds[rt], 0, 0, 0);
         }
+        const f16x4 bm4 = min_parts_b(cst);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + soff[rt]);
-          ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(cst, 0), ms[rt], 0, 0, 0);
-          ms[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(cst, 1), ms[rt], 0, 0, 0);
+          const f16x4 xs = *reinterpret_cast<const f16x4*>(xlds + base + soff[rt]);
+          ms[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(xs, bm4, ms[rt], 0, 0, 0);
         }
+        dm *= SUM_SCALE_INV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           for (int i = 0; i < 4; ++i) {
