@@ -137,6 +137,11 @@ PASS_MAX_CHUNKS = 32
 PASS_MAX_R = 48
 
 
+def pass_max_chunks(R):
+    """Most K chunks of a GEMM at R rows (16 at one row tile: one round of loads)."""
+    return 16 if R <= 16 else PASS_MAX_CHUNKS
+
+
 def pass_pieces(R):
     """Piece slots per compute wave at R rows (one from two row tiles on)."""
     return PASS_PIECES if R <= 16 else 1
@@ -149,10 +154,11 @@ def pass_x_area(R):
 PASS_X_AREA = pass_x_area(16)
 
 
-def pass_coverage(shapes, R, P=256, x_area=None, max_chunks=PASS_MAX_CHUNKS):
+def pass_coverage(shapes, R, P=256, x_area=None, max_chunks=None):
     """(per-GEMM step hit counts [NS * KB], chunks) of the pass kernel's schedule
     (x_area: the kernel's LDS area at R rows unless given)."""
     x_area = pass_x_area(R) if x_area is None else x_area
+    max_chunks = pass_max_chunks(R) if max_chunks is None else max_chunks
     G = len(shapes)
     Ns = np.array([N for N, _ in shapes], np.int64)
     Ks = np.array([K for _, K in shapes], np.int64)
@@ -199,7 +205,7 @@ def pass_block_bytes(R):
     return lib().emu_pass_block_bytes(R)
 
 
-def pass_run(mats, xs, P, x_area=None, max_chunks=PASS_MAX_CHUNKS, msum=False):
+def pass_run(mats, xs, P, x_area=None, max_chunks=None, msum=False):
     """The pass kernel replayed over GEMMs mats = [(canon, N, K)] with activations
     xs (bf16 bits, R x K each), the min term from sub-block sums (msum, and
     always beyond 16 rows, as in the kernel) or from products with the mins: the
@@ -209,6 +215,7 @@ def pass_run(mats, xs, P, x_area=None, max_chunks=PASS_MAX_CHUNKS, msum=False):
     xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
     R = xs[0].shape[0]
     x_area = pass_x_area(R) if x_area is None else x_area
+    max_chunks = pass_max_chunks(R) if max_chunks is None else max_chunks
     ys = [np.full((R, N), np.nan, dtype=np.float32) for _, N, _ in mats]
     P_ = ctypes.c_void_p * G
     Ns = np.array([N for _, N, _ in mats], dtype=np.int64)

@@ -28,6 +28,8 @@ def test_replay_constants_match_the_kernel():
     assert "return 160 * 1024 - PASS_NC * pass_pieces(RT) * RT * 1024 - 256;" in text
     assert "pass_pieces(int RT) { return RT == 1 ? PASS_PIECES : 1; }" in text
     assert "PASS_MAX_R = 16 * PASS_MAX_RT;" in text
+    assert "pass_max_chunks(int RT) { return RT == 1 ? 16 : PASS_MAX_CHUNKS; }" in text
+    assert emu.pass_max_chunks(16) == 16 and emu.pass_max_chunks(17) == chunks
     assert nc == emu.PASS_NC and pieces == emu.PASS_PIECES and chunks == emu.PASS_MAX_CHUNKS
     assert emu.PASS_MAX_R == 16 * rts
     for R in (1, 16, 17, 32, 33, 48):
@@ -56,6 +58,16 @@ def test_pass_shapes_take_every_step_once(R):
         assert chunks.tolist() == [4, 8, 4, 20, 4]
 
 
+def test_one_row_tile_takes_at_most_16_chunks():
+    """At one row tile the last chunk to arrive adds a sub-tile's partial tiles in
+    one round of 16 loads, so the planner never cuts a GEMM into more chunks there:
+    K = 34 blocks at 16 rows (fitting only as 17 chunks of 2) is refused, and at 17
+    rows (two row tiles, 32 chunks allowed) it runs in 17."""
+    _, ch16 = emu.pass_coverage([(64, 34 * 256)], 16, P=256)
+    _, ch17 = emu.pass_coverage([(64, 34 * 256)], 17, P=256)
+    assert ch16.tolist() == [0] and ch17.tolist() == [17]
+
+
 @pytest.mark.parametrize("P", [1, 3, 7, 64, 250])
 def test_odd_shapes_take_every_step_once(P):
     rng = np.random.default_rng(P)
@@ -65,11 +77,11 @@ def test_odd_shapes_take_every_step_once(P):
     for (N, K), c, S in zip(shapes, counts, chunks):
         if S == 0:                     # no chunking fits (the library refuses such a sequence)
             KB = K // 256
-            assert not any(KB % S2 == 0 and KB // S2 <= 4 for S2 in range(1, min(P, emu.PASS_MAX_CHUNKS, KB) + 1))
+            assert not any(KB % S2 == 0 and KB // S2 <= 4 for S2 in range(1, min(P, emu.pass_max_chunks(12), KB) + 1))
             assert (c == 0).all()
             continue
         planned += 1
-        assert (K // 256) % S == 0 and K // 256 // S <= 4 and S <= min(P, emu.PASS_MAX_CHUNKS)
+        assert (K // 256) % S == 0 and K // 256 // S <= 4 and S <= min(P, emu.pass_max_chunks(12))
         assert (c == 1).all(), f"P={P} N={N} K={K} S={S}"
     assert planned >= 2
 

@@ -1,5 +1,5 @@
 // pass.hip — the whole weight pass (a sequence of GEMMs) in one persistent launch,
-// for up to 16 activation rows.
+// for up to 48 activation rows in one to three 16-row tiles.
 //
 // The pages' decode step streams every quantised weight once and applies it to
 // all stacked rows (OpenJet multi-agent serving page, section on moving the
@@ -14,23 +14,26 @@
 // waves.  A compute wave streams its weight steps through a register ring of
 // RING steps that runs straight across GEMM boundaries, multiplies them on the
 // matrix cores against activations in LDS, and hands each finished partial
-// 16 x 16 tile ("piece") to LDS.  Compute waves issue only loads, so waiting for
-// a step's weights never waits for a store.  The helper waves stage each GEMM's
-// activations into LDS; helper 0 also adds the pieces of each unit in wave order,
-// stores y (or a chunk's partial tile), runs the K-chunk sums, and arrives at and
-// waits on the device-wide barrier between GEMMs.  Every wave executes exactly
-// one workgroup barrier per GEMM: after the activations of that GEMM are staged.
+// tile ("piece", RT 16 x 16 tiles) to LDS.  Compute waves issue only loads, so
+// waiting for a step's weights never waits for a store.  The helper waves copy
+// each GEMM's activations into LDS (all 12 waves then convert them in place),
+// add the pieces of each unit in wave order, store y (or a chunk's partial
+// tile), run the K-chunk sums, and arrive at and wait on the device-wide barrier
+// between GEMMs.  Every wave passes two workgroup barriers per GEMM: the raw
+// activations have landed, and they are converted.
 //
 // Work (pass_sched.h): a GEMM is cut along K into S chunks of kbc blocks; chunk c
 // goes to a contiguous set of workgroups, which share its sub-tiles as runs of
 // whole units (a unit = one 16-output sub-tile over one chunk).  With S > 1 the
-// chunks' partial tiles of a sub-tile are added by the last chunk to arrive, in
-// chunk order; every sum has a fixed order, so results are bitwise repeatable.
+// chunks' partial tiles of a sub-tile are added in chunk order, at one row tile
+// by the last chunk to arrive and from two on by one designated workgroup; every
+// sum has a fixed order, so results are bitwise repeatable.
 //
 // Per step (16 outputs x 256 weights of one block) the arithmetic is the
-// streaming kernel's: B = sc q exact in binary16, 8 v_mfma_f32_16x16x32_f16
-// against the activations, the min term from fp32 sub-block sums (two
-// v_mfma_f32_16x16x4_f32), then acc += d ds - dmin ms in fp32.
+// streaming kernel's: B = sc q exact in binary16, 8 v_mfma_f32_16x16x32_f16 per
+// row tile against the activations; the min term from 8 more products with the
+// mins, or (MSUM) from the sub-block sums staged as two binary16 parts in one
+// v_mfma_f32_16x16x16_f16 per tile; then acc += d ds - dmin ms in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -596,11 +596,11 @@ struct qgemm_seq {
 namespace {
 
 // K chunks of one GEMM in the persistent pass at R rows: the fewest (dividing
-// the blocks of K, at most PASS_MAX_CHUNKS and at most one per workgroup) whose
+// the blocks of K, at most pass_max_chunks and at most one per workgroup) whose
 // activations fit the kernel's LDS area at R's row tiles; 0 when none does.
 int pass_chunks_of(int64_t KB, int R, int P) {
   if (KB > INT32_MAX || R < 1 || R > PASS_MAX_R) return 0;
-  return pass_chunks((int)KB, R, P, pass_x_area(pass_row_tiles(R)), PASS_MAX_CHUNKS);
+  return pass_chunks((int)KB, R, P, pass_x_area(pass_row_tiles(R)), pass_max_chunks(pass_row_tiles(R)));
 }
 
 // The GEMMs' chunking and workspace needs at R rows; false if a GEMM cannot run

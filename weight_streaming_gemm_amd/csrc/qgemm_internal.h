@@ -141,6 +141,9 @@ constexpr int PASS_PIECES = 2;                   // LDS partial tiles per comput
 constexpr int PASS_RING = 8;                     // weight steps in flight per compute wave (1-2 row tiles)
 inline constexpr int pass_ring(int RT) { return RT <= 2 ? PASS_RING : 7; }   // registers left at 3 row tiles
 constexpr int PASS_MAX_CHUNKS = 32;
+// at one row tile the last chunk to arrive adds a sub-tile's partial tiles in one
+// round of 16 loads: at most 16 chunks there
+inline constexpr int pass_max_chunks(int RT) { return RT == 1 ? 16 : PASS_MAX_CHUNKS; }
 // barrier words: bar[0] global counter, bar[16] exit counter, bar[32 + 32 k] group k's
 // counter, bar[512 + 32 k] group k's release word (k < 8)
 constexpr int PASS_RELEASE_WORD = 512;
