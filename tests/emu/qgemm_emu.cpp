@@ -133,9 +133,10 @@ void pack(const uint8_t* canon, uint8_t* packed, int64_t N, int64_t K) {
 
 // ---- the row-tiled kernel (prefill.hip): plan, activation image, product ----
 
-// the image, as prefill_image_kernel writes it: per (row tile group m, block j,
+// the image as prefill_image_kernel lays it out: per (row tile group m, block j,
 // row tile rt, lane 16 g + r) the row's 64 values of sub-blocks 2g, 2g + 1 as 8
-// A operands and the two sums (bf16 widened to fp32, added in k order)
+// A operands and the two sums (bf16 widened to fp32, added in k order; kept here
+// in fp32, and split into the kernel's two binary16 parts by min_term_parts)
 void prefill_image(const uint16_t* x, int R, int64_t KB, int MT, int64_t mt, std::vector<uint8_t>& img) {
   img.assign((size_t)mt * KB * pf_buf(MT), 0);
   for (int64_t m = 0; m < mt; ++m)
@@ -586,11 +587,11 @@ int emu_prefill(const uint8_t* canon, int64_t N, int64_t K, const uint16_t* x, i
                 }
                 for (int u = 0; u < PF_U; ++u) {
                   f32x4 ms[64] = {};
-                  min_term_f32(sx, c[u], ms);
+                  min_term_parts(sx, c[u], ms);       // the kernel's two binary16 parts of X_s / 256
                   for (int lane = 0; lane < 64; ++lane)
                     for (int i = 0; i < 4; ++i) {
                       acc[rt][u][lane][i] = std::fma(c[u][lane].d, ds[rt][u][lane][i], acc[rt][u][lane][i]);
-                      acc[rt][u][lane][i] = std::fma(c[u][lane].nmin, ms[lane][i], acc[rt][u][lane][i]);
+                      acc[rt][u][lane][i] = std::fma(c[u][lane].nmin * 256.0f, ms[lane][i], acc[rt][u][lane][i]);
                     }
                 }
               }

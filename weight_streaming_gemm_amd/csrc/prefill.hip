@@ -12,8 +12,9 @@
 //
 // is computed per 256-weight block exactly as in the streaming kernel:
 // ds = sum_k (sc_s q_k) x[r, k] on the fp16 matrix cores (exact integer B
-// operands, fp32 sums) and ms = sum_s m_s X_s on the fp32 matrix cores (the
-// sub-block sums X_s kept in fp32), then acc += d ds - dmin ms.
+// operands, fp32 sums) and ms = sum_s m_s X_s from the fp32 sub-block sums X_s
+// written as two binary16 parts of X_s / 256 (one v_mfma_f32_16x16x16_f16 per
+// tile against the mins, as in the pass kernel), then acc += d ds - 256 dmin ms.
 //
 // Work: one workgroup per (128-row tile, output tile of 32 WN), over the whole
 // of K (no split unless the grid is small, so every output is written once, in
@@ -21,7 +22,7 @@
 // the rows, WN along the outputs; a wave owns 64 rows (4 row tiles of 16) x 32
 // outputs (2 sub-tiles of 16): 8 accumulator tiles.  A first kernel converts x
 // once into the LDS image of every (128-row tile, block): binary16 operands in
-// the matrix-core lane layout plus the 8 fp32 sub-block sums per row (72 KiB).  The
+// the matrix-core lane layout plus the 8 sub-block sums per row (72 KiB).  The
 // main kernel copies each block's image straight into LDS with buffer loads
 // that write LDS directly (no registers, no vector instructions),
 // double-buffered: the next block's activations and weights are in flight
@@ -38,8 +39,21 @@ namespace qg {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// The min term's sub-block sums as matrix-core A operands: X_s / 256 (in
+// binary16's range for |x| <= 65504) in two binary16 parts, hi = f16(X_s / 256)
+// and lo = f16(X_s / 256 - hi) (the difference exact in fp32): lane group g holds
+// (hi_2g, hi_2g+1, lo_2g, lo_2g+1) of its row, and B = (m_2g, m_2g+1, m_2g,
+// m_2g+1) of its output, so one 16 x 16 x 16 product adds m_s (hi + lo) over the
+// 8 sub-blocks; the 256 goes back into -dmin (exact).
+__device__ __forceinline__ f16x4 sum_parts(float s0, float s1) {
+  const float a0 = s0 * (1.0f / 256.0f), a1 = s1 * (1.0f / 256.0f);
+  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+  return f16x4{h0, h1, (_Float16)(a0 - (float)h0), (_Float16)(a1 - (float)h1)};
+}
+__device__ __forceinline__ f16x4 min_parts_b(const WConst& c) { return f16x4{c.m[0], c.m[1], c.m[0], c.m[1]}; }
 
 
 
@@ -140,14 +154,19 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
           ds[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], bo, ds[rt][u], 0, 0, 0);
       }
     }
+    f16x4 bm[PF_U];
+    float nmin[PF_U];
+    for (int u = 0; u < PF_U; ++u) {
+      bm[u] = min_parts_b(c[u]);
+      nmin[u] = c[u].nmin * 256.0f;
+    }
     for (int rt = 0; rt < PF_RT; ++rt) {
-      const f32x2 sx = *reinterpret_cast<const f32x2*>(X + pf_sum_chunk(MT, wm * PF_RT + rt) * PF_CHUNK + lane * 16);
+      const f16x4 sx = *reinterpret_cast<const f16x4*>(X + pf_sum_chunk(MT, wm * PF_RT + rt) * PF_CHUNK + lane * 16);
       for (int u = 0; u < PF_U; ++u) {
-        f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x4f32(sx.x, min_operand(c[u], 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        ms = __builtin_amdgcn_mfma_f32_16x16x4f32(sx.y, min_operand(c[u], 1), ms, 0, 0, 0);
+        const f32x4 ms = __builtin_amdgcn_mfma_f32_16x16x16f16(sx, bm[u], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         for (int i = 0; i < 4; ++i) {
           acc[rt][u][i] = __builtin_fmaf(c[u].d, ds[rt][u][i], acc[rt][u][i]);
-          acc[rt][u][i] = __builtin_fmaf(c[u].nmin, ms[i], acc[rt][u][i]);
+          acc[rt][u][i] = __builtin_fmaf(nmin[u], ms[i], acc[rt][u][i]);
         }
       }
     }
@@ -188,8 +207,8 @@ prefill_kernel(const uint8_t* __restrict__ packed, uint32_t quant_bytes, uint32_
 // block j, at (m KB + j) * 9 MT KiB, chunk (row tile rt, step t) at 1 KiB (8 rt + t)
 // holds lane 16 g + r's binary16 A operand of row 16 (MT m + rt) + r (k = 256 j +
 // 64 g + 32 (e & 1) + 4 t + (e >> 1) for element e), and chunk 8 MT + rt the
-// sub-block sums of those rows (lane 16 g + r: X_2g, X_2g+1 in fp32, then 8
-// zero bytes).  Rows past R are zeros.  One thread per
+// sub-block sums of those rows (lane 16 g + r: the two binary16 parts of X_2g /
+// 256 and X_2g+1 / 256, then 8 zero bytes).  Rows past R are zeros.  One thread per
 // (m, j, rt, lane): it reads the row's 64 values of sub-blocks 2g, 2g + 1 (one
 // 128-byte line) and writes 8 operands and one sum entry.
 __global__ void __launch_bounds__(256)
@@ -220,7 +239,9 @@ prefill_image_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ img, 
   float s0 = 0.f, s1 = 0.f;
   for (int c = 0; c < 4; ++c) s0 = sum8_bf16(v[c], s0);
   for (int c = 4; c < 8; ++c) s1 = sum8_bf16(v[c], s1);
-  *reinterpret_cast<f32x4*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) = f32x4{s0, s1, 0.f, 0.f};
+  const f16x4 parts = sum_parts(s0, s1);
+  *reinterpret_cast<u32x4*>(dst + pf_sum_chunk(MT, rt) * PF_CHUNK + lane * 16) =
+      u32x4{__builtin_bit_cast(uint32_t, f16x2{parts[0], parts[1]}), __builtin_bit_cast(uint32_t, f16x2{parts[2], parts[3]}), 0u, 0u};
 }
 
 // y[i] = sum over chunks z = 0 .. S-1 of part[z * slice + i], in chunk order;
