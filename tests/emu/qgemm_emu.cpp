@@ -403,7 +403,7 @@ int emu_stream_seq(int G, const uint8_t* const* canon, const int64_t* Ns, const 
           const int64_t tr = t % e.Treal, jr = (t / e.Treal) * KB + j;   // output tile, block
           if ((t / e.Treal) * KB != jbase) return -3;
           wave_step(e.packed.data(), e.hdr_off, (tr * nwn + wn) * NT, NT, e.NS, jr, e.KB, xslots, xsums, R, b, RT,
-                    e.msum != 0, acc.data());
+                    e.msum != 0 ? 2 : 0, acc.data());
           const bool sub_end = it + 1 == b_w;
           if (j != KB - 1 && !sub_end) continue;
           if (ja == 0 && j == KB - 1) {

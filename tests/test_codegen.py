@@ -83,7 +83,7 @@ VARIANTS = [(1, 8), (2, 8), (3, 8), (4, 8)]
 @pytest.mark.parametrize("msum", [False, True])
 def test_single_gemm_step_loop_keeps_ring_in_flight(asm, rt, nw, msum):
     body = _kernel_body(asm, rt, nw, msum)
-    per_step = 8 * rt + (2 * rt if msum else 8 * rt)  # MFMAs of one step (sums: two fp32 products)
+    per_step = 8 * rt + (rt if msum else 8 * rt)  # MFMAs of one step (sums: one fp16 product of their two parts)
     steps = [(w, n) for w, n in _mfma_groups(body) if n >= per_step]
     assert steps, "no step loop found"
     for w, n in steps:

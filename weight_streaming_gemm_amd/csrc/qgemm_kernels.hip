@@ -35,6 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ WConst header_consts(u32x4 h, int g) { return header_consts(h.x, h.y, h.z, h.w, g); }
 
@@ -108,9 +109,10 @@ pack_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int
 //
 // Min term.  Either eight more matrix-core products per step with B = m_s
 // (MSUM = false), or, when a range uses each block for several steps, one
-// pair of fp32 products per step of the sub-block sums of x (kept in fp32),
-// staged with the activations (MSUM = true).  The vector-unit variant (VR = R <= 4 rows) replaces the
-// products by dot products on the vector units and always uses the sums.
+// fp16 product per step of the sub-block sums of x, staged with the
+// activations as two binary16 parts of X_s / 256 (MSUM = true).  The
+// vector-unit variant (VR = R <= 4 rows) replaces the products by dot products
+// on the vector units and always uses the sums, staged in fp32.
 //
 // Streams.  At the start of a range the workgroup converts the activations of
 // the blocks the range touches (R rows x 256 bf16 each) into the matrix-core
@@ -145,6 +147,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 
 // the sum of four bf16 values (two dwords) in fp32, with two dot products against ones
+// The matrix-core min term's sub-block sums: X_s / 256 (in binary16's range for
+// |x| <= 65504) in two binary16 parts, hi = f16(X_s / 256) and lo = f16(X_s / 256
+// - hi) (the difference exact in fp32): lane group g holds (hi_2g, hi_2g+1,
+// lo_2g, lo_2g+1) of its row and B = (m_2g, m_2g+1, m_2g, m_2g+1) of its output,
+// so one 16 x 16 x 16 product adds m_s (hi + lo) over the 8 sub-blocks; the 256
+// goes back into -dmin (exact).
+__device__ __forceinline__ f16x4 sum_parts(float s0, float s1) {
+  const float a0 = s0 * (1.0f / 256.0f), a1 = s1 * (1.0f / 256.0f);
+  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+  return f16x4{h0, h1, (_Float16)(a0 - (float)h0), (_Float16)(a1 - (float)h1)};
+}
+__device__ __forceinline__ f16x4 min_parts_b(const WConst& c) { return f16x4{c.m[0], c.m[1], c.m[0], c.m[1]}; }
 __device__ __forceinline__ float sum4_bf16(uint32_t d0, uint32_t d1) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
@@ -349,8 +363,13 @@ stream_kernel(StreamArgs a) {
         s0 += dpp_f32<0xB1>(s0); s1 += dpp_f32<0xB1>(s1);    // lane ^ 1
         s0 += dpp_f32<0x4E>(s0); s1 += dpp_f32<0x4E>(s1);    // lane ^ 2
         s0 += dpp_f32<0x104>(s0); s1 += dpp_f32<0x104>(s1);  // lane + 4 (for lane t = 0)
-        if (t == 0)
-          *reinterpret_cast<f32x2*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 8) = f32x2{s0, s1};
+        if (t == 0) {
+          // fp32 for the vector-unit variant's multiply-adds, two binary16 parts for the matrix cores
+          if constexpr (VALU)
+            *reinterpret_cast<f32x2*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 8) = f32x2{s0, s1};
+          else
+            *reinterpret_cast<f16x4*>(xlds + rw[k].b * SB + XS + (gg * R + rw[k].r) * 8) = sum_parts(s0, s1);
+        }
         // one row at a time: few values live while the weight ring is in flight
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -429,7 +448,7 @@ stream_kernel(StreamArgs a) {
     }
   };
 
-  // MSUM: the min term from the staged fp32 sub-block sums (two fp32 products),
+  // MSUM: the min term from the staged sub-block sums (one fp16 product of their two parts),
   // else from the activation operands of the 8 steps (eight products)
   auto compute = [&](const WStage<NT>& st, int slot) __attribute__((always_inline)) {
     constexpr bool msum = MSUM;
@@ -461,20 +480,20 @@ stream_kernel(StreamArgs a) {
         }
       }
     }
+    float nmin[NT];
+    for (int u = 0; u < NT; ++u) nmin[u] = msum ? c[u].nmin * 256.0f : c[u].nmin;
     if constexpr (msum)
       for (int rt = 0; rt < RT; ++rt) {
-        const f32x2 xsum = *reinterpret_cast<const f32x2*>(xlds + base + XS + xoff[rt] / 2);
-        for (int u = 0; u < NT; ++u) {
-          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.x, min_operand(c[u], 0), ms[u][rt], 0, 0, 0);
-          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum.y, min_operand(c[u], 1), ms[u][rt], 0, 0, 0);
-        }
+        const f16x4 xsum = *reinterpret_cast<const f16x4*>(xlds + base + XS + xoff[rt] / 2);
+        for (int u = 0; u < NT; ++u)
+          ms[u][rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(xsum, min_parts_b(c[u]), ms[u][rt], 0, 0, 0);
       }
     // acc += d * ds - dmin * ms, two fused multiply-adds per element
     for (int u = 0; u < NT; ++u)
       for (int rt = 0; rt < RT; ++rt)
         for (int i = 0; i < 4; ++i) {
           acc[u][rt][i] = __builtin_fmaf(c[u].d, ds[u][rt][i], acc[u][rt][i]);
-          acc[u][rt][i] = __builtin_fmaf(c[u].nmin, ms[u][rt][i], acc[u][rt][i]);
+          acc[u][rt][i] = __builtin_fmaf(nmin[u], ms[u][rt][i], acc[u][rt][i]);
         }
   };
 
