@@ -289,9 +289,10 @@ int qgemm_destroy(qgemm_t h);
  * taken: measured faster there, as the products grow with the row tiles):
  *   0                          eight more matrix-core products per weight block,
  *                              of the activation operands with the mins;
- *   QGEMM_SEQ_SUB_BLOCK_SUMS   the fp32 sub-block sums X_s of x, computed when
- *                              the activations are staged, times the mins in
- *                              two fp32 products per block.
+ *   QGEMM_SEQ_SUB_BLOCK_SUMS   the sub-block sums X_s of x (fp32, staged as two
+ *                              binary16 parts of X_s / 256 when the activations
+ *                              are staged), times the mins in one fp16 product
+ *                              per block and row tile.
  * (Both give results within the stated tolerance; they round differently.)
  * and, with QGEMM_SEQ_PERSISTENT, the dependency between GEMMs:
  *   0                          GEMM i + 1 starts after GEMM i has finished on

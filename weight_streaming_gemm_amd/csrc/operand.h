@@ -5,8 +5,9 @@
 // For lane group g (sub-blocks 2g, 2g+1 of a block) the B operand element e of
 // step t is sc_{2g + (e & 1)} * q_k for k = operand_k(g, t, e) (layout.h): an
 // integer <= 63 * 15 = 945, exact in binary16.  The min term is either a
-// product of the activation operands with the mins (build_m_full), or two fp32
-// products of the fp32 sub-block sums of x with the mins (min_operand).
+// product of the activation operands with the mins (build_m_full), or a product
+// of the sub-block sums of x with the mins (min_operand, and the kernels' own
+// two-part staging of the sums).
 #pragma once
 #include <stdint.h>
 
@@ -94,11 +95,11 @@ QG_HD f16x8 build_b(uint32_t w, const WConst& c) {
 }
 
 // The min term of a block, sum over k of m_sub(k) x_k, is sum over s of m_s X_s
-// with X_s the sum of x over sub-block s.  The sums stay in fp32: a bf16 sum of
-// 32 values reaches 32 * 65504, far beyond binary16's range, so they enter two
-// fp32 matrix-core products of depth 4 (v_mfma_f32_16x16x4_f32).  In product h
-// (0, 1) lane group g contributes X_{2g+h} of its row (A) and m_{2g+h} of its
-// output (B); the two products together cover the 8 sub-blocks.
+// with X_s the sum of x over sub-block s.  The sums are formed in fp32 (a bf16 sum
+// of 32 values reaches 32 * 65504, far beyond binary16's range); the matrix-core
+// kernels stage them as two binary16 parts of X_s / 256 for one fp16 product per
+// tile, and the vector-unit variant multiplies them in fp32 by the mins below
+// (lane group g: m_2g for h = 0, m_2g+1 for h = 1).
 QG_HD float min_operand(const WConst& c, int h) { return (float)c.m[h]; }
 // Without the sums, the min term is the product of each step's activation
 // operand with B = (m_2g, m_2g+1) in every pair (eight products per block).
